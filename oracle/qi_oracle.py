@@ -1,0 +1,297 @@
+"""fp64 CPU oracle for block-causal 3D-RoPE joint attention with a prefix KV cache.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module; only the tests, the smoke check and the benchmark's CPU
+baseline leg use it.  It shares no code with the HIP library (no kernels,
+headers, tables or helpers): every step below is the plain definition, written
+out from the pages, in NumPy float64, slow and obvious on purpose.
+
+Sources (cited by page title and section):
+  [OV]   "Qwen-Image-2.1: how an image is made from noise" course overview
+         (OpenArchLab), lesson list and block cards 3A, 3B, 3C, 4A, 6A, 6B.
+  [1B]   "1B - Qwen3-VL Context & Zero-Center RMSNorm" (OpenArchLab), sections 1-4.
+  [3A]   "3A - 3D Axial RoPE (16, 56, 56) & Zero-Centered Grid" (OpenArchLab), sections 1-4.
+  [EDIT] "QwenImageTransformer2DModel source reading (Qwen-Image-Edit)", sections
+         5.1 (timestep embedding), 5.2 (modulation), 6 (attention processor),
+         7.1-7.3 (three-axis RoPE), 8.2 (shape walk-through).
+
+Readings taken where the pages are silent or disagree are listed in the
+repository's design notes; each is also stated at the function that uses it.
+Parity status: every function here is pinned by the CPU tests in
+tests/test_oracle_pins.py (closed forms, worked values from the pages,
+invariants and brute force on tiny inputs).
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+SEG_TEXT, SEG_IMAGE, SEG_TEXT_BIDIR = 0, 1, 2
+HEAD_DIM = 128
+BANDS = (16, 56, 56)
+THETA = 10000.0
+
+
+# ------------------------------------------------------------------------------------------------
+# sequence layout
+# ------------------------------------------------------------------------------------------------
+
+def segment_ids(segments) -> np.ndarray:
+    """Segment index of every token of the joint sequence [text | refs | target]
+    ([OV] block card 2A: one sequence, target appended last, each token labelled)."""
+    return np.concatenate([np.full(s.n_tokens, i, dtype=np.int64) for i, s in enumerate(segments)])
+
+
+def split_counts(segments) -> Tuple[int, int, int]:
+    """(S, P, T): all tokens, prefix tokens (text + references), target tokens (the last segment)."""
+    S = sum(s.n_tokens for s in segments)
+    T = segments[-1].n_tokens
+    return S, S - T, T
+
+
+# ------------------------------------------------------------------------------------------------
+# 3D axial positions and rotation tables
+# ------------------------------------------------------------------------------------------------
+
+def text_start(segments, text_pos0: Optional[int] = None) -> int:
+    """First text position.  [3A] section 1 only says text steps +1 on all axes; the start
+    follows [EDIT] section 7.2 with centred grids: text continues after max over images of
+    max(H//2, W//2).  An explicit override wins."""
+    if text_pos0 is not None and text_pos0 >= 0:
+        return int(text_pos0)
+    best = 0
+    for s in segments:
+        if s.kind == SEG_IMAGE:
+            best = max(best, s.grid_h // 2, s.grid_w // 2)
+    return best
+
+
+def positions(segments, text_pos0: Optional[int] = None) -> np.ndarray:
+    """Per-token (frame, height, width) integer coordinates, shape [S, 3].
+
+    Text ([3A] section 1): every text token advances all three axes by one.
+    Image ([3A] section 1; [EDIT] section 7.3): frame fixed for the whole image,
+    height runs -(H - H//2) .. H//2 - 1 and width -(W - W//2) .. W//2 - 1,
+    row-major (height outer, width inner)."""
+    p0 = text_start(segments, text_pos0)
+    out: List[Tuple[int, int, int]] = []
+    n_text = 0
+    for s in segments:
+        if s.kind in (SEG_TEXT, SEG_TEXT_BIDIR):
+            for _ in range(s.n_tokens):
+                p = p0 + n_text
+                out.append((p, p, p))
+                n_text += 1
+        elif s.kind == SEG_IMAGE:
+            H, W = s.grid_h, s.grid_w
+            assert H * W == s.n_tokens
+            for y in range(H):
+                for x in range(W):
+                    out.append((s.frame, y - (H - H // 2), x - (W - W // 2)))
+        else:
+            raise ValueError(s.kind)
+    return np.array(out, dtype=np.int64).reshape(-1, 3)
+
+
+def inv_freq(bands: Sequence[int] = BANDS, theta: float = THETA) -> Tuple[np.ndarray, np.ndarray]:
+    """Rotation frequency of each of the 64 complex pairs and the axis it belongs to.
+
+    Band a of width d_a owns d_a/2 pairs with frequency theta^(-2i/d_a), i < d_a/2
+    ([EDIT] section 7.1, one frequency table per axis; [3A] section 1 band split
+    16 | 56 | 56 for frame | height | width).  Returns (freq[64] fp64, axis[64] int)."""
+    freqs, axes = [], []
+    for a, d in enumerate(bands):
+        assert d % 2 == 0
+        for i in range(d // 2):
+            freqs.append(1.0 / math.pow(theta, (2 * i) / d))
+            axes.append(a)
+    return np.array(freqs, dtype=np.float64), np.array(axes, dtype=np.int64)
+
+
+def angles(pos: np.ndarray, bands=BANDS, theta=THETA) -> np.ndarray:
+    """phi[s, k] = pos[s, axis(k)] * freq[k], fp64, shape [S, 64]."""
+    f, ax = inv_freq(bands, theta)
+    out = np.empty((pos.shape[0], f.shape[0]), dtype=np.float64)
+    for k in range(f.shape[0]):
+        out[:, k] = pos[:, ax[k]].astype(np.float64) * f[k]
+    return out
+
+
+def rope_tables(pos: np.ndarray, bands=BANDS, theta=THETA) -> Tuple[np.ndarray, np.ndarray]:
+    """cos(phi), sin(phi) in fp64, shape [S, 64]."""
+    phi = angles(pos, bands, theta)
+    return np.cos(phi), np.sin(phi)
+
+
+def rope_tables_f32(pos: np.ndarray, bands=BANDS, theta=THETA) -> Tuple[np.ndarray, np.ndarray]:
+    """The same tables computed one value at a time with the C library's double cos/sin and
+    rounded once to fp32 (the stored form of the device tables)."""
+    f, ax = inv_freq(bands, theta)
+    c = np.empty((pos.shape[0], f.shape[0]), dtype=np.float32)
+    s = np.empty_like(c)
+    cache = {}
+    for r in range(pos.shape[0]):
+        for k in range(f.shape[0]):
+            key = (int(pos[r, ax[k]]), k)
+            v = cache.get(key)
+            if v is None:
+                a = float(key[0]) * float(f[k])
+                v = (np.float32(math.cos(a)), np.float32(math.sin(a)))
+                cache[key] = v
+            c[r, k], s[r, k] = v
+    return c, s
+
+
+def rotate(x: np.ndarray, cos_t: np.ndarray, sin_t: np.ndarray) -> np.ndarray:
+    """Rotate adjacent pairs (x[2k], x[2k+1]) by phi[k]: the pair read as a complex number
+    times e^{i phi} ([3A] section 1: RoPE rotates pairs of Q/K dims by an angle proportional
+    to position; [EDIT] section 7.1: the tables hold the complex factors, 64 per token).
+    x: [S, ..., 128]; cos_t/sin_t: [S, 64]."""
+    x = np.asarray(x, dtype=np.float64)
+    extra = (slice(None),) + (None,) * (x.ndim - 2)
+    c = cos_t[extra]
+    s = sin_t[extra]
+    a = x[..., 0::2]
+    b = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = a * c - b * s
+    out[..., 1::2] = a * s + b * c
+    return out
+
+
+# ------------------------------------------------------------------------------------------------
+# norms
+# ------------------------------------------------------------------------------------------------
+
+def rms_norm(x: np.ndarray, w: Optional[np.ndarray], eps: float = 1e-6) -> np.ndarray:
+    """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * w (the per-head QK-norm of
+    [EDIT] section 6; [OV] card 4A names QK-RMSNorm)."""
+    x = np.asarray(x, dtype=np.float64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    y = x * r
+    return y if w is None else y * w
+
+
+def zero_center_rms_norm(x: np.ndarray, w: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """ZeroCenterRMSNorm: x * rrms * (w + 1), weights stored as scale - 1 ([1B] sections 1-3)."""
+    x = np.asarray(x, dtype=np.float64)
+    rrms = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return x * rrms * (np.asarray(w, dtype=np.float64) + 1.0)
+
+
+# ------------------------------------------------------------------------------------------------
+# block-causal mask
+# ------------------------------------------------------------------------------------------------
+
+def mask_dense(segments) -> np.ndarray:
+    """visible[q, k] for the Block-Causal mask ([OV] card 3C and lesson 3C: text reads only
+    what precedes it, tokens of one image see each other both ways; [OV] learning goals: the
+    prefix never sees the target).  Reading: a query sees every key of earlier segments, all
+    keys of its own segment if that segment is an image (or bidirectional text), keys k <= q
+    of its own text segment, and nothing of later segments."""
+    sid = segment_ids(segments)
+    kinds = np.array([s.kind for s in segments])
+    S = sid.shape[0]
+    q = np.arange(S)[:, None]
+    k = np.arange(S)[None, :]
+    sq, sk = sid[:, None], sid[None, :]
+    same = sq == sk
+    causal_text = kinds[sid][:, None] == SEG_TEXT
+    return (sk < sq) | (same & ~causal_text) | (same & causal_text & (k <= q))
+
+
+def blockmap(mask: np.ndarray, tile_q: int, tile_k: int) -> np.ndarray:
+    """Tile classes over in-range pairs: 0 = no visible pair (skip), 1 = all visible (full),
+    2 = mixed (partial).  Shape [ceil(S/tile_q), ceil(S/tile_k)], uint8."""
+    Sq, Sk = mask.shape
+    nq, nk = -(-Sq // tile_q), -(-Sk // tile_k)
+    out = np.zeros((nq, nk), dtype=np.uint8)
+    for i in range(nq):
+        for j in range(nk):
+            sub = mask[i * tile_q:(i + 1) * tile_q, j * tile_k:(j + 1) * tile_k]
+            if sub.all():
+                out[i, j] = 1
+            elif sub.any():
+                out[i, j] = 2
+    return out
+
+
+# ------------------------------------------------------------------------------------------------
+# attention
+# ------------------------------------------------------------------------------------------------
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: Optional[np.ndarray] = None,
+              scale: Optional[float] = None, chunk: int = 512) -> np.ndarray:
+    """Masked softmax attention per head, O = softmax(Q K^T * scale, masked to -inf) V.
+    q: [Nq, H, d], k, v: [Nk, H, d], mask: [Nq, Nk] bool or None.  Scale defaults to
+    1/sqrt(d), the scaled-dot-product default used by the attention dispatch in [EDIT]
+    section 6 (no scale is passed there).  Query rows are processed in chunks to bound memory."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    Nq, H, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.empty((Nq, H, v.shape[2]), dtype=np.float64)
+    for h in range(H):
+        kh = np.ascontiguousarray(k[:, h, :])
+        vh = np.ascontiguousarray(v[:, h, :])
+        for c0 in range(0, Nq, chunk):
+            c1 = min(Nq, c0 + chunk)
+            s = (q[c0:c1, h, :] @ kh.T) * scale
+            if mask is not None:
+                s = np.where(mask[c0:c1], s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            out[c0:c1, h, :] = (p @ vh) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def prep_qk(x: np.ndarray, cos_t, sin_t, w=None, eps: float = 1e-6) -> np.ndarray:
+    """Optional per-head QK-RMSNorm, then the 3D rotation (norm before RoPE, as in [EDIT]
+    section 6: QK normalisation, then RoPE, then the joint concat)."""
+    y = np.asarray(x, dtype=np.float64)
+    if w is not None:
+        y = rms_norm(y, w, eps)
+    return rotate(y, cos_t, sin_t) if cos_t is not None else y
+
+
+def step1(q, k, v, segments, cos_t, sin_t, q_w=None, k_w=None, eps: float = 1e-6,
+          scale: Optional[float] = None):
+    """Denoising step 1: full block-causal attention over the whole sequence; the prefix's
+    K (normalised and rotated) and V are kept as the cache ([OV] card 6A: step 1 computes
+    prefix and target and stores the prefix K/V).  Returns (O [S,H,d], (K_cache, V_cache))."""
+    S, P, T = split_counts(segments)
+    qr = prep_qk(q, cos_t, sin_t, q_w, eps)
+    kr = prep_qk(k, cos_t, sin_t, k_w, eps)
+    o = attention(qr, kr, v, mask_dense(segments), scale)
+    return o, (kr[:P].copy(), np.asarray(v, dtype=np.float64)[:P].copy())
+
+
+def cached_step(q_t, k_t, v_t, cache, cos_t, sin_t, q_w=None, k_w=None, eps: float = 1e-6,
+                scale: Optional[float] = None) -> np.ndarray:
+    """Euler steps 2..N: only target queries, against [cached prefix K/V ; fresh target K/V].
+    The target sees every token ([OV] card 3C / 6A), so no mask.  cos_t/sin_t are the
+    target rows of the tables."""
+    kc, vc = cache
+    qr = prep_qk(q_t, cos_t, sin_t, q_w, eps)
+    kr = prep_qk(k_t, cos_t, sin_t, k_w, eps)
+    keys = np.concatenate([kc, kr], axis=0)
+    vals = np.concatenate([vc, np.asarray(v_t, dtype=np.float64)], axis=0)
+    return attention(qr, keys, vals, None, scale)
+
+
+def euler(x: np.ndarray, v: np.ndarray, sigma_k: float, sigma_k1: float) -> np.ndarray:
+    """x_{k+1} = x_k + (sigma_{k+1} - sigma_k) * v ([OV] learning goals and card 6B)."""
+    return np.asarray(x, dtype=np.float64) + (float(sigma_k1) - float(sigma_k)) * np.asarray(v, dtype=np.float64)
+
+
+# ------------------------------------------------------------------------------------------------
+# flop / byte accounting (used by the benchmark's reporting, not by the device path)
+# ------------------------------------------------------------------------------------------------
+
+def visible_pairs(segments) -> int:
+    """Number of visible (query, key) pairs per head for step 1, counted from the dense mask."""
+    return int(mask_dense(segments).sum())

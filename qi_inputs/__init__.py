@@ -1,0 +1,164 @@
+"""Seeded synthetic inputs shared by the oracle, the tests and the benchmark.
+
+This module holds workload shapes and random draws only.  It contains none of
+the method's arithmetic (no positions, rotations, masks, norms or attention):
+it says which token segments a workload has, draws N(0,1) numbers from a
+counter-style seed ``[cfg_id, tensor_id, step, layer]`` and rounds them to the
+storage type the device path consumes (bf16 by round-to-nearest-even, via
+fp32).  Both the fp64 oracle and the HIP path receive exactly these bits.
+
+Workloads (joint sequence order: text first, then reference images, target
+image last; the 1024x1024 latent grid is 64x64 tokens, "Qwen-Image-Edit"
+page, section 8.2 shape table):
+
+  cfg0  fp32, 2 heads; text 16 + ref 4x4 (frame 1) + target 4x4 (frame 0)
+  cfg1  bf16, 24 heads; text 256 + ref 32x32 (frame 1) + target 32x32
+  cfg2  bf16, 24 heads; text 512 + target 64x64
+  cfg3  bf16, 24 heads; text 1024 + 4 refs 64x64 (frames 1..4) + target 64x64
+        (17,408 prefix tokens, 21,504 keys)
+  cfg3_t512  the same with 512 text tokens (16,896 prefix, 20,992 keys)
+  cfg4  bf16, 24 heads; text 512 + 10 refs 32x32 (frames 1..10) + target 64x64
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Sequence, Tuple
+
+import numpy as np
+
+# segment kinds (same numbering as the C header's qi_seg_kind)
+SEG_TEXT = 0          # text, token-causal inside the segment
+SEG_IMAGE = 1         # one image: all its tokens see each other
+SEG_TEXT_BIDIR = 2    # text read as one bidirectional block
+
+# tensor ids for the seed tuple
+T_Q, T_K, T_V, T_QW, T_KW, T_X0, T_VEL, T_QT, T_KT, T_VT = range(10)
+T_WEIGHT_BASE = 100   # model weights of the full-layer workload: 100 + index
+
+
+@dataclasses.dataclass(frozen=True)
+class Segment:
+    kind: int
+    n_tokens: int
+    frame: int = 0
+    grid_h: int = 0
+    grid_w: int = 0
+
+
+def text(n: int, bidir: bool = False) -> Segment:
+    return Segment(SEG_TEXT_BIDIR if bidir else SEG_TEXT, n)
+
+
+def image(h: int, w: int, frame: int) -> Segment:
+    return Segment(SEG_IMAGE, h * w, frame, h, w)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    cfg_id: int
+    segments: Tuple[Segment, ...]
+    n_head: int = 24
+    head_dim: int = 128
+    dtype: str = "bf16"          # storage type of q/k/v/o ("bf16" or "f32")
+    theta: float = 10000.0
+    bands: Tuple[int, int, int] = (16, 56, 56)
+    qk_rmsnorm: bool = False     # q/k pass a per-head RMSNorm with weights 1+N(0,0.02)
+    n_steps: int = 8             # Euler steps (step 1 full + cached steps)
+    latent_ch: int = 64          # channels of the velocity / latent per target token
+
+    @property
+    def S(self) -> int:
+        return sum(s.n_tokens for s in self.segments)
+
+    @property
+    def T(self) -> int:
+        return self.segments[-1].n_tokens
+
+    @property
+    def P(self) -> int:
+        return self.S - self.T
+
+
+WORKLOADS = {
+    "cfg0": Workload("cfg0", 0, (text(16), image(4, 4, 1), image(4, 4, 0)), n_head=2, dtype="f32",
+                     n_steps=2),
+    "cfg1": Workload("cfg1", 1, (text(256), image(32, 32, 1), image(32, 32, 0)), qk_rmsnorm=True),
+    "cfg2": Workload("cfg2", 2, (text(512), image(64, 64, 0))),
+    "cfg3": Workload("cfg3", 3, (text(1024),) + tuple(image(64, 64, f) for f in (1, 2, 3, 4))
+                     + (image(64, 64, 0),)),
+    "cfg3_t512": Workload("cfg3_t512", 3, (text(512),) + tuple(image(64, 64, f) for f in (1, 2, 3, 4))
+                          + (image(64, 64, 0),)),
+    "cfg4": Workload("cfg4", 4, (text(512),) + tuple(image(32, 32, f) for f in range(1, 11))
+                     + (image(64, 64, 0),)),
+}
+
+
+def small_workload(name: str, segments: Sequence[Segment], n_head: int = 2, dtype: str = "bf16",
+                   cfg_id: int = 90, qk_rmsnorm: bool = False) -> Workload:
+    """An ad-hoc workload for edge-case tests (ragged tiles, odd grids, several text runs)."""
+    return Workload(name, cfg_id, tuple(segments), n_head=n_head, dtype=dtype, qk_rmsnorm=qk_rmsnorm)
+
+
+# ----------------------------------------------------------------------------------------------
+# random draws and storage rounding
+# ----------------------------------------------------------------------------------------------
+
+def rng(cfg_id: int, tensor_id: int, step: int = 0, layer: int = 0) -> np.random.Generator:
+    return np.random.default_rng([cfg_id, tensor_id, step, layer])
+
+
+def normal(cfg_id: int, tensor_id: int, shape, step: int = 0, layer: int = 0,
+           mean: float = 0.0, std: float = 1.0) -> np.ndarray:
+    """fp64 draws N(mean, std^2) from the seed tuple [cfg_id, tensor_id, step, layer]."""
+    x = rng(cfg_id, tensor_id, step, layer).standard_normal(size=shape)
+    return x * std + mean
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (nearest, ties to even); returns the uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    r = np.where(nan, (u >> 16) | 0x40, r)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@dataclasses.dataclass
+class Stored:
+    """One input tensor: the bits handed to the device and the same values as fp64."""
+    bits: np.ndarray      # uint16 (bf16) or float32 array, as stored
+    f64: np.ndarray       # the stored values, exactly, as fp64
+    dtype: str
+
+
+def stored(x64: np.ndarray, dtype: str) -> Stored:
+    if dtype == "bf16":
+        b = f32_to_bf16_bits(x64.astype(np.float32))
+        return Stored(b, bf16_bits_to_f64(b), dtype)
+    if dtype == "f32":
+        f = x64.astype(np.float32)
+        return Stored(f, f.astype(np.float64), dtype)
+    raise ValueError(dtype)
+
+
+def qkv(wl: Workload, n_tok: int, step: int = 0, layer: int = 0, ids=(T_Q, T_K, T_V)) -> List[Stored]:
+    """Q, K, V of shape [n_tok, n_head, head_dim], N(0,1), stored in the workload dtype."""
+    shape = (n_tok, wl.n_head, wl.head_dim)
+    return [stored(normal(wl.cfg_id, t, shape, step, layer), wl.dtype) for t in ids]
+
+
+def qk_norm_weights(wl: Workload, layer: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-head RMSNorm weights 1 + N(0, 0.02^2), fp32 (shared by all heads), as fp64 arrays."""
+    wq = normal(wl.cfg_id, T_QW, (wl.head_dim,), 0, layer, 1.0, 0.02).astype(np.float32)
+    wk = normal(wl.cfg_id, T_KW, (wl.head_dim,), 0, layer, 1.0, 0.02).astype(np.float32)
+    return wq.astype(np.float64), wk.astype(np.float64)
+
+
+def sigmas(n_steps: int) -> np.ndarray:
+    """Euler sigma schedule sigma_k = 1 - k/n_steps, k = 0..n_steps (fp64), the linspace(1, 0, n+1) grid."""
+    return np.array([1.0 - k / n_steps for k in range(n_steps + 1)], dtype=np.float64)

@@ -1,0 +1,430 @@
+"""Pins of the fp64 oracle against facts the pages and the mathematics fix (CPU only).
+
+Each test ties one oracle function to something other than itself: values printed on the
+pages (golden fixtures under tests/golden/, each citing its passage), closed forms,
+invariants, and brute force on tiny inputs.  The "planted mistake" tests at the end build
+plausible wrong variants of oracle steps and check that a pin rejects each one.
+"""
+import cmath
+import math
+import os
+
+import numpy as np
+import pytest
+
+import qi_inputs as qin
+from oracle import qi_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name, prefix=None):
+    out = []
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        parts = line.split()
+        if prefix is not None:
+            if parts[0] != prefix:
+                continue
+            parts = parts[1:]
+        elif not parts[0].lstrip("-").isdigit():
+            continue
+        out.append([int(x) for x in parts])
+    return np.array(out)
+
+
+TINY = (qin.text(2), qin.image(2, 2, 1), qin.image(2, 3, 0))
+MASK_TINY = (qin.text(3), qin.Segment(qin.SEG_IMAGE, 2, 1, 1, 2), qin.Segment(qin.SEG_IMAGE, 2, 0, 1, 2))
+
+
+# ---------------------------------------------------------------------------------------------
+# positions
+# ---------------------------------------------------------------------------------------------
+
+def test_grid_h4_heights_from_page():
+    want = None
+    for line in open(os.path.join(GOLDEN, "grid_h4_heights.txt")):
+        if line.startswith("heights"):
+            want = [int(x) for x in line.split()[1:]]
+    pos = O.positions((qin.image(4, 1, 0),))
+    assert list(pos[:, 1]) == want == [-2, -1, 0, 1]
+
+
+def test_tiny_positions_hand_derived():
+    assert np.array_equal(O.positions(TINY), _rows("tiny_positions.txt"))
+
+
+def test_image_coords_independent_of_prompt_length():
+    # "3A" section 4: the same target with 10 and with 30 text tokens gets the same image coords
+    a = O.positions((qin.text(10), qin.image(6, 5, 0)), text_pos0=0)
+    b = O.positions((qin.text(30), qin.image(6, 5, 0)), text_pos0=0)
+    assert np.array_equal(a[10:], b[30:])
+    # also with the automatic text start
+    a = O.positions((qin.text(10), qin.image(6, 5, 0)))
+    b = O.positions((qin.text(30), qin.image(6, 5, 0)))
+    assert np.array_equal(a[10:], b[30:])
+
+
+def test_same_row_same_height_different_width():
+    # "3A" section 3: two tokens in one row share the height and differ in width
+    pos = O.positions((qin.image(5, 7, 2),))
+    for r in range(5):
+        row = pos[r * 7:(r + 1) * 7]
+        assert len(set(row[:, 1])) == 1 and len(set(row[:, 2])) == 7 and set(row[:, 0]) == {2}
+
+
+def test_text_steps_all_axes_and_start():
+    pos = O.positions((qin.text(5), qin.image(64, 64, 1), qin.image(64, 64, 0)))
+    assert np.array_equal(pos[:5], np.array([[32 + j] * 3 for j in range(5)]))
+    # odd grid: heights -(H - H//2) .. H//2 - 1
+    p = O.positions((qin.image(5, 3, 0),))
+    assert sorted(set(p[:, 1])) == [-3, -2, -1, 0, 1] and sorted(set(p[:, 2])) == [-2, -1, 0]
+
+
+# ---------------------------------------------------------------------------------------------
+# frequencies and rotation
+# ---------------------------------------------------------------------------------------------
+
+def test_bands_sum_to_head_dim_and_closed_form_freqs():
+    assert sum(O.BANDS) == O.HEAD_DIM == 128       # "3A" section 4: 16 + 56 + 56 = 128
+    f, ax = O.inv_freq()
+    assert f.shape == (64,) and list(np.bincount(ax)) == [8, 28, 28]
+    # theta^(-2i/d): i = 0 -> 1; frame band i = 4 -> 10000^(-1/2) = 0.01; i = 1 -> 10^(-1/2)
+    assert f[0] == 1.0 and f[8] == 1.0 and f[36] == 1.0
+    assert abs(f[4] - 0.01) < 1e-17 and abs(f[1] - 10 ** -0.5) < 1e-16
+    assert abs(f[8 + 14] - 0.01) < 1e-17 and abs(f[36 + 14] - 0.01) < 1e-17
+    assert np.all(np.diff(f[:8]) < 0) and np.all(np.diff(f[8:36]) < 0)
+
+
+def test_rotation_equals_complex_multiplication_bruteforce():
+    rng = np.random.default_rng(1)
+    pos = np.array([[0, -2, 1], [3, 0, -5], [17, 17, 17]])
+    x = rng.standard_normal((3, 128))
+    c, s = O.rope_tables(pos)
+    got = O.rotate(x, c, s)
+    f, ax = O.inv_freq()
+    for r in range(3):
+        for kk in range(64):
+            z = complex(x[r, 2 * kk], x[r, 2 * kk + 1]) * cmath.exp(1j * pos[r, ax[kk]] * f[kk])
+            assert abs(got[r, 2 * kk] - z.real) < 1e-13 and abs(got[r, 2 * kk + 1] - z.imag) < 1e-13
+
+
+def test_rotation_is_isometry_and_identity_at_zero():
+    rng = np.random.default_rng(2)
+    pos = rng.integers(-40, 40, size=(50, 3))
+    x = rng.standard_normal((50, 3, 128))
+    c, s = O.rope_tables(pos)
+    y = O.rotate(x, c, s)
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-14)
+    c0, s0 = O.rope_tables(np.zeros((50, 3), dtype=np.int64))
+    assert np.array_equal(O.rotate(x, c0, s0), x)
+
+
+def test_scores_depend_only_on_position_differences():
+    # "3A" section 1: the product of two rotated vectors depends only on the angle difference.
+    rng = np.random.default_rng(3)
+    pos = rng.integers(-20, 20, size=(12, 3))
+    q = rng.standard_normal((12, 128))
+    k = rng.standard_normal((12, 128))
+
+    def scores(p):
+        c, s = O.rope_tables(p)
+        return O.rotate(q, c, s) @ O.rotate(k, c, s).T
+
+    base = scores(pos)
+    for shift in ([1, 0, 0], [0, -7, 3], [5, 5, 5], [100, -50, 13]):
+        assert np.max(np.abs(scores(pos + np.array(shift)) - base)) < 1e-12
+    # and it does depend on the differences
+    pos2 = pos.copy()
+    pos2[0, 1] += 1
+    assert np.max(np.abs(scores(pos2) - base)) > 1e-3
+
+
+def test_f32_tables_round_once():
+    pos = O.positions(TINY)
+    c32, s32 = O.rope_tables_f32(pos)
+    c64, s64 = O.rope_tables(pos)
+    assert c32.dtype == np.float32
+    # one rounding of the double value: within half an fp32 ulp of fp64 cos
+    ulp = np.spacing(np.abs(c32).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(c32.astype(np.float64) - c64) <= 0.5 * ulp + 1e-16)
+    ulp = np.spacing(np.abs(s32).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(s32.astype(np.float64) - s64) <= 0.5 * ulp + 1e-16)
+
+
+# ---------------------------------------------------------------------------------------------
+# norms
+# ---------------------------------------------------------------------------------------------
+
+def test_zero_center_rmsnorm_hand_example():
+    # "1B" sections 1-4: x * rrms * (w + 1); by hand for x = (3, 4), w = (0, 1), eps = 0:
+    # mean(x^2) = 12.5, rrms = 1/sqrt(12.5) -> (3/sqrt(12.5), 8/sqrt(12.5))
+    y = O.zero_center_rms_norm(np.array([3.0, 4.0]), np.array([0.0, 1.0]), eps=0.0)
+    assert abs(y[0] - 0.848528137423857) < 1e-15 and abs(y[1] - 2.262741699796952) < 1e-15
+
+
+def test_zero_center_rmsnorm_w0_is_plain_rmsnorm():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((7, 3072)) * 3
+    a = O.zero_center_rms_norm(x, np.zeros(3072))
+    b = x / np.sqrt(np.mean(x ** 2, axis=-1, keepdims=True) + 1e-6)
+    assert np.max(np.abs(a - b)) < 1e-13
+    assert np.allclose(np.sqrt(np.mean(O.rms_norm(x, None, 0.0) ** 2, axis=-1)), 1.0, rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------------------------
+# mask and block map
+# ---------------------------------------------------------------------------------------------
+
+def test_mask_hand_derived():
+    rows = _rows("tiny_mask.txt")
+    assert np.array_equal(O.mask_dense(MASK_TINY).astype(int), rows)
+
+
+def test_blockmap_hand_derived():
+    want = _rows("tiny_mask.txt", prefix="map")
+    assert np.array_equal(O.blockmap(O.mask_dense(MASK_TINY), 2, 2), want)
+
+
+def test_mask_visible_pair_count_closed_form():
+    # cfg1: text 256 causal, ref 1024 sees text + itself, target 1024 sees all 2304
+    wl = qin.WORKLOADS["cfg1"]
+    want = 256 * 257 // 2 + 1024 * (256 + 1024) + 1024 * 2304
+    assert O.visible_pairs(wl.segments) == want == 3702912
+
+
+def test_mask_prefix_never_sees_target_and_target_sees_all():
+    segs = (qin.text(7), qin.image(3, 2, 1), qin.image(2, 2, 2), qin.image(3, 3, 0))
+    m = O.mask_dense(segs)
+    S, P, T = O.split_counts(segs)
+    assert not m[:P, P:].any() and m[P:, :].all() and np.all(np.diag(m))
+
+
+def test_blockmap_classes_consistent_with_mask():
+    segs = qin.WORKLOADS["cfg0"].segments
+    m = O.mask_dense(segs)
+    for tq, tk in ((8, 8), (16, 4), (5, 7), (128, 64)):
+        bm = O.blockmap(m, tq, tk)
+        for i in range(bm.shape[0]):
+            for j in range(bm.shape[1]):
+                sub = m[i * tq:(i + 1) * tq, j * tk:(j + 1) * tk]
+                assert bm[i, j] == (1 if sub.all() else (2 if sub.any() else 0))
+
+
+# ---------------------------------------------------------------------------------------------
+# attention, cache, Euler
+# ---------------------------------------------------------------------------------------------
+
+def _bruteforce_attention(q, k, v, mask, scale):
+    """Pure-Python triple loop, straight from softmax's definition."""
+    Nq, H, d = q.shape
+    out = np.zeros((Nq, H, v.shape[2]))
+    for h in range(H):
+        for i in range(Nq):
+            s = []
+            for j in range(k.shape[0]):
+                if mask is None or mask[i, j]:
+                    s.append((j, sum(q[i, h, t] * k[j, h, t] for t in range(d)) * scale))
+            m = max(x for _, x in s)
+            w = [(j, math.exp(x - m)) for j, x in s]
+            z = sum(x for _, x in w)
+            for t in range(v.shape[2]):
+                out[i, h, t] = sum(x * v[j, h, t] for j, x in w) / z
+    return out
+
+
+def test_attention_matches_bruteforce_on_cfg0():
+    wl = qin.WORKLOADS["cfg0"]
+    q, k, v = (t.f64 for t in qin.qkv(wl, wl.S))
+    m = O.mask_dense(wl.segments)
+    got = O.attention(q, k, v, m, chunk=7)
+    ref = _bruteforce_attention(q, k, v, m, 1 / math.sqrt(128))
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_attention_unmasked_matches_logsumexp_form():
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(5)
+    q, k, v = rng.standard_normal((3, 40, 2, 16))
+    got = O.attention(q, k, v, None, scale=0.3)
+    for h in range(2):
+        s = q[:, h] @ k[:, h].T * 0.3
+        w = np.exp(s - logsumexp(s, axis=1, keepdims=True))
+        assert np.max(np.abs(w @ v[:, h] - got[:, h])) < 1e-13
+
+
+def test_step1_prefix_bit_identical_under_target_perturbation():
+    # the prefix never sees the target (course overview, learning goals), so prefix outputs are
+    # exactly unchanged when target Q/K/V change
+    wl = qin.WORKLOADS["cfg0"]
+    S, P, T = O.split_counts(wl.segments)
+    q, k, v = (t.f64.copy() for t in qin.qkv(wl, S))
+    c, s = O.rope_tables(O.positions(wl.segments))
+    o1, _ = O.step1(q, k, v, wl.segments, c, s)
+    rng = np.random.default_rng(6)
+    for t in (q, k, v):
+        t[P:] = rng.standard_normal(t[P:].shape) * 5
+    o2, _ = O.step1(q, k, v, wl.segments, c, s)
+    assert np.array_equal(o1[:P], o2[:P]) and not np.allclose(o1[P:], o2[P:])
+
+
+@pytest.mark.parametrize("name", ["cfg0", "mini"])
+def test_cached_step_equals_full_recompute(name):
+    # course overview: reusing the prefix cache matches recomputation to ~1e-16 (fp64)
+    if name == "cfg0":
+        wl = qin.WORKLOADS["cfg0"]
+    else:
+        wl = qin.small_workload("mini", (qin.text(9), qin.image(3, 5, 1), qin.image(2, 2, 2),
+                                         qin.image(4, 3, 0)), n_head=3, qk_rmsnorm=True)
+    S, P, T = O.split_counts(wl.segments)
+    q, k, v = (t.f64 for t in qin.qkv(wl, S))
+    qw, kw = qin.qk_norm_weights(wl) if wl.qk_rmsnorm else (None, None)
+    c, s = O.rope_tables(O.positions(wl.segments))
+    o_full, cache = O.step1(q, k, v, wl.segments, c, s, qw, kw)
+    o_t = O.cached_step(q[P:], k[P:], v[P:], cache, c[P:], s[P:], qw, kw)
+    assert np.max(np.abs(o_t - o_full[P:])) < 1e-13
+    # a later step with fresh target inputs equals a full step-1 run on [prefix | new target]
+    q2, k2, v2 = (t.f64 for t in qin.qkv(wl, S, step=1))
+    qn, kn, vn = (np.concatenate([a[:P], b[P:]]) for a, b in ((q, q2), (k, k2), (v, v2)))
+    o_new, _ = O.step1(qn, kn, vn, wl.segments, c, s, qw, kw)
+    o_t2 = O.cached_step(q2[P:], k2[P:], v2[P:], cache, c[P:], s[P:], qw, kw)
+    assert np.max(np.abs(o_t2 - o_new[P:])) < 1e-13
+
+
+def test_euler_constant_velocity_closed_form():
+    # sigma = linspace(1, 0, 9): eight steps of constant v move x by (0 - 1) v exactly
+    sig = qin.sigmas(8)
+    assert sig[0] == 1.0 and sig[-1] == 0.0 and len(sig) == 9
+    rng = np.random.default_rng(7)
+    x0 = rng.standard_normal((16, 64))
+    v = rng.standard_normal((16, 64))
+    x = x0
+    for kk in range(8):
+        x = O.euler(x, v, sig[kk], sig[kk + 1])
+    assert np.max(np.abs(x - (x0 - v))) < 1e-14
+    assert np.array_equal(O.euler(x0, v, 0.5, 0.5), x0)
+
+
+# ---------------------------------------------------------------------------------------------
+# planted mistakes: each wrong variant of an oracle step, swapped into the oracle module,
+# must make at least one of the pins above fail
+# ---------------------------------------------------------------------------------------------
+
+def _fails(test_fn, *args):
+    try:
+        test_fn(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+def _rotate_sign_flipped(x, c, s):
+    return _ORIG_ROTATE(x, c, -s)
+
+
+def _rotate_half_split(x, c, s):
+    x = np.asarray(x, dtype=np.float64)
+    extra = (slice(None),) + (None,) * (x.ndim - 2)
+    a, b = x[..., :64], x[..., 64:]
+    out = np.empty_like(x)
+    out[..., :64] = a * c[extra] - b * s[extra]
+    out[..., 64:] = a * s[extra] + b * c[extra]
+    return out
+
+
+def _positions_floor_centre(segments, text_pos0=None):
+    pos = _ORIG_POSITIONS(segments, text_pos0)
+    off = 0
+    for sg in segments:
+        if sg.kind == O.SEG_IMAGE:
+            H, W = sg.grid_h, sg.grid_w
+            pos[off:off + sg.n_tokens, 1] += (H - H // 2) - H // 2
+            pos[off:off + sg.n_tokens, 2] += (W - W // 2) - W // 2
+        off += sg.n_tokens
+    return pos
+
+
+def _positions_text_from_zero(segments, text_pos0=None):
+    return _ORIG_POSITIONS(segments, 0 if text_pos0 is None else text_pos0)
+
+
+def _mask_strict_text(segments):
+    m = _ORIG_MASK(segments)
+    n0 = segments[0].n_tokens
+    idx = np.arange(n0)
+    m[idx, idx] = False
+    return m
+
+
+def _mask_refs_see_target(segments):
+    m = _ORIG_MASK(segments)
+    S, P, T = O.split_counts(segments)
+    m[n_text(segments):P, P:] = True
+    return m
+
+
+def n_text(segments):
+    return segments[0].n_tokens
+
+
+def _inv_freq_headdim(bands=O.BANDS, theta=O.THETA):
+    f, ax = _ORIG_INVFREQ(bands, theta)
+    out = f.copy()
+    off = 0
+    for d in bands:
+        for i in range(d // 2):
+            out[off + i] = 1.0 / math.pow(theta, (2 * i) / 128)
+        off += d // 2
+    return out, ax
+
+
+def _zc_no_plus_one(x, w, eps=1e-6):
+    return O.rms_norm(x, np.asarray(w, dtype=np.float64), eps)
+
+
+def _attention_no_max_shift_wrong_scale(q, k, v, mask=None, scale=None, chunk=512):
+    return _ORIG_ATTENTION(q, k, v, mask, 1.0 / q.shape[-1] if scale is None else scale, chunk)
+
+
+def _cached_step_unrotated_target(q_t, k_t, v_t, cache, cos_t, sin_t, q_w=None, k_w=None, eps=1e-6,
+                                  scale=None):
+    return _ORIG_CACHED(q_t, k_t, v_t, cache, cos_t, sin_t * 0.0, q_w, k_w, eps, scale)
+
+
+def _euler_sign(x, v, a, b):
+    return np.asarray(x, dtype=np.float64) + (a - b) * np.asarray(v, dtype=np.float64)
+
+
+_ORIG_ROTATE = O.rotate
+_ORIG_POSITIONS = O.positions
+_ORIG_MASK = O.mask_dense
+_ORIG_INVFREQ = O.inv_freq
+_ORIG_ATTENTION = O.attention
+_ORIG_CACHED = O.cached_step
+
+PLANTED = [
+    ("rotate", _rotate_sign_flipped, [test_rotation_equals_complex_multiplication_bruteforce]),
+    ("rotate", _rotate_half_split, [test_rotation_equals_complex_multiplication_bruteforce]),
+    ("positions", _positions_floor_centre, [test_text_steps_all_axes_and_start]),
+    ("positions", _positions_text_from_zero, [test_tiny_positions_hand_derived]),
+    ("mask_dense", _mask_strict_text, [test_mask_hand_derived]),
+    ("mask_dense", _mask_refs_see_target, [test_mask_hand_derived, test_mask_prefix_never_sees_target_and_target_sees_all]),
+    ("inv_freq", _inv_freq_headdim, [test_bands_sum_to_head_dim_and_closed_form_freqs]),
+    ("zero_center_rms_norm", _zc_no_plus_one, [test_zero_center_rmsnorm_hand_example]),
+    ("attention", _attention_no_max_shift_wrong_scale, [test_attention_matches_bruteforce_on_cfg0]),
+    ("cached_step", _cached_step_unrotated_target, [lambda: test_cached_step_equals_full_recompute("cfg0")]),
+    ("euler", _euler_sign, [test_euler_constant_velocity_closed_form]),
+]
+
+
+@pytest.mark.parametrize("i", range(len(PLANTED)))
+def test_planted_mistake_is_caught(i, monkeypatch):
+    name, bad, pins = PLANTED[i]
+    # the pins pass on the real oracle ...
+    for pin in pins:
+        assert not _fails(pin), f"pin {pin} fails on the unmodified oracle"
+    # ... and at least one fails once the mistake is planted
+    monkeypatch.setattr(O, name, bad)
+    assert any(_fails(pin) for pin in pins), f"planted mistake in {name} not caught"
