@@ -1,0 +1,223 @@
+"""Benchmark: target-only cached attention step of the Qwen-Image-2.1 DiT hot path on one MI355X.
+
+Workload (default): 24 heads x 128, bf16 I/O; text 1,024 + 4 reference images 64x64 (frames 1..4)
++ target 64x64 (frame 0): 17,408 cached prefix tokens, 4,096 target queries over 21,504 keys.
+One step = the target-only cached attention for each of 32 layers (each layer reads its own
+prefix cache, so the 6.85 GB of caches cannot sit in the 256 MB Infinity Cache) followed by
+one Euler update of the 4096 x 64 fp32 latent.  Inputs are synthetic (torch RNG, seeded) and
+resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg3|cfg3_t512|cfg2] [--no-cpu]
+
+Prints one JSON line.  value = attention TFLOP/s over the timed steps (visible-pair flops,
+4*d per pair); roofline = the attention kernel's own average launch time from HIP events
+recorded around each launch on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA, published
+METRIC = "attention TFLOP/s + % bf16 MFMA peak, target-only cached step, 4096 tgt tokens"
+N_LAYERS = 32
+PROFILE = os.path.join(ROOT, "profiles", "attn_f16_cfg3_target_counters.md")
+KERNEL_SRC = os.path.join(ROOT, "image_generation_qi_amd", "csrc", "qi_attn_f16.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per launch from the committed counter summary, if it was taken on this exact
+    kernel source (else None)."""
+    if not os.path.exists(PROFILE):
+        return None
+    txt = open(PROFILE).read()
+    m_h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_h or not m_b or m_h.group(1) != kernel_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def visible_pairs_per_head(segments) -> int:
+    """Visible (query, key) pairs of step 1: query q sees keys 0..lim(q) (Block-Causal rows)."""
+    total, start = 0, 0
+    for s in segments:
+        end = start + s.n_tokens
+        if s.kind == 0:   # causal text: q sees 0..q
+            total += sum(q + 1 for q in range(start, end))
+        else:             # image / bidirectional text block: sees everything before its end
+            total += s.n_tokens * end
+        start = end
+    return total
+
+
+def cpu_baseline(wl, budget_s: float = 12.0):
+    """The fp64 oracle's cached target step, one head at a time on the host, until the budget is
+    used (at least one head)."""
+    import numpy as np
+
+    import qi_inputs as qin
+    from oracle import qi_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    S, P, T = wl.S, wl.P, wl.T
+    cos, sin = O.rope_tables(O.positions(wl.segments))
+    done, elapsed = 0, 0.0
+    while done < wl.n_head and (done == 0 or elapsed < budget_s):
+        rng = np.random.default_rng([wl.cfg_id, 900, done])
+        k = rng.standard_normal((S, 1, 128))
+        v = rng.standard_normal((S, 1, 128))
+        q = rng.standard_normal((T, 1, 128))
+        cache = (O.rotate(k[:P], cos[:P], sin[:P]), v[:P])
+        t0 = time.perf_counter()
+        O.cached_step(q, k[P:], v[P:], cache, cos[P:], sin[P:])
+        elapsed += time.perf_counter() - t0
+        done += 1
+    flops = 4.0 * 128 * T * S * done
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {wl.n_head} heads of one layer's cached target step "
+                      f"({T} queries x {S} keys, fp64 NumPy), {elapsed:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="cfg3", choices=["cfg3", "cfg3_t512", "cfg2"])
+    ap.add_argument("--layers", type=int, default=N_LAYERS)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--step1", action="store_true", help="also time one full step-1 attention per layer")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import qi_inputs as qin
+    from image_generation_qi_amd import qi as Q
+    from image_generation_qi_amd import runtime as rt
+
+    Q.lib()
+    dev = "cuda:0"
+    wl = qin.WORKLOADS[args.workload]
+    S, P, T, H = wl.S, wl.P, wl.T, wl.n_head
+    NL = args.layers
+    log(f"workload {wl.name}: S={S} P={P} T={T} H={H} layers={NL}")
+    L = rt.Layout(wl.segments, dev)
+    att = rt.Attention(L, H, Q.QI_BF16, dev)
+    cache = rt.KVCache(NL, H, P, Q.QI_BF16, dev)
+    g = torch.Generator(device=dev).manual_seed(1234)
+
+    # fill every layer's prefix cache (prepared K, V) from synthetic prefix K/V
+    for layer in range(NL):
+        kv = torch.randn((P, 2, H, 128), generator=g, device=dev).to(torch.bfloat16)
+        att.store(kv[:, 0], kv[:, 1], cache, layer)
+        del kv
+    # per-layer target Q/K/V (fused [T, 3, H, 128] buffers), output, latent and velocity
+    qkv = [torch.randn((T, 3, H, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(NL)]
+    out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    x = torch.randn((T, wl.latent_ch), generator=g, device=dev)
+    vel = torch.randn((T, wl.latent_ch), generator=g, device=dev).to(torch.bfloat16)
+    sig = qin.sigmas(8)
+    torch.cuda.synchronize()
+    log("caches filled")
+
+    def one_step(k):
+        for layer in range(NL):
+            t = qkv[layer]
+            att.cached(t[:, 0], t[:, 1], t[:, 2], cache, layer, out=out)
+        i = 1 + (k % 7)
+        rt.euler_step(x, vel, float(sig[i]), float(sig[i + 1]))
+
+    for k in range(args.warmup):
+        one_step(k)
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    Q.qi_kernel_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        one_step(k)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms, n_launch = Q.qi_kernel_timing_read()
+    Q.qi_kernel_timing(False)
+    log(f"timed {args.steps} steps in {wall:.3f} s; attention kernel {kern_ms / max(n_launch, 1):.4f} ms/launch")
+
+    flops_launch = 4.0 * 128 * H * T * (P + T)
+    value = flops_launch * NL * args.steps / wall / 1e12
+    avg_ms = kern_ms / max(n_launch, 1)
+    achieved = flops_launch / (avg_ms * 1e-3) / 1e12
+    extra = {}
+    if args.step1:
+        o1 = torch.empty((S, H, 128), dtype=torch.bfloat16, device=dev)
+        qkv1 = torch.randn((S, 3, H, 128), generator=g, device=dev).to(torch.bfloat16)
+        att.full(qkv1[:, 0], qkv1[:, 1], qkv1[:, 2], cache=cache, layer=0, out=o1)
+        torch.cuda.synchronize()
+        Q.qi_kernel_timing(True)
+        for _ in range(3):
+            att.full(qkv1[:, 0], qkv1[:, 1], qkv1[:, 2], cache=cache, layer=0, out=o1)
+        torch.cuda.synchronize()
+        ms1, n1 = Q.qi_kernel_timing_read()
+        Q.qi_kernel_timing(False)
+        f1 = 4.0 * 128 * H * visible_pairs_per_head(wl.segments)
+        extra["step1_attention_kernel_ms"] = round(ms1 / n1, 4)
+        extra["step1_attention_tflops"] = round(f1 / (ms1 / n1 * 1e-3) / 1e12, 1)
+        del qkv1, o1
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: target-only cached attention step, {H}x128 heads, text "
+                               f"{wl.segments[0].n_tokens} + {len(wl.segments) - 2} refs + target "
+                               f"{wl.segments[-1].grid_h}x{wl.segments[-1].grid_w}; {T} queries over {P + T} keys "
+                               f"({P} cached); {NL} layers + Euler per step",
+                   "io_dtype": "bf16", "cache_dtype": "f16", "mfma": "v_mfma_f32_32x32x16_f16",
+                   "layers_per_step": NL, "target_tokens": T, "prefix_tokens": P, "heads": H,
+                   "pct_of_peak": round(100.0 * value / PEAK_F16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic_from_profile(),
+                     "kernel": "k_attn_f16<false>", "kernel_ms_per_launch": round(avg_ms, 4),
+                     "flops_per_launch": flops_launch, "launches": n_launch},
+    }
+    res["config"].update(extra)
+    if not args.no_cpu:
+        log("cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

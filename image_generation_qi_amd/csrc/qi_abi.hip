@@ -1,0 +1,322 @@
+// qi_abi.hip - device entry points of the C ABI: argument checks, then kernel launches.
+//
+// Every check runs before the first launch, so a negative status means nothing was enqueued.
+// The library holds no device memory: caches and workspaces are caller buffers.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <mutex>
+#include <vector>
+
+#include "qi_launch.h"
+
+using namespace qi;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(qi_dtype t) { return t == QI_F32 ? 4 : (t == QI_BF16 || t == QI_F16) ? 2 : 0; }
+
+int check_tensor(const void* p, qi_dtype dtype, int64_t n_tok, int32_t n_head, int64_t tok_stride) {
+  if (!p) return QI_ERR_ARG;
+  if (dtype != QI_BF16 && dtype != QI_F32) return QI_ERR_DTYPE;
+  if (n_tok < 1 || n_head < 1 || n_tok > INT32_MAX) return QI_ERR_SHAPE;
+  if (tok_stride < (int64_t)n_head * QI_HEAD_DIM) return QI_ERR_SHAPE;
+  if (!aligned16(p) || (tok_stride % 8) != 0) return QI_ERR_ALIGN;
+  return QI_OK;
+}
+
+int check_prep(const qi_qkprep* prep) {
+  if (!prep) return QI_OK;
+  if ((prep->cos_t == nullptr) != (prep->sin_t == nullptr)) return QI_ERR_ARG;
+  if (!aligned16(prep->cos_t) || !aligned16(prep->sin_t) || !aligned16(prep->q_rms_w) ||
+      !aligned16(prep->k_rms_w))
+    return QI_ERR_ALIGN;
+  if ((prep->q_rms_w || prep->k_rms_w) && !(prep->eps >= 0.f && std::isfinite(prep->eps))) return QI_ERR_ARG;
+  return QI_OK;
+}
+
+int check_cache(const qi_kvcache* c, qi_dtype io_dtype, int32_t n_head, int32_t layer, int64_t P) {
+  if (!c || !c->k || !c->v) return QI_ERR_ARG;
+  const qi_dtype want = io_dtype == QI_BF16 ? QI_F16 : QI_F32;
+  if (c->dtype != want) return QI_ERR_DTYPE;
+  if (c->n_head != n_head || c->n_layers < 1 || c->p_cap < 0) return QI_ERR_SHAPE;
+  if (layer < 0 || layer >= c->n_layers || P < 0 || P > c->p_cap) return QI_ERR_CAPACITY;
+  if (!aligned16(c->k) || !aligned16(c->v)) return QI_ERR_ALIGN;
+  return QI_OK;
+}
+
+float softmax_scale(float scale) { return scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)QI_HEAD_DIM)); }
+
+// pointer to row 0 of a cache layer
+const void* cache_layer(const void* base, const qi_kvcache* c, int32_t layer) {
+  const int64_t off = (int64_t)layer * c->n_head * c->p_cap * QI_HEAD_DIM * elem_size(c->dtype);
+  return (const char*)base + off;
+}
+
+// ---- kernel timing ----------------------------------------------------------------------
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<hipEvent_t> g_ev;  // start/stop pairs
+size_t g_used = 0;
+
+struct TimedLaunch {
+  hipStream_t s;
+  hipEvent_t stop = nullptr;
+  explicit TimedLaunch(hipStream_t st) : s(st) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (!g_timing) return;
+    if (2 * g_used + 2 > g_ev.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess) return;
+      if (hipEventCreate(&b) != hipSuccess) {
+        (void)hipEventDestroy(a);
+        return;
+      }
+      g_ev.push_back(a);
+      g_ev.push_back(b);
+    }
+    (void)hipEventRecord(g_ev[2 * g_used], s);
+    stop = g_ev[2 * g_used + 1];
+    ++g_used;
+  }
+  ~TimedLaunch() {
+    if (stop) (void)hipEventRecord(stop, s);
+  }
+};
+
+int launch_status(hipError_t e) { return e == hipSuccess ? QI_OK : QI_ERR_HIP; }
+
+// Prepare rows [0, n) of k (norm + rotation) and copy v into a [head][row][128] destination.
+int prep_kv(const void* k, const void* v, qi_dtype dtype, int64_t n, int32_t n_head, int64_t tok_stride,
+            const qi_qkprep* prep, void* dk, void* dv, int64_t head_stride, hipStream_t s) {
+  if (n <= 0) return QI_OK;
+  PrepArgs pa{};
+  pa.x = k;
+  pa.x_tok_stride = tok_stride;
+  pa.dst = dk;
+  pa.dst_tok_stride = QI_HEAD_DIM;
+  pa.dst_head_stride = head_stride;
+  pa.v = v;
+  pa.dst_v = dv;
+  pa.n_tok = n;
+  pa.n_head = n_head;
+  pa.cos_t = prep ? prep->cos_t : nullptr;
+  pa.sin_t = prep ? prep->sin_t : nullptr;
+  pa.rms_w = prep ? prep->k_rms_w : nullptr;
+  pa.eps = prep ? prep->eps : 0.f;
+  return launch_status(dtype == QI_BF16 ? launch_prep_bf16_to_f16(pa, s) : launch_prep_f32(pa, s));
+}
+
+AttnArgs attn_args(const qi_qkv* io, const qi_qkprep* prep, float scale) {
+  AttnArgs a{};
+  a.q = io->q;
+  a.q_stride = io->tok_stride;
+  a.cos_q = prep ? prep->cos_t : nullptr;
+  a.sin_q = prep ? prep->sin_t : nullptr;
+  a.q_rms_w = prep ? prep->q_rms_w : nullptr;
+  a.eps = prep ? prep->eps : 0.f;
+  a.o = io->o;
+  a.o_stride = (int64_t)io->n_head * QI_HEAD_DIM;
+  a.n_q = (int32_t)io->n_tok;
+  a.n_head = io->n_head;
+  const double sc = softmax_scale(scale);
+  a.scale_log2 = io->dtype == QI_BF16 ? (float)(sc * 1.4426950408889634) : (float)sc;
+  return a;
+}
+
+int run_attn(const AttnArgs& a, qi_dtype dtype, hipStream_t s) {
+  TimedLaunch t(s);
+  return launch_status(dtype == QI_BF16 ? launch_attn_f16(a, s) : launch_attn_f32(a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int qi_rope3d_apply(void* x, qi_dtype dtype, int64_t n_tok, int32_t n_head, int64_t tok_stride,
+                    const float* cos_t, const float* sin_t, const float* rms_w, float eps, void* stream) {
+  int st = check_tensor(x, dtype, n_tok, n_head, tok_stride);
+  if (st != QI_OK) return st;
+  if ((cos_t == nullptr) != (sin_t == nullptr)) return QI_ERR_ARG;
+  if (!cos_t && !rms_w) return QI_ERR_ARG;
+  if (!aligned16(cos_t) || !aligned16(sin_t) || !aligned16(rms_w)) return QI_ERR_ALIGN;
+  if (rms_w && !(eps >= 0.f && std::isfinite(eps))) return QI_ERR_ARG;
+  PrepArgs pa{};
+  pa.x = x;
+  pa.x_tok_stride = tok_stride;
+  pa.dst = x;
+  pa.dst_tok_stride = tok_stride;
+  pa.dst_head_stride = QI_HEAD_DIM;
+  pa.n_tok = n_tok;
+  pa.n_head = n_head;
+  pa.cos_t = cos_t;
+  pa.sin_t = sin_t;
+  pa.rms_w = rms_w;
+  pa.eps = eps;
+  hipStream_t s = (hipStream_t)stream;
+  return launch_status(dtype == QI_BF16 ? launch_prep_bf16_to_bf16(pa, s) : launch_prep_f32(pa, s));
+}
+
+int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_layout* layout, float scale,
+                             const qi_kvcache* cache, int32_t layer, void* workspace, int64_t workspace_bytes,
+                             void* stream) {
+  if (!io) return QI_ERR_ARG;
+  LayoutInfo li;
+  int st = analyse_layout(layout, &li);
+  if (st != QI_OK) return st;
+  if ((st = check_tensor(io->q, io->dtype, io->n_tok, io->n_head, io->tok_stride)) != QI_OK) return st;
+  if ((st = check_tensor(io->k, io->dtype, io->n_tok, io->n_head, io->tok_stride)) != QI_OK) return st;
+  if ((st = check_tensor(io->v, io->dtype, io->n_tok, io->n_head, io->tok_stride)) != QI_OK) return st;
+  if (!io->o) return QI_ERR_ARG;
+  if (!aligned16(io->o)) return QI_ERR_ALIGN;
+  if (io->n_tok != li.S) return QI_ERR_SHAPE;
+  if ((st = check_prep(prep)) != QI_OK) return st;
+  if (cache && (st = check_cache(cache, io->dtype, io->n_head, layer, li.P)) != QI_OK) return st;
+  if (!workspace) return QI_ERR_ARG;
+  if (!aligned16(workspace)) return QI_ERR_ALIGN;
+  if (workspace_bytes < qi_attn_full_workspace_bytes(io->dtype, li.S, io->n_head)) return QI_ERR_CAPACITY;
+
+  hipStream_t s = (hipStream_t)stream;
+  const int es = elem_size(io->dtype == QI_BF16 ? QI_F16 : QI_F32);
+  const int64_t rows_ws = cache ? li.T : li.S;  // workspace rows: target only when the prefix goes to the cache
+  char* wk = (char*)workspace;
+  char* wv = wk + (int64_t)io->n_head * rows_ws * QI_HEAD_DIM * es;
+  AttnArgs a = attn_args(io, prep, scale);
+  a.masked = 1;
+  a.segs = li.tab;
+  a.q_row0 = 0;
+  if (cache) {
+    void* ck = (void*)cache_layer(cache->k, cache, layer);
+    void* cv = (void*)cache_layer(cache->v, cache, layer);
+    const int64_t chs = cache->p_cap * QI_HEAD_DIM;
+    if ((st = prep_kv(io->k, io->v, io->dtype, li.P, io->n_head, io->tok_stride, prep, ck, cv, chs, s)) != QI_OK)
+      return st;
+    const int64_t off = li.P * io->tok_stride * (io->dtype == QI_BF16 ? 2 : 4);
+    qi_qkprep tprep{};
+    if (prep) {  // table rows of the target tokens
+      tprep = *prep;
+      if (prep->cos_t) {
+        tprep.cos_t = prep->cos_t + li.P * (QI_HEAD_DIM / 2);
+        tprep.sin_t = prep->sin_t + li.P * (QI_HEAD_DIM / 2);
+      }
+    }
+    if ((st = prep_kv((const char*)io->k + off, (const char*)io->v + off, io->dtype, li.T, io->n_head,
+                      io->tok_stride, prep ? &tprep : nullptr, wk, wv, li.T * QI_HEAD_DIM, s)) != QI_OK)
+      return st;
+    a.kA = ck;
+    a.vA = cv;
+    a.a_head_stride = chs;
+    a.nA = li.P;
+    a.kB = wk;
+    a.vB = wv;
+    a.b_head_stride = li.T * QI_HEAD_DIM;
+    a.nB = li.T;
+  } else {
+    if ((st = prep_kv(io->k, io->v, io->dtype, li.S, io->n_head, io->tok_stride, prep, wk, wv,
+                      li.S * QI_HEAD_DIM, s)) != QI_OK)
+      return st;
+    a.kA = wk;
+    a.vA = wv;
+    a.a_head_stride = li.S * QI_HEAD_DIM;
+    a.nA = li.S;
+    a.kB = wk;
+    a.vB = wv;
+    a.b_head_stride = 0;
+    a.nB = 0;
+  }
+  return run_attn(a, io->dtype, s);
+}
+
+int qi_attn_prefix_store(const void* k, const void* v, qi_dtype dtype, int64_t P, int32_t n_head, int64_t tok_stride,
+                         const qi_qkprep* prep, const qi_kvcache* cache, int32_t layer, void* stream) {
+  int st;
+  if (P < 0) return QI_ERR_SHAPE;
+  if (P == 0) {
+    if (dtype != QI_BF16 && dtype != QI_F32) return QI_ERR_DTYPE;
+    return check_cache(cache, dtype, n_head, layer, 0);
+  }
+  if ((st = check_tensor(k, dtype, P, n_head, tok_stride)) != QI_OK) return st;
+  if ((st = check_tensor(v, dtype, P, n_head, tok_stride)) != QI_OK) return st;
+  if ((st = check_prep(prep)) != QI_OK) return st;
+  if ((st = check_cache(cache, dtype, n_head, layer, P)) != QI_OK) return st;
+  void* ck = (void*)cache_layer(cache->k, cache, layer);
+  void* cv = (void*)cache_layer(cache->v, cache, layer);
+  return prep_kv(k, v, dtype, P, n_head, tok_stride, prep, ck, cv, cache->p_cap * QI_HEAD_DIM,
+                 (hipStream_t)stream);
+}
+
+int qi_attn_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvcache* cache, int32_t layer,
+                          int64_t P, float scale, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!io) return QI_ERR_ARG;
+  int st;
+  if ((st = check_tensor(io->q, io->dtype, io->n_tok, io->n_head, io->tok_stride)) != QI_OK) return st;
+  if ((st = check_tensor(io->k, io->dtype, io->n_tok, io->n_head, io->tok_stride)) != QI_OK) return st;
+  if ((st = check_tensor(io->v, io->dtype, io->n_tok, io->n_head, io->tok_stride)) != QI_OK) return st;
+  if (!io->o) return QI_ERR_ARG;
+  if (!aligned16(io->o)) return QI_ERR_ALIGN;
+  if ((st = check_prep(prep)) != QI_OK) return st;
+  if ((st = check_cache(cache, io->dtype, io->n_head, layer, P)) != QI_OK) return st;
+  if (P + io->n_tok > INT32_MAX) return QI_ERR_SHAPE;
+  if (!workspace) return QI_ERR_ARG;
+  if (!aligned16(workspace)) return QI_ERR_ALIGN;
+  if (workspace_bytes < qi_attn_cached_workspace_bytes(io->dtype, io->n_tok, io->n_head)) return QI_ERR_CAPACITY;
+
+  hipStream_t s = (hipStream_t)stream;
+  const int es = elem_size(cache->dtype);
+  const int64_t T = io->n_tok;
+  char* wk = (char*)workspace;
+  char* wv = wk + (int64_t)io->n_head * T * QI_HEAD_DIM * es;
+  if ((st = prep_kv(io->k, io->v, io->dtype, T, io->n_head, io->tok_stride, prep, wk, wv, T * QI_HEAD_DIM, s)) !=
+      QI_OK)
+    return st;
+  AttnArgs a = attn_args(io, prep, scale);
+  a.masked = 0;
+  a.kA = cache_layer(cache->k, cache, layer);
+  a.vA = cache_layer(cache->v, cache, layer);
+  a.a_head_stride = cache->p_cap * QI_HEAD_DIM;
+  a.nA = P;
+  a.kB = wk;
+  a.vB = wv;
+  a.b_head_stride = T * QI_HEAD_DIM;
+  a.nB = T;
+  a.q_row0 = P;
+  return run_attn(a, io->dtype, s);
+}
+
+int qi_euler_step(float* x, const void* v, qi_dtype v_dtype, int64_t n, float sigma_k, float sigma_k1,
+                  void* stream) {
+  if (!x || !v) return QI_ERR_ARG;
+  if (n < 0) return QI_ERR_SHAPE;
+  if (v_dtype != QI_F32 && v_dtype != QI_BF16) return QI_ERR_DTYPE;
+  if (!std::isfinite(sigma_k) || !std::isfinite(sigma_k1)) return QI_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(x) & 3) || (reinterpret_cast<uintptr_t>(v) & (v_dtype == QI_F32 ? 3 : 1)))
+    return QI_ERR_ALIGN;
+  if (n == 0) return QI_OK;
+  return launch_status(launch_euler(x, v, v_dtype == QI_BF16, n, sigma_k1 - sigma_k, (hipStream_t)stream));
+}
+
+int qi_kernel_timing(int enable) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = enable != 0;
+  g_used = 0;
+  return QI_OK;
+}
+
+int qi_kernel_timing_read(double* total_ms, int64_t* n_launches) {
+  if (!total_ms || !n_launches) return QI_ERR_ARG;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  double tot = 0.0;
+  for (size_t i = 0; i < g_used; ++i) {
+    if (hipEventSynchronize(g_ev[2 * i + 1]) != hipSuccess) return QI_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_ev[2 * i], g_ev[2 * i + 1]) != hipSuccess) return QI_ERR_HIP;
+    tot += ms;
+  }
+  *total_ms = tot;
+  *n_launches = (int64_t)g_used;
+  return QI_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,273 @@
+// qi_kernels.hip - memory-bound kernels of the path: per-token QK preparation (per-head RMSNorm
+// and 3D rotation, "3A - 3D Axial RoPE (16, 56, 56)" section 1; norm-then-rotate order of the
+// joint attention processor in "QwenImageTransformer2DModel source reading", section 6), the
+// Euler update ("Qwen-Image-2.1" course overview, card 6B), and the fp32 attention used for
+// fp32 I/O.  The bf16 attention hot loop lives in qi_attn_f16.hip.
+#include <hip/hip_runtime.h>
+
+#include "qi_launch.h"
+
+namespace qi {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet)
+__device__ __forceinline__ uint32_t to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  _Float16 ha = (_Float16)a, hb = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+// ---------------------------------------------------------------------------------------------
+// QK preparation: 16 threads per (token, head) row, 8 consecutive elements per thread, so one
+// row is one coalesced 256-byte (bf16) or 512-byte (fp32) segment.
+// ---------------------------------------------------------------------------------------------
+enum { IN_BF16 = 0, IN_F32 = 1 };
+enum { OUT_BF16 = 0, OUT_F16 = 1, OUT_F32 = 2 };
+
+template <int IN, int OUT>
+__device__ __forceinline__ void load8(const void* base, int64_t off, float x[8]) {
+  if (IN == IN_BF16) {
+    const u32x4 w = *(const u32x4*)((const uint16_t*)base + off);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = bf16_lo(w[j]);
+      x[2 * j + 1] = bf16_hi(w[j]);
+    }
+  } else {
+    const f32x4* p = (const f32x4*)((const float*)base + off);
+    const f32x4 a = p[0], b = p[1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = a[j];
+      x[4 + j] = b[j];
+    }
+  }
+}
+
+template <int OUT>
+__device__ __forceinline__ void store8(void* base, int64_t off, const float x[8]) {
+  if (OUT == OUT_F32) {
+    f32x4* p = (f32x4*)((float*)base + off);
+    p[0] = f32x4{x[0], x[1], x[2], x[3]};
+    p[1] = f32x4{x[4], x[5], x[6], x[7]};
+  } else if (OUT == OUT_F16) {
+    *(u32x4*)((uint16_t*)base + off) =
+        u32x4{pack_f16(x[0], x[1]), pack_f16(x[2], x[3]), pack_f16(x[4], x[5]), pack_f16(x[6], x[7])};
+  } else {
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = to_bf16(x[2 * j]) | (to_bf16(x[2 * j + 1]) << 16);
+    *(u32x4*)((uint16_t*)base + off) = w;
+  }
+}
+
+template <int IN, int OUT>
+__global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid >> 4;
+  const int c = threadIdx.x & 15;
+  const bool ok = row < a.n_tok * (int64_t)a.n_head;
+  const int64_t t = ok ? row / a.n_head : 0;
+  const int h = ok ? (int)(row % a.n_head) : 0;
+  const int64_t src = t * a.x_tok_stride + (int64_t)h * 128 + 8 * c;
+  const int64_t dst = t * a.dst_tok_stride + (int64_t)h * a.dst_head_stride + 8 * c;
+  float x[8];
+  if (ok) {
+    load8<IN, OUT>(a.x, src, x);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = 0.f;
+  }
+  if (a.rms_w) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    ss += __shfl_xor(ss, 4);
+    ss += __shfl_xor(ss, 8);
+    const float r = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = x[j] * r * a.rms_w[8 * c + j];
+  }
+  if (a.cos_t && ok) {
+    const f32x4 cs = *(const f32x4*)(a.cos_t + t * 64 + 4 * c);
+    const f32x4 sn = *(const f32x4*)(a.sin_t + t * 64 + 4 * c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x0 = x[2 * j], x1 = x[2 * j + 1];
+      x[2 * j] = x0 * cs[j] - x1 * sn[j];
+      x[2 * j + 1] = x0 * sn[j] + x1 * cs[j];
+    }
+  }
+  if (!ok) return;
+  store8<OUT>(a.dst, dst, x);
+  if (a.v) {
+    float y[8];
+    load8<IN, OUT>(a.v, src, y);
+    store8<OUT>(a.dst_v, dst, y);
+  }
+}
+
+template <int IN, int OUT>
+hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
+  const int64_t threads = a.n_tok * (int64_t)a.n_head * 16;
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_prep<IN, OUT>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Euler update x += dt * v, four elements per thread.
+// ---------------------------------------------------------------------------------------------
+template <bool VBF16>
+__global__ __launch_bounds__(256) void k_euler(float* __restrict__ x, const void* __restrict__ v,
+                                                int64_t n, float dt) {
+  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i0 >= n) return;
+  if (i0 + 4 <= n && ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(v)) & 15) == 0) {
+    f32x4 xv = *(f32x4*)(x + i0);
+    float vv[4];
+    if (VBF16) {
+      const uint32_t* p = (const uint32_t*)((const uint16_t*)v + i0);
+      const uint32_t w0 = p[0], w1 = p[1];
+      vv[0] = bf16_lo(w0); vv[1] = bf16_hi(w0); vv[2] = bf16_lo(w1); vv[3] = bf16_hi(w1);
+    } else {
+      const f32x4 t = *(const f32x4*)((const float*)v + i0);
+      vv[0] = t[0]; vv[1] = t[1]; vv[2] = t[2]; vv[3] = t[3];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xv[j] = __builtin_fmaf(dt, vv[j], xv[j]);
+    *(f32x4*)(x + i0) = xv;
+  } else {
+    for (int64_t i = i0; i < n && i < i0 + 4; ++i) {
+      const float vi = VBF16 ? __uint_as_float((uint32_t)((const uint16_t*)v)[i] << 16) : ((const float*)v)[i];
+      x[i] = __builtin_fmaf(dt, vi, x[i]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// fp32 attention: one wavefront per (query, head).  Lanes take 64 keys at a time for the
+// scores, then 2 output dims each for the weighted sum.  Masked rows stop at their last visible
+// key (every key up to the row limit is visible, see qi_common.h).
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+__global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
+  __shared__ float qs[128];
+  __shared__ float ps[64];
+  const int64_t wid = blockIdx.x;
+  const int h = (int)(wid % a.n_head);
+  const int64_t qi = wid / a.n_head;
+  const int lane = threadIdx.x;
+  const float* qrow = (const float*)a.q + qi * a.q_stride + (int64_t)h * 128;
+  float x0 = qrow[2 * lane], x1 = qrow[2 * lane + 1];
+  if (a.q_rms_w) {
+    const float ss = wave_sum(x0 * x0 + x1 * x1);
+    const float r = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
+    x0 = x0 * r * a.q_rms_w[2 * lane];
+    x1 = x1 * r * a.q_rms_w[2 * lane + 1];
+  }
+  if (a.cos_q) {
+    const float c = a.cos_q[qi * 64 + lane], s = a.sin_q[qi * 64 + lane];
+    const float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
+    x0 = y0;
+    x1 = y1;
+  }
+  qs[2 * lane] = x0 * a.scale_log2;
+  qs[2 * lane + 1] = x1 * a.scale_log2;
+  __syncthreads();
+  const int64_t nkeys = a.nA + a.nB;
+  int64_t lim = a.masked ? row_limit(a.segs, a.q_row0 + qi) : nkeys - 1;
+  if (lim > nkeys - 1) lim = nkeys - 1;
+  const float* kA = (const float*)a.kA + (int64_t)h * a.a_head_stride;
+  const float* vA = (const float*)a.vA + (int64_t)h * a.a_head_stride;
+  const float* kB = (const float*)a.kB + (int64_t)h * a.b_head_stride;
+  const float* vB = (const float*)a.vB + (int64_t)h * a.b_head_stride;
+  float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int64_t k0 = 0; k0 <= lim; k0 += 64) {
+    const int64_t j = k0 + lane;
+    float s = -INFINITY;
+    if (j <= lim) {
+      const float* kr = j < a.nA ? kA + j * 128 : kB + (j - a.nA) * 128;
+      float acc = 0.f;
+      for (int d = 0; d < 128; d += 4) {
+        const f32x4 kv = *(const f32x4*)(kr + d);
+        acc = __builtin_fmaf(qs[d], kv[0], acc);
+        acc = __builtin_fmaf(qs[d + 1], kv[1], acc);
+        acc = __builtin_fmaf(qs[d + 2], kv[2], acc);
+        acc = __builtin_fmaf(qs[d + 3], kv[3], acc);
+      }
+      s = acc;
+    }
+    const float mt = wave_max(s);
+    const float mn = fmaxf(m, mt);
+    const float alpha = (m == -INFINITY) ? 0.f : expf(m - mn);
+    const float p = (j <= lim) ? expf(s - mn) : 0.f;
+    l = l * alpha + wave_sum(p);
+    o0 *= alpha;
+    o1 *= alpha;
+    m = mn;
+    ps[lane] = p;
+    __syncthreads();
+    const int64_t cnt = (lim - k0 + 1) < 64 ? (lim - k0 + 1) : 64;
+    for (int jj = 0; jj < cnt; ++jj) {
+      const int64_t kj = k0 + jj;
+      const float* vr = kj < a.nA ? vA + kj * 128 : vB + (kj - a.nA) * 128;
+      o0 = __builtin_fmaf(ps[jj], vr[2 * lane], o0);
+      o1 = __builtin_fmaf(ps[jj], vr[2 * lane + 1], o1);
+    }
+    __syncthreads();
+  }
+  float* orow = (float*)a.o + qi * a.o_stride + (int64_t)h * 128;
+  orow[2 * lane] = o0 / l;
+  orow[2 * lane + 1] = o1 / l;
+}
+
+}  // namespace
+
+hipError_t launch_prep_bf16_to_f16(const PrepArgs& a, hipStream_t s) { return launch_prep<IN_BF16, OUT_F16>(a, s); }
+hipError_t launch_prep_bf16_to_bf16(const PrepArgs& a, hipStream_t s) { return launch_prep<IN_BF16, OUT_BF16>(a, s); }
+hipError_t launch_prep_f32(const PrepArgs& a, hipStream_t s) { return launch_prep<IN_F32, OUT_F32>(a, s); }
+
+hipError_t launch_euler(float* x, const void* v, bool v_bf16, int64_t n, float dt, hipStream_t s) {
+  const int64_t blocks = (n + 1023) / 1024;
+  if (blocks <= 0) return hipSuccess;
+  if (v_bf16)
+    hipLaunchKernelGGL(k_euler<true>, dim3((unsigned)blocks), dim3(256), 0, s, x, v, n, dt);
+  else
+    hipLaunchKernelGGL(k_euler<false>, dim3((unsigned)blocks), dim3(256), 0, s, x, v, n, dt);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s) {
+  const int64_t blocks = (int64_t)a.n_q * a.n_head;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_attn_f32, dim3((unsigned)blocks), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace qi

@@ -1,0 +1,64 @@
+// qi_launch.h - internal kernel launch interface (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "qi_common.h"
+
+namespace qi {
+
+// Per-token preparation of one K/Q-like tensor (optional RMSNorm over each head's 128 values,
+// then optional 3D rotation) and optional copy of a V-like tensor with the same addressing.
+// Source element (t, h, d) is at x[t*x_tok_stride + h*128 + d]; destination element at
+// dst[t*dst_tok_stride + h*dst_head_stride + d].
+struct PrepArgs {
+  const void* x;
+  int64_t x_tok_stride;
+  void* dst;
+  int64_t dst_tok_stride, dst_head_stride;
+  const void* v;       // nullable: copied (converted) like x, without norm or rotation
+  void* dst_v;
+  int64_t n_tok;
+  int32_t n_head;
+  const float* cos_t;  // nullable (no rotation); [n_tok][64]
+  const float* sin_t;
+  const float* rms_w;  // nullable (no norm); [128]
+  float eps;
+};
+
+hipError_t launch_prep_bf16_to_f16(const PrepArgs& a, hipStream_t s);  // bf16 in, fp16 out
+hipError_t launch_prep_bf16_to_bf16(const PrepArgs& a, hipStream_t s); // bf16 in, bf16 out
+hipError_t launch_prep_f32(const PrepArgs& a, hipStream_t s);          // fp32 in, fp32 out
+
+hipError_t launch_euler(float* x, const void* v, bool v_bf16, int64_t n, float dt, hipStream_t s);
+
+// Attention over keys/values taken from two row sources: key j < nA comes from source A
+// (row j), key j >= nA from source B (row j - nA).  Sources are [head][row][128] with the
+// given head strides (elements).  Queries are token-major with q_stride; outputs dense with
+// o_stride.  Query i has global sequence index q_row0 + i for the mask.
+struct AttnArgs {
+  const void* q;
+  int64_t q_stride;
+  const float* cos_q;
+  const float* sin_q;
+  const float* q_rms_w;
+  float eps;
+  const void* kA;
+  const void* vA;
+  int64_t a_head_stride, nA;
+  const void* kB;
+  const void* vB;
+  int64_t b_head_stride, nB;
+  void* o;
+  int64_t o_stride;
+  int32_t n_q, n_head;
+  int64_t q_row0;
+  float scale_log2;    // softmax scale * log2(e) (fp16 path) or softmax scale (fp32 path)
+  int32_t masked;
+  SegTable segs;
+};
+
+hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);   // bf16 q/o, fp16 K/V sources
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);   // fp32 throughout
+
+}  // namespace qi

@@ -1,0 +1,243 @@
+"""ctypes binding of libqi.so: the C ABI of include/qi.h under the same names.
+
+Argument marshalling only.  Every computation of the path runs in the library's HIP kernels
+(device calls) or its C++ host helpers; nothing here computes part of the method.  Device
+pointers are plain integers (``tensor.data_ptr()``); streams are ``hipStream_t`` handles as
+integers (``torch.cuda.current_stream().cuda_stream``) or None for the null stream.
+
+If libqi.so has not been built, loading raises ``QiLibraryMissing``: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_double, c_float, c_int, c_int32, c_int64, c_uint8, c_void_p
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqi.so")
+
+QI_OK, QI_ERR_ARG, QI_ERR_DTYPE, QI_ERR_SHAPE, QI_ERR_ALIGN, QI_ERR_LAYOUT, QI_ERR_HIP, QI_ERR_CAPACITY = \
+    0, -1, -2, -3, -4, -5, -6, -7
+QI_F32, QI_BF16, QI_F16 = 0, 1, 2
+QI_SEG_TEXT, QI_SEG_IMAGE, QI_SEG_TEXT_BIDIR = 0, 1, 2
+QI_HEAD_DIM = 128
+
+
+class QiLibraryMissing(RuntimeError):
+    pass
+
+
+class QiError(RuntimeError):
+    def __init__(self, status: int, where: str = ""):
+        self.status = status
+        super().__init__(f"{where}: {qi_status_str(status)} ({status})")
+
+
+class qi_segment(ctypes.Structure):
+    _fields_ = [("kind", c_int32), ("n_tokens", c_int32), ("frame", c_int32), ("grid_h", c_int32),
+                ("grid_w", c_int32)]
+
+
+class qi_layout(ctypes.Structure):
+    _fields_ = [("n_seg", c_int32), ("seg", POINTER(qi_segment)), ("head_dim", c_int32),
+                ("bands", c_int32 * 3), ("theta", c_double), ("text_pos0", c_int32)]
+
+
+class qi_kvcache(ctypes.Structure):
+    _fields_ = [("k", c_void_p), ("v", c_void_p), ("dtype", c_int), ("n_layers", c_int32),
+                ("n_head", c_int32), ("p_cap", c_int64)]
+
+
+class qi_qkv(ctypes.Structure):
+    _fields_ = [("q", c_void_p), ("k", c_void_p), ("v", c_void_p), ("o", c_void_p), ("dtype", c_int),
+                ("n_tok", c_int64), ("n_head", c_int32), ("tok_stride", c_int64)]
+
+
+class qi_qkprep(ctypes.Structure):
+    _fields_ = [("cos_t", c_void_p), ("sin_t", c_void_p), ("q_rms_w", c_void_p), ("k_rms_w", c_void_p),
+                ("eps", c_float)]
+
+
+_SIGS = {
+    "qi_status_str": (c_char_p, [c_int]),
+    "qi_version": (c_int, []),
+    "qi_layout_tokens": (c_int, [POINTER(qi_layout), POINTER(c_int64), POINTER(c_int64), POINTER(c_int64)]),
+    "qi_rope3d_positions": (c_int, [POINTER(qi_layout), c_void_p]),
+    "qi_rope3d_tables": (c_int, [POINTER(qi_layout), c_void_p, c_void_p]),
+    "qi_blockmap": (c_int, [POINTER(qi_layout), c_int32, c_int32, c_void_p]),
+    "qi_attn_tile_shape": (c_int, [c_int, POINTER(c_int32), POINTER(c_int32)]),
+    "qi_attn_full_workspace_bytes": (c_int64, [c_int, c_int64, c_int32]),
+    "qi_attn_cached_workspace_bytes": (c_int64, [c_int, c_int64, c_int32]),
+    "qi_kvcache_bytes": (c_int64, [c_int, c_int32, c_int32, c_int64]),
+    "qi_rope3d_apply": (c_int, [c_void_p, c_int, c_int64, c_int32, c_int64, c_void_p, c_void_p, c_void_p,
+                                c_float, c_void_p]),
+    "qi_attn_blockcausal_full": (c_int, [POINTER(qi_qkv), POINTER(qi_qkprep), POINTER(qi_layout), c_float,
+                                         POINTER(qi_kvcache), c_int32, c_void_p, c_int64, c_void_p]),
+    "qi_attn_prefix_store": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_int32, c_int64, POINTER(qi_qkprep),
+                                     POINTER(qi_kvcache), c_int32, c_void_p]),
+    "qi_attn_target_cached": (c_int, [POINTER(qi_qkv), POINTER(qi_qkprep), POINTER(qi_kvcache), c_int32,
+                                      c_int64, c_float, c_void_p, c_int64, c_void_p]),
+    "qi_euler_step": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_float, c_float, c_void_p]),
+    "qi_kernel_timing": (c_int, [c_int]),
+    "qi_kernel_timing_read": (c_int, [POINTER(c_double), POINTER(c_int64)]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libqi.so (once).  Raises QiLibraryMissing when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise QiLibraryMissing(f"{LIB_PATH} not found: build it with `python -m image_generation_qi_amd.build`"
+                                   " (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def exported_symbols() -> Sequence[str]:
+    return list(_SIGS)
+
+
+def _p(x) -> Optional[int]:
+    """Device/host pointer of a tensor-like (``data_ptr()``), an int, or None."""
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if hasattr(x, "ctypes"):        # numpy array
+        return x.ctypes.data
+    return int(x)
+
+
+def _ref(s):
+    return None if s is None else ctypes.byref(s)
+
+
+def check(status: int, where: str = "qi") -> int:
+    if status != QI_OK:
+        raise QiError(status, where)
+    return status
+
+
+# ------------------------------------------------------------------------------------------------
+# struct builders
+# ------------------------------------------------------------------------------------------------
+
+def make_layout(segments, head_dim: int = 128, bands=(16, 56, 56), theta: float = 10000.0,
+                text_pos0: int = -1) -> qi_layout:
+    """qi_layout from a sequence of objects with kind/n_tokens/frame/grid_h/grid_w attributes."""
+    arr = (qi_segment * len(segments))()
+    for i, s in enumerate(segments):
+        arr[i] = qi_segment(s.kind, s.n_tokens, s.frame, s.grid_h, s.grid_w)
+    L = qi_layout(len(segments), ctypes.cast(arr, POINTER(qi_segment)), head_dim, (c_int32 * 3)(*bands),
+                  theta, text_pos0)
+    L._keep = arr
+    return L
+
+
+def make_qkv(q, k, v, o, dtype: int, n_tok: int, n_head: int, tok_stride: int) -> qi_qkv:
+    return qi_qkv(_p(q), _p(k), _p(v), _p(o), dtype, n_tok, n_head, tok_stride)
+
+
+def make_prep(cos_t=None, sin_t=None, q_rms_w=None, k_rms_w=None, eps: float = 1e-6) -> qi_qkprep:
+    return qi_qkprep(_p(cos_t), _p(sin_t), _p(q_rms_w), _p(k_rms_w), eps)
+
+
+def make_cache(k, v, dtype: int, n_layers: int, n_head: int, p_cap: int) -> qi_kvcache:
+    return qi_kvcache(_p(k), _p(v), dtype, n_layers, n_head, p_cap)
+
+
+# ------------------------------------------------------------------------------------------------
+# the C ABI, same names
+# ------------------------------------------------------------------------------------------------
+
+def qi_status_str(status: int) -> str:
+    return lib().qi_status_str(status).decode()
+
+
+def qi_version() -> int:
+    return lib().qi_version()
+
+
+def qi_layout_tokens(layout: qi_layout):
+    S, P, T = c_int64(), c_int64(), c_int64()
+    check(lib().qi_layout_tokens(ctypes.byref(layout), ctypes.byref(S), ctypes.byref(P), ctypes.byref(T)),
+          "qi_layout_tokens")
+    return S.value, P.value, T.value
+
+
+def qi_rope3d_positions(layout: qi_layout, pos) -> int:
+    return lib().qi_rope3d_positions(ctypes.byref(layout), _p(pos))
+
+
+def qi_rope3d_tables(layout: qi_layout, cos_t, sin_t) -> int:
+    return lib().qi_rope3d_tables(ctypes.byref(layout), _p(cos_t), _p(sin_t))
+
+
+def qi_blockmap(layout: qi_layout, tile_q: int, tile_k: int, out_map) -> int:
+    return lib().qi_blockmap(ctypes.byref(layout), tile_q, tile_k, _p(out_map))
+
+
+def qi_attn_tile_shape(dtype: int):
+    tq, tk = c_int32(), c_int32()
+    check(lib().qi_attn_tile_shape(dtype, ctypes.byref(tq), ctypes.byref(tk)), "qi_attn_tile_shape")
+    return tq.value, tk.value
+
+
+def qi_attn_full_workspace_bytes(dtype: int, S: int, n_head: int) -> int:
+    return lib().qi_attn_full_workspace_bytes(dtype, S, n_head)
+
+
+def qi_attn_cached_workspace_bytes(dtype: int, T: int, n_head: int) -> int:
+    return lib().qi_attn_cached_workspace_bytes(dtype, T, n_head)
+
+
+def qi_kvcache_bytes(cache_dtype: int, n_layers: int, n_head: int, p_cap: int) -> int:
+    return lib().qi_kvcache_bytes(cache_dtype, n_layers, n_head, p_cap)
+
+
+def qi_rope3d_apply(x, dtype: int, n_tok: int, n_head: int, tok_stride: int, cos_t, sin_t, rms_w, eps: float,
+                    stream=None) -> int:
+    return lib().qi_rope3d_apply(_p(x), dtype, n_tok, n_head, tok_stride, _p(cos_t), _p(sin_t), _p(rms_w), eps,
+                                 _p(stream))
+
+
+def qi_attn_blockcausal_full(io: qi_qkv, prep: Optional[qi_qkprep], layout: qi_layout, scale: float,
+                             cache: Optional[qi_kvcache], layer: int, workspace, workspace_bytes: int,
+                             stream=None) -> int:
+    return lib().qi_attn_blockcausal_full(ctypes.byref(io), _ref(prep), ctypes.byref(layout), scale, _ref(cache),
+                                          layer, _p(workspace), workspace_bytes, _p(stream))
+
+
+def qi_attn_prefix_store(k, v, dtype: int, P: int, n_head: int, tok_stride: int, prep: Optional[qi_qkprep],
+                         cache: qi_kvcache, layer: int, stream=None) -> int:
+    return lib().qi_attn_prefix_store(_p(k), _p(v), dtype, P, n_head, tok_stride, _ref(prep), _ref(cache), layer,
+                                      _p(stream))
+
+
+def qi_attn_target_cached(io: qi_qkv, prep: Optional[qi_qkprep], cache: qi_kvcache, layer: int, P: int,
+                          scale: float, workspace, workspace_bytes: int, stream=None) -> int:
+    return lib().qi_attn_target_cached(ctypes.byref(io), _ref(prep), _ref(cache), layer, P, scale, _p(workspace),
+                                       workspace_bytes, _p(stream))
+
+
+def qi_euler_step(x, v, v_dtype: int, n: int, sigma_k: float, sigma_k1: float, stream=None) -> int:
+    return lib().qi_euler_step(_p(x), _p(v), v_dtype, n, sigma_k, sigma_k1, _p(stream))
+
+
+def qi_kernel_timing(enable: bool) -> int:
+    return lib().qi_kernel_timing(1 if enable else 0)
+
+
+def qi_kernel_timing_read():
+    ms, n = c_double(), c_int64()
+    check(lib().qi_kernel_timing_read(ctypes.byref(ms), ctypes.byref(n)), "qi_kernel_timing_read")
+    return ms.value, n.value

@@ -1,0 +1,223 @@
+/*
+ * qi.h - C ABI of the block-causal 3D-RoPE joint attention library with a prefix KV cache
+ *        (the attention hot path of the Qwen-Image-2.1 DiT denoiser), for AMD Instinct
+ *        MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [OV]   "Qwen-Image-2.1: how an image is made from noise" course overview (OpenArchLab):
+ *          block cards 2A, 3A, 3C, 4A, 6A, 6B and the learning goals.
+ *   [3A]   "3A - 3D Axial RoPE (16, 56, 56) & Zero-Centered Grid" (OpenArchLab), sections 1-4.
+ *   [EDIT] "QwenImageTransformer2DModel source reading (Qwen-Image-Edit)", sections 6 (joint
+ *          attention processor), 7.1-7.3 (three-axis RoPE tables and centred grids).
+ *
+ * Conventions for every entry point:
+ *   - Every call returns a qi_status.  Arguments are checked before anything is launched; on
+ *     a negative status nothing was enqueued and no output was touched.  No exception
+ *     crosses this boundary.
+ *   - "device" pointers are HIP device memory owned by the caller; the library never
+ *     allocates, frees or keeps them.  "host" pointers are read (or written) during the call
+ *     only.  Inputs are read-only; outputs are written only in the documented range.
+ *   - Device work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is
+ *     asynchronous: no call synchronises the device.
+ *   - Tensors of q, k, v are token-major: row t, head h starts at element t*tok_stride + h*128,
+ *     so a fused [tokens, 3, heads, 128] QKV buffer can be passed with three base pointers.
+ *     Device pointers must be 16-byte aligned and tok_stride a multiple of 8 elements.
+ *   - Attention outputs are dense [n_tok][n_head*128] in the I/O dtype.
+ *   - Floating point: bf16 inputs are upcast exactly; normalisation and rotation run in fp32;
+ *     the attention contractions use fp16 MFMA operands (rotated Q and K, softmax
+ *     probabilities, V) with fp32 accumulation and an fp32 online softmax; outputs are
+ *     rounded to bf16 (nearest even).  fp32 I/O runs fp32 arithmetic throughout.
+ */
+#ifndef QI_H
+#define QI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QI_OK = 0,
+  QI_ERR_ARG = -1,       /* null pointer, negative size or a value out of its range */
+  QI_ERR_DTYPE = -2,     /* unsupported dtype or dtype combination */
+  QI_ERR_SHAPE = -3,     /* sizes inconsistent with each other or with the layout */
+  QI_ERR_ALIGN = -4,     /* pointer not 16-byte aligned or stride not a multiple of 8 */
+  QI_ERR_LAYOUT = -5,    /* invalid segment layout or rotary configuration */
+  QI_ERR_HIP = -6,       /* the HIP runtime reported an error at launch */
+  QI_ERR_CAPACITY = -7   /* cache capacity, layer index or workspace size exceeded */
+} qi_status;
+
+typedef enum { QI_F32 = 0, QI_BF16 = 1, QI_F16 = 2 } qi_dtype;
+
+/* Segment kinds of the joint sequence ([OV] card 3C: text is causal, the tokens of one image
+ * see each other both ways).  QI_SEG_TEXT_BIDIR reads a text run as one bidirectional block. */
+typedef enum { QI_SEG_TEXT = 0, QI_SEG_IMAGE = 1, QI_SEG_TEXT_BIDIR = 2 } qi_seg_kind;
+
+#define QI_HEAD_DIM 128
+#define QI_MAX_SEG 64
+
+/* One run of tokens.  Images: n_tokens == grid_h * grid_w, row-major (height outer);
+ * `frame` is the image's frame index ([3A] section 1; target 0, references 1..N). */
+typedef struct {
+  int32_t kind, n_tokens, frame, grid_h, grid_w;
+} qi_segment;
+
+/* Joint sequence [text | references | target] in order, the target image last ([OV] card 2A).
+ * Prefix = every segment but the last; the last segment must be an image. */
+typedef struct {
+  int32_t n_seg;               /* 1 .. QI_MAX_SEG */
+  const qi_segment* seg;       /* host, n_seg entries */
+  int32_t head_dim;            /* must be 128 */
+  int32_t bands[3];            /* rotary dims for frame, height, width: even, summing to head_dim
+                                  ([3A] section 1: 16, 56, 56) */
+  double theta;                /* rotary base ([EDIT] section 7.1: 10000) */
+  int32_t text_pos0;           /* first text position; -1 = automatic: max over images of
+                                  max(H/2, W/2) ([EDIT] section 7.2 with centred grids) */
+} qi_layout;
+
+/* Prefix KV cache ([OV] card 6A: stored at step 1, loaded at steps 2..N).  k and v are each
+ * [n_layers][n_head][p_cap][128] of `dtype`, device memory owned by the caller.  K is stored
+ * after the optional QK-RMSNorm and the 3D rotation; V as given.  dtype must be QI_F16 for
+ * bf16 attention and QI_F32 for fp32 attention.  fp16 holds every bf16 V with
+ * 2^-17 <= |v| < 65504 exactly (smaller values round to the fp16 subnormal grid, absolute
+ * error <= 2^-25; larger ones overflow to infinity), and keeps rotated K with 3 more mantissa
+ * bits than bf16 would. */
+typedef struct {
+  void* k;
+  void* v;
+  qi_dtype dtype;
+  int32_t n_layers, n_head;
+  int64_t p_cap;
+} qi_kvcache;
+
+/* Attention operands.  q, k, v: device, token-major with `tok_stride`; o: device, dense
+ * [n_tok][n_head*128].  dtype: QI_BF16 or QI_F32 for all four. */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  qi_dtype dtype;
+  int64_t n_tok;
+  int32_t n_head;
+  int64_t tok_stride;
+} qi_qkv;
+
+/* Per-token preparation of Q and K before the contraction ([EDIT] section 6: QK-RMSNorm per
+ * head, then RoPE).  cos_t/sin_t: device fp32 [n_tok][64], row i for the i-th q/k row passed
+ * (use the table rows of the tokens being processed, e.g. rows P.. for the target); both NULL
+ * means q/k are already rotated.  q_rms_w/k_rms_w: device fp32 [128] or NULL for no norm.
+ * eps: RMSNorm epsilon (1e-6 in the model). */
+typedef struct {
+  const float* cos_t;
+  const float* sin_t;
+  const float* q_rms_w;
+  const float* k_rms_w;
+  float eps;
+} qi_qkprep;
+
+/* ------------------------------------------------------------------------------------------
+ * Host-only helpers (no device work; usable without a GPU)
+ * ------------------------------------------------------------------------------------------ */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* qi_status_str(int status);
+
+/* Library ABI version (increments on any signature change). */
+int qi_version(void);
+
+/* Token counts of a layout: S = all, P = prefix (all but the last segment), T = target.
+ * Any output pointer may be NULL.  QI_ERR_LAYOUT for an invalid layout. */
+int qi_layout_tokens(const qi_layout* layout, int64_t* S, int64_t* P, int64_t* T);
+
+/* Integer (frame, height, width) of every token, host int32 [S][3] ([3A] section 1: text
+ * tokens step +1 on all three axes; an image keeps its frame and numbers height
+ * -(H - H/2) .. H/2 - 1 and width -(W - W/2) .. W/2 - 1 around a zero centre). */
+int qi_rope3d_positions(const qi_layout* layout, int32_t* pos);
+
+/* Rotation tables, host fp32 [S][64] each: pair k of band a (frame | height | width) turns by
+ * pos[a] * theta^(-2i/d_a), i the pair's index inside its band ([EDIT] section 7.1).  Angles
+ * and cos/sin are evaluated in double precision and rounded once to fp32. */
+int qi_rope3d_tables(const qi_layout* layout, float* cos_t, float* sin_t);
+
+/* Tile map of the Block-Causal mask ([OV] card 3C), host uint8
+ * [ceil(S/tile_q)][ceil(S/tile_k)]: 0 = no visible (query, key) pair in the tile, 1 = all
+ * in-range pairs visible, 2 = mixed.  The attention kernels skip class-0 tiles, run class-1
+ * tiles without a mask and mask class-2 tiles per element; qi_attn_tile_shape gives the tile
+ * shape they use. */
+int qi_blockmap(const qi_layout* layout, int32_t tile_q, int32_t tile_k, uint8_t* map);
+
+/* Query-tile and key-tile sizes of the attention kernel for an I/O dtype. */
+int qi_attn_tile_shape(qi_dtype dtype, int32_t* tile_q, int32_t* tile_k);
+
+/* Workspace bytes needed by qi_attn_blockcausal_full (S tokens, with or without a cache) and by
+ * qi_attn_target_cached (T target tokens).  Negative = error status. */
+int64_t qi_attn_full_workspace_bytes(qi_dtype dtype, int64_t S, int32_t n_head);
+int64_t qi_attn_cached_workspace_bytes(qi_dtype dtype, int64_t T, int32_t n_head);
+
+/* Bytes of one cache tensor (k or v) for the given shape.  Negative = error status. */
+int64_t qi_kvcache_bytes(qi_dtype cache_dtype, int32_t n_layers, int32_t n_head, int64_t p_cap);
+
+/* ------------------------------------------------------------------------------------------
+ * Device calls
+ * ------------------------------------------------------------------------------------------ */
+
+/* In-place QK preparation of one tensor: optional per-head RMSNorm (rms_w != NULL), then the
+ * 3D rotation (cos_t/sin_t != NULL; at least one of the two must be given) of x, a device
+ * token-major [n_tok][tok_stride] tensor of `dtype` (QI_BF16 or QI_F32) holding n_head heads
+ * of 128.  Tables as in qi_qkprep.  bf16 results are rounded to nearest even.
+ * ([3A] section 1; [EDIT] section 6.) */
+int qi_rope3d_apply(void* x, qi_dtype dtype, int64_t n_tok, int32_t n_head, int64_t tok_stride,
+                    const float* cos_t, const float* sin_t, const float* rms_w, float eps,
+                    void* stream);
+
+/* Step 1: full Block-Causal attention over all S tokens of `layout` ([OV] cards 3C, 4A, 6A):
+ * O = softmax(mask(Q K^T * scale)) V with Q and K prepared per `prep`.  scale <= 0 selects
+ * 1/sqrt(128).  io->n_tok must equal the layout's S.  If `cache` is not NULL the prepared
+ * prefix K and V (tokens 0..P-1) are also written to cache layer `layer`, rows 0..P-1, in the
+ * same pass (the prefix store of [OV] card 6A).  workspace: device, at least
+ * qi_attn_full_workspace_bytes(dtype, S, n_head) bytes, contents scratch. */
+int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_layout* layout,
+                             float scale, const qi_kvcache* cache, int32_t layer,
+                             void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Prefix store alone: prepare K (QK-RMSNorm if prep->k_rms_w, then rotation) and copy V of
+ * the P prefix tokens into cache layer `layer`, rows 0..P-1 ([OV] card 6A "Store").  k, v:
+ * device token-major of `dtype`; prep tables have P rows. */
+int qi_attn_prefix_store(const void* k, const void* v, qi_dtype dtype, int64_t P, int32_t n_head,
+                         int64_t tok_stride, const qi_qkprep* prep, const qi_kvcache* cache,
+                         int32_t layer, void* stream);
+
+/* Steps 2..N: target-only attention ([OV] card 6A "Load"): the T = io->n_tok target queries
+ * attend, without a mask (the target sees every token, [OV] card 3C), to the P cached prefix
+ * keys/values of cache layer `layer` followed by the T fresh target keys/values.  prep tables
+ * hold the target rows (table rows P..P+T-1 of the layout).  scale <= 0 selects 1/sqrt(128).
+ * workspace: device, at least qi_attn_cached_workspace_bytes(dtype, T, n_head) bytes. */
+int qi_attn_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvcache* cache,
+                          int32_t layer, int64_t P, float scale, void* workspace,
+                          int64_t workspace_bytes, void* stream);
+
+/* Euler update of the latent ([OV] learning goals, card 6B): x[i] += (sigma_k1 - sigma_k) * v[i]
+ * for i < n.  x: device fp32; v: device, QI_F32 or QI_BF16.  The step is computed in fp32. */
+int qi_euler_step(float* x, const void* v, qi_dtype v_dtype, int64_t n, float sigma_k,
+                  float sigma_k1, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Measurement hooks
+ * ------------------------------------------------------------------------------------------ */
+
+/* Enable (1) or disable (0) HIP-event timing of every attention-kernel launch made by this
+ * library in the calling process.  Enabling clears earlier records.  Events are host-side
+ * runtime objects; no device memory is allocated. */
+int qi_kernel_timing(int enable);
+
+/* Total elapsed milliseconds and launch count of the recorded attention-kernel launches
+ * (waits for the recorded events to complete). */
+int qi_kernel_timing_read(double* total_ms, int64_t* n_launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QI_H */

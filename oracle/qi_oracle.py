@@ -202,6 +202,19 @@ def mask_dense(segments) -> np.ndarray:
     return (sk < sq) | (same & ~causal_text) | (same & causal_text & (k <= q))
 
 
+def mask_rows(segments, rows) -> np.ndarray:
+    """The same visibility rule as mask_dense, evaluated only for the given query rows
+    (shape [len(rows), S]); used to check sampled rows of full-size sequences."""
+    sid = segment_ids(segments)
+    kinds = np.array([s.kind for s in segments])
+    rows = np.asarray(rows, dtype=np.int64)
+    k = np.arange(sid.shape[0])[None, :]
+    sq, sk = sid[rows][:, None], sid[None, :]
+    same = sq == sk
+    causal_text = kinds[sid[rows]][:, None] == SEG_TEXT
+    return (sk < sq) | (same & ~causal_text) | (same & causal_text & (k <= rows[:, None]))
+
+
 def blockmap(mask: np.ndarray, tile_q: int, tile_k: int) -> np.ndarray:
     """Tile classes over in-range pairs: 0 = no visible pair (skip), 1 = all visible (full),
     2 = mixed (partial).  Shape [ceil(S/tile_q), ceil(S/tile_k)], uint8."""

@@ -1,0 +1,231 @@
+"""CPU tests of libqi's host side: exports, host helpers bit-exact against the oracle, and
+argument checks that must fail before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import qi_inputs as qin
+from oracle import qi_oracle as O
+
+Q = pytest.importorskip("image_generation_qi_amd.qi")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+try:
+    Q.lib()
+    HAVE_LIB = True
+except Q.QiLibraryMissing:
+    HAVE_LIB = False
+
+pytestmark = pytest.mark.skipif(not HAVE_LIB, reason="libqi.so not built")
+
+EDGE_LAYOUTS = {
+    "odd_grids": (qin.text(5), qin.image(5, 3, 1), qin.image(3, 7, 0)),
+    "one_token_segments": (qin.text(1), qin.image(1, 1, 2), qin.image(1, 1, 0)),
+    "target_only": (qin.image(9, 11, 0),),
+    "two_text_runs": (qin.text(7), qin.image(4, 6, 1), qin.text(13), qin.image(2, 2, 2), qin.image(6, 5, 0)),
+    "bidir_text": (qin.text(70, bidir=True), qin.image(8, 8, 1), qin.image(10, 12, 0)),
+    "ragged_tiles": (qin.text(77), qin.image(13, 9, 1), qin.image(15, 17, 0)),
+}
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "qi.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int64_t|int)\s+(qi_\w+)\s*\(", src, re.M)))
+
+
+def all_layouts():
+    out = {k: w.segments for k, w in qin.WORKLOADS.items()}
+    out.update(EDGE_LAYOUTS)
+    return out
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = header_functions()
+    assert len(names) >= 17
+    lib = ctypes.CDLL(Q.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in qi.h but not exported"
+    assert sorted(Q.exported_symbols()) == names
+
+
+def test_status_strings_and_version():
+    assert Q.qi_version() >= 1
+    for st in range(0, -8, -1):
+        assert Q.qi_status_str(st).startswith("QI_")
+    assert "unknown" in Q.qi_status_str(-99)
+
+
+@pytest.mark.parametrize("name", sorted(all_layouts()))
+def test_positions_bit_exact(name):
+    segs = all_layouts()[name]
+    L = Q.make_layout(segs)
+    S, P, T = Q.qi_layout_tokens(L)
+    assert (S, P, T) == O.split_counts(segs)
+    pos = np.zeros((S, 3), np.int32)
+    Q.check(Q.qi_rope3d_positions(L, pos))
+    assert np.array_equal(pos.astype(np.int64), O.positions(segs))
+
+
+def test_positions_text_pos0_override():
+    segs = EDGE_LAYOUTS["two_text_runs"]
+    L = Q.make_layout(segs, text_pos0=100)
+    S, _, _ = Q.qi_layout_tokens(L)
+    pos = np.zeros((S, 3), np.int32)
+    Q.check(Q.qi_rope3d_positions(L, pos))
+    assert np.array_equal(pos.astype(np.int64), O.positions(segs, text_pos0=100))
+
+
+@pytest.mark.parametrize("name", ["cfg0", "cfg1", "cfg2", "cfg3", "odd_grids", "two_text_runs", "bidir_text"])
+def test_rope_tables_bit_exact(name):
+    segs = all_layouts()[name]
+    L = Q.make_layout(segs)
+    S, _, _ = Q.qi_layout_tokens(L)
+    c = np.empty((S, 64), np.float32)
+    s = np.empty((S, 64), np.float32)
+    Q.check(Q.qi_rope3d_tables(L, c, s))
+    rc, rs = O.rope_tables_f32(O.positions(segs))
+    bad = np.count_nonzero(c.view(np.uint32) != rc.view(np.uint32)) + np.count_nonzero(s.view(np.uint32) != rs.view(np.uint32))
+    assert bad == 0, f"{bad} table entries differ from the oracle's once-rounded values"
+
+
+def test_rope_tables_other_theta_and_bands():
+    segs = EDGE_LAYOUTS["odd_grids"]
+    L = Q.make_layout(segs, bands=(32, 48, 48), theta=500.0)
+    S, _, _ = Q.qi_layout_tokens(L)
+    c = np.empty((S, 64), np.float32)
+    s = np.empty((S, 64), np.float32)
+    Q.check(Q.qi_rope3d_tables(L, c, s))
+    rc, rs = O.rope_tables_f32(O.positions(segs), bands=(32, 48, 48), theta=500.0)
+    assert np.array_equal(c.view(np.uint32), rc.view(np.uint32)) and np.array_equal(s.view(np.uint32), rs.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["cfg0", "cfg1", "cfg2"] + sorted(EDGE_LAYOUTS))
+@pytest.mark.parametrize("tiles", [(128, 64), (1, 64), (7, 5), (64, 64), (2, 2)])
+def test_blockmap_bit_exact(name, tiles):
+    segs = all_layouts()[name]
+    tq, tk = tiles
+    L = Q.make_layout(segs)
+    S, _, _ = Q.qi_layout_tokens(L)
+    if S > 3000 and tiles in ((7, 5), (2, 2)):
+        pytest.skip("dense oracle map too slow at this tile count")
+    out = np.zeros(((S + tq - 1) // tq, (S + tk - 1) // tk), np.uint8)
+    Q.check(Q.qi_blockmap(L, tq, tk, out))
+    assert np.array_equal(out, O.blockmap(O.mask_dense(segs), tq, tk))
+
+
+def test_tile_shape_and_sizes():
+    assert Q.qi_attn_tile_shape(Q.QI_BF16) == (128, 64)
+    assert Q.qi_attn_tile_shape(Q.QI_F32) == (1, 64)
+    assert Q.qi_attn_full_workspace_bytes(Q.QI_BF16, 21504, 24) == 2 * 24 * 21504 * 128 * 2
+    assert Q.qi_attn_cached_workspace_bytes(Q.QI_F32, 16, 2) == 2 * 2 * 16 * 128 * 4
+    assert Q.qi_kvcache_bytes(Q.QI_F16, 32, 24, 17408) == 32 * 24 * 17408 * 128 * 2
+    assert Q.qi_kvcache_bytes(Q.QI_BF16, 1, 1, 1) == Q.QI_ERR_DTYPE
+
+
+# ---------------------------------------------------------------------------------------------
+# argument checks forced from the host: each returns its status before any launch
+# ---------------------------------------------------------------------------------------------
+FAKE = 0x7F0000000000  # aligned, never dereferenced (every case below fails a check first)
+
+
+def _good(T=64, H=2, dtype=Q.QI_BF16):
+    io = Q.qi_qkv(FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000, dtype, T, H, H * 128)
+    prep = Q.make_prep(FAKE + 0x4000, FAKE + 0x5000)
+    cache = Q.qi_kvcache(FAKE + 0x6000, FAKE + 0x7000, Q.QI_F16 if dtype == Q.QI_BF16 else Q.QI_F32, 4, H, 100)
+    return io, prep, cache
+
+
+def _cached(io, prep, cache, layer=0, P=50, ws=FAKE + 0x8000, wsb=1 << 40):
+    return Q.qi_attn_target_cached(io, prep, cache, layer, P, 0.0, ws, wsb, None)
+
+
+@pytest.mark.parametrize("case,want", [
+    ("null_q", Q.QI_ERR_ARG), ("null_o", Q.QI_ERR_ARG), ("bad_dtype", Q.QI_ERR_DTYPE),
+    ("f16_io", Q.QI_ERR_DTYPE), ("stride_small", Q.QI_ERR_SHAPE), ("zero_tokens", Q.QI_ERR_SHAPE),
+    ("misaligned", Q.QI_ERR_ALIGN), ("stride_not8", Q.QI_ERR_ALIGN), ("layer_oob", Q.QI_ERR_CAPACITY),
+    ("layer_neg", Q.QI_ERR_CAPACITY), ("P_over_cap", Q.QI_ERR_CAPACITY), ("cache_dtype", Q.QI_ERR_DTYPE),
+    ("cache_heads", Q.QI_ERR_SHAPE), ("ws_small", Q.QI_ERR_CAPACITY), ("ws_null", Q.QI_ERR_ARG),
+    ("cos_without_sin", Q.QI_ERR_ARG), ("null_cache", Q.QI_ERR_ARG), ("bad_eps", Q.QI_ERR_ARG),
+])
+def test_target_cached_rejects(case, want):
+    io, prep, cache = _good()
+    kw = {}
+    if case == "null_q": io.q = None
+    elif case == "null_o": io.o = None
+    elif case == "bad_dtype": io.dtype = 7
+    elif case == "f16_io": io.dtype = Q.QI_F16
+    elif case == "stride_small": io.tok_stride = 128
+    elif case == "zero_tokens": io.n_tok = 0
+    elif case == "misaligned": io.k = FAKE + 0x1008
+    elif case == "stride_not8": io.tok_stride = 2 * 128 + 4
+    elif case == "layer_oob": kw["layer"] = 4
+    elif case == "layer_neg": kw["layer"] = -1
+    elif case == "P_over_cap": kw["P"] = 101
+    elif case == "cache_dtype": cache.dtype = Q.QI_BF16
+    elif case == "cache_heads": cache.n_head = 3
+    elif case == "ws_small": kw["wsb"] = 10
+    elif case == "ws_null": kw["ws"] = None
+    elif case == "cos_without_sin": prep.sin_t = None
+    elif case == "null_cache": cache = None
+    elif case == "bad_eps":
+        prep.q_rms_w = FAKE + 0x9000
+        prep.eps = float("nan")
+    if case == "null_cache":
+        st = Q.lib().qi_attn_target_cached(ctypes.byref(io), ctypes.byref(prep), None, 0, 50, 0.0, FAKE, 1 << 40, None)
+    else:
+        st = _cached(io, prep, cache, **kw)
+    assert st == want, (case, Q.qi_status_str(st))
+
+
+@pytest.mark.parametrize("case,want", [
+    ("head_dim", Q.QI_ERR_LAYOUT), ("bands_sum", Q.QI_ERR_LAYOUT), ("bands_odd", Q.QI_ERR_LAYOUT),
+    ("text_last", Q.QI_ERR_LAYOUT), ("grid_mismatch", Q.QI_ERR_LAYOUT), ("bad_kind", Q.QI_ERR_LAYOUT),
+    ("empty_seg", Q.QI_ERR_LAYOUT), ("wrong_S", Q.QI_ERR_SHAPE), ("theta_neg", Q.QI_ERR_LAYOUT),
+])
+def test_full_rejects_bad_layouts(case, want):
+    segs = [qin.text(16), qin.image(4, 4, 1), qin.image(4, 4, 0)]
+    bands, hd, theta = (16, 56, 56), 128, 10000.0
+    S = 48
+    if case == "head_dim": hd = 64
+    elif case == "bands_sum": bands = (16, 56, 48)
+    elif case == "bands_odd": bands = (15, 57, 56)
+    elif case == "text_last": segs = segs + [qin.text(3)]; S = 51
+    elif case == "grid_mismatch": segs[1] = qin.Segment(qin.SEG_IMAGE, 15, 1, 4, 4); S = 47
+    elif case == "bad_kind": segs[0] = qin.Segment(9, 16)
+    elif case == "empty_seg": segs[0] = qin.Segment(qin.SEG_TEXT, 0); S = 32
+    elif case == "wrong_S": S = 47
+    elif case == "theta_neg": theta = -1.0
+    L = Q.make_layout(segs, hd, bands, theta)
+    io = Q.qi_qkv(FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000, Q.QI_BF16, S, 2, 256)
+    st = Q.qi_attn_blockcausal_full(io, None, L, 0.0, None, 0, FAKE + 0x8000, 1 << 40, None)
+    assert st == want, (case, Q.qi_status_str(st))
+    if want == Q.QI_ERR_LAYOUT:
+        assert Q.lib().qi_layout_tokens(ctypes.byref(L), None, None, None) == Q.QI_ERR_LAYOUT
+
+
+def test_other_entry_points_reject():
+    io, prep, cache = _good()
+    # prefix store
+    assert Q.qi_attn_prefix_store(FAKE, FAKE, Q.QI_BF16, 10, 2, 256, prep, cache, 7, None) == Q.QI_ERR_CAPACITY
+    assert Q.qi_attn_prefix_store(FAKE, None, Q.QI_BF16, 10, 2, 256, prep, cache, 0, None) == Q.QI_ERR_ARG
+    assert Q.qi_attn_prefix_store(FAKE, FAKE, Q.QI_BF16, -1, 2, 256, prep, cache, 0, None) == Q.QI_ERR_SHAPE
+    assert Q.qi_attn_prefix_store(FAKE, FAKE, Q.QI_F32, 10, 2, 256, prep, cache, 0, None) == Q.QI_ERR_DTYPE
+    # rope apply
+    assert Q.qi_rope3d_apply(FAKE, Q.QI_BF16, 8, 2, 256, None, None, None, 1e-6, None) == Q.QI_ERR_ARG
+    assert Q.qi_rope3d_apply(FAKE, Q.QI_BF16, 8, 2, 256, FAKE, None, None, 1e-6, None) == Q.QI_ERR_ARG
+    assert Q.qi_rope3d_apply(FAKE + 2, Q.QI_BF16, 8, 2, 256, FAKE, FAKE, None, 1e-6, None) == Q.QI_ERR_ALIGN
+    assert Q.qi_rope3d_apply(FAKE, Q.QI_F16, 8, 2, 256, FAKE, FAKE, None, 1e-6, None) == Q.QI_ERR_DTYPE
+    # euler
+    assert Q.qi_euler_step(None, FAKE, Q.QI_F32, 8, 1.0, 0.875, None) == Q.QI_ERR_ARG
+    assert Q.qi_euler_step(FAKE, FAKE, Q.QI_F16, 8, 1.0, 0.875, None) == Q.QI_ERR_DTYPE
+    assert Q.qi_euler_step(FAKE, FAKE, Q.QI_F32, -1, 1.0, 0.875, None) == Q.QI_ERR_SHAPE
+    assert Q.qi_euler_step(FAKE + 1, FAKE, Q.QI_F32, 8, 1.0, 0.875, None) == Q.QI_ERR_ALIGN
+    assert Q.qi_euler_step(FAKE, FAKE, Q.QI_F32, 8, float("inf"), 0.875, None) == Q.QI_ERR_ARG
+    # host helpers
+    L = Q.make_layout([qin.image(2, 2, 0)])
+    assert Q.qi_rope3d_positions(L, None) == Q.QI_ERR_ARG
+    assert Q.qi_blockmap(L, 0, 64, np.zeros(4, np.uint8)) == Q.QI_ERR_ARG
+    assert Q.lib().qi_attn_tile_shape(Q.QI_F16, ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32())) == Q.QI_ERR_DTYPE

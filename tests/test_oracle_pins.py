@@ -195,6 +195,14 @@ def test_mask_visible_pair_count_closed_form():
     assert O.visible_pairs(wl.segments) == want == 3702912
 
 
+def test_mask_rows_equals_dense_rows():
+    for segs in (MASK_TINY, qin.WORKLOADS["cfg0"].segments,
+                 (qin.text(7), qin.image(3, 2, 1), qin.text(4, bidir=True), qin.image(3, 3, 0))):
+        m = O.mask_dense(segs)
+        rows = np.arange(m.shape[0])[::3]
+        assert np.array_equal(O.mask_rows(segs, rows), m[rows])
+
+
 def test_mask_prefix_never_sees_target_and_target_sees_all():
     segs = (qin.text(7), qin.image(3, 2, 1), qin.image(2, 2, 2), qin.image(3, 3, 0))
     m = O.mask_dense(segs)
