@@ -107,6 +107,8 @@ def main():
     ap.add_argument("--layers", type=int, default=N_LAYERS)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--step1", action="store_true", help="also time one full step-1 attention per layer")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 10 device-to-device copies of MIB MiB (reference kernel for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -120,6 +122,15 @@ def main():
 
     Q.lib()
     dev = "cuda:0"
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": n * 4, "launches": 10}), flush=True)
+        return
     wl = qin.WORKLOADS[args.workload]
     S, P, T, H = wl.S, wl.P, wl.T, wl.n_head
     NL = args.layers

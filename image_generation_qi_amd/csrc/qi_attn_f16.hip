@@ -25,6 +25,8 @@
 //     workgroups of the same head, which then share that head's K/V in L2.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "qi_launch.h"
 
 namespace qi {
@@ -41,9 +43,9 @@ constexpr int BM = 128;             // query rows per workgroup
 constexpr int BN = 64;              // keys per tile
 constexpr int HD = 128;             // head dim
 constexpr int KP = HD + 8;          // K row pitch in LDS, fp16 elements (272 bytes)
-constexpr int VP = BN + 4;          // Vt row pitch in LDS, fp16 elements (136 bytes)
+constexpr int VP = HD + 32;         // V row pitch in LDS, fp16 elements (320 bytes)
 constexpr int KTILE = BN * KP;
-constexpr int VTILE = HD * VP;
+constexpr int VTILE = BN * VP;
 constexpr int BUF = KTILE + VTILE;  // one stage, fp16 elements
 constexpr float TAU = 8.0f;         // lazy-rescale threshold (log2 units)
 
@@ -60,6 +62,16 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
   return u >> 16;
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing LDS read (gfx950): within each group of 16 lanes, output lane 4a+b receives
+// element b of the 8-byte chunk addressed by lane a+4j, as its element j.
+__device__ __forceinline__ h4 lds_read_tr(const _Float16* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  return __builtin_bit_cast(h4, r);
+}
+
 template <bool MASKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_f16(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 smem[2 * BUF];
@@ -73,14 +85,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  const int64_t nkeys = a.nA + a.nB;
+  const int nA = (int)a.nA, nkeys = (int)(a.nA + a.nB);
 
   // ---- this lane's query: load, optional RMSNorm, rotate, scale, to fp16 --------------------
-  const int64_t qrow = (int64_t)qt * BM + wave * 32 + l32;
+  const int qrow = qt * BM + wave * 32 + l32;
   const bool qok = qrow < a.n_q;
   float x[64];
   {
-    const uint16_t* qp = (const uint16_t*)a.q + (qok ? qrow : 0) * a.q_stride + (int64_t)h * HD + 8 * g;
+    const uint16_t* qp = (const uint16_t*)a.q + (int64_t)(qok ? qrow : 0) * a.q_stride + h * HD + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       u32x4 w = qok ? *(const u32x4*)(qp + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
@@ -109,8 +121,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
   if (a.cos_q && qok) {
-    const float* cp = a.cos_q + qrow * 64 + 4 * g;
-    const float* sp = a.sin_q + qrow * 64 + 4 * g;
+    const float* cp = a.cos_q + (int64_t)qrow * 64 + 4 * g;
+    const float* sp = a.sin_q + (int64_t)qrow * 64 + 4 * g;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const f32x4 c = *(const f32x4*)(cp + 8 * kk);
@@ -130,114 +142,122 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = 0; i < 8; ++i) qf[kk][i] = (_Float16)(x[8 * kk + i] * a.scale_log2);
 
   // ---- key range of this tile row --------------------------------------------------------
-  const int64_t q_first = (int64_t)qt * BM;
-  const int64_t q_last = (q_first + BM < a.n_q ? q_first + BM : a.n_q) - 1;
-  int64_t lim = nkeys - 1, lim_first = nkeys - 1, lim_last = nkeys - 1;
+  const int q_first = qt * BM;
+  const int q_last = (q_first + BM < a.n_q ? q_first + BM : a.n_q) - 1;
+  int lim = nkeys - 1, lim_first = nkeys - 1, lim_last = nkeys - 1;
   if (MASKED) {
-    lim = row_limit(a.segs, a.q_row0 + (qok ? qrow : q_last));
-    lim_first = row_limit(a.segs, a.q_row0 + q_first);
-    lim_last = row_limit(a.segs, a.q_row0 + q_last);
+    lim = (int)row_limit(a.segs, a.q_row0 + (qok ? qrow : q_last));
+    lim_first = (int)row_limit(a.segs, a.q_row0 + q_first);
+    lim_last = (int)row_limit(a.segs, a.q_row0 + q_last);
     lim = lim < nkeys - 1 ? lim : nkeys - 1;
     lim_first = lim_first < nkeys - 1 ? lim_first : nkeys - 1;
     lim_last = lim_last < nkeys - 1 ? lim_last : nkeys - 1;
   }
-  const int kt_end = (int)(lim_last / BN) + 1;     // tiles past this hold no visible key
-  const int kt_full = (int)((lim_first + 1) / BN); // tiles before this need no mask
+  const int kt_end = lim_last / BN + 1;       // tiles past this hold no visible key
+  const int kt_full = (lim_first + 1) / BN;   // tiles before this need no mask
 
   const _Float16* kA = (const _Float16*)a.kA + (int64_t)h * a.a_head_stride;
   const _Float16* vA = (const _Float16*)a.vA + (int64_t)h * a.a_head_stride;
   const _Float16* kB = (const _Float16*)a.kB + (int64_t)h * a.b_head_stride;
   const _Float16* vB = (const _Float16*)a.vB + (int64_t)h * a.b_head_stride;
 
-  // ---- tile staging: global -> registers -> LDS -------------------------------------------
+  // ---- tile staging: global -> registers -> LDS (both K and V row-major) -------------------
   const int cc = (tid & 15) * 8;   // 8-element column chunk
-  const int kr0 = tid >> 4;        // K rows kr0 + 16j
-  const int vk0 = 4 * (tid >> 4);  // V keys vk0 .. vk0+3
+  const int kr0 = tid >> 4;        // rows kr0 + 16j
   u32x4 kreg[4], vreg[4];
   auto load_tile = [&](int kt) {
-    const int64_t base = (int64_t)kt * BN;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t key = base + kr0 + 16 * j;
-      const _Float16* p = key < a.nA ? kA + key * HD : kB + (key - a.nA) * HD;
-      kreg[j] = key < nkeys ? *(const u32x4*)(p + cc) : u32x4{0u, 0u, 0u, 0u};
+    const int key0 = kt * BN;
+    const _Float16* kb = nullptr;
+    const _Float16* vb = nullptr;
+    if (key0 + BN <= nA) {                       // whole tile in source A
+      kb = kA + (int64_t)key0 * HD;
+      vb = vA + (int64_t)key0 * HD;
+    } else if (key0 >= nA && key0 + BN <= nkeys) {  // whole tile in source B
+      kb = kB + (int64_t)(key0 - nA) * HD;
+      vb = vB + (int64_t)(key0 - nA) * HD;
     }
+    if (kb) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t key = base + vk0 + i;
-      const _Float16* p = key < a.nA ? vA + key * HD : vB + (key - a.nA) * HD;
-      vreg[i] = key < nkeys ? *(const u32x4*)(p + cc) : u32x4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < 4; ++j) {
+        const int off = (kr0 + 16 * j) * HD + cc;
+        kreg[j] = *(const u32x4*)(kb + off);
+        vreg[j] = *(const u32x4*)(vb + off);
+      }
+    } else {                                      // straddling or ragged tile: per row
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = key0 + kr0 + 16 * j;
+        const int64_t ro = (int64_t)(key < nA ? key : key - nA) * HD + cc;
+        const _Float16* kp = key < nA ? kA : kB;
+        const _Float16* vp = key < nA ? vA : vB;
+        kreg[j] = key < nkeys ? *(const u32x4*)(kp + ro) : u32x4{0u, 0u, 0u, 0u};
+        vreg[j] = key < nkeys ? *(const u32x4*)(vp + ro) : u32x4{0u, 0u, 0u, 0u};
+      }
     }
   };
   auto store_tile = [&](int buf) {
     _Float16* Ks = smem + buf * BUF;
-    _Float16* Vt = Ks + KTILE;
+    _Float16* Vs = Ks + KTILE;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *(u32x4*)(Ks + (kr0 + 16 * j) * KP + cc) = kreg[j];
-    // transpose 4 keys x 8 dims into 8 rows of Vt, 4 keys (8 bytes) each
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const u32x2 ev = {(vreg[0][m] & 0xFFFFu) | (vreg[1][m] << 16), (vreg[2][m] & 0xFFFFu) | (vreg[3][m] << 16)};
-      const u32x2 od = {(vreg[0][m] >> 16) | (vreg[1][m] & 0xFFFF0000u),
-                        (vreg[2][m] >> 16) | (vreg[3][m] & 0xFFFF0000u)};
-      *(u32x2*)(Vt + (cc + 2 * m) * VP + vk0) = ev;
-      *(u32x2*)(Vt + (cc + 2 * m + 1) * VP + vk0) = od;
+    for (int j = 0; j < 4; ++j) {
+      *(u32x4*)(Ks + (kr0 + 16 * j) * KP + cc) = kreg[j];
+      *(u32x4*)(Vs + (kr0 + 16 * j) * VP + cc) = vreg[j];
     }
   };
 
-  // ---- main loop -------------------------------------------------------------------------
+  // per-lane LDS offsets: K rows for the S^T A-operand; V rows/cols for the transposing reads
+  const int k_off = l32 * KP + 8 * g;
+  const int L = lane & 15;
+  const int v_off = (4 * g + (L >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
+
   f32x16 o[4];
 #pragma unroll
   for (int bd = 0; bd < 4; ++bd)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[bd][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  int buf = 0;
-  for (int kt = 0; kt < kt_end; ++kt) {
-    const bool has_next = kt + 1 < kt_end;
-    if (has_next) load_tile(kt + 1);
-
+  auto step = [&](int kt, int buf, auto masked_tag) {
+    constexpr bool MT = decltype(masked_tag)::value;
     const _Float16* Ks = smem + buf * BUF;
-    const _Float16* Vt = Ks + KTILE;
+    const _Float16* Vs = Ks + KTILE;
 
     // S^T for two blocks of 32 keys
     f32x16 s0, s1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s0[r] = 0.f;
-      s1[r] = 0.f;
+    {
+      const h8 a0 = *(const h8*)(Ks + k_off);
+      const h8 a1 = *(const h8*)(Ks + 32 * KP + k_off);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, qf[0], zero16, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, qf[0], zero16, 0, 0, 0);
     }
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const h8 ka0 = *(const h8*)(Ks + l32 * KP + 16 * kk + 8 * g);
-      const h8 ka1 = *(const h8*)(Ks + (32 + l32) * KP + 16 * kk + 8 * g);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka0, qf[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka1, qf[kk], s1, 0, 0, 0);
+    for (int kk = 1; kk < 8; ++kk) {
+      const h8 a0 = *(const h8*)(Ks + k_off + 16 * kk);
+      const h8 a1 = *(const h8*)(Ks + 32 * KP + k_off + 16 * kk);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, qf[kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, qf[kk], s1, 0, 0, 0);
     }
 
-    if (kt >= kt_full) {  // partial tile: keys past the row limit are hidden
-      const int64_t kb = (int64_t)kt * BN + 4 * g;
+    if constexpr (MT) {  // keys past the row limit (or past the last key) are hidden
+      const int rel = lim - kt * BN - 4 * g;   // key offset (within tile, minus 4g) of the last visible key
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t key = kb + 8 * (r >> 2) + (r & 3);
-        if (key > lim) s0[r] = -INFINITY;
-        if (key + 32 > lim) s1[r] = -INFINITY;
+        const int kr = 8 * (r >> 2) + (r & 3);
+        if (kr > rel) s0[r] = -INFINITY;
+        if (kr + 32 > rel) s1[r] = -INFINITY;
       }
     }
 
-    float mt = -INFINITY;
+    float mt = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, fmaxf(s0[r], s1[r]));
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, fmaxf(s0[r], s1[r]));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     // lazy rescale: only rows whose max grew by more than TAU move their reference point;
-    // other rows multiply by exactly 1, so every row's arithmetic is independent of the
-    // other rows in the wave (prefix rows stay bit-identical whatever the target holds).
+    // other rows multiply by exactly 1, so each row's arithmetic is independent of the other
+    // rows in the wave (prefix rows stay bit-identical whatever the target holds).
     const bool grow = mt > m_run + TAU;
-    if (__any(grow)) {
+    if (__builtin_expect(__any(grow), 0)) {
       const float mn = grow ? mt : m_run;
       const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mn) : 1.f;
       l_run *= alpha;
@@ -247,7 +267,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int r = 0; r < 16; ++r) o[bd][r] *= alpha;
       m_run = mn;
     }
-    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+    const float mu = MT ? ((m_run == -INFINITY) ? 0.f : m_run) : m_run;
 
     h8 pf[4];
     float ps = 0.f;
@@ -261,19 +281,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     l_run += ps;
 
-    // O^T += Vt P^T
+    // O^T += V^T P^T; V^T operand from two transposing reads per 16-key chunk
 #pragma unroll
-    for (int bd = 0; bd < 4; ++bd) {
-      const _Float16* vrow = Vt + (32 * bd + l32) * VP + 4 * g;
+    for (int c = 0; c < 4; ++c) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {  // 16-key chunk c: keys 16c + {4g..4g+3, 8+4g..8+4g+3}
-        const h4 lo = *(const h4*)(vrow + 16 * c);
-        const h4 hi = *(const h4*)(vrow + 16 * c + 8);
+      for (int bd = 0; bd < 4; ++bd) {
+        const _Float16* vp = Vs + v_off + 16 * c * VP + 32 * bd;
+        const h4 lo = lds_read_tr(vp);
+        const h4 hi = lds_read_tr(vp + 8 * VP);
         const h8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[c], o[bd], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);   // keep at most one chunk of V reads in flight
     }
+  };
 
+  // ---- main loop: unmasked tiles, then masked tiles --------------------------------------
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  int buf = 0;
+  int kt = 0;
+  const int kt_mid = kt_full < kt_end ? kt_full : kt_end;
+  for (; kt < kt_mid; ++kt) {
+    const bool has_next = kt + 1 < kt_end;
+    if (has_next) load_tile(kt + 1);
+    step(kt, buf, std::false_type{});
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+  for (; kt < kt_end; ++kt) {
+    const bool has_next = kt + 1 < kt_end;
+    if (has_next) load_tile(kt + 1);
+    step(kt, buf, std::true_type{});
     if (has_next) store_tile(buf ^ 1);
     __syncthreads();
     buf ^= 1;
@@ -283,7 +324,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float lt = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / lt;
   if (qok) {
-    uint16_t* op = (uint16_t*)a.o + qrow * a.o_stride + (int64_t)h * HD + 4 * g;
+    uint16_t* op = (uint16_t*)a.o + (int64_t)qrow * a.o_stride + h * HD + 4 * g;
 #pragma unroll
     for (int bd = 0; bd < 4; ++bd)
 #pragma unroll
