@@ -34,6 +34,7 @@ namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -42,12 +43,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int BM = 128;             // query rows per workgroup
 constexpr int BN = 64;              // keys per tile
 constexpr int HD = 128;             // head dim
-constexpr int KP = HD + 8;          // K row pitch in LDS, fp16 elements (272 bytes)
-constexpr int VP = HD + 32;         // V row pitch in LDS, fp16 elements (320 bytes)
-constexpr int KTILE = BN * KP;
-constexpr int VTILE = BN * VP;
-constexpr int BUF = KTILE + VTILE;  // one stage, fp16 elements
-constexpr float TAU = 8.0f;         // lazy-rescale threshold (log2 units)
+constexpr int TILE = BN * HD;       // one K or V tile, fp16 elements (16 KB, rows of 256 bytes)
+constexpr int BUF = 2 * TILE;       // one pipeline stage: K tile then V tile
+constexpr float TAU_P = 256.0f;     // lazy-rescale threshold: probabilities may reach 2^8
 
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
   const int q = n >> 3, r = n & 7;
@@ -70,6 +68,32 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 __device__ __forceinline__ h4 lds_read_tr(const _Float16* p) {
   const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
   return __builtin_bit_cast(h4, r);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+// LDS tiles hold unpadded 256-byte rows; the 16-byte chunk c of row r is stored at chunk
+// position c ^ swz(r).  K: swz = r & 15, so the 16 rows read by one quarter-wave (same logical
+// chunk) hit 16 distinct chunk positions.  V: swz = 4 * (r & 3), so the 4 rows x 4 chunks read
+// by a half-wave of transposing reads are all distinct.
+__device__ __forceinline__ int swz_k(int r) { return r & 15; }
+__device__ __forceinline__ int swz_v(int r) { return 4 * (r & 3); }
+
+// Direct global -> LDS copy of 16 bytes per lane; lane l lands at dst + 16*l.
+__device__ __forceinline__ void load_lds16(const void* src, void* dst_wave_base) {
+  __builtin_amdgcn_global_load_lds((const glb_void*)src, (lds_void*)dst_wave_base, 16, 0, 0);
+}
+
+// Both halves of a wave exchanged: for lane l, returns (x[l], x[l ^ 32]) in an order that is
+// the same for the two lanes of the pair, so any symmetric combination is bit-identical.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
 template <bool MASKED>
@@ -161,55 +185,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const _Float16* kB = (const _Float16*)a.kB + (int64_t)h * a.b_head_stride;
   const _Float16* vB = (const _Float16*)a.vB + (int64_t)h * a.b_head_stride;
 
-  // ---- tile staging: global -> registers -> LDS (both K and V row-major) -------------------
-  const int cc = (tid & 15) * 8;   // 8-element column chunk
-  const int kr0 = tid >> 4;        // rows kr0 + 16j
-  u32x4 kreg[4], vreg[4];
-  auto load_tile = [&](int kt) {
+  // ---- tile staging: direct global -> LDS loads into swizzled rows -------------------------
+  // wave w fills rows 16w .. 16w+15 of each tile: 4 loads of 1 KB (4 rows) for K and for V.
+  // Lane i of load j covers row 16w + 4j + i/16, chunk position i%16.
+  int koff[4], voff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 16 * wave + 4 * j + (lane >> 4);
+    const int pos = lane & 15;
+    koff[j] = row * HD + 8 * (pos ^ swz_k(row));
+    voff[j] = row * HD + 8 * (pos ^ swz_v(row));
+  }
+  auto load_tile_part = [&](int kt, int buf, bool is_k) {
+    _Float16* dst = smem + buf * BUF + (is_k ? 0 : TILE) + (16 * wave) * HD;
+    const _Float16* srcA = is_k ? kA : vA;
+    const _Float16* srcB = is_k ? kB : vB;
+    const int* off = is_k ? koff : voff;
     const int key0 = kt * BN;
-    const _Float16* kb = nullptr;
-    const _Float16* vb = nullptr;
-    if (key0 + BN <= nA) {                       // whole tile in source A
-      kb = kA + (int64_t)key0 * HD;
-      vb = vA + (int64_t)key0 * HD;
-    } else if (key0 >= nA && key0 + BN <= nkeys) {  // whole tile in source B
-      kb = kB + (int64_t)(key0 - nA) * HD;
-      vb = vB + (int64_t)(key0 - nA) * HD;
-    }
-    if (kb) {
+    const _Float16* base = nullptr;
+    if (key0 + BN <= nA)                              // whole tile in source A
+      base = srcA + (int64_t)key0 * HD;
+    else if (key0 >= nA && key0 + BN <= nkeys)        // whole tile in source B
+      base = srcB + (int64_t)(key0 - nA) * HD;
+    if (base) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) load_lds16(base + off[j], dst + j * 4 * HD);
+    } else {  // straddling or ragged tile: per-row source; rows past the last key re-read
+              // key 0 (finite data that the row limit masks out)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int off = (kr0 + 16 * j) * HD + cc;
-        kreg[j] = *(const u32x4*)(kb + off);
-        vreg[j] = *(const u32x4*)(vb + off);
+        const int row = 16 * wave + 4 * j + (lane >> 4);
+        int key = key0 + row;
+        if (key >= nkeys) key = 0;
+        const bool inA = key < nA;
+        const int64_t rb = (int64_t)(inA ? key : key - nA) * HD - (int64_t)row * HD;
+        load_lds16((inA ? srcA : srcB) + rb + off[j], dst + j * 4 * HD);
       }
-    } else {                                      // straddling or ragged tile: per row
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = key0 + kr0 + 16 * j;
-        const int64_t ro = (int64_t)(key < nA ? key : key - nA) * HD + cc;
-        const _Float16* kp = key < nA ? kA : kB;
-        const _Float16* vp = key < nA ? vA : vB;
-        kreg[j] = key < nkeys ? *(const u32x4*)(kp + ro) : u32x4{0u, 0u, 0u, 0u};
-        vreg[j] = key < nkeys ? *(const u32x4*)(vp + ro) : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    _Float16* Ks = smem + buf * BUF;
-    _Float16* Vs = Ks + KTILE;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *(u32x4*)(Ks + (kr0 + 16 * j) * KP + cc) = kreg[j];
-      *(u32x4*)(Vs + (kr0 + 16 * j) * VP + cc) = vreg[j];
     }
   };
 
-  // per-lane LDS offsets: K rows for the S^T A-operand; V rows/cols for the transposing reads
-  const int k_off = l32 * KP + 8 * g;
+  // per-lane LDS offsets: K rows for the S^T A-operand (chunk 2kk+g of row l32 or 32+l32);
+  // V rows/cols for the transposing reads (row 16c+8h+4g+L/4, dims 32bd+16(lane/16%2)+4(L%4))
   const int L = lane & 15;
-  const int v_off = (4 * g + (L >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
-
+  const int vrow0 = 4 * g + (L >> 2);                        // + 16c + 8h: same row & 3
+  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (L & 3);      // + 32bd
   f32x16 o[4];
 #pragma unroll
   for (int bd = 0; bd < 4; ++bd)
@@ -218,29 +237,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float m_run = -INFINITY, l_run = 0.f;
   const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
-  auto step = [&](int kt, int buf, auto masked_tag) {
-    constexpr bool MT = decltype(masked_tag)::value;
-    const _Float16* Ks = smem + buf * BUF;
-    const _Float16* Vs = Ks + KTILE;
-
-    // S^T for two blocks of 32 keys
-    f32x16 s0, s1;
-    {
-      const h8 a0 = *(const h8*)(Ks + k_off);
-      const h8 a1 = *(const h8*)(Ks + 32 * KP + k_off);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, qf[0], zero16, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, qf[0], zero16, 0, 0, 0);
-    }
+  // S^T = K Q^T for the 64 keys of one K buffer (two blocks of 32 keys).  Rows l32 and 32+l32
+  // share (row & 15), so both reads use the same chunk position.
+  auto qk = [&](int kbuf, f32x16& s0, f32x16& s1) {
+    const _Float16* Ks = smem + kbuf * BUF;
 #pragma unroll
-    for (int kk = 1; kk < 8; ++kk) {
-      const h8 a0 = *(const h8*)(Ks + k_off + 16 * kk);
-      const h8 a1 = *(const h8*)(Ks + 32 * KP + k_off + 16 * kk);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, qf[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, qf[kk], s1, 0, 0, 0);
+    for (int kk = 0; kk < 8; ++kk) {
+      const int pos = ((2 * kk + g) ^ swz_k(l32)) * 8;
+      const h8 a0 = *(const h8*)(Ks + l32 * HD + pos);
+      const h8 a1 = *(const h8*)(Ks + (32 + l32) * HD + pos);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, qf[kk], kk ? s0 : zero16, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, qf[kk], kk ? s1 : zero16, 0, 0, 0);
     }
+  };
 
-    if constexpr (MT) {  // keys past the row limit (or past the last key) are hidden
-      const int rel = lim - kt * BN - 4 * g;   // key offset (within tile, minus 4g) of the last visible key
+  // Online softmax of one tile's scores.  Common path, branch-free: probabilities against the
+  // current reference m_run, rounded to fp16 (the values PV consumes), their row sum taken from
+  // those same fp16 values with fp32 dot products, and a packed-fp16 max to detect rows whose
+  // scores rose more than TAU above the reference.  Rare path (first visible tile of a row or a
+  // large rise): move those rows' reference to their true max, recompute, and return the factor
+  // alpha by which the running output must be rescaled (exactly 1 for all other rows, so each
+  // row's arithmetic never depends on the other rows of the wave).
+  auto softmax = [&](int kt, f32x16& s0, f32x16& s1, h8 (&pf)[4], auto masked_tag) -> float {
+    constexpr bool MT = decltype(masked_tag)::value;
+    if constexpr (MT) {
+      const int rel = lim - kt * BN - 4 * g;   // offset (in tile, minus 4g) of the last visible key
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kr = 8 * (r >> 2) + (r & 3);
@@ -248,47 +269,61 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (kr + 32 > rel) s1[r] = -INFINITY;
       }
     }
-
-    float mt = fmaxf(s0[0], s1[0]);
+    auto probs = [&](float mu) {
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, fmaxf(s0[r], s1[r]));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    // lazy rescale: only rows whose max grew by more than TAU move their reference point;
-    // other rows multiply by exactly 1, so each row's arithmetic is independent of the other
-    // rows in the wave (prefix rows stay bit-identical whatever the target holds).
-    const bool grow = mt > m_run + TAU;
-    if (__builtin_expect(__any(grow), 0)) {
-      const float mn = grow ? mt : m_run;
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mn) : 1.f;
-      l_run *= alpha;
+      for (int r = 0; r < 16; ++r) {
+        pf[r >> 3][r & 7] = (_Float16)__builtin_amdgcn_exp2f(s0[r] - mu);
+        pf[2 + (r >> 3)][r & 7] = (_Float16)__builtin_amdgcn_exp2f(s1[r] - mu);
+      }
+    };
+    probs(m_run);
+    h2 pm = __builtin_shufflevector(pf[0], pf[0], 0, 1);
 #pragma unroll
-      for (int bd = 0; bd < 4; ++bd)
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[bd][r] *= alpha;
-      m_run = mn;
+      for (int i = 0; i < 4; ++i)
+        pm = __builtin_elementwise_max(pm, h2{pf[c][2 * i], pf[c][2 * i + 1]});
+    float pmax = fmaxf((float)pm[0], (float)pm[1]);
+    pmax = pair_max(pmax);                       // NaN-free: p >= 0 or +inf
+    float alpha = 1.f;
+    const bool need = !(pmax <= TAU_P);          // also true for +inf (reference still -inf)
+    if (__builtin_expect(__any(need), 0)) {
+      float mt = fmaxf(s0[0], s1[0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, fmaxf(s0[r], s1[r]));
+      mt = pair_max(mt);
+      if (need) {
+        alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mt);
+        m_run = mt;
+      }
+      probs(MT ? ((m_run == -INFINITY) ? 0.f : m_run) : m_run);
     }
-    const float mu = MT ? ((m_run == -INFINITY) ? 0.f : m_run) : m_run;
-
-    h8 pf[4];
-    float ps = 0.f;
+    const h2 one2 = {(_Float16)1.f, (_Float16)1.f};
+    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p0 = __builtin_amdgcn_exp2f(s0[r] - mu);
-      const float p1 = __builtin_amdgcn_exp2f(s1[r] - mu);
-      ps += p0 + p1;
-      pf[r >> 3][r & 7] = (_Float16)p0;
-      pf[2 + (r >> 3)][r & 7] = (_Float16)p1;
-    }
-    l_run += ps;
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        ps0 = __builtin_amdgcn_fdot2(h2{pf[c][2 * i], pf[c][2 * i + 1]}, one2, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2(h2{pf[c][2 * i + 2], pf[c][2 * i + 3]}, one2, ps1, false);
+      }
+    l_run = l_run * alpha + (ps0 + ps1);
+    return alpha;
+  };
 
-    // O^T += V^T P^T; V^T operand from two transposing reads per 16-key chunk
+  // O^T += V^T P^T for one V buffer; the V^T operand comes from two transposing reads per
+  // 16-key chunk (rows vrow0 + 16c + 8h share row & 3, hence one swizzle for both reads)
+  auto pv = [&](int vbuf, const h8 (&pf)[4]) {
+    const _Float16* Vs = smem + vbuf * BUF + TILE;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int bd = 0; bd < 4; ++bd) {
-        const _Float16* vp = Vs + v_off + 16 * c * VP + 32 * bd;
+        const int col = 32 * bd + vcol;
+        const int pcol = ((col >> 3) ^ swz_v(vrow0)) * 8 + (col & 7);
+        const _Float16* vp = Vs + (vrow0 + 16 * c) * HD + pcol;
         const h4 lo = lds_read_tr(vp);
-        const h4 hi = lds_read_tr(vp + 8 * VP);
+        const h4 hi = lds_read_tr(vp + 8 * HD);
         const h8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[c], o[bd], 0, 0, 0);
       }
@@ -296,32 +331,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
-  // ---- main loop: unmasked tiles, then masked tiles --------------------------------------
-  load_tile(0);
-  store_tile(0);
+  // ---- software-pipelined main loop ------------------------------------------------------
+  // K runs one tile ahead of V.  Iteration kt: start loading K[kt+2] and V[kt+1]; issue the
+  // QK^T MFMAs of tile kt+1 together with the softmax of tile kt (independent work, one basic
+  // block, so MFMA and VALU overlap); apply the rare output rescale; PV of tile kt.
+  // Buffer reuse: K buffer kt%2 (tile kt) was last read by the QK of iteration kt-1 and V buffer
+  // (kt+1)%2 by the PV of iteration kt-1; the barrier ending iteration kt-1 ordered both.
+  auto load_k = [&](int kt, int b) { load_tile_part(kt, b, true); };
+  auto load_v = [&](int kt, int b) { load_tile_part(kt, b, false); };
+  load_k(0, 0);
+  load_v(0, 0);
+  if (kt_end > 1) load_k(1, 1);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  int buf = 0;
+  f32x16 sc0, sc1;
+  qk(0, sc0, sc1);
   int kt = 0;
   const int kt_mid = kt_full < kt_end ? kt_full : kt_end;
-  for (; kt < kt_mid; ++kt) {
-    const bool has_next = kt + 1 < kt_end;
-    if (has_next) load_tile(kt + 1);
-    step(kt, buf, std::false_type{});
-    if (has_next) store_tile(buf ^ 1);
+  auto iteration = [&](auto masked_tag) {
+    const int b = kt & 1;
+    if (kt + 2 < kt_end) load_k(kt + 2, b);
+    if (kt + 1 < kt_end) load_v(kt + 1, b ^ 1);
+    // next tile's scores; on the last iteration this reads a stale (in-bounds) buffer and the
+    // result is discarded, which keeps QK and softmax in one basic block
+    f32x16 sn0, sn1;
+    qk(b ^ 1, sn0, sn1);
+    h8 pf[4];
+    const float alpha = softmax(kt, sc0, sc1, pf, masked_tag);
+    if (__builtin_expect(__any(alpha != 1.f), 0)) {
+#pragma unroll
+      for (int bd = 0; bd < 4; ++bd)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[bd][r] *= alpha;
+    }
+    pv(b, pf);
+    sc0 = sn0;
+    sc1 = sn1;
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    buf ^= 1;
-  }
-  for (; kt < kt_end; ++kt) {
-    const bool has_next = kt + 1 < kt_end;
-    if (has_next) load_tile(kt + 1);
-    step(kt, buf, std::true_type{});
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-  }
+  };
+  for (; kt < kt_mid; ++kt) iteration(std::false_type{});
+  for (; kt < kt_end; ++kt) iteration(std::true_type{});
 
   // ---- epilogue: normalise, round to bf16, store ----------------------------------------
-  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float lt = pair_sum(l_run);
   const float inv = 1.0f / lt;
   if (qok) {
     uint16_t* op = (uint16_t*)a.o + (int64_t)qrow * a.o_stride + h * HD + 4 * g;

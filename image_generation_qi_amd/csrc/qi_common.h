@@ -11,7 +11,7 @@
 
 #include <stdint.h>
 
-#include "../../include/qi.h"
+#include "qi.h"
 
 #if defined(__HIPCC__)
 #include <hip/hip_runtime.h>
