@@ -126,6 +126,18 @@ AttnArgs attn_args(const qi_qkv* io, const qi_qkprep* prep, float scale) {
   return a;
 }
 
+// Key-chunk count (from the layout's T, identical for step 1 and the cached steps) and the
+// partial-output buffers placed at `base` in the workspace.
+void set_partials(AttnArgs& a, char* base, int64_t n_q, int64_t T, int32_t n_head, qi_dtype dtype) {
+  a.n_split = 1;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  if (dtype != QI_BF16) return;
+  a.n_split = attn_f16_splits(T, n_head);
+  a.part_o = (float*)base;
+  a.part_ml = (float*)(base + (int64_t)a.n_split * n_q * n_head * QI_HEAD_DIM * (int64_t)sizeof(float));
+}
+
 int run_attn(const AttnArgs& a, qi_dtype dtype, hipStream_t s) {
   TimedLaunch t(s);
   return launch_status(dtype == QI_BF16 ? launch_attn_f16(a, s) : launch_attn_f32(a, s));
@@ -176,7 +188,7 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
   if (cache && (st = check_cache(cache, io->dtype, io->n_head, layer, li.P)) != QI_OK) return st;
   if (!workspace) return QI_ERR_ARG;
   if (!aligned16(workspace)) return QI_ERR_ALIGN;
-  if (workspace_bytes < qi_attn_full_workspace_bytes(io->dtype, li.S, io->n_head)) return QI_ERR_CAPACITY;
+  if (workspace_bytes < qi_attn_full_workspace_bytes(layout, io->dtype, io->n_head)) return QI_ERR_CAPACITY;
 
   hipStream_t s = (hipStream_t)stream;
   const int es = elem_size(io->dtype == QI_BF16 ? QI_F16 : QI_F32);
@@ -187,6 +199,10 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
   a.masked = 1;
   a.segs = li.tab;
   a.q_row0 = 0;
+  // partial outputs of the key chunks follow the K/V rows (S rows are reserved for K/V in
+  // either case, so the layout does not depend on the cache argument)
+  set_partials(a, (char*)workspace + 2 * (int64_t)io->n_head * li.S * QI_HEAD_DIM * es, li.S, li.T, io->n_head,
+               io->dtype);
   if (cache) {
     void* ck = (void*)cache_layer(cache->k, cache, layer);
     void* cv = (void*)cache_layer(cache->v, cache, layer);
@@ -273,6 +289,7 @@ int qi_attn_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvca
     return st;
   AttnArgs a = attn_args(io, prep, scale);
   a.masked = 0;
+  set_partials(a, wk + 2 * (int64_t)io->n_head * T * QI_HEAD_DIM * es, T, T, io->n_head, io->dtype);
   a.kA = cache_layer(cache->k, cache, layer);
   a.vA = cache_layer(cache->v, cache, layer);
   a.a_head_stride = cache->p_cap * QI_HEAD_DIM;

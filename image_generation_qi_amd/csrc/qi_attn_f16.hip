@@ -21,6 +21,8 @@
 //     row max grows by more than TAU (probabilities stay <= 2^TAU, well inside fp16).
 //   - the Block-Causal mask is applied per tile from the row limits (see qi_common.h): tiles
 //     with no visible pair are never loaded, tiles with all pairs visible run unmasked.
+//   - key chunks (n_split > 1) balance the grid over the CUs: each chunk of a query tile's key
+//     tiles writes an unnormalised partial output with its (max, sum), merged by k_combine.
 //   - blockIdx is remapped so that the 8 XCDs (each with its own L2) get contiguous runs of
 //     workgroups of the same head, which then share that head's K/V in L2.
 #include <hip/hip_runtime.h>
@@ -102,8 +104,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int n_qt = (a.n_q + BM - 1) / BM;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = logical / n_qt;
-  int qt = logical - h * n_qt;
+  const int split = logical % a.n_split;
+  const int rest = logical / a.n_split;
+  const int h = rest / n_qt;
+  int qt = rest - h * n_qt;
   if (MASKED) qt = n_qt - 1 - qt;  // longest rows first
 
   const int tid = threadIdx.x;
@@ -179,6 +183,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   const int kt_end = lim_last / BN + 1;       // tiles past this hold no visible key
   const int kt_full = (lim_first + 1) / BN;   // tiles before this need no mask
+  const int t_begin = split * a.split_tiles;  // this workgroup's chunk of key tiles
+  const int t_stop = (t_begin + a.split_tiles < kt_end) ? t_begin + a.split_tiles : kt_end;
+  if (t_begin >= t_stop) {  // the chunk holds no visible key for any row of the tile
+    if (qok) {
+      const int64_t row = ((int64_t)split * a.n_q + qrow) * a.n_head + h;
+      f32x4* po = (f32x4*)(a.part_o + row * HD + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) po[2 * i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (g == 0) {
+        a.part_ml[2 * row] = -INFINITY;
+        a.part_ml[2 * row + 1] = 0.f;
+      }
+    }
+    return;
+  }
 
   const _Float16* kA = (const _Float16*)a.kA + (int64_t)h * a.a_head_stride;
   const _Float16* vA = (const _Float16*)a.vA + (int64_t)h * a.a_head_stride;
@@ -339,19 +358,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // (kt+1)%2 by the PV of iteration kt-1; the barrier ending iteration kt-1 ordered both.
   auto load_k = [&](int kt, int b) { load_tile_part(kt, b, true); };
   auto load_v = [&](int kt, int b) { load_tile_part(kt, b, false); };
-  load_k(0, 0);
-  load_v(0, 0);
-  if (kt_end > 1) load_k(1, 1);
+  load_k(t_begin, 0);
+  load_v(t_begin, 0);
+  if (t_begin + 1 < t_stop) load_k(t_begin + 1, 1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16 sc0, sc1;
   qk(0, sc0, sc1);
-  int kt = 0;
-  const int kt_mid = kt_full < kt_end ? kt_full : kt_end;
+  int kt = t_begin;
+  const int kt_mid = kt_full < t_begin ? t_begin : (kt_full < t_stop ? kt_full : t_stop);
   auto iteration = [&](auto masked_tag) {
-    const int b = kt & 1;
-    if (kt + 2 < kt_end) load_k(kt + 2, b);
-    if (kt + 1 < kt_end) load_v(kt + 1, b ^ 1);
+    const int b = (kt - t_begin) & 1;
+    if (kt + 2 < t_stop) load_k(kt + 2, b);
+    if (kt + 1 < t_stop) load_v(kt + 1, b ^ 1);
     // next tile's scores; on the last iteration this reads a stale (in-bounds) buffer and the
     // result is discarded, which keeps QK and softmax in one basic block
     f32x16 sn0, sn1;
@@ -371,34 +390,109 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
   };
   for (; kt < kt_mid; ++kt) iteration(std::false_type{});
-  for (; kt < kt_end; ++kt) iteration(std::true_type{});
+  for (; kt < t_stop; ++kt) iteration(std::true_type{});
 
-  // ---- epilogue: normalise, round to bf16, store ----------------------------------------
+  // ---- epilogue: normalise and store bf16, or store the chunk's partial ---------------------
   const float lt = pair_sum(l_run);
-  const float inv = 1.0f / lt;
   if (qok) {
-    uint16_t* op = (uint16_t*)a.o + (int64_t)qrow * a.o_stride + h * HD + 4 * g;
+    if (a.n_split == 1) {
+      const float inv = 1.0f / lt;
+      uint16_t* op = (uint16_t*)a.o + (int64_t)qrow * a.o_stride + h * HD + 4 * g;
 #pragma unroll
-    for (int bd = 0; bd < 4; ++bd)
+      for (int bd = 0; bd < 4; ++bd)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const u32x2 w = {to_bf16(o[bd][4 * r4] * inv) | (to_bf16(o[bd][4 * r4 + 1] * inv) << 16),
-                         to_bf16(o[bd][4 * r4 + 2] * inv) | (to_bf16(o[bd][4 * r4 + 3] * inv) << 16)};
-        *(u32x2*)(op + 32 * bd + 8 * r4) = w;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const u32x2 w = {to_bf16(o[bd][4 * r4] * inv) | (to_bf16(o[bd][4 * r4 + 1] * inv) << 16),
+                           to_bf16(o[bd][4 * r4 + 2] * inv) | (to_bf16(o[bd][4 * r4 + 3] * inv) << 16)};
+          *(u32x2*)(op + 32 * bd + 8 * r4) = w;
+        }
+    } else {
+      const int64_t row = ((int64_t)split * a.n_q + qrow) * a.n_head + h;
+      float* po = a.part_o + row * HD + 4 * g;
+#pragma unroll
+      for (int bd = 0; bd < 4; ++bd)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(f32x4*)(po + 32 * bd + 8 * r4) = f32x4{o[bd][4 * r4], o[bd][4 * r4 + 1], o[bd][4 * r4 + 2], o[bd][4 * r4 + 3]};
+      if (g == 0) {
+        a.part_ml[2 * row] = m_run;
+        a.part_ml[2 * row + 1] = lt;
       }
+    }
   }
+}
+
+// Merge of the key chunks: for each (row, head), O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+// with M = max_s m_s, rounded to bf16.  16 threads per (row, head), 8 dims each.
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                                                 uint16_t* __restrict__ o, int64_t o_stride, int n_q, int n_head,
+                                                 int n_split) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rh = gid >> 4;
+  if (rh >= (int64_t)n_q * n_head) return;
+  const int d0 = (int)(gid & 15) * 8;
+  const int64_t stride = (int64_t)n_q * n_head;   // rows per split
+  float M = -INFINITY;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, part_ml[2 * (s * stride + rh)]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int s = 0; s < n_split; ++s) {
+    const float m = part_ml[2 * (s * stride + rh)];
+    if (m == -INFINITY) continue;
+    const float w = __builtin_amdgcn_exp2f(m - M);
+    den += w * part_ml[2 * (s * stride + rh) + 1];
+    const f32x4* p = (const f32x4*)(part_o + (s * stride + rh) * HD + d0);
+    const f32x4 x0 = p[0], x1 = p[1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[j] += w * x0[j];
+      acc[4 + j] += w * x1[j];
+    }
+  }
+  const float inv = 1.0f / den;
+  const int64_t q = rh / n_head;
+  const int h = (int)(rh - q * n_head);
+  u32x4 w;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = to_bf16(acc[2 * j] * inv) | (to_bf16(acc[2 * j + 1] * inv) << 16);
+  *(u32x4*)(o + q * o_stride + h * HD + d0) = w;
 }
 
 }  // namespace
 
-hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s) {
+int attn_f16_splits(int64_t T, int32_t n_head) {
+  // Split the key range only when the target's query tiles cannot give every CU two
+  // workgroups (512 slots); then aim at about 1024 workgroups, at most 8 chunks.  Larger
+  // grids gain nothing from splitting and would pay for the partial outputs.
+  const int64_t units = (T + BM - 1) / BM * n_head;
+  if (units >= 512) return 1;
+  int64_t s = (1024 + units - 1) / units;
+  if (s > 8) s = 8;
+  return (int)s;
+}
+
+int64_t attn_f16_partial_bytes(int64_t n_q, int32_t n_head) {
+  return (int64_t)n_q * n_head * (HD + 2) * (int64_t)sizeof(float);
+}
+
+hipError_t launch_attn_f16(const AttnArgs& a_in, hipStream_t s) {
+  AttnArgs a = a_in;
   const int64_t n_qt = (a.n_q + BM - 1) / BM;
-  const int64_t blocks = n_qt * a.n_head;
+  const int64_t kt_total = (a.nA + a.nB + BN - 1) / BN;
+  if (a.n_split < 1) a.n_split = 1;
+  a.split_tiles = (int)((kt_total + a.n_split - 1) / a.n_split);
+  if (a.split_tiles < 1) a.split_tiles = 1;
+  const int64_t blocks = n_qt * a.n_head * a.n_split;
   if (blocks <= 0) return hipSuccess;
   if (a.masked)
     hipLaunchKernelGGL(k_attn_f16<true>, dim3((unsigned)blocks), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(k_attn_f16<false>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_split == 1) return e;
+  const int64_t threads = (int64_t)a.n_q * a.n_head * 16;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a.part_o, a.part_ml,
+                     (uint16_t*)a.o, a.o_stride, a.n_q, a.n_head, a.n_split);
   return hipGetLastError();
 }
 

@@ -10,6 +10,7 @@
 #include <cstring>
 
 #include "qi_common.h"
+#include "qi_launch.h"
 
 namespace qi {
 
@@ -182,20 +183,34 @@ int qi_attn_tile_shape(qi_dtype dtype, int32_t* tile_q, int32_t* tile_k) {
   return QI_OK;
 }
 
+// K and V rows, [n_head][rows][128]: fp16 for bf16 attention, fp32 for fp32 attention
 static int64_t rows_bytes(qi_dtype dtype, int64_t rows, int32_t n_head) {
   if (rows < 0 || n_head < 1) return QI_ERR_ARG;
-  // K and V, [n_head][rows][128], fp16 for bf16 attention and fp32 for fp32 attention
   if (dtype == QI_BF16) return 2 * (int64_t)n_head * rows * QI_HEAD_DIM * 2;
   if (dtype == QI_F32) return 2 * (int64_t)n_head * rows * QI_HEAD_DIM * 4;
   return QI_ERR_DTYPE;
 }
 
-int64_t qi_attn_full_workspace_bytes(qi_dtype dtype, int64_t S, int32_t n_head) {
-  return rows_bytes(dtype, S, n_head);
+// Partial outputs of the key chunks (bf16 path with more than one chunk only).
+static int64_t partial_bytes(qi_dtype dtype, int64_t n_q, int64_t T, int32_t n_head) {
+  if (dtype != QI_BF16) return 0;
+  const int s = attn_f16_splits(T, n_head);
+  return s > 1 ? (int64_t)s * attn_f16_partial_bytes(n_q, n_head) : 0;
+}
+
+int64_t qi_attn_full_workspace_bytes(const qi_layout* layout, qi_dtype dtype, int32_t n_head) {
+  LayoutInfo li;
+  int st = analyse_layout(layout, &li);
+  if (st != QI_OK) return st;
+  const int64_t r = rows_bytes(dtype, li.S, n_head);
+  if (r < 0) return r;
+  return r + partial_bytes(dtype, li.S, li.T, n_head);
 }
 
 int64_t qi_attn_cached_workspace_bytes(qi_dtype dtype, int64_t T, int32_t n_head) {
-  return rows_bytes(dtype, T, n_head);
+  const int64_t r = rows_bytes(dtype, T, n_head);
+  if (r < 0) return r;
+  return r + partial_bytes(dtype, T, T, n_head);
 }
 
 int64_t qi_kvcache_bytes(qi_dtype cache_dtype, int32_t n_layers, int32_t n_head, int64_t p_cap) {

@@ -55,8 +55,21 @@ struct AttnArgs {
   int64_t q_row0;
   float scale_log2;    // softmax scale * log2(e) (fp16 path) or softmax scale (fp32 path)
   int32_t masked;
+  // fp16 path: the key tiles of every query tile are cut into n_split consecutive chunks of
+  // split_tiles tiles; with n_split > 1 each chunk writes an unnormalised partial output and its
+  // (max, sum) to part_o / part_ml, and a combine kernel produces o.
+  int32_t n_split, split_tiles;
+  float* part_o;       // [n_split][n_q][n_head][128]
+  float* part_ml;      // [n_split][n_q][n_head][2]
   SegTable segs;
 };
+
+// Number of key chunks of the fp16 path for a sequence whose target has T tokens and n_head
+// heads.  Step 1 and the cached steps both use the layout's T, so a target row is processed in
+// the same chunks (and gets the same bits) in both.
+int attn_f16_splits(int64_t T, int32_t n_head);
+// Workspace bytes of the partial outputs for n_q rows.
+int64_t attn_f16_partial_bytes(int64_t n_q, int32_t n_head);
 
 hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);   // bf16 q/o, fp16 K/V sources
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);   // fp32 throughout

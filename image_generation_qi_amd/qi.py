@@ -67,7 +67,7 @@ _SIGS = {
     "qi_rope3d_tables": (c_int, [POINTER(qi_layout), c_void_p, c_void_p]),
     "qi_blockmap": (c_int, [POINTER(qi_layout), c_int32, c_int32, c_void_p]),
     "qi_attn_tile_shape": (c_int, [c_int, POINTER(c_int32), POINTER(c_int32)]),
-    "qi_attn_full_workspace_bytes": (c_int64, [c_int, c_int64, c_int32]),
+    "qi_attn_full_workspace_bytes": (c_int64, [POINTER(qi_layout), c_int, c_int32]),
     "qi_attn_cached_workspace_bytes": (c_int64, [c_int, c_int64, c_int32]),
     "qi_kvcache_bytes": (c_int64, [c_int, c_int32, c_int32, c_int64]),
     "qi_rope3d_apply": (c_int, [c_void_p, c_int, c_int64, c_int32, c_int64, c_void_p, c_void_p, c_void_p,
@@ -192,8 +192,8 @@ def qi_attn_tile_shape(dtype: int):
     return tq.value, tk.value
 
 
-def qi_attn_full_workspace_bytes(dtype: int, S: int, n_head: int) -> int:
-    return lib().qi_attn_full_workspace_bytes(dtype, S, n_head)
+def qi_attn_full_workspace_bytes(layout: qi_layout, dtype: int, n_head: int) -> int:
+    return lib().qi_attn_full_workspace_bytes(ctypes.byref(layout), dtype, n_head)
 
 
 def qi_attn_cached_workspace_bytes(dtype: int, T: int, n_head: int) -> int:

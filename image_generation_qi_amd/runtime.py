@@ -62,7 +62,7 @@ class Attention:
 
     def __init__(self, layout: Layout, n_head: int, io_dtype: int = Q.QI_BF16, device="cuda"):
         self.L, self.H, self.dtype, self.device = layout, n_head, io_dtype, device
-        self.ws_full_bytes = Q.qi_attn_full_workspace_bytes(io_dtype, layout.S, n_head)
+        self.ws_full_bytes = Q.qi_attn_full_workspace_bytes(layout.c, io_dtype, n_head)
         self.ws_cached_bytes = Q.qi_attn_cached_workspace_bytes(io_dtype, layout.T, n_head)
         self.ws_full = None
         self.ws_cached = None

@@ -151,9 +151,10 @@ int qi_blockmap(const qi_layout* layout, int32_t tile_q, int32_t tile_k, uint8_t
 /* Query-tile and key-tile sizes of the attention kernel for an I/O dtype. */
 int qi_attn_tile_shape(qi_dtype dtype, int32_t* tile_q, int32_t* tile_k);
 
-/* Workspace bytes needed by qi_attn_blockcausal_full (S tokens, with or without a cache) and by
- * qi_attn_target_cached (T target tokens).  Negative = error status. */
-int64_t qi_attn_full_workspace_bytes(qi_dtype dtype, int64_t S, int32_t n_head);
+/* Workspace bytes needed by qi_attn_blockcausal_full for `layout` (with or without a cache) and
+ * by qi_attn_target_cached for T target tokens: prepared K/V rows plus, for bf16, the partial
+ * outputs of the key chunks the kernel splits long key ranges into.  Negative = error status. */
+int64_t qi_attn_full_workspace_bytes(const qi_layout* layout, qi_dtype dtype, int32_t n_head);
 int64_t qi_attn_cached_workspace_bytes(qi_dtype dtype, int64_t T, int32_t n_head);
 
 /* Bytes of one cache tensor (k or v) for the given shape.  Negative = error status. */
@@ -177,7 +178,7 @@ int qi_rope3d_apply(void* x, qi_dtype dtype, int64_t n_tok, int32_t n_head, int6
  * 1/sqrt(128).  io->n_tok must equal the layout's S.  If `cache` is not NULL the prepared
  * prefix K and V (tokens 0..P-1) are also written to cache layer `layer`, rows 0..P-1, in the
  * same pass (the prefix store of [OV] card 6A).  workspace: device, at least
- * qi_attn_full_workspace_bytes(dtype, S, n_head) bytes, contents scratch. */
+ * qi_attn_full_workspace_bytes(layout, dtype, n_head) bytes, contents scratch. */
 int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_layout* layout,
                              float scale, const qi_kvcache* cache, int32_t layer,
                              void* workspace, int64_t workspace_bytes, void* stream);

@@ -119,8 +119,16 @@ def test_blockmap_bit_exact(name, tiles):
 def test_tile_shape_and_sizes():
     assert Q.qi_attn_tile_shape(Q.QI_BF16) == (128, 64)
     assert Q.qi_attn_tile_shape(Q.QI_F32) == (1, 64)
-    assert Q.qi_attn_full_workspace_bytes(Q.QI_BF16, 21504, 24) == 2 * 24 * 21504 * 128 * 2
+    L3 = Q.make_layout(qin.WORKLOADS["cfg3"].segments)
+    # config[3]: 768 query tiles x heads fill the GPU, no key chunks: K/V fp16 rows only
+    assert Q.qi_attn_full_workspace_bytes(L3, Q.QI_BF16, 24) == 2 * 24 * 21504 * 128 * 2
+    assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, 4096, 24) == 2 * 24 * 4096 * 128 * 2
+    # config[1]: 8 x 24 = 192 units -> 6 key chunks of fp32 partials (128 values + max + sum)
+    L1 = Q.make_layout(qin.WORKLOADS["cfg1"].segments)
+    assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, 1024, 24) == 2 * 24 * 1024 * 128 * 2 + 6 * 1024 * 24 * 130 * 4
+    assert Q.qi_attn_full_workspace_bytes(L1, Q.QI_BF16, 24) == 2 * 24 * 2304 * 128 * 2 + 6 * 2304 * 24 * 130 * 4
     assert Q.qi_attn_cached_workspace_bytes(Q.QI_F32, 16, 2) == 2 * 2 * 16 * 128 * 4
+    assert Q.qi_attn_full_workspace_bytes(L3, Q.QI_F32, 2) == 2 * 2 * 21504 * 128 * 4
     assert Q.qi_kvcache_bytes(Q.QI_F16, 32, 24, 17408) == 32 * 24 * 17408 * 128 * 2
     assert Q.qi_kvcache_bytes(Q.QI_BF16, 1, 1, 1) == Q.QI_ERR_DTYPE
 
