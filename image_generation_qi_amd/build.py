@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqi.so")
-SOURCES = ["qi_host.cpp", "qi_kernels.hip", "qi_attn_f16.hip", "qi_abi.hip"]
+SOURCES = ["qi_host.cpp", "qi_kernels.hip", "qi_attn_f16.hip", "qi_dit.hip", "qi_abi.hip"]
 ARCH = "gfx950"
 
 

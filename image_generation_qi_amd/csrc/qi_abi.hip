@@ -314,6 +314,53 @@ int qi_euler_step(float* x, const void* v, qi_dtype v_dtype, int64_t n, float si
   return launch_status(launch_euler(x, v, v_dtype == QI_BF16, n, sigma_k1 - sigma_k, (hipStream_t)stream));
 }
 
+int qi_gemm_bf16(const void* x, int64_t ldx, const void* w, void* out, int64_t ldo, int64_t M, int64_t N, int64_t K,
+                 int epilogue, const float* gate, int64_t row0, int64_t P, void* stream) {
+  if (!x || !w || !out) return QI_ERR_ARG;
+  if (epilogue < QI_EPI_STORE || epilogue > QI_EPI_SWIGLU) return QI_ERR_ARG;
+  if (epilogue == QI_EPI_GATED_RESIDUAL && !gate) return QI_ERR_ARG;
+  if (M < 0 || N < 64 || K < 64 || (N % 64) || (K % 64) || M > 65535LL * 128 || N > INT32_MAX) return QI_ERR_SHAPE;
+  if (ldx < K || ldo < (epilogue == QI_EPI_SWIGLU ? N / 2 : N)) return QI_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(out) || !aligned16(gate) || (ldx % 8) || (ldo % 8))
+    return QI_ERR_ALIGN;
+  if (M == 0) return QI_OK;
+  GemmArgs a{x, ldx, w, out, ldo, M, N, K, gate, row0, P};
+  return launch_status(launch_gemm(a, epilogue, (hipStream_t)stream));
+}
+
+int qi_zc_rmsnorm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64_t M, int32_t D, const float* w,
+                      const float* scale, const float* shift, int64_t row0, int64_t P, float eps, void* stream) {
+  if (!x || !out) return QI_ERR_ARG;
+  if (M < 0 || D < 4 || (D % 4) || ldx < D || ldo < D || M > INT32_MAX) return QI_ERR_SHAPE;
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return QI_ERR_ARG;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(scale) || !aligned16(shift) || (ldx % 4) || (ldo % 4) ||
+      (reinterpret_cast<uintptr_t>(out) & 7))
+    return QI_ERR_ALIGN;
+  if (M == 0) return QI_OK;
+  NormArgs a{x, ldx, out, ldo, M, D, w, scale, shift, row0, P, eps};
+  return launch_status(launch_zc_norm_mod(a, (hipStream_t)stream));
+}
+
+int qi_timestep_embed(const float* t, int32_t n, int32_t dim, float* out, void* stream) {
+  if (!t || !out) return QI_ERR_ARG;
+  if (n < 0 || dim < 2 || (dim % 2)) return QI_ERR_SHAPE;
+  return launch_status(launch_timestep_embed(t, n, dim, out, (hipStream_t)stream));
+}
+
+int qi_linear_small(const float* x, int32_t n_vec, int32_t I, const void* w, int32_t O, int32_t silu_in, float* y,
+                    void* stream) {
+  if (!x || !w || !y) return QI_ERR_ARG;
+  if (n_vec < 1 || n_vec > 4 || I < 8 || (I % 8) || O < 0) return QI_ERR_SHAPE;
+  if (!aligned16(w)) return QI_ERR_ALIGN;
+  return launch_status(launch_linear_small(x, n_vec, I, w, O, silu_in ? 1 : 0, y, (hipStream_t)stream));
+}
+
+int qi_cast_bf16(const float* x, void* y, int64_t n, void* stream) {
+  if (!x || !y) return QI_ERR_ARG;
+  if (n < 0) return QI_ERR_SHAPE;
+  return launch_status(launch_cast_bf16(x, y, n, (hipStream_t)stream));
+}
+
 int qi_kernel_timing(int enable) {
   std::lock_guard<std::mutex> lk(g_tmu);
   g_timing = enable != 0;

@@ -71,6 +71,39 @@ int attn_f16_splits(int64_t T, int32_t n_head);
 // Workspace bytes of the partial outputs for n_q rows.
 int64_t attn_f16_partial_bytes(int64_t n_q, int32_t n_head);
 
+// y = x W^T with an epilogue (qi_epilogue): x bf16 [M][ldx], W bf16 [N][K] (K % 64 == 0).
+struct GemmArgs {
+  const void* x;
+  int64_t ldx;
+  const void* w;
+  void* out;
+  int64_t ldo;
+  int64_t M, N, K;
+  const float* gate;   // QI_EPI_GATED_RESIDUAL: fp32 [2][N]; row m uses gate[(m + row0 < P) ? 0 : 1]
+  int64_t row0, P;
+};
+// ZeroCenterRMSNorm + modulation of fp32 rows into bf16 rows.
+struct NormArgs {
+  const float* x;
+  int64_t ldx;
+  void* out;
+  int64_t ldo;
+  int64_t M;
+  int32_t D;
+  const float* w;       // nullable: (w + 1) factor
+  const float* scale;   // nullable, [2][D]: (1 + scale) factor by the row's segment
+  const float* shift;   // nullable, [2][D]
+  int64_t row0, P;
+  float eps;
+};
+
+hipError_t launch_gemm(const GemmArgs& a, int epilogue, hipStream_t s);
+hipError_t launch_zc_norm_mod(const NormArgs& a, hipStream_t s);
+hipError_t launch_timestep_embed(const float* t, int n, int dim, float* out, hipStream_t s);
+hipError_t launch_linear_small(const float* x, int nv, int I, const void* w, int O, int silu_in, float* y,
+                               hipStream_t s);
+hipError_t launch_cast_bf16(const float* x, void* y, int64_t n, hipStream_t s);
+
 hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);   // bf16 q/o, fp16 K/V sources
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);   // fp32 throughout
 

@@ -21,6 +21,7 @@ QI_OK, QI_ERR_ARG, QI_ERR_DTYPE, QI_ERR_SHAPE, QI_ERR_ALIGN, QI_ERR_LAYOUT, QI_E
     0, -1, -2, -3, -4, -5, -6, -7
 QI_F32, QI_BF16, QI_F16 = 0, 1, 2
 QI_SEG_TEXT, QI_SEG_IMAGE, QI_SEG_TEXT_BIDIR = 0, 1, 2
+QI_EPI_STORE, QI_EPI_STORE_F32, QI_EPI_GATED_RESIDUAL, QI_EPI_SWIGLU = 0, 1, 2, 3
 QI_HEAD_DIM = 128
 
 
@@ -79,6 +80,13 @@ _SIGS = {
     "qi_attn_target_cached": (c_int, [POINTER(qi_qkv), POINTER(qi_qkprep), POINTER(qi_kvcache), c_int32,
                                       c_int64, c_float, c_void_p, c_int64, c_void_p]),
     "qi_euler_step": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_float, c_float, c_void_p]),
+    "qi_gemm_bf16": (c_int, [c_void_p, c_int64, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int64, c_int,
+                             c_void_p, c_int64, c_int64, c_void_p]),
+    "qi_zc_rmsnorm_mod": (c_int, [c_void_p, c_int64, c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p,
+                                  c_void_p, c_int64, c_int64, c_float, c_void_p]),
+    "qi_timestep_embed": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+    "qi_linear_small": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+    "qi_cast_bf16": (c_int, [c_void_p, c_void_p, c_int64, c_void_p]),
     "qi_kernel_timing": (c_int, [c_int]),
     "qi_kernel_timing_read": (c_int, [POINTER(c_double), POINTER(c_int64)]),
 }
@@ -231,6 +239,29 @@ def qi_attn_target_cached(io: qi_qkv, prep: Optional[qi_qkprep], cache: qi_kvcac
 
 def qi_euler_step(x, v, v_dtype: int, n: int, sigma_k: float, sigma_k1: float, stream=None) -> int:
     return lib().qi_euler_step(_p(x), _p(v), v_dtype, n, sigma_k, sigma_k1, _p(stream))
+
+
+def qi_gemm_bf16(x, ldx: int, w, out, ldo: int, M: int, N: int, K: int, epilogue: int, gate=None, row0: int = 0,
+                 P: int = 0, stream=None) -> int:
+    return lib().qi_gemm_bf16(_p(x), ldx, _p(w), _p(out), ldo, M, N, K, epilogue, _p(gate), row0, P, _p(stream))
+
+
+def qi_zc_rmsnorm_mod(x, ldx: int, out, ldo: int, M: int, D: int, w=None, scale=None, shift=None, row0: int = 0,
+                      P: int = 0, eps: float = 1e-6, stream=None) -> int:
+    return lib().qi_zc_rmsnorm_mod(_p(x), ldx, _p(out), ldo, M, D, _p(w), _p(scale), _p(shift), row0, P, eps,
+                                   _p(stream))
+
+
+def qi_timestep_embed(t, n: int, dim: int, out, stream=None) -> int:
+    return lib().qi_timestep_embed(_p(t), n, dim, _p(out), _p(stream))
+
+
+def qi_linear_small(x, n_vec: int, I: int, w, O: int, silu_in: bool, y, stream=None) -> int:
+    return lib().qi_linear_small(_p(x), n_vec, I, _p(w), O, 1 if silu_in else 0, _p(y), _p(stream))
+
+
+def qi_cast_bf16(x, y, n: int, stream=None) -> int:
+    return lib().qi_cast_bf16(_p(x), _p(y), n, _p(stream))
 
 
 def qi_kernel_timing(enable: bool) -> int:

@@ -125,3 +125,172 @@ def from_bits(bits: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
     return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.float32)).to(device)
+
+
+# ------------------------------------------------------------------------------------------------
+# one single-stream DiT layer and the sampling loop around the attention
+# ------------------------------------------------------------------------------------------------
+
+def pack_swiglu(w_gate: torch.Tensor, w_up: torch.Tensor) -> torch.Tensor:
+    """Interleave gate and up weights [F][D] into the [2F][D] layout the SwiGLU epilogue reads:
+    blocks of 64 rows, 32 gate rows then the 32 up rows of the same features."""
+    F, D = w_gate.shape
+    assert w_up.shape == (F, D) and F % 32 == 0
+    return torch.stack([w_gate.reshape(F // 32, 32, D), w_up.reshape(F // 32, 32, D)], dim=1).reshape(2 * F, D).contiguous()
+
+
+class LayerWeights:
+    """Device weights of one layer: fp32 norm weights, bf16 Linear weights [out][in]."""
+
+    def __init__(self, norm1, norm2, q_norm, k_norm, w_qkv, w_out, w_gate, w_up, w_down):
+        self.norm1, self.norm2 = norm1.contiguous(), norm2.contiguous()
+        self.q_norm, self.k_norm = q_norm.contiguous(), k_norm.contiguous()
+        self.w_qkv, self.w_out, self.w_down = w_qkv.contiguous(), w_out.contiguous(), w_down.contiguous()
+        self.w_gu = pack_swiglu(w_gate, w_up)
+        self.D = self.w_out.shape[0]
+        self.F = w_gate.shape[0]
+
+
+class SharedWeights:
+    """Device weights shared by all layers: timestep MLP, shared modulation, head, img_in."""
+
+    def __init__(self, t_w1, t_w2, w_mod, w_scale, w_head, w_in):
+        self.t_w1, self.t_w2, self.w_mod = t_w1.contiguous(), t_w2.contiguous(), w_mod.contiguous()
+        self.w_scale, self.w_head, self.w_in = w_scale.contiguous(), w_head.contiguous(), w_in.contiguous()
+        self.D = self.w_mod.shape[1]
+        self.t_dim = self.t_w1.shape[1]
+        self.latent_ch = self.w_head.shape[0]
+
+
+def gemm(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor, epilogue: int, gate=None, row0: int = 0, P: int = 0):
+    M, K = x.shape
+    N = w.shape[0]
+    assert x.dtype == torch.bfloat16 and w.dtype == torch.bfloat16 and w.shape[1] == K and x.stride(1) == 1
+    assert out.stride(1) == 1 and out.shape[0] == M
+    Q.check(Q.qi_gemm_bf16(x, x.stride(0), w, out, out.stride(0), M, N, K, epilogue, gate, row0, P,
+                           stream_handle(x.device)), "qi_gemm_bf16")
+    return out
+
+
+def norm_mod(x: torch.Tensor, out: torch.Tensor, w=None, scale=None, shift=None, row0: int = 0, P: int = 0,
+             eps: float = 1e-6):
+    M, D = x.shape
+    assert x.dtype == torch.float32 and out.dtype == torch.bfloat16 and x.stride(1) == 1 and out.stride(1) == 1
+    Q.check(Q.qi_zc_rmsnorm_mod(x, x.stride(0), out, out.stride(0), M, D, w, scale, shift, row0, P, eps,
+                                stream_handle(x.device)), "qi_zc_rmsnorm_mod")
+    return out
+
+
+def linear_small(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, silu_in: bool):
+    nv, I = x.shape
+    O_ = w.shape[0]
+    assert x.is_contiguous() and y.is_contiguous() and w.is_contiguous() and y.shape == (nv, O_)
+    Q.check(Q.qi_linear_small(x, nv, I, w, O_, silu_in, y, stream_handle(x.device)), "qi_linear_small")
+    return y
+
+
+class DiT:
+    """The single-stream denoiser around the attention: per-step conditioning, the layer stack
+    (step 1 over the whole sequence filling the prefix caches, then target-only steps), the
+    scale-only head and the Euler update.  All arithmetic runs in libqi kernels; this class owns
+    buffers and issues the calls in order on the current stream."""
+
+    def __init__(self, layout: Layout, shared: SharedWeights, layers, device="cuda", eps: float = 1e-6):
+        self.L, self.sw, self.layers, self.device, self.eps = layout, shared, list(layers), device, eps
+        self.D = shared.D
+        self.H = self.D // 128
+        self.F = self.layers[0].F if self.layers else 0
+        self.attn = Attention(layout, self.H, Q.QI_BF16, device)
+        self.cache = KVCache(len(self.layers), self.H, layout.P, Q.QI_BF16, device)
+        S, D = layout.S, self.D
+        bf, f32 = torch.bfloat16, torch.float32
+        self.x = torch.empty((S, D), dtype=f32, device=device)          # residual stream
+        self.h = torch.empty((S, D), dtype=bf, device=device)           # normed + modulated
+        self.qkv = torch.empty((S, 3 * D), dtype=bf, device=device)
+        self.o = torch.empty((S, self.H, 128), dtype=bf, device=device)
+        self.a = torch.empty((S, max(self.F, 1)), dtype=bf, device=device)  # SwiGLU output
+        self.lat_bf = torch.empty((max(S, 1), shared.latent_ch), dtype=bf, device=device)
+        self.vel = torch.empty((layout.T, shared.latent_ch), dtype=f32, device=device)
+        self.t = torch.zeros(2, dtype=f32, device=device)
+        self.emb = torch.empty((2, shared.t_dim), dtype=f32, device=device)
+        self.t_h = torch.empty((2, D), dtype=f32, device=device)
+        self.temb = torch.empty((2, D), dtype=f32, device=device)
+        self.mods = torch.empty((6, 2, D), dtype=f32, device=device)     # [chunk][prefix | target][D]
+        self.hscale = torch.empty((2, D), dtype=f32, device=device)
+
+    # -- conditioning ------------------------------------------------------------------------
+    def condition(self, sigma: float):
+        """temb for (t = 0, t = 1000 sigma) and the six shared modulation vectors of each."""
+        sw, D = self.sw, self.D
+        self.t.copy_(torch.tensor([0.0, 1000.0 * sigma], dtype=torch.float32))
+        s = stream_handle(self.device)
+        Q.check(Q.qi_timestep_embed(self.t, 2, sw.t_dim, self.emb, s), "qi_timestep_embed")
+        linear_small(self.emb, sw.t_w1, self.t_h, False)
+        linear_small(self.t_h, sw.t_w2, self.temb, True)
+        for c in range(6):
+            linear_small(self.temb, sw.w_mod[c * D:(c + 1) * D], self.mods[c], True)
+        linear_small(self.temb, sw.w_scale, self.hscale, True)
+
+    # -- one layer ---------------------------------------------------------------------------
+    def layer(self, li: int, rows: slice, cached: bool):
+        """Layer li over residual rows [rows): the whole sequence at step 1, the target rows after."""
+        W, D, F, eps = self.layers[li], self.D, self.F, self.eps
+        r0, n, P = rows.start, rows.stop - rows.start, self.L.P
+        x, h, qkv, o, a = self.x[rows], self.h[:n], self.qkv[:n], self.o[:n], self.a[:n]
+        m = self.mods
+        norm_mod(x, h, W.norm1, m[1], m[0], r0, P, eps)
+        gemm(h, W.w_qkv, qkv, Q.QI_EPI_STORE)
+        q = qkv[:, :D].view(n, self.H, 128)
+        k = qkv[:, D:2 * D].view(n, self.H, 128)
+        v = qkv[:, 2 * D:].view(n, self.H, 128)
+        if cached:
+            self.attn.cached(q, k, v, self.cache, li, W.q_norm, W.k_norm, eps, out=o)
+        else:
+            self.attn.full(q, k, v, W.q_norm, W.k_norm, eps, cache=self.cache, layer=li, out=o)
+        gemm(o.view(n, D), W.w_out, x, Q.QI_EPI_GATED_RESIDUAL, m[2], r0, P)
+        norm_mod(x, h, W.norm2, m[4], m[3], r0, P, eps)
+        gemm(h, W.w_gu, a, Q.QI_EPI_SWIGLU)
+        gemm(a, W.w_down, x, Q.QI_EPI_GATED_RESIDUAL, m[5], r0, P)
+
+    # -- inputs, head, Euler -----------------------------------------------------------------
+    def embed(self, lat: torch.Tensor, out: torch.Tensor):
+        """img_in: fp32 latents [n][64] -> bf16 -> fp32 tokens [n][D]."""
+        n = lat.shape[0]
+        Q.check(Q.qi_cast_bf16(lat, self.lat_bf, lat.numel(), stream_handle(self.device)), "qi_cast_bf16")
+        gemm(self.lat_bf[:n], self.sw.w_in, out, Q.QI_EPI_STORE_F32)
+
+    def set_prefix(self, x_text: torch.Tensor, lat_ref: Optional[torch.Tensor]):
+        """Fill the prefix rows of the residual stream in segment order: text rows copied from
+        x_text (fp32 [n_text][D]), reference-image rows written by img_in from lat_ref."""
+        it = ir = row = 0
+        for g in self.L.segments[:-1]:
+            n = g.n_tokens
+            if g.kind == 1:
+                self.embed(lat_ref[ir:ir + n], self.x[row:row + n])
+                ir += n
+            else:
+                self.x[row:row + n].copy_(x_text[it:it + n])
+                it += n
+            row += n
+
+    def head(self, lat: torch.Tensor, sigma_k: float, sigma_k1: float):
+        """Scale-only final norm, the velocity projection, and the Euler update of lat (in place)."""
+        P, T = self.L.P, self.L.T
+        h = self.h[:T]
+        norm_mod(self.x[P:], h, None, self.hscale, None, P, P, self.eps)
+        gemm(h, self.sw.w_head, self.vel, Q.QI_EPI_STORE_F32)
+        euler_step(lat, self.vel, sigma_k, sigma_k1)
+
+    def step(self, k: int, lat: torch.Tensor, sig, x_text=None, lat_ref=None):
+        """Euler step k (0-based) of the loop: step 0 runs the whole sequence and fills the caches."""
+        S, P = self.L.S, self.L.P
+        self.condition(float(sig[k]))
+        self.embed(lat, self.x[P:])
+        if k == 0:
+            self.set_prefix(x_text, lat_ref)
+            for li in range(len(self.layers)):
+                self.layer(li, slice(0, S), False)
+        else:
+            for li in range(len(self.layers)):
+                self.layer(li, slice(P, S), True)
+        self.head(lat, float(sig[k]), float(sig[k + 1]))

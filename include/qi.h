@@ -205,6 +205,51 @@ int qi_euler_step(float* x, const void* v, qi_dtype v_dtype, int64_t n, float si
                   float sigma_k1, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * One single-stream DiT layer step around the attention: norms, projections, FFN, conditioning
+ * ------------------------------------------------------------------------------------------ */
+
+/* Epilogues of qi_gemm_bf16 (y = x W^T, fp32 accumulation):
+ *   QI_EPI_STORE          out bf16 [M][ldo] = y                         (QKV projection)
+ *   QI_EPI_STORE_F32      out fp32 [M][ldo] = y                         (img_in, velocity head)
+ *   QI_EPI_GATED_RESIDUAL out fp32 [M][ldo] += tanh(gate) * y           (attention out-projection,
+ *                         FFN down-projection: the residual tanh gate of [OV] card 5A); gate: device
+ *                         fp32 [2][N], row m uses gate[0] if row0 + m < P (prefix, t = 0 modulation,
+ *                         [OV] card 3B) else gate[1]
+ *   QI_EPI_SWIGLU         out bf16 [M][ldo] with N/2 columns = SiLU(gate) * up ([OV] card 5A);
+ *                         W rows come in blocks of 64: 32 gate rows, then the 32 up rows of the
+ *                         same output features (feature f: gate row 64(f/32) + f%32, up row +32). */
+typedef enum { QI_EPI_STORE = 0, QI_EPI_STORE_F32 = 1, QI_EPI_GATED_RESIDUAL = 2, QI_EPI_SWIGLU = 3 } qi_epilogue;
+
+/* Dense projection on bf16 MFMA: x device bf16 [M][ldx]; w device bf16 [N][K] (the Linear weight,
+ * out x in); K % 64 == 0, N % 64 == 0, M <= 8388480, ldx/ldo multiples of 8, pointers 16-byte
+ * aligned.  gate, row0 and P are used by QI_EPI_GATED_RESIDUAL only (gate may be NULL otherwise).
+ * out must not overlap x or w.  Errors: QI_ERR_ARG (null pointer, unknown epilogue),
+ * QI_ERR_SHAPE, QI_ERR_ALIGN, QI_ERR_HIP (launch). */
+int qi_gemm_bf16(const void* x, int64_t ldx, const void* w, void* out, int64_t ldo, int64_t M, int64_t N,
+                 int64_t K, int epilogue, const float* gate, int64_t row0, int64_t P, void* stream);
+
+/* ZeroCenterRMSNorm with modulation ([1B] sections 1-3: x * rrms * (w + 1), weights stored as
+ * scale - 1, fp32 math; [EDIT] section 5.2: x * (1 + scale) + shift): x device fp32 [M][ldx],
+ * out device bf16 [M][ldo]; w fp32 [D] or NULL (no (w + 1) factor: plain RMS norm); scale and shift
+ * fp32 [2][D] or NULL, row m using index 0 if row0 + m < P (prefix, t = 0) else 1.  D % 4 == 0. */
+int qi_zc_rmsnorm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64_t M, int32_t D, const float* w,
+                      const float* scale, const float* shift, int64_t row0, int64_t P, float eps, void* stream);
+
+/* Sinusoidal timestep embedding ([EDIT] section 5.1: 256 channels, cos half first, frequencies
+ * 10000^(-i/(dim/2))): t device fp32 [n] (the timestep, e.g. 1000 * sigma), out device fp32
+ * [n][dim], dim even. */
+int qi_timestep_embed(const float* t, int32_t n, int32_t dim, float* out, void* stream);
+
+/* Conditioning linear on up to 4 vectors: y[v][o] = sum_i act(x[v][i]) w[o][i], act = SiLU if
+ * silu_in else identity ([EDIT] sections 5.1-5.2: the t-embedding MLP and the modulation Linear
+ * act on SiLU(temb)).  x device fp32 [n_vec][I], w device bf16 [O][I] (I % 8 == 0), y fp32. */
+int qi_linear_small(const float* x, int32_t n_vec, int32_t I, const void* w, int32_t O, int32_t silu_in, float* y,
+                    void* stream);
+
+/* fp32 -> bf16 (nearest even) of n elements (latents into the img_in projection). */
+int qi_cast_bf16(const float* x, void* y, int64_t n, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * Measurement hooks
  * ------------------------------------------------------------------------------------------ */
 

@@ -8,7 +8,7 @@ out from the pages, in NumPy float64, slow and obvious on purpose.
 
 Sources (cited by page title and section):
   [OV]   "Qwen-Image-2.1: how an image is made from noise" course overview
-         (OpenArchLab), lesson list and block cards 3A, 3B, 3C, 4A, 6A, 6B.
+         (OpenArchLab), lesson list and block cards 1A, 2A, 3A, 3B, 3C, 4A, 5A, 6A, 6B.
   [1B]   "1B - Qwen3-VL Context & Zero-Center RMSNorm" (OpenArchLab), sections 1-4.
   [3A]   "3A - 3D Axial RoPE (16, 56, 56) & Zero-Centered Grid" (OpenArchLab), sections 1-4.
   [EDIT] "QwenImageTransformer2DModel source reading (Qwen-Image-Edit)", sections
@@ -308,3 +308,161 @@ def euler(x: np.ndarray, v: np.ndarray, sigma_k: float, sigma_k1: float) -> np.n
 def visible_pairs(segments) -> int:
     """Number of visible (query, key) pairs per head for step 1, counted from the dense mask."""
     return int(mask_dense(segments).sum())
+
+
+# ------------------------------------------------------------------------------------------------
+# one single-stream DiT layer around the attention (the full-layer workload)
+# ------------------------------------------------------------------------------------------------
+
+def silu(x):
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def timestep_embedding(t, dim: int = 256, max_period: float = 10000.0) -> np.ndarray:
+    """Sinusoidal timestep embedding ([EDIT] section 5.1: 256 channels, frequencies
+    max_period^(-i/(dim/2)), cos half first).  t: array of timesteps (1000 * sigma here)."""
+    t = np.atleast_1d(np.asarray(t, dtype=np.float64))
+    half = dim // 2
+    freqs = np.array([math.exp(-math.log(max_period) * i / half) for i in range(half)])
+    arg = t[:, None] * freqs[None, :]
+    return np.concatenate([np.cos(arg), np.sin(arg)], axis=1)
+
+
+def linear(x, w):
+    """y = x W^T with W in the Linear layout [out][in]."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
+
+
+def time_condition(sigma, w1, w2) -> np.ndarray:
+    """temb = W2 SiLU(W1 emb(1000 sigma)) ([EDIT] section 5.1: timestep embedding, Linear, SiLU,
+    Linear; no biases in this random-init reading)."""
+    return linear(silu(linear(timestep_embedding(1000.0 * np.atleast_1d(sigma)), w1)), w2)
+
+
+def modulation(temb, wm, d: int):
+    """Shared modulation ([OV] card 3B, one modulator for all layers): W_mod SiLU(temb) split into
+    (shift1, scale1, gate1, shift2, scale2, gate2), each [n, d] ([EDIT] section 5.2 order)."""
+    m = linear(silu(temb), wm)
+    return tuple(m[:, i * d:(i + 1) * d] for i in range(6))
+
+
+def norm_mod(x, w, scale, shift, eps: float = 1e-6):
+    """ZeroCenterRMSNorm then x (1 + scale) + shift ([1B] sections 1-3; [EDIT] section 5.2)."""
+    y = zero_center_rms_norm(x, w, eps) if w is not None else rms_norm(x, None, eps)
+    if scale is not None:
+        y = y * (1.0 + scale)
+    if shift is not None:
+        y = y + shift
+    return y
+
+
+def per_row(vec_prefix, vec_target, n_rows: int, row0: int, P: int):
+    """Per-row parameters: rows with global index < P (prefix) take the t = 0 values, the rest the
+    current step's ([OV] card 3B: prefix at t = 0, target at t)."""
+    rows = np.arange(row0, row0 + n_rows)
+    return np.where((rows < P)[:, None], np.asarray(vec_prefix)[None, :], np.asarray(vec_target)[None, :])
+
+
+def swiglu(g, u):
+    """SiLU(gate) * up ([OV] card 5A)."""
+    return silu(g) * np.asarray(u, dtype=np.float64)
+
+
+def dit_layer(x, L, mods, segments, cos_t, sin_t, cache=None, eps: float = 1e-6,
+              tanh_gate: bool = True):
+    """One single-stream DiT layer ([OV] cards 4A, 5A; [EDIT] sections 5.2 and 6 for the order):
+        h  = ZeroCenterRMSNorm(x) (1 + scale1) + shift1
+        q, k, v = h W_qkv^T, per-head QK-RMSNorm, 3D RoPE
+        x += tanh(gate1) * (Attention(q, k, v) W_out^T)
+        h2 = ZeroCenterRMSNorm(x) (1 + scale2) + shift2
+        x += tanh(gate2) * ((SiLU(h2 W_gate^T) * (h2 W_up^T)) W_down^T)
+    Step 1 (cache None): x holds all S tokens, block-causal attention, returns (x_out, (K, V)) with
+    the prefix K (normalised, rotated) and V.  Cached step: x holds the T target tokens, cache the
+    prefix K/V; returns (x_out, None).  mods: (prefix_params, target_params), each the six
+    modulation vectors; L: dict of layer weights; tanh_gate False gives the plain gate of the
+    v1 model."""
+    x = np.asarray(x, dtype=np.float64)
+    S, P, T = split_counts(segments)
+    n = x.shape[0]
+    row0 = 0 if cache is None else P
+    D = x.shape[1]
+    H = D // HEAD_DIM
+    (sh1p, sc1p, g1p, sh2p, sc2p, g2p), (sh1t, sc1t, g1t, sh2t, sc2t, g2t) = mods
+    pr = lambda a, b: per_row(a, b, n, row0, P)
+    gate = (lambda g: np.tanh(g)) if tanh_gate else (lambda g: g)
+    h = norm_mod(x, L["norm1"], pr(sc1p, sc1t), pr(sh1p, sh1t), eps)
+    qkv = linear(h, L["w_qkv"]).reshape(n, 3, H, HEAD_DIM)
+    q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+    c, s = cos_t[row0:row0 + n], sin_t[row0:row0 + n]
+    if cache is None:
+        o, new_cache = step1(q, k, v, segments, c, s, L["q_norm"], L["k_norm"], eps)
+    else:
+        o = cached_step(q, k, v, cache, c, s, L["q_norm"], L["k_norm"], eps)
+        new_cache = None
+    x = x + gate(pr(g1p, g1t)) * linear(o.reshape(n, D), L["w_out"])
+    h2 = norm_mod(x, L["norm2"], pr(sc2p, sc2t), pr(sh2p, sh2t), eps)
+    a = swiglu(linear(h2, L["w_gate"]), linear(h2, L["w_up"]))
+    x = x + gate(pr(g2p, g2t)) * linear(a, L["w_down"])
+    return x, new_cache
+
+
+def velocity_head(x_t, temb, w_scale, w_head, eps: float = 1e-6):
+    """Scale-only final AdaLN and the 64-channel velocity projection ([OV] card 6B):
+    v = (RMSNorm(x) (1 + W_scale SiLU(temb))) W_head^T."""
+    scale = linear(silu(temb), w_scale)
+    return linear(rms_norm(x_t, None, eps) * (1.0 + scale), w_head)
+
+
+def img_in(latent, w_in):
+    """Latent cell (64 channels) -> one DiT token ([OV] card 1A; no bias in this reading)."""
+    return linear(latent, w_in)
+
+
+def prefix_states(segments, x_text, ref_tokens):
+    """Hidden states of the prefix in sequence order: text segments take consecutive rows of
+    x_text, reference images consecutive rows of ref_tokens ([OV] card 2A joint packing)."""
+    rows, it, ir = [], 0, 0
+    for g in segments[:-1]:
+        if g.kind == SEG_IMAGE:
+            rows.append(ref_tokens[ir:ir + g.n_tokens])
+            ir += g.n_tokens
+        else:
+            rows.append(x_text[it:it + g.n_tokens])
+            it += g.n_tokens
+    return np.concatenate(rows, axis=0) if rows else np.zeros((0, x_text.shape[1]))
+
+
+def denoise(segments, x_text, lat_ref, lat0, shared, layers, n_steps: int, eps: float = 1e-6,
+            return_velocities: bool = False):
+    """The Euler sampling loop with the prefix KV cache ([OV] cards 3B, 6A, 6B): step 1 runs every
+    layer over the whole sequence (prefix at t = 0, target at t = 1000 sigma_0) and keeps each
+    layer's prefix K/V; steps 2..n run only the target tokens against those caches.  After each
+    step the target's velocity (scale-only final norm, 64-channel head) moves the latent by
+    (sigma_{k+1} - sigma_k) v.  shared: t_w1, t_w2, w_mod, w_scale, w_head, w_in (fp64 arrays);
+    layers: list of per-layer weight dicts.  Returns the final latent (and the velocities)."""
+    S, P, T = split_counts(segments)
+    D = shared["w_mod"].shape[1]
+    c, s = rope_tables(positions(segments))
+    sig = np.array([1.0 - k / n_steps for k in range(n_steps + 1)])
+    lat = np.asarray(lat0, dtype=np.float64).copy()
+    caches = [None] * len(layers)
+    vels = []
+    for k in range(n_steps):
+        temb = time_condition(np.array([0.0, sig[k]]), shared["t_w1"], shared["t_w2"])
+        mod = modulation(temb, shared["w_mod"], D)
+        mods = (tuple(m[0] for m in mod), tuple(m[1] for m in mod))
+        xt = img_in(lat, shared["w_in"])
+        if k == 0:
+            x = np.concatenate([prefix_states(segments, x_text, img_in(lat_ref, shared["w_in"])), xt], axis=0)
+            for li, L in enumerate(layers):
+                x, caches[li] = dit_layer(x, L, mods, segments, c, s, eps=eps)
+            x_t = x[P:]
+        else:
+            x_t = xt
+            for li, L in enumerate(layers):
+                x_t, _ = dit_layer(x_t, L, mods, segments, c, s, cache=caches[li], eps=eps)
+        v = velocity_head(x_t, temb[1:2], shared["w_scale"], shared["w_head"], eps)
+        vels.append(v)
+        lat = euler(lat, v, sig[k], sig[k + 1])
+    return (lat, vels) if return_velocities else lat

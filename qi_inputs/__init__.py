@@ -22,6 +22,7 @@ page, section 8.2 shape table):
 from __future__ import annotations
 
 import dataclasses
+import math
 from typing import List, Sequence, Tuple
 
 import numpy as np
@@ -162,3 +163,65 @@ def qk_norm_weights(wl: Workload, layer: int = 0) -> Tuple[np.ndarray, np.ndarra
 def sigmas(n_steps: int) -> np.ndarray:
     """Euler sigma schedule sigma_k = 1 - k/n_steps, k = 0..n_steps (fp64), the linspace(1, 0, n+1) grid."""
     return np.array([1.0 - k / n_steps for k in range(n_steps + 1)], dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------------------------
+# random-init weights and inputs of the full single-stream layer workload
+# ----------------------------------------------------------------------------------------------
+
+# weight indices (tensor id = T_WEIGHT_BASE + index); per layer:
+W_NORM1, W_NORM2, W_QNORM, W_KNORM, W_QKV, W_OUT, W_GATE, W_UP, W_DOWN = range(9)
+# shared (layer 0): timestep MLP, modulation, head scale, velocity head, img_in, prefix inputs
+W_T1, W_T2, W_MOD, W_HSCALE, W_HEAD, W_IN, X_TEXT, LAT_REF, LAT_TGT = range(20, 29)
+
+
+def linear_weight(cfg_id: int, index: int, n_out: int, n_in: int, layer: int = 0) -> Stored:
+    """A Linear weight [n_out][n_in] ~ N(0, 1/n_in), stored bf16."""
+    return stored(normal(cfg_id, T_WEIGHT_BASE + index, (n_out, n_in), 0, layer, 0.0, 1.0 / math.sqrt(n_in)), "bf16")
+
+
+def f32_vector(cfg_id: int, index: int, shape, layer: int = 0, mean: float = 0.0, std: float = 1.0) -> np.ndarray:
+    """fp32-stored draws, returned as fp64 values."""
+    return normal(cfg_id, T_WEIGHT_BASE + index, shape, 0, layer, mean, std).astype(np.float32).astype(np.float64)
+
+
+def layer_weights(cfg_id: int, D: int, F: int, layer: int) -> dict:
+    """Random-init weights of one single-stream layer: ZeroCenterRMSNorm weights N(0, 0.02^2)
+    (stored as scale - 1), QK-RMSNorm weights 1 + N(0, 0.02^2), Linear weights N(0, 1/fan_in) in
+    bf16 (QKV [3D][D] in q | k | v order, out [D][D], gate and up [F][D], down [D][F])."""
+    return {
+        "norm1": f32_vector(cfg_id, W_NORM1, (D,), layer, 0.0, 0.02),
+        "norm2": f32_vector(cfg_id, W_NORM2, (D,), layer, 0.0, 0.02),
+        "q_norm": f32_vector(cfg_id, W_QNORM, (128,), layer, 1.0, 0.02),
+        "k_norm": f32_vector(cfg_id, W_KNORM, (128,), layer, 1.0, 0.02),
+        "w_qkv": linear_weight(cfg_id, W_QKV, 3 * D, D, layer),
+        "w_out": linear_weight(cfg_id, W_OUT, D, D, layer),
+        "w_gate": linear_weight(cfg_id, W_GATE, F, D, layer),
+        "w_up": linear_weight(cfg_id, W_UP, F, D, layer),
+        "w_down": linear_weight(cfg_id, W_DOWN, D, F, layer),
+    }
+
+
+def shared_weights(cfg_id: int, D: int, t_dim: int = 256, latent_ch: int = 64) -> dict:
+    """Random-init conditioning and projection weights shared by all layers (bf16)."""
+    return {
+        "t_w1": linear_weight(cfg_id, W_T1, D, t_dim),
+        "t_w2": linear_weight(cfg_id, W_T2, D, D),
+        "w_mod": linear_weight(cfg_id, W_MOD, 6 * D, D),
+        "w_scale": linear_weight(cfg_id, W_HSCALE, D, D),
+        "w_head": linear_weight(cfg_id, W_HEAD, latent_ch, D),
+        "w_in": linear_weight(cfg_id, W_IN, D, latent_ch),
+    }
+
+
+def prefix_inputs(cfg_id: int, n_text: int, n_ref: int, D: int, latent_ch: int = 64):
+    """Text hidden states [n_text][D] (fp32, N(0,1): stand-in for the projected VLM context) and
+    clean reference latents [n_ref][latent_ch] (fp32, N(0,1))."""
+    xt = f32_vector(cfg_id, X_TEXT, (n_text, D))
+    lr = f32_vector(cfg_id, LAT_REF, (n_ref, latent_ch))
+    return xt, lr
+
+
+def target_noise(cfg_id: int, T: int, latent_ch: int = 64) -> np.ndarray:
+    """The target latent at sigma = 1: N(0,1) fp32 [T][latent_ch]."""
+    return f32_vector(cfg_id, LAT_TGT, (T, latent_ch))

@@ -1,0 +1,438 @@
+"""GPU parity of the single-stream layer pieces around the attention (projection GEMMs with their
+epilogues, ZeroCenterRMSNorm + modulation, timestep embedding, conditioning linears, bf16 cast),
+of one whole layer (step 1 and cached step), and of a small sampling loop, all called through the
+C ABI and checked against the fp64 oracle on the same seeded inputs.
+
+Tolerances (written here, per output tensor):
+  bf16 outputs (and fp32 outputs of a chain that passes bf16 intermediates):
+        max|d| <= 1e-2 * max|ref|  and  sum|d| / sum|ref| <= 2e-3
+  fp32 outputs of one fp32-accumulated step on stored inputs:
+        max|d| <= 1e-5 * max|ref|  and  sum|d| / sum|ref| <= 1e-5
+  chained bf16 (a result computed through k bf16-rounded intermediates in sequence, each held
+  to the bf16 bar: the layer's residual increment passes h, qkv, o and h2/a, k = 4; the first
+  velocity passes two layers and the head): independent roundings add in quadrature, so
+        max|d| <= 1e-2 * max|ref|  and  sum|d| / sum|ref| <= 2e-3 * sqrt(k) + 1e-3 = 5e-3 (k = 4)
+  timestep embedding (fp64 in the kernel, one fp32 rounding): max|d| <= 2e-7
+  bf16 cast: bit-exact (round to nearest even)
+The one-layer parity feeds the oracle the GPU's layer input (and the GPU's modulation vectors),
+so errors of earlier layers do not count twice; it holds the layer output to the bf16 bar and its
+residual increment to the chained bar.  The sampling loop holds the first step's velocity to the
+chained bar and the final latent to the bf16 bar, and reports the later velocities.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import qi_inputs as qin
+from oracle import qi_oracle as O
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from image_generation_qi_amd import qi as Q  # noqa: E402
+from image_generation_qi_amd import runtime as rt  # noqa: E402
+
+DEV = "cuda:0"
+CFG = 91   # seed id of the ad-hoc shapes here
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check(got, ref, bar, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    d = np.abs(got - ref)
+    max_rel = d.max() / max(np.abs(ref).max(), 1e-300)
+    mean_rel = d.sum() / max(np.abs(ref).sum(), 1e-300)
+    lim_max, lim_mean = {"bf16": (1e-2, 2e-3), "f32": (1e-5, 1e-5), "chain": (1e-2, 5e-3)}[bar]
+    say(f"  {what}: max_rel={max_rel:.3e} mean_rel={mean_rel:.3e}")
+    assert max_rel <= lim_max and mean_rel <= lim_mean, (what, max_rel, mean_rel)
+    return max_rel, mean_rel
+
+
+def bf(st: qin.Stored) -> torch.Tensor:
+    return rt.from_bits(st.bits, "bf16", DEV)
+
+
+def f32(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------------------------------------
+# GEMM epilogues
+# ------------------------------------------------------------------------------------------------
+
+GEMM_SHAPES = [(300, 192, 320), (1, 64, 64), (129, 128, 128), (257, 256, 64), (64, 320, 192)]
+
+
+def gemm_inputs(M, N, K, tag=0):
+    x = qin.stored(qin.normal(CFG, 200 + tag, (M, K)), "bf16")
+    w = qin.linear_weight(CFG, 40 + tag, N, K)
+    return x, w
+
+
+def padded(rows, cols, ld, dtype, fill):
+    """A [rows][cols] view with leading dimension ld inside a buffer with 3 spare rows, all
+    filled with `fill` so that writes outside the view can be detected."""
+    buf = torch.full((rows + 3, ld), fill, dtype=dtype, device=DEV)
+    return buf, buf[:rows, :cols]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_store_and_store_f32(M, N, K):
+    say(f"[gemm store] M={M} N={N} K={K}")
+    x, w = gemm_inputs(M, N, K)
+    ref = O.linear(x.f64, w.f64)
+    # x with a wider leading dimension, outputs padded to catch stray writes
+    xbuf = torch.zeros((M, K + 64), dtype=torch.bfloat16, device=DEV)
+    xbuf[:, :K] = bf(x)
+    xv = xbuf[:, :K]
+    for epi, dt, bar in ((Q.QI_EPI_STORE, torch.bfloat16, "bf16"), (Q.QI_EPI_STORE_F32, torch.float32, "f32")):
+        buf, out = padded(M, N, N + 8, dt, 7.0)
+        rt.gemm(xv, bf(w), out, epi)
+        sync()
+        check(host(out), ref, bar, f"epi {epi}")
+        assert torch.all(buf[:M, N:] == 7.0) and torch.all(buf[M:] == 7.0), "write outside the output view"
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_gated_residual(M, N, K):
+    say(f"[gemm gated residual] M={M} N={N} K={K}")
+    x, w = gemm_inputs(M, N, K, 1)
+    x0 = qin.normal(CFG, 210, (M, N)).astype(np.float32).astype(np.float64)
+    gate = qin.normal(CFG, 211, (2, N), std=0.7).astype(np.float32).astype(np.float64)
+    for row0, P in ((0, M // 3), (50, 60), (0, 0), (M, M)):
+        y = O.linear(x.f64, w.f64)
+        g = O.per_row(gate[0], gate[1], M, row0, P)
+        ref = x0 + np.tanh(g) * y
+        buf, out = padded(M, N, N + 8, torch.float32, 5.0)
+        out.copy_(f32(x0))
+        rt.gemm(bf(x), bf(w), out, Q.QI_EPI_GATED_RESIDUAL, f32(gate), row0, P)
+        sync()
+        check(host(out), ref, "f32", f"row0={row0} P={P}")
+        assert torch.all(buf[:M, N:] == 5.0) and torch.all(buf[M:] == 5.0)
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_swiglu(M, N, K):
+    say(f"[gemm swiglu] M={M} 2F={N} K={K}")
+    F = N // 2
+    x = qin.stored(qin.normal(CFG, 220, (M, K)), "bf16")
+    wg = qin.linear_weight(CFG, 50, F, K)
+    wu = qin.linear_weight(CFG, 51, F, K)
+    ref = O.swiglu(O.linear(x.f64, wg.f64), O.linear(x.f64, wu.f64))
+    buf, out = padded(M, F, F + 8, torch.bfloat16, 3.0)
+    rt.gemm(bf(x), rt.pack_swiglu(bf(wg), bf(wu)), out, Q.QI_EPI_SWIGLU)
+    sync()
+    check(host(out), ref, "bf16", "swiglu")
+    assert torch.all(buf[:M, F:] == 3.0) and torch.all(buf[M:] == 3.0)
+
+
+def test_gemm_argument_errors():
+    x = torch.zeros((8, 64), dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros((64, 64), dtype=torch.bfloat16, device=DEV)
+    o = torch.zeros((8, 64), dtype=torch.float32, device=DEV)
+    s = rt.stream_handle(DEV)
+    assert Q.qi_gemm_bf16(x, 64, w, o, 64, 8, 64, 64, Q.QI_EPI_GATED_RESIDUAL, None, 0, 0, s) == Q.QI_ERR_ARG
+    assert Q.qi_gemm_bf16(x, 64, w, o, 64, 8, 96, 64, Q.QI_EPI_STORE_F32, None, 0, 0, s) == Q.QI_ERR_SHAPE
+    assert Q.qi_gemm_bf16(x, 64, w, o, 64, 8, 64, 32, Q.QI_EPI_STORE_F32, None, 0, 0, s) == Q.QI_ERR_SHAPE
+    assert Q.qi_gemm_bf16(x, 60, w, o, 64, 8, 64, 64, Q.QI_EPI_STORE_F32, None, 0, 0, s) == Q.QI_ERR_SHAPE
+    assert Q.qi_gemm_bf16(x, 64, w, o, 64, 8, 64, 64, 9, None, 0, 0, s) == Q.QI_ERR_ARG
+    assert Q.qi_gemm_bf16(x, 64, w, o, 64, 0, 64, 64, Q.QI_EPI_STORE_F32, None, 0, 0, s) == Q.QI_OK
+
+
+# full-size projections of one layer of the 14,848-token workload (hidden 3072, FFN 8192), on
+# sampled rows: the cached-step row count (4096) and the step-1 row count (14,848)
+FULL = [("qkv", 4096, 9216, 3072, Q.QI_EPI_STORE), ("out", 4096, 3072, 3072, Q.QI_EPI_GATED_RESIDUAL),
+        ("gate_up", 4096, 16384, 3072, Q.QI_EPI_SWIGLU), ("down", 4096, 3072, 8192, Q.QI_EPI_GATED_RESIDUAL),
+        ("qkv_step1", 14848, 9216, 3072, Q.QI_EPI_STORE)]
+
+
+@pytest.mark.parametrize("name,M,N,K,epi", FULL)
+def test_gemm_full_size_sampled(name, M, N, K, epi):
+    say(f"[gemm full] {name} M={M} N={N} K={K}")
+    x = qin.stored(qin.normal(CFG, 230, (M, K)), "bf16")
+    rows = np.unique(np.concatenate([[0, M - 1], qin.rng(CFG, 231).integers(0, M, 40)]))
+    if epi == Q.QI_EPI_SWIGLU:
+        F = N // 2
+        wg, wu = qin.linear_weight(CFG, 52, F, K), qin.linear_weight(CFG, 53, F, K)
+        out = torch.empty((M, F), dtype=torch.bfloat16, device=DEV)
+        rt.gemm(bf(x), rt.pack_swiglu(bf(wg), bf(wu)), out, epi)
+        ref = O.swiglu(O.linear(x.f64[rows], wg.f64), O.linear(x.f64[rows], wu.f64))
+        bar = "bf16"
+    else:
+        w = qin.linear_weight(CFG, 54, N, K)
+        y = O.linear(x.f64[rows], w.f64)
+        if epi == Q.QI_EPI_STORE:
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+            rt.gemm(bf(x), bf(w), out, epi)
+            ref, bar = y, "bf16"
+        else:
+            P = M // 4
+            x0 = qin.normal(CFG, 232, (M, N)).astype(np.float32).astype(np.float64)
+            gate = qin.normal(CFG, 233, (2, N), std=0.7).astype(np.float32).astype(np.float64)
+            out = f32(x0)
+            rt.gemm(bf(x), bf(w), out, epi, f32(gate), 0, P)
+            ref = x0[rows] + np.tanh(O.per_row(gate[0], gate[1], M, 0, P)[rows]) * y
+            bar = "f32"
+    sync()
+    check(host(out)[rows], ref, bar, name)
+
+
+# ------------------------------------------------------------------------------------------------
+# norm + modulation, timestep embedding, conditioning linears, cast
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,D,row0,P,parts", [(300, 3072, 0, 170, "wss"), (129, 256, 40, 100, "wss"),
+                                              (77, 132, 0, 0, "w"), (5, 3072, 10, 0, "s"),
+                                              (64, 512, 0, 64, "")])
+def test_zc_rmsnorm_mod(M, D, row0, P, parts):
+    say(f"[norm mod] M={M} D={D} row0={row0} P={P} parts={parts!r}")
+    x = qin.normal(CFG, 240, (M, D), std=3.0).astype(np.float32).astype(np.float64)
+    w = qin.normal(CFG, 241, (D,), std=0.02).astype(np.float32).astype(np.float64) if "w" in parts else None
+    sc = qin.normal(CFG, 242, (2, D), std=0.3).astype(np.float32).astype(np.float64) if "s" in parts else None
+    sh = qin.normal(CFG, 243, (2, D), std=0.3).astype(np.float32).astype(np.float64) if parts.count("s") > 1 else None
+    ref = O.norm_mod(x, w, None if sc is None else O.per_row(sc[0], sc[1], M, row0, P),
+                     None if sh is None else O.per_row(sh[0], sh[1], M, row0, P))
+    buf, out = padded(M, D, D + 4, torch.bfloat16, 9.0)
+    rt.norm_mod(f32(x), out, None if w is None else f32(w), None if sc is None else f32(sc),
+                None if sh is None else f32(sh), row0, P)
+    sync()
+    check(host(out), ref, "bf16", "norm_mod")
+    assert torch.all(buf[:M, D:] == 9.0) and torch.all(buf[M:] == 9.0)
+
+
+def test_timestep_embed():
+    t = np.concatenate([1000.0 * qin.sigmas(8), [0.5, 999.9, 123.456]]).astype(np.float32)
+    out = torch.empty((len(t), 256), dtype=torch.float32, device=DEV)
+    Q.check(Q.qi_timestep_embed(f32(t), len(t), 256, out, rt.stream_handle(DEV)), "qi_timestep_embed")
+    sync()
+    ref = O.timestep_embedding(t.astype(np.float64))
+    err = np.abs(host(out) - ref).max()
+    say(f"  timestep embed max abs err {err:.2e}")
+    assert err <= 2e-7
+
+
+@pytest.mark.parametrize("nv,I,O_,silu", [(2, 256, 3072, False), (2, 3072, 3072, True), (1, 8, 5, True),
+                                           (4, 520, 70, False), (3, 3072, 18432, True)])
+def test_linear_small(nv, I, O_, silu):
+    say(f"[linear small] nv={nv} I={I} O={O_} silu={silu}")
+    x = qin.normal(CFG, 250, (nv, I), std=2.0).astype(np.float32).astype(np.float64)
+    w = qin.linear_weight(CFG, 60, O_, I)
+    y = torch.empty((nv, O_), dtype=torch.float32, device=DEV)
+    rt.linear_small(f32(x), bf(w), y, silu)
+    sync()
+    ref = O.linear(O.silu(x) if silu else x, w.f64)
+    check(host(y), ref, "f32", "linear_small")
+
+
+def test_cast_bf16_bit_exact():
+    vals = np.concatenate([
+        qin.normal(CFG, 260, (5000,), std=100.0),
+        [0.0, -0.0, np.inf, -np.inf, 1e-40, -1e-42, 3.0e38, 3.3961776e38, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8,
+         1.0 + 2 ** -8 + 2 ** -20, 65504.0, 2 ** -126, 2 ** -133]]).astype(np.float32)
+    n = len(vals)
+    y = torch.empty(n + 5, dtype=torch.bfloat16, device=DEV)
+    y.fill_(1.0)
+    Q.check(Q.qi_cast_bf16(f32(vals), y, n, rt.stream_handle(DEV)), "qi_cast_bf16")
+    sync()
+    got = y.cpu().view(torch.int16).numpy().view(np.uint16)
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got[:n], ref)
+    assert np.all(got[n:] == 0x3F80)
+    nanv = np.array([np.nan, -np.nan], dtype=np.float32)
+    yn = torch.empty(2, dtype=torch.bfloat16, device=DEV)
+    Q.check(Q.qi_cast_bf16(f32(nanv), yn, 2, rt.stream_handle(DEV)), "qi_cast_bf16")
+    sync()
+    assert torch.all(torch.isnan(yn.float().cpu()))
+
+
+# ------------------------------------------------------------------------------------------------
+# one whole layer, the conditioning, and a small sampling loop
+# ------------------------------------------------------------------------------------------------
+
+def make_model(segments, D, F, n_layers, cfg=CFG):
+    layout = rt.Layout(segments, DEV)
+    sw_np = qin.shared_weights(cfg, D)
+    lw_np = [qin.layer_weights(cfg, D, F, l) for l in range(n_layers)]
+    sw = rt.SharedWeights(*(bf(sw_np[k]) for k in ("t_w1", "t_w2", "w_mod", "w_scale", "w_head", "w_in")))
+    layers = [rt.LayerWeights(f32(L["norm1"]), f32(L["norm2"]), f32(L["q_norm"]), f32(L["k_norm"]),
+                              bf(L["w_qkv"]), bf(L["w_out"]), bf(L["w_gate"]), bf(L["w_up"]), bf(L["w_down"]))
+              for L in lw_np]
+    model = rt.DiT(layout, sw, layers, DEV)
+    shared64 = {k: v.f64 for k, v in sw_np.items()}
+    layers64 = [{k: (v.f64 if isinstance(v, qin.Stored) else v) for k, v in L.items()} for L in lw_np]
+    return model, shared64, layers64
+
+
+SMALL = (qin.text(37), qin.image(9, 7, 1), qin.image(11, 13, 0))
+
+
+@pytest.mark.parametrize("sigma", [1.0, 0.375])
+def test_condition(sigma):
+    model, sh, _ = make_model(SMALL, 256, 512, 1)
+    model.condition(sigma)
+    sync()
+    temb = O.time_condition(np.array([0.0, sigma]), sh["t_w1"], sh["t_w2"])
+    mods = O.modulation(temb, sh["w_mod"], 256)
+    for c in range(6):
+        check(host(model.mods[c]), mods[c], "f32", f"mod chunk {c}")
+    check(host(model.hscale), O.linear(O.silu(temb), sh["w_scale"]), "f32", "head scale")
+
+
+def gpu_mods(model):
+    m = host(model.mods)
+    return tuple(m[c][0] for c in range(6)), tuple(m[c][1] for c in range(6))
+
+
+@pytest.mark.parametrize("segments,D,F", [(SMALL, 256, 512), ((qin.text(130), qin.image(8, 16, 1), qin.text(3),
+                                                             qin.image(10, 10, 2), qin.image(16, 9, 0)), 384, 320)])
+def test_layer_step1_and_cached(segments, D, F):
+    say(f"[layer] S={sum(g.n_tokens for g in segments)} D={D} F={F}")
+    model, sh, layers64 = make_model(segments, D, F, 1)
+    L = model.L
+    S, P, T = L.S, L.P, L.T
+    c, s = O.rope_tables(O.positions(segments))
+    model.condition(1.0)
+    x_in = qin.normal(CFG, 270, (S, D)).astype(np.float32)
+    model.x.copy_(f32(x_in))
+    model.layer(0, slice(0, S), False)
+    sync()
+    mods = gpu_mods(model)
+    ref, cache = O.dit_layer(x_in.astype(np.float64), layers64[0], mods, segments, c, s)
+    check(host(model.x), ref, "bf16", "step-1 layer output")
+    check(host(model.x) - x_in, ref - x_in, "chain", "step-1 layer increment")
+    # cached step: new target rows, the prefix K/V from step 1
+    model.condition(0.625)
+    xt_in = qin.normal(CFG, 271, (T, D)).astype(np.float32)
+    model.x[P:].copy_(f32(xt_in))
+    model.layer(0, slice(P, S), True)
+    sync()
+    mods = gpu_mods(model)
+    ref_t, _ = O.dit_layer(xt_in.astype(np.float64), layers64[0], mods, segments, c, s, cache=cache)
+    check(host(model.x[P:]), ref_t, "bf16", "cached layer output")
+    check(host(model.x[P:]) - xt_in, ref_t - xt_in, "chain", "cached layer increment")
+
+
+def test_cached_layer_equals_step1_target_rows_bitwise():
+    # the same target input through step 1 (whole sequence) and through the cached path gives the
+    # same target rows, bit for bit: the prefix K/V in the cache are the ones step 1 used
+    model, _, _ = make_model(SMALL, 256, 512, 1)
+    S, P = model.L.S, model.L.P
+    model.condition(0.5)
+    x_in = f32(qin.normal(CFG, 272, (S, 256)))
+    model.x.copy_(x_in)
+    model.layer(0, slice(0, S), False)
+    full_t = model.x[P:].clone()
+    model.x.copy_(x_in)
+    model.layer(0, slice(P, S), True)
+    sync()
+    assert torch.equal(model.x[P:], full_t)
+
+
+def test_sampling_loop_small():
+    segments = (qin.text(20), qin.image(6, 5, 1), qin.image(7, 6, 0))
+    D, F, n_layers, n_steps = 256, 512, 2, 3
+    model, sh, layers64 = make_model(segments, D, F, n_layers)
+    L = model.L
+    n_text = 20
+    x_text, lat_ref = qin.prefix_inputs(CFG, n_text, 30, D)
+    lat0 = qin.target_noise(CFG, L.T)
+    sig = qin.sigmas(n_steps)
+    lat = f32(lat0)
+    vels = []
+    xt, lr = f32(x_text), f32(lat_ref)
+    for k in range(n_steps):
+        model.step(k, lat, sig, xt, lr)
+        vels.append(host(model.vel))
+    sync()
+    ref_lat, ref_vels = O.denoise(segments, x_text, lat_ref, lat0, sh, layers64, n_steps, return_velocities=True)
+    check(vels[0], ref_vels[0], "chain", "velocity step 1")
+    for k in range(1, n_steps):
+        d = np.abs(vels[k] - ref_vels[k])
+        say(f"  velocity step {k + 1}: max_rel={d.max() / np.abs(ref_vels[k]).max():.3e} "
+            f"mean_rel={d.sum() / np.abs(ref_vels[k]).sum():.3e} (reported)")
+    check(host(lat), ref_lat, "bf16", "final latent")
+
+
+# ------------------------------------------------------------------------------------------------
+# a full-size layer of the 14,848-token workload, stage by stage on sampled rows
+# ------------------------------------------------------------------------------------------------
+
+def test_full_size_layer_stages_sampled():
+    wl = qin.WORKLOADS["cfg4"]
+    D, F, H = 3072, 8192, 24
+    say(f"[layer full] S={wl.S} P={wl.P} T={wl.T}")
+    model, sh, layers64 = make_model(wl.segments, D, F, 1, cfg=wl.cfg_id)
+    W = layers64[0]
+    Lw = model.layers[0]
+    S, P, T = wl.S, wl.P, wl.T
+    c, s = O.rope_tables(O.positions(wl.segments))
+    rows = np.unique(np.concatenate([[0, P - 1, P, S - 1], qin.rng(CFG, 280).integers(0, S, 28)]))
+    model.condition(1.0)
+    x_in = qin.normal(CFG, 281, (S, D)).astype(np.float32)
+    model.x.copy_(f32(x_in))
+    mods = gpu_mods(model)
+    m = model.mods
+    sel = lambda i, r: O.per_row(mods[0][i], mods[1][i], S, 0, P)[r]
+    # norm1 + modulation
+    h = model.h
+    rt.norm_mod(model.x, h, Lw.norm1, m[1], m[0], 0, P)
+    sync()
+    x64 = x_in.astype(np.float64)
+    ref_h = O.norm_mod(x64[rows], W["norm1"], sel(1, rows), sel(0, rows))
+    check(host(h[rows]), ref_h, "bf16", "norm1+mod")
+    # QKV projection
+    rt.gemm(h, Lw.w_qkv, model.qkv, Q.QI_EPI_STORE)
+    sync()
+    h64 = host(h)
+    check(host(model.qkv[rows]), O.linear(h64[rows], W["w_qkv"]), "bf16", "qkv")
+    # attention over the GPU's q/k/v (QK-RMSNorm + RoPE fused)
+    qkv64 = host(model.qkv).reshape(S, 3, H, 128)
+    q = model.qkv[:, :D].view(S, H, 128)
+    k = model.qkv[:, D:2 * D].view(S, H, 128)
+    v = model.qkv[:, 2 * D:].view(S, H, 128)
+    model.attn.full(q, k, v, Lw.q_norm, Lw.k_norm, 1e-6, cache=model.cache, layer=0, out=model.o)
+    sync()
+    qr = O.prep_qk(qkv64[rows, 0], c[rows], s[rows], W["q_norm"], 1e-6)
+    kr = O.prep_qk(qkv64[:, 1], c, s, W["k_norm"], 1e-6)
+    ref_o = O.attention(qr, kr, qkv64[:, 2], O.mask_rows(wl.segments, rows))
+    check(host(model.o[rows]), ref_o, "bf16", "attention")
+    # out-projection, gated residual
+    o64 = host(model.o).reshape(S, D)
+    rt.gemm(model.o.view(S, D), Lw.w_out, model.x, Q.QI_EPI_GATED_RESIDUAL, m[2], 0, P)
+    sync()
+    ref_x1 = x64[rows] + np.tanh(sel(2, rows)) * O.linear(o64[rows], W["w_out"])
+    check(host(model.x[rows]), ref_x1, "f32", "out-proj residual")
+    # norm2, SwiGLU, down-projection
+    x1 = host(model.x)
+    rt.norm_mod(model.x, h, Lw.norm2, m[4], m[3], 0, P)
+    rt.gemm(h, Lw.w_gu, model.a, Q.QI_EPI_SWIGLU)
+    sync()
+    h2 = host(h)
+    check(h2[rows], O.norm_mod(x1[rows], W["norm2"], sel(4, rows), sel(3, rows)), "bf16", "norm2+mod")
+    ref_a = O.swiglu(O.linear(h2[rows], W["w_gate"]), O.linear(h2[rows], W["w_up"]))
+    check(host(model.a[rows]), ref_a, "bf16", "swiglu")
+    a64 = host(model.a)
+    rt.gemm(model.a, Lw.w_down, model.x, Q.QI_EPI_GATED_RESIDUAL, m[5], 0, P)
+    sync()
+    ref_x2 = x1[rows] + np.tanh(sel(5, rows)) * O.linear(a64[rows], W["w_down"])
+    check(host(model.x[rows]), ref_x2, "f32", "down-proj residual")

@@ -436,3 +436,139 @@ def test_planted_mistake_is_caught(i, monkeypatch):
     # ... and at least one fails once the mistake is planted
     monkeypatch.setattr(O, name, bad)
     assert any(_fails(pin) for pin in pins), f"planted mistake in {name} not caught"
+
+
+# ---------------------------------------------------------------------------------------------
+# the DiT layer pieces
+# ---------------------------------------------------------------------------------------------
+
+def test_timestep_embedding_closed_forms():
+    e0 = O.timestep_embedding(0.0)
+    assert e0.shape == (1, 256) and np.all(e0[0, :128] == 1.0) and np.all(e0[0, 128:] == 0.0)   # cos first
+    # frequency index 64 of 128 is 10000^(-1/2) = 0.01: at t = 50*pi the angle is pi/2
+    e = O.timestep_embedding(50 * math.pi)
+    assert abs(e[0, 64]) < 1e-12 and abs(e[0, 128 + 64] - 1.0) < 1e-12
+    # index 0 has frequency 1: cos(t), sin(t)
+    assert abs(e[0, 0] - math.cos(50 * math.pi)) < 1e-12 and abs(e[0, 128]) < 1e-12
+
+
+def test_silu_and_swiglu_hand_values():
+    assert O.silu(0.0) == 0.0 and abs(O.silu(1.0) - 0.7310585786300049) < 1e-15
+    assert abs(O.silu(-40.0)) < 1e-15 and abs(O.silu(40.0) - 40.0) < 1e-14
+    assert np.allclose(O.swiglu(np.array([1.0, 0.0]), np.array([2.0, 5.0])), [1.4621171572600098, 0.0], atol=1e-15)
+
+
+def _tiny_layer(seed=0, D=256, F=384):
+    rng = np.random.default_rng(seed)
+    L = {"norm1": rng.standard_normal(D) * 0.02, "norm2": rng.standard_normal(D) * 0.02,
+         "q_norm": 1 + rng.standard_normal(128) * 0.02, "k_norm": 1 + rng.standard_normal(128) * 0.02,
+         "w_qkv": rng.standard_normal((3 * D, D)) * 0.02 * 3, "w_out": rng.standard_normal((D, D)) * 0.05,
+         "w_gate": rng.standard_normal((F, D)) * 0.05, "w_up": rng.standard_normal((F, D)) * 0.05,
+         "w_down": rng.standard_normal((D, F)) * 0.05}
+    mods = tuple(tuple(rng.standard_normal(D) * 0.3 for _ in range(6)) for _ in range(2))
+    return L, mods
+
+
+def test_dit_layer_zero_gates_is_identity():
+    segs = (qin.text(5), qin.image(2, 3, 1), qin.image(3, 2, 0))
+    L, mods = _tiny_layer()
+    mods = tuple(tuple(np.zeros_like(v) if i in (2, 5) else v for i, v in enumerate(m)) for m in mods)
+    x = np.random.default_rng(1).standard_normal((17, 256))
+    c, s = O.rope_tables(O.positions(segs))
+    y, _ = O.dit_layer(x, L, mods, segs, c, s)
+    assert np.array_equal(y, x)    # tanh(0) = 0: both residual branches vanish exactly
+
+
+def test_dit_layer_cached_equals_full_and_prefix_uses_t0():
+    segs = (qin.text(5), qin.image(2, 3, 1), qin.image(3, 2, 0))
+    S, P, T = O.split_counts(segs)
+    L, mods = _tiny_layer(2)
+    x = np.random.default_rng(3).standard_normal((S, 256))
+    c, s = O.rope_tables(O.positions(segs))
+    y, cache = O.dit_layer(x, L, mods, segs, c, s)
+    yt, _ = O.dit_layer(x[P:], L, mods, segs, c, s, cache=cache)
+    assert np.max(np.abs(yt - y[P:])) < 1e-12
+    # prefix rows depend only on the t = 0 parameters: changing the target's modulation leaves them alone
+    mods2 = (mods[0], tuple(v * 3 for v in mods[1]))
+    y2, _ = O.dit_layer(x, L, mods2, segs, c, s)
+    assert np.array_equal(y2[:P], y[:P]) and not np.allclose(y2[P:], y[P:])
+
+
+def test_dit_layer_matches_hand_composition():
+    # the layer equals its steps composed by hand with the oracle's own attention on rotated q/k
+    segs = (qin.text(4), qin.image(2, 2, 1), qin.image(2, 2, 0))
+    S, P, T = O.split_counts(segs)
+    L, mods = _tiny_layer(4, D=128, F=256)
+    x = np.random.default_rng(5).standard_normal((S, 128))
+    c, s = O.rope_tables(O.positions(segs))
+    y, _ = O.dit_layer(x, L, mods, segs, c, s, tanh_gate=False)
+    rows_pre = np.arange(S) < P
+    def sel(i):
+        return np.where(rows_pre[:, None], mods[0][i][None, :], mods[1][i][None, :])
+    r1 = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + 1e-6) * (L["norm1"] + 1) * (1 + sel(1)) + sel(0)
+    qkv = r1 @ L["w_qkv"].T
+    q, k, v = qkv[:, :128], qkv[:, 128:256], qkv[:, 256:]
+    def qkn(z, w):
+        return z / np.sqrt(np.mean(z * z, axis=1, keepdims=True) + 1e-6) * w
+    q = O.rotate(qkn(q, L["q_norm"]), c, s)
+    k = O.rotate(qkn(k, L["k_norm"]), c, s)
+    m = O.mask_dense(segs)
+    att = np.zeros_like(v)
+    for i in range(S):
+        sc = q[i] @ k.T / math.sqrt(128)
+        sc = np.where(m[i], sc, -np.inf)
+        w = np.exp(sc - sc.max())
+        att[i] = (w / w.sum()) @ v
+    x1 = x + sel(2) * (att @ L["w_out"].T)
+    r2 = x1 / np.sqrt(np.mean(x1 * x1, axis=1, keepdims=True) + 1e-6) * (L["norm2"] + 1) * (1 + sel(4)) + sel(3)
+    g, u = r2 @ L["w_gate"].T, r2 @ L["w_up"].T
+    x2 = x1 + sel(5) * ((g / (1 + np.exp(-g)) * u) @ L["w_down"].T)
+    assert np.max(np.abs(y - x2)) < 1e-12
+
+
+def test_velocity_head_scale_zero_is_plain_norm_projection():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((5, 64)) * 3
+    w_head = rng.standard_normal((8, 64))
+    v = O.velocity_head(x, np.zeros((1, 64)), np.zeros((64, 64)), w_head)
+    ref = (x / np.sqrt(np.mean(x ** 2, axis=1, keepdims=True) + 1e-6)) @ w_head.T
+    assert np.max(np.abs(v - ref)) < 1e-13
+
+
+def test_denoise_one_step_is_euler_of_head_and_cache_matches_recompute():
+    # two layers, three steps: the cached loop equals recomputing the whole sequence each step
+    segs = (qin.text(6), qin.image(2, 3, 1), qin.image(3, 3, 0))
+    S, P, T = O.split_counts(segs)
+    D, F = 128, 256
+    rng = np.random.default_rng(7)
+    shared = {"t_w1": rng.standard_normal((D, 256)) / 16, "t_w2": rng.standard_normal((D, D)) / 11,
+              "w_mod": rng.standard_normal((6 * D, D)) / 11, "w_scale": rng.standard_normal((D, D)) / 11,
+              "w_head": rng.standard_normal((64, D)) / 11, "w_in": rng.standard_normal((D, 64)) / 8}
+    layers = [_tiny_layer(10 + i, D=D, F=F)[0] for i in range(2)]
+    x_text = rng.standard_normal((6, D))
+    lat_ref = rng.standard_normal((6, 64))
+    lat0 = rng.standard_normal((T, 64))
+    lat, vels = O.denoise(segs, x_text, lat_ref, lat0, shared, layers, 3, return_velocities=True)
+    # recompute: every step runs the full sequence (the prefix at t = 0 is the same every step)
+    c, s = O.rope_tables(O.positions(segs))
+    sig = [1.0, 2 / 3, 1 / 3, 0.0]
+    ref = lat0.copy()
+    for k in range(3):
+        temb = O.time_condition(np.array([0.0, sig[k]]), shared["t_w1"], shared["t_w2"])
+        mod = O.modulation(temb, shared["w_mod"], D)
+        mods = (tuple(m[0] for m in mod), tuple(m[1] for m in mod))
+        x = np.concatenate([O.prefix_states(segs, x_text, O.img_in(lat_ref, shared["w_in"])),
+                            O.img_in(ref, shared["w_in"])])
+        for L in layers:
+            x, _ = O.dit_layer(x, L, mods, segs, c, s)
+        v = O.velocity_head(x[P:], temb[1:2], shared["w_scale"], shared["w_head"])
+        assert np.max(np.abs(v - vels[k])) < 1e-11
+        ref = ref + (sig[k + 1] - sig[k]) * v
+    assert np.max(np.abs(ref - lat)) < 1e-11
+
+
+def test_prefix_states_follow_segment_order():
+    segs = (qin.text(2), qin.image(1, 2, 1), qin.text(1), qin.image(1, 1, 2), qin.image(1, 1, 0))
+    xt = np.array([[1.0], [2.0], [3.0]])
+    rt = np.array([[10.0], [11.0], [12.0]])
+    assert O.prefix_states(segs, xt, rt)[:, 0].tolist() == [1, 2, 10, 11, 3, 12]
