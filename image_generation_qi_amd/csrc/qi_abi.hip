@@ -139,6 +139,8 @@ void set_partials(AttnArgs& a, char* base, int64_t n_q, int64_t T, int32_t n_hea
 }
 
 int run_attn(const AttnArgs& a, qi_dtype dtype, hipStream_t s) {
+  // the bf16 path addresses each key source through a buffer resource with 32-bit byte offsets
+  if (dtype == QI_BF16 && (a.nA > QI_MAX_SOURCE_KEYS || a.nB > QI_MAX_SOURCE_KEYS)) return QI_ERR_SHAPE;
   TimedLaunch t(s);
   return launch_status(dtype == QI_BF16 ? launch_attn_f16(a, s) : launch_attn_f32(a, s));
 }
@@ -233,14 +235,17 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
     if ((st = prep_kv(io->k, io->v, io->dtype, li.S, io->n_head, io->tok_stride, prep, wk, wv,
                       li.S * QI_HEAD_DIM, s)) != QI_OK)
       return st;
+    // the prefix rows and the target rows as two sources, exactly as with a cache, so that the
+    // key tiles (and hence the output bits) are the same with and without one
+    const int64_t es_kv = io->dtype == QI_BF16 ? 2 : 4;
     a.kA = wk;
     a.vA = wv;
     a.a_head_stride = li.S * QI_HEAD_DIM;
-    a.nA = li.S;
-    a.kB = wk;
-    a.vB = wv;
-    a.b_head_stride = 0;
-    a.nB = 0;
+    a.nA = li.P;
+    a.kB = (const char*)wk + li.P * QI_HEAD_DIM * es_kv;
+    a.vB = (const char*)wv + li.P * QI_HEAD_DIM * es_kv;
+    a.b_head_stride = li.S * QI_HEAD_DIM;
+    a.nB = li.T;
   }
   return run_attn(a, io->dtype, s);
 }

@@ -7,18 +7,24 @@
 //
 // Work decomposition
 //   - one workgroup = 4 wavefronts = 128 query rows of one head; wave w owns rows 32w..32w+31.
-//   - keys are streamed in tiles of 64 through LDS (double buffered): K row-major with a
-//     16-byte pad per row, V transposed (Vt[d][key]) with an 8-byte pad, so that both MFMA
-//     A-operand reads are bank-conflict free.
-//   - S^T = K Q^T with v_mfma_f32_32x32x16_f16: A = 32 keys x 16 dims read from LDS, B = the
-//     wave's 32 queries (rotated, scaled by scale*log2(e), fp16) held in registers for the
-//     whole kernel.  The result leaves each lane with one query and 16 keys per 32-key block,
-//     so the softmax row max is in-lane plus one exchange with lane^32.
-//   - O^T += Vt P^T with the same MFMA: B = the lane's own probabilities (fp16), A = 32 dims x
-//     16 keys of Vt.  The key order inside the contraction follows the S^T register order, so
-//     P never moves between lanes.
-//   - online softmax in base 2 with a lazy running max: the output is rescaled only when a
-//     row max grows by more than TAU (probabilities stay <= 2^TAU, well inside fp16).
+//   - keys stream in tiles of 64 through LDS (two stages of K and V, 64 KB), copied with MUBUF
+//     buffer -> LDS loads (keeps the compute phases' LDS waits exact) into unpadded 256-byte
+//     rows whose 16-byte chunks are XOR-swizzled (K: chunk ^ (row & 15), V: chunk ^ 4(row & 3)),
+//     so both MFMA A-operand reads are bank-conflict free.  Source A (cache or workspace prefix)
+//     and source B (fresh keys) are tiled separately, so every copy reads one source.
+//   - S^T = K Q^T - m with v_mfma_f32_32x32x16_f16: A = 32 keys x 16 dims from LDS, B = the
+//     wave's 32 queries (rotated, scaled by scale*log2(e), fp16) held in registers; the
+//     accumulators start at minus the row's reference m, so the scores come out shifted.  Each
+//     lane then holds one query and 16 keys per 32-key block.
+//   - O^T += V^T P^T with the same instruction: B = the lane's own probabilities (fp16), A = V^T
+//     from the row-major V tile through the transposing ds_read_b64_tr_b16.  The key order of the
+//     contraction follows the S^T register order, so P never moves between lanes.
+//   - online softmax in base 2 with a lazy reference: probabilities 2^(s) are formed against the
+//     current reference and only rows whose probabilities exceed 2^8 (or that have no reference
+//     yet) move it (a rare, wave-uniform branch); other rows keep a factor of exactly 1.
+//   - software pipeline: the QK^T MFMAs of tile kt+1, the probabilities of tile kt, the LDS
+//     operand reads one step ahead and the copies of later tiles are one fenced sequence, so
+//     MFMA, VALU, LDS and memory work interleave; then PV of tile kt with its row sums.
 //   - the Block-Causal mask is applied per tile from the row limits (see qi_common.h): tiles
 //     with no visible pair are never loaded, tiles with all pairs visible run unmasked.
 //   - key chunks (n_split > 1) balance the grid over the CUs: each chunk of a query tile's key
@@ -47,7 +53,6 @@ constexpr int BN = 64;              // keys per tile
 constexpr int HD = 128;             // head dim
 constexpr int TILE = BN * HD;       // one K or V tile, fp16 elements (16 KB, rows of 256 bytes)
 constexpr int BUF = 2 * TILE;       // one pipeline stage: K tile then V tile
-constexpr float TAU_P = 256.0f;     // lazy-rescale threshold: probabilities may reach 2^8
 
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
   const int q = n >> 3, r = n & 7;
@@ -73,7 +78,6 @@ __device__ __forceinline__ h4 lds_read_tr(const _Float16* p) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
 
 // LDS tiles hold unpadded 256-byte rows; the 16-byte chunk c of row r is stored at chunk
 // position c ^ swz(r).  K: swz = r & 15, so the 16 rows read by one quarter-wave (same logical
@@ -81,11 +85,6 @@ typedef __attribute__((address_space(1))) void glb_void;
 // by a half-wave of transposing reads are all distinct.
 __device__ __forceinline__ int swz_k(int r) { return r & 15; }
 __device__ __forceinline__ int swz_v(int r) { return 4 * (r & 3); }
-
-// Direct global -> LDS copy of 16 bytes per lane; lane l lands at dst + 16*l.
-__device__ __forceinline__ void load_lds16(const void* src, void* dst_wave_base) {
-  __builtin_amdgcn_global_load_lds((const glb_void*)src, (lds_void*)dst_wave_base, 16, 0, 0);
-}
 
 // Both halves of a wave exchanged: for lane l, returns (x[l], x[l ^ 32]) in an order that is
 // the same for the two lanes of the pair, so any symmetric combination is bit-identical.
@@ -111,9 +110,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (MASKED) qt = n_qt - 1 - qt;  // longest rows first
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
-  const int nA = (int)a.nA, nkeys = (int)(a.nA + a.nB);
+  const int nA = (int)a.nA, nB = (int)a.nB, nkeys = nA + nB;
 
   // ---- this lane's query: load, optional RMSNorm, rotate, scale, to fp16 --------------------
   const int qrow = qt * BM + wave * 32 + l32;
@@ -169,7 +168,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int i = 0; i < 8; ++i) qf[kk][i] = (_Float16)(x[8 * kk + i] * a.scale_log2);
 
-  // ---- key range of this tile row --------------------------------------------------------
+  // ---- key tiles of this tile row ----------------------------------------------------------
+  // Sources A and B are tiled separately: tiles 0 .. ntA-1 hold keys 64t .. of A, tiles ntA ..
+  // hold keys nA + 64(t - ntA) .. of B.  Only the last tile of each source can be short.
+  const int ntA = (nA + BN - 1) / BN;
   const int q_first = qt * BM;
   const int q_last = (q_first + BM < a.n_q ? q_first + BM : a.n_q) - 1;
   int lim = nkeys - 1, lim_first = nkeys - 1, lim_last = nkeys - 1;
@@ -181,8 +183,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     lim_first = lim_first < nkeys - 1 ? lim_first : nkeys - 1;
     lim_last = lim_last < nkeys - 1 ? lim_last : nkeys - 1;
   }
-  const int kt_end = lim_last / BN + 1;       // tiles past this hold no visible key
-  const int kt_full = (lim_first + 1) / BN;   // tiles before this need no mask
+  // tiles from kt_end on hold no visible key; tiles before kt_full are whole and visible to all
+  const int kt_end = lim_last < nA ? lim_last / BN + 1 : ntA + (lim_last - nA) / BN + 1;
+  const int kt_full = (lim_first + 1 < nA || (nA % BN) != 0) ? (lim_first + 1 < nA ? lim_first + 1 : nA) / BN
+                                                            : ntA + (lim_first + 1 - nA) / BN;
   const int t_begin = split * a.split_tiles;  // this workgroup's chunk of key tiles
   const int t_stop = (t_begin + a.split_tiles < kt_end) ? t_begin + a.split_tiles : kt_end;
   if (t_begin >= t_stop) {  // the chunk holds no visible key for any row of the tile
@@ -204,47 +208,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const _Float16* kB = (const _Float16*)a.kB + (int64_t)h * a.b_head_stride;
   const _Float16* vB = (const _Float16*)a.vB + (int64_t)h * a.b_head_stride;
 
-  // ---- tile staging: direct global -> LDS loads into swizzled rows -------------------------
-  // wave w fills rows 16w .. 16w+15 of each tile: 4 loads of 1 KB (4 rows) for K and for V.
-  // Lane i of load j covers row 16w + 4j + i/16, chunk position i%16.
+  // ---- tile staging: buffer -> LDS copies (MUBUF with the LDS bit) ---------------------------
+  // The MUBUF form keeps the LDS reads of the compute phases on exact lgkmcnt waits while these
+  // copies are in flight.  One buffer resource per head and source, sized to that source's rows:
+  // rows past the end of a short tile fall outside it and are not read from memory (the LDS
+  // tiles are zero-filled once at the start, so those rows always hold finite values, which the
+  // mask then excludes).
+  // Wave w fills rows 16w .. 16w+15 of each tile: 4 copies of 1 KB (4 rows) for K and for V.
+  // Lane i of copy j covers row 16w + 4j + i/16, chunk position i%16; offsets are in bytes.
+  const __amdgpu_buffer_rsrc_t rkA = __builtin_amdgcn_make_buffer_rsrc((void*)kA, (short)0, nA * HD * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rvA = __builtin_amdgcn_make_buffer_rsrc((void*)vA, (short)0, nA * HD * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rkB = __builtin_amdgcn_make_buffer_rsrc((void*)kB, (short)0, nB * HD * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rvB = __builtin_amdgcn_make_buffer_rsrc((void*)vB, (short)0, nB * HD * 2, 0x00020000);
   int koff[4], voff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 16 * wave + 4 * j + (lane >> 4);
     const int pos = lane & 15;
-    koff[j] = row * HD + 8 * (pos ^ swz_k(row));
-    voff[j] = row * HD + 8 * (pos ^ swz_v(row));
+    koff[j] = 2 * (row * HD + 8 * (pos ^ swz_k(row)));
+    voff[j] = 2 * (row * HD + 8 * (pos ^ swz_v(row)));
   }
-  auto load_tile_part = [&](int kt, int buf, bool is_k) {
-    _Float16* dst = smem + buf * BUF + (is_k ? 0 : TILE) + (16 * wave) * HD;
-    const _Float16* srcA = is_k ? kA : vA;
-    const _Float16* srcB = is_k ? kB : vB;
-    const int* off = is_k ? koff : voff;
-    const int key0 = kt * BN;
-    const _Float16* base = nullptr;
-    if (key0 + BN <= nA)                              // whole tile in source A
-      base = srcA + (int64_t)key0 * HD;
-    else if (key0 >= nA && key0 + BN <= nkeys)        // whole tile in source B
-      base = srcB + (int64_t)(key0 - nA) * HD;
-    if (base) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) load_lds16(base + off[j], dst + j * 4 * HD);
-    } else {  // straddling or ragged tile: per-row source; rows past the last key re-read
-              // key 0 (finite data that the row limit masks out)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 16 * wave + 4 * j + (lane >> 4);
-        int key = key0 + row;
-        if (key >= nkeys) key = 0;
-        const bool inA = key < nA;
-        const int64_t rb = (int64_t)(inA ? key : key - nA) * HD - (int64_t)row * HD;
-        load_lds16((inA ? srcA : srcB) + rb + off[j], dst + j * 4 * HD);
-      }
-    }
+  // copy j of K (is_k) or V of key tile t into stage buf
+  auto copy = [&](int t, int buf, int j, auto is_k_tag) {
+    constexpr bool IS_K = decltype(is_k_tag)::value;
+    const bool inA = t < ntA;
+    const __amdgpu_buffer_rsrc_t rs = IS_K ? (inA ? rkA : rkB) : (inA ? rvA : rvB);
+    const int soff = (inA ? t : t - ntA) * (BN * HD * 2);
+    _Float16* dst = smem + buf * BUF + (IS_K ? 0 : TILE) + (16 * wave + 4 * j) * HD;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, IS_K ? koff[j] : voff[j], soff, 0, 0);
   };
 
-  // per-lane LDS offsets: K rows for the S^T A-operand (chunk 2kk+g of row l32 or 32+l32);
-  // V rows/cols for the transposing reads (row 16c+8h+4g+L/4, dims 32bd+16(lane/16%2)+4(L%4))
+  // per-lane LDS offsets: V rows/cols for the transposing reads (row 16c+8h+4g+L/4, dims
+  // 32bd+16(lane/16%2)+4(L%4))
   const int L = lane & 15;
   const int vrow0 = 4 * g + (L >> 2);                        // + 16c + 8h: same row & 3
   const int vcol = 16 * ((lane >> 4) & 1) + 4 * (L & 3);      // + 32bd
@@ -253,34 +248,155 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int bd = 0; bd < 4; ++bd)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[bd][r] = 0.f;
+  // m_run: the reference (log2 units) the scores of the current tile were taken against; -inf
+  // until a row has seen a visible key (its scores are then taken against 0)
   float m_run = -INFINITY, l_run = 0.f;
-  const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
-  // S^T = K Q^T for the 64 keys of one K buffer (two blocks of 32 keys).  Rows l32 and 32+l32
-  // share (row & 15), so both reads use the same chunk position.
-  auto qk = [&](int kbuf, f32x16& s0, f32x16& s1) {
+  // ---- LDS operand reads -------------------------------------------------------------------
+  // K: the two S^T A operands of reduction step kk (keys l32 and 32 + l32, dims 16kk + 8g ..).
+  // Rows l32 and 32 + l32 share (row & 15), so both reads use the same chunk position.
+  auto read_k = [&](int kbuf, int kk, h8 (&dst)[2]) {
     const _Float16* Ks = smem + kbuf * BUF;
+    const int pos = ((2 * kk + g) ^ swz_k(l32)) * 8;
+    dst[0] = *(const h8*)(Ks + l32 * HD + pos);
+    dst[1] = *(const h8*)(Ks + (32 + l32) * HD + pos);
+  };
+  // V: the four O^T A operands (dims 32bd .. 32bd + 31) of 16-key chunk c, each from two
+  // transposing reads (rows vrow0 + 16c and vrow0 + 16c + 8 share row & 3, hence one swizzle).
+  auto read_v = [&](int vbuf, int c, h8 (&dst)[4]) {
+    const _Float16* Vs = smem + vbuf * BUF + TILE;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int pos = ((2 * kk + g) ^ swz_k(l32)) * 8;
-      const h8 a0 = *(const h8*)(Ks + l32 * HD + pos);
-      const h8 a1 = *(const h8*)(Ks + (32 + l32) * HD + pos);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, qf[kk], kk ? s0 : zero16, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, qf[kk], kk ? s1 : zero16, 0, 0, 0);
+    for (int bd = 0; bd < 4; ++bd) {
+      const int col = 32 * bd + vcol;
+      const int pcol = ((col >> 3) ^ swz_v(vrow0)) * 8 + (col & 7);
+      const _Float16* vp = Vs + (vrow0 + 16 * c) * HD + pcol;
+      const h4 lo = lds_read_tr(vp);
+      const h4 hi = lds_read_tr(vp + 8 * HD);
+      dst[bd] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
 
-  // Online softmax of one tile's scores.  Common path, branch-free: probabilities against the
-  // current reference m_run, rounded to fp16 (the values PV consumes), their row sum taken from
-  // those same fp16 values with fp32 dot products, and a packed-fp16 max to detect rows whose
-  // scores rose more than TAU above the reference.  Rare path (first visible tile of a row or a
-  // large rise): move those rows' reference to their true max, recompute, and return the factor
-  // alpha by which the running output must be rescaled (exactly 1 for all other rows, so each
-  // row's arithmetic never depends on the other rows of the wave).
-  auto softmax = [&](int kt, f32x16& s0, f32x16& s1, h8 (&pf)[4], auto masked_tag) -> float {
+  // S^T - m = K Q^T - m for the 64 keys of one K buffer: the accumulators start at minus the
+  // reference, so the scores come out already shifted.  Prologue only.
+  auto qk = [&](int kbuf, f32x16& s0, f32x16& s1) {
+    const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
+    f32x16 init;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) init[r] = nm;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      h8 ka[2];
+      read_k(kbuf, kk, ka);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[0], qf[kk], kk ? s0 : init, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[1], qf[kk], kk ? s1 : init, 0, 0, 0);
+    }
+  };
+
+  // The shifted scores of the next tile and the probabilities of the current one, as one fenced
+  // sequence of eight steps.  Step kk issues the K reads of step kk + 1 and, in steps 0-3, two
+  // of the eight buffer -> LDS copies of the iteration (K of tile kt+2 and V of tile kt+1; past
+  // the chunk's last tile the last tile is copied again into the free stage), then the two
+  // MFMAs of step kk with, between them, the probabilities 2^s of scores 2kk and 2kk+1 of both
+  // 32-key blocks, rounded to fp16 (the values PV consumes) and folded into a packed max.
+  auto qk_probs = [&](int kbuf, int tk, int tv, f32x16& sn0, f32x16& sn1, const f32x16& s0, const f32x16& s1,
+                      h8 (&pf)[4]) -> h2 {
+    const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
+    f32x16 init;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) init[r] = nm;
+    h8 ka[2][2];
+    read_k(kbuf, 0, ka[0]);
+    h2 pm0 = {(_Float16)0.f, (_Float16)0.f}, pm1 = pm0;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      if (kk + 1 < 8) read_k(kbuf, kk + 1, ka[(kk + 1) & 1]);
+      if (kk < 4) {
+        copy(tk, kbuf ^ 1, kk, std::true_type{});
+        copy(tv, kbuf, kk, std::false_type{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      sn0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[kk & 1][0], qf[kk], kk ? sn0 : init, 0, 0, 0);
+      const float p0a = __builtin_amdgcn_exp2f(s0[2 * kk]);
+      const float p0b = __builtin_amdgcn_exp2f(s0[2 * kk + 1]);
+      const float p1a = __builtin_amdgcn_exp2f(s1[2 * kk]);
+      const float p1b = __builtin_amdgcn_exp2f(s1[2 * kk + 1]);
+      sn1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[kk & 1][1], qf[kk], kk ? sn1 : init, 0, 0, 0);
+      const h2 q0 = {(_Float16)p0a, (_Float16)p0b};
+      const h2 q1 = {(_Float16)p1a, (_Float16)p1b};
+      pf[kk >> 2][2 * (kk & 3)] = q0[0];
+      pf[kk >> 2][2 * (kk & 3) + 1] = q0[1];
+      pf[2 + (kk >> 2)][2 * (kk & 3)] = q1[0];
+      pf[2 + (kk >> 2)][2 * (kk & 3) + 1] = q1[1];
+      pm0 = __builtin_elementwise_max(pm0, q0);
+      pm1 = __builtin_elementwise_max(pm1, q1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return __builtin_elementwise_max(pm0, pm1);
+  };
+
+  // O^T += V^T P^T for one V buffer, as four fenced steps: each issues the V reads of chunk
+  // c + 1 and the four MFMAs of chunk c, with the row sum of chunk c's probabilities (fp32 dot
+  // products of the same fp16 values) between them.
+  auto pv_sums = [&](int vbuf, const h8 (&pf)[4]) -> float {
+    h8 va[2][4];
+    read_v(vbuf, 0, va[0]);
+    const h2 one2 = {(_Float16)1.f, (_Float16)1.f};
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (c + 1 < 4) read_v(vbuf, c + 1, va[(c + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int bd = 0; bd < 4; ++bd) {
+        o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[c & 1][bd], pf[c], o[bd], 0, 0, 0);
+        if (bd & 1)
+          ps1 = __builtin_amdgcn_fdot2(h2{pf[c][2 * bd], pf[c][2 * bd + 1]}, one2, ps1, false);
+        else
+          ps0 = __builtin_amdgcn_fdot2(h2{pf[c][2 * bd], pf[c][2 * bd + 1]}, one2, ps0, false);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return ps0 + ps1;
+  };
+
+  // ---- software-pipelined main loop ------------------------------------------------------
+  // When iteration kt starts, stage b = (kt - t_begin) & 1 holds K[kt] and V[kt] and stage b^1
+  // holds K[kt+1].  Iteration kt: the QK^T MFMAs of tile kt+1 (stage b^1) interleaved with the
+  // probabilities of tile kt and with the copies of K[kt+2] into stage b (its K was last read by
+  // the QK of iteration kt-1) and of V[kt+1] into stage b^1 (its V was last read by the PV of
+  // iteration kt-1); the rare reference update; PV of tile kt from stage b; then the copies are
+  // waited for and a barrier ends the iteration.  The loop is unrolled twice so that the current
+  // and next scores swap register sets instead of being copied.
+  {
+    // zero-fill both stages once, so that rows of short tiles that no copy writes hold zeros
+    u32x4* z = (u32x4*)smem;
+#pragma unroll
+    for (int i = 0; i < (2 * BUF * 2) / (16 * 256); ++i) z[i * 256 + tid] = u32x4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    copy(t_begin, 0, j, std::true_type{});
+    copy(t_begin, 0, j, std::false_type{});
+    copy(t_begin + 1 < t_stop ? t_begin + 1 : t_begin, 1, j, std::true_type{});
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 sa0, sa1, sb0, sb1;
+  qk(0, sa0, sa1);
+  // every wave has read K[t_begin] from stage 0 before the first iteration copies into it
+  __syncthreads();
+  int kt = t_begin;
+  const int kt_mid = kt_full < t_begin ? t_begin : (kt_full < t_stop ? kt_full : t_stop);
+  auto iteration = [&](auto masked_tag, f32x16& s0, f32x16& s1, f32x16& sn0, f32x16& sn1) {
     constexpr bool MT = decltype(masked_tag)::value;
+    const int b = (kt - t_begin) & 1;
     if constexpr (MT) {
-      const int rel = lim - kt * BN - 4 * g;   // offset (in tile, minus 4g) of the last visible key
+      const int key0 = kt < ntA ? kt * BN : nA + (kt - ntA) * BN;
+      const int cnt = kt < ntA ? nA - kt * BN : nkeys - key0;   // keys of the tile (capped below)
+      int rel = lim - key0;
+      if (rel > cnt - 1) rel = cnt - 1;
+      rel -= 4 * g;                 // offset (in tile, minus 4g) of the last visible key
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kr = 8 * (r >> 2) + (r & 3);
@@ -288,109 +404,78 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (kr + 32 > rel) s1[r] = -INFINITY;
       }
     }
-    auto probs = [&](float mu) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pf[r >> 3][r & 7] = (_Float16)__builtin_amdgcn_exp2f(s0[r] - mu);
-        pf[2 + (r >> 3)][r & 7] = (_Float16)__builtin_amdgcn_exp2f(s1[r] - mu);
-      }
-    };
-    probs(m_run);
-    h2 pm = __builtin_shufflevector(pf[0], pf[0], 0, 1);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        pm = __builtin_elementwise_max(pm, h2{pf[c][2 * i], pf[c][2 * i + 1]});
-    float pmax = fmaxf((float)pm[0], (float)pm[1]);
-    pmax = pair_max(pmax);                       // NaN-free: p >= 0 or +inf
+    // next tile's scores (on the last iteration from a stale, in-bounds stage, discarded)
+    const int tk = kt + 2 < t_stop ? kt + 2 : t_stop - 1;
+    const int tv = kt + 1 < t_stop ? kt + 1 : t_stop - 1;
+    h8 pf[4];
+    const h2 pm = qk_probs(b ^ 1, tk, tv, sn0, sn1, s0, s1, pf);
+    // Rare path: a row's first visible tile (reference still -inf) or probabilities above 2^8
+    // (fp16 bits of a non-negative value above 0x5C00, which includes +inf).  The row's new
+    // reference is its true max; the probabilities are recomputed, the running output and sum
+    // are rescaled by alpha, and the next tile's scores (taken against the old reference) are
+    // shifted.  Rows that do not take it keep alpha = 1 exactly, so each row's arithmetic never
+    // depends on the other rows of the wave.
+    const uint32_t pmb = __builtin_bit_cast(uint32_t, pm);
+    const uint32_t pmx = (pmb & 0xFFFFu) > (pmb >> 16) ? (pmb & 0xFFFFu) : (pmb >> 16);
+    const bool need1 = pmx > 0x5C00u || m_run == -INFINITY;
     float alpha = 1.f;
-    const bool need = !(pmax <= TAU_P);          // also true for +inf (reference still -inf)
-    if (__builtin_expect(__any(need), 0)) {
+    if (__builtin_expect(__any(need1), 0)) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(need1 ? 1u : 0u, need1 ? 1u : 0u, false, false);
+      const bool need = (sw[0] | sw[1]) != 0u;     // either half of the row
       float mt = fmaxf(s0[0], s1[0]);
 #pragma unroll
       for (int r = 1; r < 16; ++r) mt = fmaxf(mt, fmaxf(s0[r], s1[r]));
-      mt = pair_max(mt);
+      mt = pair_max(mt);                           // row max of the shifted scores
+      float shift = 0.f;
       if (need) {
-        alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mt);
-        m_run = mt;
+        if (m_run == -INFINITY) {
+          alpha = 0.f;
+          shift = (mt == -INFINITY) ? 0.f : mt;
+          m_run = mt;
+        } else {
+          alpha = __builtin_amdgcn_exp2f(-mt);
+          shift = mt;
+          m_run = m_run + mt;
+        }
       }
-      probs(MT ? ((m_run == -INFINITY) ? 0.f : m_run) : m_run);
-    }
-    const h2 one2 = {(_Float16)1.f, (_Float16)1.f};
-    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        ps0 = __builtin_amdgcn_fdot2(h2{pf[c][2 * i], pf[c][2 * i + 1]}, one2, ps0, false);
-        ps1 = __builtin_amdgcn_fdot2(h2{pf[c][2 * i + 2], pf[c][2 * i + 3]}, one2, ps1, false);
+      for (int r = 0; r < 16; ++r) {
+        pf[r >> 3][r & 7] = (_Float16)__builtin_amdgcn_exp2f(s0[r] - shift);
+        pf[2 + (r >> 3)][r & 7] = (_Float16)__builtin_amdgcn_exp2f(s1[r] - shift);
+        sn0[r] -= shift;
+        sn1[r] -= shift;
       }
-    l_run = l_run * alpha + (ps0 + ps1);
-    return alpha;
-  };
-
-  // O^T += V^T P^T for one V buffer; the V^T operand comes from two transposing reads per
-  // 16-key chunk (rows vrow0 + 16c + 8h share row & 3, hence one swizzle for both reads)
-  auto pv = [&](int vbuf, const h8 (&pf)[4]) {
-    const _Float16* Vs = smem + vbuf * BUF + TILE;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-      for (int bd = 0; bd < 4; ++bd) {
-        const int col = 32 * bd + vcol;
-        const int pcol = ((col >> 3) ^ swz_v(vrow0)) * 8 + (col & 7);
-        const _Float16* vp = Vs + (vrow0 + 16 * c) * HD + pcol;
-        const h4 lo = lds_read_tr(vp);
-        const h4 hi = lds_read_tr(vp + 8 * HD);
-        const h8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[c], o[bd], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);   // keep at most one chunk of V reads in flight
-    }
-  };
-
-  // ---- software-pipelined main loop ------------------------------------------------------
-  // K runs one tile ahead of V.  Iteration kt: start loading K[kt+2] and V[kt+1]; issue the
-  // QK^T MFMAs of tile kt+1 together with the softmax of tile kt (independent work, one basic
-  // block, so MFMA and VALU overlap); apply the rare output rescale; PV of tile kt.
-  // Buffer reuse: K buffer kt%2 (tile kt) was last read by the QK of iteration kt-1 and V buffer
-  // (kt+1)%2 by the PV of iteration kt-1; the barrier ending iteration kt-1 ordered both.
-  auto load_k = [&](int kt, int b) { load_tile_part(kt, b, true); };
-  auto load_v = [&](int kt, int b) { load_tile_part(kt, b, false); };
-  load_k(t_begin, 0);
-  load_v(t_begin, 0);
-  if (t_begin + 1 < t_stop) load_k(t_begin + 1, 1);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  f32x16 sc0, sc1;
-  qk(0, sc0, sc1);
-  int kt = t_begin;
-  const int kt_mid = kt_full < t_begin ? t_begin : (kt_full < t_stop ? kt_full : t_stop);
-  auto iteration = [&](auto masked_tag) {
-    const int b = (kt - t_begin) & 1;
-    if (kt + 2 < t_stop) load_k(kt + 2, b);
-    if (kt + 1 < t_stop) load_v(kt + 1, b ^ 1);
-    // next tile's scores; on the last iteration this reads a stale (in-bounds) buffer and the
-    // result is discarded, which keeps QK and softmax in one basic block
-    f32x16 sn0, sn1;
-    qk(b ^ 1, sn0, sn1);
-    h8 pf[4];
-    const float alpha = softmax(kt, sc0, sc1, pf, masked_tag);
-    if (__builtin_expect(__any(alpha != 1.f), 0)) {
 #pragma unroll
       for (int bd = 0; bd < 4; ++bd)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[bd][r] *= alpha;
     }
-    pv(b, pf);
-    sc0 = sn0;
-    sc1 = sn1;
+    l_run = l_run * alpha + pv_sums(b, pf);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  for (; kt < kt_mid; ++kt) iteration(std::false_type{});
-  for (; kt < t_stop; ++kt) iteration(std::true_type{});
+  while (kt + 1 < kt_mid) {
+    iteration(std::false_type{}, sa0, sa1, sb0, sb1);
+    ++kt;
+    iteration(std::false_type{}, sb0, sb1, sa0, sa1);
+    ++kt;
+  }
+  if (kt < kt_mid) {
+    iteration(std::false_type{}, sa0, sa1, sb0, sb1);
+    ++kt;
+    sa0 = sb0;
+    sa1 = sb1;
+  }
+  while (kt + 1 < t_stop) {
+    iteration(std::true_type{}, sa0, sa1, sb0, sb1);
+    ++kt;
+    iteration(std::true_type{}, sb0, sb1, sa0, sa1);
+    ++kt;
+  }
+  if (kt < t_stop) {
+    iteration(std::true_type{}, sa0, sa1, sb0, sb1);
+    ++kt;
+  }
 
   // ---- epilogue: normalise and store bf16, or store the chunk's partial ---------------------
   const float lt = pair_sum(l_run);
@@ -478,7 +563,7 @@ int64_t attn_f16_partial_bytes(int64_t n_q, int32_t n_head) {
 hipError_t launch_attn_f16(const AttnArgs& a_in, hipStream_t s) {
   AttnArgs a = a_in;
   const int64_t n_qt = (a.n_q + BM - 1) / BM;
-  const int64_t kt_total = (a.nA + a.nB + BN - 1) / BN;
+  const int64_t kt_total = (a.nA + BN - 1) / BN + (a.nB + BN - 1) / BN;
   if (a.n_split < 1) a.n_split = 1;
   a.split_tiles = (int)((kt_total + a.n_split - 1) / a.n_split);
   if (a.split_tiles < 1) a.split_tiles = 1;

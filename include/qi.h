@@ -27,6 +27,8 @@
  *     the attention contractions use fp16 MFMA operands (rotated Q and K, softmax
  *     probabilities, V) with fp32 accumulation and an fp32 online softmax; outputs are
  *     rounded to bf16 (nearest even).  fp32 I/O runs fp32 arithmetic throughout.
+ *   - bf16 attention takes at most QI_MAX_SOURCE_KEYS prefix keys and as many target keys
+ *     (QI_ERR_SHAPE beyond).
  */
 #ifndef QI_H
 #define QI_H
@@ -36,6 +38,8 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+#define QI_MAX_SOURCE_KEYS 8388607   /* 2^31 / 256 - 1 rows of 128 fp16 values */
 
 typedef enum {
   QI_OK = 0,
