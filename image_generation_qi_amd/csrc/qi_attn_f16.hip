@@ -294,12 +294,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // The shifted scores of the next tile and the probabilities of the current one, as one fenced
   // sequence of eight steps.  Step kk issues the K reads of step kk + 1 and, in steps 0-3, two
-  // of the eight buffer -> LDS copies of the iteration (K of tile kt+2 and V of tile kt+1; past
-  // the chunk's last tile the last tile is copied again into the free stage), then the two
-  // MFMAs of step kk with, between them, the probabilities 2^s of scores 2kk and 2kk+1 of both
-  // 32-key blocks, rounded to fp16 (the values PV consumes) and folded into a packed max.
-  auto qk_probs = [&](int kbuf, int tk, int tv, f32x16& sn0, f32x16& sn1, const f32x16& s0, const f32x16& s1,
-                      h8 (&pf)[4]) -> h2 {
+  // of the eight buffer -> LDS copies of the iteration (K of tile tk and V of tile tv into stage
+  // cbuf), then the two MFMAs of step kk with, between them, the probabilities 2^s of scores
+  // 2kk and 2kk+1 of both 32-key blocks, rounded to fp16 (the values PV consumes) and folded
+  // into a packed max.
+  auto qk_probs = [&](int kbuf, int cbuf, int tk, int tv, f32x16& sn0, f32x16& sn1, const f32x16& s0,
+                      const f32x16& s1, h8 (&pf)[4]) -> h2 {
     const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
     f32x16 init;
 #pragma unroll
@@ -311,8 +311,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int kk = 0; kk < 8; ++kk) {
       if (kk + 1 < 8) read_k(kbuf, kk + 1, ka[(kk + 1) & 1]);
       if (kk < 4) {
-        copy(tk, kbuf ^ 1, kk, std::true_type{});
-        copy(tv, kbuf, kk, std::false_type{});
+        copy(tk, cbuf, kk, std::true_type{});
+        copy(tv, cbuf, kk, std::false_type{});
       }
       __builtin_amdgcn_sched_barrier(0);
       sn0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[kk & 1][0], qf[kk], kk ? sn0 : init, 0, 0, 0);
@@ -360,13 +360,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   // ---- software-pipelined main loop ------------------------------------------------------
-  // When iteration kt starts, stage b = (kt - t_begin) & 1 holds K[kt] and V[kt] and stage b^1
-  // holds K[kt+1].  Iteration kt: the QK^T MFMAs of tile kt+1 (stage b^1) interleaved with the
-  // probabilities of tile kt and with the copies of K[kt+2] into stage b (its K was last read by
-  // the QK of iteration kt-1) and of V[kt+1] into stage b^1 (its V was last read by the PV of
-  // iteration kt-1); the rare reference update; PV of tile kt from stage b; then the copies are
-  // waited for and a barrier ends the iteration.  The loop is unrolled twice so that the current
-  // and next scores swap register sets instead of being copied.
+  // Tile j's K and V live in stage (j - t_begin) & 1.  Iteration kt reads only the other stage
+  // b' = (kt - 1 - t_begin) & 1 and copies only into stage b = (kt - t_begin) & 1:
+  //   1. PV of tile kt-1 (V from stage b', probabilities carried from the previous iteration)
+  //      with its row sums;
+  //   2. the QK^T MFMAs of tile kt+1 (K from stage b') interleaved with the probabilities of
+  //      tile kt and with the copies of K[kt+2] and V[kt] into stage b (last read in
+  //      iteration kt-1);
+  //   3. the rare reference update of tile kt;
+  //   4. wait for the copies and a barrier.
+  // So the transposing V reads of step 1 never wait for copies still in flight, and the copies
+  // have steps 2-3 to land.  The loop is unrolled twice so that the current and next scores
+  // swap register sets instead of being copied; the PV of the last tile follows the loop.
   {
     // zero-fill both stages once, so that rows of short tiles that no copy writes hold zeros
     u32x4* z = (u32x4*)smem;
@@ -377,7 +382,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     copy(t_begin, 0, j, std::true_type{});
-    copy(t_begin, 0, j, std::false_type{});
     copy(t_begin + 1 < t_stop ? t_begin + 1 : t_begin, 1, j, std::true_type{});
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -388,9 +392,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __syncthreads();
   int kt = t_begin;
   const int kt_mid = kt_full < t_begin ? t_begin : (kt_full < t_stop ? kt_full : t_stop);
+  h8 pf[4];   // probabilities of the tile whose PV is pending
   auto iteration = [&](auto masked_tag, f32x16& s0, f32x16& s1, f32x16& sn0, f32x16& sn1) {
     constexpr bool MT = decltype(masked_tag)::value;
     const int b = (kt - t_begin) & 1;
+    if (kt > t_begin) l_run += pv_sums(b ^ 1, pf);
     if constexpr (MT) {
       const int key0 = kt < ntA ? kt * BN : nA + (kt - ntA) * BN;
       const int cnt = kt < ntA ? nA - kt * BN : nkeys - key0;   // keys of the tile (capped below)
@@ -406,9 +412,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     // next tile's scores (on the last iteration from a stale, in-bounds stage, discarded)
     const int tk = kt + 2 < t_stop ? kt + 2 : t_stop - 1;
-    const int tv = kt + 1 < t_stop ? kt + 1 : t_stop - 1;
-    h8 pf[4];
-    const h2 pm = qk_probs(b ^ 1, tk, tv, sn0, sn1, s0, s1, pf);
+    const h2 pm = qk_probs(b ^ 1, b, tk, kt, sn0, sn1, s0, s1, pf);
     // Rare path: a row's first visible tile (reference still -inf) or probabilities above 2^8
     // (fp16 bits of a non-negative value above 0x5C00, which includes +inf).  The row's new
     // reference is its true max; the probabilities are recomputed, the running output and sum
@@ -418,7 +422,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint32_t pmb = __builtin_bit_cast(uint32_t, pm);
     const uint32_t pmx = (pmb & 0xFFFFu) > (pmb >> 16) ? (pmb & 0xFFFFu) : (pmb >> 16);
     const bool need1 = pmx > 0x5C00u || m_run == -INFINITY;
-    float alpha = 1.f;
     if (__builtin_expect(__any(need1), 0)) {
       const auto sw = __builtin_amdgcn_permlane32_swap(need1 ? 1u : 0u, need1 ? 1u : 0u, false, false);
       const bool need = (sw[0] | sw[1]) != 0u;     // either half of the row
@@ -426,7 +429,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int r = 1; r < 16; ++r) mt = fmaxf(mt, fmaxf(s0[r], s1[r]));
       mt = pair_max(mt);                           // row max of the shifted scores
-      float shift = 0.f;
+      float shift = 0.f, alpha = 1.f;
       if (need) {
         if (m_run == -INFINITY) {
           alpha = 0.f;
@@ -449,8 +452,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int bd = 0; bd < 4; ++bd)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[bd][r] *= alpha;
+      l_run *= alpha;
     }
-    l_run = l_run * alpha + pv_sums(b, pf);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -476,6 +479,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     iteration(std::true_type{}, sa0, sa1, sb0, sb1);
     ++kt;
   }
+  // PV of the last tile (its V was copied in the last iteration, before its barrier)
+  l_run += pv_sums((kt - 1 - t_begin) & 1, pf);
 
   // ---- epilogue: normalise and store bf16, or store the chunk's partial ---------------------
   const float lt = pair_sum(l_run);
@@ -546,14 +551,23 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_
 }  // namespace
 
 int attn_f16_splits(int64_t T, int32_t n_head) {
-  // Split the key range only when the target's query tiles cannot give every CU two
-  // workgroups (512 slots); then aim at about 1024 workgroups, at most 8 chunks.  Larger
-  // grids gain nothing from splitting and would pay for the partial outputs.
+  // Workgroups run two per CU (512 slots on 256 CUs).  Small grids are cut into key chunks to
+  // reach about 1024 workgroups (at most 8 chunks).  Larger grids are cut in two only when that
+  // removes a half-empty last round: 768 query tiles (the 4096-token target at 24 heads) take
+  // 1.5 rounds unsplit, 3 full rounds in two chunks.  The partial outputs and their merge cost
+  // a few percent, so a grid that already fills its rounds to 90 % stays whole.
   const int64_t units = (T + BM - 1) / BM * n_head;
-  if (units >= 512) return 1;
-  int64_t s = (1024 + units - 1) / units;
-  if (s > 8) s = 8;
-  return (int)s;
+  if (units < 512) {
+    int64_t s = (1024 + units - 1) / units;
+    if (s > 8) s = 8;
+    return (int)s;
+  }
+  auto fill = [&](int64_t s) {
+    const int64_t wg = units * s, rounds = (wg + 511) / 512;
+    return (double)wg / (double)(rounds * 512);
+  };
+  if (fill(1) >= 0.9) return 1;
+  return fill(2) > fill(1) ? 2 : 1;
 }
 
 int64_t attn_f16_partial_bytes(int64_t n_q, int32_t n_head) {
