@@ -8,10 +8,17 @@ one Euler update of the 4096 x 64 fp32 latent.  Inputs are synthetic (torch RNG,
 resident in HBM before timing starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg3|cfg3_t512|cfg2] [--no-cpu]
+    python bench.py --dit [--layers L] [--steps K]     # full single-stream layer steps (see below)
 
 Prints one JSON line.  value = attention TFLOP/s over the timed steps (visible-pair flops,
-4*d per pair); roofline = the attention kernel's own average launch time from HIP events
-recorded around each launch on the launch stream.
+4*d per pair); roofline = one attention call's average device time (the attention kernel plus,
+when the keys are cut in chunks, the merge kernel) from HIP events recorded around each call on
+the launch stream.
+
+--dit times the whole denoiser step of the 14,848-token workload (text 512 + 10 references 32x32
++ target 64x64, hidden 3072, 24x128 heads, SwiGLU 8192, random-init weights): step 1 over the
+whole sequence (filling the per-layer prefix caches) and the cached target-only steps, each with
+the conditioning, all layers, the head and the Euler update.  It prints its own JSON line.
 """
 from __future__ import annotations
 
@@ -98,6 +105,70 @@ def cpu_baseline(wl, budget_s: float = 12.0):
                       f"({T} queries x {S} keys, fp64 NumPy), {elapsed:.1f} s"}
 
 
+def dit_bench(args):
+    """Full single-stream layer steps at the 14,848-token shape (random-init weights)."""
+    import torch
+
+    import qi_inputs as qin
+    from image_generation_qi_amd import runtime as rt
+
+    wl = qin.WORKLOADS["cfg4"]
+    dev = "cuda:0"
+    D, F, H, NL = 3072, 8192, 24, args.layers
+    S, P, T = wl.S, wl.P, wl.T
+    log(f"dit workload: S={S} P={P} T={T} layers={NL}")
+    g = torch.Generator(device=dev).manual_seed(4321)
+
+    def lin(n_out, n_in):
+        return (torch.randn((n_out, n_in), generator=g, device=dev) / n_in ** 0.5).to(torch.bfloat16)
+
+    def vec(n, mean=0.0, std=0.02):
+        return torch.randn(n, generator=g, device=dev) * std + mean
+
+    layers = [rt.LayerWeights(vec(D), vec(D), vec(128, 1.0), vec(128, 1.0), lin(3 * D, D), lin(D, D), lin(F, D),
+                              lin(F, D), lin(D, F)) for _ in range(NL)]
+    shared = rt.SharedWeights(lin(D, 256), lin(D, D), lin(6 * D, D), lin(D, D), lin(64, D), lin(D, 64))
+    layout = rt.Layout(wl.segments, dev)
+    model = rt.DiT(layout, shared, layers, dev)
+    n_text = wl.segments[0].n_tokens
+    x_text = torch.randn((n_text, D), generator=g, device=dev)
+    lat_ref = torch.randn((P - n_text, 64), generator=g, device=dev)
+    lat = torch.randn((T, 64), generator=g, device=dev)
+    sig = qin.sigmas(8)
+    torch.cuda.synchronize()
+    # flops: GEMMs 2*M*(3D*D + D*D + 2F*D + D*F) per layer; attention 4*128*H*pairs
+    gemm_per_row = 2 * (3 * D * D + D * D + 2 * F * D + D * F)
+    pairs1 = visible_pairs_per_head(wl.segments)
+    f_step1 = NL * (S * gemm_per_row + 4.0 * 128 * H * pairs1)
+    f_cached = NL * (T * gemm_per_row + 4.0 * 128 * H * T * S)
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    model.step(0, lat, sig, x_text, lat_ref)       # warm-up (also fills the caches)
+    model.step(1, lat, sig)
+    torch.cuda.synchronize()
+    ms1 = timed(lambda: model.step(0, lat, sig, x_text, lat_ref))
+    cached = [timed(lambda k=k: model.step(k, lat, sig)) for k in range(1, 1 + args.steps)]
+    msc = sum(cached) / len(cached)
+    res = {
+        "metric": "single-stream DiT denoiser step time (conditioning + layers + head + Euler)",
+        "value": round(msc, 3), "unit": "ms per cached step", "higher_is_better": False,
+        "n_gpus": 1, "steps": args.steps, "dtype": "bf16", "data": "synthetic, random-init weights",
+        "config": {"workload": f"text {n_text} + 10 refs 32x32 + target 64x64 (S={S}, P={P}, T={T}); "
+                               f"hidden {D}, {H}x128 heads, SwiGLU {F}; {NL} layers",
+                   "step1_ms": round(ms1, 3), "step1_tflops": round(f_step1 / (ms1 * 1e-3) / 1e12, 1),
+                   "cached_step_tflops": round(f_cached / (msc * 1e-3) / 1e12, 1),
+                   "eight_step_loop_ms": round(ms1 + 7 * msc, 2)},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,10 +180,16 @@ def main():
     ap.add_argument("--step1", action="store_true", help="also time one full step-1 attention per layer")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 10 device-to-device copies of MIB MiB (reference kernel for HBM counters)")
+    ap.add_argument("--dit", action="store_true", help="time full single-stream layer steps instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.dit:
+        from image_generation_qi_amd import qi as Q
+        Q.lib()
+        dit_bench(args)
+        return
 
     import torch
 
@@ -178,6 +255,8 @@ def main():
     log(f"timed {args.steps} steps in {wall:.3f} s; attention kernel {kern_ms / max(n_launch, 1):.4f} ms/launch")
 
     flops_launch = 4.0 * 128 * H * T * (P + T)
+    ws_rows = 2 * H * T * 128 * 2
+    n_chunks = max(1, (Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, T, H) - ws_rows) // (T * H * 130 * 4))
     value = flops_launch * NL * args.steps / wall / 1e12
     avg_ms = kern_ms / max(n_launch, 1)
     achieved = flops_launch / (avg_ms * 1e-3) / 1e12
@@ -220,7 +299,8 @@ def main():
                    "pct_of_peak": round(100.0 * value / PEAK_F16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic_from_profile(),
-                     "kernel": "k_attn_f16<false>", "kernel_ms_per_launch": round(avg_ms, 4),
+                     "kernel": "k_attn_f16<false> + k_combine (one attention call)" if n_chunks > 1 else "k_attn_f16<false>",
+                     "key_chunks": n_chunks, "kernel_ms_per_launch": round(avg_ms, 4),
                      "flops_per_launch": flops_launch, "launches": n_launch},
     }
     res["config"].update(extra)

@@ -86,7 +86,19 @@ struct TimedLaunch {
   }
 };
 
-int launch_status(hipError_t e) { return e == hipSuccess ? QI_OK : QI_ERR_HIP; }
+// The HIP error of the last failed launch in this thread (0 if none), for diagnostics.
+thread_local int g_last_hip_error = 0;
+
+int launch_status(hipError_t e) {
+  if (e == hipSuccess) return QI_OK;
+  g_last_hip_error = (int)e;
+  return QI_ERR_HIP;
+}
+
+// hipGetLastError also reports errors of earlier, unrelated runtime calls in this thread (a
+// failed pointer query inside another library, say); clear it before this library launches so
+// that the status it returns belongs to its own launches.
+void clear_hip_error() { (void)hipGetLastError(); }
 
 // Prepare rows [0, n) of k (norm + rotation) and copy v into a [head][row][128] destination.
 int prep_kv(const void* k, const void* v, qi_dtype dtype, int64_t n, int32_t n_head, int64_t tok_stride,
@@ -151,6 +163,7 @@ extern "C" {
 
 int qi_rope3d_apply(void* x, qi_dtype dtype, int64_t n_tok, int32_t n_head, int64_t tok_stride,
                     const float* cos_t, const float* sin_t, const float* rms_w, float eps, void* stream) {
+  clear_hip_error();
   int st = check_tensor(x, dtype, n_tok, n_head, tok_stride);
   if (st != QI_OK) return st;
   if ((cos_t == nullptr) != (sin_t == nullptr)) return QI_ERR_ARG;
@@ -176,6 +189,7 @@ int qi_rope3d_apply(void* x, qi_dtype dtype, int64_t n_tok, int32_t n_head, int6
 int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_layout* layout, float scale,
                              const qi_kvcache* cache, int32_t layer, void* workspace, int64_t workspace_bytes,
                              void* stream) {
+  clear_hip_error();
   if (!io) return QI_ERR_ARG;
   LayoutInfo li;
   int st = analyse_layout(layout, &li);
@@ -252,6 +266,7 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
 
 int qi_attn_prefix_store(const void* k, const void* v, qi_dtype dtype, int64_t P, int32_t n_head, int64_t tok_stride,
                          const qi_qkprep* prep, const qi_kvcache* cache, int32_t layer, void* stream) {
+  clear_hip_error();
   int st;
   if (P < 0) return QI_ERR_SHAPE;
   if (P == 0) {
@@ -270,6 +285,7 @@ int qi_attn_prefix_store(const void* k, const void* v, qi_dtype dtype, int64_t P
 
 int qi_attn_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvcache* cache, int32_t layer,
                           int64_t P, float scale, void* workspace, int64_t workspace_bytes, void* stream) {
+  clear_hip_error();
   if (!io) return QI_ERR_ARG;
   int st;
   if ((st = check_tensor(io->q, io->dtype, io->n_tok, io->n_head, io->tok_stride)) != QI_OK) return st;
@@ -309,6 +325,7 @@ int qi_attn_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvca
 
 int qi_euler_step(float* x, const void* v, qi_dtype v_dtype, int64_t n, float sigma_k, float sigma_k1,
                   void* stream) {
+  clear_hip_error();
   if (!x || !v) return QI_ERR_ARG;
   if (n < 0) return QI_ERR_SHAPE;
   if (v_dtype != QI_F32 && v_dtype != QI_BF16) return QI_ERR_DTYPE;
@@ -321,6 +338,7 @@ int qi_euler_step(float* x, const void* v, qi_dtype v_dtype, int64_t n, float si
 
 int qi_gemm_bf16(const void* x, int64_t ldx, const void* w, void* out, int64_t ldo, int64_t M, int64_t N, int64_t K,
                  int epilogue, const float* gate, int64_t row0, int64_t P, void* stream) {
+  clear_hip_error();
   if (!x || !w || !out) return QI_ERR_ARG;
   if (epilogue < QI_EPI_STORE || epilogue > QI_EPI_SWIGLU) return QI_ERR_ARG;
   if (epilogue == QI_EPI_GATED_RESIDUAL && !gate) return QI_ERR_ARG;
@@ -335,6 +353,7 @@ int qi_gemm_bf16(const void* x, int64_t ldx, const void* w, void* out, int64_t l
 
 int qi_zc_rmsnorm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64_t M, int32_t D, const float* w,
                       const float* scale, const float* shift, int64_t row0, int64_t P, float eps, void* stream) {
+  clear_hip_error();
   if (!x || !out) return QI_ERR_ARG;
   if (M < 0 || D < 4 || (D % 4) || ldx < D || ldo < D || M > INT32_MAX) return QI_ERR_SHAPE;
   if (!(eps >= 0.f) || !std::isfinite(eps)) return QI_ERR_ARG;
@@ -347,6 +366,7 @@ int qi_zc_rmsnorm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64
 }
 
 int qi_timestep_embed(const float* t, int32_t n, int32_t dim, float* out, void* stream) {
+  clear_hip_error();
   if (!t || !out) return QI_ERR_ARG;
   if (n < 0 || dim < 2 || (dim % 2)) return QI_ERR_SHAPE;
   return launch_status(launch_timestep_embed(t, n, dim, out, (hipStream_t)stream));
@@ -354,6 +374,7 @@ int qi_timestep_embed(const float* t, int32_t n, int32_t dim, float* out, void* 
 
 int qi_linear_small(const float* x, int32_t n_vec, int32_t I, const void* w, int32_t O, int32_t silu_in, float* y,
                     void* stream) {
+  clear_hip_error();
   if (!x || !w || !y) return QI_ERR_ARG;
   if (n_vec < 1 || n_vec > 4 || I < 8 || (I % 8) || O < 0) return QI_ERR_SHAPE;
   if (!aligned16(w)) return QI_ERR_ALIGN;
@@ -361,10 +382,15 @@ int qi_linear_small(const float* x, int32_t n_vec, int32_t I, const void* w, int
 }
 
 int qi_cast_bf16(const float* x, void* y, int64_t n, void* stream) {
+  clear_hip_error();
   if (!x || !y) return QI_ERR_ARG;
   if (n < 0) return QI_ERR_SHAPE;
   return launch_status(launch_cast_bf16(x, y, n, (hipStream_t)stream));
 }
+
+int qi_last_hip_error(void) { return g_last_hip_error; }
+
+const char* qi_hip_error_name(int error) { return hipGetErrorName((hipError_t)error); }
 
 int qi_kernel_timing(int enable) {
   std::lock_guard<std::mutex> lk(g_tmu);

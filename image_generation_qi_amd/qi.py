@@ -32,7 +32,11 @@ class QiLibraryMissing(RuntimeError):
 class QiError(RuntimeError):
     def __init__(self, status: int, where: str = ""):
         self.status = status
-        super().__init__(f"{where}: {qi_status_str(status)} ({status})")
+        msg = f"{where}: {qi_status_str(status)} ({status})"
+        if status == QI_ERR_HIP:
+            code = lib().qi_last_hip_error()
+            msg += f" [HIP error {code}: {lib().qi_hip_error_name(code).decode()}]"
+        super().__init__(msg)
 
 
 class qi_segment(ctypes.Structure):
@@ -62,6 +66,8 @@ class qi_qkprep(ctypes.Structure):
 
 _SIGS = {
     "qi_status_str": (c_char_p, [c_int]),
+    "qi_last_hip_error": (c_int, []),
+    "qi_hip_error_name": (c_char_p, [c_int]),
     "qi_version": (c_int, []),
     "qi_layout_tokens": (c_int, [POINTER(qi_layout), POINTER(c_int64), POINTER(c_int64), POINTER(c_int64)]),
     "qi_rope3d_positions": (c_int, [POINTER(qi_layout), c_void_p]),
@@ -101,6 +107,14 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise QiLibraryMissing(f"{LIB_PATH} not found: build it with `python -m image_generation_qi_amd.build`"
                                    " (or __graft_entry__.build())")
+        # PyTorch bundles its own HIP runtime (same soname as the system one, but its libraries
+        # ask for it by another name).  Loaded first, it is the one this library binds to;
+        # loaded after this library, the process would hold two runtimes and launches made
+        # through this one fail with hipErrorNoDevice.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             fn = getattr(L, name)

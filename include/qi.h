@@ -253,6 +253,11 @@ int qi_linear_small(const float* x, int32_t n_vec, int32_t I, const void* w, int
 /* fp32 -> bf16 (nearest even) of n elements (latents into the img_in projection). */
 int qi_cast_bf16(const float* x, void* y, int64_t n, void* stream);
 
+/* HIP error code of the last launch of this library that failed in the calling thread (the
+ * cause behind a QI_ERR_HIP status; 0 if none), and its name (a static string). */
+int qi_last_hip_error(void);
+const char* qi_hip_error_name(int error);
+
 /* ------------------------------------------------------------------------------------------
  * Measurement hooks
  * ------------------------------------------------------------------------------------------ */
