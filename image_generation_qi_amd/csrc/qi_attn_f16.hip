@@ -551,23 +551,16 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_
 }  // namespace
 
 int attn_f16_splits(int64_t T, int32_t n_head) {
-  // Workgroups run two per CU (512 slots on 256 CUs).  Small grids are cut into key chunks to
-  // reach about 1024 workgroups (at most 8 chunks).  Larger grids are cut in two only when that
-  // removes a half-empty last round: 768 query tiles (the 4096-token target at 24 heads) take
-  // 1.5 rounds unsplit, 3 full rounds in two chunks.  The partial outputs and their merge cost
-  // a few percent, so a grid that already fills its rounds to 90 % stays whole.
+  // Split the key range only when the target's query tiles cannot give every CU two
+  // workgroups (512 slots); then aim at about 1024 workgroups, at most 8 chunks.  Larger grids
+  // stay whole: at 768 query tiles (the 4096-token target at 24 heads) two chunks would fill the
+  // last round of workgroups (3 % faster) but fetch the keys from memory almost twice and move
+  // 200 MB of partial outputs through the merge.
   const int64_t units = (T + BM - 1) / BM * n_head;
-  if (units < 512) {
-    int64_t s = (1024 + units - 1) / units;
-    if (s > 8) s = 8;
-    return (int)s;
-  }
-  auto fill = [&](int64_t s) {
-    const int64_t wg = units * s, rounds = (wg + 511) / 512;
-    return (double)wg / (double)(rounds * 512);
-  };
-  if (fill(1) >= 0.9) return 1;
-  return fill(2) > fill(1) ? 2 : 1;
+  if (units >= 512) return 1;
+  int64_t s = (1024 + units - 1) / units;
+  if (s > 8) s = 8;
+  return (int)s;
 }
 
 int64_t attn_f16_partial_bytes(int64_t n_q, int32_t n_head) {

@@ -120,12 +120,9 @@ def test_tile_shape_and_sizes():
     assert Q.qi_attn_tile_shape(Q.QI_BF16) == (128, 64)
     assert Q.qi_attn_tile_shape(Q.QI_F32) == (1, 64)
     L3 = Q.make_layout(qin.WORKLOADS["cfg3"].segments)
-    # 4096-token target: 32 x 24 = 768 query tiles fill 1.5 rounds of 512 workgroup slots, so the
-    # keys are cut in two chunks (3 full rounds): K/V fp16 rows plus two sets of fp32 partials
-    assert Q.qi_attn_full_workspace_bytes(L3, Q.QI_BF16, 24) == 2 * 24 * 21504 * 128 * 2 + 2 * 21504 * 24 * 130 * 4
-    assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, 4096, 24) == 2 * 24 * 4096 * 128 * 2 + 2 * 4096 * 24 * 130 * 4
-    # 1024 query tiles fill two rounds exactly: no chunks
-    assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, 4096, 32) == 2 * 32 * 4096 * 128 * 2
+    # 4096-token target: 32 x 24 = 768 query tiles fill the GPU, no key chunks: K/V fp16 rows only
+    assert Q.qi_attn_full_workspace_bytes(L3, Q.QI_BF16, 24) == 2 * 24 * 21504 * 128 * 2
+    assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, 4096, 24) == 2 * 24 * 4096 * 128 * 2
     # config[1]: 8 x 24 = 192 units -> 6 key chunks of fp32 partials (128 values + max + sum)
     L1 = Q.make_layout(qin.WORKLOADS["cfg1"].segments)
     assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, 1024, 24) == 2 * 24 * 1024 * 128 * 2 + 6 * 1024 * 24 * 130 * 4
