@@ -336,19 +336,28 @@ int qi_euler_step(float* x, const void* v, qi_dtype v_dtype, int64_t n, float si
   return launch_status(launch_euler(x, v, v_dtype == QI_BF16, n, sigma_k1 - sigma_k, (hipStream_t)stream));
 }
 
-int qi_gemm_bf16(const void* x, int64_t ldx, const void* w, void* out, int64_t ldo, int64_t M, int64_t N, int64_t K,
-                 int epilogue, const float* gate, int64_t row0, int64_t P, void* stream) {
+int qi_gemm_bf16_ex(const void* x, int64_t ldx, const void* w, void* out, int64_t ldo, int64_t M, int64_t N,
+                    int64_t K, int epilogue, const float* gate, int64_t row0, int64_t P, int32_t tile_n, void* stream) {
   clear_hip_error();
   if (!x || !w || !out) return QI_ERR_ARG;
   if (epilogue < QI_EPI_STORE || epilogue > QI_EPI_SWIGLU) return QI_ERR_ARG;
   if (epilogue == QI_EPI_GATED_RESIDUAL && !gate) return QI_ERR_ARG;
-  if (M < 0 || N < 64 || K < 64 || (N % 64) || (K % 64) || M > 65535LL * 128 || N > INT32_MAX) return QI_ERR_SHAPE;
+  if (tile_n != 0 && tile_n != 256 && tile_n != 192 && tile_n != 128) return QI_ERR_ARG;
+  if (tile_n == 192 && epilogue == QI_EPI_SWIGLU) return QI_ERR_ARG;
+  if (M < 0 || N < 64 || K < 64 || (N % 64) || (K % 64)) return QI_ERR_SHAPE;
   if (ldx < K || ldo < (epilogue == QI_EPI_SWIGLU ? N / 2 : N)) return QI_ERR_SHAPE;
+  // x and w are addressed through buffer resources with 32-bit byte offsets
+  if (M * ldx * 2 > INT32_MAX || N * K * 2 > INT32_MAX) return QI_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(w) || !aligned16(out) || !aligned16(gate) || (ldx % 8) || (ldo % 8))
     return QI_ERR_ALIGN;
   if (M == 0) return QI_OK;
   GemmArgs a{x, ldx, w, out, ldo, M, N, K, gate, row0, P};
-  return launch_status(launch_gemm(a, epilogue, (hipStream_t)stream));
+  return launch_status(launch_gemm(a, epilogue, tile_n, (hipStream_t)stream));
+}
+
+int qi_gemm_bf16(const void* x, int64_t ldx, const void* w, void* out, int64_t ldo, int64_t M, int64_t N, int64_t K,
+                 int epilogue, const float* gate, int64_t row0, int64_t P, void* stream) {
+  return qi_gemm_bf16_ex(x, ldx, w, out, ldo, M, N, K, epilogue, gate, row0, P, 0, stream);
 }
 
 int qi_zc_rmsnorm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64_t M, int32_t D, const float* w,

@@ -1,5 +1,5 @@
 // qi_dit.hip - the non-attention kernels of one single-stream DiT layer step on gfx950:
-//   - k_gemm<EPI>: y = x W^T on bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulation) with
+//   - k_gemm_big<EPI, BN>: y = x W^T on bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulation) with
 //     fused epilogues: bf16 store (QKV projection), fp32 store (img_in, velocity head),
 //     tanh-gated residual add into the fp32 residual stream (attention out-projection and FFN
 //     down-projection), and SwiGLU (FFN gate|up projection) ("Qwen-Image-2.1" course overview,
@@ -28,10 +28,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
-constexpr int GBM = 128;   // tokens per workgroup tile
-constexpr int GBN = 128;   // output features per workgroup tile
 constexpr int GBK = 64;    // reduction slice per LDS stage
-constexpr int GTILE = 128 * GBK;   // bf16 elements of one X or W stage tile (16 KB)
 
 __device__ __forceinline__ uint32_t to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
@@ -42,6 +39,14 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// blockIdx -> logical tile: the hardware hands consecutive workgroups to the 8 XCDs in turn;
+// this gives each XCD a contiguous run of logical tiles (which then share panels in its L2).
+__device__ __forceinline__ int xcd_order(int bid, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int xcd = bid & 7, slot = bid >> 3;
+  return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + slot;
+}
+
 __device__ __forceinline__ void load_lds16(const void* src, void* dst_wave_base) {
   __builtin_amdgcn_global_load_lds((const glb_void*)src, (lds_void*)dst_wave_base, 16, 0, 0);
 }
@@ -51,126 +56,171 @@ __device__ __forceinline__ void load_lds16(const void* src, void* dst_wave_base)
 // 16 distinct bank groups.
 __device__ __forceinline__ int gswz(int r) { return (r >> 1) & 7; }
 
-template <int EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * GTILE];   // [stage][X | W]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, l32 = lane & 31;
-  const int wm = wave & 1, wn = wave >> 1;          // wave's 64x64 quadrant of the tile
-  const int64_t m0 = (int64_t)blockIdx.y * GBM;
-  const int64_t n0 = (int64_t)blockIdx.x * GBN;
+// ---- large-tile GEMM: 256 x BN workgroup tiles, one wavefront per SIMD ------------------------
+// Four waves in a 2 x 2 grid, each owning 128 tokens x BN/2 features as 4 x (BN/64) blocks of
+// 32 x 32 (accumulators in the accumulation registers).  Per reduction step of 16 every X operand
+// read from LDS feeds BN/64 MFMAs and every W operand four: half the LDS bytes per MFMA of 64 x 64
+// wave tiles, which at two workgroups per CU would need about all of the LDS bandwidth.  Stage tiles are
+// copied by MUBUF buffer -> LDS loads (exact LDS waits while copies are in flight) into 128-byte
+// rows with the (row/2)-XOR chunk swizzle; rows past M or N fall outside the buffer resources and
+// are not read (their results are never stored).
+constexpr int BBM = 256;
 
-  // direct loads: wave w fills rows 32w..32w+31 of both stage tiles with 4 loads of 1 KB (8 rows);
-  // lane i of load j covers row 32w + 8j + i/8 at chunk position i%8.  Rows past M or N re-read
-  // the last valid row (results for them are never stored).
-  const __bf16* xs[4];
-  const __bf16* ws[4];
+template <int EPI, int BN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_big(GemmArgs a) {
+  constexpr int WN = BN / 2;              // features per wave
+  constexpr int NB = WN / 32;             // 32-feature blocks per wave
+  constexpr int MB = 4;                   // 32-token blocks per wave
+  constexpr int XT = BBM * GBK, WT = BN * GBK;
+  constexpr int WROWS = BN / 4;           // W rows each wave copies per stage
+  constexpr int NXC = 8, NWC = WROWS / 8; // copies of 1 KB (8 rows) per wave and stage
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (XT + WT)];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // tile order: groups of 8 token tiles sweep all feature tiles, so that workgroups running at
+  // the same time share both X and W panels in L2; the groups are spread over the XCDs
+  const int tiles_m = (int)((a.M + BBM - 1) / BBM), tiles_n = (int)((a.N + BN - 1) / BN);
+  const int t = xcd_order(blockIdx.x, gridDim.x);
+  const int per_group = 8 * tiles_n;
+  const int first_m = (t / per_group) * 8;
+  const int gsize = tiles_m - first_m < 8 ? tiles_m - first_m : 8;
+  const int tm = first_m + (t % per_group) % gsize, tn = (t % per_group) / gsize;
+  const int64_t m0 = (int64_t)tm * BBM, n0 = (int64_t)tn * BN;
+
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)(a.M * a.ldx * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, (short)0, (int)(a.N * a.K * 2), 0x00020000);
+  // lane i of copy j: row (within the wave's rows) 8j + i/8, chunk position i%8.  (Arrays touched
+  // by the lambdas below have fixed sizes: with sizes that depend on BN the host compiler silently
+  // drops the kernel instance and its launch stub.)
+  int xo[8], wo[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 32 * wave + 8 * j + (lane >> 3);
-    const int chunk = (lane & 7) ^ gswz(row);
-    int64_t mr = m0 + row, nr = n0 + row;
-    if (mr >= a.M) mr = a.M - 1;
-    if (nr >= a.N) nr = a.N - 1;
-    xs[j] = (const __bf16*)a.x + mr * a.ldx + 8 * chunk;
-    ws[j] = (const __bf16*)a.w + nr * a.K + 8 * chunk;
+  for (int j = 0; j < NXC; ++j) {
+    const int row = 64 * wave + 8 * j + (lane >> 3);
+    xo[j] = (int)((m0 + row) * a.ldx * 2) + 16 * ((lane & 7) ^ gswz(row));
   }
-  auto load_stage = [&](int kt, int st) {
-    __bf16* X = smem + st * 2 * GTILE + (32 * wave) * GBK;
-    __bf16* W = X + GTILE;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      load_lds16(xs[j] + (int64_t)kt * GBK, X + j * 8 * GBK);
-      load_lds16(ws[j] + (int64_t)kt * GBK, W + j * 8 * GBK);
+  for (int j = 0; j < NWC; ++j) {
+    const int row = WROWS * wave + 8 * j + (lane >> 3);
+    wo[j] = (int)((n0 + row) * a.K * 2) + 16 * ((lane & 7) ^ gswz(row));
+  }
+  auto copy_x = [&](int kt, int st, int j) {
+    __bf16* dst = smem + st * (XT + WT) + (64 * wave + 8 * j) * GBK;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)dst, 16, xo[j], kt * GBK * 2, 0, 0);
+  };
+  auto copy_w = [&](int kt, int st, int j) {
+    __bf16* dst = smem + st * (XT + WT) + XT + (WROWS * wave + 8 * j) * GBK;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)dst, 16, wo[j], kt * GBK * 2, 0, 0);
+  };
+  // operands of reduction step kk from stage st
+  auto read_ops = [&](int st, int kk, bf8 (&xf)[4], bf8 (&wf)[4]) {
+    const __bf16* X = smem + st * (XT + WT);
+    const __bf16* W = X + XT;
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      const int r = 128 * wm + 32 * b + l32;
+      xf[b] = *(const bf8*)(X + r * GBK + 8 * ((2 * kk + g) ^ gswz(r)));
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int r = WN * wn + 32 * b + l32;
+      wf[b] = *(const bf8*)(W + r * GBK + 8 * ((2 * kk + g) ^ gswz(r)));
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[MB][NB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nkt = (int)(a.K / GBK);
-  load_stage(0, 0);
+#pragma unroll
+  for (int j = 0; j < NXC; ++j) copy_x(0, 0, j);
+#pragma unroll
+  for (int j = 0; j < NWC; ++j) copy_w(0, 0, j);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
     const int st = kt & 1;
-    if (kt + 1 < nkt) load_stage(kt + 1, st ^ 1);
-    const __bf16* X = smem + st * 2 * GTILE;
-    const __bf16* W = X + GTILE;
+    const int kn = kt + 1 < nkt ? kt + 1 : kt;   // the last step re-copies its own tile into the free stage
+    bf8 xf[2][4], wf[2][4];
+    read_ops(st, 0, xf[0], wf[0]);
 #pragma unroll
     for (int kk = 0; kk < GBK / 16; ++kk) {
-      bf8 wf[2], xf[2];
+      // operands of step kk + 1 and a quarter of the next stage's copies, then this step's MFMAs
+      if (kk + 1 < GBK / 16) read_ops(st, kk + 1, xf[(kk + 1) & 1], wf[(kk + 1) & 1]);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int rw = 64 * wn + 32 * b + l32;
-        const int rx = 64 * wm + 32 * b + l32;
-        wf[b] = *(const bf8*)(W + rw * GBK + 8 * ((2 * kk + g) ^ gswz(rw)));
-        xf[b] = *(const bf8*)(X + rx * GBK + 8 * ((2 * kk + g) ^ gswz(rx)));
-      }
+      for (int j = 0; j < NXC / 4; ++j) copy_x(kn, st ^ 1, kk * (NXC / 4) + j);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int j = 0; j < (NWC + 3) / 4; ++j)
+        if (kk * ((NWC + 3) / 4) + j < NWC) copy_w(kn, st ^ 1, kk * ((NWC + 3) / 4) + j);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], xf[mb], acc[mb][nb], 0, 0, 0);
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[kk & 1][nb], xf[kk & 1][mb], acc[mb][nb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
-  // epilogue: acc[mb][nb][r] = y[m][n] with m = m0 + 64wm + 32mb + l32 and
-  // n = n0 + 64wn + 32nb + 8(r/4) + 4g + r%4 (four consecutive features per r/4)
+  // epilogue: acc[mb][nb][r] = y[m][n], m = m0 + 128wm + 32mb + l32,
+  // n = n0 + WN*wn + 32nb + 8(r/4) + 4g + r%4
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int64_t m = m0 + 64 * wm + 32 * mb + l32;
+  for (int mb = 0; mb < MB; ++mb) {
+    const int64_t m = m0 + 128 * wm + 32 * mb + l32;
     if (m >= a.M) continue;
-    if (EPI == QI_EPI_SWIGLU) {
-      // weight rows come in blocks of 64: 32 gate rows then the 32 up rows of the same features
-      if (n0 + 64 * wn >= a.N) continue;   // N % 128 == 64: the last tile's upper half is empty
-      const int64_t f0 = (n0 + 64 * wn) / 2;
-      __bf16* op = (__bf16*)a.out + m * a.ldo + f0 + 4 * g;
+    if constexpr (EPI == QI_EPI_SWIGLU) {
+      // weight rows in blocks of 64: 32 gate rows, then the 32 up rows of the same features
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        uint32_t w2[2];
+      for (int blk = 0; blk < NB / 2; ++blk) {
+        if (n0 + WN * wn + 64 * blk >= a.N) continue;
+        const int64_t f0 = (n0 + WN * wn + 64 * blk) / 2;
+        __bf16* op = (__bf16*)a.out + m * a.ldo + f0 + 4 * g;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          float v[2];
+        for (int r4 = 0; r4 < 4; ++r4) {
+          uint32_t w2[2];
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const float gt = acc[mb][0][4 * r4 + 2 * h + e], up = acc[mb][1][4 * r4 + 2 * h + e];
-            v[e] = gt / (1.0f + __expf(-gt)) * up;
+          for (int h = 0; h < 2; ++h) {
+            float v[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const float gt = acc[mb][2 * blk][4 * r4 + 2 * h + e], up = acc[mb][2 * blk + 1][4 * r4 + 2 * h + e];
+              v[e] = gt / (1.0f + __expf(-gt)) * up;
+            }
+            w2[h] = to_bf16(v[0]) | (to_bf16(v[1]) << 16);
           }
-          w2[h] = to_bf16(v[0]) | (to_bf16(v[1]) << 16);
+          *(u32x2*)(op + 8 * r4) = u32x2{w2[0], w2[1]};
         }
-        *(u32x2*)(op + 8 * r4) = u32x2{w2[0], w2[1]};
       }
-      continue;
-    }
+    } else {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int64_t nbase = n0 + 64 * wn + 32 * nb + 4 * g;
+      for (int nb = 0; nb < NB; ++nb) {
+        const int64_t nbase = n0 + WN * wn + 32 * nb + 4 * g;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int64_t n = nbase + 8 * r4;
-        if (n >= a.N) continue;
-        const f32x4 y = {acc[mb][nb][4 * r4], acc[mb][nb][4 * r4 + 1], acc[mb][nb][4 * r4 + 2], acc[mb][nb][4 * r4 + 3]};
-        if (EPI == QI_EPI_STORE) {
-          *(u32x2*)((__bf16*)a.out + m * a.ldo + n) =
-              u32x2{to_bf16(y[0]) | (to_bf16(y[1]) << 16), to_bf16(y[2]) | (to_bf16(y[3]) << 16)};
-        } else if (EPI == QI_EPI_STORE_F32) {
-          *(f32x4*)((float*)a.out + m * a.ldo + n) = y;
-        } else {  // QI_EPI_GATED_RESIDUAL: x += tanh(gate) * y, gate by the row's segment
-          const float* gv = a.gate + ((m + a.row0 < a.P) ? 0 : a.N) + n;
-          const f32x4 gt = *(const f32x4*)gv;
-          f32x4* xp = (f32x4*)((float*)a.out + m * a.ldo + n);
-          f32x4 xv = *xp;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int64_t n = nbase + 8 * r4;
+          if (n >= a.N) continue;
+          const f32x4 y = {acc[mb][nb][4 * r4], acc[mb][nb][4 * r4 + 1], acc[mb][nb][4 * r4 + 2], acc[mb][nb][4 * r4 + 3]};
+          if constexpr (EPI == QI_EPI_STORE) {
+            *(u32x2*)((__bf16*)a.out + m * a.ldo + n) =
+                u32x2{to_bf16(y[0]) | (to_bf16(y[1]) << 16), to_bf16(y[2]) | (to_bf16(y[3]) << 16)};
+          } else if constexpr (EPI == QI_EPI_STORE_F32) {
+            *(f32x4*)((float*)a.out + m * a.ldo + n) = y;
+          } else {  // QI_EPI_GATED_RESIDUAL
+            const f32x4 gt = *(const f32x4*)(a.gate + ((m + a.row0 < a.P) ? 0 : a.N) + n);
+            f32x4* xp = (f32x4*)((float*)a.out + m * a.ldo + n);
+            f32x4 xv = *xp;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) xv[e] = __builtin_fmaf(tanhf(gt[e]), y[e], xv[e]);
-          *xp = xv;
+            for (int e = 0; e < 4; ++e) xv[e] = __builtin_fmaf(tanhf(gt[e]), y[e], xv[e]);
+            *xp = xv;
+          }
         }
       }
     }
@@ -268,17 +318,74 @@ __global__ void k_cast_bf16(const float* __restrict__ x, __bf16* __restrict__ y,
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s) {
-  if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.N + GBN - 1) / GBN), (unsigned)((a.M + GBM - 1) / GBM));
-  switch (epi) {
-    case QI_EPI_STORE: hipLaunchKernelGGL(k_gemm<QI_EPI_STORE>, grid, dim3(256), 0, s, a); break;
-    case QI_EPI_STORE_F32: hipLaunchKernelGGL(k_gemm<QI_EPI_STORE_F32>, grid, dim3(256), 0, s, a); break;
-    case QI_EPI_GATED_RESIDUAL: hipLaunchKernelGGL(k_gemm<QI_EPI_GATED_RESIDUAL>, grid, dim3(256), 0, s, a); break;
-    case QI_EPI_SWIGLU: hipLaunchKernelGGL(k_gemm<QI_EPI_SWIGLU>, grid, dim3(256), 0, s, a); break;
-    default: return hipErrorInvalidValue;
+namespace {
+
+// Kernel template instances are launched from plain functions: instantiated only inside another
+// function template, their host stubs are not emitted by this compiler.
+#define QI_LAUNCH_BIG(EPI_, BN_) \
+  hipLaunchKernelGGL((k_gemm_big<EPI_, BN_>), dim3(blocks), dim3(256), 0, s, a)
+
+hipError_t launch_big(const GemmArgs& a, int epi, int bn, hipStream_t s) {
+  const unsigned blocks = (unsigned)(((a.M + BBM - 1) / BBM) * ((a.N + bn - 1) / bn));
+  if (bn == 256) {
+    switch (epi) {
+      case QI_EPI_STORE: QI_LAUNCH_BIG(QI_EPI_STORE, 256); break;
+      case QI_EPI_STORE_F32: QI_LAUNCH_BIG(QI_EPI_STORE_F32, 256); break;
+      case QI_EPI_GATED_RESIDUAL: QI_LAUNCH_BIG(QI_EPI_GATED_RESIDUAL, 256); break;
+      case QI_EPI_SWIGLU: QI_LAUNCH_BIG(QI_EPI_SWIGLU, 256); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (bn == 192) {
+    switch (epi) {
+      case QI_EPI_STORE: QI_LAUNCH_BIG(QI_EPI_STORE, 192); break;
+      case QI_EPI_STORE_F32: QI_LAUNCH_BIG(QI_EPI_STORE_F32, 192); break;
+      case QI_EPI_GATED_RESIDUAL: QI_LAUNCH_BIG(QI_EPI_GATED_RESIDUAL, 192); break;
+      default: return hipErrorInvalidValue;   // SwiGLU needs whole 64-row gate|up blocks per wave
+    }
+  } else if (bn == 128) {
+    switch (epi) {
+      case QI_EPI_STORE: QI_LAUNCH_BIG(QI_EPI_STORE, 128); break;
+      case QI_EPI_STORE_F32: QI_LAUNCH_BIG(QI_EPI_STORE_F32, 128); break;
+      case QI_EPI_GATED_RESIDUAL: QI_LAUNCH_BIG(QI_EPI_GATED_RESIDUAL, 128); break;
+      case QI_EPI_SWIGLU: QI_LAUNCH_BIG(QI_EPI_SWIGLU, 128); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+#undef QI_LAUNCH_BIG
+
+}  // namespace
+
+int gemm_config(int64_t M, int64_t N, int epi) {
+  // Feature width BN of the 256 x BN tiles: the least tile area per CU over whole rounds of 256
+  // workgroups (one per CU), weighted by the LDS bytes per MFMA of the tile (per wave and step,
+  // 4 + BN/64 operand reads for 4 * BN/64 MFMAs: 0.50, 0.58, 0.75 for 256, 192, 128; measured
+  // rates follow this order when the rounds are equal).  E.g. 4096 x 3072 is exactly 256 tiles of
+  // 256 x 192 but 192 tiles of 256 x 256; 4096 x 16384 fills four rounds of 256 x 256.
+  int best = 256;
+  double best_cost = 0.0;
+  const int cands[3] = {256, 192, 128};
+  for (int bn : cands) {
+    if (bn == 192 && epi == QI_EPI_SWIGLU) continue;   // SwiGLU needs whole 64-row gate|up blocks per wave
+    const int64_t tiles = ((M + BBM - 1) / BBM) * ((N + bn - 1) / bn);
+    const int64_t rounds = (tiles + 255) / 256;
+    double cost = (double)rounds * (double)(BBM * bn);
+    if (bn == 192) cost *= 1.1;
+    if (bn == 128) cost *= 1.2;
+    if (best_cost == 0.0 || cost < best_cost) {
+      best_cost = cost;
+      best = bn;
+    }
+  }
+  return best;
+}
+
+hipError_t launch_gemm(const GemmArgs& a, int epi, int tile_n, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  return launch_big(a, epi, tile_n ? tile_n : gemm_config(a.M, a.N, epi), s);
 }
 
 hipError_t launch_zc_norm_mod(const NormArgs& a, hipStream_t s) {

@@ -97,7 +97,10 @@ struct NormArgs {
   float eps;
 };
 
-hipError_t launch_gemm(const GemmArgs& a, int epilogue, hipStream_t s);
+// tile_n: feature width of the 256 x tile_n workgroup tiles (256, 192 or 128; 192 not with
+// SwiGLU), 0 = chosen by gemm_config.
+hipError_t launch_gemm(const GemmArgs& a, int epilogue, int tile_n, hipStream_t s);
+int gemm_config(int64_t M, int64_t N, int epilogue);
 hipError_t launch_zc_norm_mod(const NormArgs& a, hipStream_t s);
 hipError_t launch_timestep_embed(const float* t, int n, int dim, float* out, hipStream_t s);
 hipError_t launch_linear_small(const float* x, int nv, int I, const void* w, int O, int silu_in, float* y,

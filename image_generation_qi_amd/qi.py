@@ -88,6 +88,8 @@ _SIGS = {
     "qi_euler_step": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_float, c_float, c_void_p]),
     "qi_gemm_bf16": (c_int, [c_void_p, c_int64, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int64, c_int,
                              c_void_p, c_int64, c_int64, c_void_p]),
+    "qi_gemm_bf16_ex": (c_int, [c_void_p, c_int64, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int64, c_int,
+                                c_void_p, c_int64, c_int64, c_int32, c_void_p]),
     "qi_zc_rmsnorm_mod": (c_int, [c_void_p, c_int64, c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p,
                                   c_void_p, c_int64, c_int64, c_float, c_void_p]),
     "qi_timestep_embed": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
@@ -258,6 +260,12 @@ def qi_euler_step(x, v, v_dtype: int, n: int, sigma_k: float, sigma_k1: float, s
 def qi_gemm_bf16(x, ldx: int, w, out, ldo: int, M: int, N: int, K: int, epilogue: int, gate=None, row0: int = 0,
                  P: int = 0, stream=None) -> int:
     return lib().qi_gemm_bf16(_p(x), ldx, _p(w), _p(out), ldo, M, N, K, epilogue, _p(gate), row0, P, _p(stream))
+
+
+def qi_gemm_bf16_ex(x, ldx: int, w, out, ldo: int, M: int, N: int, K: int, epilogue: int, gate=None, row0: int = 0,
+                    P: int = 0, tile_n: int = 0, stream=None) -> int:
+    return lib().qi_gemm_bf16_ex(_p(x), ldx, _p(w), _p(out), ldo, M, N, K, epilogue, _p(gate), row0, P, tile_n,
+                                 _p(stream))
 
 
 def qi_zc_rmsnorm_mod(x, ldx: int, out, ldo: int, M: int, D: int, w=None, scale=None, shift=None, row0: int = 0,

@@ -162,13 +162,14 @@ class SharedWeights:
         self.latent_ch = self.w_head.shape[0]
 
 
-def gemm(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor, epilogue: int, gate=None, row0: int = 0, P: int = 0):
+def gemm(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor, epilogue: int, gate=None, row0: int = 0, P: int = 0,
+         tile_n: int = 0):
     M, K = x.shape
     N = w.shape[0]
     assert x.dtype == torch.bfloat16 and w.dtype == torch.bfloat16 and w.shape[1] == K and x.stride(1) == 1
     assert out.stride(1) == 1 and out.shape[0] == M
-    Q.check(Q.qi_gemm_bf16(x, x.stride(0), w, out, out.stride(0), M, N, K, epilogue, gate, row0, P,
-                           stream_handle(x.device)), "qi_gemm_bf16")
+    Q.check(Q.qi_gemm_bf16_ex(x, x.stride(0), w, out, out.stride(0), M, N, K, epilogue, gate, row0, P, tile_n,
+                              stream_handle(x.device)), "qi_gemm_bf16_ex")
     return out
 
 

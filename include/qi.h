@@ -225,12 +225,20 @@ int qi_euler_step(float* x, const void* v, qi_dtype v_dtype, int64_t n, float si
 typedef enum { QI_EPI_STORE = 0, QI_EPI_STORE_F32 = 1, QI_EPI_GATED_RESIDUAL = 2, QI_EPI_SWIGLU = 3 } qi_epilogue;
 
 /* Dense projection on bf16 MFMA: x device bf16 [M][ldx]; w device bf16 [N][K] (the Linear weight,
- * out x in); K % 64 == 0, N % 64 == 0, M <= 8388480, ldx/ldo multiples of 8, pointers 16-byte
- * aligned.  gate, row0 and P are used by QI_EPI_GATED_RESIDUAL only (gate may be NULL otherwise).
- * out must not overlap x or w.  Errors: QI_ERR_ARG (null pointer, unknown epilogue),
- * QI_ERR_SHAPE, QI_ERR_ALIGN, QI_ERR_HIP (launch). */
+ * out x in); K % 64 == 0, N % 64 == 0, ldx/ldo multiples of 8, M * ldx and N * K below 2^30
+ * elements, pointers 16-byte aligned.  gate, row0 and P are used by QI_EPI_GATED_RESIDUAL only
+ * (gate may be NULL otherwise).  out must not overlap x or w.  The workgroup tile (256 tokens x
+ * 256, 192 or 128 features) is chosen from M and N.  Errors: QI_ERR_ARG (null pointer, unknown
+ * epilogue), QI_ERR_SHAPE, QI_ERR_ALIGN, QI_ERR_HIP (launch). */
 int qi_gemm_bf16(const void* x, int64_t ldx, const void* w, void* out, int64_t ldo, int64_t M, int64_t N,
                  int64_t K, int epilogue, const float* gate, int64_t row0, int64_t P, void* stream);
+
+/* qi_gemm_bf16 with the tile's feature width given: tile_n = 256, 192 (not with QI_EPI_SWIGLU) or
+ * 128, or 0 for the automatic choice (QI_ERR_ARG otherwise).  Results do not depend on the tile:
+ * every output is one fp32 sum in the same order. */
+int qi_gemm_bf16_ex(const void* x, int64_t ldx, const void* w, void* out, int64_t ldo, int64_t M, int64_t N,
+                    int64_t K, int epilogue, const float* gate, int64_t row0, int64_t P, int32_t tile_n,
+                    void* stream);
 
 /* ZeroCenterRMSNorm with modulation ([1B] sections 1-3: x * rrms * (w + 1), weights stored as
  * scale - 1, fp32 math; [EDIT] section 5.2: x * (1 + scale) + shift): x device fp32 [M][ldx],

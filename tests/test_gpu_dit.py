@@ -80,7 +80,8 @@ def sync():
 # GEMM epilogues
 # ------------------------------------------------------------------------------------------------
 
-GEMM_SHAPES = [(300, 192, 320), (1, 64, 64), (129, 128, 128), (257, 256, 64), (64, 320, 192)]
+GEMM_SHAPES = [(300, 192, 320), (1, 64, 64), (257, 256, 64), (600, 448, 192), (513, 640, 128)]
+TILES = [128, 192, 256]   # feature width of the 256-token workgroup tiles (0 = automatic)
 
 
 def gemm_inputs(M, N, K, tag=0):
@@ -96,9 +97,10 @@ def padded(rows, cols, ld, dtype, fill):
     return buf, buf[:rows, :cols]
 
 
+@pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
-def test_gemm_store_and_store_f32(M, N, K):
-    say(f"[gemm store] M={M} N={N} K={K}")
+def test_gemm_store_and_store_f32(M, N, K, tile):
+    say(f"[gemm store] M={M} N={N} K={K} tile={tile}")
     x, w = gemm_inputs(M, N, K)
     ref = O.linear(x.f64, w.f64)
     # x with a wider leading dimension, outputs padded to catch stray writes
@@ -107,15 +109,16 @@ def test_gemm_store_and_store_f32(M, N, K):
     xv = xbuf[:, :K]
     for epi, dt, bar in ((Q.QI_EPI_STORE, torch.bfloat16, "bf16"), (Q.QI_EPI_STORE_F32, torch.float32, "f32")):
         buf, out = padded(M, N, N + 8, dt, 7.0)
-        rt.gemm(xv, bf(w), out, epi)
+        rt.gemm(xv, bf(w), out, epi, tile_n=tile)
         sync()
         check(host(out), ref, bar, f"epi {epi}")
         assert torch.all(buf[:M, N:] == 7.0) and torch.all(buf[M:] == 7.0), "write outside the output view"
 
 
+@pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
-def test_gemm_gated_residual(M, N, K):
-    say(f"[gemm gated residual] M={M} N={N} K={K}")
+def test_gemm_gated_residual(M, N, K, tile):
+    say(f"[gemm gated residual] M={M} N={N} K={K} tile={tile}")
     x, w = gemm_inputs(M, N, K, 1)
     x0 = qin.normal(CFG, 210, (M, N)).astype(np.float32).astype(np.float64)
     gate = qin.normal(CFG, 211, (2, N), std=0.7).astype(np.float32).astype(np.float64)
@@ -125,25 +128,44 @@ def test_gemm_gated_residual(M, N, K):
         ref = x0 + np.tanh(g) * y
         buf, out = padded(M, N, N + 8, torch.float32, 5.0)
         out.copy_(f32(x0))
-        rt.gemm(bf(x), bf(w), out, Q.QI_EPI_GATED_RESIDUAL, f32(gate), row0, P)
+        rt.gemm(bf(x), bf(w), out, Q.QI_EPI_GATED_RESIDUAL, f32(gate), row0, P, tile_n=tile)
         sync()
         check(host(out), ref, "f32", f"row0={row0} P={P}")
         assert torch.all(buf[:M, N:] == 5.0) and torch.all(buf[M:] == 5.0)
 
 
+@pytest.mark.parametrize("tile", [128, 256])
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
-def test_gemm_swiglu(M, N, K):
-    say(f"[gemm swiglu] M={M} 2F={N} K={K}")
+def test_gemm_swiglu(M, N, K, tile):
+    say(f"[gemm swiglu] M={M} 2F={N} K={K} tile={tile}")
     F = N // 2
     x = qin.stored(qin.normal(CFG, 220, (M, K)), "bf16")
     wg = qin.linear_weight(CFG, 50, F, K)
     wu = qin.linear_weight(CFG, 51, F, K)
     ref = O.swiglu(O.linear(x.f64, wg.f64), O.linear(x.f64, wu.f64))
     buf, out = padded(M, F, F + 8, torch.bfloat16, 3.0)
-    rt.gemm(bf(x), rt.pack_swiglu(bf(wg), bf(wu)), out, Q.QI_EPI_SWIGLU)
+    rt.gemm(bf(x), rt.pack_swiglu(bf(wg), bf(wu)), out, Q.QI_EPI_SWIGLU, tile_n=tile)
     sync()
     check(host(out), ref, "bf16", "swiglu")
     assert torch.all(buf[:M, F:] == 3.0) and torch.all(buf[M:] == 3.0)
+
+
+@pytest.mark.parametrize("epi", [Q.QI_EPI_STORE, Q.QI_EPI_STORE_F32, Q.QI_EPI_GATED_RESIDUAL, Q.QI_EPI_SWIGLU])
+def test_gemm_tiles_give_identical_bits(epi):
+    # every output is the same fp32 sum in the same order whatever the tile, so the bits agree
+    M, N, K = 600, 448, 192
+    x, w = gemm_inputs(M, N, K, 2)
+    gate = f32(qin.normal(CFG, 212, (2, N), std=0.7))
+    F = N // 2 if epi == Q.QI_EPI_SWIGLU else N
+    dt = torch.bfloat16 if epi in (Q.QI_EPI_STORE, Q.QI_EPI_SWIGLU) else torch.float32
+    outs = []
+    for tile in ([0, 128, 256] if epi == Q.QI_EPI_SWIGLU else [0, 128, 192, 256]):
+        out = torch.zeros((M, F), dtype=dt, device=DEV) + 0.5
+        rt.gemm(bf(x), bf(w), out, epi, gate, 0, 100, tile_n=tile)
+        outs.append(out)
+    sync()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
 
 
 def test_gemm_argument_errors():
@@ -157,6 +179,10 @@ def test_gemm_argument_errors():
     assert Q.qi_gemm_bf16(x, 60, w, o, 64, 8, 64, 64, Q.QI_EPI_STORE_F32, None, 0, 0, s) == Q.QI_ERR_SHAPE
     assert Q.qi_gemm_bf16(x, 64, w, o, 64, 8, 64, 64, 9, None, 0, 0, s) == Q.QI_ERR_ARG
     assert Q.qi_gemm_bf16(x, 64, w, o, 64, 0, 64, 64, Q.QI_EPI_STORE_F32, None, 0, 0, s) == Q.QI_OK
+    assert Q.qi_gemm_bf16_ex(x, 64, w, o, 64, 8, 64, 64, Q.QI_EPI_STORE_F32, None, 0, 0, 64, s) == Q.QI_ERR_ARG
+    assert Q.qi_gemm_bf16_ex(x, 64, w, o, 64, 8, 64, 64, Q.QI_EPI_SWIGLU, None, 0, 0, 192, s) == Q.QI_ERR_ARG
+    # x beyond 2^30 elements (32-bit byte offsets), checked before any launch
+    assert Q.qi_gemm_bf16(x, 1 << 20, w, o, 64, 1 << 10, 64, 64, Q.QI_EPI_STORE_F32, None, 0, 0, s) == Q.QI_ERR_SHAPE
 
 
 # full-size projections of one layer of the 14,848-token workload (hidden 3072, FFN 8192), on
