@@ -49,9 +49,12 @@ int check_cache(const qi_kvcache* c, qi_dtype io_dtype, int32_t n_head, int32_t 
 
 float softmax_scale(float scale) { return scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)QI_HEAD_DIM)); }
 
+// rows per head of a cache: fp16 caches are padded to whole 64-key tiles
+int64_t cache_rows(const qi_kvcache* c) { return c->dtype == QI_F16 ? rows64(c->p_cap) : c->p_cap; }
+
 // pointer to row 0 of a cache layer
 const void* cache_layer(const void* base, const qi_kvcache* c, int32_t layer) {
-  const int64_t off = (int64_t)layer * c->n_head * c->p_cap * QI_HEAD_DIM * elem_size(c->dtype);
+  const int64_t off = (int64_t)layer * c->n_head * cache_rows(c) * QI_HEAD_DIM * elem_size(c->dtype);
   return (const char*)base + off;
 }
 
@@ -208,59 +211,58 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
 
   hipStream_t s = (hipStream_t)stream;
   const int es = elem_size(io->dtype == QI_BF16 ? QI_F16 : QI_F32);
-  const int64_t rows_ws = cache ? li.T : li.S;  // workspace rows: target only when the prefix goes to the cache
+  // workspace: K then V, each [head][RA + RB][128] with the prefix rows at row 0 and the target
+  // rows at row RA (both padded to whole 64-key tiles), then the partial outputs of the key
+  // chunks; the same layout with or without a cache (which then holds the prefix instead)
+  const int64_t RA = rows64(li.P), RB = rows64(li.T), R = RA + RB;
   char* wk = (char*)workspace;
-  char* wv = wk + (int64_t)io->n_head * rows_ws * QI_HEAD_DIM * es;
+  char* wv = wk + (int64_t)io->n_head * R * QI_HEAD_DIM * es;
   AttnArgs a = attn_args(io, prep, scale);
   a.masked = 1;
   a.segs = li.tab;
   a.q_row0 = 0;
-  // partial outputs of the key chunks follow the K/V rows (S rows are reserved for K/V in
-  // either case, so the layout does not depend on the cache argument)
-  set_partials(a, (char*)workspace + 2 * (int64_t)io->n_head * li.S * QI_HEAD_DIM * es, li.S, li.T, io->n_head,
+  set_partials(a, (char*)workspace + 2 * (int64_t)io->n_head * R * QI_HEAD_DIM * es, li.S, li.T, io->n_head,
                io->dtype);
+  // target rows: K/V prepared into the workspace at row RA (with the target's table rows)
+  const int64_t off = li.P * io->tok_stride * (io->dtype == QI_BF16 ? 2 : 4);
+  qi_qkprep tprep{};
+  if (prep) {
+    tprep = *prep;
+    if (prep->cos_t) {
+      tprep.cos_t = prep->cos_t + li.P * (QI_HEAD_DIM / 2);
+      tprep.sin_t = prep->sin_t + li.P * (QI_HEAD_DIM / 2);
+    }
+  }
+  char* tk = wk + RA * QI_HEAD_DIM * es;
+  char* tv = wv + RA * QI_HEAD_DIM * es;
+  if ((st = prep_kv((const char*)io->k + off, (const char*)io->v + off, io->dtype, li.T, io->n_head,
+                    io->tok_stride, prep ? &tprep : nullptr, tk, tv, R * QI_HEAD_DIM, s)) != QI_OK)
+    return st;
+  a.kB = tk;
+  a.vB = tv;
+  a.b_head_stride = R * QI_HEAD_DIM;
+  a.nB = li.T;
+  // prefix rows: into the cache (kept for the later steps) or the workspace at row 0; either way
+  // the prefix and the target are the two key sources, so the key tiles and the output bits are
+  // the same with and without a cache
   if (cache) {
     void* ck = (void*)cache_layer(cache->k, cache, layer);
     void* cv = (void*)cache_layer(cache->v, cache, layer);
-    const int64_t chs = cache->p_cap * QI_HEAD_DIM;
+    const int64_t chs = cache_rows(cache) * QI_HEAD_DIM;
     if ((st = prep_kv(io->k, io->v, io->dtype, li.P, io->n_head, io->tok_stride, prep, ck, cv, chs, s)) != QI_OK)
-      return st;
-    const int64_t off = li.P * io->tok_stride * (io->dtype == QI_BF16 ? 2 : 4);
-    qi_qkprep tprep{};
-    if (prep) {  // table rows of the target tokens
-      tprep = *prep;
-      if (prep->cos_t) {
-        tprep.cos_t = prep->cos_t + li.P * (QI_HEAD_DIM / 2);
-        tprep.sin_t = prep->sin_t + li.P * (QI_HEAD_DIM / 2);
-      }
-    }
-    if ((st = prep_kv((const char*)io->k + off, (const char*)io->v + off, io->dtype, li.T, io->n_head,
-                      io->tok_stride, prep ? &tprep : nullptr, wk, wv, li.T * QI_HEAD_DIM, s)) != QI_OK)
       return st;
     a.kA = ck;
     a.vA = cv;
     a.a_head_stride = chs;
-    a.nA = li.P;
-    a.kB = wk;
-    a.vB = wv;
-    a.b_head_stride = li.T * QI_HEAD_DIM;
-    a.nB = li.T;
   } else {
-    if ((st = prep_kv(io->k, io->v, io->dtype, li.S, io->n_head, io->tok_stride, prep, wk, wv,
-                      li.S * QI_HEAD_DIM, s)) != QI_OK)
+    if ((st = prep_kv(io->k, io->v, io->dtype, li.P, io->n_head, io->tok_stride, prep, wk, wv, R * QI_HEAD_DIM,
+                      s)) != QI_OK)
       return st;
-    // the prefix rows and the target rows as two sources, exactly as with a cache, so that the
-    // key tiles (and hence the output bits) are the same with and without one
-    const int64_t es_kv = io->dtype == QI_BF16 ? 2 : 4;
     a.kA = wk;
     a.vA = wv;
-    a.a_head_stride = li.S * QI_HEAD_DIM;
-    a.nA = li.P;
-    a.kB = (const char*)wk + li.P * QI_HEAD_DIM * es_kv;
-    a.vB = (const char*)wv + li.P * QI_HEAD_DIM * es_kv;
-    a.b_head_stride = li.S * QI_HEAD_DIM;
-    a.nB = li.T;
+    a.a_head_stride = R * QI_HEAD_DIM;
   }
+  a.nA = li.P;
   return run_attn(a, io->dtype, s);
 }
 
@@ -279,7 +281,7 @@ int qi_attn_prefix_store(const void* k, const void* v, qi_dtype dtype, int64_t P
   if ((st = check_cache(cache, dtype, n_head, layer, P)) != QI_OK) return st;
   void* ck = (void*)cache_layer(cache->k, cache, layer);
   void* cv = (void*)cache_layer(cache->v, cache, layer);
-  return prep_kv(k, v, dtype, P, n_head, tok_stride, prep, ck, cv, cache->p_cap * QI_HEAD_DIM,
+  return prep_kv(k, v, dtype, P, n_head, tok_stride, prep, ck, cv, cache_rows(cache) * QI_HEAD_DIM,
                  (hipStream_t)stream);
 }
 
@@ -302,22 +304,22 @@ int qi_attn_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvca
 
   hipStream_t s = (hipStream_t)stream;
   const int es = elem_size(cache->dtype);
-  const int64_t T = io->n_tok;
+  const int64_t T = io->n_tok, RB = rows64(T);
   char* wk = (char*)workspace;
-  char* wv = wk + (int64_t)io->n_head * T * QI_HEAD_DIM * es;
-  if ((st = prep_kv(io->k, io->v, io->dtype, T, io->n_head, io->tok_stride, prep, wk, wv, T * QI_HEAD_DIM, s)) !=
+  char* wv = wk + (int64_t)io->n_head * RB * QI_HEAD_DIM * es;
+  if ((st = prep_kv(io->k, io->v, io->dtype, T, io->n_head, io->tok_stride, prep, wk, wv, RB * QI_HEAD_DIM, s)) !=
       QI_OK)
     return st;
   AttnArgs a = attn_args(io, prep, scale);
   a.masked = 0;
-  set_partials(a, wk + 2 * (int64_t)io->n_head * T * QI_HEAD_DIM * es, T, T, io->n_head, io->dtype);
+  set_partials(a, wk + 2 * (int64_t)io->n_head * RB * QI_HEAD_DIM * es, T, T, io->n_head, io->dtype);
   a.kA = cache_layer(cache->k, cache, layer);
   a.vA = cache_layer(cache->v, cache, layer);
-  a.a_head_stride = cache->p_cap * QI_HEAD_DIM;
+  a.a_head_stride = cache_rows(cache) * QI_HEAD_DIM;
   a.nA = P;
   a.kB = wk;
   a.vB = wv;
-  a.b_head_stride = T * QI_HEAD_DIM;
+  a.b_head_stride = RB * QI_HEAD_DIM;
   a.nB = T;
   a.q_row0 = P;
   return run_attn(a, io->dtype, s);

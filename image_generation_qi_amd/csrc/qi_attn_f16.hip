@@ -8,17 +8,19 @@
 // Work decomposition
 //   - one workgroup = 4 wavefronts = 128 query rows of one head; wave w owns rows 32w..32w+31.
 //   - keys stream in tiles of 64 through LDS (two stages of K and V, 64 KB), copied with MUBUF
-//     buffer -> LDS loads (keeps the compute phases' LDS waits exact) into unpadded 256-byte
-//     rows whose 16-byte chunks are XOR-swizzled (K: chunk ^ (row & 15), V: chunk ^ 4(row & 3)),
-//     so both MFMA A-operand reads are bank-conflict free.  Source A (cache or workspace prefix)
-//     and source B (fresh keys) are tiled separately, so every copy reads one source.
+//     buffer -> LDS loads (keeps the compute phases' LDS waits exact) into unpadded rows whose
+//     16-byte chunks are XOR-swizzled, so both MFMA A-operand reads are bank-conflict free.
+//     K is row-major [key][128]; V is stored (by the prep kernel) and staged transposed, as
+//     tiles of [128 dims][64 keys].  Source A (cache or workspace prefix) and source B (fresh
+//     keys) are tiled separately, so every copy reads one source.
 //   - S^T = K Q^T - m with v_mfma_f32_32x32x16_f16: A = 32 keys x 16 dims from LDS, B = the
 //     wave's 32 queries (rotated, scaled by scale*log2(e), fp16) held in registers; the
 //     accumulators start at minus the row's reference m, so the scores come out shifted.  Each
 //     lane then holds one query and 16 keys per 32-key block.
 //   - O^T += V^T P^T with the same instruction: B = the lane's own probabilities (fp16), A = V^T
-//     from the row-major V tile through the transposing ds_read_b64_tr_b16.  The key order of the
-//     contraction follows the S^T register order, so P never moves between lanes.
+//     rows of the transposed tile.  K rows are loaded with a fixed permutation inside every 16,
+//     so that the keys a lane holds in S^T are 8 consecutive keys per 16-key chunk: P never moves
+//     between lanes and each V^T operand is one 16-byte read.
 //   - online softmax in base 2 with a lazy reference: probabilities 2^(s) are formed against the
 //     current reference and only rows whose probabilities exceed 2^8 (or that have no reference
 //     yet) move it (a rare, wave-uniform branch); other rows keep a factor of exactly 1.
@@ -41,7 +43,6 @@ namespace qi {
 namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -67,24 +68,20 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
   return u >> 16;
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// Transposing LDS read (gfx950): within each group of 16 lanes, output lane 4a+b receives
-// element b of the 8-byte chunk addressed by lane a+4j, as its element j.
-__device__ __forceinline__ h4 lds_read_tr(const _Float16* p) {
-  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-  return __builtin_bit_cast(h4, r);
-}
-
 typedef __attribute__((address_space(3))) void lds_void;
 
-// LDS tiles hold unpadded 256-byte rows; the 16-byte chunk c of row r is stored at chunk
-// position c ^ swz(r).  K: swz = r & 15, so the 16 rows read by one quarter-wave (same logical
-// chunk) hit 16 distinct chunk positions.  V: swz = 4 * (r & 3), so the 4 rows x 4 chunks read
-// by a half-wave of transposing reads are all distinct.
+// LDS tiles hold unpadded rows whose 16-byte chunk c of row r sits at chunk position c ^ swz(r).
+// K tile: 64 rows (keys) of 256 bytes, swz = r & 15, so the 16 rows read by a quarter-wave at one
+// logical chunk hit 16 distinct positions.  V^T tile: 128 rows (dims) of 128 bytes (64 keys),
+// swz = (r >> 1) & 7: the 16 rows of a quarter-wave span 8 row pairs x 2 halves of the bank
+// space, again 16 distinct positions.
 __device__ __forceinline__ int swz_k(int r) { return r & 15; }
-__device__ __forceinline__ int swz_v(int r) { return 4 * (r & 3); }
+__device__ __forceinline__ int swz_v(int r) { return (r >> 1) & 7; }
+
+// K rows are loaded with rows 4-7 and 8-11 of every 16 swapped, so that the keys a lane holds in
+// the S^T accumulator (rows 8(r/4) + 4g + r%4) are keys 16(r/8) + 8g + r%8: each lane's 8
+// probabilities of a 16-key chunk are 8 consecutive keys, one 16-byte row piece of V^T.
+__device__ __forceinline__ int k_row_perm(int j) { return j == 1 ? 2 : (j == 2 ? 1 : j); }
 
 // Both halves of a wave exchanged: for lane l, returns (x[l], x[l ^ 32]) in an order that is
 // the same for the two lanes of the pair, so any symmetric combination is bit-identical.
@@ -217,32 +214,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Wave w fills rows 16w .. 16w+15 of each tile: 4 copies of 1 KB (4 rows) for K and for V.
   // Lane i of copy j covers row 16w + 4j + i/16, chunk position i%16; offsets are in bytes.
   const __amdgpu_buffer_rsrc_t rkA = __builtin_amdgcn_make_buffer_rsrc((void*)kA, (short)0, nA * HD * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rvA = __builtin_amdgcn_make_buffer_rsrc((void*)vA, (short)0, nA * HD * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rvA = __builtin_amdgcn_make_buffer_rsrc((void*)vA, (short)0, ntA * BN * HD * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t rkB = __builtin_amdgcn_make_buffer_rsrc((void*)kB, (short)0, nB * HD * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rvB = __builtin_amdgcn_make_buffer_rsrc((void*)vB, (short)0, nB * HD * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rvB = __builtin_amdgcn_make_buffer_rsrc((void*)vB, (short)0, (nB + BN - 1) / BN * BN * HD * 2, 0x00020000);
+  // K: wave w fills LDS rows 16w .. 16w+15 with 4 copies of 1 KB (4 rows of 256 bytes); lane i of
+  // copy j writes row 16w + 4j + i/16 at chunk position i%16, from key 16w + 4perm(j) + i/16.
+  // V^T: wave w fills rows (dims) 32w .. 32w+31 with 4 copies of 1 KB (8 rows of 128 bytes); lane
+  // i of copy j writes row 32w + 8j + i/8 at chunk position i%8.  Byte offsets within the tile.
   int koff[4], voff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 16 * wave + 4 * j + (lane >> 4);
-    const int pos = lane & 15;
-    koff[j] = 2 * (row * HD + 8 * (pos ^ swz_k(row)));
-    voff[j] = 2 * (row * HD + 8 * (pos ^ swz_v(row)));
+    const int src = 16 * wave + 4 * k_row_perm(j) + (lane >> 4);
+    koff[j] = 2 * (src * HD + 8 * ((lane & 15) ^ swz_k(row)));
+    const int vrow = 32 * wave + 8 * j + (lane >> 3);
+    voff[j] = 2 * (vrow * BN + 8 * ((lane & 7) ^ swz_v(vrow)));
   }
-  // copy j of K (is_k) or V of key tile t into stage buf
+  // copy j of K (is_k) or V^T of key tile t into stage buf (both tiles are 16 KB in memory)
   auto copy = [&](int t, int buf, int j, auto is_k_tag) {
     constexpr bool IS_K = decltype(is_k_tag)::value;
     const bool inA = t < ntA;
     const __amdgpu_buffer_rsrc_t rs = IS_K ? (inA ? rkA : rkB) : (inA ? rvA : rvB);
     const int soff = (inA ? t : t - ntA) * (BN * HD * 2);
-    _Float16* dst = smem + buf * BUF + (IS_K ? 0 : TILE) + (16 * wave + 4 * j) * HD;
+    _Float16* dst = smem + buf * BUF + (IS_K ? (16 * wave + 4 * j) * HD : TILE + (32 * wave + 8 * j) * BN);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, IS_K ? koff[j] : voff[j], soff, 0, 0);
   };
 
-  // per-lane LDS offsets: V rows/cols for the transposing reads (row 16c+8h+4g+L/4, dims
-  // 32bd+16(lane/16%2)+4(L%4))
-  const int L = lane & 15;
-  const int vrow0 = 4 * g + (L >> 2);                        // + 16c + 8h: same row & 3
-  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (L & 3);      // + 32bd
   f32x16 o[4];
 #pragma unroll
   for (int bd = 0; bd < 4; ++bd)
@@ -261,18 +258,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     dst[0] = *(const h8*)(Ks + l32 * HD + pos);
     dst[1] = *(const h8*)(Ks + (32 + l32) * HD + pos);
   };
-  // V: the four O^T A operands (dims 32bd .. 32bd + 31) of 16-key chunk c, each from two
-  // transposing reads (rows vrow0 + 16c and vrow0 + 16c + 8 share row & 3, hence one swizzle).
+  // V^T: the four O^T A operands (dims 32bd + l32) of 16-key chunk c: keys 16c + 8g .. + 7, one
+  // 16-byte piece of the dim's 128-byte row.
   auto read_v = [&](int vbuf, int c, h8 (&dst)[4]) {
     const _Float16* Vs = smem + vbuf * BUF + TILE;
 #pragma unroll
     for (int bd = 0; bd < 4; ++bd) {
-      const int col = 32 * bd + vcol;
-      const int pcol = ((col >> 3) ^ swz_v(vrow0)) * 8 + (col & 7);
-      const _Float16* vp = Vs + (vrow0 + 16 * c) * HD + pcol;
-      const h4 lo = lds_read_tr(vp);
-      const h4 hi = lds_read_tr(vp + 8 * HD);
-      dst[bd] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      const int d = 32 * bd + l32;
+      dst[bd] = *(const h8*)(Vs + d * BN + 8 * ((2 * c + g) ^ swz_v(d)));
     }
   };
 
@@ -402,10 +395,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int cnt = kt < ntA ? nA - kt * BN : nkeys - key0;   // keys of the tile (capped below)
       int rel = lim - key0;
       if (rel > cnt - 1) rel = cnt - 1;
-      rel -= 4 * g;                 // offset (in tile, minus 4g) of the last visible key
+      rel -= 8 * g;                 // offset (in tile, minus 8g) of the last visible key
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kr = 8 * (r >> 2) + (r & 3);
+        const int kr = 16 * (r >> 3) + (r & 7);   // key of accumulator entry r (rows permuted at load)
         if (kr > rel) s0[r] = -INFINITY;
         if (kr + 32 > rel) s1[r] = -INFINITY;
       }

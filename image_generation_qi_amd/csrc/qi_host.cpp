@@ -183,7 +183,8 @@ int qi_attn_tile_shape(qi_dtype dtype, int32_t* tile_q, int32_t* tile_k) {
   return QI_OK;
 }
 
-// K and V rows, [n_head][rows][128]: fp16 for bf16 attention, fp32 for fp32 attention
+// K and V rows, [n_head][rows][128]: fp16 for bf16 attention, fp32 for fp32 attention (callers
+// pass rows already padded to whole 64-key tiles)
 static int64_t rows_bytes(qi_dtype dtype, int64_t rows, int32_t n_head) {
   if (rows < 0 || n_head < 1) return QI_ERR_ARG;
   if (dtype == QI_BF16) return 2 * (int64_t)n_head * rows * QI_HEAD_DIM * 2;
@@ -202,13 +203,14 @@ int64_t qi_attn_full_workspace_bytes(const qi_layout* layout, qi_dtype dtype, in
   LayoutInfo li;
   int st = analyse_layout(layout, &li);
   if (st != QI_OK) return st;
-  const int64_t r = rows_bytes(dtype, li.S, n_head);
+  // prefix rows and target rows, each padded to whole 64-key tiles
+  const int64_t r = rows_bytes(dtype, rows64(li.P) + rows64(li.T), n_head);
   if (r < 0) return r;
   return r + partial_bytes(dtype, li.S, li.T, n_head);
 }
 
 int64_t qi_attn_cached_workspace_bytes(qi_dtype dtype, int64_t T, int32_t n_head) {
-  const int64_t r = rows_bytes(dtype, T, n_head);
+  const int64_t r = rows_bytes(dtype, rows64(T), n_head);
   if (r < 0) return r;
   return r + partial_bytes(dtype, T, T, n_head);
 }
@@ -217,7 +219,8 @@ int64_t qi_kvcache_bytes(qi_dtype cache_dtype, int32_t n_layers, int32_t n_head,
   if (n_layers < 1 || n_head < 1 || p_cap < 0) return QI_ERR_ARG;
   int64_t es = cache_dtype == QI_F16 ? 2 : (cache_dtype == QI_F32 ? 4 : 0);
   if (!es) return QI_ERR_DTYPE;
-  return es * (int64_t)n_layers * n_head * p_cap * QI_HEAD_DIM;
+  const int64_t rows = cache_dtype == QI_F16 ? rows64(p_cap) : p_cap;
+  return es * (int64_t)n_layers * n_head * rows * QI_HEAD_DIM;
 }
 
 }  // extern "C"

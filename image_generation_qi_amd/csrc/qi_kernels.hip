@@ -121,6 +121,40 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
   }
 }
 
+// V of the fp16 attention path, transposed into 64-key tiles: tile t of head h is [128 dims][64
+// keys] fp16 (key-minor), so the PV MFMA's V^T operand is a plain 16-byte row read.  Keys at or
+// past n in the last tile are written as zero.  One workgroup per (tile, head); the transpose
+// goes through LDS so that both the bf16 rows read and the 128-byte fp16 rows written are whole.
+__global__ __launch_bounds__(256) void k_prep_vt(const uint16_t* __restrict__ v, int64_t tok_stride, int64_t n,
+                                                 uint16_t* __restrict__ dst, int64_t dst_head_stride) {
+  __shared__ uint32_t sm[64][68];   // [key][dim pair]: fp16 pairs, rows padded to 68 words
+  const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  {
+    const int key = tid >> 2, d0 = (tid & 3) * 32;
+    const int64_t j = (int64_t)t * 64 + key;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (j < n) w = *(const u32x4*)(v + j * tok_stride + (int64_t)h * 128 + d0 + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm[key][(d0 + 8 * c) / 2 + e] = pack_f16(bf16_lo(w[e]), bf16_hi(w[e]));
+    }
+  }
+  __syncthreads();
+  const int d = tid >> 1, k0 = (tid & 1) * 32;
+  uint16_t* out = dst + (int64_t)h * dst_head_stride + ((int64_t)t * 128 + d) * 64 + k0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t a = sm[k0 + 8 * c + 2 * e][d >> 1], b = sm[k0 + 8 * c + 2 * e + 1][d >> 1];
+      w[e] = (d & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+    }
+    *(u32x4*)(out + 8 * c) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
 template <int IN, int OUT>
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
   const int64_t threads = a.n_tok * (int64_t)a.n_head * 16;
@@ -249,7 +283,16 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
 
 }  // namespace
 
-hipError_t launch_prep_bf16_to_f16(const PrepArgs& a, hipStream_t s) { return launch_prep<IN_BF16, OUT_F16>(a, s); }
+hipError_t launch_prep_bf16_to_f16(const PrepArgs& a, hipStream_t s) {
+  PrepArgs k = a;
+  k.v = nullptr;   // V goes through the transposing kernel
+  hipError_t e = launch_prep<IN_BF16, OUT_F16>(k, s);
+  if (e != hipSuccess || !a.v || a.n_tok <= 0) return e;
+  const dim3 grid((unsigned)((a.n_tok + 63) / 64), (unsigned)a.n_head);
+  hipLaunchKernelGGL(k_prep_vt, grid, dim3(256), 0, s, (const uint16_t*)a.v, a.x_tok_stride, a.n_tok,
+                     (uint16_t*)a.dst_v, a.dst_head_stride);
+  return hipGetLastError();
+}
 hipError_t launch_prep_bf16_to_bf16(const PrepArgs& a, hipStream_t s) { return launch_prep<IN_BF16, OUT_BF16>(a, s); }
 hipError_t launch_prep_f32(const PrepArgs& a, hipStream_t s) { return launch_prep<IN_F32, OUT_F32>(a, s); }
 

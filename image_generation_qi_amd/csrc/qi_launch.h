@@ -11,6 +11,13 @@ namespace qi {
 // then optional 3D rotation) and optional copy of a V-like tensor with the same addressing.
 // Source element (t, h, d) is at x[t*x_tok_stride + h*128 + d]; destination element at
 // dst[t*dst_tok_stride + h*dst_head_stride + d].
+// Rows per head of the fp16 K/V layouts (caches and workspaces of the bf16 attention path):
+// padded to whole 64-key tiles.
+inline int64_t rows64(int64_t n) { return (n + 63) / 64 * 64; }
+
+// K/V preparation.  x (K) rows go to dst[head][row][128] with dst_tok_stride = 128.  v rows go
+// to dst_v with the same head stride: fp32 outputs row-major like K; fp16 outputs (bf16 inputs)
+// transposed into 64-key tiles [tile][128 dims][64 keys], the last tile's missing keys zero.
 struct PrepArgs {
   const void* x;
   int64_t x_tok_stride;

@@ -43,14 +43,28 @@ class Layout:
 
 
 class KVCache:
-    """Per-layer prefix K/V cache [n_layers][n_head][p_cap][128] (fp16 for bf16 attention)."""
+    """Per-layer prefix K/V cache (fp16 for bf16 attention, fp32 for fp32 attention).
+
+    k: [n_layers][n_head][R][128] rows; v: the same storage, for fp16 caches holding each head's
+    V transposed in tiles of [128 dims][64 keys] (R = p_cap rounded up to a multiple of 64), for
+    fp32 caches row-major like k (R = p_cap)."""
 
     def __init__(self, n_layers: int, n_head: int, p_cap: int, io_dtype: int = Q.QI_BF16, device="cuda"):
         self.dtype = Q.QI_F16 if io_dtype == Q.QI_BF16 else Q.QI_F32
         td = TORCH_DTYPE[self.dtype]
-        self.k = torch.empty((n_layers, n_head, max(p_cap, 1), 128), dtype=td, device=device)
-        self.v = torch.empty_like(self.k)
+        rows = (p_cap + 63) // 64 * 64 if self.dtype == Q.QI_F16 else p_cap
+        self.rows = max(rows, 64 if self.dtype == Q.QI_F16 else 1)
+        self.k = torch.zeros((n_layers, n_head, self.rows, 128), dtype=td, device=device)
+        self.v = torch.zeros_like(self.k)
         self.c = Q.make_cache(self.k, self.v, self.dtype, n_layers, n_head, p_cap)
+
+    def v_rows(self, layer: int) -> torch.Tensor:
+        """V of one layer as [n_head][R][128] rows (a copy for fp16 caches)."""
+        v = self.v[layer]
+        if self.dtype != Q.QI_F16:
+            return v
+        H = v.shape[0]
+        return v.reshape(H, self.rows // 64, 128, 64).permute(0, 1, 3, 2).reshape(H, self.rows, 128)
 
 
 def _ws(nbytes: int, device) -> torch.Tensor:

@@ -81,9 +81,13 @@ typedef struct {
 } qi_layout;
 
 /* Prefix KV cache ([OV] card 6A: stored at step 1, loaded at steps 2..N).  k and v are each
- * [n_layers][n_head][p_cap][128] of `dtype`, device memory owned by the caller.  K is stored
- * after the optional QK-RMSNorm and the 3D rotation; V as given.  dtype must be QI_F16 for
- * bf16 attention and QI_F32 for fp32 attention.  fp16 holds every bf16 V with
+ * [n_layers][n_head][R][128] elements of `dtype`, device memory owned by the caller, with R =
+ * p_cap for QI_F32 and p_cap rounded up to a multiple of 64 for QI_F16 (qi_kvcache_bytes gives
+ * the size).  K rows are stored row-major after the optional QK-RMSNorm and the 3D rotation.
+ * V is stored as given: row-major for QI_F32; for QI_F16 each head's V is transposed into R/64
+ * tiles of [128 dims][64 keys] (tile t holds keys 64t .. 64t+63, key-minor; keys past the
+ * stored count in the last tile are zero).  dtype must be QI_F16 for bf16 attention and QI_F32
+ * for fp32 attention.  fp16 holds every bf16 V with
  * 2^-17 <= |v| < 65504 exactly (smaller values round to the fp16 subnormal grid, absolute
  * error <= 2^-25; larger ones overflow to infinity), and keeps rotated K with 3 more mantissa
  * bits than bf16 would. */
@@ -161,7 +165,8 @@ int qi_attn_tile_shape(qi_dtype dtype, int32_t* tile_q, int32_t* tile_k);
 int64_t qi_attn_full_workspace_bytes(const qi_layout* layout, qi_dtype dtype, int32_t n_head);
 int64_t qi_attn_cached_workspace_bytes(qi_dtype dtype, int64_t T, int32_t n_head);
 
-/* Bytes of one cache tensor (k or v) for the given shape.  Negative = error status. */
+/* Bytes of one cache tensor (k or v) for the given shape (fp16 rows padded to a multiple of
+ * 64).  Negative = error status. */
 int64_t qi_kvcache_bytes(qi_dtype cache_dtype, int32_t n_layers, int32_t n_head, int64_t p_cap);
 
 /* ------------------------------------------------------------------------------------------

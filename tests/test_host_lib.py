@@ -127,9 +127,16 @@ def test_tile_shape_and_sizes():
     L1 = Q.make_layout(qin.WORKLOADS["cfg1"].segments)
     assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, 1024, 24) == 2 * 24 * 1024 * 128 * 2 + 6 * 1024 * 24 * 130 * 4
     assert Q.qi_attn_full_workspace_bytes(L1, Q.QI_BF16, 24) == 2 * 24 * 2304 * 128 * 2 + 6 * 2304 * 24 * 130 * 4
-    assert Q.qi_attn_cached_workspace_bytes(Q.QI_F32, 16, 2) == 2 * 2 * 16 * 128 * 4
+    # workspace rows are padded to whole 64-key tiles for both dtypes
+    assert Q.qi_attn_cached_workspace_bytes(Q.QI_F32, 16, 2) == 2 * 2 * 64 * 128 * 4
     assert Q.qi_attn_full_workspace_bytes(L3, Q.QI_F32, 2) == 2 * 2 * 21504 * 128 * 4
     assert Q.qi_kvcache_bytes(Q.QI_F16, 32, 24, 17408) == 32 * 24 * 17408 * 128 * 2
+    # fp16 caches hold whole 64-key tiles (V transposed per tile); fp32 caches are unpadded
+    assert Q.qi_kvcache_bytes(Q.QI_F16, 2, 3, 100) == 2 * 3 * 128 * 128 * 2
+    assert Q.qi_kvcache_bytes(Q.QI_F32, 2, 3, 100) == 2 * 3 * 100 * 128 * 4
+    # ragged prefix and target: each padded to whole tiles in the workspace
+    Lr = Q.make_layout((qin.text(77), qin.image(13, 9, 1), qin.image(15, 17, 0)))
+    assert Q.qi_attn_full_workspace_bytes(Lr, Q.QI_BF16, 2) >= 2 * 2 * (256 + 256) * 128 * 2
     assert Q.qi_kvcache_bytes(Q.QI_BF16, 1, 1, 1) == Q.QI_ERR_DTYPE
 
 
