@@ -24,9 +24,10 @@
 //   - online softmax in base 2 with a lazy reference: probabilities 2^(s) are formed against the
 //     current reference and only rows whose probabilities exceed 2^8 (or that have no reference
 //     yet) move it (a rare, wave-uniform branch); other rows keep a factor of exactly 1.
-//   - software pipeline: the QK^T MFMAs of tile kt+1, the probabilities of tile kt, the LDS
-//     operand reads one step ahead and the copies of later tiles are one fenced sequence, so
-//     MFMA, VALU, LDS and memory work interleave; then PV of tile kt with its row sums.
+//   - software pipeline: the PV MFMAs of tile kt-1, the QK^T MFMAs of tile kt+1, the
+//     probabilities of tile kt, the LDS operand reads one step ahead and the copies of later
+//     tiles are one fenced sequence of 16 two-MFMA steps, so the softmax VALU work is spread
+//     over all 32 MFMAs of a tile and MFMA, VALU, LDS and memory work interleave.
 //   - the Block-Causal mask is applied per tile from the row limits (see qi_common.h): tiles
 //     with no visible pair are never loaded, tiles with all pairs visible run unmasked.
 //   - key chunks (n_split > 1) balance the grid over the CUs: each chunk of a query tile's key
@@ -285,45 +286,70 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
-  // The shifted scores of the next tile and the probabilities of the current one, as one fenced
-  // sequence of eight steps.  Step kk issues the K reads of step kk + 1 and, in steps 0-3, two
-  // of the eight buffer -> LDS copies of the iteration (K of tile tk and V of tile tv into stage
-  // cbuf), then the two MFMAs of step kk with, between them, the probabilities 2^s of scores
-  // 2kk and 2kk+1 of both 32-key blocks, rounded to fp16 (the values PV consumes) and folded
-  // into a packed max.
-  auto qk_probs = [&](int kbuf, int cbuf, int tk, int tv, f32x16& sn0, f32x16& sn1, const f32x16& s0,
-                      const f32x16& s1, h8 (&pf)[4]) -> h2 {
+  // V^T operands of PV step i (chunk i/2, dims 64(i%2) .. 64(i%2) + 63: two 32-dim blocks)
+  auto read_v2 = [&](int vbuf, int i, h8 (&dst)[2]) {
+    const _Float16* Vs = smem + vbuf * BUF + TILE;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int d = 32 * (2 * (i & 1) + e) + l32;
+      dst[e] = *(const h8*)(Vs + d * BN + 8 * ((2 * (i >> 1) + g) ^ swz_v(d)));
+    }
+  };
+
+  // One iteration's compute as a single fenced sequence of 16 steps of two MFMAs each: steps 0-7
+  // are the PV of the previous tile (probabilities pp, chunk i/2, dims 64(i%2) .. + 63) with two
+  // of its row-sum dot products, steps 8-15 the QK^T of the next tile (reduction step i - 8,
+  // accumulators starting at minus the reference).  Every step also issues the LDS operand reads
+  // of the next step and forms two probabilities 2^s of the current tile (scores 2i, 2i+1 of
+  // the first 32-key block in steps 0-7, of the second in steps 8-15), rounded to fp16 and folded
+  // into a packed max; steps 0-3 issue the eight copies of later tiles (K of tile tk, V of tile
+  // tv, into stage cb).  So the softmax VALU work is spread over all 32 MFMAs of the tile.
+  auto seq = [&](int rb, int cb, int tk, int tv, f32x16& sn0, f32x16& sn1, const f32x16& s0, const f32x16& s1,
+                 const h8 (&pp)[4], h8 (&pf)[4], float& lsum) -> h2 {
     const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
     f32x16 init;
 #pragma unroll
     for (int r = 0; r < 16; ++r) init[r] = nm;
-    h8 ka[2][2];
-    read_k(kbuf, 0, ka[0]);
+    const h2 one2 = {(_Float16)1.f, (_Float16)1.f};
+    h8 va[2][2], ka[2][2];
+    read_v2(rb, 0, va[0]);
     h2 pm0 = {(_Float16)0.f, (_Float16)0.f}, pm1 = pm0;
+    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      if (kk + 1 < 8) read_k(kbuf, kk + 1, ka[(kk + 1) & 1]);
-      if (kk < 4) {
-        copy(tk, cbuf, kk, std::true_type{});
-        copy(tv, cbuf, kk, std::false_type{});
+    for (int i = 0; i < 16; ++i) {
+      if (i + 1 < 8)
+        read_v2(rb, i + 1, va[(i + 1) & 1]);
+      else if (i + 1 < 16)
+        read_k(rb, i + 1 - 8, ka[(i + 1) & 1]);
+      if (i < 4) {
+        copy(tk, cb, i, std::true_type{});
+        copy(tv, cb, i, std::false_type{});
       }
       __builtin_amdgcn_sched_barrier(0);
-      sn0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[kk & 1][0], qf[kk], kk ? sn0 : init, 0, 0, 0);
-      const float p0a = __builtin_amdgcn_exp2f(s0[2 * kk]);
-      const float p0b = __builtin_amdgcn_exp2f(s0[2 * kk + 1]);
-      const float p1a = __builtin_amdgcn_exp2f(s1[2 * kk]);
-      const float p1b = __builtin_amdgcn_exp2f(s1[2 * kk + 1]);
-      sn1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[kk & 1][1], qf[kk], kk ? sn1 : init, 0, 0, 0);
-      const h2 q0 = {(_Float16)p0a, (_Float16)p0b};
-      const h2 q1 = {(_Float16)p1a, (_Float16)p1b};
-      pf[kk >> 2][2 * (kk & 3)] = q0[0];
-      pf[kk >> 2][2 * (kk & 3) + 1] = q0[1];
-      pf[2 + (kk >> 2)][2 * (kk & 3)] = q1[0];
-      pf[2 + (kk >> 2)][2 * (kk & 3) + 1] = q1[1];
-      pm0 = __builtin_elementwise_max(pm0, q0);
-      pm1 = __builtin_elementwise_max(pm1, q1);
+      if (i < 8) {
+        const int c = i >> 1, bd = 2 * (i & 1);
+        o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i & 1][0], pp[c], o[bd], 0, 0, 0);
+        o[bd + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i & 1][1], pp[c], o[bd + 1], 0, 0, 0);
+        ps0 = __builtin_amdgcn_fdot2(h2{pp[c][4 * (i & 1)], pp[c][4 * (i & 1) + 1]}, one2, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2(h2{pp[c][4 * (i & 1) + 2], pp[c][4 * (i & 1) + 3]}, one2, ps1, false);
+      } else {
+        const int kk = i - 8;
+        sn0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[i & 1][0], qf[kk], kk ? sn0 : init, 0, 0, 0);
+        sn1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[i & 1][1], qf[kk], kk ? sn1 : init, 0, 0, 0);
+      }
+      const int j = i & 7;
+      const float p0 = __builtin_amdgcn_exp2f(i < 8 ? s0[2 * j] : s1[2 * j]);
+      const float p1 = __builtin_amdgcn_exp2f(i < 8 ? s0[2 * j + 1] : s1[2 * j + 1]);
+      const h2 q = {(_Float16)p0, (_Float16)p1};
+      pf[(i < 8 ? 0 : 2) + (j >> 2)][2 * (j & 3)] = q[0];
+      pf[(i < 8 ? 0 : 2) + (j >> 2)][2 * (j & 3) + 1] = q[1];
+      if (i < 8)
+        pm0 = __builtin_elementwise_max(pm0, q);
+      else
+        pm1 = __builtin_elementwise_max(pm1, q);
       __builtin_amdgcn_sched_barrier(0);
     }
+    lsum = ps0 + ps1;
     return __builtin_elementwise_max(pm0, pm1);
   };
 
@@ -354,17 +380,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // ---- software-pipelined main loop ------------------------------------------------------
   // Tile j's K and V live in stage (j - t_begin) & 1.  Iteration kt reads only the other stage
-  // b' = (kt - 1 - t_begin) & 1 and copies only into stage b = (kt - t_begin) & 1:
-  //   1. PV of tile kt-1 (V from stage b', probabilities carried from the previous iteration)
-  //      with its row sums;
-  //   2. the QK^T MFMAs of tile kt+1 (K from stage b') interleaved with the probabilities of
-  //      tile kt and with the copies of K[kt+2] and V[kt] into stage b (last read in
-  //      iteration kt-1);
-  //   3. the rare reference update of tile kt;
-  //   4. wait for the copies and a barrier.
-  // So the transposing V reads of step 1 never wait for copies still in flight, and the copies
-  // have steps 2-3 to land.  The loop is unrolled twice so that the current and next scores
-  // swap register sets instead of being copied; the PV of the last tile follows the loop.
+  // b' = (kt - 1 - t_begin) & 1 and copies only into stage b = (kt - t_begin) & 1: one fenced
+  // sequence runs the PV of tile kt-1 (V from stage b', probabilities carried from the previous
+  // iteration), the QK^T of tile kt+1 (K from stage b') and the probabilities of tile kt, and
+  // issues the copies of K[kt+2] and V[kt] into stage b (last read in iteration kt-1); then the
+  // rare reference update of tile kt; then the copies are waited for and a barrier ends the
+  // iteration.  The first iteration's PV multiplies zero probabilities with the zero-filled V
+  // stage.  The loop is unrolled twice so that scores and probabilities swap register sets
+  // instead of being copied; the PV of the last tile follows the loop.
   {
     // zero-fill both stages once, so that rows of short tiles that no copy writes hold zeros
     u32x4* z = (u32x4*)smem;
@@ -385,11 +408,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __syncthreads();
   int kt = t_begin;
   const int kt_mid = kt_full < t_begin ? t_begin : (kt_full < t_stop ? kt_full : t_stop);
-  h8 pf[4];   // probabilities of the tile whose PV is pending
-  auto iteration = [&](auto masked_tag, f32x16& s0, f32x16& s1, f32x16& sn0, f32x16& sn1) {
+  // probabilities of the previous and the current tile (two register sets, swapped per iteration)
+  h8 pa[4], pb[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pa[c][e] = (_Float16)0.f;
+  auto iteration = [&](auto masked_tag, f32x16& s0, f32x16& s1, f32x16& sn0, f32x16& sn1, const h8 (&pp)[4],
+                       h8 (&pf)[4]) {
     constexpr bool MT = decltype(masked_tag)::value;
     const int b = (kt - t_begin) & 1;
-    if (kt > t_begin) l_run += pv_sums(b ^ 1, pf);
     if constexpr (MT) {
       const int key0 = kt < ntA ? kt * BN : nA + (kt - ntA) * BN;
       const int cnt = kt < ntA ? nA - kt * BN : nkeys - key0;   // keys of the tile (capped below)
@@ -405,7 +433,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     // next tile's scores (on the last iteration from a stale, in-bounds stage, discarded)
     const int tk = kt + 2 < t_stop ? kt + 2 : t_stop - 1;
-    const h2 pm = qk_probs(b ^ 1, b, tk, kt, sn0, sn1, s0, s1, pf);
+    float lsum;
+    const h2 pm = seq(b ^ 1, b, tk, kt, sn0, sn1, s0, s1, pp, pf, lsum);
+    l_run += lsum;
     // Rare path: a row's first visible tile (reference still -inf) or probabilities above 2^8
     // (fp16 bits of a non-negative value above 0x5C00, which includes +inf).  The row's new
     // reference is its true max; the probabilities are recomputed, the running output and sum
@@ -450,30 +480,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
+  // between the loops the latest scores are in sa and the latest probabilities in pa
+  auto swap_in = [&]() {
+    sa0 = sb0;
+    sa1 = sb1;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pa[c] = pb[c];
+  };
   while (kt + 1 < kt_mid) {
-    iteration(std::false_type{}, sa0, sa1, sb0, sb1);
+    iteration(std::false_type{}, sa0, sa1, sb0, sb1, pa, pb);
     ++kt;
-    iteration(std::false_type{}, sb0, sb1, sa0, sa1);
+    iteration(std::false_type{}, sb0, sb1, sa0, sa1, pb, pa);
     ++kt;
   }
   if (kt < kt_mid) {
-    iteration(std::false_type{}, sa0, sa1, sb0, sb1);
+    iteration(std::false_type{}, sa0, sa1, sb0, sb1, pa, pb);
     ++kt;
-    sa0 = sb0;
-    sa1 = sb1;
+    swap_in();
   }
   while (kt + 1 < t_stop) {
-    iteration(std::true_type{}, sa0, sa1, sb0, sb1);
+    iteration(std::true_type{}, sa0, sa1, sb0, sb1, pa, pb);
     ++kt;
-    iteration(std::true_type{}, sb0, sb1, sa0, sa1);
+    iteration(std::true_type{}, sb0, sb1, sa0, sa1, pb, pa);
     ++kt;
   }
   if (kt < t_stop) {
-    iteration(std::true_type{}, sa0, sa1, sb0, sb1);
+    iteration(std::true_type{}, sa0, sa1, sb0, sb1, pa, pb);
     ++kt;
+    swap_in();
   }
   // PV of the last tile (its V was copied in the last iteration, before its barrier)
-  l_run += pv_sums((kt - 1 - t_begin) & 1, pf);
+  l_run += pv_sums((kt - 1 - t_begin) & 1, pa);
 
   // ---- epilogue: normalise and store bf16, or store the chunk's partial ---------------------
   const float lt = pair_sum(l_run);
