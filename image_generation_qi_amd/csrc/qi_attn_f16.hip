@@ -6,7 +6,9 @@
 // card 3C: Block-Causal visibility; card 6A: target-only steps read a cached prefix).
 //
 // Work decomposition
-//   - one workgroup = 4 wavefronts = 128 query rows of one head; wave w owns rows 32w..32w+31.
+//   - one workgroup = 8 wavefronts = 256 query rows of one head; wave w owns rows 32w..32w+31.
+//     Two waves share each SIMD and one workgroup fills a CU, so every K/V tile brought into
+//     LDS serves 256 queries.
 //   - keys stream in tiles of 64 through LDS (two stages of K and V, 64 KB), copied with MUBUF
 //     buffer -> LDS loads (keeps the compute phases' LDS waits exact) into unpadded rows whose
 //     16-byte chunks are XOR-swizzled, so both MFMA A-operand reads are bank-conflict free.
@@ -50,7 +52,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128;             // query rows per workgroup
+constexpr int BM = kAttnF16TileQ;   // query rows per workgroup (8 waves of 32)
 constexpr int BN = 64;              // keys per tile
 constexpr int HD = 128;             // head dim
 constexpr int TILE = BN * HD;       // one K or V tile, fp16 elements (16 KB, rows of 256 bytes)
@@ -96,7 +98,7 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 template <bool MASKED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_f16(AttnArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_f16(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 smem[2 * BUF];
 
   const int n_qt = (a.n_q + BM - 1) / BM;
@@ -212,23 +214,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // rows past the end of a short tile fall outside it and are not read from memory (the LDS
   // tiles are zero-filled once at the start, so those rows always hold finite values, which the
   // mask then excludes).
-  // Wave w fills rows 16w .. 16w+15 of each tile: 4 copies of 1 KB (4 rows) for K and for V.
-  // Lane i of copy j covers row 16w + 4j + i/16, chunk position i%16; offsets are in bytes.
   const __amdgpu_buffer_rsrc_t rkA = __builtin_amdgcn_make_buffer_rsrc((void*)kA, (short)0, nA * HD * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t rvA = __builtin_amdgcn_make_buffer_rsrc((void*)vA, (short)0, ntA * BN * HD * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t rkB = __builtin_amdgcn_make_buffer_rsrc((void*)kB, (short)0, nB * HD * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t rvB = __builtin_amdgcn_make_buffer_rsrc((void*)vB, (short)0, (nB + BN - 1) / BN * BN * HD * 2, 0x00020000);
-  // K: wave w fills LDS rows 16w .. 16w+15 with 4 copies of 1 KB (4 rows of 256 bytes); lane i of
-  // copy j writes row 16w + 4j + i/16 at chunk position i%16, from key 16w + 4perm(j) + i/16.
-  // V^T: wave w fills rows (dims) 32w .. 32w+31 with 4 copies of 1 KB (8 rows of 128 bytes); lane
-  // i of copy j writes row 32w + 8j + i/8 at chunk position i%8.  Byte offsets within the tile.
-  int koff[4], voff[4];
+  // K: wave w fills LDS rows 8w .. 8w+7 with 2 copies of 1 KB (4 rows of 256 bytes); lane i of
+  // copy j writes row r = 8w + 4j + i/16 at chunk position i%16, from the key that the row
+  // permutation puts there.  V^T: wave w fills rows (dims) 16w .. 16w+15 with 2 copies of 1 KB
+  // (8 rows of 128 bytes); lane i of copy j writes row 16w + 8j + i/8 at chunk position i%8.
+  // Byte offsets within the tile.
+  int koff[2], voff[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 16 * wave + 4 * j + (lane >> 4);
-    const int src = 16 * wave + 4 * k_row_perm(j) + (lane >> 4);
+  for (int j = 0; j < 2; ++j) {
+    const int row = 8 * wave + 4 * j + (lane >> 4);
+    const int src = (row & ~15) + 4 * k_row_perm((row >> 2) & 3) + (row & 3);
     koff[j] = 2 * (src * HD + 8 * ((lane & 15) ^ swz_k(row)));
-    const int vrow = 32 * wave + 8 * j + (lane >> 3);
+    const int vrow = 16 * wave + 8 * j + (lane >> 3);
     voff[j] = 2 * (vrow * BN + 8 * ((lane & 7) ^ swz_v(vrow)));
   }
   // copy j of K (is_k) or V^T of key tile t into stage buf (both tiles are 16 KB in memory)
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bool inA = t < ntA;
     const __amdgpu_buffer_rsrc_t rs = IS_K ? (inA ? rkA : rkB) : (inA ? rvA : rvB);
     const int soff = (inA ? t : t - ntA) * (BN * HD * 2);
-    _Float16* dst = smem + buf * BUF + (IS_K ? (16 * wave + 4 * j) * HD : TILE + (32 * wave + 8 * j) * BN);
+    _Float16* dst = smem + buf * BUF + (IS_K ? (8 * wave + 4 * j) * HD : TILE + (16 * wave + 8 * j) * BN);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, IS_K ? koff[j] : voff[j], soff, 0, 0);
   };
 
@@ -302,8 +303,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // accumulators starting at minus the reference).  Every step also issues the LDS operand reads
   // of the next step and forms two probabilities 2^s of the current tile (scores 2i, 2i+1 of
   // the first 32-key block in steps 0-7, of the second in steps 8-15), rounded to fp16 and folded
-  // into a packed max; steps 0-3 issue the eight copies of later tiles (K of tile tk, V of tile
-  // tv, into stage cb).  So the softmax VALU work is spread over all 32 MFMAs of the tile.
+  // into a packed max; steps 0-1 issue the wave's four copies of later tiles (K of tile tk, V of
+  // tile tv, into stage cb).  So the softmax VALU work is spread over all 32 MFMAs of the tile.
   auto seq = [&](int rb, int cb, int tk, int tv, f32x16& sn0, f32x16& sn1, const f32x16& s0, const f32x16& s1,
                  const h8 (&pp)[4], h8 (&pf)[4], float& lsum) -> h2 {
     const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         read_v2(rb, i + 1, va[(i + 1) & 1]);
       else if (i + 1 < 16)
         read_k(rb, i + 1 - 8, ka[(i + 1) & 1]);
-      if (i < 4) {
+      if (i < 2) {
         copy(tk, cb, i, std::true_type{});
         copy(tv, cb, i, std::false_type{});
       }
@@ -392,11 +393,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // zero-fill both stages once, so that rows of short tiles that no copy writes hold zeros
     u32x4* z = (u32x4*)smem;
 #pragma unroll
-    for (int i = 0; i < (2 * BUF * 2) / (16 * 256); ++i) z[i * 256 + tid] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < (2 * BUF * 2) / (16 * 512); ++i) z[i * 512 + tid] = u32x4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     copy(t_begin, 0, j, std::true_type{});
     copy(t_begin + 1 < t_stop ? t_begin + 1 : t_begin, 1, j, std::true_type{});
   }
@@ -581,16 +582,26 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_
 }  // namespace
 
 int attn_f16_splits(int64_t T, int32_t n_head) {
-  // Split the key range only when the target's query tiles cannot give every CU two
-  // workgroups (512 slots); then aim at about 1024 workgroups, at most 8 chunks.  Larger grids
-  // stay whole: at 768 query tiles (the 4096-token target at 24 heads) two chunks would fill the
-  // last round of workgroups (3 % faster) but fetch the keys from memory almost twice and move
-  // 200 MB of partial outputs through the merge.
+  // One workgroup fills a CU, so a launch runs in rounds of 256 workgroups.  Grids of four or
+  // more rounds stay whole.  Smaller ones are cut into s key chunks, s = 1 .. 8, chosen for the
+  // fullest last round, each chunk beyond the first charged 1 % and any chunking 3 % for the
+  // partial outputs and their merge: the 4096-token target at 24 heads (384 query tiles) runs
+  // as two chunks in three full rounds instead of one and a half.
+  constexpr int64_t slots = 256;
   const int64_t units = (T + BM - 1) / BM * n_head;
-  if (units >= 512) return 1;
-  int64_t s = (1024 + units - 1) / units;
-  if (s > 8) s = 8;
-  return (int)s;
+  if (units >= 4 * slots || units <= 0) return 1;
+  int best = 1;
+  double best_score = -1.0;
+  for (int s = 1; s <= 8; ++s) {
+    const int64_t blocks = units * s;
+    const double eff = (double)blocks / (double)(slots * ((blocks + slots - 1) / slots));
+    const double score = eff - (s > 1 ? 0.03 : 0.0) - 0.01 * s;
+    if (score > best_score + 1e-9) {
+      best_score = score;
+      best = s;
+    }
+  }
+  return best;
 }
 
 int64_t attn_f16_partial_bytes(int64_t n_q, int32_t n_head) {
@@ -607,9 +618,9 @@ hipError_t launch_attn_f16(const AttnArgs& a_in, hipStream_t s) {
   const int64_t blocks = n_qt * a.n_head * a.n_split;
   if (blocks <= 0) return hipSuccess;
   if (a.masked)
-    hipLaunchKernelGGL(k_attn_f16<true>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attn_f16<true>, dim3((unsigned)blocks), dim3(2 * BM), 0, s, a);
   else
-    hipLaunchKernelGGL(k_attn_f16<false>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attn_f16<false>, dim3((unsigned)blocks), dim3(2 * BM), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   const int64_t threads = (int64_t)a.n_q * a.n_head * 16;

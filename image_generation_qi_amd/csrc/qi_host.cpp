@@ -172,7 +172,7 @@ int qi_blockmap(const qi_layout* layout, int32_t tile_q, int32_t tile_k, uint8_t
 int qi_attn_tile_shape(qi_dtype dtype, int32_t* tile_q, int32_t* tile_k) {
   if (!tile_q || !tile_k) return QI_ERR_ARG;
   if (dtype == QI_BF16) {
-    *tile_q = 128;
+    *tile_q = kAttnF16TileQ;
     *tile_k = 64;
   } else if (dtype == QI_F32) {
     *tile_q = 1;

@@ -71,6 +71,9 @@ struct AttnArgs {
   SegTable segs;
 };
 
+// Query rows per workgroup of the fp16 path (the tile height reported by qi_attn_tile_shape).
+constexpr int kAttnF16TileQ = 256;
+
 // Number of key chunks of the fp16 path for a sequence whose target has T tokens and n_head
 // heads.  Step 1 and the cached steps both use the layout's T, so a target row is processed in
 // the same chunks (and gets the same bits) in both.
