@@ -154,7 +154,9 @@ def dit_bench(args):
     model.step(1, lat, sig)
     torch.cuda.synchronize()
     ms1 = timed(lambda: model.step(0, lat, sig, x_text, lat_ref))
-    cached = [timed(lambda k=k: model.step(k, lat, sig)) for k in range(1, 1 + args.steps)]
+    # cached steps cycle through the schedule's steps 1..7 (sig holds 8 steps + the end point)
+    n_cached = len(sig) - 2
+    cached = [timed(lambda k=1 + i % n_cached: model.step(k, lat, sig)) for i in range(args.steps)]
     msc = sum(cached) / len(cached)
     res = {
         "metric": "single-stream DiT denoiser step time (conditioning + layers + head + Euler)",

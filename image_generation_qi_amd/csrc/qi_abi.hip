@@ -160,6 +160,34 @@ int run_attn(const AttnArgs& a, qi_dtype dtype, hipStream_t s) {
   return launch_status(dtype == QI_BF16 ? launch_attn_f16(a, s) : launch_attn_f32(a, s));
 }
 
+// Step 1 on the bf16 path: the prefix query rows [0, P) run as one launch over whole key ranges,
+// the target rows [P, S) as a second launch in the target's key chunks, exactly as a cached step
+// runs them, so the target rows get the same bits in both.  Partials cover the target rows only.
+int run_attn_step1_f16(const AttnArgs& a, int64_t P, int64_t T, char* part_base, hipStream_t s) {
+  if (a.nA > QI_MAX_SOURCE_KEYS || a.nB > QI_MAX_SOURCE_KEYS) return QI_ERR_SHAPE;
+  TimedLaunch t(s);
+  AttnArgs ap = a;
+  ap.n_q = (int32_t)P;
+  ap.n_split = 1;
+  ap.part_o = nullptr;
+  ap.part_ml = nullptr;
+  AttnArgs at = a;
+  at.q = (const char*)a.q + P * a.q_stride * 2;
+  at.o = (char*)a.o + P * a.o_stride * 2;
+  if (a.cos_q) {
+    at.cos_q = a.cos_q + P * (QI_HEAD_DIM / 2);
+    at.sin_q = a.sin_q + P * (QI_HEAD_DIM / 2);
+  }
+  at.n_q = (int32_t)T;
+  at.q_row0 = a.q_row0 + P;
+  set_partials(at, part_base, T, T, a.n_head, QI_BF16);
+  if (P > 0) {
+    const hipError_t e = launch_attn_f16(ap, s);
+    if (e != hipSuccess) return launch_status(e);
+  }
+  return launch_status(launch_attn_f16(at, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -221,8 +249,7 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
   a.masked = 1;
   a.segs = li.tab;
   a.q_row0 = 0;
-  set_partials(a, (char*)workspace + 2 * (int64_t)io->n_head * R * QI_HEAD_DIM * es, li.S, li.T, io->n_head,
-               io->dtype);
+  a.n_split = 1;   // the bf16 launches set their own chunking (run_attn_step1_f16)
   // target rows: K/V prepared into the workspace at row RA (with the target's table rows)
   const int64_t off = li.P * io->tok_stride * (io->dtype == QI_BF16 ? 2 : 4);
   qi_qkprep tprep{};
@@ -263,6 +290,8 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
     a.a_head_stride = R * QI_HEAD_DIM;
   }
   a.nA = li.P;
+  if (io->dtype == QI_BF16)
+    return run_attn_step1_f16(a, li.P, li.T, (char*)workspace + 2 * (int64_t)io->n_head * R * QI_HEAD_DIM * es, s);
   return run_attn(a, io->dtype, s);
 }
 

@@ -206,7 +206,7 @@ int64_t qi_attn_full_workspace_bytes(const qi_layout* layout, qi_dtype dtype, in
   // prefix rows and target rows, each padded to whole 64-key tiles
   const int64_t r = rows_bytes(dtype, rows64(li.P) + rows64(li.T), n_head);
   if (r < 0) return r;
-  return r + partial_bytes(dtype, li.S, li.T, n_head);
+  return r + partial_bytes(dtype, li.T, li.T, n_head);   // partials of the target rows only
 }
 
 int64_t qi_attn_cached_workspace_bytes(qi_dtype dtype, int64_t T, int32_t n_head) {
