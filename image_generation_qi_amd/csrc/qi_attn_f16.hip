@@ -9,27 +9,31 @@
 //   - one workgroup = 8 wavefronts = 256 query rows of one head; wave w owns rows 32w..32w+31.
 //     Two waves share each SIMD and one workgroup fills a CU, so every K/V tile brought into
 //     LDS serves 256 queries.
-//   - keys stream in tiles of 64 through LDS (two stages of K and V, 64 KB), copied with MUBUF
-//     buffer -> LDS loads (keeps the compute phases' LDS waits exact) into unpadded rows whose
-//     16-byte chunks are XOR-swizzled, so both MFMA A-operand reads are bank-conflict free.
-//     K is row-major [key][128]; V is stored (by the prep kernel) and staged transposed, as
-//     tiles of [128 dims][64 keys].  Source A (cache or workspace prefix) and source B (fresh
-//     keys) are tiled separately, so every copy reads one source.
+//   - keys stream in tiles of 64 through LDS (two stages of K and V, 64 KB), copied whole with
+//     MUBUF buffer -> LDS loads (which keep the compute phases' LDS waits exact).  The tiles are
+//     stored by the prep kernels in the order the MFMA operands are read (K as [16 dim chunks][64
+//     key slots][8 dims], V as [8 key chunks][128 dims][8 keys]): every operand read of 16 lanes
+//     is 256 contiguous bytes (no bank conflicts, no swizzle) at a constant offset from one
+//     per-lane base, the stage of each read is known at compile time, and every 1 KB copy is
+//     contiguous at both ends.  Source A (cache or workspace prefix) and source B (fresh keys)
+//     are tiled separately, so every copy reads one source.
 //   - S^T = K Q^T - m with v_mfma_f32_32x32x16_f16: A = 32 keys x 16 dims from LDS, B = the
 //     wave's 32 queries (rotated, scaled by scale*log2(e), fp16) held in registers; the
-//     accumulators start at minus the row's reference m, so the scores come out shifted.  Each
-//     lane then holds one query and 16 keys per 32-key block.
+//     accumulators start at minus the row's reference m (kept broadcast in registers), so the
+//     scores come out shifted.  Each lane then holds one query and 16 keys per 32-key block.
 //   - O^T += V^T P^T with the same instruction: B = the lane's own probabilities (fp16), A = V^T
-//     rows of the transposed tile.  K rows are loaded with a fixed permutation inside every 16,
-//     so that the keys a lane holds in S^T are 8 consecutive keys per 16-key chunk: P never moves
-//     between lanes and each V^T operand is one 16-byte read.
+//     (32 dims x 16 keys).  K's key slots are permuted inside every 16 (rows 4-7 and 8-11
+//     exchanged), so that the keys a lane holds in S^T are 8 consecutive keys per 16-key chunk:
+//     P never moves between lanes.
 //   - online softmax in base 2 with a lazy reference: probabilities 2^(s) are formed against the
-//     current reference and only rows whose probabilities exceed 2^8 (or that have no reference
-//     yet) move it (a rare, wave-uniform branch); other rows keep a factor of exactly 1.
+//     current reference and only rows whose 32 probabilities in a lane sum above 2^8 (or that
+//     have no reference yet) move it (a rare, wave-uniform branch); other rows keep a factor of
+//     exactly 1.  Every probability therefore stays at or below 2^8.
 //   - software pipeline: the PV MFMAs of tile kt-1, the QK^T MFMAs of tile kt+1, the
-//     probabilities of tile kt, the LDS operand reads one step ahead and the copies of later
-//     tiles are one fenced sequence of 16 two-MFMA steps, so the softmax VALU work is spread
-//     over all 32 MFMAs of a tile and MFMA, VALU, LDS and memory work interleave.
+//     probabilities of tile kt (with their row sums), the LDS operand reads one step ahead and
+//     the copies of later tiles are one fenced sequence of 16 two-MFMA steps, so the softmax
+//     VALU work is spread over all 32 MFMAs of a tile and MFMA, VALU, LDS and memory work
+//     interleave.
 //   - the Block-Causal mask is applied per tile from the row limits (see qi_common.h): tiles
 //     with no visible pair are never loaded, tiles with all pairs visible run unmasked.
 //   - key chunks (n_split > 1) balance the grid over the CUs: each chunk of a query tile's key
@@ -55,8 +59,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int BM = kAttnF16TileQ;   // query rows per workgroup (8 waves of 32)
 constexpr int BN = 64;              // keys per tile
 constexpr int HD = 128;             // head dim
-constexpr int TILE = BN * HD;       // one K or V tile, fp16 elements (16 KB, rows of 256 bytes)
-constexpr int BUF = 2 * TILE;       // one pipeline stage: K tile then V tile
+constexpr int TILE_B = BN * HD * 2; // bytes of one K or V tile (16 KB)
+constexpr int STAGE_B = 2 * TILE_B; // one pipeline stage: K tile then V tile
 
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
   const int q = n >> 3, r = n & 7;
@@ -73,18 +77,8 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// LDS tiles hold unpadded rows whose 16-byte chunk c of row r sits at chunk position c ^ swz(r).
-// K tile: 64 rows (keys) of 256 bytes, swz = r & 15, so the 16 rows read by a quarter-wave at one
-// logical chunk hit 16 distinct positions.  V^T tile: 128 rows (dims) of 128 bytes (64 keys),
-// swz = (r >> 1) & 7: the 16 rows of a quarter-wave span 8 row pairs x 2 halves of the bank
-// space, again 16 distinct positions.
-__device__ __forceinline__ int swz_k(int r) { return r & 15; }
-__device__ __forceinline__ int swz_v(int r) { return (r >> 1) & 7; }
-
-// K rows are loaded with rows 4-7 and 8-11 of every 16 swapped, so that the keys a lane holds in
-// the S^T accumulator (rows 8(r/4) + 4g + r%4) are keys 16(r/8) + 8g + r%8: each lane's 8
-// probabilities of a 16-key chunk are 8 consecutive keys, one 16-byte row piece of V^T.
-__device__ __forceinline__ int k_row_perm(int j) { return j == 1 ? 2 : (j == 2 ? 1 : j); }
+template <int N>
+using ic = std::integral_constant<int, N>;
 
 // Both halves of a wave exchanged: for lane l, returns (x[l], x[l ^ 32]) in an order that is
 // the same for the two lanes of the pair, so any symmetric combination is bit-identical.
@@ -99,7 +93,7 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 template <bool MASKED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_f16(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 smem[2 * BUF];
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_B];
 
   const int n_qt = (a.n_q + BM - 1) / BM;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -203,43 +197,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return;
   }
 
-  const _Float16* kA = (const _Float16*)a.kA + (int64_t)h * a.a_head_stride;
-  const _Float16* vA = (const _Float16*)a.vA + (int64_t)h * a.a_head_stride;
-  const _Float16* kB = (const _Float16*)a.kB + (int64_t)h * a.b_head_stride;
-  const _Float16* vB = (const _Float16*)a.vB + (int64_t)h * a.b_head_stride;
-
   // ---- tile staging: buffer -> LDS copies (MUBUF with the LDS bit) ---------------------------
-  // The MUBUF form keeps the LDS reads of the compute phases on exact lgkmcnt waits while these
-  // copies are in flight.  One buffer resource per head and source, sized to that source's rows:
-  // rows past the end of a short tile fall outside it and are not read from memory (the LDS
-  // tiles are zero-filled once at the start, so those rows always hold finite values, which the
-  // mask then excludes).
-  const __amdgpu_buffer_rsrc_t rkA = __builtin_amdgcn_make_buffer_rsrc((void*)kA, (short)0, nA * HD * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rvA = __builtin_amdgcn_make_buffer_rsrc((void*)vA, (short)0, ntA * BN * HD * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rkB = __builtin_amdgcn_make_buffer_rsrc((void*)kB, (short)0, nB * HD * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rvB = __builtin_amdgcn_make_buffer_rsrc((void*)vB, (short)0, (nB + BN - 1) / BN * BN * HD * 2, 0x00020000);
-  // K: wave w fills LDS rows 8w .. 8w+7 with 2 copies of 1 KB (4 rows of 256 bytes); lane i of
-  // copy j writes row r = 8w + 4j + i/16 at chunk position i%16, from the key that the row
-  // permutation puts there.  V^T: wave w fills rows (dims) 16w .. 16w+15 with 2 copies of 1 KB
-  // (8 rows of 128 bytes); lane i of copy j writes row 16w + 8j + i/8 at chunk position i%8.
-  // Byte offsets within the tile.
-  int koff[2], voff[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = 8 * wave + 4 * j + (lane >> 4);
-    const int src = (row & ~15) + 4 * k_row_perm((row >> 2) & 3) + (row & 3);
-    koff[j] = 2 * (src * HD + 8 * ((lane & 15) ^ swz_k(row)));
-    const int vrow = 16 * wave + 8 * j + (lane >> 3);
-    voff[j] = 2 * (vrow * BN + 8 * ((lane & 7) ^ swz_v(vrow)));
-  }
-  // copy j of K (is_k) or V^T of key tile t into stage buf (both tiles are 16 KB in memory)
-  auto copy = [&](int t, int buf, int j, auto is_k_tag) {
+  // One buffer resource per head and source, sized to that source's whole tiles (the prep
+  // kernels zero the keys of a short last tile, so staged rows are always finite and the mask
+  // excludes them).  Wave w copies 1 KB pieces 2w and 2w+1 of each K and V tile: lane i moves
+  // bytes 16i .. 16i+15 of the piece, so both the memory and the LDS side are contiguous.
+  const int ntB = (nB + BN - 1) / BN;
+  const char* kA = (const char*)a.kA + (int64_t)h * a.a_head_stride * 2;
+  const char* vA = (const char*)a.vA + (int64_t)h * a.a_head_stride * 2;
+  const char* kB = (const char*)a.kB + (int64_t)h * a.b_head_stride * 2;
+  const char* vB = (const char*)a.vB + (int64_t)h * a.b_head_stride * 2;
+  const __amdgpu_buffer_rsrc_t rkA = __builtin_amdgcn_make_buffer_rsrc((void*)kA, (short)0, ntA * TILE_B, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rvA = __builtin_amdgcn_make_buffer_rsrc((void*)vA, (short)0, ntA * TILE_B, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rkB = __builtin_amdgcn_make_buffer_rsrc((void*)kB, (short)0, ntB * TILE_B, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rvB = __builtin_amdgcn_make_buffer_rsrc((void*)vB, (short)0, ntB * TILE_B, 0x00020000);
+  const int voff = lane * 16;
+  // copy j (0 or 1) of the K (is_k) or V tile t into stage `stage`
+  auto copy = [&](int t, int stage, int j, auto is_k_tag) {
     constexpr bool IS_K = decltype(is_k_tag)::value;
     const bool inA = t < ntA;
     const __amdgpu_buffer_rsrc_t rs = IS_K ? (inA ? rkA : rkB) : (inA ? rvA : rvB);
-    const int soff = (inA ? t : t - ntA) * (BN * HD * 2);
-    _Float16* dst = smem + buf * BUF + (IS_K ? (8 * wave + 4 * j) * HD : TILE + (16 * wave + 8 * j) * BN);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, IS_K ? koff[j] : voff[j], soff, 0, 0);
+    const int piece = (2 * wave + j) * 1024;
+    const int soff = (inA ? t : t - ntA) * TILE_B + piece;
+    char* dst = smem + stage * STAGE_B + (IS_K ? 0 : TILE_B) + piece;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, soff, 0, 0);
   };
 
   f32x16 o[4];
@@ -248,95 +229,72 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[bd][r] = 0.f;
   // m_run: the reference (log2 units) the scores of the current tile were taken against; -inf
-  // until a row has seen a visible key (its scores are then taken against 0)
+  // until a row has seen a visible key (its scores are then taken against 0).  ninit holds the
+  // accumulator start value (minus the reference, 0 while it is -inf) broadcast over 16 entries.
   float m_run = -INFINITY, l_run = 0.f;
-
-  // ---- LDS operand reads -------------------------------------------------------------------
-  // K: the two S^T A operands of reduction step kk (keys l32 and 32 + l32, dims 16kk + 8g ..).
-  // Rows l32 and 32 + l32 share (row & 15), so both reads use the same chunk position.
-  auto read_k = [&](int kbuf, int kk, h8 (&dst)[2]) {
-    const _Float16* Ks = smem + kbuf * BUF;
-    const int pos = ((2 * kk + g) ^ swz_k(l32)) * 8;
-    dst[0] = *(const h8*)(Ks + l32 * HD + pos);
-    dst[1] = *(const h8*)(Ks + (32 + l32) * HD + pos);
-  };
-  // V^T: the four O^T A operands (dims 32bd + l32) of 16-key chunk c: keys 16c + 8g .. + 7, one
-  // 16-byte piece of the dim's 128-byte row.
-  auto read_v = [&](int vbuf, int c, h8 (&dst)[4]) {
-    const _Float16* Vs = smem + vbuf * BUF + TILE;
+  f32x16 ninit;
 #pragma unroll
-    for (int bd = 0; bd < 4; ++bd) {
-      const int d = 32 * bd + l32;
-      dst[bd] = *(const h8*)(Vs + d * BN + 8 * ((2 * c + g) ^ swz_v(d)));
-    }
+  for (int r = 0; r < 16; ++r) ninit[r] = 0.f;
+
+  // ---- LDS operand reads (byte offsets from one per-lane base, the rest constant) -----------
+  // K (reduction step kk, key block kb): slot 32kb + l32, dims 16kk + 8g .. + 7 = piece
+  // (2kk + g) * 1024 + slot * 16.  V^T (16-key chunk c, dims 32bd + l32): keys 16c + 8g .. + 7 =
+  // piece (2c + g) * 2048 + dim * 16.
+  const int base_k = g * 1024 + l32 * 16;
+  const int base_v = TILE_B + g * 2048 + l32 * 16;
+  auto read_k = [&](auto stag, int kk, int kb) -> h8 {
+    return *(const h8*)(smem + decltype(stag)::value * STAGE_B + base_k + kk * 2048 + kb * 512);
+  };
+  auto read_v = [&](auto stag, int c, int bd) -> h8 {
+    return *(const h8*)(smem + decltype(stag)::value * STAGE_B + base_v + c * 4096 + bd * 512);
   };
 
-  // S^T - m = K Q^T - m for the 64 keys of one K buffer: the accumulators start at minus the
-  // reference, so the scores come out already shifted.  Prologue only.
-  auto qk = [&](int kbuf, f32x16& s0, f32x16& s1) {
-    const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
-    f32x16 init;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) init[r] = nm;
+  // S^T - m = K Q^T - m for the 64 keys of stage 0's K tile.  Prologue only.
+  auto qk0 = [&](f32x16& s0, f32x16& s1) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      h8 ka[2];
-      read_k(kbuf, kk, ka);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[0], qf[kk], kk ? s0 : init, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[1], qf[kk], kk ? s1 : init, 0, 0, 0);
-    }
-  };
-
-  // V^T operands of PV step i (chunk i/2, dims 64(i%2) .. 64(i%2) + 63: two 32-dim blocks)
-  auto read_v2 = [&](int vbuf, int i, h8 (&dst)[2]) {
-    const _Float16* Vs = smem + vbuf * BUF + TILE;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int d = 32 * (2 * (i & 1) + e) + l32;
-      dst[e] = *(const h8*)(Vs + d * BN + 8 * ((2 * (i >> 1) + g) ^ swz_v(d)));
+      const h8 k0 = read_k(ic<0>{}, kk, 0), k1 = read_k(ic<0>{}, kk, 1);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qf[kk], kk ? s0 : ninit, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qf[kk], kk ? s1 : ninit, 0, 0, 0);
     }
   };
 
   // One iteration's compute as a single fenced sequence of 16 steps of two MFMAs each: steps 0-7
-  // are the PV of the previous tile (probabilities pp, chunk i/2, dims 64(i%2) .. + 63) with two
-  // of its row-sum dot products, steps 8-15 the QK^T of the next tile (reduction step i - 8,
-  // accumulators starting at minus the reference).  Every step also issues the LDS operand reads
-  // of the next step and forms two probabilities 2^s of the current tile (scores 2i, 2i+1 of
-  // the first 32-key block in steps 0-7, of the second in steps 8-15), rounded to fp16 and folded
-  // into a packed max; steps 0-1 issue the wave's four copies of later tiles (K of tile tk, V of
-  // tile tv, into stage cb).  So the softmax VALU work is spread over all 32 MFMAs of the tile.
-  auto seq = [&](int rb, int cb, int tk, int tv, f32x16& sn0, f32x16& sn1, const f32x16& s0, const f32x16& s1,
-                 const h8 (&pp)[4], h8 (&pf)[4], float& lsum) -> h2 {
-    const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
-    f32x16 init;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) init[r] = nm;
+  // are the PV of the previous tile (probabilities pp, chunk i/2, dims 64(i%2) .. + 63), steps
+  // 8-15 the QK^T of the next tile (reduction step i - 8, both 32-key blocks, accumulators
+  // starting at minus the reference).  Every step also issues the LDS operand reads of the next
+  // step and forms two probabilities 2^s of the current tile (scores 2i, 2i+1 of the first
+  // 32-key block in steps 0-7, of the second in steps 8-15), rounded to fp16 and added into the
+  // row sum; steps 0-3 issue the wave's four copies of later tiles (K of tile tk, V of tile tv,
+  // into stage cs).  So the softmax VALU work is spread over all 32 MFMAs of the tile.
+  auto seq = [&](auto rtag, int cs, int tk, int tv, f32x16& sn0, f32x16& sn1, const f32x16& s0, const f32x16& s1,
+                 const h8 (&pp)[4], h8 (&pf)[4]) -> float {
     const h2 one2 = {(_Float16)1.f, (_Float16)1.f};
-    h8 va[2][2], ka[2][2];
-    read_v2(rb, 0, va[0]);
-    h2 pm0 = {(_Float16)0.f, (_Float16)0.f}, pm1 = pm0;
+    // operands of step n: V^T (chunk n/2, dims 64(n%2) + 32e ..) for n < 8, K (step n - 8,
+    // key blocks e = 0, 1) after
+    auto read_ops = [&](int n, h8 (&d)[2]) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) d[e] = n < 8 ? read_v(rtag, n >> 1, 2 * (n & 1) + e) : read_k(rtag, n - 8, e);
+    };
+    h8 op[2][2];
+    read_ops(0, op[0]);
     float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if (i + 1 < 8)
-        read_v2(rb, i + 1, va[(i + 1) & 1]);
-      else if (i + 1 < 16)
-        read_k(rb, i + 1 - 8, ka[(i + 1) & 1]);
-      if (i < 2) {
-        copy(tk, cb, i, std::true_type{});
-        copy(tv, cb, i, std::false_type{});
-      }
+      if (i + 1 < 16) read_ops(i + 1, op[(i + 1) & 1]);
+      if (i < 2)
+        copy(tk, cs, i, std::true_type{});
+      else if (i < 4)
+        copy(tv, cs, i - 2, std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
       if (i < 8) {
         const int c = i >> 1, bd = 2 * (i & 1);
-        o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i & 1][0], pp[c], o[bd], 0, 0, 0);
-        o[bd + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i & 1][1], pp[c], o[bd + 1], 0, 0, 0);
-        ps0 = __builtin_amdgcn_fdot2(h2{pp[c][4 * (i & 1)], pp[c][4 * (i & 1) + 1]}, one2, ps0, false);
-        ps1 = __builtin_amdgcn_fdot2(h2{pp[c][4 * (i & 1) + 2], pp[c][4 * (i & 1) + 3]}, one2, ps1, false);
+        o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[i & 1][0], pp[c], o[bd], 0, 0, 0);
+        o[bd + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[i & 1][1], pp[c], o[bd + 1], 0, 0, 0);
       } else {
         const int kk = i - 8;
-        sn0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[i & 1][0], qf[kk], kk ? sn0 : init, 0, 0, 0);
-        sn1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[i & 1][1], qf[kk], kk ? sn1 : init, 0, 0, 0);
+        sn0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[i & 1][0], qf[kk], kk ? sn0 : ninit, 0, 0, 0);
+        sn1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[i & 1][1], qf[kk], kk ? sn1 : ninit, 0, 0, 0);
       }
       const int j = i & 7;
       const float p0 = __builtin_amdgcn_exp2f(i < 8 ? s0[2 * j] : s1[2 * j]);
@@ -345,55 +303,39 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       pf[(i < 8 ? 0 : 2) + (j >> 2)][2 * (j & 3)] = q[0];
       pf[(i < 8 ? 0 : 2) + (j >> 2)][2 * (j & 3) + 1] = q[1];
       if (i < 8)
-        pm0 = __builtin_elementwise_max(pm0, q);
+        ps0 = __builtin_amdgcn_fdot2(q, one2, ps0, false);
       else
-        pm1 = __builtin_elementwise_max(pm1, q);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    lsum = ps0 + ps1;
-    return __builtin_elementwise_max(pm0, pm1);
-  };
-
-  // O^T += V^T P^T for one V buffer, as four fenced steps: each issues the V reads of chunk
-  // c + 1 and the four MFMAs of chunk c, with the row sum of chunk c's probabilities (fp32 dot
-  // products of the same fp16 values) between them.
-  auto pv_sums = [&](int vbuf, const h8 (&pf)[4]) -> float {
-    h8 va[2][4];
-    read_v(vbuf, 0, va[0]);
-    const h2 one2 = {(_Float16)1.f, (_Float16)1.f};
-    float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (c + 1 < 4) read_v(vbuf, c + 1, va[(c + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int bd = 0; bd < 4; ++bd) {
-        o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[c & 1][bd], pf[c], o[bd], 0, 0, 0);
-        if (bd & 1)
-          ps1 = __builtin_amdgcn_fdot2(h2{pf[c][2 * bd], pf[c][2 * bd + 1]}, one2, ps1, false);
-        else
-          ps0 = __builtin_amdgcn_fdot2(h2{pf[c][2 * bd], pf[c][2 * bd + 1]}, one2, ps0, false);
-      }
+        ps1 = __builtin_amdgcn_fdot2(q, one2, ps1, false);
       __builtin_amdgcn_sched_barrier(0);
     }
     return ps0 + ps1;
   };
 
+  // PV of the last tile (V in stage `stage`, known only at run time), after the loop.
+  auto pv_last = [&](int stage, const h8 (&pp)[4]) {
+    const char* vs = smem + stage * STAGE_B + base_v;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int bd = 0; bd < 4; ++bd)
+        o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const h8*)(vs + c * 4096 + bd * 512), pp[c], o[bd], 0, 0, 0);
+  };
+
   // ---- software-pipelined main loop ------------------------------------------------------
-  // Tile j's K and V live in stage (j - t_begin) & 1.  Iteration kt reads only the other stage
-  // b' = (kt - 1 - t_begin) & 1 and copies only into stage b = (kt - t_begin) & 1: one fenced
-  // sequence runs the PV of tile kt-1 (V from stage b', probabilities carried from the previous
-  // iteration), the QK^T of tile kt+1 (K from stage b') and the probabilities of tile kt, and
-  // issues the copies of K[kt+2] and V[kt] into stage b (last read in iteration kt-1); then the
-  // rare reference update of tile kt; then the copies are waited for and a barrier ends the
-  // iteration.  The first iteration's PV multiplies zero probabilities with the zero-filled V
-  // stage.  The loop is unrolled twice so that scores and probabilities swap register sets
-  // instead of being copied; the PV of the last tile follows the loop.
+  // Tile j's K and V live in stage (j - t_begin) & 1.  Iteration kt (stage b = (kt - t_begin)
+  // & 1, known at compile time: the loops run in pairs from an even offset) reads only the other
+  // stage b' and copies only into stage b: one fenced sequence runs the PV of tile kt-1 (V from
+  // stage b', probabilities carried from the previous iteration), the QK^T of tile kt+1 (K from
+  // stage b') and the probabilities of tile kt, and issues the copies of K[kt+2] and V[kt] into
+  // stage b (last read in iteration kt-1); then the rare reference update of tile kt; then the
+  // copies are waited for and a barrier ends the iteration.  The first iteration's PV multiplies
+  // zero probabilities with the zero-filled V stage.  Scores and probabilities alternate between
+  // two register sets; the PV of the last tile follows the loop.
   {
-    // zero-fill both stages once, so that rows of short tiles that no copy writes hold zeros
+    // zero-fill both stages once, so that the first iteration's V stage holds zeros
     u32x4* z = (u32x4*)smem;
 #pragma unroll
-    for (int i = 0; i < (2 * BUF * 2) / (16 * 512); ++i) z[i * 512 + tid] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < (2 * STAGE_B) / (16 * 512); ++i) z[i * 512 + tid] = u32x4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
 #pragma unroll
@@ -404,21 +346,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16 sa0, sa1, sb0, sb1;
-  qk(0, sa0, sa1);
+  qk0(sa0, sa1);
   // every wave has read K[t_begin] from stage 0 before the first iteration copies into it
   __syncthreads();
   int kt = t_begin;
   const int kt_mid = kt_full < t_begin ? t_begin : (kt_full < t_stop ? kt_full : t_stop);
+  const int kt_mid2 = t_begin + ((kt_mid - t_begin) & ~1);   // unmasked pairs end here
   // probabilities of the previous and the current tile (two register sets, swapped per iteration)
   h8 pa[4], pb[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) pa[c][e] = (_Float16)0.f;
-  auto iteration = [&](auto masked_tag, f32x16& s0, f32x16& s1, f32x16& sn0, f32x16& sn1, const h8 (&pp)[4],
-                       h8 (&pf)[4]) {
+  auto iteration = [&](auto btag, auto masked_tag, f32x16& s0, f32x16& s1, f32x16& sn0, f32x16& sn1,
+                       const h8 (&pp)[4], h8 (&pf)[4]) {
+    constexpr int B = decltype(btag)::value;
     constexpr bool MT = decltype(masked_tag)::value;
-    const int b = (kt - t_begin) & 1;
     if constexpr (MT) {
       const int key0 = kt < ntA ? kt * BN : nA + (kt - ntA) * BN;
       const int cnt = kt < ntA ? nA - kt * BN : nkeys - key0;   // keys of the tile (capped below)
@@ -427,25 +370,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       rel -= 8 * g;                 // offset (in tile, minus 8g) of the last visible key
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kr = 16 * (r >> 3) + (r & 7);   // key of accumulator entry r (rows permuted at load)
+        const int kr = 16 * (r >> 3) + (r & 7);   // key of accumulator entry r (slots permuted)
         if (kr > rel) s0[r] = -INFINITY;
         if (kr + 32 > rel) s1[r] = -INFINITY;
       }
     }
     // next tile's scores (on the last iteration from a stale, in-bounds stage, discarded)
     const int tk = kt + 2 < t_stop ? kt + 2 : t_stop - 1;
-    float lsum;
-    const h2 pm = seq(b ^ 1, b, tk, kt, sn0, sn1, s0, s1, pp, pf, lsum);
-    l_run += lsum;
-    // Rare path: a row's first visible tile (reference still -inf) or probabilities above 2^8
-    // (fp16 bits of a non-negative value above 0x5C00, which includes +inf).  The row's new
-    // reference is its true max; the probabilities are recomputed, the running output and sum
-    // are rescaled by alpha, and the next tile's scores (taken against the old reference) are
-    // shifted.  Rows that do not take it keep alpha = 1 exactly, so each row's arithmetic never
-    // depends on the other rows of the wave.
-    const uint32_t pmb = __builtin_bit_cast(uint32_t, pm);
-    const uint32_t pmx = (pmb & 0xFFFFu) > (pmb >> 16) ? (pmb & 0xFFFFu) : (pmb >> 16);
-    const bool need1 = pmx > 0x5C00u || m_run == -INFINITY;
+    float ps = seq(ic<B ^ 1>{}, B, tk, kt, sn0, sn1, s0, s1, pp, pf);
+    // Rare path: a row's first visible tile (reference still -inf) or a lane's 32 probabilities
+    // summing above 2^8 (which includes +inf and NaN).  The row's new reference is its true max;
+    // the probabilities and their sum are recomputed, the running output and sum are rescaled by
+    // alpha, the next tile's scores (taken against the old reference) are shifted and the
+    // accumulator start value follows the new reference.  Rows that do not take it keep alpha =
+    // 1 exactly, so each row's arithmetic never depends on the other rows of the wave.
+    const bool need1 = !(ps <= 256.f) || m_run == -INFINITY;
     if (__builtin_expect(__any(need1), 0)) {
       const auto sw = __builtin_amdgcn_permlane32_swap(need1 ? 1u : 0u, need1 ? 1u : 0u, false, false);
       const bool need = (sw[0] | sw[1]) != 0u;     // either half of the row
@@ -465,12 +404,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           m_run = m_run + mt;
         }
       }
+      const h2 one2 = {(_Float16)1.f, (_Float16)1.f};
+      float sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const h2 q0 = {(_Float16)__builtin_amdgcn_exp2f(s0[r] - shift), (_Float16)__builtin_amdgcn_exp2f(s0[r + 1] - shift)};
+        const h2 q1 = {(_Float16)__builtin_amdgcn_exp2f(s1[r] - shift), (_Float16)__builtin_amdgcn_exp2f(s1[r + 1] - shift)};
+        pf[r >> 3][r & 7] = q0[0];
+        pf[r >> 3][(r & 7) + 1] = q0[1];
+        pf[2 + (r >> 3)][r & 7] = q1[0];
+        pf[2 + (r >> 3)][(r & 7) + 1] = q1[1];
+        sum = __builtin_amdgcn_fdot2(q0, one2, sum, false);
+        sum = __builtin_amdgcn_fdot2(q1, one2, sum, false);
+      }
+      ps = sum;
+      const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        pf[r >> 3][r & 7] = (_Float16)__builtin_amdgcn_exp2f(s0[r] - shift);
-        pf[2 + (r >> 3)][r & 7] = (_Float16)__builtin_amdgcn_exp2f(s1[r] - shift);
         sn0[r] -= shift;
         sn1[r] -= shift;
+        ninit[r] = nm;
       }
 #pragma unroll
       for (int bd = 0; bd < 4; ++bd)
@@ -478,40 +431,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int r = 0; r < 16; ++r) o[bd][r] *= alpha;
       l_run *= alpha;
     }
+    l_run += ps;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  // between the loops the latest scores are in sa and the latest probabilities in pa
-  auto swap_in = [&]() {
-    sa0 = sb0;
-    sa1 = sb1;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) pa[c] = pb[c];
-  };
-  while (kt + 1 < kt_mid) {
-    iteration(std::false_type{}, sa0, sa1, sb0, sb1, pa, pb);
+  while (kt + 1 < kt_mid2) {
+    iteration(ic<0>{}, std::false_type{}, sa0, sa1, sb0, sb1, pa, pb);
     ++kt;
-    iteration(std::false_type{}, sb0, sb1, sa0, sa1, pb, pa);
+    iteration(ic<1>{}, std::false_type{}, sb0, sb1, sa0, sa1, pb, pa);
     ++kt;
-  }
-  if (kt < kt_mid) {
-    iteration(std::false_type{}, sa0, sa1, sb0, sb1, pa, pb);
-    ++kt;
-    swap_in();
   }
   while (kt + 1 < t_stop) {
-    iteration(std::true_type{}, sa0, sa1, sb0, sb1, pa, pb);
+    iteration(ic<0>{}, std::true_type{}, sa0, sa1, sb0, sb1, pa, pb);
     ++kt;
-    iteration(std::true_type{}, sb0, sb1, sa0, sa1, pb, pa);
+    iteration(ic<1>{}, std::true_type{}, sb0, sb1, sa0, sa1, pb, pa);
     ++kt;
   }
   if (kt < t_stop) {
-    iteration(std::true_type{}, sa0, sa1, sb0, sb1, pa, pb);
+    iteration(ic<0>{}, std::true_type{}, sa0, sa1, sb0, sb1, pa, pb);
     ++kt;
-    swap_in();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pa[c] = pb[c];
   }
   // PV of the last tile (its V was copied in the last iteration, before its barrier)
-  l_run += pv_sums((kt - 1 - t_begin) & 1, pa);
+  pv_last((kt - 1 - t_begin) & 1, pa);
 
   // ---- epilogue: normalise and store bf16, or store the chunk's partial ---------------------
   const float lt = pair_sum(l_run);

@@ -121,13 +121,72 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
   }
 }
 
-// V of the fp16 attention path, transposed into 64-key tiles: tile t of head h is [128 dims][64
-// keys] fp16 (key-minor), so the PV MFMA's V^T operand is a plain 16-byte row read.  Keys at or
-// past n in the last tile are written as zero.  One workgroup per (tile, head); the transpose
-// goes through LDS so that both the bf16 rows read and the 128-byte fp16 rows written are whole.
-__global__ __launch_bounds__(256) void k_prep_vt(const uint16_t* __restrict__ v, int64_t tok_stride, int64_t n,
-                                                 uint16_t* __restrict__ dst, int64_t dst_head_stride) {
-  __shared__ uint32_t sm[64][68];   // [key][dim pair]: fp16 pairs, rows padded to 68 words
+// K and V of the fp16 attention path, in the tiles its kernel copies whole into LDS: per head,
+// tiles of 64 keys, 16 KB each, keys at or past n written as zero.
+//   K tile: [16 dim chunks][64 key slots][8 dims] fp16.  Slot p holds key perm16(p) of the tile,
+//     perm16 exchanging rows 4-7 and 8-11 of every 16: then the keys a lane holds in the S^T
+//     accumulator of v_mfma_f32_32x32x16_f16 are 8 consecutive keys per 16-key chunk.
+//   V tile: [8 key chunks][128 dims][8 keys] fp16 (V transposed per 8-key chunk), so the P V
+//     MFMA's V^T operand (one dim, 8 keys) is one 16-byte piece.
+// In both, the 16-byte pieces that one MFMA operand read takes for 16 consecutive lanes are
+// consecutive in memory, and every 1 KB of a tile is one contiguous copy.
+__device__ __forceinline__ int perm16(int p) {
+  const int grp = (p >> 2) & 3;
+  return (p & ~15) | ((grp == 1 ? 2 : (grp == 2 ? 1 : grp)) << 2) | (p & 3);
+}
+
+// One workgroup per (64-key tile, head); 16 threads per key row (8 dims each), four rows each.
+__global__ __launch_bounds__(256) void k_prep_k64(PrepArgs a) {
+  const int t = blockIdx.x, h = blockIdx.y;
+  const int rr = threadIdx.x >> 4, c = threadIdx.x & 15;
+  uint16_t* tile = (uint16_t*)a.dst + (int64_t)h * a.dst_head_stride + (int64_t)t * 8192;
+#pragma unroll
+  for (int quarter = 0; quarter < 4; ++quarter) {
+    const int r = rr + 16 * quarter;
+    const int64_t j = (int64_t)t * 64 + r;
+    const bool ok = j < a.n_tok;
+    float x[8];
+    if (ok) {
+      load8<IN_BF16, OUT_F16>(a.x, j * a.x_tok_stride + (int64_t)h * 128 + 8 * c, x);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+    if (a.rms_w) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+      ss += __shfl_xor(ss, 1);
+      ss += __shfl_xor(ss, 2);
+      ss += __shfl_xor(ss, 4);
+      ss += __shfl_xor(ss, 8);
+      const float rs = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = x[e] * rs * a.rms_w[8 * c + e];
+    }
+    if (a.cos_t && ok) {
+      const f32x4 cs = *(const f32x4*)(a.cos_t + j * 64 + 4 * c);
+      const f32x4 sn = *(const f32x4*)(a.sin_t + j * 64 + 4 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = x[2 * e], x1 = x[2 * e + 1];
+        x[2 * e] = x0 * cs[e] - x1 * sn[e];
+        x[2 * e + 1] = x0 * sn[e] + x1 * cs[e];
+      }
+    }
+    if (!ok) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+    store8<OUT_F16>(tile, c * 512 + perm16(r) * 8, x);
+  }
+}
+
+// One workgroup per (64-key tile, head): the bf16 rows go through LDS as fp16 [key][dim], then
+// each thread writes four 16-byte pieces (8 keys of one dim) of the transposed tile.
+__global__ __launch_bounds__(256) void k_prep_vt64(const uint16_t* __restrict__ v, int64_t tok_stride, int64_t n,
+                                                   uint16_t* __restrict__ dst, int64_t dst_head_stride) {
+  __shared__ uint32_t sm[64][65];   // [key][dim pair]: fp16 pairs, rows padded to 65 words
   const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   {
     const int key = tid >> 2, d0 = (tid & 3) * 32;
@@ -141,17 +200,18 @@ __global__ __launch_bounds__(256) void k_prep_vt(const uint16_t* __restrict__ v,
     }
   }
   __syncthreads();
-  const int d = tid >> 1, k0 = (tid & 1) * 32;
-  uint16_t* out = dst + (int64_t)h * dst_head_stride + ((int64_t)t * 128 + d) * 64 + k0;
+  uint16_t* tile = dst + (int64_t)h * dst_head_stride + (int64_t)t * 8192;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int i = 0; i < 4; ++i) {
+    const int piece = tid + 256 * i;
+    const int kc = piece >> 7, d = piece & 127;
     uint32_t w[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t a = sm[k0 + 8 * c + 2 * e][d >> 1], b = sm[k0 + 8 * c + 2 * e + 1][d >> 1];
-      w[e] = (d & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+      const uint32_t lo = sm[8 * kc + 2 * e][d >> 1], hi = sm[8 * kc + 2 * e + 1][d >> 1];
+      w[e] = (d & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
     }
-    *(u32x4*)(out + 8 * c) = u32x4{w[0], w[1], w[2], w[3]};
+    *(u32x4*)(tile + kc * 1024 + d * 8) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -284,12 +344,12 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_prep_bf16_to_f16(const PrepArgs& a, hipStream_t s) {
-  PrepArgs k = a;
-  k.v = nullptr;   // V goes through the transposing kernel
-  hipError_t e = launch_prep<IN_BF16, OUT_F16>(k, s);
-  if (e != hipSuccess || !a.v || a.n_tok <= 0) return e;
+  if (a.n_tok <= 0) return hipSuccess;
   const dim3 grid((unsigned)((a.n_tok + 63) / 64), (unsigned)a.n_head);
-  hipLaunchKernelGGL(k_prep_vt, grid, dim3(256), 0, s, (const uint16_t*)a.v, a.x_tok_stride, a.n_tok,
+  hipLaunchKernelGGL(k_prep_k64, grid, dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !a.v) return e;
+  hipLaunchKernelGGL(k_prep_vt64, grid, dim3(256), 0, s, (const uint16_t*)a.v, a.x_tok_stride, a.n_tok,
                      (uint16_t*)a.dst_v, a.dst_head_stride);
   return hipGetLastError();
 }

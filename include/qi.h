@@ -83,11 +83,12 @@ typedef struct {
 /* Prefix KV cache ([OV] card 6A: stored at step 1, loaded at steps 2..N).  k and v are each
  * [n_layers][n_head][R][128] elements of `dtype`, device memory owned by the caller, with R =
  * p_cap for QI_F32 and p_cap rounded up to a multiple of 64 for QI_F16 (qi_kvcache_bytes gives
- * the size).  K rows are stored row-major after the optional QK-RMSNorm and the 3D rotation.
- * V is stored as given: row-major for QI_F32; for QI_F16 each head's V is transposed into R/64
- * tiles of [128 dims][64 keys] (tile t holds keys 64t .. 64t+63, key-minor; keys past the
- * stored count in the last tile are zero).  dtype must be QI_F16 for bf16 attention and QI_F32
- * for fp32 attention.  fp16 holds every bf16 V with
+ * the size).  K is stored after the optional QK-RMSNorm and the 3D rotation, V as given.
+ * QI_F32: both row-major.  QI_F16: each head's keys form R/64 tiles of 64 keys (16 KB each;
+ * keys past the stored count in the last tile are zero), laid out in the order the attention
+ * kernel's matrix-core operands read them: K as [16 dim chunks][64 key slots][8 dims], where
+ * slot p holds key p with rows 4-7 and 8-11 of every 16 exchanged; V as [8 key chunks][128
+ * dims][8 keys].  dtype must be QI_F16 for bf16 attention and QI_F32 for fp32 attention.  fp16 holds every bf16 V with
  * 2^-17 <= |v| < 65504 exactly (smaller values round to the fp16 subnormal grid, absolute
  * error <= 2^-25; larger ones overflow to infinity), and keeps rotated K with 3 more mantissa
  * bits than bf16 would. */

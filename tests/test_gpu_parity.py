@@ -154,7 +154,7 @@ def test_step1_parity_and_cache(name, dtype, qk):
     ref, (kc, vc) = O.step1(c.q.f64, c.k.f64, c.v.f64, wl.segments, c.cos, c.sin, c.qw, c.kw)
     check_close(to_np(o), ref, wl.dtype, f"{name} step1 O")
     if c.P > 0:
-        kd = to_np(cache.k[1, :, :c.P].permute(1, 0, 2))
+        kd = to_np(cache.k_rows(1)[:, :c.P].permute(1, 0, 2))
         vd = to_np(cache.v_rows(1)[:, :c.P].permute(1, 0, 2))
         tolk = 2.0 ** -11 if wl.dtype == "bf16" else 1e-6     # fp16 / fp32 storage of rotated K
         assert np.all(np.abs(kd - kc) <= tolk * np.abs(kc) + 1e-6), "cached K"
@@ -177,8 +177,9 @@ def test_prefix_store_bytes_match_step1_store(name):
     att.full(c.qd, c.kd, c.vd, c.qw_d, c.kw_d, cache=c1)
     att.store(c.kd[:c.P], c.vd[:c.P], c2, 0, c.kw_d)
     torch.cuda.synchronize()
-    assert torch.equal(c1.k[:, :, :c.P].view(torch.int16), c2.k[:, :, :c.P].view(torch.int16))
-    assert torch.equal(c1.v.view(torch.int16), c2.v.view(torch.int16))   # whole tiles incl. zero padding
+    # whole tiles, including the zeros of the last tile's missing keys
+    assert torch.equal(c1.k.view(torch.int16), c2.k.view(torch.int16))
+    assert torch.equal(c1.v.view(torch.int16), c2.v.view(torch.int16))
 
 
 def test_prefix_bit_identical_under_target_perturbation():
@@ -330,6 +331,6 @@ def test_full_size_step1_sampled(name):
     check_close(to_np(o[rows]), ref, "bf16", f"{name} step-1 rows")
     # cache contents at sampled prefix rows
     pr = sample_rows(0, c.P, 64, 3)
-    kd = to_np(cache.k[0][:, pr].permute(1, 0, 2))
+    kd = to_np(cache.k_rows(0)[:, pr].permute(1, 0, 2))
     assert np.all(np.abs(kd - kr[pr]) <= 2.0 ** -11 * np.abs(kr[pr]) + 1e-6)
     check_cached_v(to_np(cache.v_rows(0)[:, pr].permute(1, 0, 2)), c.v.f64[pr], "bf16")
