@@ -135,83 +135,104 @@ __device__ __forceinline__ int perm16(int p) {
   return (p & ~15) | ((grp == 1 ? 2 : (grp == 2 ? 1 : grp)) << 2) | (p & 3);
 }
 
-// One workgroup per (64-key tile, head); 16 threads per key row (8 dims each), four rows each.
-__global__ __launch_bounds__(256) void k_prep_k64(PrepArgs a) {
-  const int t = blockIdx.x, h = blockIdx.y;
-  const int rr = threadIdx.x >> 4, c = threadIdx.x & 15;
-  uint16_t* tile = (uint16_t*)a.dst + (int64_t)h * a.dst_head_stride + (int64_t)t * 8192;
+// One workgroup per (64-key tile, head).  K: 16 threads per key row (8 dims each, four rows per
+// thread) normalise and rotate, and put each row's fp16 chunks at their tile positions in LDS
+// (chunk rows padded by 16 bytes, so the 16 chunks of one key land in distinct banks); V: the bf16
+// rows go through LDS as fp16 [key][dim].  Both tiles then leave as whole 1 KB runs: every global
+// read is a run of 256 bytes of one token's row and every write 16 contiguous bytes per lane.
+template <bool WITH_V>
+__global__ __launch_bounds__(256) void k_prep_kv64(PrepArgs a) {
+  constexpr int KROW = 64 * 16 + 16;           // bytes per dim chunk of the staged K tile (padded)
+  __shared__ __attribute__((aligned(16))) char kt[16 * KROW];
+  __shared__ uint32_t vt[WITH_V ? 64 : 1][65];  // [key][dim pair]: fp16 pairs, rows padded to 65 words
+  const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int rr = tid >> 4, c = tid & 15;
+  // V rows first (their loads overlap the K arithmetic)
+  u32x4 vw[4];
+  if (WITH_V) {
+    const int key = tid >> 2, d0 = (tid & 3) * 32;
+    const int64_t j = (int64_t)t * 64 + key;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      vw[i] = j < a.n_tok ? *(const u32x4*)((const uint16_t*)a.v + j * a.x_tok_stride + (int64_t)h * 128 + d0 + 8 * i)
+                          : u32x4{0u, 0u, 0u, 0u};
+  }
+  float x[4][8];
+#pragma unroll
+  for (int quarter = 0; quarter < 4; ++quarter) {
+    const int64_t j = (int64_t)t * 64 + rr + 16 * quarter;
+    if (j < a.n_tok) {
+      load8<IN_BF16, OUT_F16>(a.x, j * a.x_tok_stride + (int64_t)h * 128 + 8 * c, x[quarter]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[quarter][e] = 0.f;
+    }
+  }
 #pragma unroll
   for (int quarter = 0; quarter < 4; ++quarter) {
     const int r = rr + 16 * quarter;
     const int64_t j = (int64_t)t * 64 + r;
     const bool ok = j < a.n_tok;
-    float x[8];
-    if (ok) {
-      load8<IN_BF16, OUT_F16>(a.x, j * a.x_tok_stride + (int64_t)h * 128 + 8 * c, x);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
-    }
+    float* xq = x[quarter];
     if (a.rms_w) {
       float ss = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+      for (int e = 0; e < 8; ++e) ss += xq[e] * xq[e];
       ss += __shfl_xor(ss, 1);
       ss += __shfl_xor(ss, 2);
       ss += __shfl_xor(ss, 4);
       ss += __shfl_xor(ss, 8);
       const float rs = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = x[e] * rs * a.rms_w[8 * c + e];
+      for (int e = 0; e < 8; ++e) xq[e] = xq[e] * rs * a.rms_w[8 * c + e];
     }
     if (a.cos_t && ok) {
       const f32x4 cs = *(const f32x4*)(a.cos_t + j * 64 + 4 * c);
       const f32x4 sn = *(const f32x4*)(a.sin_t + j * 64 + 4 * c);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float x0 = x[2 * e], x1 = x[2 * e + 1];
-        x[2 * e] = x0 * cs[e] - x1 * sn[e];
-        x[2 * e + 1] = x0 * sn[e] + x1 * cs[e];
+        const float x0 = xq[2 * e], x1 = xq[2 * e + 1];
+        xq[2 * e] = x0 * cs[e] - x1 * sn[e];
+        xq[2 * e + 1] = x0 * sn[e] + x1 * cs[e];
       }
     }
     if (!ok) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      for (int e = 0; e < 8; ++e) xq[e] = 0.f;
     }
-    store8<OUT_F16>(tile, c * 512 + perm16(r) * 8, x);
+    *(u32x4*)(kt + c * KROW + perm16(r) * 16) =
+        u32x4{pack_f16(xq[0], xq[1]), pack_f16(xq[2], xq[3]), pack_f16(xq[4], xq[5]), pack_f16(xq[6], xq[7])};
   }
-}
-
-// One workgroup per (64-key tile, head): the bf16 rows go through LDS as fp16 [key][dim], then
-// each thread writes four 16-byte pieces (8 keys of one dim) of the transposed tile.
-__global__ __launch_bounds__(256) void k_prep_vt64(const uint16_t* __restrict__ v, int64_t tok_stride, int64_t n,
-                                                   uint16_t* __restrict__ dst, int64_t dst_head_stride) {
-  __shared__ uint32_t sm[64][65];   // [key][dim pair]: fp16 pairs, rows padded to 65 words
-  const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  {
+  if (WITH_V) {
     const int key = tid >> 2, d0 = (tid & 3) * 32;
-    const int64_t j = (int64_t)t * 64 + key;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (j < n) w = *(const u32x4*)(v + j * tok_stride + (int64_t)h * 128 + d0 + 8 * c);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm[key][(d0 + 8 * c) / 2 + e] = pack_f16(bf16_lo(w[e]), bf16_hi(w[e]));
-    }
+      for (int e = 0; e < 4; ++e) vt[key][(d0 + 8 * i) / 2 + e] = pack_f16(bf16_lo(vw[i][e]), bf16_hi(vw[i][e]));
   }
   __syncthreads();
-  uint16_t* tile = dst + (int64_t)h * dst_head_stride + (int64_t)t * 8192;
+  // K tile out: piece p (16 bytes) = chunk p / 64, slot p % 64
+  uint16_t* ktile = (uint16_t*)a.dst + (int64_t)h * a.dst_head_stride + (int64_t)t * 8192;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int piece = tid + 256 * i;
-    const int kc = piece >> 7, d = piece & 127;
-    uint32_t w[4];
+    *(u32x4*)(ktile + piece * 8) = *(const u32x4*)(kt + (piece >> 6) * KROW + (piece & 63) * 16);
+  }
+  if (WITH_V) {
+    // V tile out: piece p = key chunk p / 128, dim p % 128 (8 keys of that dim)
+    uint16_t* vtile = (uint16_t*)a.dst_v + (int64_t)h * a.dst_head_stride + (int64_t)t * 8192;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = sm[8 * kc + 2 * e][d >> 1], hi = sm[8 * kc + 2 * e + 1][d >> 1];
-      w[e] = (d & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+    for (int i = 0; i < 4; ++i) {
+      const int piece = tid + 256 * i;
+      const int kc = piece >> 7, d = piece & 127;
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = vt[8 * kc + 2 * e][d >> 1], hi = vt[8 * kc + 2 * e + 1][d >> 1];
+        w[e] = (d & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+      }
+      *(u32x4*)(vtile + kc * 1024 + d * 8) = u32x4{w[0], w[1], w[2], w[3]};
     }
-    *(u32x4*)(tile + kc * 1024 + d * 8) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -346,11 +367,10 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
 hipError_t launch_prep_bf16_to_f16(const PrepArgs& a, hipStream_t s) {
   if (a.n_tok <= 0) return hipSuccess;
   const dim3 grid((unsigned)((a.n_tok + 63) / 64), (unsigned)a.n_head);
-  hipLaunchKernelGGL(k_prep_k64, grid, dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !a.v) return e;
-  hipLaunchKernelGGL(k_prep_vt64, grid, dim3(256), 0, s, (const uint16_t*)a.v, a.x_tok_stride, a.n_tok,
-                     (uint16_t*)a.dst_v, a.dst_head_stride);
+  if (a.v)
+    hipLaunchKernelGGL(k_prep_kv64<true>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_prep_kv64<false>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_prep_bf16_to_bf16(const PrepArgs& a, hipStream_t s) { return launch_prep<IN_BF16, OUT_BF16>(a, s); }
