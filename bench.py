@@ -61,6 +61,12 @@ def traffic_from_profile():
     return float(m_b.group(1))
 
 
+def pct(sorted_vals, q):
+    """q-th percentile (nearest rank) of an ascending list."""
+    i = min(len(sorted_vals) - 1, max(0, int(round(q / 100.0 * (len(sorted_vals) - 1)))))
+    return sorted_vals[i]
+
+
 def visible_pairs_per_head(segments) -> int:
     """Visible (query, key) pairs of step 1: query q sees keys 0..lim(q) (Block-Causal rows)."""
     total, start = 0, 0
@@ -253,6 +259,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms, n_launch = Q.qi_kernel_timing_read()
+    per_call = sorted(Q.qi_kernel_timing_read_each())
     Q.qi_kernel_timing(False)
     log(f"timed {args.steps} steps in {wall:.3f} s; attention kernel {kern_ms / max(n_launch, 1):.4f} ms/launch")
 
@@ -303,7 +310,11 @@ def main():
                      "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic_from_profile(),
                      "kernel": "k_attn_f16<false> + k_combine (one attention call)" if n_chunks > 1 else "k_attn_f16<false>",
                      "key_chunks": n_chunks, "kernel_ms_per_launch": round(avg_ms, 4),
-                     "flops_per_launch": flops_launch, "launches": n_launch},
+                     "flops_per_launch": flops_launch, "launches": n_launch,
+                     # per-call duration percentiles (p95/p99: the slow tail) and the TFLOP/s at each
+                     "per_call_ms": {q: round(pct(per_call, int(q[1:])), 4) for q in ("p50", "p95", "p99")},
+                     "per_call_tflops": {q: round(flops_launch / (pct(per_call, int(q[1:])) * 1e-3) / 1e12, 1)
+                                         for q in ("p50", "p95", "p99")}},
     }
     res["config"].update(extra)
     if not args.no_cpu:

@@ -454,4 +454,18 @@ int qi_kernel_timing_read(double* total_ms, int64_t* n_launches) {
   return QI_OK;
 }
 
+int qi_kernel_timing_read_each(float* ms, int64_t cap, int64_t* n) {
+  if (!n || cap < 0 || (cap > 0 && !ms)) return QI_ERR_ARG;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  for (size_t i = 0; i < g_used; ++i) {
+    if (hipEventSynchronize(g_ev[2 * i + 1]) != hipSuccess) return QI_ERR_HIP;
+    if ((int64_t)i >= cap) continue;
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, g_ev[2 * i], g_ev[2 * i + 1]) != hipSuccess) return QI_ERR_HIP;
+    ms[i] = t;
+  }
+  *n = (int64_t)g_used;
+  return QI_OK;
+}
+
 }  // extern "C"

@@ -97,6 +97,7 @@ _SIGS = {
     "qi_cast_bf16": (c_int, [c_void_p, c_void_p, c_int64, c_void_p]),
     "qi_kernel_timing": (c_int, [c_int]),
     "qi_kernel_timing_read": (c_int, [POINTER(c_double), POINTER(c_int64)]),
+    "qi_kernel_timing_read_each": (c_int, [POINTER(c_float), c_int64, POINTER(c_int64)]),
 }
 
 _lib = None
@@ -294,3 +295,12 @@ def qi_kernel_timing_read():
     ms, n = c_double(), c_int64()
     check(lib().qi_kernel_timing_read(ctypes.byref(ms), ctypes.byref(n)), "qi_kernel_timing_read")
     return ms.value, n.value
+
+
+def qi_kernel_timing_read_each():
+    """Per-call elapsed milliseconds of the recorded attention calls, in launch order."""
+    n = c_int64()
+    check(lib().qi_kernel_timing_read_each(None, 0, ctypes.byref(n)), "qi_kernel_timing_read_each")
+    buf = (c_float * max(n.value, 1))()
+    check(lib().qi_kernel_timing_read_each(buf, n.value, ctypes.byref(n)), "qi_kernel_timing_read_each")
+    return [buf[i] for i in range(n.value)]

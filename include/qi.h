@@ -287,6 +287,11 @@ int qi_kernel_timing(int enable);
  * (waits for the recorded events to complete). */
 int qi_kernel_timing_read(double* total_ms, int64_t* n_launches);
 
+/* Elapsed milliseconds of each recorded attention call, in launch order: writes min(cap, n)
+ * values to ms (host memory, caller-owned) and the number recorded to *n (waits for the
+ * recorded events to complete).  ms may be NULL when cap is 0. */
+int qi_kernel_timing_read_each(float* ms, int64_t cap, int64_t* n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,6 +10,8 @@ GPU, repeated runs, the prefix-store bytes of the two store paths, V in the cach
 import math
 import sys
 
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -206,6 +208,24 @@ def test_repeat_runs_bit_identical():
     outs = [att.full(c.qd, c.kd, c.vd, c.qw_d, c.kw_d).clone() for _ in range(3)]
     torch.cuda.synchronize()
     assert all(torch.equal(outs[0].view(torch.int16), x.view(torch.int16)) for x in outs[1:])
+
+
+def test_kernel_timing_hooks_record_each_call():
+    wl = qin.WORKLOADS["cfg1"]
+    c = Case(wl)
+    L, att = make(wl)
+    att.full(c.qd, c.kd, c.vd, c.qw_d, c.kw_d)
+    torch.cuda.synchronize()
+    Q.qi_kernel_timing(True)
+    for _ in range(3):
+        att.full(c.qd, c.kd, c.vd, c.qw_d, c.kw_d)
+    each = Q.qi_kernel_timing_read_each()
+    total, n = Q.qi_kernel_timing_read()
+    Q.qi_kernel_timing(False)
+    assert n == 3 and len(each) == 3 and all(t > 0 for t in each)
+    assert abs(sum(each) - total) <= 1e-3 * total + 1e-6
+    # a negative capacity is rejected before anything is read
+    assert Q.lib().qi_kernel_timing_read_each(None, -1, ctypes.byref(ctypes.c_int64())) == Q.QI_ERR_ARG
 
 
 # ---------------------------------------------------------------------------------------------
