@@ -147,8 +147,15 @@ void set_partials(AttnArgs& a, char* base, int64_t n_q, int64_t T, int32_t n_hea
   a.n_split = 1;
   a.part_o = nullptr;
   a.part_ml = nullptr;
+  a.xcd_units = 0;
+  a.xcd_whole = 0;
   if (dtype != QI_BF16) return;
-  a.n_split = attn_f16_splits(T, n_head);
+  const AttnSched sc = attn_f16_schedule(T, n_head);
+  a.n_split = sc.n_split;
+  if (n_q == T) {   // the XCD schedule covers the target's query tiles only
+    a.xcd_units = sc.xcd_units;
+    a.xcd_whole = sc.xcd_whole;
+  }
   a.part_o = (float*)base;
   a.part_ml = (float*)(base + (int64_t)a.n_split * n_q * n_head * QI_HEAD_DIM * (int64_t)sizeof(float));
 }
@@ -171,6 +178,9 @@ int run_attn_step1_f16(const AttnArgs& a, int64_t P, int64_t T, char* part_base,
   ap.n_split = 1;
   ap.part_o = nullptr;
   ap.part_ml = nullptr;
+  ap.xcd_units = 0;
+  ap.reverse_qt = 1;   // prefix rows: longest rows first
+  // the target rows keep the order and schedule of a cached step (the same bits)
   AttnArgs at = a;
   at.q = (const char*)a.q + P * a.q_stride * 2;
   at.o = (char*)a.o + P * a.o_stride * 2;
@@ -180,6 +190,7 @@ int run_attn_step1_f16(const AttnArgs& a, int64_t P, int64_t T, char* part_base,
   }
   at.n_q = (int32_t)T;
   at.q_row0 = a.q_row0 + P;
+  at.reverse_qt = 0;
   set_partials(at, part_base, T, T, a.n_head, QI_BF16);
   if (P > 0) {
     const hipError_t e = launch_attn_f16(ap, s);

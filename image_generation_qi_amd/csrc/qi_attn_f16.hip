@@ -36,8 +36,10 @@
 //     interleave.
 //   - the Block-Causal mask is applied per tile from the row limits (see qi_common.h): tiles
 //     with no visible pair are never loaded, tiles with all pairs visible run unmasked.
-//   - key chunks (n_split > 1) balance the grid over the CUs: each chunk of a query tile's key
+//   - grids under four rounds are balanced over the CUs with key chunks: a chunk of a unit's key
 //     tiles writes an unnormalised partial output with its (max, sum), merged by k_combine.
+//     Where the units split evenly over the 8 XCDs, each XCD runs its first units whole (one
+//     per CU) and cuts only the rest into chunks, so few rows pay for the partials.
 //   - blockIdx is remapped so that the 8 XCDs (each with its own L2) get contiguous runs of
 //     workgroups of the same head, which then share that head's K/V in L2.
 #include <hip/hip_runtime.h>
@@ -96,12 +98,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_B];
 
   const int n_qt = (a.n_q + BM - 1) / BM;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int split = logical % a.n_split;
-  const int rest = logical / a.n_split;
-  const int h = rest / n_qt;
-  int qt = rest - h * n_qt;
-  if (MASKED) qt = n_qt - 1 - qt;  // longest rows first
+  // which unit (query tile x head) and which key chunk of it (of nsp) this workgroup runs
+  int unit, split, nsp;
+  if (a.xcd_units > 0) {
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    if (j < a.xcd_whole) {
+      unit = x * a.xcd_units + j;
+      split = 0;
+      nsp = 1;
+    } else {
+      const int t = j - a.xcd_whole;
+      unit = x * a.xcd_units + a.xcd_whole + t / a.n_split;
+      split = t % a.n_split;
+      nsp = a.n_split;
+    }
+  } else {
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    split = logical % a.n_split;
+    unit = logical / a.n_split;
+    nsp = a.n_split;
+  }
+  const int h = unit / n_qt;
+  int qt = unit - h * n_qt;
+  if (MASKED && a.reverse_qt) qt = n_qt - 1 - qt;  // longest rows first
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -181,8 +200,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int kt_end = lim_last < nA ? lim_last / BN + 1 : ntA + (lim_last - nA) / BN + 1;
   const int kt_full = (lim_first + 1 < nA || (nA % BN) != 0) ? (lim_first + 1 < nA ? lim_first + 1 : nA) / BN
                                                             : ntA + (lim_first + 1 - nA) / BN;
-  const int t_begin = split * a.split_tiles;  // this workgroup's chunk of key tiles
-  const int t_stop = (t_begin + a.split_tiles < kt_end) ? t_begin + a.split_tiles : kt_end;
+  // this workgroup's chunk of key tiles (all of them for a whole unit)
+  const int t_begin = nsp == 1 ? 0 : split * a.split_tiles;
+  const int t_stop = (nsp == 1 || t_begin + a.split_tiles > kt_end) ? kt_end : t_begin + a.split_tiles;
   if (t_begin >= t_stop) {  // the chunk holds no visible key for any row of the tile
     if (qok) {
       const int64_t row = ((int64_t)split * a.n_q + qrow) * a.n_head + h;
@@ -459,7 +479,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // ---- epilogue: normalise and store bf16, or store the chunk's partial ---------------------
   const float lt = pair_sum(l_run);
   if (qok) {
-    if (a.n_split == 1) {
+    if (nsp == 1) {
       const float inv = 1.0f / lt;
       uint16_t* op = (uint16_t*)a.o + (int64_t)qrow * a.o_stride + h * HD + 4 * g;
 #pragma unroll
@@ -486,15 +506,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// Merge of the key chunks: for each (row, head), O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
-// with M = max_s m_s, rounded to bf16.  16 threads per (row, head), 8 dims each.
+// Merge of the key chunks: for each (row, head) of a chunked unit, O = sum_s 2^(m_s - M) O_s /
+// sum_s 2^(m_s - M) l_s with M = max_s m_s, rounded to bf16.  16 threads per (row, head), 8 dims
+// each.  With an XCD schedule only the chunked units (the last xcd_units - xcd_whole units of
+// each of the 8 runs) are merged; otherwise every (row, head).
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                                  uint16_t* __restrict__ o, int64_t o_stride, int n_q, int n_head,
-                                                 int n_split) {
+                                                 int n_split, int xcd_units, int xcd_whole) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t rh = gid >> 4;
-  if (rh >= (int64_t)n_q * n_head) return;
   const int d0 = (int)(gid & 15) * 8;
+  int64_t rh;
+  if (xcd_units > 0) {
+    const int per_run = xcd_units - xcd_whole;
+    const int64_t k = gid >> 4;                     // (chunked unit, row in its tile)
+    const int tu = (int)(k / BM), rr = (int)(k % BM);
+    if (tu >= 8 * per_run) return;
+    const int unit = (tu / per_run) * xcd_units + xcd_whole + tu % per_run;
+    const int n_qt = (n_q + BM - 1) / BM;
+    const int h = unit / n_qt, qt = unit - h * n_qt;
+    const int row = qt * BM + rr;
+    if (row >= n_q) return;
+    rh = (int64_t)row * n_head + h;
+  } else {
+    rh = gid >> 4;
+    if (rh >= (int64_t)n_q * n_head) return;
+  }
   const int64_t stride = (int64_t)n_q * n_head;   // rows per split
   float M = -INFINITY;
   for (int s = 0; s < n_split; ++s) M = fmaxf(M, part_ml[2 * (s * stride + rh)]);
@@ -524,28 +560,50 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_
 
 }  // namespace
 
-int attn_f16_splits(int64_t T, int32_t n_head) {
-  // One workgroup fills a CU, so a launch runs in rounds of 256 workgroups.  Grids of four or
-  // more rounds stay whole.  Smaller ones are cut into s key chunks, s = 1 .. 8, chosen for the
-  // fullest last round, each chunk beyond the first charged 1 % and any chunking 3 % for the
-  // partial outputs and their merge: the 4096-token target at 24 heads (384 query tiles) runs
-  // as two chunks in three full rounds instead of one and a half.
-  constexpr int64_t slots = 256;
+AttnSched attn_f16_schedule(int64_t T, int32_t n_head) {
+  // One workgroup fills a CU; the 256 CUs are 8 XCDs of 32.  Grids of four or more rounds stay
+  // whole.  Smaller grids whose units split evenly over the 8 XCDs get the XCD schedule: each
+  // XCD runs whole rounds of whole units (one per CU) and cuts only its remaining units into s
+  // key chunks, s = 1 .. 8 chosen for the shortest tail (each chunk beyond the first charged 1 %
+  // of a unit, chunking at all 3 %).  The 4,096-token target at 24 heads (384 units, 48 per XCD)
+  // runs 32 whole units and 16 units in 2 chunks per XCD: every CU does one whole unit and one
+  // half.  Other small grids cut every unit into the s chunks that best fill the last round.
+  constexpr int64_t slots = 256, per_xcd = 32;
+  AttnSched r{1, 0, 0};
   const int64_t units = (T + BM - 1) / BM * n_head;
-  if (units >= 4 * slots || units <= 0) return 1;
+  if (units >= 4 * slots || units <= 0) return r;
+  auto chunk_cost = [](int s) { return 0.01 * s + (s > 1 ? 0.03 : 0.0); };
+  if (units % 8 == 0) {
+    const int64_t ux = units / 8, wx = per_xcd * (ux / per_xcd), rem = ux - wx;
+    if (rem == 0) return r;
+    int best = 1;
+    double best_t = 1e30;
+    for (int s = 1; s <= 8; ++s) {
+      const double t = (double)((rem * s + per_xcd - 1) / per_xcd) / s + chunk_cost(s);
+      if (t < best_t - 1e-9) {
+        best_t = t;
+        best = s;
+      }
+    }
+    if (best == 1) return r;
+    return AttnSched{best, (int32_t)ux, (int32_t)wx};
+  }
   int best = 1;
   double best_score = -1.0;
   for (int s = 1; s <= 8; ++s) {
     const int64_t blocks = units * s;
     const double eff = (double)blocks / (double)(slots * ((blocks + slots - 1) / slots));
-    const double score = eff - (s > 1 ? 0.03 : 0.0) - 0.01 * s;
+    const double score = eff - chunk_cost(s);
     if (score > best_score + 1e-9) {
       best_score = score;
       best = s;
     }
   }
-  return best;
+  r.n_split = best;
+  return r;
 }
+
+int attn_f16_splits(int64_t T, int32_t n_head) { return attn_f16_schedule(T, n_head).n_split; }
 
 int64_t attn_f16_partial_bytes(int64_t n_q, int32_t n_head) {
   return (int64_t)n_q * n_head * (HD + 2) * (int64_t)sizeof(float);
@@ -558,7 +616,9 @@ hipError_t launch_attn_f16(const AttnArgs& a_in, hipStream_t s) {
   if (a.n_split < 1) a.n_split = 1;
   a.split_tiles = (int)((kt_total + a.n_split - 1) / a.n_split);
   if (a.split_tiles < 1) a.split_tiles = 1;
-  const int64_t blocks = n_qt * a.n_head * a.n_split;
+  if (a.xcd_units > 0 && (int64_t)8 * a.xcd_units != n_qt * a.n_head) return hipErrorInvalidValue;
+  const int64_t blocks = a.xcd_units > 0 ? 8 * (int64_t)(a.xcd_whole + (a.xcd_units - a.xcd_whole) * a.n_split)
+                                         : n_qt * a.n_head * a.n_split;
   if (blocks <= 0) return hipSuccess;
   if (a.masked)
     hipLaunchKernelGGL(k_attn_f16<true>, dim3((unsigned)blocks), dim3(2 * BM), 0, s, a);
@@ -566,9 +626,10 @@ hipError_t launch_attn_f16(const AttnArgs& a_in, hipStream_t s) {
     hipLaunchKernelGGL(k_attn_f16<false>, dim3((unsigned)blocks), dim3(2 * BM), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  const int64_t threads = (int64_t)a.n_q * a.n_head * 16;
+  const int64_t threads = a.xcd_units > 0 ? (int64_t)8 * (a.xcd_units - a.xcd_whole) * BM * 16
+                                          : (int64_t)a.n_q * a.n_head * 16;
   hipLaunchKernelGGL(k_combine, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a.part_o, a.part_ml,
-                     (uint16_t*)a.o, a.o_stride, a.n_q, a.n_head, a.n_split);
+                     (uint16_t*)a.o, a.o_stride, a.n_q, a.n_head, a.n_split, a.xcd_units, a.xcd_whole);
   return hipGetLastError();
 }
 

@@ -70,8 +70,21 @@ struct AttnArgs {
   int32_t n_split, split_tiles;
   float* part_o;       // [n_split][n_q][n_head][128]
   float* part_ml;      // [n_split][n_q][n_head][2]
+  // Work schedule of the fp16 path.  xcd_units > 0: the grid is read as 8 interleaved runs (run
+  // x = the blocks with blockIdx % 8 == x, which the hardware places on XCD x) of xcd_units
+  // query-tile units each (unit u = head * n_qt + query tile); the first xcd_whole units of a
+  // run are single workgroups over all their key tiles, each later unit is cut into n_split
+  // key chunks (one workgroup each).  xcd_units == 0: every unit is cut into n_split chunks.
+  int32_t xcd_units, xcd_whole;
+  int32_t reverse_qt;  // masked kernel: visit a head's query tiles last-first (longest rows first)
   SegTable segs;
 };
+
+// The fp16 path's schedule for a target of T tokens and n_head heads (see AttnArgs).
+struct AttnSched {
+  int32_t n_split, xcd_units, xcd_whole;
+};
+AttnSched attn_f16_schedule(int64_t T, int32_t n_head);
 
 // Query rows per workgroup of the fp16 path (the tile height reported by qi_attn_tile_shape).
 constexpr int kAttnF16TileQ = 256;

@@ -120,15 +120,15 @@ def test_tile_shape_and_sizes():
     assert Q.qi_attn_tile_shape(Q.QI_BF16) == (256, 64)
     assert Q.qi_attn_tile_shape(Q.QI_F32) == (1, 64)
     L3 = Q.make_layout(qin.WORKLOADS["cfg3"].segments)
-    # 4096-token target: 16 x 24 = 384 query tiles, one per CU -> 2 key chunks (768 workgroups,
-    # three full rounds): K/V fp16 rows plus 2 chunks of fp32 partials (128 values + max + sum)
+    # 4096-token target: 16 x 24 = 384 query tiles (48 per XCD): per XCD 32 whole, 16 in 2 key
+    # chunks: K/V fp16 rows plus 2 chunks of fp32 partials (128 values + max + sum)
     # (step 1 chunks only the target rows; the prefix rows run whole)
     assert Q.qi_attn_full_workspace_bytes(L3, Q.QI_BF16, 24) == 2 * 24 * 21504 * 128 * 2 + 2 * 4096 * 24 * 130 * 4
     assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, 4096, 24) == 2 * 24 * 4096 * 128 * 2 + 2 * 4096 * 24 * 130 * 4
-    # config[1]: 4 x 24 = 96 units -> 8 key chunks (768 workgroups)
+    # config[1]: 4 x 24 = 96 units (12 per XCD, none whole) -> 5 key chunks
     L1 = Q.make_layout(qin.WORKLOADS["cfg1"].segments)
-    assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, 1024, 24) == 2 * 24 * 1024 * 128 * 2 + 8 * 1024 * 24 * 130 * 4
-    assert Q.qi_attn_full_workspace_bytes(L1, Q.QI_BF16, 24) == 2 * 24 * 2304 * 128 * 2 + 8 * 1024 * 24 * 130 * 4
+    assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, 1024, 24) == 2 * 24 * 1024 * 128 * 2 + 5 * 1024 * 24 * 130 * 4
+    assert Q.qi_attn_full_workspace_bytes(L1, Q.QI_BF16, 24) == 2 * 24 * 2304 * 128 * 2 + 5 * 1024 * 24 * 130 * 4
     # long targets stay whole: 16384 tokens x 24 heads = 1536 query tiles (six rounds)
     assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, 16384, 24) == 2 * 24 * 16384 * 128 * 2
     # workspace rows are padded to whole 64-key tiles for both dtypes
