@@ -9,7 +9,8 @@ out from the pages, in NumPy float64, slow and obvious on purpose.
 Sources (cited by page title and section):
   [OV]   "Qwen-Image-2.1: how an image is made from noise" course overview
          (OpenArchLab), lesson list and block cards 1A, 2A, 3A, 3B, 3C, 4A, 5A, 6A, 6B.
-  [1B]   "1B - Qwen3-VL Context & Zero-Center RMSNorm" (OpenArchLab), sections 1-4.
+  [1B]   "1B - Qwen3-VL Context & Zero-Center RMSNorm" (OpenArchLab), sections 1-4
+         (ZeroCenterRMSNorm; the context TextProjection Linear -> GELU(tanh) -> Linear).
   [3A]   "3A - 3D Axial RoPE (16, 56, 56) & Zero-Centered Grid" (OpenArchLab), sections 1-4.
   [EDIT] "QwenImageTransformer2DModel source reading (Qwen-Image-Edit)", sections
          5.1 (timestep embedding), 5.2 (modulation), 6 (attention processor),
@@ -362,6 +363,20 @@ def per_row(vec_prefix, vec_target, n_rows: int, row0: int, P: int):
     current step's ([OV] card 3B: prefix at t = 0, target at t)."""
     rows = np.arange(row0, row0 + n_rows)
     return np.where((rows < P)[:, None], np.asarray(vec_prefix)[None, :], np.asarray(vec_target)[None, :])
+
+
+def gelu_tanh(x):
+    """GELU in its tanh form, 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))): the activation
+    the TextProjection of [1B] sections 1-3 names GELU(tanh)."""
+    x = np.asarray(x, np.float64)
+    return 0.5 * x * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+def text_projection(x_ctx, w_norm, w1, w2, eps: float = 1e-6):
+    """The context path of [1B] sections 1-3: ZeroCenterRMSNorm, Linear, GELU(tanh), Linear
+    (no biases: random-init weights; widths D -> D -> D)."""
+    h = zero_center_rms_norm(np.asarray(x_ctx, np.float64), w_norm, eps)
+    return linear(gelu_tanh(linear(h, w1)), w2)
 
 
 def swiglu(g, u):

@@ -173,6 +173,8 @@ def sigmas(n_steps: int) -> np.ndarray:
 W_NORM1, W_NORM2, W_QNORM, W_KNORM, W_QKV, W_OUT, W_GATE, W_UP, W_DOWN = range(9)
 # shared (layer 0): timestep MLP, modulation, head scale, velocity head, img_in, prefix inputs
 W_T1, W_T2, W_MOD, W_HSCALE, W_HEAD, W_IN, X_TEXT, LAT_REF, LAT_TGT = range(20, 29)
+# context TextProjection (ZeroCenterRMSNorm weight, two Linears) and its synthetic VLM context
+W_TPN, W_TP1, W_TP2, X_CTX = range(29, 33)
 
 
 def linear_weight(cfg_id: int, index: int, n_out: int, n_in: int, layer: int = 0) -> Stored:
@@ -212,6 +214,22 @@ def shared_weights(cfg_id: int, D: int, t_dim: int = 256, latent_ch: int = 64) -
         "w_head": linear_weight(cfg_id, W_HEAD, latent_ch, D),
         "w_in": linear_weight(cfg_id, W_IN, D, latent_ch),
     }
+
+
+def text_projection_weights(cfg_id: int, D: int) -> dict:
+    """Random-init context TextProjection: ZeroCenterRMSNorm weight N(0, 0.02^2) (stored as
+    scale - 1, fp32) and two Linear weights [D][D] ~ N(0, 1/D) in bf16."""
+    return {
+        "tp_norm": f32_vector(cfg_id, W_TPN, (D,), 0, 0.0, 0.02),
+        "tp_w1": linear_weight(cfg_id, W_TP1, D, D),
+        "tp_w2": linear_weight(cfg_id, W_TP2, D, D),
+    }
+
+
+def context_inputs(cfg_id: int, n_ctx: int, D: int) -> np.ndarray:
+    """Synthetic vision-language context rows [n_ctx][D] (fp32, N(0,1)): the stand-in for the
+    Qwen3-VL hidden states that the TextProjection maps into the DiT's text rows."""
+    return f32_vector(cfg_id, X_CTX, (n_ctx, D))
 
 
 def prefix_inputs(cfg_id: int, n_text: int, n_ref: int, D: int, latent_ch: int = 64):

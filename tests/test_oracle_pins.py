@@ -572,3 +572,42 @@ def test_prefix_states_follow_segment_order():
     xt = np.array([[1.0], [2.0], [3.0]])
     rt = np.array([[10.0], [11.0], [12.0]])
     assert O.prefix_states(segs, xt, rt)[:, 0].tolist() == [1, 2, 10, 11, 3, 12]
+
+
+# ------------------------------------------------------------------------------------------------
+# context TextProjection ([1B] sections 1-3): ZeroCenterRMSNorm -> Linear -> GELU(tanh) -> Linear
+# ------------------------------------------------------------------------------------------------
+
+def test_gelu_tanh_pins():
+    from scipy.special import erf
+    x = np.linspace(-8.0, 8.0, 20001)
+    g = O.gelu_tanh(x)
+    # the tanh form's odd part is exactly x/2: g(x) - g(-x) = x
+    assert np.max(np.abs(g - O.gelu_tanh(-x) - x)) <= 1e-14 * np.max(np.abs(x))
+    # it approximates the exact GELU x * Phi(x) to within 5e-4 over the whole line (a wrong
+    # constant, e.g. 0.04 or 0.05 for 0.044715, or 1/sqrt(pi) for sqrt(2/pi), misses by > 2.8e-3)
+    exact = 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+    assert np.max(np.abs(g - exact)) < 5e-4
+    assert O.gelu_tanh(0.0) == 0.0
+    assert abs(O.gelu_tanh(10.0) - 10.0) < 1e-12 and abs(O.gelu_tanh(-10.0)) < 1e-12
+
+
+def test_text_projection_structure():
+    rng = np.random.default_rng(7)
+    D = 64
+    x = rng.standard_normal((9, D))
+    wn = rng.normal(0.0, 0.02, D)
+    w1 = rng.standard_normal((D, D)) / np.sqrt(D)
+    w2 = rng.standard_normal((D, D)) / np.sqrt(D)
+    y = O.text_projection(x, wn, w1, w2)
+    # the norm comes first: with eps = 0 a positive scale of the input leaves the output unchanged
+    y0 = O.text_projection(x, wn, w1, w2, eps=0.0)
+    assert np.allclose(O.text_projection(3.7 * x, wn, w1, w2, eps=0.0), y0, rtol=1e-12, atol=1e-14)
+    # with W1 = c I and W2 = I the path is GELU(c * x * rrms * (w + 1)) elementwise
+    c = 1.9
+    rr = 1.0 / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + 1e-6)
+    yi = O.text_projection(x, wn, c * np.eye(D), np.eye(D))
+    assert np.allclose(yi, O.gelu_tanh(c * x * rr * (wn + 1.0)), rtol=1e-13, atol=1e-15)
+    # rows are independent and zero rows map to zero
+    assert np.allclose(O.text_projection(x[3:4], wn, w1, w2), y[3:4], rtol=1e-13, atol=1e-15)
+    assert np.all(O.text_projection(np.zeros((2, D)), wn, w1, w2) == 0.0)
