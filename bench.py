@@ -137,7 +137,10 @@ def dit_bench(args):
     layout = rt.Layout(wl.segments, dev)
     model = rt.DiT(layout, shared, layers, dev)
     n_text = wl.segments[0].n_tokens
-    x_text = torch.randn((n_text, D), generator=g, device=dev)
+    # the context path: synthetic vision-language rows through the TextProjection give the text rows
+    tp = rt.TextProjection(vec(D), lin(D, D), lin(D, D))
+    x_ctx = torch.randn((n_text, D), generator=g, device=dev)
+    x_text = tp(x_ctx)
     lat_ref = torch.randn((P - n_text, 64), generator=g, device=dev)
     lat = torch.randn((T, 64), generator=g, device=dev)
     sig = qin.sigmas(8)
@@ -159,7 +162,8 @@ def dit_bench(args):
     model.step(0, lat, sig, x_text, lat_ref)       # warm-up (also fills the caches)
     model.step(1, lat, sig)
     torch.cuda.synchronize()
-    ms1 = timed(lambda: model.step(0, lat, sig, x_text, lat_ref))
+    ms1 = timed(lambda: model.step(0, lat, sig, tp(x_ctx, out=x_text), lat_ref))
+    ms_tp = min(timed(lambda: tp(x_ctx, out=x_text)) for _ in range(5))
     # cached steps cycle through the schedule's steps 1..7 (sig holds 8 steps + the end point)
     n_cached = len(sig) - 2
     cached = [timed(lambda k=1 + i % n_cached: model.step(k, lat, sig)) for i in range(args.steps)]
@@ -168,11 +172,13 @@ def dit_bench(args):
         "metric": "single-stream DiT denoiser step time (conditioning + layers + head + Euler)",
         "value": round(msc, 3), "unit": "ms per cached step", "higher_is_better": False,
         "n_gpus": 1, "steps": args.steps, "dtype": "bf16", "data": "synthetic, random-init weights",
-        "config": {"workload": f"text {n_text} + 10 refs 32x32 + target 64x64 (S={S}, P={P}, T={T}); "
+        "config": {"workload": f"text {n_text} (context through the TextProjection) + 10 refs 32x32 + target 64x64 (S={S}, P={P}, T={T}); "
                                f"hidden {D}, {H}x128 heads, SwiGLU {F}; {NL} layers",
                    "step1_ms": round(ms1, 3), "step1_tflops": round(f_step1 / (ms1 * 1e-3) / 1e12, 1),
                    "cached_step_tflops": round(f_cached / (msc * 1e-3) / 1e12, 1),
-                   "eight_step_loop_ms": round(ms1 + 7 * msc, 2)},
+                   "eight_step_loop_ms": round(ms1 + 7 * msc, 2),
+                   "text_projection_ms": round(ms_tp, 4),
+                   "text_projection_tflops": round(2 * 2 * n_text * D * D / (ms_tp * 1e-3) / 1e12, 1)},
     }
     print(json.dumps(res), flush=True)
 

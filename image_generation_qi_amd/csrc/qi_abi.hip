@@ -382,7 +382,7 @@ int qi_gemm_bf16_ex(const void* x, int64_t ldx, const void* w, void* out, int64_
                     int64_t K, int epilogue, const float* gate, int64_t row0, int64_t P, int32_t tile_n, void* stream) {
   clear_hip_error();
   if (!x || !w || !out) return QI_ERR_ARG;
-  if (epilogue < QI_EPI_STORE || epilogue > QI_EPI_SWIGLU) return QI_ERR_ARG;
+  if (epilogue < QI_EPI_STORE || epilogue > QI_EPI_GELU) return QI_ERR_ARG;
   if (epilogue == QI_EPI_GATED_RESIDUAL && !gate) return QI_ERR_ARG;
   if (tile_n != 0 && tile_n != 256 && tile_n != 192 && tile_n != 128) return QI_ERR_ARG;
   if (tile_n == 192 && epilogue == QI_EPI_SWIGLU) return QI_ERR_ARG;

@@ -2,9 +2,11 @@
 //   - k_gemm_big<EPI, BN>: y = x W^T on bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulation) with
 //     fused epilogues: bf16 store (QKV projection), fp32 store (img_in, velocity head),
 //     tanh-gated residual add into the fp32 residual stream (attention out-projection and FFN
-//     down-projection), and SwiGLU (FFN gate|up projection) ("Qwen-Image-2.1" course overview,
+//     down-projection), SwiGLU (FFN gate|up projection) ("Qwen-Image-2.1" course overview,
 //     card 5A: modulated SwiGLU FFN with a residual tanh gate; projections as in the attention
-//     processor of "QwenImageTransformer2DModel source reading (Qwen-Image-Edit)", section 6).
+//     processor of "QwenImageTransformer2DModel source reading (Qwen-Image-Edit)", section 6), and
+//     tanh-form GELU (the first Linear of the context TextProjection, "1B - Qwen3-VL Context &
+//     Zero-Center RMSNorm", sections 1-3).
 //   - k_zc_norm_mod: ZeroCenterRMSNorm x*rrms*(w+1) ("1B - Qwen3-VL Context & Zero-Center
 //     RMSNorm", sections 1-3) followed by the AdaLN modulation x*(1+scale)+shift (source reading,
 //     section 5.2), with the prefix rows taking the t = 0 parameters and the target rows the
@@ -213,6 +215,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 u32x2{to_bf16(y[0]) | (to_bf16(y[1]) << 16), to_bf16(y[2]) | (to_bf16(y[3]) << 16)};
           } else if constexpr (EPI == QI_EPI_STORE_F32) {
             *(f32x4*)((float*)a.out + m * a.ldo + n) = y;
+          } else if constexpr (EPI == QI_EPI_GELU) {
+            // tanh-form GELU: 0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3)))
+            float gl[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float u = 0.7978845608028654f * __builtin_fmaf(0.044715f * y[e] * y[e], y[e], y[e]);
+              gl[e] = 0.5f * y[e] * (1.0f + tanhf(u));
+            }
+            *(u32x2*)((__bf16*)a.out + m * a.ldo + n) =
+                u32x2{to_bf16(gl[0]) | (to_bf16(gl[1]) << 16), to_bf16(gl[2]) | (to_bf16(gl[3]) << 16)};
           } else {  // QI_EPI_GATED_RESIDUAL
             const f32x4 gt = *(const f32x4*)(a.gate + ((m + a.row0 < a.P) ? 0 : a.N) + n);
             f32x4* xp = (f32x4*)((float*)a.out + m * a.ldo + n);
@@ -332,6 +344,7 @@ hipError_t launch_big(const GemmArgs& a, int epi, int bn, hipStream_t s) {
       case QI_EPI_STORE: QI_LAUNCH_BIG(QI_EPI_STORE, 256); break;
       case QI_EPI_STORE_F32: QI_LAUNCH_BIG(QI_EPI_STORE_F32, 256); break;
       case QI_EPI_GATED_RESIDUAL: QI_LAUNCH_BIG(QI_EPI_GATED_RESIDUAL, 256); break;
+      case QI_EPI_GELU: QI_LAUNCH_BIG(QI_EPI_GELU, 256); break;
       case QI_EPI_SWIGLU: QI_LAUNCH_BIG(QI_EPI_SWIGLU, 256); break;
       default: return hipErrorInvalidValue;
     }
@@ -340,6 +353,7 @@ hipError_t launch_big(const GemmArgs& a, int epi, int bn, hipStream_t s) {
       case QI_EPI_STORE: QI_LAUNCH_BIG(QI_EPI_STORE, 192); break;
       case QI_EPI_STORE_F32: QI_LAUNCH_BIG(QI_EPI_STORE_F32, 192); break;
       case QI_EPI_GATED_RESIDUAL: QI_LAUNCH_BIG(QI_EPI_GATED_RESIDUAL, 192); break;
+      case QI_EPI_GELU: QI_LAUNCH_BIG(QI_EPI_GELU, 192); break;
       default: return hipErrorInvalidValue;   // SwiGLU needs whole 64-row gate|up blocks per wave
     }
   } else if (bn == 128) {
@@ -347,6 +361,7 @@ hipError_t launch_big(const GemmArgs& a, int epi, int bn, hipStream_t s) {
       case QI_EPI_STORE: QI_LAUNCH_BIG(QI_EPI_STORE, 128); break;
       case QI_EPI_STORE_F32: QI_LAUNCH_BIG(QI_EPI_STORE_F32, 128); break;
       case QI_EPI_GATED_RESIDUAL: QI_LAUNCH_BIG(QI_EPI_GATED_RESIDUAL, 128); break;
+      case QI_EPI_GELU: QI_LAUNCH_BIG(QI_EPI_GELU, 128); break;
       case QI_EPI_SWIGLU: QI_LAUNCH_BIG(QI_EPI_SWIGLU, 128); break;
       default: return hipErrorInvalidValue;
     }

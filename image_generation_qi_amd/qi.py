@@ -21,7 +21,7 @@ QI_OK, QI_ERR_ARG, QI_ERR_DTYPE, QI_ERR_SHAPE, QI_ERR_ALIGN, QI_ERR_LAYOUT, QI_E
     0, -1, -2, -3, -4, -5, -6, -7
 QI_F32, QI_BF16, QI_F16 = 0, 1, 2
 QI_SEG_TEXT, QI_SEG_IMAGE, QI_SEG_TEXT_BIDIR = 0, 1, 2
-QI_EPI_STORE, QI_EPI_STORE_F32, QI_EPI_GATED_RESIDUAL, QI_EPI_SWIGLU = 0, 1, 2, 3
+QI_EPI_STORE, QI_EPI_STORE_F32, QI_EPI_GATED_RESIDUAL, QI_EPI_SWIGLU, QI_EPI_GELU = 0, 1, 2, 3, 4
 QI_HEAD_DIM = 128
 
 

@@ -212,6 +212,30 @@ def norm_mod(x: torch.Tensor, out: torch.Tensor, w=None, scale=None, shift=None,
     return out
 
 
+class TextProjection:
+    """The context path of [1B] sections 1-3: ZeroCenterRMSNorm (weights stored as scale - 1),
+    Linear, GELU(tanh), Linear; vision-language context rows (fp32 [n][D]) in, the DiT's text
+    rows (fp32 [n][D]) out.  Three library calls: the norm, a GEMM with the GELU epilogue, a GEMM
+    with the fp32 store."""
+
+    def __init__(self, norm_w: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, eps: float = 1e-6):
+        self.norm_w, self.w1, self.w2, self.eps = norm_w.contiguous(), w1.contiguous(), w2.contiguous(), eps
+        self.D = self.w1.shape[1]
+        assert self.w1.shape == (self.D, self.D) and self.w2.shape == (self.D, self.D)
+
+    def __call__(self, x_ctx: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        n, D = x_ctx.shape
+        assert D == self.D and x_ctx.dtype == torch.float32
+        dev = x_ctx.device
+        h = torch.empty((n, D), dtype=torch.bfloat16, device=dev)
+        a = torch.empty((n, D), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((n, D), dtype=torch.float32, device=dev) if out is None else out
+        norm_mod(x_ctx, h, self.norm_w, None, None, 0, 0, self.eps)
+        gemm(h, self.w1, a, Q.QI_EPI_GELU)
+        gemm(a, self.w2, out, Q.QI_EPI_STORE_F32)
+        return out
+
+
 def linear_small(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, silu_in: bool):
     nv, I = x.shape
     O_ = w.shape[0]

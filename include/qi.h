@@ -229,8 +229,16 @@ int qi_euler_step(float* x, const void* v, qi_dtype v_dtype, int64_t n, float si
  *                         [OV] card 3B) else gate[1]
  *   QI_EPI_SWIGLU         out bf16 [M][ldo] with N/2 columns = SiLU(gate) * up ([OV] card 5A);
  *                         W rows come in blocks of 64: 32 gate rows, then the 32 up rows of the
- *                         same output features (feature f: gate row 64(f/32) + f%32, up row +32). */
-typedef enum { QI_EPI_STORE = 0, QI_EPI_STORE_F32 = 1, QI_EPI_GATED_RESIDUAL = 2, QI_EPI_SWIGLU = 3 } qi_epilogue;
+ *                         same output features (feature f: gate row 64(f/32) + f%32, up row +32).
+ *   QI_EPI_GELU           out bf16 [M][ldo] = GELU(y), the tanh form 0.5 y (1 + tanh(sqrt(2/pi) (y +
+ *                         0.044715 y^3))) (the context TextProjection of [1B] sections 1-3). */
+typedef enum {
+  QI_EPI_STORE = 0,
+  QI_EPI_STORE_F32 = 1,
+  QI_EPI_GATED_RESIDUAL = 2,
+  QI_EPI_SWIGLU = 3,
+  QI_EPI_GELU = 4
+} qi_epilogue;
 
 /* Dense projection on bf16 MFMA: x device bf16 [M][ldx]; w device bf16 [N][K] (the Linear weight,
  * out x in); K % 64 == 0, N % 64 == 0, ldx/ldo multiples of 8, M * ldx and N * K below 2^30

@@ -150,14 +150,28 @@ def test_gemm_swiglu(M, N, K, tile):
     assert torch.all(buf[:M, F:] == 3.0) and torch.all(buf[M:] == 3.0)
 
 
-@pytest.mark.parametrize("epi", [Q.QI_EPI_STORE, Q.QI_EPI_STORE_F32, Q.QI_EPI_GATED_RESIDUAL, Q.QI_EPI_SWIGLU])
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_gelu(M, N, K, tile):
+    say(f"[gemm gelu] M={M} N={N} K={K} tile={tile}")
+    x, w = gemm_inputs(M, N, K, 3)
+    ref = O.gelu_tanh(O.linear(x.f64, w.f64))
+    buf, out = padded(M, N, N + 8, torch.bfloat16, 9.0)
+    rt.gemm(bf(x), bf(w), out, Q.QI_EPI_GELU, tile_n=tile)
+    sync()
+    check(host(out), ref, "bf16", "gelu")
+    assert torch.all(buf[:M, N:] == 9.0) and torch.all(buf[M:] == 9.0), "write outside the output view"
+
+
+@pytest.mark.parametrize("epi", [Q.QI_EPI_STORE, Q.QI_EPI_STORE_F32, Q.QI_EPI_GATED_RESIDUAL, Q.QI_EPI_SWIGLU,
+                                 Q.QI_EPI_GELU])
 def test_gemm_tiles_give_identical_bits(epi):
     # every output is the same fp32 sum in the same order whatever the tile, so the bits agree
     M, N, K = 600, 448, 192
     x, w = gemm_inputs(M, N, K, 2)
     gate = f32(qin.normal(CFG, 212, (2, N), std=0.7))
     F = N // 2 if epi == Q.QI_EPI_SWIGLU else N
-    dt = torch.bfloat16 if epi in (Q.QI_EPI_STORE, Q.QI_EPI_SWIGLU) else torch.float32
+    dt = torch.bfloat16 if epi in (Q.QI_EPI_STORE, Q.QI_EPI_SWIGLU, Q.QI_EPI_GELU) else torch.float32
     outs = []
     for tile in ([0, 128, 256] if epi == Q.QI_EPI_SWIGLU else [0, 128, 192, 256]):
         out = torch.zeros((M, F), dtype=dt, device=DEV) + 0.5
@@ -174,6 +188,7 @@ def test_gemm_argument_errors():
     o = torch.zeros((8, 64), dtype=torch.float32, device=DEV)
     s = rt.stream_handle(DEV)
     assert Q.qi_gemm_bf16(x, 64, w, o, 64, 8, 64, 64, Q.QI_EPI_GATED_RESIDUAL, None, 0, 0, s) == Q.QI_ERR_ARG
+    assert Q.qi_gemm_bf16(x, 64, w, o, 64, 8, 64, 64, Q.QI_EPI_GELU + 1, None, 0, 0, s) == Q.QI_ERR_ARG
     assert Q.qi_gemm_bf16(x, 64, w, o, 64, 8, 96, 64, Q.QI_EPI_STORE_F32, None, 0, 0, s) == Q.QI_ERR_SHAPE
     assert Q.qi_gemm_bf16(x, 64, w, o, 64, 8, 64, 32, Q.QI_EPI_STORE_F32, None, 0, 0, s) == Q.QI_ERR_SHAPE
     assert Q.qi_gemm_bf16(x, 60, w, o, 64, 8, 64, 64, Q.QI_EPI_STORE_F32, None, 0, 0, s) == Q.QI_ERR_SHAPE
@@ -289,6 +304,24 @@ def test_cast_bf16_bit_exact():
     Q.check(Q.qi_cast_bf16(f32(nanv), yn, 2, rt.stream_handle(DEV)), "qi_cast_bf16")
     sync()
     assert torch.all(torch.isnan(yn.float().cpu()))
+
+
+# ------------------------------------------------------------------------------------------------
+# the context TextProjection ([1B] sections 1-3)
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,D", [(37, 256), (1, 128), (512, 3072)])
+def test_text_projection(n, D):
+    say(f"[text projection] n={n} D={D}")
+    tw = qin.text_projection_weights(CFG, D)
+    x = qin.context_inputs(CFG, n, D)
+    tp = rt.TextProjection(f32(tw["tp_norm"]), bf(tw["tp_w1"]), bf(tw["tp_w2"]))
+    y = tp(f32(x))
+    sync()
+    ref = O.text_projection(x, tw["tp_norm"], tw["tp_w1"].f64, tw["tp_w2"].f64)
+    # two bf16-rounded intermediates (the normed rows and the GELU output) precede the last
+    # product, so the chained bar applies (each GEMM alone meets the bf16 bar)
+    check(host(y), ref, "chain", "text projection")
 
 
 # ------------------------------------------------------------------------------------------------
