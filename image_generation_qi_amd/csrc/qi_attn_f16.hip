@@ -62,7 +62,7 @@ constexpr int BM = kAttnF16TileQ;   // query rows per workgroup (8 waves of 32)
 constexpr int BN = 64;              // keys per tile
 constexpr int HD = 128;             // head dim
 constexpr int TILE_B = BN * HD * 2; // bytes of one K or V tile (16 KB)
-constexpr int STAGE_B = 2 * TILE_B; // one pipeline stage: K tile then V tile
+constexpr int SLOTS = 4;            // LDS slots for K tiles, and as many for V tiles (128 KB)
 
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
   const int q = n >> 3, r = n & 7;
@@ -95,7 +95,7 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 template <bool MASKED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_f16(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_B];
+  __shared__ __attribute__((aligned(16))) char smem[2 * SLOTS * TILE_B];   // K slots, then V slots
 
   const int n_qt = (a.n_q + BM - 1) / BM;
   // which unit (query tile x head) and which key chunk of it (of nsp) this workgroup runs
@@ -232,14 +232,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const __amdgpu_buffer_rsrc_t rkB = __builtin_amdgcn_make_buffer_rsrc((void*)kB, (short)0, ntB * TILE_B, 0x00020000);
   const __amdgpu_buffer_rsrc_t rvB = __builtin_amdgcn_make_buffer_rsrc((void*)vB, (short)0, ntB * TILE_B, 0x00020000);
   const int voff = lane * 16;
-  // copy j (0 or 1) of the K (is_k) or V tile t into stage `stage`
-  auto copy = [&](int t, int stage, int j, auto is_k_tag) {
+  // copy j (0 or 1) of the K (is_k) or V tile t into K or V slot `slot`
+  auto copy = [&](int t, int slot, int j, auto is_k_tag) {
     constexpr bool IS_K = decltype(is_k_tag)::value;
     const bool inA = t < ntA;
     const __amdgpu_buffer_rsrc_t rs = IS_K ? (inA ? rkA : rkB) : (inA ? rvA : rvB);
     const int piece = (2 * wave + j) * 1024;
     const int soff = (inA ? t : t - ntA) * TILE_B + piece;
-    char* dst = smem + stage * STAGE_B + (IS_K ? 0 : TILE_B) + piece;
+    char* dst = smem + ((IS_K ? 0 : SLOTS) + slot) * TILE_B + piece;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, soff, 0, 0);
   };
 
@@ -260,16 +260,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // K (reduction step kk, key block kb): slot 32kb + l32, dims 16kk + 8g .. + 7 = piece
   // (2kk + g) * 1024 + slot * 16.  V^T (16-key chunk c, dims 32bd + l32): keys 16c + 8g .. + 7 =
   // piece (2c + g) * 2048 + dim * 16.
+  // The slot of every read is a compile-time constant; the V base holds the V region's offset,
+  // so all constant parts stay within the 16-bit offset field of ds_read_b128.
   const int base_k = g * 1024 + l32 * 16;
-  const int base_v = TILE_B + g * 2048 + l32 * 16;
+  const int base_v = SLOTS * TILE_B + g * 2048 + l32 * 16;
   auto read_k = [&](auto stag, int kk, int kb) -> h8 {
-    return *(const h8*)(smem + decltype(stag)::value * STAGE_B + base_k + kk * 2048 + kb * 512);
+    return *(const h8*)(smem + base_k + (decltype(stag)::value * TILE_B + kk * 2048 + kb * 512));
   };
   auto read_v = [&](auto stag, int c, int bd) -> h8 {
-    return *(const h8*)(smem + decltype(stag)::value * STAGE_B + base_v + c * 4096 + bd * 512);
+    return *(const h8*)(smem + base_v + (decltype(stag)::value * TILE_B + c * 4096 + bd * 512));
   };
 
-  // S^T - m = K Q^T - m for the 64 keys of stage 0's K tile.  Prologue only.
+  // S^T - m = K Q^T - m for the 64 keys of K slot 0.  Prologue only.
   auto qk0 = [&](f32x16& s0, f32x16& s1) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
@@ -285,16 +287,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // starting at minus the reference).  Every step also issues the LDS operand reads of the next
   // step and forms two probabilities 2^s of the current tile (scores 2i, 2i+1 of the first
   // 32-key block in steps 0-7, of the second in steps 8-15), rounded to fp16 and added into the
-  // row sum; steps 0-3 issue the wave's four copies of later tiles (K of tile tk, V of tile tv,
-  // into stage cs).  So the softmax VALU work is spread over all 32 MFMAs of the tile.
-  auto seq = [&](auto rtag, int cs, int tk, int tv, f32x16& sn0, f32x16& sn1, const f32x16& s0, const f32x16& s1,
-                 const h8 (&pp)[4], h8 (&pf)[4]) -> float {
+  // row sum; steps 0-3 issue the wave's four copies of later tiles (K of tile tk into K slot kcs,
+  // V of tile tv into V slot vcs).  So the softmax VALU work is spread over all 32 MFMAs of the
+  // tile.  ktag / vtag: the slots the K and V operands are read from.
+  auto seq = [&](auto ktag, auto vtag, int kcs, int vcs, int tk, int tv, f32x16& sn0, f32x16& sn1,
+                 const f32x16& s0, const f32x16& s1, const h8 (&pp)[4], h8 (&pf)[4]) -> float {
     const h2 one2 = {(_Float16)1.f, (_Float16)1.f};
     // operands of step n: V^T (chunk n/2, dims 64(n%2) + 32e ..) for n < 8, K (step n - 8,
     // key blocks e = 0, 1) after
     auto read_ops = [&](int n, h8 (&d)[2]) {
 #pragma unroll
-      for (int e = 0; e < 2; ++e) d[e] = n < 8 ? read_v(rtag, n >> 1, 2 * (n & 1) + e) : read_k(rtag, n - 8, e);
+      for (int e = 0; e < 2; ++e) d[e] = n < 8 ? read_v(vtag, n >> 1, 2 * (n & 1) + e) : read_k(ktag, n - 8, e);
     };
     h8 op[2][2];
     read_ops(0, op[0]);
@@ -303,9 +306,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = 0; i < 16; ++i) {
       if (i + 1 < 16) read_ops(i + 1, op[(i + 1) & 1]);
       if (i < 2)
-        copy(tk, cs, i, std::true_type{});
+        copy(tk, kcs, i, std::true_type{});
       else if (i < 4)
-        copy(tv, cs, i - 2, std::false_type{});
+        copy(tv, vcs, i - 2, std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
       if (i < 8) {
         const int c = i >> 1, bd = 2 * (i & 1);
@@ -331,9 +334,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return ps0 + ps1;
   };
 
-  // PV of the last tile (V in stage `stage`, known only at run time), after the loop.
-  auto pv_last = [&](int stage, const h8 (&pp)[4]) {
-    const char* vs = smem + stage * STAGE_B + base_v;
+  // PV of the last tile (V in slot `slot`, known only at run time), after the loop.
+  auto pv_last = [&](int slot, const h8 (&pp)[4]) {
+    const char* vs = smem + slot * TILE_B + base_v;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -342,45 +345,50 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   // ---- software-pipelined main loop ------------------------------------------------------
-  // Tile j's K and V live in stage (j - t_begin) & 1.  Iteration kt (stage b = (kt - t_begin)
-  // & 1, known at compile time: the loops run in pairs from an even offset) reads only the other
-  // stage b' and copies only into stage b: one fenced sequence runs the PV of tile kt-1 (V from
-  // stage b', probabilities carried from the previous iteration), the QK^T of tile kt+1 (K from
-  // stage b') and the probabilities of tile kt, and issues the copies of K[kt+2] and V[kt] into
-  // stage b (last read in iteration kt-1); then the rare reference update of tile kt; then the
-  // copies are waited for and a barrier ends the iteration.  The first iteration's PV multiplies
-  // zero probabilities with the zero-filled V stage.  Scores and probabilities alternate between
-  // two register sets; the PV of the last tile follows the loop.
+  // K tile j lives in K slot (j - t_begin) % 4 and V tile j in V slot (j - t_begin) % 4.
+  // Iteration kt (r = (kt - t_begin) % 4, known at compile time: the loops run in groups of four
+  // from t_begin) is one fenced sequence: the PV of tile kt-1 (V slot r-1, probabilities carried
+  // from the previous iteration), the QK^T of tile kt+1 (K slot r+1) and the probabilities of
+  // tile kt, issuing the copies of K[kt+3] into K slot r+3 and V[kt+1] into V slot r+1; then the
+  // rare reference update of tile kt.  Iterations go in pairs (r = 0, 1 and r = 2, 3), and one
+  // wait for the copies plus one barrier end each pair: every slot that a pair copies into was
+  // last read two iterations earlier (before the previous barrier), and every tile a pair reads
+  // was copied in the pair before, so waves may drift by an iteration inside a pair.  The first
+  // iteration's PV multiplies zero probabilities with the zero-filled V slot 3.  Scores and
+  // probabilities alternate between two register sets; the PV of the last tile follows the loop.
   {
-    // zero-fill both stages once, so that the first iteration's V stage holds zeros
+    // zero-fill all slots once, so that the first iteration's V slot holds zeros
     u32x4* z = (u32x4*)smem;
 #pragma unroll
-    for (int i = 0; i < (2 * STAGE_B) / (16 * 512); ++i) z[i * 512 + tid] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < (2 * SLOTS * TILE_B) / (16 * 512); ++i) z[i * 512 + tid] = u32x4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
+  auto last = [&](int t) { return t < t_stop ? t : t_stop - 1; };
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     copy(t_begin, 0, j, std::true_type{});
-    copy(t_begin + 1 < t_stop ? t_begin + 1 : t_begin, 1, j, std::true_type{});
+    copy(last(t_begin + 1), 1, j, std::true_type{});
+    copy(last(t_begin + 2), 2, j, std::true_type{});
+    copy(t_begin, 0, j, std::false_type{});
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16 sa0, sa1, sb0, sb1;
   qk0(sa0, sa1);
-  // every wave has read K[t_begin] from stage 0 before the first iteration copies into it
+  // every wave has read K slot 0 before the pair that copies into it
   __syncthreads();
   int kt = t_begin;
   const int kt_mid = kt_full < t_begin ? t_begin : (kt_full < t_stop ? kt_full : t_stop);
-  const int kt_mid2 = t_begin + ((kt_mid - t_begin) & ~1);   // unmasked pairs end here
+  const int kt_mid4 = t_begin + ((kt_mid - t_begin) & ~3);   // unmasked groups of four end here
   // probabilities of the previous and the current tile (two register sets, swapped per iteration)
   h8 pa[4], pb[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) pa[c][e] = (_Float16)0.f;
-  auto iteration = [&](auto btag, auto masked_tag, f32x16& s0, f32x16& s1, f32x16& sn0, f32x16& sn1,
+  auto iteration = [&](auto rtag, auto masked_tag, f32x16& s0, f32x16& s1, f32x16& sn0, f32x16& sn1,
                        const h8 (&pp)[4], h8 (&pf)[4]) {
-    constexpr int B = decltype(btag)::value;
+    constexpr int R = decltype(rtag)::value;
     constexpr bool MT = decltype(masked_tag)::value;
     if constexpr (MT) {
       const int key0 = kt < ntA ? kt * BN : nA + (kt - ntA) * BN;
@@ -395,9 +403,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (kr + 32 > rel) s1[r] = -INFINITY;
       }
     }
-    // next tile's scores (on the last iteration from a stale, in-bounds stage, discarded)
-    const int tk = kt + 2 < t_stop ? kt + 2 : t_stop - 1;
-    float ps = seq(ic<B ^ 1>{}, B, tk, kt, sn0, sn1, s0, s1, pp, pf);
+    // next tile's scores (on the last iteration from a stale, in-bounds slot, discarded); copies
+    // past the last tile repeat the last tile into slots nothing reads again
+    float ps = seq(ic<(R + 1) % SLOTS>{}, ic<(R + 3) % SLOTS>{}, (R + 3) % SLOTS, (R + 1) % SLOTS, last(kt + 3),
+                   last(kt + 1), sn0, sn1, s0, s1, pp, pf);
     // Rare path: a row's first visible tile (reference still -inf) or a lane's 32 probabilities
     // summing above 2^8 (which includes +inf and NaN).  The row's new reference is its true max;
     // the probabilities and their sum are recomputed, the running output and sum are rescaled by
@@ -452,29 +461,57 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       l_run *= alpha;
     }
     l_run += ps;
+  };
+  auto pair_end = [&]() {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  while (kt + 1 < kt_mid2) {
+  while (kt + 3 < kt_mid4) {
     iteration(ic<0>{}, std::false_type{}, sa0, sa1, sb0, sb1, pa, pb);
     ++kt;
     iteration(ic<1>{}, std::false_type{}, sb0, sb1, sa0, sa1, pb, pa);
     ++kt;
+    pair_end();
+    iteration(ic<2>{}, std::false_type{}, sa0, sa1, sb0, sb1, pa, pb);
+    ++kt;
+    iteration(ic<3>{}, std::false_type{}, sb0, sb1, sa0, sa1, pb, pa);
+    ++kt;
+    pair_end();
   }
-  while (kt + 1 < t_stop) {
+  while (kt + 3 < t_stop) {
     iteration(ic<0>{}, std::true_type{}, sa0, sa1, sb0, sb1, pa, pb);
     ++kt;
     iteration(ic<1>{}, std::true_type{}, sb0, sb1, sa0, sa1, pb, pa);
     ++kt;
+    pair_end();
+    iteration(ic<2>{}, std::true_type{}, sa0, sa1, sb0, sb1, pa, pb);
+    ++kt;
+    iteration(ic<3>{}, std::true_type{}, sb0, sb1, sa0, sa1, pb, pa);
+    ++kt;
+    pair_end();
   }
-  if (kt < t_stop) {
+  // up to three more tiles (slots 0, 1, 2)
+  const int rest = t_stop - kt;
+  if (rest >= 1) {
     iteration(ic<0>{}, std::true_type{}, sa0, sa1, sb0, sb1, pa, pb);
     ++kt;
+    if (rest >= 2) {
+      iteration(ic<1>{}, std::true_type{}, sb0, sb1, sa0, sa1, pb, pa);
+      ++kt;
+      if (rest >= 3) {
+        pair_end();
+        iteration(ic<2>{}, std::true_type{}, sa0, sa1, sb0, sb1, pa, pb);
+        ++kt;
+      }
+    }
+    if (rest != 2) {   // the latest probabilities are in pb
 #pragma unroll
-    for (int c = 0; c < 4; ++c) pa[c] = pb[c];
+      for (int c = 0; c < 4; ++c) pa[c] = pb[c];
+    }
   }
-  // PV of the last tile (its V was copied in the last iteration, before its barrier)
-  pv_last((kt - 1 - t_begin) & 1, pa);
+  // every wave's copies of the last V tile have landed before its PV
+  pair_end();
+  pv_last((kt - 1 - t_begin) % SLOTS, pa);
 
   // ---- epilogue: normalise and store bf16, or store the chunk's partial ---------------------
   const float lt = pair_sum(l_run);
