@@ -42,6 +42,12 @@ int analyse_layout(const qi_layout* L, LayoutInfo* info) {
     out.tab.causal[s] = g.kind == QI_SEG_TEXT ? 1 : 0;
   }
   if (L->seg[L->n_seg - 1].kind != QI_SEG_IMAGE) return QI_ERR_LAYOUT;  // target image last
+  if (L->attention != QI_ATTN_BLOCK_CAUSAL && L->attention != QI_ATTN_FULL) return QI_ERR_LAYOUT;
+  if (L->attention == QI_ATTN_FULL) {   // one bidirectional span: every row sees keys 0 .. S-1
+    out.tab.n = 1;
+    out.tab.end[0] = (int32_t)S;
+    out.tab.causal[0] = 0;
+  }
   out.S = S;
   out.T = L->seg[L->n_seg - 1].n_tokens;
   out.P = S - out.T;

@@ -22,6 +22,7 @@ QI_OK, QI_ERR_ARG, QI_ERR_DTYPE, QI_ERR_SHAPE, QI_ERR_ALIGN, QI_ERR_LAYOUT, QI_E
 QI_F32, QI_BF16, QI_F16 = 0, 1, 2
 QI_SEG_TEXT, QI_SEG_IMAGE, QI_SEG_TEXT_BIDIR = 0, 1, 2
 QI_EPI_STORE, QI_EPI_STORE_F32, QI_EPI_GATED_RESIDUAL, QI_EPI_SWIGLU, QI_EPI_GELU = 0, 1, 2, 3, 4
+QI_ATTN_BLOCK_CAUSAL, QI_ATTN_FULL = 0, 1
 QI_HEAD_DIM = 128
 
 
@@ -46,7 +47,7 @@ class qi_segment(ctypes.Structure):
 
 class qi_layout(ctypes.Structure):
     _fields_ = [("n_seg", c_int32), ("seg", POINTER(qi_segment)), ("head_dim", c_int32),
-                ("bands", c_int32 * 3), ("theta", c_double), ("text_pos0", c_int32)]
+                ("bands", c_int32 * 3), ("theta", c_double), ("text_pos0", c_int32), ("attention", c_int32)]
 
 
 class qi_kvcache(ctypes.Structure):
@@ -157,13 +158,14 @@ def check(status: int, where: str = "qi") -> int:
 # ------------------------------------------------------------------------------------------------
 
 def make_layout(segments, head_dim: int = 128, bands=(16, 56, 56), theta: float = 10000.0,
-                text_pos0: int = -1) -> qi_layout:
-    """qi_layout from a sequence of objects with kind/n_tokens/frame/grid_h/grid_w attributes."""
+                text_pos0: int = -1, attention: int = 0) -> qi_layout:
+    """qi_layout from a sequence of objects with kind/n_tokens/frame/grid_h/grid_w attributes;
+    attention is QI_ATTN_BLOCK_CAUSAL (default) or QI_ATTN_FULL."""
     arr = (qi_segment * len(segments))()
     for i, s in enumerate(segments):
         arr[i] = qi_segment(s.kind, s.n_tokens, s.frame, s.grid_h, s.grid_w)
     L = qi_layout(len(segments), ctypes.cast(arr, POINTER(qi_segment)), head_dim, (c_int32 * 3)(*bands),
-                  theta, text_pos0)
+                  theta, text_pos0, attention)
     L._keep = arr
     return L
 

@@ -26,9 +26,11 @@ def dtype_code(name: str) -> int:
 class Layout:
     """A segment layout with its host-built rotation tables uploaded to the device."""
 
-    def __init__(self, segments, device="cuda", bands=(16, 56, 56), theta: float = 10000.0, text_pos0: int = -1):
+    def __init__(self, segments, device="cuda", bands=(16, 56, 56), theta: float = 10000.0, text_pos0: int = -1,
+                 attention: int = Q.QI_ATTN_BLOCK_CAUSAL):
         self.segments = tuple(segments)
-        self.c = Q.make_layout(self.segments, 128, bands, theta, text_pos0)
+        self.attention = attention
+        self.c = Q.make_layout(self.segments, 128, bands, theta, text_pos0, attention)
         self.S, self.P, self.T = Q.qi_layout_tokens(self.c)
         cos = np.empty((self.S, 64), np.float32)
         sin = np.empty((self.S, 64), np.float32)

@@ -67,8 +67,17 @@ typedef struct {
   int32_t kind, n_tokens, frame, grid_h, grid_w;
 } qi_segment;
 
+/* Attention mask of a layout.  QI_ATTN_BLOCK_CAUSAL: the Block-Causal mask of [OV] card 3C
+ * (text causal, each image bidirectional within itself, a segment sees the segments before it).
+ * QI_ATTN_FULL: every token sees every token -- the joint attention of the v1 / Edit model
+ * ([EDIT] section 6: text and image streams concatenated, no mask; [EDIT] section 10: Edit-Plus
+ * with several references), whose sequence is [text | noisy target | references]. */
+typedef enum { QI_ATTN_BLOCK_CAUSAL = 0, QI_ATTN_FULL = 1 } qi_attn_mask;
+
 /* Joint sequence [text | references | target] in order, the target image last ([OV] card 2A).
- * Prefix = every segment but the last; the last segment must be an image. */
+ * Prefix = every segment but the last; the last segment must be an image.  With QI_ATTN_FULL
+ * any segment order is allowed (the last segment must still be an image); the prefix / target
+ * split then only partitions the query rows. */
 typedef struct {
   int32_t n_seg;               /* 1 .. QI_MAX_SEG */
   const qi_segment* seg;       /* host, n_seg entries */
@@ -78,6 +87,7 @@ typedef struct {
   double theta;                /* rotary base ([EDIT] section 7.1: 10000) */
   int32_t text_pos0;           /* first text position; -1 = automatic: max over images of
                                   max(H/2, W/2) ([EDIT] section 7.2 with centred grids) */
+  int32_t attention;           /* qi_attn_mask (zero-initialised layouts are Block-Causal) */
 } qi_layout;
 
 /* Prefix KV cache ([OV] card 6A: stored at step 1, loaded at steps 2..N).  k and v are each

@@ -186,13 +186,16 @@ def zero_center_rms_norm(x: np.ndarray, w: np.ndarray, eps: float = 1e-6) -> np.
 # block-causal mask
 # ------------------------------------------------------------------------------------------------
 
-def mask_dense(segments) -> np.ndarray:
+def mask_dense(segments, full: bool = False) -> np.ndarray:
     """visible[q, k] for the Block-Causal mask ([OV] card 3C and lesson 3C: text reads only
     what precedes it, tokens of one image see each other both ways; [OV] learning goals: the
     prefix never sees the target).  Reading: a query sees every key of earlier segments, all
     keys of its own segment if that segment is an image (or bidirectional text), keys k <= q
-    of its own text segment, and nothing of later segments."""
+    of its own text segment, and nothing of later segments.  full=True: the joint attention of
+    the v1 / Edit model ([EDIT] section 6), every token sees every token."""
     sid = segment_ids(segments)
+    if full:
+        return np.ones((sid.shape[0], sid.shape[0]), dtype=bool)
     kinds = np.array([s.kind for s in segments])
     S = sid.shape[0]
     q = np.arange(S)[:, None]
@@ -203,10 +206,12 @@ def mask_dense(segments) -> np.ndarray:
     return (sk < sq) | (same & ~causal_text) | (same & causal_text & (k <= q))
 
 
-def mask_rows(segments, rows) -> np.ndarray:
+def mask_rows(segments, rows, full: bool = False) -> np.ndarray:
     """The same visibility rule as mask_dense, evaluated only for the given query rows
     (shape [len(rows), S]); used to check sampled rows of full-size sequences."""
     sid = segment_ids(segments)
+    if full:
+        return np.ones((len(rows), sid.shape[0]), dtype=bool)
     kinds = np.array([s.kind for s in segments])
     rows = np.asarray(rows, dtype=np.int64)
     k = np.arange(sid.shape[0])[None, :]
@@ -273,14 +278,15 @@ def prep_qk(x: np.ndarray, cos_t, sin_t, w=None, eps: float = 1e-6) -> np.ndarra
 
 
 def step1(q, k, v, segments, cos_t, sin_t, q_w=None, k_w=None, eps: float = 1e-6,
-          scale: Optional[float] = None):
+          scale: Optional[float] = None, full: bool = False):
     """Denoising step 1: full block-causal attention over the whole sequence; the prefix's
     K (normalised and rotated) and V are kept as the cache ([OV] card 6A: step 1 computes
-    prefix and target and stores the prefix K/V).  Returns (O [S,H,d], (K_cache, V_cache))."""
+    prefix and target and stores the prefix K/V).  Returns (O [S,H,d], (K_cache, V_cache)).
+    full=True: the unmasked joint attention of the v1 / Edit model instead."""
     S, P, T = split_counts(segments)
     qr = prep_qk(q, cos_t, sin_t, q_w, eps)
     kr = prep_qk(k, cos_t, sin_t, k_w, eps)
-    o = attention(qr, kr, v, mask_dense(segments), scale)
+    o = attention(qr, kr, v, mask_dense(segments, full), scale)
     return o, (kr[:P].copy(), np.asarray(v, dtype=np.float64)[:P].copy())
 
 
@@ -306,9 +312,9 @@ def euler(x: np.ndarray, v: np.ndarray, sigma_k: float, sigma_k1: float) -> np.n
 # flop / byte accounting (used by the benchmark's reporting, not by the device path)
 # ------------------------------------------------------------------------------------------------
 
-def visible_pairs(segments) -> int:
+def visible_pairs(segments, full: bool = False) -> int:
     """Number of visible (query, key) pairs per head for step 1, counted from the dense mask."""
-    return int(mask_dense(segments).sum())
+    return int(mask_dense(segments, full).sum())
 
 
 # ------------------------------------------------------------------------------------------------

@@ -94,6 +94,14 @@ WORKLOADS = {
                      + (image(64, 64, 0),)),
 }
 
+# The v1 / Edit joint attention (full, unmasked) on the Edit shapes of the source-reading page:
+# [text | noisy 1024^2 target (64x64 tokens, frame 0) | references (frame 1..)] -- Edit with one
+# reference, Edit-Plus with two.  Run with the QI_ATTN_FULL layout.
+V1_WORKLOADS = {
+    "edit_v1": Workload("edit_v1", 5, (text(512), image(64, 64, 0), image(64, 64, 1))),
+    "editplus_v1": Workload("editplus_v1", 6, (text(512), image(64, 64, 0), image(64, 64, 1), image(64, 64, 2))),
+}
+
 
 def small_workload(name: str, segments: Sequence[Segment], n_head: int = 2, dtype: str = "bf16",
                    cfg_id: int = 90, qk_rmsnorm: bool = False) -> Workload:

@@ -248,3 +248,23 @@ def test_other_entry_points_reject():
     assert Q.qi_rope3d_positions(L, None) == Q.QI_ERR_ARG
     assert Q.qi_blockmap(L, 0, 64, np.zeros(4, np.uint8)) == Q.QI_ERR_ARG
     assert Q.lib().qi_attn_tile_shape(Q.QI_F16, ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32())) == Q.QI_ERR_DTYPE
+
+
+def test_full_attention_layout_maps_and_positions():
+    segs = (qin.text(77), qin.image(13, 9, 0), qin.image(15, 17, 1), qin.image(4, 4, 2))
+    Lf = Q.make_layout(segs, attention=Q.QI_ATTN_FULL)
+    Lb = Q.make_layout(segs)
+    S, P, T = Q.qi_layout_tokens(Lf)
+    assert (S, P, T) == Q.qi_layout_tokens(Lb)
+    for tq, tk in ((256, 64), (7, 5), (64, 64)):
+        out = np.zeros(((S + tq - 1) // tq, (S + tk - 1) // tk), np.uint8)
+        Q.check(Q.qi_blockmap(Lf, tq, tk, out))
+        assert np.all(out == 1)
+        assert np.array_equal(out, O.blockmap(O.mask_dense(segs, full=True), tq, tk))
+    pf, pb = (np.zeros((S, 3), np.int32) for _ in range(2))
+    Q.check(Q.qi_rope3d_positions(Lf, pf))
+    Q.check(Q.qi_rope3d_positions(Lb, pb))
+    assert np.array_equal(pf, pb)
+    bad = Q.make_layout(segs, attention=7)
+    n = [ctypes.c_int64() for _ in range(3)]
+    assert Q.lib().qi_layout_tokens(ctypes.byref(bad), *(ctypes.byref(x) for x in n)) == Q.QI_ERR_LAYOUT

@@ -611,3 +611,34 @@ def test_text_projection_structure():
     # rows are independent and zero rows map to zero
     assert np.allclose(O.text_projection(x[3:4], wn, w1, w2), y[3:4], rtol=1e-13, atol=1e-15)
     assert np.all(O.text_projection(np.zeros((2, D)), wn, w1, w2) == 0.0)
+
+
+# ------------------------------------------------------------------------------------------------
+# the v1 / Edit joint attention: [text | noisy target | references], every token sees every token
+# ------------------------------------------------------------------------------------------------
+
+def test_v1_order_positions_hand_fixture():
+    # [EDIT] section 7.2: the text stream continues after max over images of max(H/2, W/2) even
+    # though it comes first in the joint sequence; images are centred, frame = image index
+    segs = (qin.text(3), qin.image(2, 2, 0), qin.image(2, 2, 1))
+    want = np.array([[1, 1, 1], [2, 2, 2], [3, 3, 3],
+                     [0, -1, -1], [0, -1, 0], [0, 0, -1], [0, 0, 0],
+                     [1, -1, -1], [1, -1, 0], [1, 0, -1], [1, 0, 0]])
+    assert np.array_equal(O.positions(segs), want)
+
+
+def test_full_mask_is_unmasked_attention():
+    segs = (qin.text(5), qin.image(3, 2, 0), qin.image(2, 3, 1))
+    m = O.mask_dense(segs, full=True)
+    assert m.shape == (17, 17) and m.all()
+    assert O.mask_rows(segs, [0, 16], full=True).all()
+    assert O.visible_pairs(segs, full=True) == 17 * 17
+    rng = np.random.default_rng(3)
+    q, k, v = (rng.standard_normal((17, 2, 128)) for _ in range(3))
+    cos, sin = O.rope_tables(O.positions(segs))
+    o, _ = O.step1(q, k, v, segs, cos, sin, full=True)
+    qr, kr = O.rotate(q, cos, sin), O.rotate(k, cos, sin)
+    assert np.allclose(o, O.attention(qr, kr, v), rtol=1e-13, atol=1e-15)
+    # and it differs from the Block-Causal step (the text row 0 now sees the images)
+    ob, _ = O.step1(q, k, v, segs, cos, sin)
+    assert not np.allclose(o[0], ob[0])
