@@ -9,6 +9,7 @@ resident in HBM before timing starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg3|cfg3_t512|cfg2] [--no-cpu]
     python bench.py --dit [--layers L] [--steps K]     # full single-stream layer steps (see below)
+    python bench.py --v1edit [--steps K]                # v1 / Edit-Plus full joint attention
 
 Prints one JSON line.  value = attention TFLOP/s over the timed steps (visible-pair flops,
 4*d per pair); roofline = one attention call's average device time (the attention kernel plus,
@@ -19,6 +20,9 @@ the launch stream.
 + target 64x64, hidden 3072, 24x128 heads, SwiGLU 8192, random-init weights): step 1 over the
 whole sequence (filling the per-layer prefix caches) and the cached target-only steps, each with
 the conditioning, all layers, the head and the Euler update.  It prints its own JSON line.
+
+--v1edit times the unmasked joint attention of the v1 / Edit model at the Edit-Plus shape (text
+512 + noisy target 64x64 + two references 64x64, 12,800 tokens) and prints its own JSON line.
 """
 from __future__ import annotations
 
@@ -183,6 +187,48 @@ def dit_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def v1edit_bench(args):
+    """The unmasked joint attention of the v1 / Edit model at the Edit-Plus shape: text 512 +
+    noisy 64x64 target + two 64x64 references (12,800 tokens, 24 heads), one call per layer over
+    distinct Q/K/V; TFLOP/s per call from the library's HIP-event timing."""
+    import torch
+
+    import qi_inputs as qin
+    from image_generation_qi_amd import qi as Q
+    from image_generation_qi_amd import runtime as rt
+
+    wl = qin.V1_WORKLOADS["editplus_v1"]
+    dev = "cuda:0"
+    S, H = wl.S, wl.n_head
+    layout = rt.Layout(wl.segments, dev, attention=Q.QI_ATTN_FULL)
+    att = rt.Attention(layout, H, Q.QI_BF16, dev)
+    g = torch.Generator(device=dev).manual_seed(77)
+    n_sets = 4
+    qkv = [torch.randn((S, 3, H, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(n_sets)]
+    out = torch.empty((S, H, 128), dtype=torch.bfloat16, device=dev)
+    for i in range(args.warmup + 1):
+        x = qkv[i % n_sets]
+        att.full(x[:, 0], x[:, 1], x[:, 2], out=out)
+    torch.cuda.synchronize()
+    Q.qi_kernel_timing(True)
+    for i in range(args.steps):
+        x = qkv[i % n_sets]
+        att.full(x[:, 0], x[:, 1], x[:, 2], out=out)
+    torch.cuda.synchronize()
+    per_call = sorted(Q.qi_kernel_timing_read_each())
+    Q.qi_kernel_timing(False)
+    flops = 4.0 * 128 * H * S * S
+    ms = sum(per_call) / len(per_call)
+    res = {"metric": "v1 / Edit-Plus joint full attention TFLOP/s per call", "value": round(flops / (ms * 1e-3) / 1e12, 2),
+           "unit": "TFLOP/s", "higher_is_better": True, "n_gpus": 1, "steps": args.steps, "dtype": "f16",
+           "data": "synthetic", "ms_per_call": round(ms, 4),
+           "per_call_ms": {q: round(pct(per_call, int(q[1:])), 4) for q in ("p50", "p95", "p99")},
+           "config": {"workload": f"text 512 + noisy target 64x64 + 2 references 64x64, full attention, S={S}, "
+                                  f"{H}x128 heads", "flops_per_call": flops,
+                      "pct_of_peak": round(100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2)}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,6 +241,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 10 device-to-device copies of MIB MiB (reference kernel for HBM counters)")
     ap.add_argument("--dit", action="store_true", help="time full single-stream layer steps instead")
+    ap.add_argument("--v1edit", action="store_true",
+                    help="time the v1 / Edit-Plus joint full attention (text 512 + target + 2 references) instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -203,6 +251,11 @@ def main():
         from image_generation_qi_amd import qi as Q
         Q.lib()
         dit_bench(args)
+        return
+    if args.v1edit:
+        from image_generation_qi_amd import qi as Q
+        Q.lib()
+        v1edit_bench(args)
         return
 
     import torch

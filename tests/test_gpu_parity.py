@@ -354,3 +354,45 @@ def test_full_size_step1_sampled(name):
     kd = to_np(cache.k_rows(0)[:, pr].permute(1, 0, 2))
     assert np.all(np.abs(kd - kr[pr]) <= 2.0 ** -11 * np.abs(kr[pr]) + 1e-6)
     check_cached_v(to_np(cache.v_rows(0)[:, pr].permute(1, 0, 2)), c.v.f64[pr], "bf16")
+
+
+# ---------------------------------------------------------------------------------------------
+# the v1 / Edit joint attention: full (unmasked) over [text | noisy target | references]
+# ---------------------------------------------------------------------------------------------
+
+FULL_ATTN_CASES = [
+    ("v1_small", (qin.text(37), qin.image(9, 7, 0), qin.image(9, 7, 1)), "f32", False),
+    ("v1_small", (qin.text(37), qin.image(9, 7, 0), qin.image(9, 7, 1)), "bf16", True),
+    ("editplus_small", (qin.text(21), qin.image(6, 5, 0), qin.image(6, 5, 1), qin.image(6, 5, 2)), "bf16", False),
+    ("v1_ragged", (qin.text(77), qin.image(13, 9, 0), qin.image(15, 17, 1)), "bf16", True),
+    ("v1_multi_tile", (qin.text(300), qin.image(16, 20, 0), qin.image(17, 19, 1)), "bf16", False),
+]
+
+
+@pytest.mark.parametrize("name,segs,dtype,qk", FULL_ATTN_CASES)
+def test_full_attention_parity(name, segs, dtype, qk):
+    wl = qin.small_workload(name, segs, n_head=2, dtype=dtype, qk_rmsnorm=qk)
+    say(f"full attention {name} dtype={dtype} S={sum(s.n_tokens for s in segs)}")
+    c = Case(wl)
+    L = rt.Layout(wl.segments, DEV, attention=Q.QI_ATTN_FULL)
+    att = rt.Attention(L, wl.n_head, rt.dtype_code(wl.dtype), DEV)
+    o = att.full(c.qd, c.kd, c.vd, c.qw_d, c.kw_d)
+    torch.cuda.synchronize()
+    ref, _ = O.step1(c.q.f64, c.k.f64, c.v.f64, wl.segments, c.cos, c.sin, c.qw, c.kw, full=True)
+    check_close(to_np(o), ref, wl.dtype, f"{name} full attention")
+
+
+@pytest.mark.parametrize("name", ["edit_v1", "editplus_v1"])
+def test_full_attention_full_size_sampled(name):
+    wl = qin.V1_WORKLOADS[name]
+    say(f"full attention full size {name} S={wl.S}")
+    c = Case(wl)
+    L = rt.Layout(wl.segments, DEV, attention=Q.QI_ATTN_FULL)
+    att = rt.Attention(L, wl.n_head, Q.QI_BF16, DEV)
+    o = att.full(c.qd, c.kd, c.vd)
+    torch.cuda.synchronize()
+    bounds = np.cumsum([0] + [s.n_tokens for s in wl.segments])
+    rows = np.unique(np.concatenate([sample_rows(bounds[i], bounds[i + 1], 10, 30 + i) for i in range(len(bounds) - 1)]))
+    qr = O.rotate(c.q.f64[rows], c.cos[rows], c.sin[rows])
+    kr = O.rotate(c.k.f64, c.cos, c.sin)
+    check_close(to_np(o[rows]), O.attention(qr, kr, c.v.f64), "bf16", f"{name} sampled rows")
