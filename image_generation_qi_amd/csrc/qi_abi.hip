@@ -141,23 +141,19 @@ AttnArgs attn_args(const qi_qkv* io, const qi_qkprep* prep, float scale) {
   return a;
 }
 
-// Key-chunk count (from the layout's T, identical for step 1 and the cached steps) and the
-// partial-output buffers placed at `base` in the workspace.
-void set_partials(AttnArgs& a, char* base, int64_t n_q, int64_t T, int32_t n_head, qi_dtype dtype) {
+// The chunked schedule for a launch over a.n_q rows of units of equal cost, with its
+// partial-output buffers placed at `base` in the workspace (bf16 path only).
+void set_partials(AttnArgs& a, char* base, qi_dtype dtype) {
+  a.xcd_sched = 0;
+  a.reverse_qt = 0;
   a.n_split = 1;
   a.part_o = nullptr;
   a.part_ml = nullptr;
-  a.xcd_units = 0;
-  a.xcd_whole = 0;
   if (dtype != QI_BF16) return;
-  const AttnSched sc = attn_f16_schedule(T, n_head);
-  a.n_split = sc.n_split;
-  if (n_q == T) {   // the XCD schedule covers the target's query tiles only
-    a.xcd_units = sc.xcd_units;
-    a.xcd_whole = sc.xcd_whole;
-  }
+  const AttnSched sc = attn_f16_schedule(a.n_q, a.n_head);
+  a.xcd_sched = 1;
   a.part_o = (float*)base;
-  a.part_ml = (float*)(base + (int64_t)a.n_split * n_q * n_head * QI_HEAD_DIM * (int64_t)sizeof(float));
+  a.part_ml = (float*)(base + (int64_t)sc.tail_units * sc.n_split * kAttnF16TileQ * QI_HEAD_DIM * (int64_t)sizeof(float));
 }
 
 int run_attn(const AttnArgs& a, qi_dtype dtype, hipStream_t s) {
@@ -167,19 +163,23 @@ int run_attn(const AttnArgs& a, qi_dtype dtype, hipStream_t s) {
   return launch_status(dtype == QI_BF16 ? launch_attn_f16(a, s) : launch_attn_f32(a, s));
 }
 
-// Step 1 on the bf16 path: the prefix query rows [0, P) run as one launch over whole key ranges,
-// the target rows [P, S) as a second launch in the target's key chunks, exactly as a cached step
-// runs them, so the target rows get the same bits in both.  Partials cover the target rows only.
-int run_attn_step1_f16(const AttnArgs& a, int64_t P, int64_t T, char* part_base, hipStream_t s) {
+// Step 1 on the bf16 path: the prefix query rows [0, P) run as one launch, the target rows
+// [P, S) as a second launch in the target's schedule, exactly as a cached step runs them, so
+// the target rows get the same bits in both.  Prefix tiles that all end at the same key tile
+// (one bidirectional span, or the unmasked layout) take the chunked schedule too; otherwise
+// they run whole, longest rows first.  The two launches share the partial outputs.
+int run_attn_step1_f16(const AttnArgs& a, const SegTable& tab, int64_t P, int64_t T, char* part_base,
+                       hipStream_t s) {
   if (a.nA > QI_MAX_SOURCE_KEYS || a.nB > QI_MAX_SOURCE_KEYS) return QI_ERR_SHAPE;
   TimedLaunch t(s);
   AttnArgs ap = a;
   ap.n_q = (int32_t)P;
-  ap.n_split = 1;
-  ap.part_o = nullptr;
-  ap.part_ml = nullptr;
-  ap.xcd_units = 0;
-  ap.reverse_qt = 1;   // prefix rows: longest rows first
+  if (attn_prefix_tiles_equal(tab, P, T)) {
+    set_partials(ap, part_base, QI_BF16);
+  } else {
+    ap.xcd_sched = 0;     // whole units, longest rows first
+    ap.reverse_qt = 1;
+  }
   // the target rows keep the order and schedule of a cached step (the same bits)
   AttnArgs at = a;
   at.q = (const char*)a.q + P * a.q_stride * 2;
@@ -190,8 +190,7 @@ int run_attn_step1_f16(const AttnArgs& a, int64_t P, int64_t T, char* part_base,
   }
   at.n_q = (int32_t)T;
   at.q_row0 = a.q_row0 + P;
-  at.reverse_qt = 0;
-  set_partials(at, part_base, T, T, a.n_head, QI_BF16);
+  set_partials(at, part_base, QI_BF16);
   if (P > 0) {
     const hipError_t e = launch_attn_f16(ap, s);
     if (e != hipSuccess) return launch_status(e);
@@ -260,7 +259,7 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
   a.masked = 1;
   a.segs = li.tab;
   a.q_row0 = 0;
-  a.n_split = 1;   // the bf16 launches set their own chunking (run_attn_step1_f16)
+  // (the bf16 launches set their own schedule in run_attn_step1_f16)
   // target rows: K/V prepared into the workspace at row RA (with the target's table rows)
   const int64_t off = li.P * io->tok_stride * (io->dtype == QI_BF16 ? 2 : 4);
   qi_qkprep tprep{};
@@ -302,7 +301,7 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
   }
   a.nA = li.P;
   if (io->dtype == QI_BF16)
-    return run_attn_step1_f16(a, li.P, li.T, (char*)workspace + 2 * (int64_t)io->n_head * R * QI_HEAD_DIM * es, s);
+    return run_attn_step1_f16(a, li.tab, li.P, li.T, (char*)workspace + 2 * (int64_t)io->n_head * R * QI_HEAD_DIM * es, s);
   return run_attn(a, io->dtype, s);
 }
 
@@ -352,7 +351,7 @@ int qi_attn_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvca
     return st;
   AttnArgs a = attn_args(io, prep, scale);
   a.masked = 0;
-  set_partials(a, wk + 2 * (int64_t)io->n_head * RB * QI_HEAD_DIM * es, T, T, io->n_head, io->dtype);
+  set_partials(a, wk + 2 * (int64_t)io->n_head * RB * QI_HEAD_DIM * es, io->dtype);
   a.kA = cache_layer(cache->k, cache, layer);
   a.vA = cache_layer(cache->v, cache, layer);
   a.a_head_stride = cache_rows(cache) * QI_HEAD_DIM;

@@ -98,25 +98,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(16))) char smem[2 * SLOTS * TILE_B];   // K slots, then V slots
 
   const int n_qt = (a.n_q + BM - 1) / BM;
-  // which unit (query tile x head) and which key chunk of it (of nsp) this workgroup runs
-  int unit, split, nsp;
-  if (a.xcd_units > 0) {
+  // which unit (query tile x head) and which key chunk of it (of nsp) this workgroup runs, and
+  // for a chunk the first of its partial rows
+  int unit, split = 0, nsp = 1;
+  int64_t prow0 = 0;
+  if (a.xcd_sched) {
+    // run x (the blocks with blockIdx % 8 == x) owns units [base, base + ux): whole units
+    // first, then the remaining units in n_split chunks each, then idle blocks
+    const int n_units = n_qt * a.n_head, u8 = n_units >> 3, ur = n_units & 7;
     const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int ux = u8 + (x < ur), base = x * u8 + (x < ur ? x : ur);
     if (j < a.xcd_whole) {
-      unit = x * a.xcd_units + j;
-      split = 0;
-      nsp = 1;
+      unit = base + j;
     } else {
-      const int t = j - a.xcd_whole;
-      unit = x * a.xcd_units + a.xcd_whole + t / a.n_split;
-      split = t % a.n_split;
-      nsp = a.n_split;
+      const int t = j - a.xcd_whole, tl = t / a.n_split;
+      if (tl >= ux - a.xcd_whole) return;   // idle block of a shorter run
+      unit = base + a.xcd_whole + tl;
+      if (a.n_split > 1) {
+        split = t - tl * a.n_split;
+        nsp = a.n_split;
+        const int tu = x * (u8 - a.xcd_whole) + (x < ur ? x : ur) + tl;   // chunked unit index
+        prow0 = ((int64_t)tu * nsp + split) * BM;
+      }
     }
   } else {
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    split = logical % a.n_split;
-    unit = logical / a.n_split;
-    nsp = a.n_split;
+    unit = xcd_remap(blockIdx.x, gridDim.x);
   }
   const int h = unit / n_qt;
   int qt = unit - h * n_qt;
@@ -205,7 +211,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int t_stop = (nsp == 1 || t_begin + a.split_tiles > kt_end) ? kt_end : t_begin + a.split_tiles;
   if (t_begin >= t_stop) {  // the chunk holds no visible key for any row of the tile
     if (qok) {
-      const int64_t row = ((int64_t)split * a.n_q + qrow) * a.n_head + h;
+      const int64_t row = prow0 + wave * 32 + l32;
       f32x4* po = (f32x4*)(a.part_o + row * HD + 4 * g);
 #pragma unroll
       for (int i = 0; i < 16; ++i) po[2 * i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -528,7 +534,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           *(u32x2*)(op + 32 * bd + 8 * r4) = w;
         }
     } else {
-      const int64_t row = ((int64_t)split * a.n_q + qrow) * a.n_head + h;
+      const int64_t row = prow0 + wave * 32 + l32;
       float* po = a.part_o + row * HD + 4 * g;
 #pragma unroll
       for (int bd = 0; bd < 4; ++bd)
@@ -543,42 +549,45 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// Merge of the key chunks: for each (row, head) of a chunked unit, O = sum_s 2^(m_s - M) O_s /
-// sum_s 2^(m_s - M) l_s with M = max_s m_s, rounded to bf16.  16 threads per (row, head), 8 dims
-// each.  With an XCD schedule only the chunked units (the last xcd_units - xcd_whole units of
-// each of the 8 runs) are merged; otherwise every (row, head).
+// Merge of the key chunks: for each row of a chunked unit, O = sum_s 2^(m_s - M) O_s /
+// sum_s 2^(m_s - M) l_s with M = max_s m_s, rounded to bf16.  16 threads per row, 8 dims each.
+// Chunked unit tu is the tl-th remaining unit of run x, in run order (see k_attn_f16); its
+// partial rows are [tu][chunk][256].
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                                  uint16_t* __restrict__ o, int64_t o_stride, int n_q, int n_head,
-                                                 int n_split, int xcd_units, int xcd_whole) {
+                                                 int n_split, int xcd_whole, int n_tail) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int d0 = (int)(gid & 15) * 8;
-  int64_t rh;
-  if (xcd_units > 0) {
-    const int per_run = xcd_units - xcd_whole;
-    const int64_t k = gid >> 4;                     // (chunked unit, row in its tile)
-    const int tu = (int)(k / BM), rr = (int)(k % BM);
-    if (tu >= 8 * per_run) return;
-    const int unit = (tu / per_run) * xcd_units + xcd_whole + tu % per_run;
-    const int n_qt = (n_q + BM - 1) / BM;
-    const int h = unit / n_qt, qt = unit - h * n_qt;
-    const int row = qt * BM + rr;
-    if (row >= n_q) return;
-    rh = (int64_t)row * n_head + h;
+  const int64_t k = gid >> 4;                     // (chunked unit, row in its tile)
+  const int tu = (int)(k / BM), rr = (int)(k % BM);
+  if (tu >= n_tail) return;
+  const int n_qt = (n_q + BM - 1) / BM, n_units = n_qt * n_head, u8 = n_units >> 3, ur = n_units & 7;
+  const int r0 = u8 - xcd_whole;                  // remaining units of a run with u8 units
+  int x, tl;
+  if (tu < ur * (r0 + 1)) {
+    x = tu / (r0 + 1);
+    tl = tu - x * (r0 + 1);
   } else {
-    rh = gid >> 4;
-    if (rh >= (int64_t)n_q * n_head) return;
+    const int t = tu - ur * (r0 + 1);
+    x = ur + t / r0;
+    tl = t - (x - ur) * r0;
   }
-  const int64_t stride = (int64_t)n_q * n_head;   // rows per split
+  const int unit = x * u8 + (x < ur ? x : ur) + xcd_whole + tl;
+  const int h = unit / n_qt, qt = unit - h * n_qt;
+  const int row = qt * BM + rr;
+  if (row >= n_q) return;
+  const int64_t p0 = (int64_t)tu * n_split * BM + rr;   // chunk s of this row: p0 + s * BM
   float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, part_ml[2 * (s * stride + rh)]);
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, part_ml[2 * (p0 + s * BM)]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   for (int s = 0; s < n_split; ++s) {
-    const float m = part_ml[2 * (s * stride + rh)];
+    const int64_t pr = p0 + s * BM;
+    const float m = part_ml[2 * pr];
     if (m == -INFINITY) continue;
     const float w = __builtin_amdgcn_exp2f(m - M);
-    den += w * part_ml[2 * (s * stride + rh) + 1];
-    const f32x4* p = (const f32x4*)(part_o + (s * stride + rh) * HD + d0);
+    den += w * part_ml[2 * pr + 1];
+    const f32x4* p = (const f32x4*)(part_o + pr * HD + d0);
     const f32x4 x0 = p[0], x1 = p[1];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -587,75 +596,68 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_
     }
   }
   const float inv = 1.0f / den;
-  const int64_t q = rh / n_head;
-  const int h = (int)(rh - q * n_head);
   u32x4 w;
 #pragma unroll
   for (int j = 0; j < 4; ++j) w[j] = to_bf16(acc[2 * j] * inv) | (to_bf16(acc[2 * j + 1] * inv) << 16);
-  *(u32x4*)(o + q * o_stride + h * HD + d0) = w;
+  *(u32x4*)(o + (int64_t)row * o_stride + h * HD + d0) = w;
 }
 
 }  // namespace
 
-AttnSched attn_f16_schedule(int64_t T, int32_t n_head) {
-  // One workgroup fills a CU; the 256 CUs are 8 XCDs of 32.  Grids of four or more rounds stay
-  // whole.  Smaller grids whose units split evenly over the 8 XCDs get the XCD schedule: each
-  // XCD runs whole rounds of whole units (one per CU) and cuts only its remaining units into s
-  // key chunks, s = 1 .. 8 chosen for the shortest tail (each chunk beyond the first charged 1 %
-  // of a unit, chunking at all 3 %).  The 4,096-token target at 24 heads (384 units, 48 per XCD)
-  // runs 32 whole units and 16 units in 2 chunks per XCD: every CU does one whole unit and one
-  // half.  Other small grids cut every unit into the s chunks that best fill the last round.
-  constexpr int64_t slots = 256, per_xcd = 32;
-  AttnSched r{1, 0, 0};
-  const int64_t units = (T + BM - 1) / BM * n_head;
-  if (units >= 4 * slots || units <= 0) return r;
-  auto chunk_cost = [](int s) { return 0.01 * s + (s > 1 ? 0.03 : 0.0); };
-  if (units % 8 == 0) {
-    const int64_t ux = units / 8, wx = per_xcd * (ux / per_xcd), rem = ux - wx;
-    if (rem == 0) return r;
-    int best = 1;
-    double best_t = 1e30;
-    for (int s = 1; s <= 8; ++s) {
-      const double t = (double)((rem * s + per_xcd - 1) / per_xcd) / s + chunk_cost(s);
-      if (t < best_t - 1e-9) {
-        best_t = t;
-        best = s;
-      }
-    }
-    if (best == 1) return r;
-    return AttnSched{best, (int32_t)ux, (int32_t)wx};
-  }
+AttnSched attn_f16_schedule(int64_t n_q, int32_t n_head) {
+  // For query-tile units of equal cost.  One workgroup fills a CU; the 256 CUs are 8 XCDs of 32,
+  // and block b runs on XCD b % 8.  The U units are spread over the 8 XCDs (the first U % 8 get
+  // one more), each XCD runs whole rounds of whole units (one per CU) and cuts only its
+  // remaining units into s key chunks, s = 1 .. 8 chosen for the shortest tail (each chunk
+  // beyond the first charged 1 % of a unit, chunking at all 3 %).  The 4,096-token target at 24
+  // heads (384 units, 48 per XCD) runs 32 whole units and 16 units in 2 chunks per XCD: every
+  // CU does one whole unit and one half.
+  constexpr int64_t per_xcd = 32;
+  AttnSched r{1, 0, 0, 0};
+  const int64_t units = (n_q + BM - 1) / BM * n_head;
+  if (units <= 0) return r;
+  const int64_t u8 = units / 8, wx = per_xcd * (u8 / per_xcd);
+  const int64_t rmax = u8 - wx + (units % 8 != 0);   // remaining units of the longest run
   int best = 1;
-  double best_score = -1.0;
-  for (int s = 1; s <= 8; ++s) {
-    const int64_t blocks = units * s;
-    const double eff = (double)blocks / (double)(slots * ((blocks + slots - 1) / slots));
-    const double score = eff - chunk_cost(s);
-    if (score > best_score + 1e-9) {
-      best_score = score;
+  double best_t = 1e30;
+  for (int s = 1; s <= 8 && rmax > 0; ++s) {
+    const double t = (double)((rmax * s + per_xcd - 1) / per_xcd) / s + 0.01 * s + (s > 1 ? 0.03 : 0.0);
+    if (t < best_t - 1e-9) {
+      best_t = t;
       best = s;
     }
   }
   r.n_split = best;
+  r.xcd_whole = (int32_t)wx;
+  r.tail_units = best > 1 ? (int32_t)(units - 8 * wx) : 0;
+  r.blocks = 8 * (wx + rmax * best);
   return r;
 }
 
-int attn_f16_splits(int64_t T, int32_t n_head) { return attn_f16_schedule(T, n_head).n_split; }
-
 int64_t attn_f16_partial_bytes(int64_t n_q, int32_t n_head) {
-  return (int64_t)n_q * n_head * (HD + 2) * (int64_t)sizeof(float);
+  const AttnSched sc = attn_f16_schedule(n_q, n_head);
+  return (int64_t)sc.tail_units * sc.n_split * BM * (HD + 2) * (int64_t)sizeof(float);
 }
 
 hipError_t launch_attn_f16(const AttnArgs& a_in, hipStream_t s) {
   AttnArgs a = a_in;
   const int64_t n_qt = (a.n_q + BM - 1) / BM;
   const int64_t kt_total = (a.nA + BN - 1) / BN + (a.nB + BN - 1) / BN;
-  if (a.n_split < 1) a.n_split = 1;
+  int64_t blocks = n_qt * a.n_head;
+  int32_t n_tail = 0;
+  if (a.xcd_sched) {
+    const AttnSched sc = attn_f16_schedule(a.n_q, a.n_head);
+    a.n_split = sc.n_split;
+    a.xcd_whole = sc.xcd_whole;
+    a.reverse_qt = 0;
+    blocks = sc.blocks;
+    n_tail = sc.tail_units;
+    if (a.n_split > 1 && (!a.part_o || !a.part_ml)) return hipErrorInvalidValue;
+  } else {
+    a.n_split = 1;
+  }
   a.split_tiles = (int)((kt_total + a.n_split - 1) / a.n_split);
   if (a.split_tiles < 1) a.split_tiles = 1;
-  if (a.xcd_units > 0 && (int64_t)8 * a.xcd_units != n_qt * a.n_head) return hipErrorInvalidValue;
-  const int64_t blocks = a.xcd_units > 0 ? 8 * (int64_t)(a.xcd_whole + (a.xcd_units - a.xcd_whole) * a.n_split)
-                                         : n_qt * a.n_head * a.n_split;
   if (blocks <= 0) return hipSuccess;
   if (a.masked)
     hipLaunchKernelGGL(k_attn_f16<true>, dim3((unsigned)blocks), dim3(2 * BM), 0, s, a);
@@ -663,10 +665,9 @@ hipError_t launch_attn_f16(const AttnArgs& a_in, hipStream_t s) {
     hipLaunchKernelGGL(k_attn_f16<false>, dim3((unsigned)blocks), dim3(2 * BM), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  const int64_t threads = a.xcd_units > 0 ? (int64_t)8 * (a.xcd_units - a.xcd_whole) * BM * 16
-                                          : (int64_t)a.n_q * a.n_head * 16;
+  const int64_t threads = (int64_t)n_tail * BM * 16;
   hipLaunchKernelGGL(k_combine, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a.part_o, a.part_ml,
-                     (uint16_t*)a.o, a.o_stride, a.n_q, a.n_head, a.n_split, a.xcd_units, a.xcd_whole);
+                     (uint16_t*)a.o, a.o_stride, a.n_q, a.n_head, a.n_split, a.xcd_whole, n_tail);
   return hipGetLastError();
 }
 

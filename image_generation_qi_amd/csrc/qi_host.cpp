@@ -67,6 +67,19 @@ static int text_start(const qi_layout* L) {
   return best;
 }
 
+bool attn_prefix_tiles_equal(const SegTable& tab, int64_t P, int64_t T) {
+  if (P <= 0) return true;
+  // last key tile seen by a query row with last visible key lim (prefix keys are tiled from 0,
+  // target keys from the first tile after the prefix's)
+  auto last_tile = [&](int64_t lim) {
+    const int64_t ntA = (P + 63) / 64;
+    lim = lim < P + T - 1 ? lim : P + T - 1;
+    return lim < P ? lim / 64 : ntA + (lim - P) / 64;
+  };
+  const int64_t first_last_row = (P < kAttnF16TileQ ? P : kAttnF16TileQ) - 1;
+  return last_tile(row_limit(tab, first_last_row)) == last_tile(row_limit(tab, P - 1));
+}
+
 }  // namespace qi
 
 using namespace qi;
@@ -198,12 +211,11 @@ static int64_t rows_bytes(qi_dtype dtype, int64_t rows, int32_t n_head) {
   return QI_ERR_DTYPE;
 }
 
-// Partial outputs of the key chunks (bf16 path with more than one chunk only).
-static int64_t partial_bytes(qi_dtype dtype, int64_t n_q, int64_t T, int32_t n_head) {
-  if (dtype != QI_BF16) return 0;
-  const int s = attn_f16_splits(T, n_head);
-  return s > 1 ? (int64_t)s * attn_f16_partial_bytes(n_q, n_head) : 0;
+// Partial outputs of the key chunks (bf16 path only).
+static int64_t partial_bytes(qi_dtype dtype, int64_t n_q, int32_t n_head) {
+  return dtype == QI_BF16 ? attn_f16_partial_bytes(n_q, n_head) : 0;
 }
+
 
 int64_t qi_attn_full_workspace_bytes(const qi_layout* layout, qi_dtype dtype, int32_t n_head) {
   LayoutInfo li;
@@ -212,13 +224,16 @@ int64_t qi_attn_full_workspace_bytes(const qi_layout* layout, qi_dtype dtype, in
   // prefix rows and target rows, each padded to whole 64-key tiles
   const int64_t r = rows_bytes(dtype, rows64(li.P) + rows64(li.T), n_head);
   if (r < 0) return r;
-  return r + partial_bytes(dtype, li.T, li.T, n_head);   // partials of the target rows only
+  // the prefix and target launches run one after the other and share the partial outputs
+  const int64_t pt = partial_bytes(dtype, li.T, n_head);
+  const int64_t pp = attn_prefix_tiles_equal(li.tab, li.P, li.T) ? partial_bytes(dtype, li.P, n_head) : 0;
+  return r + (pt > pp ? pt : pp);
 }
 
 int64_t qi_attn_cached_workspace_bytes(qi_dtype dtype, int64_t T, int32_t n_head) {
   const int64_t r = rows_bytes(dtype, rows64(T), n_head);
   if (r < 0) return r;
-  return r + partial_bytes(dtype, T, T, n_head);
+  return r + partial_bytes(dtype, T, n_head);
 }
 
 int64_t qi_kvcache_bytes(qi_dtype cache_dtype, int32_t n_layers, int32_t n_head, int64_t p_cap) {

@@ -64,37 +64,40 @@ struct AttnArgs {
   int64_t q_row0;
   float scale_log2;    // softmax scale * log2(e) (fp16 path) or softmax scale (fp32 path)
   int32_t masked;
-  // fp16 path: the key tiles of every query tile are cut into n_split consecutive chunks of
-  // split_tiles tiles; with n_split > 1 each chunk writes an unnormalised partial output and its
-  // (max, sum) to part_o / part_ml, and a combine kernel produces o.
-  int32_t n_split, split_tiles;
-  float* part_o;       // [n_split][n_q][n_head][128]
-  float* part_ml;      // [n_split][n_q][n_head][2]
-  // Work schedule of the fp16 path.  xcd_units > 0: the grid is read as 8 interleaved runs (run
-  // x = the blocks with blockIdx % 8 == x, which the hardware places on XCD x) of xcd_units
-  // query-tile units each (unit u = head * n_qt + query tile); the first xcd_whole units of a
-  // run are single workgroups over all their key tiles, each later unit is cut into n_split
-  // key chunks (one workgroup each).  xcd_units == 0: every unit is cut into n_split chunks.
-  int32_t xcd_units, xcd_whole;
-  int32_t reverse_qt;  // masked kernel: visit a head's query tiles last-first (longest rows first)
+  // Work schedule of the fp16 path over the U = n_qt * n_head query-tile units (unit u = head *
+  // n_qt + query tile).  xcd_sched = 0: one workgroup per unit, all key tiles (for units of
+  // unequal cost, visited longest first with reverse_qt).  xcd_sched = 1 (units of equal cost):
+  // run x = the blocks with blockIdx % 8 == x (which the hardware places on XCD x) owns U / 8
+  // consecutive units (the first U % 8 runs one more); its first xcd_whole units are whole, each
+  // later unit is cut into n_split chunks of split_tiles key tiles, and each chunk writes an
+  // unnormalised partial output and its (max, sum) for a combine kernel.  launch_attn_f16 fills
+  // n_split, split_tiles and xcd_whole from attn_f16_schedule.
+  int32_t xcd_sched, reverse_qt;
+  int32_t n_split, split_tiles, xcd_whole;
+  float* part_o;       // [chunked unit][chunk][256 rows][128]
+  float* part_ml;      // [chunked unit][chunk][256 rows][2]
   SegTable segs;
 };
 
-// The fp16 path's schedule for a target of T tokens and n_head heads (see AttnArgs).
+// The fp16 path's schedule (xcd_sched = 1, see AttnArgs) for n_q query rows and n_head heads.
 struct AttnSched {
-  int32_t n_split, xcd_units, xcd_whole;
+  int32_t n_split;      // key chunks of each chunked unit (1: every unit whole)
+  int32_t xcd_whole;    // whole units at the start of each run
+  int32_t tail_units;   // chunked units over all runs (0 when n_split == 1)
+  int64_t blocks;       // workgroups (8 runs of equal length; surplus blocks exit at once)
 };
-AttnSched attn_f16_schedule(int64_t T, int32_t n_head);
+AttnSched attn_f16_schedule(int64_t n_q, int32_t n_head);
 
 // Query rows per workgroup of the fp16 path (the tile height reported by qi_attn_tile_shape).
 constexpr int kAttnF16TileQ = 256;
 
-// Number of key chunks of the fp16 path for a sequence whose target has T tokens and n_head
-// heads.  Step 1 and the cached steps both use the layout's T, so a target row is processed in
-// the same chunks (and gets the same bits) in both.
-int attn_f16_splits(int64_t T, int32_t n_head);
-// Workspace bytes of the partial outputs for n_q rows.
+// Workspace bytes of the partial outputs of an xcd_sched launch over n_q rows (0 without
+// chunks).  The schedule depends on n_q and n_head only, so the target rows of step 1 and of a
+// cached step are cut into the same chunks and get the same bits.
 int64_t attn_f16_partial_bytes(int64_t n_q, int32_t n_head);
+// Whether the prefix query tiles of step 1 over layout `tab` (P prefix rows, T target rows) all
+// end at the same key tile, so the prefix launch can take the xcd_sched schedule.
+bool attn_prefix_tiles_equal(const SegTable& tab, int64_t P, int64_t T);
 
 // y = x W^T with an epilogue (qi_epilogue): x bf16 [M][ldx], W bf16 [N][K] (K % 64 == 0).
 struct GemmArgs {

@@ -172,8 +172,9 @@ int qi_attn_tile_shape(qi_dtype dtype, int32_t* tile_q, int32_t* tile_k);
 
 /* Workspace bytes needed by qi_attn_blockcausal_full for `layout` (with or without a cache) and
  * by qi_attn_target_cached for T target tokens: prepared K/V rows plus, for bf16, the partial
- * outputs of the key chunks that the target's query rows are split into when the target alone
- * would not fill whole rounds of the GPU (the prefix rows of step 1 always run unchunked).
+ * outputs of the key chunks that the query tiles left over after whole rounds of the GPU are
+ * split into (target rows always; prefix rows of step 1 when every prefix tile sees the same
+ * key tiles, as in an unmasked layout; otherwise the prefix rows run unchunked).
  * Negative = error status. */
 int64_t qi_attn_full_workspace_bytes(const qi_layout* layout, qi_dtype dtype, int32_t n_head);
 int64_t qi_attn_cached_workspace_bytes(qi_dtype dtype, int64_t T, int32_t n_head);

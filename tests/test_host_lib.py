@@ -120,15 +120,24 @@ def test_tile_shape_and_sizes():
     assert Q.qi_attn_tile_shape(Q.QI_BF16) == (256, 64)
     assert Q.qi_attn_tile_shape(Q.QI_F32) == (1, 64)
     L3 = Q.make_layout(qin.WORKLOADS["cfg3"].segments)
+    PART = 256 * 130 * 4   # fp32 partials of one chunk of one query tile: 256 rows x (128 values + max + sum)
     # 4096-token target: 16 x 24 = 384 query tiles (48 per XCD): per XCD 32 whole, 16 in 2 key
-    # chunks: K/V fp16 rows plus 2 chunks of fp32 partials (128 values + max + sum)
-    # (step 1 chunks only the target rows; the prefix rows run whole)
-    assert Q.qi_attn_full_workspace_bytes(L3, Q.QI_BF16, 24) == 2 * 24 * 21504 * 128 * 2 + 2 * 4096 * 24 * 130 * 4
-    assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, 4096, 24) == 2 * 24 * 4096 * 128 * 2 + 2 * 4096 * 24 * 130 * 4
-    # config[1]: 4 x 24 = 96 units (12 per XCD, none whole) -> 5 key chunks
+    # chunks: K/V fp16 rows plus the partials of the 128 chunked tiles
+    # (the block-causal prefix rows of step 1 run whole)
+    assert Q.qi_attn_full_workspace_bytes(L3, Q.QI_BF16, 24) == 2 * 24 * 21504 * 128 * 2 + 128 * 2 * PART
+    assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, 4096, 24) == 2 * 24 * 4096 * 128 * 2 + 128 * 2 * PART
+    # config[1]: 4 x 24 = 96 units (12 per XCD, none whole) -> all in 5 key chunks
     L1 = Q.make_layout(qin.WORKLOADS["cfg1"].segments)
-    assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, 1024, 24) == 2 * 24 * 1024 * 128 * 2 + 5 * 1024 * 24 * 130 * 4
-    assert Q.qi_attn_full_workspace_bytes(L1, Q.QI_BF16, 24) == 2 * 24 * 2304 * 128 * 2 + 5 * 1024 * 24 * 130 * 4
+    assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, 1024, 24) == 2 * 24 * 1024 * 128 * 2 + 96 * 5 * PART
+    assert Q.qi_attn_full_workspace_bytes(L1, Q.QI_BF16, 24) == 2 * 24 * 2304 * 128 * 2 + 96 * 5 * PART
+    # unmasked Edit-Plus (text 512 + target + 2 references of 64 x 64): the 8,704 prefix rows
+    # (34 x 24 = 816 tiles, 102 per XCD: 96 whole, 6 in 5 chunks) share the partials with the
+    # target rows, which need more
+    Lv = Q.make_layout(qin.V1_WORKLOADS["editplus_v1"].segments, attention=Q.QI_ATTN_FULL)
+    assert Q.qi_layout_tokens(Lv)[1:] == (8704, 4096)
+    assert Q.qi_attn_full_workspace_bytes(Lv, Q.QI_BF16, 24) == 2 * 24 * 12800 * 128 * 2 + 128 * 2 * PART
+    # with 2 heads the prefix partials are the larger: 68 tiles (8 or 9 per XCD, all in 7 chunks)
+    assert Q.qi_attn_full_workspace_bytes(Lv, Q.QI_BF16, 2) == 2 * 2 * 12800 * 128 * 2 + 68 * 7 * PART
     # long targets stay whole: 16384 tokens x 24 heads = 1536 query tiles (six rounds)
     assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, 16384, 24) == 2 * 24 * 16384 * 128 * 2
     # workspace rows are padded to whole 64-key tiles for both dtypes
