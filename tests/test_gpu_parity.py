@@ -396,3 +396,55 @@ def test_full_attention_full_size_sampled(name):
     qr = O.rotate(c.q.f64[rows], c.cos[rows], c.sin[rows])
     kr = O.rotate(c.k.f64, c.cos, c.sin)
     check_close(to_np(o[rows]), O.attention(qr, kr, c.v.f64), "bf16", f"{name} sampled rows")
+
+
+# ---------------------------------------------------------------------------------------------
+# the work schedule: query-tile unit counts that take each path of the per-XCD schedule
+# (runs of unequal length with idle blocks, whole rounds plus chunked remainders, remainders
+# run whole, many chunks per unit), on sampled rows including the first and last row of every
+# query tile; the step-1 target rows of the same shapes equal the cached step bit for bit
+# ---------------------------------------------------------------------------------------------
+
+SCHED_CASES = [
+    # name, target grid, heads: units = ceil(T / 256) * heads
+    ("u12_ragged", (31, 33), 3),      # 12 units: runs of 2 and 1, all in 8 chunks, last tile 255 rows
+    ("u33", (16, 16), 33),            # 33 units: runs of 5 and 4, 6 chunks each
+    ("u270", (60, 64), 18),           # 270 units: 32 whole per run, then runs of 2 and 1 in 8 chunks
+    ("u505_whole_tail", (101, 256), 5),   # 505 units: 32 whole, then 32 or 31 more run whole
+    ("u567", (115, 180), 7),          # 567 units: 64 whole per run, then 7 each in 4 chunks
+]
+
+
+@pytest.mark.parametrize("name,grid,heads", SCHED_CASES)
+def test_schedule_unit_counts(name, grid, heads):
+    segs = (qin.text(64), qin.image(8, 8, 1), qin.image(grid[0], grid[1], 0))
+    wl = qin.small_workload(name, segs, n_head=heads, dtype="bf16")
+    c = Case(wl)
+    P, T = c.P, c.T
+    n_qt = (T + 255) // 256
+    say(f"schedule {name}: T={T} heads={heads} units={n_qt * heads}")
+    L, att = make(wl)
+    cache = rt.KVCache(1, heads, P, Q.QI_BF16, DEV)
+    o1 = att.full(c.qd, c.kd, c.vd, cache=cache)
+    ot = att.cached(c.qd[P:], c.kd[P:], c.vd[P:], cache, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(ot, o1[P:]), "cached step != step-1 target rows"
+    tiles = np.arange(n_qt) * 256
+    rows = np.unique(np.concatenate([tiles, np.minimum(tiles + 255, T - 1), sample_rows(0, T, 32, 5)]))
+    qr = O.rotate(c.q.f64[P:][rows], c.cos[P:][rows], c.sin[P:][rows])
+    kr = O.rotate(c.k.f64, c.cos, c.sin)
+    check_close(to_np(ot[rows]), O.attention(qr, kr, c.v.f64), "bf16", f"{name} target rows")
+
+
+def test_schedule_full_attention_chunked_prefix():
+    # unmasked: the 2,100 leading rows (9 tiles x 3 heads = 27 units, runs of 4 and 3) and the
+    # 900 trailing rows (12 units) both run in 8 key chunks and share the partial outputs
+    segs = (qin.text(100), qin.image(40, 50, 0), qin.image(30, 30, 1))
+    wl = qin.small_workload("full_chunked_prefix", segs, n_head=3, dtype="bf16")
+    c = Case(wl)
+    L = rt.Layout(wl.segments, DEV, attention=Q.QI_ATTN_FULL)
+    att = rt.Attention(L, wl.n_head, Q.QI_BF16, DEV)
+    o = att.full(c.qd, c.kd, c.vd)
+    torch.cuda.synchronize()
+    ref, _ = O.step1(c.q.f64, c.k.f64, c.v.f64, wl.segments, c.cos, c.sin, None, None, full=True)
+    check_close(to_np(o), ref, "bf16", "full attention, chunked prefix")
