@@ -30,7 +30,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
-constexpr int GBK = 64;    // reduction slice per LDS stage
+constexpr int GBK = 32;    // reduction slice per LDS stage
+constexpr int GSTAGES = 4; // LDS stages: copies run three slices ahead of the MFMAs
 
 __device__ __forceinline__ uint32_t to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
@@ -49,37 +50,48 @@ __device__ __forceinline__ int xcd_order(int bid, int n) {
   return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + slot;
 }
 
+// s_waitcnt vmcnt(N) lgkmcnt(0): at most N of this wave's buffer -> LDS copies still in flight and
+// none of its LDS reads (expcnt left free)
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
 __device__ __forceinline__ void load_lds16(const void* src, void* dst_wave_base) {
   __builtin_amdgcn_global_load_lds((const glb_void*)src, (lds_void*)dst_wave_base, 16, 0, 0);
 }
 
-// Rows of a stage tile are 128 bytes (8 chunks of 16 bytes); chunk c of row r sits at chunk
-// position c ^ ((r >> 1) & 7), so the 16 rows a quarter-wave reads at one logical chunk land in
-// 16 distinct bank groups.
-__device__ __forceinline__ int gswz(int r) { return (r >> 1) & 7; }
+// Rows of a stage tile are 64 bytes (4 chunks of 16 bytes); chunk c of row r sits at chunk
+// position c ^ (((r >> 2) ^ (r >> 1)) & 3), so the rows that 16 lanes (or 8 lanes) read at one
+// logical chunk in one LDS cycle land in 16 (or 8) distinct 16-byte bank groups.
+__device__ __forceinline__ int gswz(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
 
-// ---- large-tile GEMM: 256 x BN workgroup tiles, one wavefront per SIMD ------------------------
-// Four waves in a 2 x 2 grid, each owning 128 tokens x BN/2 features as 4 x (BN/64) blocks of
-// 32 x 32 (accumulators in the accumulation registers).  Per reduction step of 16 every X operand
-// read from LDS feeds BN/64 MFMAs and every W operand four: half the LDS bytes per MFMA of 64 x 64
-// wave tiles, which at two workgroups per CU would need about all of the LDS bandwidth.  Stage tiles are
-// copied by MUBUF buffer -> LDS loads (exact LDS waits while copies are in flight) into 128-byte
-// rows with the (row/2)-XOR chunk swizzle; rows past M or N fall outside the buffer resources and
-// are not read (their results are never stored).
+// ---- large-tile GEMM: 256 x BN workgroup tiles, two wavefronts per SIMD ----------------------
+// Eight waves in a 4 x 2 grid, each owning 64 tokens x BN/2 features as 2 x (BN/64) blocks of
+// 32 x 32 (128 accumulators at BN = 256, so two waves fit a SIMD and each hides the other's LDS
+// waits).  The reduction runs in slices of 32 through four LDS stages (4 x 32 KB at BN = 256):
+// the copies of slice kt + 4 are issued in slice kt, into the stage slice kt has just been read
+// from, so each copy has three slices of MFMA work to land in.  Stage tiles are copied by MUBUF
+// buffer -> LDS loads (exact waits while copies are in flight) into 64-byte rows with the chunk
+// swizzle above; rows past M or N fall outside the buffer resources and are not read (their
+// results are never stored).
 constexpr int BBM = 256;
 
 template <int EPI, int BN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_big(GemmArgs a) {
-  constexpr int WN = BN / 2;              // features per wave
-  constexpr int NB = WN / 32;             // 32-feature blocks per wave
-  constexpr int MB = 4;                   // 32-token blocks per wave
-  constexpr int XT = BBM * GBK, WT = BN * GBK;
-  constexpr int WROWS = BN / 4;           // W rows each wave copies per stage
-  constexpr int NXC = 8, NWC = WROWS / 8; // copies of 1 KB (8 rows) per wave and stage
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (XT + WT)];
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_big(GemmArgs a) {
+  constexpr int WTM = 64, WTN = BN / 2;    // wave tile
+  constexpr int MB = WTM / 32, NB = WTN / 32;
+  constexpr int XT = BBM * GBK, WT = BN * GBK, ST = XT + WT;
+  constexpr int NXC = 2;                   // X copies of 1 KB (16 rows) per wave and stage
+  constexpr int NWT = BN / 16;             // W copies per stage, spread over the 8 waves
+  constexpr int NWC = (NWT + 7) / 8;       // most W copies of one wave
+  __shared__ __attribute__((aligned(16))) __bf16 smem[GSTAGES * ST];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;
+  // this wave's W copies (NWC or NWC - 1; always NWC when the copies split evenly)
+  const int nwc = NWT % 8 == 0 ? NWC : (NWT - wave + 7) / 8;
 
   // tile order: groups of 8 token tiles sweep all feature tiles, so that workgroups running at
   // the same time share both X and W panels in L2; the groups are spread over the XCDs
@@ -93,42 +105,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)(a.M * a.ldx * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, (short)0, (int)(a.N * a.K * 2), 0x00020000);
-  // lane i of copy j: row (within the wave's rows) 8j + i/8, chunk position i%8.  (Arrays touched
-  // by the lambdas below have fixed sizes: with sizes that depend on BN the host compiler silently
-  // drops the kernel instance and its launch stub.)
-  int xo[8], wo[8];
+  // lane i of a copy of rows [r0, r0 + 16): row r0 + i/4, chunk position i%4.  X copy j of wave w
+  // covers rows 32w + 16j, W copy j rows 16(w + 8j).  (Arrays touched by the lambdas below have
+  // fixed sizes: with sizes that depend on BN the host compiler silently drops the kernel instance
+  // and its launch stub.)
+  int xo[2], wo[2];
 #pragma unroll
   for (int j = 0; j < NXC; ++j) {
-    const int row = 64 * wave + 8 * j + (lane >> 3);
-    xo[j] = (int)((m0 + row) * a.ldx * 2) + 16 * ((lane & 7) ^ gswz(row));
+    const int row = 32 * wave + 16 * j + (lane >> 2);
+    xo[j] = (int)((m0 + row) * a.ldx * 2) + 16 * ((lane & 3) ^ gswz(row));
   }
 #pragma unroll
   for (int j = 0; j < NWC; ++j) {
-    const int row = WROWS * wave + 8 * j + (lane >> 3);
-    wo[j] = (int)((n0 + row) * a.K * 2) + 16 * ((lane & 7) ^ gswz(row));
+    const int row = 16 * (wave + 8 * j) + (lane >> 2);
+    wo[j] = (int)((n0 + row) * a.K * 2) + 16 * ((lane & 3) ^ gswz(row));
   }
-  auto copy_x = [&](int kt, int st, int j) {
-    __bf16* dst = smem + st * (XT + WT) + (64 * wave + 8 * j) * GBK;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)dst, 16, xo[j], kt * GBK * 2, 0, 0);
+  // all of this wave's copies of slice kt into stage st
+  auto copy_slice = [&](int kt, int st) {
+#pragma unroll
+    for (int j = 0; j < NXC; ++j) {
+      __bf16* dst = smem + st * ST + (32 * wave + 16 * j) * GBK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)dst, 16, xo[j], kt * GBK * 2, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NWC; ++j) {
+      if (j < nwc) {
+        __bf16* dst = smem + st * ST + XT + 16 * (wave + 8 * j) * GBK;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)dst, 16, wo[j], kt * GBK * 2, 0, 0);
+      }
+    }
   };
-  auto copy_w = [&](int kt, int st, int j) {
-    __bf16* dst = smem + st * (XT + WT) + XT + (WROWS * wave + 8 * j) * GBK;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)dst, 16, wo[j], kt * GBK * 2, 0, 0);
-  };
-  // operands of reduction step kk from stage st
-  auto read_ops = [&](int st, int kk, bf8 (&xf)[4], bf8 (&wf)[4]) {
-    const __bf16* X = smem + st * (XT + WT);
+  // operands of reduction step kk (of 2) from stage st
+  auto read_ops = [&](int st, int kk, bf8 (&xf)[2], bf8 (&wf)[4]) {
+    const __bf16* X = smem + st * ST;
     const __bf16* W = X + XT;
 #pragma unroll
     for (int b = 0; b < MB; ++b) {
-      const int r = 128 * wm + 32 * b + l32;
+      const int r = WTM * wm + 32 * b + l32;
       xf[b] = *(const bf8*)(X + r * GBK + 8 * ((2 * kk + g) ^ gswz(r)));
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int r = WN * wn + 32 * b + l32;
+      const int r = WTN * wn + 32 * b + l32;
       wf[b] = *(const bf8*)(W + r * GBK + 8 * ((2 * kk + g) ^ gswz(r)));
     }
+  };
+  auto mfmas = [&](f32x16 (&acc)[MB][NB], const bf8 (&xf)[2], const bf8 (&wf)[4]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], xf[mb], acc[mb][nb], 0, 0, 0);
+  };
+  // "slice kt + 1 has landed": at most the copies of slices kt + 2 and kt + 3 still in flight
+  // (every slice issues the same copies: slices past the end re-copy the last slice into the
+  // stage just read, which nothing reads again)
+  auto wait_next = [&]() {
+    if (nwc == NWC) wait_copies<2 * (NXC + NWC)>();
+    else wait_copies<2 * (NXC + NWC - 1)>();
   };
 
   f32x16 acc[MB][NB];
@@ -140,50 +174,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nkt = (int)(a.K / GBK);
+  auto last = [&](int k) { return k < nkt ? k : nkt - 1; };
 #pragma unroll
-  for (int j = 0; j < NXC; ++j) copy_x(0, 0, j);
-#pragma unroll
-  for (int j = 0; j < NWC; ++j) copy_w(0, 0, j);
+  for (int i = 0; i < GSTAGES; ++i) copy_slice(last(i), i);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  bf8 xf0[2], wf0[4], xf1[2], wf1[4];
+  read_ops(0, 0, xf0, wf0);
   for (int kt = 0; kt < nkt; ++kt) {
-    const int st = kt & 1;
-    const int kn = kt + 1 < nkt ? kt + 1 : kt;   // the last step re-copies its own tile into the free stage
-    bf8 xf[2][4], wf[2][4];
-    read_ops(st, 0, xf[0], wf[0]);
-#pragma unroll
-    for (int kk = 0; kk < GBK / 16; ++kk) {
-      // operands of step kk + 1 and a quarter of the next stage's copies, then this step's MFMAs
-      if (kk + 1 < GBK / 16) read_ops(st, kk + 1, xf[(kk + 1) & 1], wf[(kk + 1) & 1]);
-#pragma unroll
-      for (int j = 0; j < NXC / 4; ++j) copy_x(kn, st ^ 1, kk * (NXC / 4) + j);
-#pragma unroll
-      for (int j = 0; j < (NWC + 3) / 4; ++j)
-        if (kk * ((NWC + 3) / 4) + j < NWC) copy_w(kn, st ^ 1, kk * ((NWC + 3) / 4) + j);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[kk & 1][nb], xf[kk & 1][mb], acc[mb][nb], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
+    const int st = kt & (GSTAGES - 1);
+    read_ops(st, 1, xf1, wf1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(acc, xf0, wf0);
+    __builtin_amdgcn_sched_barrier(0);
+    // slice kt + 1 has landed for every wave, and every wave holds its operands of slice kt:
+    // stage st takes the copies of slice kt + 4
+    wait_next();
     __syncthreads();
+    copy_slice(last(kt + GSTAGES), st);
+    read_ops((kt + 1) & (GSTAGES - 1), 0, xf0, wf0);   // (unused after the last slice)
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(acc, xf1, wf1);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  // the re-copies of the last slices are still in flight: they land before the workgroup's LDS
+  // can pass to another workgroup
+  __builtin_amdgcn_s_waitcnt(0);
 
-  // epilogue: acc[mb][nb][r] = y[m][n], m = m0 + 128wm + 32mb + l32,
-  // n = n0 + WN*wn + 32nb + 8(r/4) + 4g + r%4
+  // epilogue: acc[mb][nb][r] = y[m][n], m = m0 + 64wm + 32mb + l32,
+  // n = n0 + WTN*wn + 32nb + 8(r/4) + 4g + r%4
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    const int64_t m = m0 + 128 * wm + 32 * mb + l32;
+    const int64_t m = m0 + WTM * wm + 32 * mb + l32;
     if (m >= a.M) continue;
     if constexpr (EPI == QI_EPI_SWIGLU) {
       // weight rows in blocks of 64: 32 gate rows, then the 32 up rows of the same features
 #pragma unroll
       for (int blk = 0; blk < NB / 2; ++blk) {
-        if (n0 + WN * wn + 64 * blk >= a.N) continue;
-        const int64_t f0 = (n0 + WN * wn + 64 * blk) / 2;
+        if (n0 + WTN * wn + 64 * blk >= a.N) continue;
+        const int64_t f0 = (n0 + WTN * wn + 64 * blk) / 2;
         __bf16* op = (__bf16*)a.out + m * a.ldo + f0 + 4 * g;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
@@ -204,7 +233,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     } else {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int64_t nbase = n0 + WN * wn + 32 * nb + 4 * g;
+        const int64_t nbase = n0 + WTN * wn + 32 * nb + 4 * g;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int64_t n = nbase + 8 * r4;
@@ -335,7 +364,7 @@ namespace {
 // Kernel template instances are launched from plain functions: instantiated only inside another
 // function template, their host stubs are not emitted by this compiler.
 #define QI_LAUNCH_BIG(EPI_, BN_) \
-  hipLaunchKernelGGL((k_gemm_big<EPI_, BN_>), dim3(blocks), dim3(256), 0, s, a)
+  hipLaunchKernelGGL((k_gemm_big<EPI_, BN_>), dim3(blocks), dim3(512), 0, s, a)
 
 hipError_t launch_big(const GemmArgs& a, int epi, int bn, hipStream_t s) {
   const unsigned blocks = (unsigned)(((a.M + BBM - 1) / BBM) * ((a.N + bn - 1) / bn));
@@ -377,7 +406,7 @@ hipError_t launch_big(const GemmArgs& a, int epi, int bn, hipStream_t s) {
 int gemm_config(int64_t M, int64_t N, int epi) {
   // Feature width BN of the 256 x BN tiles: the least tile area per CU over whole rounds of 256
   // workgroups (one per CU), weighted by the LDS bytes per MFMA of the tile (per wave and step,
-  // 4 + BN/64 operand reads for 4 * BN/64 MFMAs: 0.50, 0.58, 0.75 for 256, 192, 128; measured
+  // 2 + BN/64 operand reads for 2 * BN/64 MFMAs: 0.75, 0.83, 1.0 KB for 256, 192, 128; measured
   // rates follow this order when the rounds are equal).  E.g. 4096 x 3072 is exactly 256 tiles of
   // 256 x 192 but 192 tiles of 256 x 256; 4096 x 16384 fills four rounds of 256 x 256.
   int best = 256;
