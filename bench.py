@@ -65,6 +65,19 @@ def traffic_from_profile():
     return float(m_b.group(1))
 
 
+def sclk_from_profile():
+    """Median shader clock (GHz) during the attention kernel from the committed counter summary,
+    if it was taken on this exact kernel source (else None)."""
+    if not os.path.exists(PROFILE):
+        return None
+    txt = open(PROFILE).read()
+    m_h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_c = re.search(r"sclk_median_ghz:\s*([0-9.]+)", txt)
+    if not m_h or not m_c or m_h.group(1) != kernel_hash():
+        return None
+    return float(m_c.group(1))
+
+
 def pct(sorted_vals, q):
     """q-th percentile (nearest rank) of an ascending list."""
     i = min(len(sorted_vals) - 1, max(0, int(round(q / 100.0 * (len(sorted_vals) - 1)))))
@@ -323,8 +336,7 @@ def main():
     log(f"timed {args.steps} steps in {wall:.3f} s; attention kernel {kern_ms / max(n_launch, 1):.4f} ms/launch")
 
     flops_launch = 4.0 * 128 * H * T * (P + T)
-    ws_rows = 2 * H * T * 128 * 2
-    n_chunks = max(1, (Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, T, H) - ws_rows) // (T * H * 130 * 4))
+    n_chunks, whole_per_xcd, chunked_tiles = Q.qi_attn_schedule(T, H)
     value = flops_launch * NL * args.steps / wall / 1e12
     avg_ms = kern_ms / max(n_launch, 1)
     achieved = flops_launch / (avg_ms * 1e-3) / 1e12
@@ -368,13 +380,22 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic_from_profile(),
                      "kernel": "k_attn_f16<false> + k_combine (one attention call)" if n_chunks > 1 else "k_attn_f16<false>",
-                     "key_chunks": n_chunks, "kernel_ms_per_launch": round(avg_ms, 4),
+                     "schedule": {"query_tiles": -(-T // 256) * H, "whole_tiles_per_xcd": whole_per_xcd,
+                                  "chunked_tiles": chunked_tiles, "key_chunks": n_chunks},
+                     "kernel_ms_per_launch": round(avg_ms, 4),
                      "flops_per_launch": flops_launch, "launches": n_launch,
                      # per-call duration percentiles (p95/p99: the slow tail) and the TFLOP/s at each
                      "per_call_ms": {q: round(pct(per_call, int(q[1:])), 4) for q in ("p50", "p95", "p99")},
                      "per_call_tflops": {q: round(flops_launch / (pct(per_call, int(q[1:])) * 1e-3) / 1e12, 1)
                                          for q in ("p50", "p95", "p99")}},
     }
+    sclk = sclk_from_profile()
+    if sclk:
+        # the same fraction against the MFMA rate at the clock the chip actually ran the kernel at
+        # (256 CUs x 4 SIMDs x 1,024 flop per clock; from the committed counter summary)
+        peak_at_sclk = 256 * 4096 * sclk * 1e9 / 1e12
+        res["roofline"]["sclk_ghz_measured"] = sclk
+        res["roofline"]["frac_at_measured_sclk"] = round(achieved / peak_at_sclk, 4)
     res["config"].update(extra)
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")

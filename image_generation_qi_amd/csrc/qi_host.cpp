@@ -202,6 +202,16 @@ int qi_attn_tile_shape(qi_dtype dtype, int32_t* tile_q, int32_t* tile_k) {
   return QI_OK;
 }
 
+int qi_attn_schedule(int64_t n_q, int32_t n_head, int32_t* key_chunks, int32_t* whole_per_xcd,
+                     int32_t* chunked_tiles) {
+  if (n_q < 0 || n_head < 1 || !key_chunks || !whole_per_xcd || !chunked_tiles) return QI_ERR_ARG;
+  const AttnSched sc = attn_f16_schedule(n_q, n_head);
+  *key_chunks = sc.n_split;
+  *whole_per_xcd = sc.xcd_whole;
+  *chunked_tiles = sc.tail_units;
+  return QI_OK;
+}
+
 // K and V rows, [n_head][rows][128]: fp16 for bf16 attention, fp32 for fp32 attention (callers
 // pass rows already padded to whole 64-key tiles)
 static int64_t rows_bytes(qi_dtype dtype, int64_t rows, int32_t n_head) {

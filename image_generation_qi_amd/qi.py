@@ -75,6 +75,7 @@ _SIGS = {
     "qi_rope3d_tables": (c_int, [POINTER(qi_layout), c_void_p, c_void_p]),
     "qi_blockmap": (c_int, [POINTER(qi_layout), c_int32, c_int32, c_void_p]),
     "qi_attn_tile_shape": (c_int, [c_int, POINTER(c_int32), POINTER(c_int32)]),
+    "qi_attn_schedule": (c_int, [c_int64, c_int32, POINTER(c_int32), POINTER(c_int32), POINTER(c_int32)]),
     "qi_attn_full_workspace_bytes": (c_int64, [POINTER(qi_layout), c_int, c_int32]),
     "qi_attn_cached_workspace_bytes": (c_int64, [c_int, c_int64, c_int32]),
     "qi_kvcache_bytes": (c_int64, [c_int, c_int32, c_int32, c_int64]),
@@ -217,6 +218,13 @@ def qi_attn_tile_shape(dtype: int):
     tq, tk = c_int32(), c_int32()
     check(lib().qi_attn_tile_shape(dtype, ctypes.byref(tq), ctypes.byref(tk)), "qi_attn_tile_shape")
     return tq.value, tk.value
+
+
+def qi_attn_schedule(n_q: int, n_head: int):
+    """(key chunks per cut query tile, whole tiles per XCD run, cut tiles) of a bf16 launch."""
+    s, w, c = c_int32(), c_int32(), c_int32()
+    check(lib().qi_attn_schedule(n_q, n_head, ctypes.byref(s), ctypes.byref(w), ctypes.byref(c)), "qi_attn_schedule")
+    return s.value, w.value, c.value
 
 
 def qi_attn_full_workspace_bytes(layout: qi_layout, dtype: int, n_head: int) -> int:

@@ -170,6 +170,16 @@ int qi_blockmap(const qi_layout* layout, int32_t tile_q, int32_t tile_k, uint8_t
 /* Query-tile and key-tile sizes of the attention kernel for an I/O dtype. */
 int qi_attn_tile_shape(qi_dtype dtype, int32_t* tile_q, int32_t* tile_k);
 
+/* Work schedule of a bf16 attention launch over n_q query rows and n_head heads whose query tiles
+ * all see the same keys (every cached step, the target rows of step 1, unmasked layouts): the
+ * ceil(n_q / 256) * n_head query tiles are spread over the 8 XCDs; each XCD runs whole rounds of
+ * one tile per CU and cuts only its remaining tiles into key chunks, merged afterwards.  Host
+ * query (no GPU): *key_chunks = chunks per cut tile (1: no tile is cut), *whole_per_xcd = whole
+ * tiles at the start of each XCD's run, *chunked_tiles = cut tiles over all XCDs.  QI_OK, or
+ * QI_ERR_ARG for n_q < 0, n_head < 1 or a null output pointer. */
+int qi_attn_schedule(int64_t n_q, int32_t n_head, int32_t* key_chunks, int32_t* whole_per_xcd,
+                     int32_t* chunked_tiles);
+
 /* Workspace bytes needed by qi_attn_blockcausal_full for `layout` (with or without a cache) and
  * by qi_attn_target_cached for T target tokens: prepared K/V rows plus, for bf16, the partial
  * outputs of the key chunks that the query tiles left over after whole rounds of the GPU are

@@ -119,6 +119,13 @@ def test_blockmap_bit_exact(name, tiles):
 def test_tile_shape_and_sizes():
     assert Q.qi_attn_tile_shape(Q.QI_BF16) == (256, 64)
     assert Q.qi_attn_tile_shape(Q.QI_F32) == (1, 64)
+    # schedules: (key chunks, whole tiles per XCD run, chunked tiles)
+    assert Q.qi_attn_schedule(4096, 24) == (2, 32, 128)     # 384 tiles: 48 per XCD
+    assert Q.qi_attn_schedule(1024, 24) == (5, 0, 96)       # 96 tiles: 12 per XCD, all chunked
+    assert Q.qi_attn_schedule(16384, 24) == (1, 192, 0)     # six whole rounds
+    assert Q.qi_attn_schedule(8704, 24) == (5, 96, 48)      # 816 tiles: 102 per XCD
+    assert Q.qi_attn_schedule(101 * 256, 5) == (1, 32, 0)   # 505 tiles: the remaining 32 / 31 run whole
+    assert Q.qi_attn_schedule(0, 24) == (1, 0, 0)
     L3 = Q.make_layout(qin.WORKLOADS["cfg3"].segments)
     PART = 256 * 130 * 4   # fp32 partials of one chunk of one query tile: 256 rows x (128 values + max + sum)
     # 4096-token target: 16 x 24 = 384 query tiles (48 per XCD): per XCD 32 whole, 16 in 2 key
@@ -257,6 +264,9 @@ def test_other_entry_points_reject():
     assert Q.qi_rope3d_positions(L, None) == Q.QI_ERR_ARG
     assert Q.qi_blockmap(L, 0, 64, np.zeros(4, np.uint8)) == Q.QI_ERR_ARG
     assert Q.lib().qi_attn_tile_shape(Q.QI_F16, ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32())) == Q.QI_ERR_DTYPE
+    assert Q.lib().qi_attn_schedule(-1, 24, ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32())) == Q.QI_ERR_ARG
+    assert Q.lib().qi_attn_schedule(4096, 0, ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32())) == Q.QI_ERR_ARG
+    assert Q.lib().qi_attn_schedule(4096, 24, None, ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32())) == Q.QI_ERR_ARG
 
 
 def test_full_attention_layout_maps_and_positions():
