@@ -428,6 +428,90 @@ def dit_layer(x, L, mods, segments, cos_t, sin_t, cache=None, eps: float = 1e-6,
     return x, new_cache
 
 
+# ------------------------------------------------------------------------------------------------
+# the v1 / Edit dual-stream block around the unmasked joint attention
+# ------------------------------------------------------------------------------------------------
+
+def layer_norm(x, eps: float = 1e-6):
+    """LayerNorm over the last axis without affine parameters: (x - mean) / sqrt(var + eps) with
+    the biased variance ([EDIT] section 5.2: the v1 block's norm1 / norm2 have elementwise_affine
+    off, eps 1e-6)."""
+    x = np.asarray(x, np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps)
+
+
+def linear_bias(x, w, b):
+    """y = x W^T + b (a Linear with its bias: every Linear of the v1 block carries one, as the
+    per-block parameter table of [EDIT] counts them)."""
+    y = linear(x, w)
+    return y if b is None else y + np.asarray(b, np.float64)
+
+
+def v1_block(x_txt, x_img, temb, B, cos_t, sin_t, temb0=None, n_noise: Optional[int] = None,
+             eps: float = 1e-6):
+    """One dual-stream block of the v1 / Edit model ([EDIT] section 5.2 for the block's forward,
+    section 6 for the attention processor), both streams in fp64.
+
+    x_txt [Lt, D], x_img [Li, D]: the text stream and the image stream (the noisy target's rows
+    first, then the references').  temb [D]: the conditioning of the current t.  Each stream has
+    its own modulation, SiLU then a Linear(D, 6 D) with bias, cut into (shift1, scale1, gate1,
+    shift2, scale2, gate2).  With temb0 (the optional per-token modulation of the Edit model),
+    image rows [0, n_noise) take temb's parameters and the rest temb0's; the text always takes
+    temb's.  Per stream:
+        h = LayerNorm(x) (1 + scale1) + shift1
+        q, k, v = h W^T + b (image: to_q / to_k / to_v; text: add_q_proj / add_k_proj /
+                  add_v_proj, stacked q | k | v as [3 D][D]), per-head RMSNorm of q and k with the
+                  stream's weights (norm_q / norm_k, norm_added_q / norm_added_k), RoPE
+    then the joint sequence [text | image] under unmasked softmax attention, the text rows through
+    to_add_out and the image rows through to_out (both with bias), and per stream
+        x += gate1 * out
+        h2 = LayerNorm(x) (1 + scale2) + shift2
+        x += gate2 * (GELU_tanh(h2 W1^T + b1) W2^T + b2)        (img_mlp / txt_mlp, D -> 4 D -> D)
+    cos_t / sin_t: rotation tables of the joint sequence [Lt + Li, 64] (text positions first).
+    B: dict of the block's weights (keys as read below).  Returns (x_txt, x_img)."""
+    xt = np.asarray(x_txt, np.float64)
+    xi = np.asarray(x_img, np.float64)
+    Lt, D = xt.shape
+    Li = xi.shape[0]
+    H = D // HEAD_DIM
+
+    def mods(which, t):
+        m = linear_bias(silu(np.atleast_2d(t)), B[which + "_mod_w"], B[which + "_mod_b"])[0]
+        return [m[i * D:(i + 1) * D] for i in range(6)]
+
+    mt, mi = mods("txt", temb), mods("img", temb)
+    if temb0 is not None:
+        mi0 = mods("img", temb0)
+        nn_ = Li if n_noise is None else n_noise
+        sel = (np.arange(Li) < nn_)[:, None]
+        mi = [np.where(sel, a[None, :], b[None, :]) for a, b in zip(mi, mi0)]
+    sh1t, sc1t, g1t, sh2t, sc2t, g2t = mt
+    sh1i, sc1i, g1i, sh2i, sc2i, g2i = mi
+
+    def qkv(x, sc, sh, pre, nq, nk):
+        h = layer_norm(x, eps) * (1.0 + sc) + sh
+        y = linear_bias(h, B[pre + "_qkv_w"], B[pre + "_qkv_b"]).reshape(x.shape[0], 3, H, HEAD_DIM)
+        return rms_norm(y[:, 0], B[nq], eps), rms_norm(y[:, 1], B[nk], eps), y[:, 2]
+
+    qt, kt, vt = qkv(xt, sc1t, sh1t, "txt", "norm_added_q", "norm_added_k")
+    qi, ki, vi = qkv(xi, sc1i, sh1i, "img", "norm_q", "norm_k")
+    q = rotate(np.concatenate([qt, qi]), cos_t, sin_t)
+    k = rotate(np.concatenate([kt, ki]), cos_t, sin_t)
+    v = np.concatenate([vt, vi])
+    o = attention(q, k, v).reshape(Lt + Li, D)
+    xt = xt + g1t * linear_bias(o[:Lt], B["txt_out_w"], B["txt_out_b"])
+    xi = xi + g1i * linear_bias(o[Lt:], B["img_out_w"], B["img_out_b"])
+
+    def mlp(x, sc, sh, g, pre):
+        h = layer_norm(x, eps) * (1.0 + sc) + sh
+        a = gelu_tanh(linear_bias(h, B[pre + "_fc1_w"], B[pre + "_fc1_b"]))
+        return x + g * linear_bias(a, B[pre + "_fc2_w"], B[pre + "_fc2_b"])
+
+    return mlp(xt, sc2t, sh2t, g2t, "txt"), mlp(xi, sc2i, sh2i, g2i, "img")
+
+
 def velocity_head(x_t, temb, w_scale, w_head, eps: float = 1e-6):
     """Scale-only final AdaLN and the 64-channel velocity projection ([OV] card 6B):
     v = (RMSNorm(x) (1 + W_scale SiLU(temb))) W_head^T."""

@@ -234,6 +234,39 @@ def text_projection_weights(cfg_id: int, D: int) -> dict:
     }
 
 
+# the v1 / Edit dual-stream block: weights (bf16 Linears, fp32 biases and QK-norm weights) and inputs
+V1_LINEARS = ("img_mod", "txt_mod", "img_qkv", "txt_qkv", "img_out", "txt_out", "img_fc1", "img_fc2", "txt_fc1",
+              "txt_fc2")
+W_V1_BASE = 33                                # ids 33 .. 52: each Linear's weight, then its bias
+W_V1_QN, W_V1_KN, W_V1_AQN, W_V1_AKN = range(53, 57)
+X_V1_TXT, X_V1_IMG, X_V1_TEMB, X_V1_TEMB0 = range(57, 61)
+
+
+def v1_block_weights(cfg_id: int, D: int, F: int, layer: int = 0) -> dict:
+    """Random-init weights of one v1 dual-stream block: every Linear W ~ N(0, 1/fan_in) in bf16
+    with a bias N(0, 0.1^2) in fp32 (modulation [6D][D], QKV [3D][D] in q | k | v order, out
+    [D][D], MLP [F][D] then [D][F]); QK-RMSNorm weights 1 + N(0, 0.02^2)."""
+    shapes = {"img_mod": (6 * D, D), "txt_mod": (6 * D, D), "img_qkv": (3 * D, D), "txt_qkv": (3 * D, D),
+              "img_out": (D, D), "txt_out": (D, D), "img_fc1": (F, D), "img_fc2": (D, F), "txt_fc1": (F, D),
+              "txt_fc2": (D, F)}
+    out = {}
+    for i, name in enumerate(V1_LINEARS):
+        n_out, n_in = shapes[name]
+        out[name + "_w"] = linear_weight(cfg_id, W_V1_BASE + 2 * i, n_out, n_in, layer)
+        out[name + "_b"] = f32_vector(cfg_id, W_V1_BASE + 2 * i + 1, (n_out,), layer, 0.0, 0.1)
+    for key, idx in (("norm_q", W_V1_QN), ("norm_k", W_V1_KN), ("norm_added_q", W_V1_AQN),
+                     ("norm_added_k", W_V1_AKN)):
+        out[key] = f32_vector(cfg_id, idx, (128,), layer, 1.0, 0.02)
+    return out
+
+
+def v1_block_inputs(cfg_id: int, n_txt: int, n_img: int, D: int):
+    """Residual streams (fp32 N(0, 1)) of the text and image rows and two conditioning vectors
+    (temb, temb0; fp32 N(0, 1)) of one v1 block."""
+    f = lambda idx, shape: normal(cfg_id, idx, shape).astype(np.float32).astype(np.float64)
+    return f(X_V1_TXT, (n_txt, D)), f(X_V1_IMG, (n_img, D)), f(X_V1_TEMB, (D,)), f(X_V1_TEMB0, (D,))
+
+
 def context_inputs(cfg_id: int, n_ctx: int, D: int) -> np.ndarray:
     """Synthetic vision-language context rows [n_ctx][D] (fp32, N(0,1)): the stand-in for the
     Qwen3-VL hidden states that the TextProjection maps into the DiT's text rows."""

@@ -642,3 +642,204 @@ def test_full_mask_is_unmasked_attention():
     # and it differs from the Block-Causal step (the text row 0 now sees the images)
     ob, _ = O.step1(q, k, v, segs, cos, sin)
     assert not np.allclose(o[0], ob[0])
+
+
+# ---------------------------------------------------------------------------------------------
+# the v1 / Edit dual-stream block ("QwenImageTransformer2DModel source reading (Qwen-Image-Edit)",
+# section 5.2 block forward, section 6 attention processor)
+# ---------------------------------------------------------------------------------------------
+
+def test_layer_norm_closed_forms():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((7, 48)) * 3.0 + 1.5
+    y = O.layer_norm(x, 0.0)
+    assert np.allclose(y.mean(axis=1), 0.0, atol=1e-13)
+    assert np.allclose((y * y).mean(axis=1), 1.0, atol=1e-13)
+    # no affine parameters: invariant to a positive scale and a common offset of the row
+    assert np.allclose(O.layer_norm(2.5 * x - 4.0, 0.0), y, atol=1e-12)
+    # brute force on one row with eps
+    r = x[3]
+    mu = sum(r) / len(r)
+    var = sum((t - mu) ** 2 for t in r) / len(r)
+    ref = [(t - mu) / math.sqrt(var + 1e-6) for t in r]
+    assert np.allclose(O.layer_norm(x, 1e-6)[3], ref, atol=1e-13)
+
+
+def _v1_small(D=256, F=512, Lt=3, Li=4, seed=11):
+    rng = np.random.default_rng(seed)
+    B = {}
+    for name, (n_out, n_in) in {"img_mod": (6 * D, D), "txt_mod": (6 * D, D), "img_qkv": (3 * D, D),
+                                "txt_qkv": (3 * D, D), "img_out": (D, D), "txt_out": (D, D), "img_fc1": (F, D),
+                                "img_fc2": (D, F), "txt_fc1": (F, D), "txt_fc2": (D, F)}.items():
+        B[name + "_w"] = rng.standard_normal((n_out, n_in)) / math.sqrt(n_in)
+        B[name + "_b"] = 0.1 * rng.standard_normal(n_out)
+    for key in ("norm_q", "norm_k", "norm_added_q", "norm_added_k"):
+        B[key] = 1.0 + 0.02 * rng.standard_normal(128)
+    segs = (qin.text(Lt), qin.image(2, Li // 2, 0))
+    cos, sin = O.rope_tables(O.positions(segs))
+    xt = rng.standard_normal((Lt, D))
+    xi = rng.standard_normal((Li, D))
+    temb = rng.standard_normal(D)
+    return B, xt, xi, temb, cos, sin
+
+
+def _set_mod(B, which, D, chunks):
+    """Modulation of one stream fixed to constant vectors: zero weight, bias = the six chunks
+    (shift1, scale1, gate1, shift2, scale2, gate2)."""
+    B[which + "_mod_w"] = np.zeros((6 * D, D))
+    B[which + "_mod_b"] = np.concatenate(chunks)
+
+
+def test_v1_block_zero_gates_is_identity():
+    D = 256
+    B, xt, xi, temb, cos, sin = _v1_small(D)
+    rng = np.random.default_rng(3)
+    for w in ("txt", "img"):
+        ch = [rng.standard_normal(D) for _ in range(6)]
+        ch[2] = np.zeros(D)
+        ch[5] = np.zeros(D)
+        _set_mod(B, w, D, ch)
+    yt, yi = O.v1_block(xt, xi, temb, B, cos, sin)
+    assert np.array_equal(yt, xt) and np.array_equal(yi, xi)
+
+
+def test_v1_block_attention_half_by_hand():
+    # q = k = 0 (zero weights and biases): every query attends uniformly to all Lt + Li keys of
+    # both streams; v = h (identity weight, zero bias); out projections 2 I (text) and I (image)
+    D = 256
+    B, xt, xi, temb, cos, sin = _v1_small(D)
+    rng = np.random.default_rng(4)
+    g_t, g_i = rng.standard_normal(D), rng.standard_normal(D)
+    a_t, a_i, s_t, s_i = (0.3 * rng.standard_normal(D) for _ in range(4))
+    z = np.zeros(D)
+    _set_mod(B, "txt", D, [s_t, a_t, g_t, z, z, z])
+    _set_mod(B, "img", D, [s_i, a_i, g_i, z, z, z])
+    for w in ("txt", "img"):
+        B[w + "_qkv_w"] = np.concatenate([np.zeros((2 * D, D)), np.eye(D)])
+        B[w + "_qkv_b"] = np.zeros(3 * D)
+        B[w + "_out_b"] = np.zeros(D)
+    B["txt_out_w"] = 2.0 * np.eye(D)
+    B["img_out_w"] = np.eye(D)
+    yt, yi = O.v1_block(xt, xi, temb, B, cos, sin)
+    h = np.concatenate([O.layer_norm(xt) * (1 + a_t) + s_t, O.layer_norm(xi) * (1 + a_i) + s_i])
+    mean_v = h.mean(axis=0)
+    assert np.allclose(yt, xt + g_t * 2.0 * mean_v, atol=1e-12)
+    assert np.allclose(yi, xi + g_i * mean_v, atol=1e-12)
+
+
+def test_v1_block_mlp_half_by_hand():
+    D, F = 256, 512
+    B, xt, xi, temb, cos, sin = _v1_small(D, F)
+    rng = np.random.default_rng(6)
+    z = np.zeros(D)
+    g2_t, g2_i = rng.standard_normal(D), rng.standard_normal(D)
+    _set_mod(B, "txt", D, [z, z, z, z, z, g2_t])
+    _set_mod(B, "img", D, [z, z, z, z, z, g2_i])
+    want = {}
+    for w in ("txt", "img"):
+        B[w + "_fc1_w"] = np.zeros((F, D))
+        c = rng.standard_normal(F)
+        B[w + "_fc1_b"] = c
+        gel = 0.5 * c * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (c + 0.044715 * c ** 3)))
+        want[w] = B[w + "_fc2_w"] @ gel + B[w + "_fc2_b"]
+    yt, yi = O.v1_block(xt, xi, temb, B, cos, sin)
+    assert np.allclose(yt, xt + g2_t * want["txt"], atol=1e-12)
+    assert np.allclose(yi, xi + g2_i * want["img"], atol=1e-12)
+
+
+def test_v1_block_per_token_modulation_selects_noise_rows():
+    # temb0 = 0 and zero gate biases: the rows that take temb0's parameters (the references,
+    # after the n_noise target rows) have zero gates and pass unchanged; the target rows and the
+    # text (which always takes temb) change
+    D = 256
+    B, xt, xi, temb, cos, sin = _v1_small(D, Li=6)
+    for w in ("txt", "img"):
+        b = B[w + "_mod_b"].copy()
+        b[2 * D:3 * D] = 0.0
+        b[5 * D:6 * D] = 0.0
+        B[w + "_mod_b"] = b
+    segs = (qin.text(3), qin.image(2, 2, 0), qin.image(1, 2, 1))
+    cos, sin = O.rope_tables(O.positions(segs))
+    yt, yi = O.v1_block(xt, xi, temb, B, cos, sin, temb0=np.zeros(D), n_noise=4)
+    assert np.array_equal(yi[4:], xi[4:])
+    assert np.all(np.abs(yi[:4] - xi[:4]).max(axis=1) > 1e-3)
+    assert np.all(np.abs(yt - xt).max(axis=1) > 1e-3)
+    # temb0 equal to temb: the same as no per-token modulation
+    a = O.v1_block(xt, xi, temb, B, cos, sin, temb0=temb, n_noise=4)
+    b = O.v1_block(xt, xi, temb, B, cos, sin)
+    assert np.allclose(a[0], b[0], atol=1e-13) and np.allclose(a[1], b[1], atol=1e-13)
+
+
+def test_v1_block_common_position_shift_invariance():
+    D = 256
+    B, xt, xi, temb, cos, sin = _v1_small(D)
+    segs = (qin.text(3), qin.image(2, 2, 0))
+    pos = O.positions(segs)
+    c2, s2 = O.rope_tables(pos + 7)
+    a = O.v1_block(xt, xi, temb, B, cos, sin)
+    b = O.v1_block(xt, xi, temb, B, c2, s2)
+    assert np.allclose(a[0], b[0], atol=1e-11) and np.allclose(a[1], b[1], atol=1e-11)
+    # a relative shift of the image against the text does change it
+    p3 = pos.copy()
+    p3[3:] += 5
+    c3, s3 = O.rope_tables(p3)
+    c = O.v1_block(xt, xi, temb, B, c3, s3)
+    assert np.abs(c[1] - a[1]).max() > 1e-6
+
+
+# planted mistakes in the v1 block: each must make one of the pins above fail
+def _ln_no_centre(x, eps=1e-6):
+    return O.rms_norm(x, None, eps)
+
+
+def _linear_bias_dropped(x, w, b):
+    return O.linear(x, w)
+
+
+def _gelu_erf(x):
+    x = np.asarray(x, np.float64)
+    return 0.5 * x * (1.0 + np.vectorize(math.erf)(x / math.sqrt(2.0)))
+
+
+def _v1_out_swapped(xt, xi, temb, B, cos, sin, temb0=None, n_noise=None, eps=1e-6):
+    B2 = dict(B)
+    B2["txt_out_w"], B2["img_out_w"] = B["img_out_w"], B["txt_out_w"]
+    B2["txt_out_b"], B2["img_out_b"] = B["img_out_b"], B["txt_out_b"]
+    return _ORIG_V1(xt, xi, temb, B2, cos, sin, temb0, n_noise, eps)
+
+
+def _v1_scale_gate_swapped(xt, xi, temb, B, cos, sin, temb0=None, n_noise=None, eps=1e-6):
+    B2 = dict(B)
+    D = xt.shape[1]
+    order = [0, 2, 1, 3, 5, 4]   # (shift, gate, scale) read where (shift, scale, gate) are
+    for w in ("txt", "img"):
+        B2[w + "_mod_w"] = np.concatenate([B[w + "_mod_w"][i * D:(i + 1) * D] for i in order])
+        B2[w + "_mod_b"] = np.concatenate([B[w + "_mod_b"][i * D:(i + 1) * D] for i in order])
+    return _ORIG_V1(xt, xi, temb, B2, cos, sin, temb0, n_noise, eps)
+
+
+def _v1_selection_reversed(xt, xi, temb, B, cos, sin, temb0=None, n_noise=None, eps=1e-6):
+    if temb0 is None:
+        return _ORIG_V1(xt, xi, temb, B, cos, sin, None, n_noise, eps)
+    return _ORIG_V1(xt, xi, temb0, B, cos, sin, temb, n_noise, eps)
+
+
+_ORIG_V1 = O.v1_block
+
+PLANTED_V1 = [
+    ("layer_norm", _ln_no_centre, [test_layer_norm_closed_forms, test_v1_block_attention_half_by_hand]),
+    ("linear_bias", _linear_bias_dropped, [test_v1_block_mlp_half_by_hand]),
+    ("gelu_tanh", _gelu_erf, [test_v1_block_mlp_half_by_hand]),
+    ("v1_block", _v1_out_swapped, [test_v1_block_attention_half_by_hand]),
+    ("v1_block", _v1_scale_gate_swapped, [test_v1_block_attention_half_by_hand, test_v1_block_mlp_half_by_hand]),
+    ("v1_block", _v1_selection_reversed, [test_v1_block_per_token_modulation_selects_noise_rows]),
+]
+
+
+@pytest.mark.parametrize("i", range(len(PLANTED_V1)))
+def test_planted_v1_mistake_is_caught(i, monkeypatch):
+    name, bad, pins = PLANTED_V1[i]
+    for pin in pins:
+        assert not _fails(pin), f"pin {pin} fails on the unmodified oracle"
+    monkeypatch.setattr(O, name, bad)
+    assert any(_fails(pin) for pin in pins), f"planted mistake in {name} not caught"
