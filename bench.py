@@ -22,7 +22,8 @@ whole sequence (filling the per-layer prefix caches) and the cached target-only 
 the conditioning, all layers, the head and the Euler update.  It prints its own JSON line.
 
 --v1edit times the unmasked joint attention of the v1 / Edit model at the Edit-Plus shape (text
-512 + noisy target 64x64 + two references 64x64, 12,800 tokens) and prints its own JSON line.
+512 + noisy target 64x64 + two references 64x64, 12,800 tokens), and one whole dual-stream block
+of that model at the same shape (random-init weights), and prints its own JSON line.
 """
 from __future__ import annotations
 
@@ -232,13 +233,52 @@ def v1edit_bench(args):
     Q.qi_kernel_timing(False)
     flops = 4.0 * 128 * H * S * S
     ms = sum(per_call) / len(per_call)
+    del qkv
+    # the whole dual-stream block at this shape (random-init weights, D = 3072, MLP 4 D)
+    D, F = H * 128, 4 * H * 128
+    Lt = wl.segments[0].n_tokens
+    Li = S - Lt
+
+    def lin(n_out, n_in):
+        return (torch.randn((n_out, n_in), generator=g, device=dev) / n_in ** 0.5).to(torch.bfloat16)
+
+    shapes = {"img_mod": (6 * D, D), "txt_mod": (6 * D, D), "img_qkv": (3 * D, D), "txt_qkv": (3 * D, D),
+              "img_out": (D, D), "txt_out": (D, D), "img_fc1": (F, D), "img_fc2": (D, F), "txt_fc1": (F, D),
+              "txt_fc2": (D, F)}
+    Wt = {}
+    for name, (n_out, n_in) in shapes.items():
+        Wt[name + "_w"] = lin(n_out, n_in)
+        Wt[name + "_b"] = 0.1 * torch.randn(n_out, generator=g, device=dev)
+    for key in ("norm_q", "norm_k", "norm_added_q", "norm_added_k"):
+        Wt[key] = 1.0 + 0.02 * torch.randn(128, generator=g, device=dev)
+    blk = rt.V1Block(rt.V1BlockWeights(Wt), layout, H, dev)
+    x_txt = torch.randn((Lt, D), generator=g, device=dev)
+    x_img = torch.randn((Li, D), generator=g, device=dev)
+    cond = torch.randn((2, D), generator=g, device=dev)
+    for _ in range(2):
+        blk(x_txt, x_img, cond)
+    torch.cuda.synchronize()
+    n_blk = max(3, args.steps // 2)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n_blk):
+        blk(x_txt, x_img, cond)
+    e1.record()
+    torch.cuda.synchronize()
+    blk_ms = e0.elapsed_time(e1) / n_blk
+    blk_flops = 2.0 * S * D * (3 * D + D + 2 * F) + flops
     res = {"metric": "v1 / Edit-Plus joint full attention TFLOP/s per call", "value": round(flops / (ms * 1e-3) / 1e12, 2),
            "unit": "TFLOP/s", "higher_is_better": True, "n_gpus": 1, "steps": args.steps, "dtype": "f16",
            "data": "synthetic", "ms_per_call": round(ms, 4),
            "per_call_ms": {q: round(pct(per_call, int(q[1:])), 4) for q in ("p50", "p95", "p99")},
            "config": {"workload": f"text 512 + noisy target 64x64 + 2 references 64x64, full attention, S={S}, "
                                   f"{H}x128 heads", "flops_per_call": flops,
-                      "pct_of_peak": round(100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2)}}
+                      "pct_of_peak": round(100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2),
+                      # one whole dual-stream block (both streams' modulation, norms, projections and
+                      # MLPs with the joint attention), random-init weights, D 3072, MLP 12288
+                      "block_ms": round(blk_ms, 3), "block_flops": blk_flops,
+                      "block_tflops": round(blk_flops / (blk_ms * 1e-3) / 1e12, 1),
+                      "block_attention_share": round(ms / blk_ms, 3)}}
     print(json.dumps(res), flush=True)
 
 

@@ -377,23 +377,35 @@ int qi_euler_step(float* x, const void* v, qi_dtype v_dtype, int64_t n, float si
   return launch_status(launch_euler(x, v, v_dtype == QI_BF16, n, sigma_k1 - sigma_k, (hipStream_t)stream));
 }
 
-int qi_gemm_bf16_ex(const void* x, int64_t ldx, const void* w, void* out, int64_t ldo, int64_t M, int64_t N,
-                    int64_t K, int epilogue, const float* gate, int64_t row0, int64_t P, int32_t tile_n, void* stream) {
+static int gemm_bf16(const void* x, int64_t ldx, const void* w, const float* bias, void* out, int64_t ldo,
+                     int64_t M, int64_t N, int64_t K, int epilogue, const float* gate, int64_t row0, int64_t P,
+                     int32_t tile_n, void* stream) {
   clear_hip_error();
   if (!x || !w || !out) return QI_ERR_ARG;
-  if (epilogue < QI_EPI_STORE || epilogue > QI_EPI_GELU) return QI_ERR_ARG;
-  if (epilogue == QI_EPI_GATED_RESIDUAL && !gate) return QI_ERR_ARG;
+  if (epilogue < QI_EPI_STORE || epilogue > QI_EPI_GATED_RESIDUAL_LINEAR) return QI_ERR_ARG;
+  if ((epilogue == QI_EPI_GATED_RESIDUAL || epilogue == QI_EPI_GATED_RESIDUAL_LINEAR) && !gate) return QI_ERR_ARG;
   if (tile_n != 0 && tile_n != 256 && tile_n != 192 && tile_n != 128) return QI_ERR_ARG;
   if (tile_n == 192 && epilogue == QI_EPI_SWIGLU) return QI_ERR_ARG;
   if (M < 0 || N < 64 || K < 64 || (N % 64) || (K % 64)) return QI_ERR_SHAPE;
   if (ldx < K || ldo < (epilogue == QI_EPI_SWIGLU ? N / 2 : N)) return QI_ERR_SHAPE;
   // x and w are addressed through buffer resources with 32-bit byte offsets
   if (M * ldx * 2 > INT32_MAX || N * K * 2 > INT32_MAX) return QI_ERR_SHAPE;
-  if (!aligned16(x) || !aligned16(w) || !aligned16(out) || !aligned16(gate) || (ldx % 8) || (ldo % 8))
+  if (!aligned16(x) || !aligned16(w) || !aligned16(out) || !aligned16(gate) || !aligned16(bias) || (ldx % 8) ||
+      (ldo % 8))
     return QI_ERR_ALIGN;
   if (M == 0) return QI_OK;
-  GemmArgs a{x, ldx, w, out, ldo, M, N, K, gate, row0, P};
+  GemmArgs a{x, ldx, w, out, ldo, M, N, K, gate, row0, P, bias};
   return launch_status(launch_gemm(a, epilogue, tile_n, (hipStream_t)stream));
+}
+
+int qi_gemm_bf16_ex(const void* x, int64_t ldx, const void* w, void* out, int64_t ldo, int64_t M, int64_t N,
+                    int64_t K, int epilogue, const float* gate, int64_t row0, int64_t P, int32_t tile_n, void* stream) {
+  return gemm_bf16(x, ldx, w, nullptr, out, ldo, M, N, K, epilogue, gate, row0, P, tile_n, stream);
+}
+
+int qi_gemm_bf16_bias(const void* x, int64_t ldx, const void* w, const float* bias, void* out, int64_t ldo, int64_t M,
+                      int64_t N, int64_t K, int epilogue, const float* gate, int64_t row0, int64_t P, void* stream) {
+  return gemm_bf16(x, ldx, w, bias, out, ldo, M, N, K, epilogue, gate, row0, P, 0, stream);
 }
 
 int qi_gemm_bf16(const void* x, int64_t ldx, const void* w, void* out, int64_t ldo, int64_t M, int64_t N, int64_t K,
@@ -411,7 +423,21 @@ int qi_zc_rmsnorm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64
       (reinterpret_cast<uintptr_t>(out) & 7))
     return QI_ERR_ALIGN;
   if (M == 0) return QI_OK;
-  NormArgs a{x, ldx, out, ldo, M, D, w, scale, shift, row0, P, eps};
+  NormArgs a{x, ldx, out, ldo, M, D, w, scale, shift, row0, P, eps, 0};
+  return launch_status(launch_zc_norm_mod(a, (hipStream_t)stream));
+}
+
+int qi_layernorm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64_t M, int32_t D, const float* scale,
+                     const float* shift, int64_t row0, int64_t P, float eps, void* stream) {
+  clear_hip_error();
+  if (!x || !out) return QI_ERR_ARG;
+  if (M < 0 || D < 4 || (D % 4) || ldx < D || ldo < D || M > INT32_MAX) return QI_ERR_SHAPE;
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return QI_ERR_ARG;
+  if (!aligned16(x) || !aligned16(scale) || !aligned16(shift) || (ldx % 4) || (ldo % 4) ||
+      (reinterpret_cast<uintptr_t>(out) & 7))
+    return QI_ERR_ALIGN;
+  if (M == 0) return QI_OK;
+  NormArgs a{x, ldx, out, ldo, M, D, nullptr, scale, shift, row0, P, eps, 1};
   return launch_status(launch_zc_norm_mod(a, (hipStream_t)stream));
 }
 
@@ -422,13 +448,18 @@ int qi_timestep_embed(const float* t, int32_t n, int32_t dim, float* out, void* 
   return launch_status(launch_timestep_embed(t, n, dim, out, (hipStream_t)stream));
 }
 
-int qi_linear_small(const float* x, int32_t n_vec, int32_t I, const void* w, int32_t O, int32_t silu_in, float* y,
-                    void* stream) {
+int qi_linear_small_bias(const float* x, int32_t n_vec, int32_t I, const void* w, const float* bias, int32_t O,
+                         int32_t silu_in, float* y, void* stream) {
   clear_hip_error();
   if (!x || !w || !y) return QI_ERR_ARG;
   if (n_vec < 1 || n_vec > 4 || I < 8 || (I % 8) || O < 0) return QI_ERR_SHAPE;
   if (!aligned16(w)) return QI_ERR_ALIGN;
-  return launch_status(launch_linear_small(x, n_vec, I, w, O, silu_in ? 1 : 0, y, (hipStream_t)stream));
+  return launch_status(launch_linear_small(x, n_vec, I, w, bias, O, silu_in ? 1 : 0, y, (hipStream_t)stream));
+}
+
+int qi_linear_small(const float* x, int32_t n_vec, int32_t I, const void* w, int32_t O, int32_t silu_in, float* y,
+                    void* stream) {
+  return qi_linear_small_bias(x, n_vec, I, w, nullptr, O, silu_in, y, stream);
 }
 
 int qi_cast_bf16(const float* x, void* y, int64_t n, void* stream) {

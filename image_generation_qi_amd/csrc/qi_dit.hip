@@ -207,6 +207,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int mb = 0; mb < MB; ++mb) {
     const int64_t m = m0 + WTM * wm + 32 * mb + l32;
     if (m >= a.M) continue;
+    if (a.bias) {   // (uniform) bias of the feature rows, before the epilogue
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int64_t nbase = n0 + WTN * wn + 32 * nb + 4 * g;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int64_t n = nbase + 8 * r4;
+          if (n >= a.N) continue;
+          const f32x4 b = *(const f32x4*)(a.bias + n);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[mb][nb][4 * r4 + e] += b[e];
+        }
+      }
+    }
     if constexpr (EPI == QI_EPI_SWIGLU) {
       // weight rows in blocks of 64: 32 gate rows, then the 32 up rows of the same features
 #pragma unroll
@@ -254,12 +268,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
             *(u32x2*)((__bf16*)a.out + m * a.ldo + n) =
                 u32x2{to_bf16(gl[0]) | (to_bf16(gl[1]) << 16), to_bf16(gl[2]) | (to_bf16(gl[3]) << 16)};
-          } else {  // QI_EPI_GATED_RESIDUAL
+          } else {  // QI_EPI_GATED_RESIDUAL (tanh gate) or QI_EPI_GATED_RESIDUAL_LINEAR (gate as is)
             const f32x4 gt = *(const f32x4*)(a.gate + ((m + a.row0 < a.P) ? 0 : a.N) + n);
             f32x4* xp = (f32x4*)((float*)a.out + m * a.ldo + n);
             f32x4 xv = *xp;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) xv[e] = __builtin_fmaf(tanhf(gt[e]), y[e], xv[e]);
+            for (int e = 0; e < 4; ++e)
+              xv[e] = __builtin_fmaf(EPI == QI_EPI_GATED_RESIDUAL ? tanhf(gt[e]) : gt[e], y[e], xv[e]);
             *xp = xv;
           }
         }
@@ -270,13 +285,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // ZeroCenterRMSNorm + modulation, one workgroup per row; D % 4 == 0.
 __global__ __launch_bounds__(256) void k_zc_norm_mod(NormArgs a) {
-  __shared__ float red[4];
+  __shared__ float red[8];
   const int64_t m = blockIdx.x;
   const float* x = a.x + m * a.ldx;
+  // LayerNorm: the row mean first (a second pass over the row, which is in cache)
+  float mu = 0.f;
+  if (a.center) {
+    float sum = 0.f;
+    for (int i = 4 * threadIdx.x; i < a.D; i += 1024) {
+      const f32x4 v = *(const f32x4*)(x + i);
+      sum += (v[0] + v[1]) + (v[2] + v[3]);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+    if ((threadIdx.x & 63) == 0) red[4 + (threadIdx.x >> 6)] = sum;
+    __syncthreads();
+    mu = ((red[4] + red[5]) + (red[6] + red[7])) / (float)a.D;
+  }
   float ss = 0.f;
   for (int i = 4 * threadIdx.x; i < a.D; i += 1024) {
     const f32x4 v = *(const f32x4*)(x + i);
-    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    const float d0 = v[0] - mu, d1 = v[1] - mu, d2 = v[2] - mu, d3 = v[3] - mu;
+    ss += d0 * d0 + d1 * d1 + d2 * d2 + d3 * d3;
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
@@ -293,7 +323,7 @@ __global__ __launch_bounds__(256) void k_zc_norm_mod(NormArgs a) {
     float y[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float t = v[e] * rr;
+      float t = (v[e] - mu) * rr;
       if (a.w) t *= a.w[i + e] + 1.0f;
       if (sc) t *= 1.0f + sc[i + e];
       if (sh) t += sh[i + e];
@@ -319,8 +349,8 @@ __global__ void k_timestep_embed(const float* t, int n, int dim, float* out) {
 
 // y[v][o] = sum_i act(x[v][i]) * W[o][i] for v < nv <= 4; one wavefront per output o.
 __global__ __launch_bounds__(256) void k_linear_small(const float* __restrict__ x, int nv, int I,
-                                                     const __bf16* __restrict__ w, int O, int silu_in,
-                                                     float* __restrict__ y) {
+                                                     const __bf16* __restrict__ w, const float* __restrict__ bias,
+                                                     int O, int silu_in, float* __restrict__ y) {
   const int o = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (o >= O) return;
@@ -348,7 +378,7 @@ __global__ __launch_bounds__(256) void k_linear_small(const float* __restrict__ 
     float s = acc[v];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) y[(int64_t)v * O + o] = s;
+    if (lane == 0) y[(int64_t)v * O + o] = bias ? s + bias[o] : s;
   }
 }
 
@@ -374,6 +404,7 @@ hipError_t launch_big(const GemmArgs& a, int epi, int bn, hipStream_t s) {
       case QI_EPI_STORE_F32: QI_LAUNCH_BIG(QI_EPI_STORE_F32, 256); break;
       case QI_EPI_GATED_RESIDUAL: QI_LAUNCH_BIG(QI_EPI_GATED_RESIDUAL, 256); break;
       case QI_EPI_GELU: QI_LAUNCH_BIG(QI_EPI_GELU, 256); break;
+      case QI_EPI_GATED_RESIDUAL_LINEAR: QI_LAUNCH_BIG(QI_EPI_GATED_RESIDUAL_LINEAR, 256); break;
       case QI_EPI_SWIGLU: QI_LAUNCH_BIG(QI_EPI_SWIGLU, 256); break;
       default: return hipErrorInvalidValue;
     }
@@ -383,6 +414,7 @@ hipError_t launch_big(const GemmArgs& a, int epi, int bn, hipStream_t s) {
       case QI_EPI_STORE_F32: QI_LAUNCH_BIG(QI_EPI_STORE_F32, 192); break;
       case QI_EPI_GATED_RESIDUAL: QI_LAUNCH_BIG(QI_EPI_GATED_RESIDUAL, 192); break;
       case QI_EPI_GELU: QI_LAUNCH_BIG(QI_EPI_GELU, 192); break;
+      case QI_EPI_GATED_RESIDUAL_LINEAR: QI_LAUNCH_BIG(QI_EPI_GATED_RESIDUAL_LINEAR, 192); break;
       default: return hipErrorInvalidValue;   // SwiGLU needs whole 64-row gate|up blocks per wave
     }
   } else if (bn == 128) {
@@ -391,6 +423,7 @@ hipError_t launch_big(const GemmArgs& a, int epi, int bn, hipStream_t s) {
       case QI_EPI_STORE_F32: QI_LAUNCH_BIG(QI_EPI_STORE_F32, 128); break;
       case QI_EPI_GATED_RESIDUAL: QI_LAUNCH_BIG(QI_EPI_GATED_RESIDUAL, 128); break;
       case QI_EPI_GELU: QI_LAUNCH_BIG(QI_EPI_GELU, 128); break;
+      case QI_EPI_GATED_RESIDUAL_LINEAR: QI_LAUNCH_BIG(QI_EPI_GATED_RESIDUAL_LINEAR, 128); break;
       case QI_EPI_SWIGLU: QI_LAUNCH_BIG(QI_EPI_SWIGLU, 128); break;
       default: return hipErrorInvalidValue;
     }
@@ -445,10 +478,11 @@ hipError_t launch_timestep_embed(const float* t, int n, int dim, float* out, hip
   return hipGetLastError();
 }
 
-hipError_t launch_linear_small(const float* x, int nv, int I, const void* w, int O, int silu_in, float* y,
-                               hipStream_t s) {
+hipError_t launch_linear_small(const float* x, int nv, int I, const void* w, const float* bias, int O, int silu_in,
+                               float* y, hipStream_t s) {
   if (O <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_linear_small, dim3((O + 3) / 4), dim3(256), 0, s, x, nv, I, (const __bf16*)w, O, silu_in, y);
+  hipLaunchKernelGGL(k_linear_small, dim3((O + 3) / 4), dim3(256), 0, s, x, nv, I, (const __bf16*)w, bias, O, silu_in,
+                     y);
   return hipGetLastError();
 }
 

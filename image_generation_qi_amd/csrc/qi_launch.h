@@ -107,8 +107,9 @@ struct GemmArgs {
   void* out;
   int64_t ldo;
   int64_t M, N, K;
-  const float* gate;   // QI_EPI_GATED_RESIDUAL: fp32 [2][N]; row m uses gate[(m + row0 < P) ? 0 : 1]
+  const float* gate;   // gated residual epilogues: fp32 [2][N]; row m uses gate[(m + row0 < P) ? 0 : 1]
   int64_t row0, P;
+  const float* bias;   // nullable fp32 [N], added to y before the epilogue
 };
 // ZeroCenterRMSNorm + modulation of fp32 rows into bf16 rows.
 struct NormArgs {
@@ -123,6 +124,7 @@ struct NormArgs {
   const float* shift;   // nullable, [2][D]
   int64_t row0, P;
   float eps;
+  int32_t center;       // 1: subtract the row mean first (LayerNorm without affine)
 };
 
 // tile_n: feature width of the 256 x tile_n workgroup tiles (256, 192 or 128; 192 not with
@@ -131,7 +133,7 @@ hipError_t launch_gemm(const GemmArgs& a, int epilogue, int tile_n, hipStream_t 
 int gemm_config(int64_t M, int64_t N, int epilogue);
 hipError_t launch_zc_norm_mod(const NormArgs& a, hipStream_t s);
 hipError_t launch_timestep_embed(const float* t, int n, int dim, float* out, hipStream_t s);
-hipError_t launch_linear_small(const float* x, int nv, int I, const void* w, int O, int silu_in, float* y,
+hipError_t launch_linear_small(const float* x, int nv, int I, const void* w, const float* bias, int O, int silu_in, float* y,
                                hipStream_t s);
 hipError_t launch_cast_bf16(const float* x, void* y, int64_t n, hipStream_t s);
 

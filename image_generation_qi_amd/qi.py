@@ -22,6 +22,7 @@ QI_OK, QI_ERR_ARG, QI_ERR_DTYPE, QI_ERR_SHAPE, QI_ERR_ALIGN, QI_ERR_LAYOUT, QI_E
 QI_F32, QI_BF16, QI_F16 = 0, 1, 2
 QI_SEG_TEXT, QI_SEG_IMAGE, QI_SEG_TEXT_BIDIR = 0, 1, 2
 QI_EPI_STORE, QI_EPI_STORE_F32, QI_EPI_GATED_RESIDUAL, QI_EPI_SWIGLU, QI_EPI_GELU = 0, 1, 2, 3, 4
+QI_EPI_GATED_RESIDUAL_LINEAR = 5
 QI_ATTN_BLOCK_CAUSAL, QI_ATTN_FULL = 0, 1
 QI_HEAD_DIM = 128
 
@@ -92,10 +93,16 @@ _SIGS = {
                              c_void_p, c_int64, c_int64, c_void_p]),
     "qi_gemm_bf16_ex": (c_int, [c_void_p, c_int64, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int64, c_int,
                                 c_void_p, c_int64, c_int64, c_int32, c_void_p]),
+    "qi_gemm_bf16_bias": (c_int, [c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int64,
+                                  c_int64, c_int, c_void_p, c_int64, c_int64, c_void_p]),
     "qi_zc_rmsnorm_mod": (c_int, [c_void_p, c_int64, c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p,
                                   c_void_p, c_int64, c_int64, c_float, c_void_p]),
+    "qi_layernorm_mod": (c_int, [c_void_p, c_int64, c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p,
+                                 c_int64, c_int64, c_float, c_void_p]),
     "qi_timestep_embed": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
     "qi_linear_small": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+    "qi_linear_small_bias": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
+                                     c_void_p]),
     "qi_cast_bf16": (c_int, [c_void_p, c_void_p, c_int64, c_void_p]),
     "qi_kernel_timing": (c_int, [c_int]),
     "qi_kernel_timing_read": (c_int, [POINTER(c_double), POINTER(c_int64)]),
@@ -277,6 +284,21 @@ def qi_gemm_bf16_ex(x, ldx: int, w, out, ldo: int, M: int, N: int, K: int, epilo
                     P: int = 0, tile_n: int = 0, stream=None) -> int:
     return lib().qi_gemm_bf16_ex(_p(x), ldx, _p(w), _p(out), ldo, M, N, K, epilogue, _p(gate), row0, P, tile_n,
                                  _p(stream))
+
+
+def qi_gemm_bf16_bias(x, ldx: int, w, bias, out, ldo: int, M: int, N: int, K: int, epilogue: int, gate=None,
+                      row0: int = 0, P: int = 0, stream=None) -> int:
+    return lib().qi_gemm_bf16_bias(_p(x), ldx, _p(w), _p(bias), _p(out), ldo, M, N, K, epilogue, _p(gate), row0, P,
+                                   _p(stream))
+
+
+def qi_layernorm_mod(x, ldx: int, out, ldo: int, M: int, D: int, scale=None, shift=None, row0: int = 0, P: int = 0,
+                     eps: float = 1e-6, stream=None) -> int:
+    return lib().qi_layernorm_mod(_p(x), ldx, _p(out), ldo, M, D, _p(scale), _p(shift), row0, P, eps, _p(stream))
+
+
+def qi_linear_small_bias(x, n_vec: int, I: int, w, bias, O: int, silu_in: bool, y, stream=None) -> int:
+    return lib().qi_linear_small_bias(_p(x), n_vec, I, _p(w), _p(bias), O, 1 if silu_in else 0, _p(y), _p(stream))
 
 
 def qi_zc_rmsnorm_mod(x, ldx: int, out, ldo: int, M: int, D: int, w=None, scale=None, shift=None, row0: int = 0,

@@ -195,11 +195,16 @@ class SharedWeights:
 
 
 def gemm(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor, epilogue: int, gate=None, row0: int = 0, P: int = 0,
-         tile_n: int = 0):
+         tile_n: int = 0, bias=None):
     M, K = x.shape
     N = w.shape[0]
     assert x.dtype == torch.bfloat16 and w.dtype == torch.bfloat16 and w.shape[1] == K and x.stride(1) == 1
     assert out.stride(1) == 1 and out.shape[0] == M
+    if bias is not None:
+        assert tile_n == 0 and bias.dtype == torch.float32 and bias.is_contiguous() and bias.numel() == N
+        Q.check(Q.qi_gemm_bf16_bias(x, x.stride(0), w, bias, out, out.stride(0), M, N, K, epilogue, gate, row0, P,
+                                    stream_handle(x.device)), "qi_gemm_bf16_bias")
+        return out
     Q.check(Q.qi_gemm_bf16_ex(x, x.stride(0), w, out, out.stride(0), M, N, K, epilogue, gate, row0, P, tile_n,
                               stream_handle(x.device)), "qi_gemm_bf16_ex")
     return out
@@ -211,6 +216,15 @@ def norm_mod(x: torch.Tensor, out: torch.Tensor, w=None, scale=None, shift=None,
     assert x.dtype == torch.float32 and out.dtype == torch.bfloat16 and x.stride(1) == 1 and out.stride(1) == 1
     Q.check(Q.qi_zc_rmsnorm_mod(x, x.stride(0), out, out.stride(0), M, D, w, scale, shift, row0, P, eps,
                                 stream_handle(x.device)), "qi_zc_rmsnorm_mod")
+    return out
+
+
+def layernorm_mod(x: torch.Tensor, out: torch.Tensor, scale=None, shift=None, row0: int = 0, P: int = 0,
+                  eps: float = 1e-6):
+    M, D = x.shape
+    assert x.dtype == torch.float32 and out.dtype == torch.bfloat16 and x.stride(1) == 1 and out.stride(1) == 1
+    Q.check(Q.qi_layernorm_mod(x, x.stride(0), out, out.stride(0), M, D, scale, shift, row0, P, eps,
+                               stream_handle(x.device)), "qi_layernorm_mod")
     return out
 
 
@@ -238,10 +252,15 @@ class TextProjection:
         return out
 
 
-def linear_small(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, silu_in: bool):
+def linear_small(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, silu_in: bool, bias=None):
     nv, I = x.shape
     O_ = w.shape[0]
     assert x.is_contiguous() and y.is_contiguous() and w.is_contiguous() and y.shape == (nv, O_)
+    if bias is not None:
+        assert bias.dtype == torch.float32 and bias.is_contiguous() and bias.numel() == O_
+        Q.check(Q.qi_linear_small_bias(x, nv, I, w, bias, O_, silu_in, y, stream_handle(x.device)),
+                "qi_linear_small_bias")
+        return y
     Q.check(Q.qi_linear_small(x, nv, I, w, O_, silu_in, y, stream_handle(x.device)), "qi_linear_small")
     return y
 
@@ -351,3 +370,87 @@ class DiT:
             for li in range(len(self.layers)):
                 self.layer(li, slice(P, S), True)
         self.head(lat, float(sig[k]), float(sig[k + 1]))
+
+
+# ------------------------------------------------------------------------------------------------
+# the v1 / Edit dual-stream block around the unmasked joint attention
+# ------------------------------------------------------------------------------------------------
+
+V1_LINEARS = ("img_mod", "txt_mod", "img_qkv", "txt_qkv", "img_out", "txt_out", "img_fc1", "img_fc2", "txt_fc1",
+              "txt_fc2")
+
+
+class V1BlockWeights:
+    """Device weights of one v1 dual-stream block: bf16 Linear weights [out][in] with fp32 biases
+    (`<name>_w`, `<name>_b` for each name in V1_LINEARS: modulation [6D][D], QKV [3D][D] in
+    q | k | v order, out [D][D], MLP [F][D] and [D][F]) and fp32 QK-RMSNorm weights [128]
+    (`norm_q`, `norm_k` of the image stream, `norm_added_q`, `norm_added_k` of the text)."""
+
+    def __init__(self, tensors: dict):
+        self.t = {k: v.contiguous() for k, v in tensors.items()}
+        self.D = self.t["img_out_w"].shape[0]
+        self.F = self.t["img_fc1_w"].shape[0]
+        for name in V1_LINEARS:
+            assert self.t[name + "_w"].dtype == torch.bfloat16 and self.t[name + "_b"].dtype == torch.float32
+
+    def __getitem__(self, key):
+        return self.t[key]
+
+
+class V1Block:
+    """One dual-stream block of the v1 / Edit model ("QwenImageTransformer2DModel source reading
+    (Qwen-Image-Edit)", section 5.2 for the block, section 6 for the attention processor) as a
+    sequence of library calls.  The layout must be the unmasked one (QI_ATTN_FULL) with the text
+    first, then the image rows (the noisy target, then the references).  Per stream: six
+    conditioning linears (one per modulation chunk, SiLU then Linear with bias), LayerNorm +
+    modulation, the QKV GEMM with bias written straight into the joint [text | image] QKV buffer,
+    and the stream's QK-RMSNorm in place; then one joint attention over the layout (RoPE applied
+    in it); per stream again the out-projection GEMM with bias adding gate1 * y into the residual,
+    LayerNorm + modulation, the MLP (GEMM with bias and GELU(tanh), GEMM with bias adding
+    gate2 * y)."""
+
+    def __init__(self, W: V1BlockWeights, layout: Layout, n_head: int, device="cuda", eps: float = 1e-6):
+        assert layout.attention == Q.QI_ATTN_FULL
+        assert W.D == n_head * 128
+        self.W, self.L, self.H, self.eps, self.device = W, layout, n_head, eps, device
+        self.att = Attention(layout, n_head, Q.QI_BF16, device)
+
+    def __call__(self, x_txt: torch.Tensor, x_img: torch.Tensor, cond: torch.Tensor, n_noise: Optional[int] = None):
+        """x_txt fp32 [Lt][D] and x_img fp32 [Li][D] (updated in place and returned); cond fp32
+        [2][D]: row 0 the current t's conditioning, row 1 the t = 0 one, which image rows
+        n_noise.. take when n_noise is given (the per-token modulation; the text and, without
+        n_noise, every image row take row 0)."""
+        W, D, H, eps, dev = self.W, self.W.D, self.H, self.eps, self.device
+        Lt, Li = x_txt.shape[0], x_img.shape[0]
+        S = Lt + Li
+        assert S == self.L.S and x_txt.shape[1] == D and x_img.shape[1] == D
+        assert cond.shape == (2, D) and cond.dtype == torch.float32 and cond.is_contiguous()
+        streams = (("txt", x_txt, 0, Lt, Lt, "norm_added_q", "norm_added_k"),
+                   ("img", x_img, Lt, Li, Li if n_noise is None else n_noise, "norm_q", "norm_k"))
+        # modulation: chunk i of a stream for both conditioning rows, [2][D] each
+        mods = {}
+        for name, *_ in streams:
+            m = torch.empty((6, 2, D), dtype=torch.float32, device=dev)
+            for i in range(6):
+                linear_small(cond, W[name + "_mod_w"][i * D:(i + 1) * D], m[i], True,
+                             W[name + "_mod_b"][i * D:(i + 1) * D])
+            mods[name] = m
+        h = torch.empty((S, D), dtype=torch.bfloat16, device=dev)
+        qkv = torch.empty((S, 3, H, 128), dtype=torch.bfloat16, device=dev)
+        for name, x, r0, n, P, nq, nk in streams:
+            m = mods[name]
+            layernorm_mod(x, h[r0:r0 + n], m[1], m[0], 0, P, eps)
+            gemm(h[r0:r0 + n], W[name + "_qkv_w"], qkv[r0:r0 + n].view(n, 3 * D), Q.QI_EPI_STORE,
+                 bias=W[name + "_qkv_b"])
+            rope3d_apply(qkv[r0:r0 + n, 0], None, None, W[nq], eps)
+            rope3d_apply(qkv[r0:r0 + n, 1], None, None, W[nk], eps)
+        o = self.att.full(qkv[:, 0], qkv[:, 1], qkv[:, 2])
+        a = torch.empty((max(Lt, Li), W.F), dtype=torch.bfloat16, device=dev)
+        for name, x, r0, n, P, nq, nk in streams:
+            m = mods[name]
+            gemm(o[r0:r0 + n].view(n, D), W[name + "_out_w"], x, Q.QI_EPI_GATED_RESIDUAL_LINEAR, m[2], 0, P,
+                 bias=W[name + "_out_b"])
+            layernorm_mod(x, h[r0:r0 + n], m[4], m[3], 0, P, eps)
+            gemm(h[r0:r0 + n], W[name + "_fc1_w"], a[:n], Q.QI_EPI_GELU, bias=W[name + "_fc1_b"])
+            gemm(a[:n], W[name + "_fc2_w"], x, Q.QI_EPI_GATED_RESIDUAL_LINEAR, m[5], 0, P, bias=W[name + "_fc2_b"])
+        return x_txt, x_img

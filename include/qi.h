@@ -252,13 +252,19 @@ int qi_euler_step(float* x, const void* v, qi_dtype v_dtype, int64_t n, float si
  *                         W rows come in blocks of 64: 32 gate rows, then the 32 up rows of the
  *                         same output features (feature f: gate row 64(f/32) + f%32, up row +32).
  *   QI_EPI_GELU           out bf16 [M][ldo] = GELU(y), the tanh form 0.5 y (1 + tanh(sqrt(2/pi) (y +
- *                         0.044715 y^3))) (the context TextProjection of [1B] sections 1-3). */
+ *                         0.044715 y^3))) (the context TextProjection of [1B] sections 1-3; the
+ *                         MLP of the v1 dual-stream block, [EDIT] section 5.2).
+ *   QI_EPI_GATED_RESIDUAL_LINEAR
+ *                         out fp32 [M][ldo] += gate * y, the gate as given (the v1 dual-stream
+ *                         block's residual gates, [EDIT] section 5.2); gate as for
+ *                         QI_EPI_GATED_RESIDUAL. */
 typedef enum {
   QI_EPI_STORE = 0,
   QI_EPI_STORE_F32 = 1,
   QI_EPI_GATED_RESIDUAL = 2,
   QI_EPI_SWIGLU = 3,
-  QI_EPI_GELU = 4
+  QI_EPI_GELU = 4,
+  QI_EPI_GATED_RESIDUAL_LINEAR = 5
 } qi_epilogue;
 
 /* Dense projection on bf16 MFMA: x device bf16 [M][ldx]; w device bf16 [N][K] (the Linear weight,
@@ -277,12 +283,27 @@ int qi_gemm_bf16_ex(const void* x, int64_t ldx, const void* w, void* out, int64_
                     int64_t K, int epilogue, const float* gate, int64_t row0, int64_t P, int32_t tile_n,
                     void* stream);
 
+/* qi_gemm_bf16 of a Linear with a bias ([EDIT] section 5.2 and its per-block parameter table: every
+ * Linear of the v1 dual-stream block carries one): bias device fp32 [N] (16-byte aligned, in the
+ * order of W's rows) is added to y before the epilogue; NULL = no bias. */
+int qi_gemm_bf16_bias(const void* x, int64_t ldx, const void* w, const float* bias, void* out, int64_t ldo, int64_t M,
+                      int64_t N, int64_t K, int epilogue, const float* gate, int64_t row0, int64_t P, void* stream);
+
 /* ZeroCenterRMSNorm with modulation ([1B] sections 1-3: x * rrms * (w + 1), weights stored as
  * scale - 1, fp32 math; [EDIT] section 5.2: x * (1 + scale) + shift): x device fp32 [M][ldx],
  * out device bf16 [M][ldo]; w fp32 [D] or NULL (no (w + 1) factor: plain RMS norm); scale and shift
  * fp32 [2][D] or NULL, row m using index 0 if row0 + m < P (prefix, t = 0) else 1.  D % 4 == 0. */
 int qi_zc_rmsnorm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64_t M, int32_t D, const float* w,
                       const float* scale, const float* shift, int64_t row0, int64_t P, float eps, void* stream);
+
+/* LayerNorm without affine parameters, then the modulation ([EDIT] section 5.2: the v1 block's
+ * norm1 / norm2, elementwise_affine off, eps 1e-6): (x - mean) / sqrt(var + eps) * (1 + scale) +
+ * shift, fp32 math; x device fp32 [M][ldx], out device bf16 [M][ldo]; scale and shift fp32 [2][D]
+ * or NULL, row m using index 0 if row0 + m < P else 1 (the caller orders the two parameter sets,
+ * e.g. the noisy target's and the t = 0 ones of the Edit model's optional per-token
+ * modulation).  D % 4 == 0. */
+int qi_layernorm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64_t M, int32_t D, const float* scale,
+                     const float* shift, int64_t row0, int64_t P, float eps, void* stream);
 
 /* Sinusoidal timestep embedding ([EDIT] section 5.1: 256 channels, cos half first, frequencies
  * 10000^(-i/(dim/2))): t device fp32 [n] (the timestep, e.g. 1000 * sigma), out device fp32
@@ -294,6 +315,12 @@ int qi_timestep_embed(const float* t, int32_t n, int32_t dim, float* out, void* 
  * act on SiLU(temb)).  x device fp32 [n_vec][I], w device bf16 [O][I] (I % 8 == 0), y fp32. */
 int qi_linear_small(const float* x, int32_t n_vec, int32_t I, const void* w, int32_t O, int32_t silu_in, float* y,
                     void* stream);
+
+/* qi_linear_small with a bias: y[v][o] = sum_i act(x[v][i]) w[o][i] + bias[o]; bias device fp32 [O]
+ * or NULL (the v1 block's modulation Linear, SiLU then Linear(D, 6 D) with bias, [EDIT] section
+ * 5.2). */
+int qi_linear_small_bias(const float* x, int32_t n_vec, int32_t I, const void* w, const float* bias, int32_t O,
+                         int32_t silu_in, float* y, void* stream);
 
 /* fp32 -> bf16 (nearest even) of n elements (latents into the img_in projection). */
 int qi_cast_bf16(const float* x, void* y, int64_t n, void* stream);
