@@ -103,6 +103,15 @@ V1_WORKLOADS = {
 }
 
 
+# Joint packing with text between the images (the prompt may interleave text with up to ten
+# reference images): text 64, then ten (reference 32x32, text 16) pairs, then the target 64x64.
+INTERLEAVED_WORKLOADS = {
+    "interleaved10": Workload("interleaved10", 7, (text(64),) + tuple(s for f in range(1, 11)
+                                                                      for s in (image(32, 32, f), text(16)))
+                              + (image(64, 64, 0),)),
+}
+
+
 def small_workload(name: str, segments: Sequence[Segment], n_head: int = 2, dtype: str = "bf16",
                    cfg_id: int = 90, qk_rmsnorm: bool = False) -> Workload:
     """An ad-hoc workload for edge-case tests (ragged tiles, odd grids, several text runs)."""

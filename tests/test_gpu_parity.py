@@ -312,9 +312,13 @@ def sample_rows(lo, hi, n, seed):
     return np.unique(np.concatenate([r, [lo, hi - 1]]))
 
 
-@pytest.mark.parametrize("name", ["cfg2", "cfg3", "cfg3_t512"])
+def full_size_wl(name):
+    return qin.WORKLOADS[name] if name in qin.WORKLOADS else qin.INTERLEAVED_WORKLOADS[name]
+
+
+@pytest.mark.parametrize("name", ["cfg2", "cfg3", "cfg3_t512", "interleaved10"])
 def test_full_size_target_step_sampled(name):
-    wl = qin.WORKLOADS[name]
+    wl = full_size_wl(name)
     say(f"full-size target step {name} S={wl.S} P={wl.P} T={wl.T}")
     c = Case(wl)
     L, att = make(wl)
@@ -333,9 +337,9 @@ def test_full_size_target_step_sampled(name):
     check_close(to_np(ot[rows]), ref, "bf16", f"{name} target rows")
 
 
-@pytest.mark.parametrize("name", ["cfg2", "cfg3"])
+@pytest.mark.parametrize("name", ["cfg2", "cfg3", "interleaved10"])
 def test_full_size_step1_sampled(name):
-    wl = qin.WORKLOADS[name]
+    wl = full_size_wl(name)
     say(f"full-size step 1 {name} S={wl.S}")
     c = Case(wl)
     L, att = make(wl)
