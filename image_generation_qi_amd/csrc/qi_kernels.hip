@@ -143,8 +143,12 @@ __device__ __forceinline__ int perm16(int p) {
 template <bool WITH_V>
 __global__ __launch_bounds__(256) void k_prep_kv64(PrepArgs a) {
   constexpr int KROW = 64 * 16 + 16;           // bytes per dim chunk of the staged K tile (padded)
-  __shared__ __attribute__((aligned(16))) char kt[16 * KROW];
-  __shared__ uint32_t vt[WITH_V ? 64 : 1][65];  // [key][dim pair]: fp16 pairs, rows padded to 65 words
+  // one staging buffer, the K tile first and then the V tile (16.6 KB, so that 8 workgroups fit a
+  // CU and the 64-key tiles of a 4,096-token target over 24 heads run in one round)
+  static_assert(16 * KROW == 64 * 65 * 4, "the K and V staging layouts share one buffer");
+  __shared__ __attribute__((aligned(16))) char lds[16 * KROW];
+  char* kt = lds;                                               // [dim chunk][slot], rows padded
+  uint32_t(*vt)[65] = reinterpret_cast<uint32_t(*)[65]>(lds);   // [key][dim pair]: fp16 pairs
   const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int rr = tid >> 4, c = tid & 15;
   // V rows first (their loads overlap the K arithmetic)
@@ -203,13 +207,6 @@ __global__ __launch_bounds__(256) void k_prep_kv64(PrepArgs a) {
     *(u32x4*)(kt + c * KROW + perm16(r) * 16) =
         u32x4{pack_f16(xq[0], xq[1]), pack_f16(xq[2], xq[3]), pack_f16(xq[4], xq[5]), pack_f16(xq[6], xq[7])};
   }
-  if (WITH_V) {
-    const int key = tid >> 2, d0 = (tid & 3) * 32;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vt[key][(d0 + 8 * i) / 2 + e] = pack_f16(bf16_lo(vw[i][e]), bf16_hi(vw[i][e]));
-  }
   __syncthreads();
   // K tile out: piece p (16 bytes) = chunk p / 64, slot p % 64
   uint16_t* ktile = (uint16_t*)a.dst + (int64_t)h * a.dst_head_stride + (int64_t)t * 8192;
@@ -219,6 +216,15 @@ __global__ __launch_bounds__(256) void k_prep_kv64(PrepArgs a) {
     *(u32x4*)(ktile + piece * 8) = *(const u32x4*)(kt + (piece >> 6) * KROW + (piece & 63) * 16);
   }
   if (WITH_V) {
+    __syncthreads();   // every K piece has been read before the V rows overwrite the buffer
+    {
+      const int key = tid >> 2, d0 = (tid & 3) * 32;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vt[key][(d0 + 8 * i) / 2 + e] = pack_f16(bf16_lo(vw[i][e]), bf16_hi(vw[i][e]));
+    }
+    __syncthreads();
     // V tile out: piece p = key chunk p / 128, dim p % 128 (8 keys of that dim)
     uint16_t* vtile = (uint16_t*)a.dst_v + (int64_t)h * a.dst_head_stride + (int64_t)t * 8192;
 #pragma unroll
