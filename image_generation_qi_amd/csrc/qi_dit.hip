@@ -284,6 +284,76 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ZeroCenterRMSNorm + modulation, one workgroup per row; D % 4 == 0.
+// The same for rows of up to 256 * NCH features: one wave per row (four rows per workgroup), the
+// row held in registers (NCH float4 per lane, all loads in flight at once), so the mean, the sum of
+// squares and the output need one read of the row.
+template <int NCH>
+__global__ __launch_bounds__(256) void k_norm_rows(NormArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= a.M) return;
+  const float* x = a.x + m * a.ldx;
+  const int nq = a.D / 4;
+  f32x4 v[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int q = lane + 64 * c;
+    v[c] = q < nq ? *(const f32x4*)(x + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float mu = 0.f;
+  if (a.center) {
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) sum += (v[c][0] + v[c][1]) + (v[c][2] + v[c][3]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+    mu = sum / (float)a.D;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (lane + 64 * c < nq) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float d = v[c][e] - mu;
+        ss += d * d;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  const float rr = rsqrtf(ss / (float)a.D + a.eps);
+  const int seg = (m + a.row0 < a.P) ? 0 : 1;
+  const float* sc = a.scale ? a.scale + seg * a.D : nullptr;
+  const float* sh = a.shift ? a.shift + seg * a.D : nullptr;
+  __bf16* out = (__bf16*)a.out + m * a.ldo;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int q = lane + 64 * c;
+    if (q >= nq) continue;
+    const int i = 4 * q;
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = (v[c][e] - mu) * rr;
+    if (a.w) {
+      const f32x4 w = *(const f32x4*)(a.w + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] *= w[e] + 1.0f;
+    }
+    if (sc) {
+      const f32x4 t = *(const f32x4*)(sc + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] *= 1.0f + t[e];
+    }
+    if (sh) {
+      const f32x4 t = *(const f32x4*)(sh + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] += t[e];
+    }
+    *(u32x2*)(out + i) = u32x2{to_bf16(y[0]) | (to_bf16(y[1]) << 16), to_bf16(y[2]) | (to_bf16(y[3]) << 16)};
+  }
+}
+
 __global__ __launch_bounds__(256) void k_zc_norm_mod(NormArgs a) {
   __shared__ float red[8];
   const int64_t m = blockIdx.x;
@@ -467,7 +537,13 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, int tile_n, hipStream_t s) {
 
 hipError_t launch_zc_norm_mod(const NormArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_zc_norm_mod, dim3((unsigned)a.M), dim3(256), 0, s, a);
+  const unsigned rows4 = (unsigned)((a.M + 3) / 4);
+  if (a.D <= 1024)
+    hipLaunchKernelGGL(k_norm_rows<4>, dim3(rows4), dim3(256), 0, s, a);
+  else if (a.D <= 4096)
+    hipLaunchKernelGGL(k_norm_rows<16>, dim3(rows4), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_zc_norm_mod, dim3((unsigned)a.M), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

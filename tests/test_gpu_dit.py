@@ -244,7 +244,7 @@ def test_gemm_full_size_sampled(name, M, N, K, epi):
 
 @pytest.mark.parametrize("M,D,row0,P,parts", [(300, 3072, 0, 170, "wss"), (129, 256, 40, 100, "wss"),
                                               (77, 132, 0, 0, "w"), (5, 3072, 10, 0, "s"),
-                                              (64, 512, 0, 64, "")])
+                                              (64, 512, 0, 64, ""), (9, 4104, 0, 5, "wss")])
 def test_zc_rmsnorm_mod(M, D, row0, P, parts):
     say(f"[norm mod] M={M} D={D} row0={row0} P={P} parts={parts!r}")
     x = qin.normal(CFG, 240, (M, D), std=3.0).astype(np.float32).astype(np.float64)

@@ -70,7 +70,7 @@ def f32v(idx, shape, std=1.0):
 # ------------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,D,row0,P,mod", [(300, 3072, 0, 170, True), (129, 256, 40, 100, True), (77, 132, 0, 0, False),
-                                            (64, 768, 0, 64, True)])
+                                            (64, 768, 0, 64, True), (9, 4104, 0, 5, True)])
 def test_layernorm_mod(M, D, row0, P, mod):
     say(f"[layernorm mod] M={M} D={D} row0={row0} P={P} mod={mod}")
     x = f32v(300, (M, D), 3.0) + 1.7   # rows with a large common offset: the mean matters
