@@ -50,7 +50,14 @@ def log(msg):
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the attention kernel's code lines (// comments and blank lines stripped), so that a
+    counter summary stays valid across comment-only edits."""
+    lines = []
+    for line in open(KERNEL_SRC).read().splitlines():
+        line = re.sub(r"//.*", "", line).rstrip()
+        if line.strip():
+            lines.append(line)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
 def traffic_from_profile():

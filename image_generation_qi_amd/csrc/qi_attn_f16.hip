@@ -9,8 +9,9 @@
 //   - one workgroup = 8 wavefronts = 256 query rows of one head; wave w owns rows 32w..32w+31.
 //     Two waves share each SIMD and one workgroup fills a CU, so every K/V tile brought into
 //     LDS serves 256 queries.
-//   - keys stream in tiles of 64 through LDS (two stages of K and V, 64 KB), copied whole with
-//     MUBUF buffer -> LDS loads (which keep the compute phases' LDS waits exact).  The tiles are
+//   - keys stream in tiles of 64 through LDS (four slots for K tiles and four for V tiles, 128 KB;
+//     K runs three tiles ahead, V one, and one wait and barrier end each pair of tiles), copied
+//     whole with MUBUF buffer -> LDS loads (which keep the compute phases' LDS waits exact).  The tiles are
 //     stored by the prep kernels in the order the MFMA operands are read (K as [16 dim chunks][64
 //     key slots][8 dims], V as [8 key chunks][128 dims][8 keys]): every operand read of 16 lanes
 //     is 256 contiguous bytes (no bank conflicts, no swizzle) at a constant offset from one
@@ -36,12 +37,13 @@
 //     interleave.
 //   - the Block-Causal mask is applied per tile from the row limits (see qi_common.h): tiles
 //     with no visible pair are never loaded, tiles with all pairs visible run unmasked.
-//   - grids under four rounds are balanced over the CUs with key chunks: a chunk of a unit's key
-//     tiles writes an unnormalised partial output with its (max, sum), merged by k_combine.
-//     Where the units split evenly over the 8 XCDs, each XCD runs its first units whole (one
-//     per CU) and cuts only the rest into chunks, so few rows pay for the partials.
-//   - blockIdx is remapped so that the 8 XCDs (each with its own L2) get contiguous runs of
-//     workgroups of the same head, which then share that head's K/V in L2.
+//   - launches whose query tiles all see the same keys (every cached step, step 1's target rows,
+//     unmasked layouts) are scheduled per XCD: block b runs on XCD b % 8, each XCD owns a
+//     contiguous run of query tiles (so the tiles of a head share its K/V in that XCD's L2),
+//     runs whole rounds of whole tiles (one per CU) and cuts only its remaining tiles into key
+//     chunks; a chunk writes an unnormalised partial output with its (max, sum), merged by
+//     k_combine, so few rows pay for the partials.  Tiles of unequal cost (block-causal prefix
+//     rows) run whole, longest first, in contiguous runs per XCD.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
