@@ -30,8 +30,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
-constexpr int GBK = 32;    // reduction slice per LDS stage
-constexpr int GSTAGES = 4; // LDS stages: copies run three slices ahead of the MFMAs
+constexpr int GBK = 64;    // reduction slice per LDS stage: copied rows are whole 128-byte lines
+constexpr int GSTAGES = 2; // LDS stages (2 x 64 KB at BN = 256)
 
 __device__ __forceinline__ uint32_t to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
@@ -50,32 +50,21 @@ __device__ __forceinline__ int xcd_order(int bid, int n) {
   return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + slot;
 }
 
-// s_waitcnt vmcnt(N) lgkmcnt(0): at most N of this wave's buffer -> LDS copies still in flight and
-// none of its LDS reads (expcnt left free)
-template <int N>
-__device__ __forceinline__ void wait_copies() {
-  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-
-__device__ __forceinline__ void load_lds16(const void* src, void* dst_wave_base) {
-  __builtin_amdgcn_global_load_lds((const glb_void*)src, (lds_void*)dst_wave_base, 16, 0, 0);
-}
-
-// Rows of a stage tile are 64 bytes (4 chunks of 16 bytes); chunk c of row r sits at chunk
-// position c ^ (((r >> 2) ^ (r >> 1)) & 3), so the rows that 16 lanes (or 8 lanes) read at one
-// logical chunk in one LDS cycle land in 16 (or 8) distinct 16-byte bank groups.
-__device__ __forceinline__ int gswz(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
+// Rows of a stage tile are 128 bytes (8 chunks of 16 bytes); chunk c of row r sits at chunk
+// position c ^ ((r ^ (r >> 3)) & 7), so the rows that 16 lanes (or 8 lanes) read at one logical
+// chunk in one LDS cycle land in 16 (or 8) distinct 16-byte bank groups.
+__device__ __forceinline__ int gswz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // ---- large-tile GEMM: 256 x BN workgroup tiles, two wavefronts per SIMD ----------------------
 // Eight waves in a 4 x 2 grid, each owning 64 tokens x BN/2 features as 2 x (BN/64) blocks of
 // 32 x 32 (128 accumulators at BN = 256, so two waves fit a SIMD and each hides the other's LDS
-// waits).  The reduction runs in slices of 32 through four LDS stages (4 x 32 KB at BN = 256):
-// the copies of slice kt + 4 are issued in slice kt, into the stage slice kt has just been read
-// from, so each copy has three slices of MFMA work to land in.  Stage tiles are copied by MUBUF
-// buffer -> LDS loads (exact waits while copies are in flight) into 64-byte rows with the chunk
-// swizzle above; rows past M or N fall outside the buffer resources and are not read (their
-// results are never stored).
+// waits).  The reduction runs in slices of 64 through two LDS stages (2 x 64 KB at BN = 256): the
+// copies of slice kt + 1 are issued at the start of slice kt into the other stage, and one wait
+// and barrier end each slice.  Slices of 64 make every copied row a whole 128-byte line (with
+// slices of 32 and four stages, half-line rows, the same kernel ran 3-9 % slower: the copies
+// cost by request, not by byte).  Stage tiles are copied by MUBUF buffer -> LDS loads into
+// 128-byte rows with the chunk swizzle above; rows past M or N fall outside the buffer resources
+// and are not read (their results are never stored).
 constexpr int BBM = 256;
 
 template <int EPI, int BN>
@@ -83,8 +72,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int WTM = 64, WTN = BN / 2;    // wave tile
   constexpr int MB = WTM / 32, NB = WTN / 32;
   constexpr int XT = BBM * GBK, WT = BN * GBK, ST = XT + WT;
-  constexpr int NXC = 2;                   // X copies of 1 KB (16 rows) per wave and stage
-  constexpr int NWT = BN / 16;             // W copies per stage, spread over the 8 waves
+  constexpr int NXC = 4;                   // X copies of 1 KB (8 rows) per wave and stage
+  constexpr int NWT = BN / 8;              // W copies per stage, spread over the 8 waves
   constexpr int NWC = (NWT + 7) / 8;       // most W copies of one wave
   __shared__ __attribute__((aligned(16))) __bf16 smem[GSTAGES * ST];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -105,37 +94,37 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)(a.M * a.ldx * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)a.w, (short)0, (int)(a.N * a.K * 2), 0x00020000);
-  // lane i of a copy of rows [r0, r0 + 16): row r0 + i/4, chunk position i%4.  X copy j of wave w
-  // covers rows 32w + 16j, W copy j rows 16(w + 8j).  (Arrays touched by the lambdas below have
+  // lane i of a copy of rows [r0, r0 + 8): row r0 + i/8, chunk position i%8.  X copy j of wave w
+  // covers rows 32w + 8j, W copy j rows 8(w + 8j).  (Arrays touched by the lambdas below have
   // fixed sizes: with sizes that depend on BN the host compiler silently drops the kernel instance
   // and its launch stub.)
-  int xo[2], wo[2];
+  int xo[4], wo[4];
 #pragma unroll
   for (int j = 0; j < NXC; ++j) {
-    const int row = 32 * wave + 16 * j + (lane >> 2);
-    xo[j] = (int)((m0 + row) * a.ldx * 2) + 16 * ((lane & 3) ^ gswz(row));
+    const int row = 32 * wave + 8 * j + (lane >> 3);
+    xo[j] = (int)((m0 + row) * a.ldx * 2) + 16 * ((lane & 7) ^ gswz(row));
   }
 #pragma unroll
   for (int j = 0; j < NWC; ++j) {
-    const int row = 16 * (wave + 8 * j) + (lane >> 2);
-    wo[j] = (int)((n0 + row) * a.K * 2) + 16 * ((lane & 3) ^ gswz(row));
+    const int row = 8 * (wave + 8 * j) + (lane >> 3);
+    wo[j] = (int)((n0 + row) * a.K * 2) + 16 * ((lane & 7) ^ gswz(row));
   }
   // all of this wave's copies of slice kt into stage st
   auto copy_slice = [&](int kt, int st) {
 #pragma unroll
     for (int j = 0; j < NXC; ++j) {
-      __bf16* dst = smem + st * ST + (32 * wave + 16 * j) * GBK;
+      __bf16* dst = smem + st * ST + (32 * wave + 8 * j) * GBK;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)dst, 16, xo[j], kt * GBK * 2, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < NWC; ++j) {
       if (j < nwc) {
-        __bf16* dst = smem + st * ST + XT + 16 * (wave + 8 * j) * GBK;
+        __bf16* dst = smem + st * ST + XT + 8 * (wave + 8 * j) * GBK;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)dst, 16, wo[j], kt * GBK * 2, 0, 0);
       }
     }
   };
-  // operands of reduction step kk (of 2) from stage st
+  // operands of reduction step kk (of 4) from stage st
   auto read_ops = [&](int st, int kk, bf8 (&xf)[2], bf8 (&wf)[4]) {
     const __bf16* X = smem + st * ST;
     const __bf16* W = X + XT;
@@ -157,14 +146,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int nb = 0; nb < NB; ++nb)
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], xf[mb], acc[mb][nb], 0, 0, 0);
   };
-  // "slice kt + 1 has landed": at most the copies of slices kt + 2 and kt + 3 still in flight
-  // (every slice issues the same copies: slices past the end re-copy the last slice into the
-  // stage just read, which nothing reads again)
-  auto wait_next = [&]() {
-    if (nwc == NWC) wait_copies<2 * (NXC + NWC)>();
-    else wait_copies<2 * (NXC + NWC - 1)>();
-  };
-
   f32x16 acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
@@ -175,31 +156,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int nkt = (int)(a.K / GBK);
   auto last = [&](int k) { return k < nkt ? k : nkt - 1; };
-#pragma unroll
-  for (int i = 0; i < GSTAGES; ++i) copy_slice(last(i), i);
+  copy_slice(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  bf8 xf0[2], wf0[4], xf1[2], wf1[4];
-  read_ops(0, 0, xf0, wf0);
+  bf8 xf[2][2], wf[2][4];
+  read_ops(0, 0, xf[0], wf[0]);
   for (int kt = 0; kt < nkt; ++kt) {
-    const int st = kt & (GSTAGES - 1);
-    read_ops(st, 1, xf1, wf1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(acc, xf0, wf0);
-    __builtin_amdgcn_sched_barrier(0);
-    // slice kt + 1 has landed for every wave, and every wave holds its operands of slice kt:
-    // stage st takes the copies of slice kt + 4
-    wait_next();
+    const int st = kt & 1;
+    copy_slice(last(kt + 1), st ^ 1);   // stage st ^ 1 was last read in slice kt - 1
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk < 3) read_ops(st, kk + 1, xf[(kk + 1) & 1], wf[(kk + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(acc, xf[kk & 1], wf[kk & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of slice kt + 1 have landed
     __syncthreads();
-    copy_slice(last(kt + GSTAGES), st);
-    read_ops((kt + 1) & (GSTAGES - 1), 0, xf0, wf0);   // (unused after the last slice)
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(acc, xf1, wf1);
-    __builtin_amdgcn_sched_barrier(0);
+    read_ops(st ^ 1, 0, xf[0], wf[0]);   // (unused after the last slice)
   }
-  // the re-copies of the last slices are still in flight: they land before the workgroup's LDS
-  // can pass to another workgroup
-  __builtin_amdgcn_s_waitcnt(0);
 
   // epilogue: acc[mb][nb][r] = y[m][n], m = m0 + 64wm + 32mb + l32,
   // n = n0 + WTN*wn + 32nb + 8(r/4) + 4g + r%4
