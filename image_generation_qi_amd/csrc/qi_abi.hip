@@ -134,6 +134,8 @@ AttnArgs attn_args(const qi_qkv* io, const qi_qkprep* prep, float scale) {
   a.eps = prep ? prep->eps : 0.f;
   a.o = io->o;
   a.o_stride = (int64_t)io->n_head * QI_HEAD_DIM;
+  a.lse = io->lse;
+  a.lse_stride = io->n_tok;
   a.n_q = (int32_t)io->n_tok;
   a.n_head = io->n_head;
   const double sc = softmax_scale(scale);
@@ -184,6 +186,7 @@ int run_attn_step1_f16(const AttnArgs& a, const SegTable& tab, int64_t P, int64_
   AttnArgs at = a;
   at.q = (const char*)a.q + P * a.q_stride * 2;
   at.o = (char*)a.o + P * a.o_stride * 2;
+  if (a.lse) at.lse = a.lse + P;
   if (a.cos_q) {
     at.cos_q = a.cos_q + P * (QI_HEAD_DIM / 2);
     at.sin_q = a.sin_q + P * (QI_HEAD_DIM / 2);

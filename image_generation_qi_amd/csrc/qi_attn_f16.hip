@@ -525,6 +525,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float lt = pair_sum(l_run);
   if (qok) {
     if (nsp == 1) {
+      // log-sum-exp in natural units: the scores are in units of log2(e) against the reference
+      if (a.lse && g == 0) a.lse[(int64_t)h * a.lse_stride + qrow] = (m_run + __log2f(lt)) * 0.6931471805599453f;
       const float inv = 1.0f / lt;
       uint16_t* op = (uint16_t*)a.o + (int64_t)qrow * a.o_stride + h * HD + 4 * g;
 #pragma unroll
@@ -556,8 +558,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // Chunked unit tu is the tl-th remaining unit of run x, in run order (see k_attn_f16); its
 // partial rows are [tu][chunk][256].
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                                                 uint16_t* __restrict__ o, int64_t o_stride, int n_q, int n_head,
-                                                 int n_split, int xcd_whole, int n_tail) {
+                                                 uint16_t* __restrict__ o, int64_t o_stride, float* __restrict__ lse,
+                                                 int64_t lse_stride, int n_q, int n_head, int n_split, int xcd_whole,
+                                                 int n_tail) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int d0 = (int)(gid & 15) * 8;
   const int64_t k = gid >> 4;                     // (chunked unit, row in its tile)
@@ -598,6 +601,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_
     }
   }
   const float inv = 1.0f / den;
+  if (lse && d0 == 0) lse[(int64_t)h * lse_stride + row] = (M + __log2f(den)) * 0.6931471805599453f;
   u32x4 w;
 #pragma unroll
   for (int j = 0; j < 4; ++j) w[j] = to_bf16(acc[2 * j] * inv) | (to_bf16(acc[2 * j + 1] * inv) << 16);
@@ -669,7 +673,8 @@ hipError_t launch_attn_f16(const AttnArgs& a_in, hipStream_t s) {
   if (e != hipSuccess || a.n_split == 1) return e;
   const int64_t threads = (int64_t)n_tail * BM * 16;
   hipLaunchKernelGGL(k_combine, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a.part_o, a.part_ml,
-                     (uint16_t*)a.o, a.o_stride, a.n_q, a.n_head, a.n_split, a.xcd_whole, n_tail);
+                     (uint16_t*)a.o, a.o_stride, a.lse, a.lse_stride, a.n_q, a.n_head, a.n_split, a.xcd_whole,
+                     n_tail);
   return hipGetLastError();
 }
 

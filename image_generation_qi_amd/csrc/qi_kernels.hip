@@ -366,6 +366,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
   float* orow = (float*)a.o + qi * a.o_stride + (int64_t)h * 128;
   orow[2 * lane] = o0 / l;
   orow[2 * lane + 1] = o1 / l;
+  if (a.lse && lane == 0) a.lse[(int64_t)h * a.lse_stride + qi] = m + logf(l);
 }
 
 }  // namespace

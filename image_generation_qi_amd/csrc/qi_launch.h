@@ -73,6 +73,8 @@ struct AttnArgs {
   // unnormalised partial output and its (max, sum) for a combine kernel.  launch_attn_f16 fills
   // n_split, split_tiles and xcd_whole from attn_f16_schedule.
   int32_t xcd_sched, reverse_qt;
+  float* lse;           // nullable: [n_head][lse_stride], row q of the launch at lse[h * lse_stride + q]
+  int64_t lse_stride;
   int32_t n_split, split_tiles, xcd_whole;
   float* part_o;       // [chunked unit][chunk][256 rows][128]
   float* part_ml;      // [chunked unit][chunk][256 rows][2]

@@ -58,7 +58,7 @@ class qi_kvcache(ctypes.Structure):
 
 class qi_qkv(ctypes.Structure):
     _fields_ = [("q", c_void_p), ("k", c_void_p), ("v", c_void_p), ("o", c_void_p), ("dtype", c_int),
-                ("n_tok", c_int64), ("n_head", c_int32), ("tok_stride", c_int64)]
+                ("n_tok", c_int64), ("n_head", c_int32), ("tok_stride", c_int64), ("lse", c_void_p)]
 
 
 class qi_qkprep(ctypes.Structure):
@@ -178,8 +178,8 @@ def make_layout(segments, head_dim: int = 128, bands=(16, 56, 56), theta: float 
     return L
 
 
-def make_qkv(q, k, v, o, dtype: int, n_tok: int, n_head: int, tok_stride: int) -> qi_qkv:
-    return qi_qkv(_p(q), _p(k), _p(v), _p(o), dtype, n_tok, n_head, tok_stride)
+def make_qkv(q, k, v, o, dtype: int, n_tok: int, n_head: int, tok_stride: int, lse=None) -> qi_qkv:
+    return qi_qkv(_p(q), _p(k), _p(v), _p(o), dtype, n_tok, n_head, tok_stride, _p(lse))
 
 
 def make_prep(cos_t=None, sin_t=None, q_rms_w=None, k_rms_w=None, eps: float = 1e-6) -> qi_qkprep:

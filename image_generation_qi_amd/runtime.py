@@ -108,11 +108,14 @@ class Attention:
         return Q.make_prep(cos, sin, q_w, k_w, eps), (cos, sin)
 
     def full(self, q, k, v, q_w=None, k_w=None, eps=1e-6, cache: Optional[KVCache] = None, layer: int = 0,
-             scale: float = 0.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+             scale: float = 0.0, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Step 1 over the layout; lse (optional fp32 [H][S]) receives each row's log-sum-exp."""
         if self.ws_full is None:
             self.ws_full = _ws(self.ws_full_bytes, self.device)
         o = out if out is not None else torch.empty((self.L.S, self.H, 128), dtype=q.dtype, device=self.device)
-        io = Q.make_qkv(q, k, v, o, self.dtype, self.L.S, self.H, self._stride(q))
+        if lse is not None:
+            assert lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == (self.H, self.L.S)
+        io = Q.make_qkv(q, k, v, o, self.dtype, self.L.S, self.H, self._stride(q), lse)
         prep, keep = self.prep(slice(0, self.L.S), q_w, k_w, eps)
         Q.check(Q.qi_attn_blockcausal_full(io, prep, self.L.c, scale, cache.c if cache else None, layer,
                                            self.ws_full, self.ws_full_bytes, stream_handle(self.device)),
@@ -125,12 +128,15 @@ class Attention:
                                        stream_handle(self.device)), "qi_attn_prefix_store")
 
     def cached(self, q_t, k_t, v_t, cache: KVCache, layer: int = 0, q_w=None, k_w=None, eps=1e-6,
-               scale: float = 0.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+               scale: float = 0.0, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """A cached target step; lse (optional fp32 [H][T]) receives each row's log-sum-exp."""
         if self.ws_cached is None:
             self.ws_cached = _ws(self.ws_cached_bytes, self.device)
         T = q_t.shape[0]
         o = out if out is not None else torch.empty((T, self.H, 128), dtype=q_t.dtype, device=self.device)
-        io = Q.make_qkv(q_t, k_t, v_t, o, self.dtype, T, self.H, self._stride(q_t))
+        if lse is not None:
+            assert lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == (self.H, T)
+        io = Q.make_qkv(q_t, k_t, v_t, o, self.dtype, T, self.H, self._stride(q_t), lse)
         prep, keep = self.prep(slice(self.L.P, self.L.P + T), q_w, k_w, eps)
         Q.check(Q.qi_attn_target_cached(io, prep, cache.c, layer, self.L.P, scale, self.ws_cached,
                                         self.ws_cached_bytes, stream_handle(self.device)), "qi_attn_target_cached")

@@ -111,7 +111,9 @@ typedef struct {
 } qi_kvcache;
 
 /* Attention operands.  q, k, v: device, token-major with `tok_stride`; o: device, dense
- * [n_tok][n_head*128].  dtype: QI_BF16 or QI_F32 for all four. */
+ * [n_tok][n_head*128].  dtype: QI_BF16 or QI_F32 for all four.  lse: NULL, or device fp32
+ * [n_head][n_tok] that receives each query row's log-sum-exp, ln(sum_k exp(scale * q.k)) over its
+ * visible keys (the softmax denominator; what a merge of attention over split key ranges needs). */
 typedef struct {
   const void* q;
   const void* k;
@@ -121,6 +123,7 @@ typedef struct {
   int64_t n_tok;
   int32_t n_head;
   int64_t tok_stride;
+  float* lse;
 } qi_qkv;
 
 /* Per-token preparation of Q and K before the contraction ([EDIT] section 6: QK-RMSNorm per

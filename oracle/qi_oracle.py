@@ -268,6 +268,26 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: Optional[np.nda
     return out
 
 
+def attention_lse(q: np.ndarray, k: np.ndarray, mask: Optional[np.ndarray] = None,
+                  scale: Optional[float] = None) -> np.ndarray:
+    """Per query row and head, the log-sum-exp of the scaled scores over the visible keys,
+    ln(sum_k exp(scale q.k)): the softmax denominator of the attention above, in natural log.
+    q: [Nq, H, d], k: [Nk, H, d], mask: [Nq, Nk] bool or None.  Returns [H, Nq]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    Nq, H, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.empty((H, Nq), dtype=np.float64)
+    for h in range(H):
+        s = (q[:, h, :] @ k[:, h, :].T) * scale
+        if mask is not None:
+            s = np.where(mask, s, -np.inf)
+        mx = s.max(axis=1, keepdims=True)
+        out[h] = (mx + np.log(np.exp(s - mx).sum(axis=1, keepdims=True)))[:, 0]
+    return out
+
+
 def prep_qk(x: np.ndarray, cos_t, sin_t, w=None, eps: float = 1e-6) -> np.ndarray:
     """Optional per-head QK-RMSNorm, then the 3D rotation (norm before RoPE, as in [EDIT]
     section 6: QK normalisation, then RoPE, then the joint concat)."""

@@ -452,3 +452,52 @@ def test_schedule_full_attention_chunked_prefix():
     torch.cuda.synchronize()
     ref, _ = O.step1(c.q.f64, c.k.f64, c.v.f64, wl.segments, c.cos, c.sin, None, None, full=True)
     check_close(to_np(o), ref, "bf16", "full attention, chunked prefix")
+
+
+# ---------------------------------------------------------------------------------------------
+# the log-sum-exp output (from whole query tiles in the attention kernel, from chunked ones in
+# the merge, and from the fp32 kernel):  |d| <= 5e-3 on the bf16 path, 1e-5 (1 + |ref|) on fp32
+# ---------------------------------------------------------------------------------------------
+
+def check_lse(got, ref, dtype, what):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    assert got.shape == ref.shape and np.all(np.isfinite(got)), what
+    err = np.abs(got - ref)
+    lim = 5e-3 if dtype == "bf16" else 1e-5 * (1.0 + np.abs(ref))
+    say(f"  {what}: max |d lse| = {err.max():.2e}")
+    assert np.all(err <= lim), (what, err.max())
+
+
+@pytest.mark.parametrize("name,dtype,full", [("cfg0", "f32", False), ("multi_tile", "bf16", False),
+                                             ("ragged_tiles", "bf16", True), ("two_text_runs", "bf16", False)])
+def test_lse_step1(name, dtype, full):
+    wl = wl_of(name, dtype=dtype, n_head=2, qk=True) if name in EDGE else qin.WORKLOADS[name]
+    say(f"lse step 1 {name} dtype={wl.dtype} full={full}")
+    c = Case(wl)
+    L = rt.Layout(wl.segments, DEV, attention=Q.QI_ATTN_FULL if full else Q.QI_ATTN_BLOCK_CAUSAL)
+    att = rt.Attention(L, wl.n_head, rt.dtype_code(wl.dtype), DEV)
+    lse = torch.full((wl.n_head, c.S), float("nan"), dtype=torch.float32, device=DEV)
+    att.full(c.qd, c.kd, c.vd, c.qw_d, c.kw_d, lse=lse)
+    torch.cuda.synchronize()
+    qr = O.prep_qk(c.q.f64, c.cos, c.sin, c.qw)
+    kr = O.prep_qk(c.k.f64, c.cos, c.sin, c.kw)
+    ref = O.attention_lse(qr, kr, None if full else O.mask_dense(wl.segments))
+    check_lse(lse.cpu().numpy(), ref, wl.dtype, f"{name} step-1 lse")
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg3"])
+def test_lse_cached(name):
+    wl = qin.WORKLOADS[name]
+    say(f"lse cached step {name} T={wl.T}")
+    c = Case(wl)
+    L, att = make(wl)
+    P, T = c.P, c.T
+    cache = rt.KVCache(1, wl.n_head, P, Q.QI_BF16, DEV)
+    att.store(c.kd[:P], c.vd[:P], cache, 0, c.kw_d)
+    lse = torch.full((wl.n_head, T), float("nan"), dtype=torch.float32, device=DEV)
+    att.cached(c.qd[P:], c.kd[P:], c.vd[P:], cache, 0, c.qw_d, c.kw_d, lse=lse)
+    torch.cuda.synchronize()
+    rows = np.arange(T) if T <= 1024 else sample_rows(0, T, 64, 9)
+    kr = O.prep_qk(c.k.f64, c.cos, c.sin, c.kw)
+    qr = O.prep_qk(c.q.f64[P:][rows], c.cos[P:][rows], c.sin[P:][rows], c.qw)
+    check_lse(lse.cpu().numpy()[:, rows], O.attention_lse(qr, kr), "bf16", f"{name} cached lse")

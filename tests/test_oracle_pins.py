@@ -843,3 +843,50 @@ def test_planted_v1_mistake_is_caught(i, monkeypatch):
         assert not _fails(pin), f"pin {pin} fails on the unmodified oracle"
     monkeypatch.setattr(O, name, bad)
     assert any(_fails(pin) for pin in pins), f"planted mistake in {name} not caught"
+
+
+# ---------------------------------------------------------------------------------------------
+# the softmax denominator (log-sum-exp) output
+# ---------------------------------------------------------------------------------------------
+
+def test_attention_lse_closed_forms():
+    rng = np.random.default_rng(21)
+    k = rng.standard_normal((9, 2, 128))
+    mask = np.tril(np.ones((5, 9), bool), 3)             # row i sees keys 0 .. i + 3
+    # zero queries: every visible score is 0, so lse = ln(number of visible keys)
+    lse0 = O.attention_lse(np.zeros((5, 2, 128)), k, mask)
+    assert np.allclose(lse0, np.log(mask.sum(axis=1))[None, :], atol=1e-14)
+    # one visible key: lse = its scaled score
+    q = rng.standard_normal((5, 2, 128))
+    one = np.zeros((5, 9), bool)
+    one[np.arange(5), [0, 3, 8, 2, 5]] = True
+    lse1 = O.attention_lse(q, k, one)
+    for i, j in enumerate([0, 3, 8, 2, 5]):
+        for h in range(2):
+            assert abs(lse1[h, i] - float(q[i, h] @ k[j, h]) / math.sqrt(128)) < 1e-12
+
+
+def test_attention_lse_gives_the_softmax_weights_bruteforce():
+    rng = np.random.default_rng(22)
+    q, k, v = (rng.standard_normal((n, 1, 128)) for n in (3, 6, 6))
+    lse = O.attention_lse(q, k)
+    o = O.attention(q, k, v)
+    for i in range(3):
+        acc = np.zeros(128)
+        for j in range(6):
+            s = sum(q[i, 0, d] * k[j, 0, d] for d in range(128)) / math.sqrt(128)
+            acc += math.exp(s - lse[0, i]) * v[j, 0]
+        assert np.allclose(acc, o[i, 0], atol=1e-12)
+
+
+def test_attention_lse_merges_split_key_ranges():
+    # attention over keys [0, n) from the halves [0, n1) and [n1, n) and their log-sum-exps
+    rng = np.random.default_rng(23)
+    q, k, v = rng.standard_normal((7, 2, 128)), rng.standard_normal((40, 2, 128)), rng.standard_normal((40, 2, 128))
+    n1 = 17
+    o1, o2 = O.attention(q, k[:n1], v[:n1]), O.attention(q, k[n1:], v[n1:])
+    l1, l2 = O.attention_lse(q, k[:n1]), O.attention_lse(q, k[n1:])
+    L = np.logaddexp(l1, l2)
+    w1, w2 = np.exp(l1 - L).T[:, :, None], np.exp(l2 - L).T[:, :, None]
+    assert np.allclose(w1 * o1 + w2 * o2, O.attention(q, k, v), atol=1e-12)
+    assert np.allclose(L, O.attention_lse(q, k), atol=1e-12)
