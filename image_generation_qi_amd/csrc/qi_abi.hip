@@ -244,6 +244,9 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
   if (!io->o) return QI_ERR_ARG;
   if (!aligned16(io->o)) return QI_ERR_ALIGN;
   if (io->n_tok != li.S) return QI_ERR_SHAPE;
+  // the bf16 path addresses each key source through a buffer resource with 32-bit byte offsets
+  if (io->dtype == QI_BF16 && (li.P > QI_MAX_SOURCE_KEYS || li.T > QI_MAX_SOURCE_KEYS)) return QI_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(io->lse) & 3) return QI_ERR_ALIGN;
   if ((st = check_prep(prep)) != QI_OK) return st;
   if (cache && (st = check_cache(cache, io->dtype, io->n_head, layer, li.P)) != QI_OK) return st;
   if (!workspace) return QI_ERR_ARG;
@@ -340,6 +343,8 @@ int qi_attn_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvca
   if ((st = check_prep(prep)) != QI_OK) return st;
   if ((st = check_cache(cache, io->dtype, io->n_head, layer, P)) != QI_OK) return st;
   if (P + io->n_tok > INT32_MAX) return QI_ERR_SHAPE;
+  if (io->dtype == QI_BF16 && (P > QI_MAX_SOURCE_KEYS || io->n_tok > QI_MAX_SOURCE_KEYS)) return QI_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(io->lse) & 3) return QI_ERR_ALIGN;
   if (!workspace) return QI_ERR_ARG;
   if (!aligned16(workspace)) return QI_ERR_ALIGN;
   if (workspace_bytes < qi_attn_cached_workspace_bytes(io->dtype, io->n_tok, io->n_head)) return QI_ERR_CAPACITY;

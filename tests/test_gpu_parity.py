@@ -501,3 +501,24 @@ def test_lse_cached(name):
     kr = O.prep_qk(c.k.f64, c.cos, c.sin, c.kw)
     qr = O.prep_qk(c.q.f64[P:][rows], c.cos[P:][rows], c.sin[P:][rows], c.qw)
     check_lse(lse.cpu().numpy()[:, rows], O.attention_lse(qr, kr), "bf16", f"{name} cached lse")
+
+
+def test_long_prefix_cached():
+    # a 262,147-key prefix (4,097 key tiles, the last one ragged) and a 64-token target, 1 head
+    segs = (qin.text(262147, bidir=True), qin.image(8, 8, 0))
+    wl = qin.small_workload("long_prefix", segs, n_head=1, dtype="bf16")
+    c = Case(wl)
+    P, T = c.P, c.T
+    say(f"long prefix: P={P} T={T}")
+    L, att = make(wl)
+    cache = rt.KVCache(1, 1, P, Q.QI_BF16, DEV)
+    att.store(c.kd[:P], c.vd[:P], cache, 0)
+    lse = torch.empty((1, T), dtype=torch.float32, device=DEV)
+    ot = att.cached(c.qd[P:], c.kd[P:], c.vd[P:], cache, 0, lse=lse)
+    o1 = att.full(c.qd, c.kd, c.vd)
+    torch.cuda.synchronize()
+    kr = O.rotate(c.k.f64, c.cos, c.sin)
+    qr = O.rotate(c.q.f64[P:], c.cos[P:], c.sin[P:])
+    check_close(to_np(ot), O.attention(qr, kr, c.v.f64), "bf16", "long-prefix target rows")
+    check_lse(lse.cpu().numpy(), O.attention_lse(qr, kr), "bf16", "long-prefix lse")
+    assert torch.equal(ot, o1[P:]), "cached step != step-1 target rows"

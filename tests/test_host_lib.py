@@ -184,6 +184,7 @@ def _cached(io, prep, cache, layer=0, P=50, ws=FAKE + 0x8000, wsb=1 << 40):
     ("layer_neg", Q.QI_ERR_CAPACITY), ("P_over_cap", Q.QI_ERR_CAPACITY), ("cache_dtype", Q.QI_ERR_DTYPE),
     ("cache_heads", Q.QI_ERR_SHAPE), ("ws_small", Q.QI_ERR_CAPACITY), ("ws_null", Q.QI_ERR_ARG),
     ("cos_without_sin", Q.QI_ERR_ARG), ("null_cache", Q.QI_ERR_ARG), ("bad_eps", Q.QI_ERR_ARG),
+    ("prefix_over_max", Q.QI_ERR_SHAPE), ("target_over_max", Q.QI_ERR_SHAPE), ("lse_misaligned", Q.QI_ERR_ALIGN),
 ])
 def test_target_cached_rejects(case, want):
     io, prep, cache = _good()
@@ -208,6 +209,13 @@ def test_target_cached_rejects(case, want):
     elif case == "bad_eps":
         prep.q_rms_w = FAKE + 0x9000
         prep.eps = float("nan")
+    elif case == "prefix_over_max":   # within the cache's capacity, past what 32-bit offsets reach
+        cache.p_cap = 1 << 24
+        kw["P"] = Q.QI_MAX_SOURCE_KEYS + 1
+    elif case == "target_over_max":
+        io.n_tok = Q.QI_MAX_SOURCE_KEYS + 1
+    elif case == "lse_misaligned":
+        io.lse = FAKE + 0xA002
     if case == "null_cache":
         st = Q.lib().qi_attn_target_cached(ctypes.byref(io), ctypes.byref(prep), None, 0, 50, 0.0, FAKE, 1 << 40, None)
     else:
@@ -239,6 +247,19 @@ def test_full_rejects_bad_layouts(case, want):
     assert st == want, (case, Q.qi_status_str(st))
     if want == Q.QI_ERR_LAYOUT:
         assert Q.lib().qi_layout_tokens(ctypes.byref(L), None, None, None) == Q.QI_ERR_LAYOUT
+
+
+def test_full_rejects_sources_over_the_key_limit():
+    # a prefix one key past the bf16 path's limit (fp32 I/O has no such limit, but this is bf16)
+    n = Q.QI_MAX_SOURCE_KEYS + 1 - 16
+    L = Q.make_layout([qin.text(n, bidir=True), qin.image(4, 4, 1), qin.image(4, 4, 0)])
+    S = n + 32
+    io = Q.qi_qkv(FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000, Q.QI_BF16, S, 2, 256)
+    assert Q.qi_attn_blockcausal_full(io, None, L, 0.0, None, 0, FAKE + 0x8000, 1 << 40, None) == Q.QI_ERR_SHAPE
+    assert Q.qi_layout_tokens(L)[1] == Q.QI_MAX_SOURCE_KEYS + 1
+    # the header's limit is the binding's
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "qi.h")).read()
+    assert re.search(r"#define QI_MAX_SOURCE_KEYS (\d+)", hdr).group(1) == str(Q.QI_MAX_SOURCE_KEYS)
 
 
 def test_other_entry_points_reject():
