@@ -100,7 +100,7 @@ const char* qi_status_str(int status) {
   }
 }
 
-int qi_version(void) { return 1; }
+int qi_version(void) { return 2; }
 
 int qi_layout_tokens(const qi_layout* layout, int64_t* S, int64_t* P, int64_t* T) {
   LayoutInfo li;

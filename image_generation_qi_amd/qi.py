@@ -24,6 +24,7 @@ QI_SEG_TEXT, QI_SEG_IMAGE, QI_SEG_TEXT_BIDIR = 0, 1, 2
 QI_EPI_STORE, QI_EPI_STORE_F32, QI_EPI_GATED_RESIDUAL, QI_EPI_SWIGLU, QI_EPI_GELU = 0, 1, 2, 3, 4
 QI_EPI_GATED_RESIDUAL_LINEAR = 5
 QI_MAX_SOURCE_KEYS = 8388607   # keys per source of the bf16 attention (include/qi.h)
+QI_ABI_VERSION = 2             # the qi_version() these bindings are written against
 QI_ATTN_BLOCK_CAUSAL, QI_ATTN_FULL = 0, 1
 QI_HEAD_DIM = 128
 
@@ -133,6 +134,9 @@ def lib():
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
+        if L.qi_version() != QI_ABI_VERSION:
+            raise QiLibraryMissing(f"{LIB_PATH} has ABI version {L.qi_version()}, these bindings need "
+                                   f"{QI_ABI_VERSION}: rebuild it")
         _lib = L
     return _lib
 

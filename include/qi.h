@@ -5,10 +5,13 @@
  *
  * Sources, cited by page title and section:
  *   [OV]   "Qwen-Image-2.1: how an image is made from noise" course overview (OpenArchLab):
- *          block cards 2A, 3A, 3C, 4A, 6A, 6B and the learning goals.
+ *          block cards 2A, 3A, 3B, 3C, 4A, 5A, 6A, 6B and the learning goals.
+ *   [1B]   "1B - Qwen3-VL Context & Zero-Center RMSNorm" (OpenArchLab), sections 1-3
+ *          (ZeroCenterRMSNorm, the context TextProjection).
  *   [3A]   "3A - 3D Axial RoPE (16, 56, 56) & Zero-Centered Grid" (OpenArchLab), sections 1-4.
- *   [EDIT] "QwenImageTransformer2DModel source reading (Qwen-Image-Edit)", sections 6 (joint
- *          attention processor), 7.1-7.3 (three-axis RoPE tables and centred grids).
+ *   [EDIT] "QwenImageTransformer2DModel source reading (Qwen-Image-Edit)", sections 5.1-5.2
+ *          (timestep embedding, modulation, the dual-stream block), 6 (joint attention
+ *          processor), 7.1-7.3 (three-axis RoPE tables and centred grids), 10 (Edit-Plus).
  *
  * Conventions for every entry point:
  *   - Every call returns a qi_status.  Arguments are checked before anything is launched; on
@@ -146,7 +149,7 @@ typedef struct {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* qi_status_str(int status);
 
-/* Library ABI version (increments on any signature change). */
+/* Library ABI version (increments on any signature or struct change; 2 added qi_qkv.lse). */
 int qi_version(void);
 
 /* Token counts of a layout: S = all, P = prefix (all but the last segment), T = target.
