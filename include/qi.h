@@ -213,8 +213,9 @@ int qi_rope3d_apply(void* x, qi_dtype dtype, int64_t n_tok, int32_t n_head, int6
                     void* stream);
 
 /* Step 1: full Block-Causal attention over all S tokens of `layout` ([OV] cards 3C, 4A, 6A):
- * O = softmax(mask(Q K^T * scale)) V with Q and K prepared per `prep`.  scale <= 0 selects
- * 1/sqrt(128).  io->n_tok must equal the layout's S.  If `cache` is not NULL the prepared
+ * O = softmax(mask(Q K^T * scale)) V with Q and K prepared per `prep` (no mask for a
+ * QI_ATTN_FULL layout, the v1 / Edit joint attention).  scale <= 0 selects 1/sqrt(128).
+ * io->n_tok must equal the layout's S; io->lse, if given, receives every row's log-sum-exp.  If `cache` is not NULL the prepared
  * prefix K and V (tokens 0..P-1) are also written to cache layer `layer`, rows 0..P-1, in the
  * same pass (the prefix store of [OV] card 6A).  workspace: device, at least
  * qi_attn_full_workspace_bytes(layout, dtype, n_head) bytes, contents scratch. */
@@ -233,7 +234,8 @@ int qi_attn_prefix_store(const void* k, const void* v, qi_dtype dtype, int64_t P
  * attend, without a mask (the target sees every token, [OV] card 3C), to the P cached prefix
  * keys/values of cache layer `layer` followed by the T fresh target keys/values.  prep tables
  * hold the target rows (table rows P..P+T-1 of the layout).  scale <= 0 selects 1/sqrt(128).
- * workspace: device, at least qi_attn_cached_workspace_bytes(dtype, T, n_head) bytes. */
+ * workspace: device, at least qi_attn_cached_workspace_bytes(dtype, T, n_head) bytes.
+ * io->lse, if given, receives the target rows' log-sum-exps over all P + T keys. */
 int qi_attn_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvcache* cache,
                           int32_t layer, int64_t P, float scale, void* workspace,
                           int64_t workspace_bytes, void* stream);
