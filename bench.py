@@ -7,7 +7,7 @@ prefix cache, so the 6.85 GB of caches cannot sit in the 256 MB Infinity Cache) 
 one Euler update of the 4096 x 64 fp32 latent.  Inputs are synthetic (torch RNG, seeded) and
 resident in HBM before timing starts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg3|cfg3_t512|cfg2] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload txt1024_4ref64_tgt64|txt512_4ref64_tgt64|txt512_tgt64] [--no-cpu]
     python bench.py --dit [--layers L] [--steps K]     # full single-stream layer steps (see below)
     python bench.py --v1edit [--steps K]                # v1 / Edit-Plus full joint attention
 
@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA, published
 METRIC = "attention TFLOP/s + % bf16 MFMA peak, target-only cached step, 4096 tgt tokens"
 N_LAYERS = 32
-PROFILE = os.path.join(ROOT, "profiles", "attn_f16_cfg3_target_counters.md")
+PROFILE = os.path.join(ROOT, "profiles", "attn_f16_4096q_21504k_counters.md")
 KERNEL_SRC = os.path.join(ROOT, "image_generation_qi_amd", "csrc", "qi_attn_f16.hip")
 
 
@@ -143,7 +143,7 @@ def dit_bench(args):
     import qi_inputs as qin
     from image_generation_qi_amd import runtime as rt
 
-    wl = qin.WORKLOADS["cfg4"]
+    wl = qin.WORKLOADS["txt512_10ref32_tgt64"]
     dev = "cuda:0"
     D, F, H, NL = 3072, 8192, 24, args.layers
     S, P, T = wl.S, wl.P, wl.T
@@ -294,7 +294,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="cfg3", choices=["cfg3", "cfg3_t512", "cfg2"])
+    ap.add_argument("--workload", default="txt1024_4ref64_tgt64", choices=["txt1024_4ref64_tgt64", "txt512_4ref64_tgt64", "txt512_tgt64"])
     ap.add_argument("--layers", type=int, default=N_LAYERS)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--step1", action="store_true", help="also time one full step-1 attention per layer")

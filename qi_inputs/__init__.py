@@ -11,13 +11,13 @@ Workloads (joint sequence order: text first, then reference images, target
 image last; the 1024x1024 latent grid is 64x64 tokens, "Qwen-Image-Edit"
 page, section 8.2 shape table):
 
-  cfg0  fp32, 2 heads; text 16 + ref 4x4 (frame 1) + target 4x4 (frame 0)
-  cfg1  bf16, 24 heads; text 256 + ref 32x32 (frame 1) + target 32x32
-  cfg2  bf16, 24 heads; text 512 + target 64x64
-  cfg3  bf16, 24 heads; text 1024 + 4 refs 64x64 (frames 1..4) + target 64x64
+  tiny_f32  fp32, 2 heads; text 16 + ref 4x4 (frame 1) + target 4x4 (frame 0)
+  txt256_ref32_tgt32  bf16, 24 heads; text 256 + ref 32x32 (frame 1) + target 32x32
+  txt512_tgt64  bf16, 24 heads; text 512 + target 64x64
+  txt1024_4ref64_tgt64  bf16, 24 heads; text 1024 + 4 refs 64x64 (frames 1..4) + target 64x64
         (17,408 prefix tokens, 21,504 keys)
-  cfg3_t512  the same with 512 text tokens (16,896 prefix, 20,992 keys)
-  cfg4  bf16, 24 heads; text 512 + 10 refs 32x32 (frames 1..10) + target 64x64
+  txt512_4ref64_tgt64  the same with 512 text tokens (16,896 prefix, 20,992 keys)
+  txt512_10ref32_tgt64  bf16, 24 heads; text 512 + 10 refs 32x32 (frames 1..10) + target 64x64
 """
 from __future__ import annotations
 
@@ -82,15 +82,15 @@ class Workload:
 
 
 WORKLOADS = {
-    "cfg0": Workload("cfg0", 0, (text(16), image(4, 4, 1), image(4, 4, 0)), n_head=2, dtype="f32",
+    "tiny_f32": Workload("tiny_f32", 0, (text(16), image(4, 4, 1), image(4, 4, 0)), n_head=2, dtype="f32",
                      n_steps=2),
-    "cfg1": Workload("cfg1", 1, (text(256), image(32, 32, 1), image(32, 32, 0)), qk_rmsnorm=True),
-    "cfg2": Workload("cfg2", 2, (text(512), image(64, 64, 0))),
-    "cfg3": Workload("cfg3", 3, (text(1024),) + tuple(image(64, 64, f) for f in (1, 2, 3, 4))
+    "txt256_ref32_tgt32": Workload("txt256_ref32_tgt32", 1, (text(256), image(32, 32, 1), image(32, 32, 0)), qk_rmsnorm=True),
+    "txt512_tgt64": Workload("txt512_tgt64", 2, (text(512), image(64, 64, 0))),
+    "txt1024_4ref64_tgt64": Workload("txt1024_4ref64_tgt64", 3, (text(1024),) + tuple(image(64, 64, f) for f in (1, 2, 3, 4))
                      + (image(64, 64, 0),)),
-    "cfg3_t512": Workload("cfg3_t512", 3, (text(512),) + tuple(image(64, 64, f) for f in (1, 2, 3, 4))
+    "txt512_4ref64_tgt64": Workload("txt512_4ref64_tgt64", 3, (text(512),) + tuple(image(64, 64, f) for f in (1, 2, 3, 4))
                           + (image(64, 64, 0),)),
-    "cfg4": Workload("cfg4", 4, (text(512),) + tuple(image(32, 32, f) for f in range(1, 11))
+    "txt512_10ref32_tgt64": Workload("txt512_10ref32_tgt64", 4, (text(512),) + tuple(image(32, 32, f) for f in range(1, 11))
                      + (image(64, 64, 0),)),
 }
 

@@ -437,7 +437,7 @@ def test_sampling_loop_small():
 # ------------------------------------------------------------------------------------------------
 
 def test_full_size_layer_stages_sampled():
-    wl = qin.WORKLOADS["cfg4"]
+    wl = qin.WORKLOADS["txt512_10ref32_tgt64"]
     D, F, H = 3072, 8192, 24
     say(f"[layer full] S={wl.S} P={wl.P} T={wl.T}")
     model, sh, layers64 = make_model(wl.segments, D, F, 1, cfg=wl.cfg_id)

@@ -113,7 +113,7 @@ def wl_of(name, dtype="bf16", n_head=2, qk=False):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("norm", [False, True])
 def test_rope3d_apply(dtype, norm):
-    wl = qin.small_workload("rope", qin.WORKLOADS["cfg1"].segments, n_head=24, dtype=dtype, qk_rmsnorm=norm)
+    wl = qin.small_workload("rope", qin.WORKLOADS["txt256_ref32_tgt32"].segments, n_head=24, dtype=dtype, qk_rmsnorm=norm)
     say(f"rope3d_apply dtype={dtype} norm={norm} S={wl.S}")
     c = Case(wl)
     L = rt.Layout(wl.segments, DEV)
@@ -140,7 +140,7 @@ def test_rope3d_apply(dtype, norm):
 # step 1 (full block-causal) and the prefix cache
 # ---------------------------------------------------------------------------------------------
 
-STEP1_CASES = [("cfg0", "f32", False), ("cfg1", "bf16", True)] + \
+STEP1_CASES = [("tiny_f32", "f32", False), ("txt256_ref32_tgt32", "bf16", True)] + \
               [(n, "bf16", False) for n in EDGE] + [("ragged_tiles", "f32", True), ("multi_tile", "bf16", True)]
 
 
@@ -168,7 +168,7 @@ def test_step1_parity_and_cache(name, dtype, qk):
                        o2.view(torch.int16) if o2.dtype == torch.bfloat16 else o2), "cache on/off differ"
 
 
-@pytest.mark.parametrize("name", ["cfg1", "ragged_tiles", "two_text_runs"])
+@pytest.mark.parametrize("name", ["txt256_ref32_tgt32", "ragged_tiles", "two_text_runs"])
 def test_prefix_store_bytes_match_step1_store(name):
     wl = wl_of(name, qk=True)
     say(f"prefix_store {name}")
@@ -185,7 +185,7 @@ def test_prefix_store_bytes_match_step1_store(name):
 
 
 def test_prefix_bit_identical_under_target_perturbation():
-    for name in ("cfg1", "ragged_tiles", "multi_tile"):
+    for name in ("txt256_ref32_tgt32", "ragged_tiles", "multi_tile"):
         wl = wl_of(name, qk=True)
         say(f"prefix bit-identity {name}")
         c = Case(wl)
@@ -202,7 +202,7 @@ def test_prefix_bit_identical_under_target_perturbation():
 
 
 def test_repeat_runs_bit_identical():
-    wl = qin.WORKLOADS["cfg1"]
+    wl = qin.WORKLOADS["txt256_ref32_tgt32"]
     c = Case(wl)
     L, att = make(wl)
     outs = [att.full(c.qd, c.kd, c.vd, c.qw_d, c.kw_d).clone() for _ in range(3)]
@@ -211,7 +211,7 @@ def test_repeat_runs_bit_identical():
 
 
 def test_kernel_timing_hooks_record_each_call():
-    wl = qin.WORKLOADS["cfg1"]
+    wl = qin.WORKLOADS["txt256_ref32_tgt32"]
     c = Case(wl)
     L, att = make(wl)
     att.full(c.qd, c.kd, c.vd, c.qw_d, c.kw_d)
@@ -232,7 +232,7 @@ def test_kernel_timing_hooks_record_each_call():
 # cached target-only steps
 # ---------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name,dtype,qk", [("cfg0", "f32", False), ("cfg1", "bf16", True), ("ragged_tiles", "bf16", True),
+@pytest.mark.parametrize("name,dtype,qk", [("tiny_f32", "f32", False), ("txt256_ref32_tgt32", "bf16", True), ("ragged_tiles", "bf16", True),
                                            ("target_only", "bf16", False), ("one_token_segments", "bf16", False),
                                            ("multi_tile", "f32", False)])
 def test_cached_step_parity_and_equals_full(name, dtype, qk):
@@ -259,9 +259,9 @@ def test_cached_step_parity_and_equals_full(name, dtype, qk):
     assert torch.equal(a, b), "cached step differs from full recompute"
 
 
-def test_cfg1_eight_step_loop_with_euler():
-    wl = qin.WORKLOADS["cfg1"]
-    say("cfg1 8-step loop")
+def test_eight_step_loop_with_euler():
+    wl = qin.WORKLOADS["txt256_ref32_tgt32"]
+    say("txt256_ref32_tgt32 8-step loop")
     c = Case(wl)
     L, att = make(wl)
     P, T = c.P, c.T
@@ -316,7 +316,7 @@ def full_size_wl(name):
     return qin.WORKLOADS[name] if name in qin.WORKLOADS else qin.INTERLEAVED_WORKLOADS[name]
 
 
-@pytest.mark.parametrize("name", ["cfg2", "cfg3", "cfg3_t512", "interleaved10"])
+@pytest.mark.parametrize("name", ["txt512_tgt64", "txt1024_4ref64_tgt64", "txt512_4ref64_tgt64", "interleaved10"])
 def test_full_size_target_step_sampled(name):
     wl = full_size_wl(name)
     say(f"full-size target step {name} S={wl.S} P={wl.P} T={wl.T}")
@@ -337,7 +337,7 @@ def test_full_size_target_step_sampled(name):
     check_close(to_np(ot[rows]), ref, "bf16", f"{name} target rows")
 
 
-@pytest.mark.parametrize("name", ["cfg2", "cfg3", "interleaved10"])
+@pytest.mark.parametrize("name", ["txt512_tgt64", "txt1024_4ref64_tgt64", "interleaved10"])
 def test_full_size_step1_sampled(name):
     wl = full_size_wl(name)
     say(f"full-size step 1 {name} S={wl.S}")
@@ -468,7 +468,7 @@ def check_lse(got, ref, dtype, what):
     assert np.all(err <= lim), (what, err.max())
 
 
-@pytest.mark.parametrize("name,dtype,full", [("cfg0", "f32", False), ("multi_tile", "bf16", False),
+@pytest.mark.parametrize("name,dtype,full", [("tiny_f32", "f32", False), ("multi_tile", "bf16", False),
                                              ("ragged_tiles", "bf16", True), ("two_text_runs", "bf16", False)])
 def test_lse_step1(name, dtype, full):
     wl = wl_of(name, dtype=dtype, n_head=2, qk=True) if name in EDGE else qin.WORKLOADS[name]
@@ -485,7 +485,7 @@ def test_lse_step1(name, dtype, full):
     check_lse(lse.cpu().numpy(), ref, wl.dtype, f"{name} step-1 lse")
 
 
-@pytest.mark.parametrize("name", ["cfg1", "cfg3"])
+@pytest.mark.parametrize("name", ["txt256_ref32_tgt32", "txt1024_4ref64_tgt64"])
 def test_lse_cached(name):
     wl = qin.WORKLOADS[name]
     say(f"lse cached step {name} T={wl.T}")

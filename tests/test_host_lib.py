@@ -78,7 +78,7 @@ def test_positions_text_pos0_override():
     assert np.array_equal(pos.astype(np.int64), O.positions(segs, text_pos0=100))
 
 
-@pytest.mark.parametrize("name", ["cfg0", "cfg1", "cfg2", "cfg3", "odd_grids", "two_text_runs", "bidir_text"])
+@pytest.mark.parametrize("name", ["tiny_f32", "txt256_ref32_tgt32", "txt512_tgt64", "txt1024_4ref64_tgt64", "odd_grids", "two_text_runs", "bidir_text"])
 def test_rope_tables_bit_exact(name):
     segs = all_layouts()[name]
     L = Q.make_layout(segs)
@@ -102,7 +102,7 @@ def test_rope_tables_other_theta_and_bands():
     assert np.array_equal(c.view(np.uint32), rc.view(np.uint32)) and np.array_equal(s.view(np.uint32), rs.view(np.uint32))
 
 
-@pytest.mark.parametrize("name", ["cfg0", "cfg1", "cfg2"] + sorted(EDGE_LAYOUTS))
+@pytest.mark.parametrize("name", ["tiny_f32", "txt256_ref32_tgt32", "txt512_tgt64"] + sorted(EDGE_LAYOUTS))
 @pytest.mark.parametrize("tiles", [(128, 64), (1, 64), (7, 5), (64, 64), (2, 2)])
 def test_blockmap_bit_exact(name, tiles):
     segs = all_layouts()[name]
@@ -126,15 +126,15 @@ def test_tile_shape_and_sizes():
     assert Q.qi_attn_schedule(8704, 24) == (5, 96, 48)      # 816 tiles: 102 per XCD
     assert Q.qi_attn_schedule(101 * 256, 5) == (1, 32, 0)   # 505 tiles: the remaining 32 / 31 run whole
     assert Q.qi_attn_schedule(0, 24) == (1, 0, 0)
-    L3 = Q.make_layout(qin.WORKLOADS["cfg3"].segments)
+    L3 = Q.make_layout(qin.WORKLOADS["txt1024_4ref64_tgt64"].segments)
     PART = 256 * 130 * 4   # fp32 partials of one chunk of one query tile: 256 rows x (128 values + max + sum)
     # 4096-token target: 16 x 24 = 384 query tiles (48 per XCD): per XCD 32 whole, 16 in 2 key
     # chunks: K/V fp16 rows plus the partials of the 128 chunked tiles
     # (the block-causal prefix rows of step 1 run whole)
     assert Q.qi_attn_full_workspace_bytes(L3, Q.QI_BF16, 24) == 2 * 24 * 21504 * 128 * 2 + 128 * 2 * PART
     assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, 4096, 24) == 2 * 24 * 4096 * 128 * 2 + 128 * 2 * PART
-    # config[1]: 4 x 24 = 96 units (12 per XCD, none whole) -> all in 5 key chunks
-    L1 = Q.make_layout(qin.WORKLOADS["cfg1"].segments)
+    # text 256 + 32x32 reference + 32x32 target: 4 x 24 = 96 units (12 per XCD, none whole) -> all in 5 key chunks
+    L1 = Q.make_layout(qin.WORKLOADS["txt256_ref32_tgt32"].segments)
     assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, 1024, 24) == 2 * 24 * 1024 * 128 * 2 + 96 * 5 * PART
     assert Q.qi_attn_full_workspace_bytes(L1, Q.QI_BF16, 24) == 2 * 24 * 2304 * 128 * 2 + 96 * 5 * PART
     # unmasked Edit-Plus (text 512 + target + 2 references of 64 x 64): the 8,704 prefix rows

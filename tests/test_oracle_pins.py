@@ -189,14 +189,14 @@ def test_blockmap_hand_derived():
 
 
 def test_mask_visible_pair_count_closed_form():
-    # cfg1: text 256 causal, ref 1024 sees text + itself, target 1024 sees all 2304
-    wl = qin.WORKLOADS["cfg1"]
+    # txt256_ref32_tgt32: text 256 causal, ref 1024 sees text + itself, target 1024 sees all 2304
+    wl = qin.WORKLOADS["txt256_ref32_tgt32"]
     want = 256 * 257 // 2 + 1024 * (256 + 1024) + 1024 * 2304
     assert O.visible_pairs(wl.segments) == want == 3702912
 
 
 def test_mask_rows_equals_dense_rows():
-    for segs in (MASK_TINY, qin.WORKLOADS["cfg0"].segments,
+    for segs in (MASK_TINY, qin.WORKLOADS["tiny_f32"].segments,
                  (qin.text(7), qin.image(3, 2, 1), qin.text(4, bidir=True), qin.image(3, 3, 0))):
         m = O.mask_dense(segs)
         rows = np.arange(m.shape[0])[::3]
@@ -211,7 +211,7 @@ def test_mask_prefix_never_sees_target_and_target_sees_all():
 
 
 def test_blockmap_classes_consistent_with_mask():
-    segs = qin.WORKLOADS["cfg0"].segments
+    segs = qin.WORKLOADS["tiny_f32"].segments
     m = O.mask_dense(segs)
     for tq, tk in ((8, 8), (16, 4), (5, 7), (128, 64)):
         bm = O.blockmap(m, tq, tk)
@@ -243,8 +243,8 @@ def _bruteforce_attention(q, k, v, mask, scale):
     return out
 
 
-def test_attention_matches_bruteforce_on_cfg0():
-    wl = qin.WORKLOADS["cfg0"]
+def test_attention_matches_bruteforce_on_tiny_f32():
+    wl = qin.WORKLOADS["tiny_f32"]
     q, k, v = (t.f64 for t in qin.qkv(wl, wl.S))
     m = O.mask_dense(wl.segments)
     got = O.attention(q, k, v, m, chunk=7)
@@ -266,7 +266,7 @@ def test_attention_unmasked_matches_logsumexp_form():
 def test_step1_prefix_bit_identical_under_target_perturbation():
     # the prefix never sees the target (course overview, learning goals), so prefix outputs are
     # exactly unchanged when target Q/K/V change
-    wl = qin.WORKLOADS["cfg0"]
+    wl = qin.WORKLOADS["tiny_f32"]
     S, P, T = O.split_counts(wl.segments)
     q, k, v = (t.f64.copy() for t in qin.qkv(wl, S))
     c, s = O.rope_tables(O.positions(wl.segments))
@@ -278,11 +278,11 @@ def test_step1_prefix_bit_identical_under_target_perturbation():
     assert np.array_equal(o1[:P], o2[:P]) and not np.allclose(o1[P:], o2[P:])
 
 
-@pytest.mark.parametrize("name", ["cfg0", "mini"])
+@pytest.mark.parametrize("name", ["tiny_f32", "mini"])
 def test_cached_step_equals_full_recompute(name):
     # course overview: reusing the prefix cache matches recomputation to ~1e-16 (fp64)
-    if name == "cfg0":
-        wl = qin.WORKLOADS["cfg0"]
+    if name == "tiny_f32":
+        wl = qin.WORKLOADS["tiny_f32"]
     else:
         wl = qin.small_workload("mini", (qin.text(9), qin.image(3, 5, 1), qin.image(2, 2, 2),
                                          qin.image(4, 3, 0)), n_head=3, qk_rmsnorm=True)
@@ -421,8 +421,8 @@ PLANTED = [
     ("mask_dense", _mask_refs_see_target, [test_mask_hand_derived, test_mask_prefix_never_sees_target_and_target_sees_all]),
     ("inv_freq", _inv_freq_headdim, [test_bands_sum_to_head_dim_and_closed_form_freqs]),
     ("zero_center_rms_norm", _zc_no_plus_one, [test_zero_center_rmsnorm_hand_example]),
-    ("attention", _attention_no_max_shift_wrong_scale, [test_attention_matches_bruteforce_on_cfg0]),
-    ("cached_step", _cached_step_unrotated_target, [lambda: test_cached_step_equals_full_recompute("cfg0")]),
+    ("attention", _attention_no_max_shift_wrong_scale, [test_attention_matches_bruteforce_on_tiny_f32]),
+    ("cached_step", _cached_step_unrotated_target, [lambda: test_cached_step_equals_full_recompute("tiny_f32")]),
     ("euler", _euler_sign, [test_euler_constant_velocity_closed_form]),
 ]
 
