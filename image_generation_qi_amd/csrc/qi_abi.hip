@@ -397,7 +397,7 @@ static int gemm_bf16(const void* x, int64_t ldx, const void* w, const float* bia
   if (M < 0 || N < 64 || K < 64 || (N % 64) || (K % 64)) return QI_ERR_SHAPE;
   if (ldx < K || ldo < (epilogue == QI_EPI_SWIGLU ? N / 2 : N)) return QI_ERR_SHAPE;
   // x and w are addressed through buffer resources with 32-bit byte offsets
-  if (M * ldx * 2 > INT32_MAX || N * K * 2 > INT32_MAX) return QI_ERR_SHAPE;
+  if (M > INT32_MAX / 2 / ldx || N > INT32_MAX / 2 / K) return QI_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(w) || !aligned16(out) || !aligned16(gate) || !aligned16(bias) || (ldx % 8) ||
       (ldo % 8))
     return QI_ERR_ALIGN;
@@ -452,7 +452,8 @@ int qi_layernorm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64_
 int qi_timestep_embed(const float* t, int32_t n, int32_t dim, float* out, void* stream) {
   clear_hip_error();
   if (!t || !out) return QI_ERR_ARG;
-  if (n < 0 || dim < 2 || (dim % 2)) return QI_ERR_SHAPE;
+  if (n < 0 || dim < 2 || (dim % 2) || (int64_t)n * (dim / 2) > INT32_MAX) return QI_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(t) & 3) || (reinterpret_cast<uintptr_t>(out) & 3)) return QI_ERR_ALIGN;
   return launch_status(launch_timestep_embed(t, n, dim, out, (hipStream_t)stream));
 }
 
@@ -461,7 +462,9 @@ int qi_linear_small_bias(const float* x, int32_t n_vec, int32_t I, const void* w
   clear_hip_error();
   if (!x || !w || !y) return QI_ERR_ARG;
   if (n_vec < 1 || n_vec > 4 || I < 8 || (I % 8) || O < 0) return QI_ERR_SHAPE;
-  if (!aligned16(w)) return QI_ERR_ALIGN;
+  if (!aligned16(w) || (reinterpret_cast<uintptr_t>(x) & 3) || (reinterpret_cast<uintptr_t>(bias) & 3) ||
+      (reinterpret_cast<uintptr_t>(y) & 3))
+    return QI_ERR_ALIGN;
   return launch_status(launch_linear_small(x, n_vec, I, w, bias, O, silu_in ? 1 : 0, y, (hipStream_t)stream));
 }
 
@@ -474,6 +477,7 @@ int qi_cast_bf16(const float* x, void* y, int64_t n, void* stream) {
   clear_hip_error();
   if (!x || !y) return QI_ERR_ARG;
   if (n < 0) return QI_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(x) & 3) || (reinterpret_cast<uintptr_t>(y) & 1)) return QI_ERR_ALIGN;
   return launch_status(launch_cast_bf16(x, y, n, (hipStream_t)stream));
 }
 

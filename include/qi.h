@@ -277,8 +277,8 @@ typedef enum {
 
 /* Dense projection on bf16 MFMA: x device bf16 [M][ldx]; w device bf16 [N][K] (the Linear weight,
  * out x in); K % 64 == 0, N % 64 == 0, ldx/ldo multiples of 8, M * ldx and N * K below 2^30
- * elements, pointers 16-byte aligned.  gate, row0 and P are used by QI_EPI_GATED_RESIDUAL only
- * (gate may be NULL otherwise).  out must not overlap x or w.  The workgroup tile (256 tokens x
+ * elements, pointers 16-byte aligned.  gate, row0 and P are used by the gated epilogues only
+ * (QI_EPI_GATED_RESIDUAL and QI_EPI_GATED_RESIDUAL_LINEAR; gate may be NULL otherwise).  out must not overlap x or w.  The workgroup tile (256 tokens x
  * 256, 192 or 128 features) is chosen from M and N.  Errors: QI_ERR_ARG (null pointer, unknown
  * epilogue), QI_ERR_SHAPE, QI_ERR_ALIGN, QI_ERR_HIP (launch). */
 int qi_gemm_bf16(const void* x, int64_t ldx, const void* w, void* out, int64_t ldo, int64_t M, int64_t N,
@@ -300,7 +300,10 @@ int qi_gemm_bf16_bias(const void* x, int64_t ldx, const void* w, const float* bi
 /* ZeroCenterRMSNorm with modulation ([1B] sections 1-3: x * rrms * (w + 1), weights stored as
  * scale - 1, fp32 math; [EDIT] section 5.2: x * (1 + scale) + shift): x device fp32 [M][ldx],
  * out device bf16 [M][ldo]; w fp32 [D] or NULL (no (w + 1) factor: plain RMS norm); scale and shift
- * fp32 [2][D] or NULL, row m using index 0 if row0 + m < P (prefix, t = 0) else 1.  D % 4 == 0. */
+ * fp32 [2][D] or NULL, row m using index 0 if row0 + m < P (prefix, t = 0) else 1.  D % 4 == 0.
+ * Errors: QI_ERR_ARG (NULL x or out, eps negative or not finite), QI_ERR_SHAPE (M < 0 or above
+ * 2^31 - 1, D < 4 or D % 4, ldx or ldo < D), QI_ERR_ALIGN (x, w, scale or shift not 16-byte
+ * aligned, ldx or ldo not a multiple of 4, out not 8-byte aligned), QI_ERR_HIP (launch). */
 int qi_zc_rmsnorm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64_t M, int32_t D, const float* w,
                       const float* scale, const float* shift, int64_t row0, int64_t P, float eps, void* stream);
 
@@ -309,28 +312,34 @@ int qi_zc_rmsnorm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64
  * shift, fp32 math; x device fp32 [M][ldx], out device bf16 [M][ldo]; scale and shift fp32 [2][D]
  * or NULL, row m using index 0 if row0 + m < P else 1 (the caller orders the two parameter sets,
  * e.g. the noisy target's and the t = 0 ones of the Edit model's optional per-token
- * modulation).  D % 4 == 0. */
+ * modulation).  D % 4 == 0.  Errors as qi_zc_rmsnorm_mod. */
 int qi_layernorm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64_t M, int32_t D, const float* scale,
                      const float* shift, int64_t row0, int64_t P, float eps, void* stream);
 
 /* Sinusoidal timestep embedding ([EDIT] section 5.1: 256 channels, cos half first, frequencies
  * 10000^(-i/(dim/2))): t device fp32 [n] (the timestep, e.g. 1000 * sigma), out device fp32
- * [n][dim], dim even. */
+ * [n][dim], dim even.  Errors: QI_ERR_ARG (NULL pointer), QI_ERR_SHAPE (n < 0, dim odd or < 2,
+ * n * dim / 2 above 2^31 - 1), QI_ERR_ALIGN (a pointer not 4-byte aligned), QI_ERR_HIP (launch). */
 int qi_timestep_embed(const float* t, int32_t n, int32_t dim, float* out, void* stream);
 
 /* Conditioning linear on up to 4 vectors: y[v][o] = sum_i act(x[v][i]) w[o][i], act = SiLU if
  * silu_in else identity ([EDIT] sections 5.1-5.2: the t-embedding MLP and the modulation Linear
- * act on SiLU(temb)).  x device fp32 [n_vec][I], w device bf16 [O][I] (I % 8 == 0), y fp32. */
+ * act on SiLU(temb)).  x device fp32 [n_vec][I], w device bf16 [O][I] (I % 8 == 0, 16-byte
+ * aligned), y device fp32 [n_vec][O].  Errors: QI_ERR_ARG (NULL x, w or y), QI_ERR_SHAPE (n_vec
+ * outside 1..4, I < 8 or I % 8, O < 0), QI_ERR_ALIGN (w not 16-byte or x / y not 4-byte aligned),
+ * QI_ERR_HIP (launch). */
 int qi_linear_small(const float* x, int32_t n_vec, int32_t I, const void* w, int32_t O, int32_t silu_in, float* y,
                     void* stream);
 
 /* qi_linear_small with a bias: y[v][o] = sum_i act(x[v][i]) w[o][i] + bias[o]; bias device fp32 [O]
- * or NULL (the v1 block's modulation Linear, SiLU then Linear(D, 6 D) with bias, [EDIT] section
- * 5.2). */
+ * or NULL, 4-byte aligned (the v1 block's modulation Linear, SiLU then Linear(D, 6 D) with bias,
+ * [EDIT] section 5.2).  Errors as qi_linear_small. */
 int qi_linear_small_bias(const float* x, int32_t n_vec, int32_t I, const void* w, const float* bias, int32_t O,
                          int32_t silu_in, float* y, void* stream);
 
-/* fp32 -> bf16 (nearest even) of n elements (latents into the img_in projection). */
+/* fp32 -> bf16 (nearest even) of n elements (latents into the img_in projection): x device fp32
+ * [n], y device bf16 [n].  Errors: QI_ERR_ARG (NULL pointer), QI_ERR_SHAPE (n < 0), QI_ERR_ALIGN
+ * (x not 4-byte or y not 2-byte aligned), QI_ERR_HIP (launch). */
 int qi_cast_bf16(const float* x, void* y, int64_t n, void* stream);
 
 /* HIP error code of the last launch of this library that failed in the calling thread (the

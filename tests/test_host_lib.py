@@ -308,3 +308,62 @@ def test_full_attention_layout_maps_and_positions():
     bad = Q.make_layout(segs, attention=7)
     n = [ctypes.c_int64() for _ in range(3)]
     assert Q.lib().qi_layout_tokens(ctypes.byref(bad), *(ctypes.byref(x) for x in n)) == Q.QI_ERR_LAYOUT
+
+
+def test_layer_entry_points_reject():
+    """Argument checks of the layer pieces run before any launch, so they answer without a GPU."""
+    G = Q.lib().qi_gemm_bf16_ex
+    big = 1 << 40
+    ok = (FAKE, 256, FAKE, FAKE, 256, 64, 256, 256)
+    assert G(None, *ok[1:], Q.QI_EPI_STORE, None, 0, 0, 0, None) == Q.QI_ERR_ARG
+    assert G(*ok, 9, None, 0, 0, 0, None) == Q.QI_ERR_ARG
+    assert G(*ok, Q.QI_EPI_GATED_RESIDUAL, None, 0, 0, 0, None) == Q.QI_ERR_ARG
+    assert G(*ok, Q.QI_EPI_GATED_RESIDUAL_LINEAR, None, 0, 0, 0, None) == Q.QI_ERR_ARG
+    assert G(*ok, Q.QI_EPI_STORE, None, 0, 0, 64, None) == Q.QI_ERR_ARG
+    assert G(*ok, Q.QI_EPI_SWIGLU, None, 0, 0, 192, None) == Q.QI_ERR_ARG
+    assert G(FAKE, 256, FAKE, FAKE, 256, 64, 256, 200, Q.QI_EPI_STORE, None, 0, 0, 0, None) == Q.QI_ERR_SHAPE
+    assert G(FAKE, 128, FAKE, FAKE, 256, 64, 256, 256, Q.QI_EPI_STORE, None, 0, 0, 0, None) == Q.QI_ERR_SHAPE
+    # 32-bit buffer offsets: the checks may not overflow for huge sizes either
+    assert G(FAKE, 256, FAKE, FAKE, 256, 1 << 22, 256, 256, Q.QI_EPI_STORE, None, 0, 0, 0, None) == Q.QI_ERR_SHAPE
+    assert G(FAKE, big, FAKE, FAKE, 256, big, 256, 256, Q.QI_EPI_STORE, None, 0, 0, 0, None) == Q.QI_ERR_SHAPE
+    assert G(FAKE, 256, FAKE, FAKE, big, 64, big, 256, Q.QI_EPI_STORE, None, 0, 0, 0, None) == Q.QI_ERR_SHAPE
+    assert G(FAKE + 8, *ok[1:], Q.QI_EPI_STORE, None, 0, 0, 0, None) == Q.QI_ERR_ALIGN
+    assert G(FAKE, 260, FAKE, FAKE, 256, 64, 256, 256, Q.QI_EPI_STORE, None, 0, 0, 0, None) == Q.QI_ERR_ALIGN
+    assert G(*ok, Q.QI_EPI_GATED_RESIDUAL, FAKE + 4, 0, 0, 0, None) == Q.QI_ERR_ALIGN
+    assert Q.lib().qi_gemm_bf16_bias(FAKE, 256, FAKE, FAKE + 4, FAKE, 256, 64, 256, 256, Q.QI_EPI_STORE, None, 0, 0,
+                                     None) == Q.QI_ERR_ALIGN  # bias
+    # M == 0 is a no-op that launches nothing
+    assert Q.lib().qi_gemm_bf16(FAKE, 256, FAKE, FAKE, 256, 0, 256, 256, Q.QI_EPI_STORE, None, 0, 0, None) == Q.QI_OK
+    # norms
+    N = Q.lib().qi_zc_rmsnorm_mod
+    assert N(None, 256, FAKE, 256, 8, 256, None, None, None, 0, 0, 1e-6, None) == Q.QI_ERR_ARG
+    assert N(FAKE, 256, FAKE, 256, 8, 258, None, None, None, 0, 0, 1e-6, None) == Q.QI_ERR_SHAPE
+    assert N(FAKE, 128, FAKE, 256, 8, 256, None, None, None, 0, 0, 1e-6, None) == Q.QI_ERR_SHAPE
+    assert N(FAKE, 256, FAKE, 256, -1, 256, None, None, None, 0, 0, 1e-6, None) == Q.QI_ERR_SHAPE
+    assert N(FAKE, 256, FAKE, 256, 8, 256, None, None, None, 0, 0, -1.0, None) == Q.QI_ERR_ARG
+    assert N(FAKE, 256, FAKE + 4, 256, 8, 256, None, None, None, 0, 0, 1e-6, None) == Q.QI_ERR_ALIGN
+    assert N(FAKE, 256, FAKE, 256, 8, 256, FAKE + 4, None, None, 0, 0, 1e-6, None) == Q.QI_ERR_ALIGN
+    LN = Q.lib().qi_layernorm_mod
+    assert LN(None, 256, FAKE, 256, 8, 256, None, None, 0, 0, 1e-6, None) == Q.QI_ERR_ARG
+    assert LN(FAKE, 256, FAKE, 256, 8, 6, None, None, 0, 0, 1e-6, None) == Q.QI_ERR_SHAPE
+    assert LN(FAKE, 256, FAKE, 256, 8, 256, FAKE + 4, None, 0, 0, 1e-6, None) == Q.QI_ERR_ALIGN
+    assert LN(FAKE, 256, FAKE, 256, 8, 256, None, None, 0, 0, float("nan"), None) == Q.QI_ERR_ARG
+    # conditioning vectors and the latent cast
+    T = Q.lib().qi_timestep_embed
+    assert T(None, 2, 256, FAKE, None) == Q.QI_ERR_ARG
+    assert T(FAKE, 2, 255, FAKE, None) == Q.QI_ERR_SHAPE
+    assert T(FAKE, -1, 256, FAKE, None) == Q.QI_ERR_SHAPE
+    assert T(FAKE, 1 << 30, 256, FAKE, None) == Q.QI_ERR_SHAPE
+    assert T(FAKE + 2, 2, 256, FAKE, None) == Q.QI_ERR_ALIGN
+    LS = Q.lib().qi_linear_small_bias
+    assert LS(FAKE, 2, 256, None, None, 64, 1, FAKE, None) == Q.QI_ERR_ARG
+    assert LS(FAKE, 5, 256, FAKE, None, 64, 1, FAKE, None) == Q.QI_ERR_SHAPE
+    assert LS(FAKE, 2, 260, FAKE, None, 64, 1, FAKE, None) == Q.QI_ERR_SHAPE
+    assert LS(FAKE, 2, 256, FAKE + 8, None, 64, 1, FAKE, None) == Q.QI_ERR_ALIGN
+    assert LS(FAKE, 2, 256, FAKE, FAKE + 2, 64, 1, FAKE, None) == Q.QI_ERR_ALIGN
+    assert LS(FAKE + 2, 2, 256, FAKE, None, 64, 1, FAKE, None) == Q.QI_ERR_ALIGN
+    C = Q.lib().qi_cast_bf16
+    assert C(None, FAKE, 8, None) == Q.QI_ERR_ARG
+    assert C(FAKE, FAKE, -1, None) == Q.QI_ERR_SHAPE
+    assert C(FAKE + 2, FAKE, 8, None) == Q.QI_ERR_ALIGN
+    assert C(FAKE, FAKE + 1, 8, None) == Q.QI_ERR_ALIGN
