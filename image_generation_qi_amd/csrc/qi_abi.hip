@@ -154,8 +154,8 @@ void set_partials(AttnArgs& a, char* base, qi_dtype dtype) {
   if (dtype != QI_BF16) return;
   const AttnSched sc = attn_f16_schedule(a.n_q, a.n_head);
   a.xcd_sched = 1;
-  a.part_o = (float*)base;
-  a.part_ml = (float*)(base + (int64_t)sc.tail_units * sc.n_split * kAttnF16TileQ * QI_HEAD_DIM * (int64_t)sizeof(float));
+  a.part_o = (uint16_t*)base;
+  a.part_ml = (float*)(base + (int64_t)sc.tail_units * sc.n_split * kAttnF16TileQ * QI_HEAD_DIM * (int64_t)sizeof(uint16_t));
 }
 
 int run_attn(const AttnArgs& a, qi_dtype dtype, hipStream_t s) {

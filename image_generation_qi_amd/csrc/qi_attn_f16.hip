@@ -214,9 +214,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (t_begin >= t_stop) {  // the chunk holds no visible key for any row of the tile
     if (qok) {
       const int64_t row = prow0 + wave * 32 + l32;
-      f32x4* po = (f32x4*)(a.part_o + row * HD + 4 * g);
+      uint16_t* po = a.part_o + row * HD + 4 * g;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) po[2 * i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int bd = 0; bd < 4; ++bd)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) *(u32x2*)(po + 32 * bd + 8 * r4) = u32x2{0u, 0u};
       if (g == 0) {
         a.part_ml[2 * row] = -INFINITY;
         a.part_ml[2 * row + 1] = 0.f;
@@ -538,13 +540,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           *(u32x2*)(op + 32 * bd + 8 * r4) = w;
         }
     } else {
+      // the chunk's output divided by its own sum: a convex combination of fp16 V rows, so it
+      // fits fp16, which halves the partial traffic; the merge weights it back by (m, l)
       const int64_t row = prow0 + wave * 32 + l32;
-      float* po = a.part_o + row * HD + 4 * g;
+      uint16_t* po = a.part_o + row * HD + 4 * g;
+      const float inv = 1.0f / lt;
 #pragma unroll
       for (int bd = 0; bd < 4; ++bd)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-          *(f32x4*)(po + 32 * bd + 8 * r4) = f32x4{o[bd][4 * r4], o[bd][4 * r4 + 1], o[bd][4 * r4 + 2], o[bd][4 * r4 + 3]};
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const h2 lo = {(_Float16)(o[bd][4 * r4] * inv), (_Float16)(o[bd][4 * r4 + 1] * inv)};
+          const h2 hi = {(_Float16)(o[bd][4 * r4 + 2] * inv), (_Float16)(o[bd][4 * r4 + 3] * inv)};
+          *(u32x2*)(po + 32 * bd + 8 * r4) = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        }
       if (g == 0) {
         a.part_ml[2 * row] = m_run;
         a.part_ml[2 * row + 1] = lt;
@@ -553,11 +561,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// Merge of the key chunks: for each row of a chunked unit, O = sum_s 2^(m_s - M) O_s /
-// sum_s 2^(m_s - M) l_s with M = max_s m_s, rounded to bf16.  16 threads per row, 8 dims each.
+// Merge of the key chunks: for each row of a chunked unit, with chunk s's normalised output
+// A_s = O_s / l_s (fp16), O = sum_s w_s A_s / sum_s w_s with w_s = 2^(m_s - M) l_s and M = max_s
+// m_s, rounded to bf16.  16 threads per row, 8 dims each.
 // Chunked unit tu is the tl-th remaining unit of run x, in run order (see k_attn_f16); its
 // partial rows are [tu][chunk][256].
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml,
                                                  uint16_t* __restrict__ o, int64_t o_stride, float* __restrict__ lse,
                                                  int64_t lse_stride, int n_q, int n_head, int n_split, int xcd_whole,
                                                  int n_tail) {
@@ -590,15 +599,11 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_
     const int64_t pr = p0 + s * BM;
     const float m = part_ml[2 * pr];
     if (m == -INFINITY) continue;
-    const float w = __builtin_amdgcn_exp2f(m - M);
-    den += w * part_ml[2 * pr + 1];
-    const f32x4* p = (const f32x4*)(part_o + pr * HD + d0);
-    const f32x4 x0 = p[0], x1 = p[1];
+    const float w = __builtin_amdgcn_exp2f(m - M) * part_ml[2 * pr + 1];
+    den += w;
+    const h8 x = __builtin_bit_cast(h8, *(const u32x4*)(part_o + pr * HD + d0));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[j] += w * x0[j];
-      acc[4 + j] += w * x1[j];
-    }
+    for (int j = 0; j < 8; ++j) acc[j] += w * (float)x[j];
   }
   const float inv = 1.0f / den;
   if (lse && d0 == 0) lse[(int64_t)h * lse_stride + row] = (M + __log2f(den)) * 0.6931471805599453f;
@@ -642,7 +647,7 @@ AttnSched attn_f16_schedule(int64_t n_q, int32_t n_head) {
 
 int64_t attn_f16_partial_bytes(int64_t n_q, int32_t n_head) {
   const AttnSched sc = attn_f16_schedule(n_q, n_head);
-  return (int64_t)sc.tail_units * sc.n_split * BM * (HD + 2) * (int64_t)sizeof(float);
+  return (int64_t)sc.tail_units * sc.n_split * BM * (HD * (int64_t)sizeof(uint16_t) + 2 * (int64_t)sizeof(float));
 }
 
 hipError_t launch_attn_f16(const AttnArgs& a_in, hipStream_t s) {

@@ -76,7 +76,7 @@ struct AttnArgs {
   float* lse;           // nullable: [n_head][lse_stride], row q of the launch at lse[h * lse_stride + q]
   int64_t lse_stride;
   int32_t n_split, split_tiles, xcd_whole;
-  float* part_o;       // [chunked unit][chunk][256 rows][128]
+  uint16_t* part_o;    // [chunked unit][chunk][256 rows][128] fp16, divided by the chunk's own sum
   float* part_ml;      // [chunked unit][chunk][256 rows][2]
   SegTable segs;
 };

@@ -127,7 +127,7 @@ def test_tile_shape_and_sizes():
     assert Q.qi_attn_schedule(101 * 256, 5) == (1, 32, 0)   # 505 tiles: the remaining 32 / 31 run whole
     assert Q.qi_attn_schedule(0, 24) == (1, 0, 0)
     L3 = Q.make_layout(qin.WORKLOADS["txt1024_4ref64_tgt64"].segments)
-    PART = 256 * 130 * 4   # fp32 partials of one chunk of one query tile: 256 rows x (128 values + max + sum)
+    PART = 256 * (128 * 2 + 2 * 4)   # partials of one chunk of one query tile: 256 rows x (128 fp16 + fp32 max, sum)
     # 4096-token target: 16 x 24 = 384 query tiles (48 per XCD): per XCD 32 whole, 16 in 2 key
     # chunks: K/V fp16 rows plus the partials of the 128 chunked tiles
     # (the block-causal prefix rows of step 1 run whole)
