@@ -367,3 +367,26 @@ def test_layer_entry_points_reject():
     assert C(FAKE, FAKE, -1, None) == Q.QI_ERR_SHAPE
     assert C(FAKE + 2, FAKE, 8, None) == Q.QI_ERR_ALIGN
     assert C(FAKE, FAKE + 1, 8, None) == Q.QI_ERR_ALIGN
+
+
+def test_schedule_invariants_over_shapes():
+    """For every shape: whole tiles come in whole rounds of the 32 CUs of an XCD and never exceed
+    an XCD's share, a launch cuts tiles into 1..8 key chunks only when some remain after the whole
+    rounds, exactly those remaining tiles are chunked, and the cached workspace holds the prepared
+    K/V rows plus exactly their partials."""
+    PART = 256 * (128 * 2 + 2 * 4)
+    rng = np.random.default_rng(7)
+    shapes = [(int(n), int(h)) for n, h in zip(rng.integers(1, 70000, 200), rng.integers(1, 48, 200))]
+    shapes += [(256 * t, h) for t in (1, 2, 31, 32, 33) for h in (1, 8, 24, 40)]
+    for n_q, heads in shapes:
+        units = -(-n_q // 256) * heads
+        chunks, whole, chunked = Q.qi_attn_schedule(n_q, heads)
+        assert 1 <= chunks <= 8, (n_q, heads)
+        assert whole % 32 == 0 and 8 * whole <= units, (n_q, heads)
+        assert whole == 32 * ((units // 8) // 32), (n_q, heads)
+        rest = units - 8 * whole
+        assert chunked == (rest if chunks > 1 else 0), (n_q, heads)
+        if rest == 0:
+            assert chunks == 1
+        rows = -(-n_q // 64) * 64
+        assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, n_q, heads) == 2 * heads * rows * 128 * 2 + chunked * chunks * PART, (n_q, heads)
