@@ -116,6 +116,34 @@ def test_blockmap_bit_exact(name, tiles):
     assert np.array_equal(out, O.blockmap(O.mask_dense(segs), tq, tk))
 
 
+def _oracle_blockmap_by_rows(segs, tq, tk):
+    """The oracle's tile map of a full-size layout, one query tile at a time: O.blockmap over the
+    rows of O.mask_rows (the dense mask of 21,504 tokens would take 460 MB)."""
+    S = sum(g.n_tokens for g in segs)
+    rows = []
+    for i in range(0, S, tq):
+        m = O.mask_rows(segs, np.arange(i, min(i + tq, S)))
+        rows.append(O.blockmap(m, tq, tk))
+    return np.concatenate(rows, axis=0)
+
+
+@pytest.mark.parametrize("name", ["txt1024_4ref64_tgt64", "txt512_4ref64_tgt64", "txt512_10ref32_tgt64"])
+@pytest.mark.parametrize("tiles", [(256, 64), (64, 64)])
+def test_blockmap_bit_exact_full_size(name, tiles):
+    # the Block-Causal tile map ([OV] card 3C) of the headline and full-layer workloads, at the
+    # attention kernel's tile and at a square tile, bit for bit against the oracle's mask
+    segs = qin.WORKLOADS[name].segments
+    tq, tk = tiles
+    L = Q.make_layout(segs)
+    S, _, _ = Q.qi_layout_tokens(L)
+    out = np.zeros(((S + tq - 1) // tq, (S + tk - 1) // tk), np.uint8)
+    Q.check(Q.qi_blockmap(L, tq, tk, out))
+    ref = _oracle_blockmap_by_rows(segs, tq, tk)
+    assert np.array_equal(out, ref)
+    # all three classes occur: skipped tiles above the diagonal blocks, full and mixed tiles
+    assert set(np.unique(ref).tolist()) == {0, 1, 2}
+
+
 def test_tile_shape_and_sizes():
     assert Q.qi_attn_tile_shape(Q.QI_BF16) == (256, 64)
     assert Q.qi_attn_tile_shape(Q.QI_F32) == (1, 64)

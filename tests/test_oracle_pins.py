@@ -494,17 +494,24 @@ def test_dit_layer_cached_equals_full_and_prefix_uses_t0():
     assert np.array_equal(y2[:P], y[:P]) and not np.allclose(y2[P:], y[P:])
 
 
-def test_dit_layer_matches_hand_composition():
-    # the layer equals its steps composed by hand with the oracle's own attention on rotated q/k
+@pytest.mark.parametrize("tanh_gate", [True, False])
+def test_dit_layer_matches_hand_composition(tanh_gate):
+    # the layer equals its steps composed by hand with the oracle's own attention on rotated q/k;
+    # with the 2.1 residual gate ([OV] card 5A) the gates enter through tanh, with the v1 one as given.
+    # The gates are drawn with std 0.3 and pushed away from 0, where tanh(g) and g would agree.
     segs = (qin.text(4), qin.image(2, 2, 1), qin.image(2, 2, 0))
     S, P, T = O.split_counts(segs)
     L, mods = _tiny_layer(4, D=128, F=256)
+    mods = tuple(tuple(v + np.sign(v) * 0.8 if i in (2, 5) else v for i, v in enumerate(m)) for m in mods)
     x = np.random.default_rng(5).standard_normal((S, 128))
     c, s = O.rope_tables(O.positions(segs))
-    y, _ = O.dit_layer(x, L, mods, segs, c, s, tanh_gate=False)
+    y, _ = O.dit_layer(x, L, mods, segs, c, s, tanh_gate=tanh_gate)
     rows_pre = np.arange(S) < P
     def sel(i):
-        return np.where(rows_pre[:, None], mods[0][i][None, :], mods[1][i][None, :])
+        g = np.where(rows_pre[:, None], mods[0][i][None, :], mods[1][i][None, :])
+        if tanh_gate and i in (2, 5):
+            g = (np.exp(g) - np.exp(-g)) / (np.exp(g) + np.exp(-g))   # tanh written out
+        return g
     r1 = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + 1e-6) * (L["norm1"] + 1) * (1 + sel(1)) + sel(0)
     qkv = r1 @ L["w_qkv"].T
     q, k, v = qkv[:, :128], qkv[:, 128:256], qkv[:, 256:]
@@ -524,6 +531,29 @@ def test_dit_layer_matches_hand_composition():
     g, u = r2 @ L["w_gate"].T, r2 @ L["w_up"].T
     x2 = x1 + sel(5) * ((g / (1 + np.exp(-g)) * u) @ L["w_down"].T)
     assert np.max(np.abs(y - x2)) < 1e-12
+
+
+def test_time_condition_matches_hand_composition():
+    # [EDIT] section 5.1: the timestep MLP is Linear -> SiLU -> Linear on the sinusoidal embedding
+    # of 1000 sigma, with no activation after the second Linear.  Composed by hand: cos half first,
+    # frequency i of 128 is 10000^(-i/128), SiLU(z) = z / (1 + e^-z).  The weights are large enough
+    # that SiLU after the second Linear (or a missing SiLU) changes the result by far more than
+    # rounding.
+    rng = np.random.default_rng(11)
+    w1 = rng.standard_normal((32, 256)) / 4
+    w2 = rng.standard_normal((24, 32)) / 3
+    sig = np.array([0.0, 0.375, 1.0])
+    got = O.time_condition(sig, w1, w2)
+    for r, sg in enumerate(sig):
+        t = 1000.0 * sg
+        f = np.array([10000.0 ** (-i / 128.0) for i in range(128)])
+        emb = np.concatenate([np.cos(t * f), np.sin(t * f)])
+        z = w1 @ emb
+        hid = z / (1.0 + np.exp(-z))
+        ref = w2 @ hid
+        assert np.max(np.abs(got[r] - ref)) < 1e-12 * max(1.0, np.max(np.abs(ref)))
+    # the result has negative entries: an activation after the second Linear would bound them below
+    assert got.min() < -1.0
 
 
 def test_velocity_head_scale_zero_is_plain_norm_projection():
@@ -572,6 +602,46 @@ def test_prefix_states_follow_segment_order():
     xt = np.array([[1.0], [2.0], [3.0]])
     rt = np.array([[10.0], [11.0], [12.0]])
     assert O.prefix_states(segs, xt, rt)[:, 0].tolist() == [1, 2, 10, 11, 3, 12]
+
+
+_ORIG_DIT_LAYER = O.dit_layer
+_ORIG_TIME_CONDITION = O.time_condition
+
+
+def _dit_layer_gate_without_tanh(*args, **kw):
+    kw["tanh_gate"] = False
+    return _ORIG_DIT_LAYER(*args, **kw)
+
+
+def _time_condition_silu_after_second(sigma, w1, w2):
+    emb = O.timestep_embedding(1000.0 * np.atleast_1d(sigma))
+    return O.silu(O.linear(O.silu(O.linear(emb, w1)), w2))
+
+
+def _time_condition_no_silu(sigma, w1, w2):
+    return O.linear(O.linear(O.timestep_embedding(1000.0 * np.atleast_1d(sigma)), w1), w2)
+
+
+def _time_condition_silu_moved(sigma, w1, w2):
+    emb = O.timestep_embedding(1000.0 * np.atleast_1d(sigma))
+    return O.silu(O.linear(O.linear(emb, w1), w2))
+
+
+PLANTED_LAYER = [
+    ("dit_layer", _dit_layer_gate_without_tanh, [lambda: test_dit_layer_matches_hand_composition(True)]),
+    ("time_condition", _time_condition_silu_after_second, [test_time_condition_matches_hand_composition]),
+    ("time_condition", _time_condition_no_silu, [test_time_condition_matches_hand_composition]),
+    ("time_condition", _time_condition_silu_moved, [test_time_condition_matches_hand_composition]),
+]
+
+
+@pytest.mark.parametrize("i", range(len(PLANTED_LAYER)))
+def test_planted_layer_mistake_is_caught(i, monkeypatch):
+    name, bad, pins = PLANTED_LAYER[i]
+    for pin in pins:
+        assert not _fails(pin), f"pin {pin} fails on the unmodified oracle"
+    monkeypatch.setattr(O, name, bad)
+    assert any(_fails(pin) for pin in pins), f"planted mistake in {name} not caught"
 
 
 # ------------------------------------------------------------------------------------------------
