@@ -16,9 +16,9 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int elem_size(qi_dtype t) { return t == QI_F32 ? 4 : (t == QI_BF16 || t == QI_F16) ? 2 : 0; }
+int elem_size(int32_t t) { return t == QI_F32 ? 4 : (t == QI_BF16 || t == QI_F16) ? 2 : 0; }
 
-int check_tensor(const void* p, qi_dtype dtype, int64_t n_tok, int32_t n_head, int64_t tok_stride) {
+int check_tensor(const void* p, int32_t dtype, int64_t n_tok, int32_t n_head, int64_t tok_stride) {
   if (!p) return QI_ERR_ARG;
   if (dtype != QI_BF16 && dtype != QI_F32) return QI_ERR_DTYPE;
   if (n_tok < 1 || n_head < 1 || n_tok > INT32_MAX) return QI_ERR_SHAPE;
@@ -37,9 +37,9 @@ int check_prep(const qi_qkprep* prep) {
   return QI_OK;
 }
 
-int check_cache(const qi_kvcache* c, qi_dtype io_dtype, int32_t n_head, int32_t layer, int64_t P) {
+int check_cache(const qi_kvcache* c, int32_t io_dtype, int32_t n_head, int32_t layer, int64_t P) {
   if (!c || !c->k || !c->v) return QI_ERR_ARG;
-  const qi_dtype want = io_dtype == QI_BF16 ? QI_F16 : QI_F32;
+  const int32_t want = io_dtype == QI_BF16 ? QI_F16 : QI_F32;
   if (c->dtype != want) return QI_ERR_DTYPE;
   if (c->n_head != n_head || c->n_layers < 1 || c->p_cap < 0) return QI_ERR_SHAPE;
   if (layer < 0 || layer >= c->n_layers || P < 0 || P > c->p_cap) return QI_ERR_CAPACITY;
@@ -104,8 +104,8 @@ int launch_status(hipError_t e) {
 void clear_hip_error() { (void)hipGetLastError(); }
 
 // Prepare rows [0, n) of k (norm + rotation) and copy v into a [head][row][128] destination.
-int prep_kv(const void* k, const void* v, qi_dtype dtype, int64_t n, int32_t n_head, int64_t tok_stride,
-            const qi_qkprep* prep, void* dk, void* dv, int64_t head_stride, hipStream_t s) {
+int prep_kv(const void* k, const void* v, int32_t dtype, int64_t n, int32_t n_head, int64_t tok_stride,
+            const qi_qkprep* prep, void* dk, void* dv, int64_t head_stride, uint32_t* flags, hipStream_t s) {
   if (n <= 0) return QI_OK;
   PrepArgs pa{};
   pa.x = k;
@@ -121,6 +121,7 @@ int prep_kv(const void* k, const void* v, qi_dtype dtype, int64_t n, int32_t n_h
   pa.sin_t = prep ? prep->sin_t : nullptr;
   pa.rms_w = prep ? prep->k_rms_w : nullptr;
   pa.eps = prep ? prep->eps : 0.f;
+  pa.flags = flags;
   return launch_status(dtype == QI_BF16 ? launch_prep_bf16_to_f16(pa, s) : launch_prep_f32(pa, s));
 }
 
@@ -136,6 +137,7 @@ AttnArgs attn_args(const qi_qkv* io, const qi_qkprep* prep, float scale) {
   a.o_stride = (int64_t)io->n_head * QI_HEAD_DIM;
   a.lse = io->lse;
   a.lse_stride = io->n_tok;
+  a.flags = io->range_flags;
   a.n_q = (int32_t)io->n_tok;
   a.n_head = io->n_head;
   const double sc = softmax_scale(scale);
@@ -145,7 +147,7 @@ AttnArgs attn_args(const qi_qkv* io, const qi_qkprep* prep, float scale) {
 
 // The chunked schedule for a launch over a.n_q rows of units of equal cost, with its
 // partial-output buffers placed at `base` in the workspace (bf16 path only).
-void set_partials(AttnArgs& a, char* base, qi_dtype dtype) {
+void set_partials(AttnArgs& a, char* base, int32_t dtype) {
   a.xcd_sched = 0;
   a.reverse_qt = 0;
   a.n_split = 1;
@@ -158,7 +160,7 @@ void set_partials(AttnArgs& a, char* base, qi_dtype dtype) {
   a.part_ml = (float*)(base + (int64_t)sc.tail_units * sc.n_split * kAttnF16TileQ * QI_HEAD_DIM * (int64_t)sizeof(uint16_t));
 }
 
-int run_attn(const AttnArgs& a, qi_dtype dtype, hipStream_t s) {
+int run_attn(const AttnArgs& a, int32_t dtype, hipStream_t s) {
   // the bf16 path addresses each key source through a buffer resource with 32-bit byte offsets
   if (dtype == QI_BF16 && (a.nA > QI_MAX_SOURCE_KEYS || a.nB > QI_MAX_SOURCE_KEYS)) return QI_ERR_SHAPE;
   TimedLaunch t(s);
@@ -205,7 +207,7 @@ int run_attn_step1_f16(const AttnArgs& a, const SegTable& tab, int64_t P, int64_
 
 extern "C" {
 
-int qi_rope3d_apply(void* x, qi_dtype dtype, int64_t n_tok, int32_t n_head, int64_t tok_stride,
+int qi_rope3d_apply(void* x, int32_t dtype, int64_t n_tok, int32_t n_head, int64_t tok_stride,
                     const float* cos_t, const float* sin_t, const float* rms_w, float eps, void* stream) {
   clear_hip_error();
   int st = check_tensor(x, dtype, n_tok, n_head, tok_stride);
@@ -246,7 +248,8 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
   if (io->n_tok != li.S) return QI_ERR_SHAPE;
   // the bf16 path addresses each key source through a buffer resource with 32-bit byte offsets
   if (io->dtype == QI_BF16 && (li.P > QI_MAX_SOURCE_KEYS || li.T > QI_MAX_SOURCE_KEYS)) return QI_ERR_SHAPE;
-  if (reinterpret_cast<uintptr_t>(io->lse) & 3) return QI_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(io->lse) & 3) || (reinterpret_cast<uintptr_t>(io->range_flags) & 3))
+    return QI_ERR_ALIGN;
   if ((st = check_prep(prep)) != QI_OK) return st;
   if (cache && (st = check_cache(cache, io->dtype, io->n_head, layer, li.P)) != QI_OK) return st;
   if (!workspace) return QI_ERR_ARG;
@@ -279,7 +282,7 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
   char* tk = wk + RA * QI_HEAD_DIM * es;
   char* tv = wv + RA * QI_HEAD_DIM * es;
   if ((st = prep_kv((const char*)io->k + off, (const char*)io->v + off, io->dtype, li.T, io->n_head,
-                    io->tok_stride, prep ? &tprep : nullptr, tk, tv, R * QI_HEAD_DIM, s)) != QI_OK)
+                    io->tok_stride, prep ? &tprep : nullptr, tk, tv, R * QI_HEAD_DIM, io->range_flags, s)) != QI_OK)
     return st;
   a.kB = tk;
   a.vB = tv;
@@ -292,14 +295,15 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
     void* ck = (void*)cache_layer(cache->k, cache, layer);
     void* cv = (void*)cache_layer(cache->v, cache, layer);
     const int64_t chs = cache_rows(cache) * QI_HEAD_DIM;
-    if ((st = prep_kv(io->k, io->v, io->dtype, li.P, io->n_head, io->tok_stride, prep, ck, cv, chs, s)) != QI_OK)
+    if ((st = prep_kv(io->k, io->v, io->dtype, li.P, io->n_head, io->tok_stride, prep, ck, cv, chs, io->range_flags,
+                      s)) != QI_OK)
       return st;
     a.kA = ck;
     a.vA = cv;
     a.a_head_stride = chs;
   } else {
     if ((st = prep_kv(io->k, io->v, io->dtype, li.P, io->n_head, io->tok_stride, prep, wk, wv, R * QI_HEAD_DIM,
-                      s)) != QI_OK)
+                      io->range_flags, s)) != QI_OK)
       return st;
     a.kA = wk;
     a.vA = wv;
@@ -311,8 +315,9 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
   return run_attn(a, io->dtype, s);
 }
 
-int qi_attn_prefix_store(const void* k, const void* v, qi_dtype dtype, int64_t P, int32_t n_head, int64_t tok_stride,
-                         const qi_qkprep* prep, const qi_kvcache* cache, int32_t layer, void* stream) {
+int qi_attn_prefix_store(const void* k, const void* v, int32_t dtype, int64_t P, int32_t n_head, int64_t tok_stride,
+                         const qi_qkprep* prep, const qi_kvcache* cache, int32_t layer, uint32_t* range_flags,
+                         void* stream) {
   clear_hip_error();
   int st;
   if (P < 0) return QI_ERR_SHAPE;
@@ -324,15 +329,19 @@ int qi_attn_prefix_store(const void* k, const void* v, qi_dtype dtype, int64_t P
   if ((st = check_tensor(v, dtype, P, n_head, tok_stride)) != QI_OK) return st;
   if ((st = check_prep(prep)) != QI_OK) return st;
   if ((st = check_cache(cache, dtype, n_head, layer, P)) != QI_OK) return st;
+  if (reinterpret_cast<uintptr_t>(range_flags) & 3) return QI_ERR_ALIGN;
   void* ck = (void*)cache_layer(cache->k, cache, layer);
   void* cv = (void*)cache_layer(cache->v, cache, layer);
-  return prep_kv(k, v, dtype, P, n_head, tok_stride, prep, ck, cv, cache_rows(cache) * QI_HEAD_DIM,
+  return prep_kv(k, v, dtype, P, n_head, tok_stride, prep, ck, cv, cache_rows(cache) * QI_HEAD_DIM, range_flags,
                  (hipStream_t)stream);
 }
 
-int qi_attn_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvcache* cache, int32_t layer,
-                          int64_t P, float scale, void* workspace, int64_t workspace_bytes, void* stream) {
-  clear_hip_error();
+}  // extern "C"
+
+namespace {
+
+// Argument checks of a cached step that do not involve the workspace.
+int check_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvcache* cache, int32_t layer, int64_t P) {
   if (!io) return QI_ERR_ARG;
   int st;
   if ((st = check_tensor(io->q, io->dtype, io->n_tok, io->n_head, io->tok_stride)) != QI_OK) return st;
@@ -344,18 +353,24 @@ int qi_attn_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvca
   if ((st = check_cache(cache, io->dtype, io->n_head, layer, P)) != QI_OK) return st;
   if (P + io->n_tok > INT32_MAX) return QI_ERR_SHAPE;
   if (io->dtype == QI_BF16 && (P > QI_MAX_SOURCE_KEYS || io->n_tok > QI_MAX_SOURCE_KEYS)) return QI_ERR_SHAPE;
-  if (reinterpret_cast<uintptr_t>(io->lse) & 3) return QI_ERR_ALIGN;
-  if (!workspace) return QI_ERR_ARG;
-  if (!aligned16(workspace)) return QI_ERR_ALIGN;
-  if (workspace_bytes < qi_attn_cached_workspace_bytes(io->dtype, io->n_tok, io->n_head)) return QI_ERR_CAPACITY;
+  if ((reinterpret_cast<uintptr_t>(io->lse) & 3) || (reinterpret_cast<uintptr_t>(io->range_flags) & 3))
+    return QI_ERR_ALIGN;
+  return QI_OK;
+}
 
-  hipStream_t s = (hipStream_t)stream;
+// The cached step's launches, arguments already checked; `workspace` holds at least
+// qi_attn_cached_workspace_bytes.  Every workspace byte a launch reads was written earlier in the
+// same call (the target K/V tiles by the prep, each partial row by its key chunk), so the
+// workspace needs no clearing between calls.
+int run_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvcache* cache, int32_t layer, int64_t P,
+                      float scale, void* workspace, hipStream_t s) {
+  int st;
   const int es = elem_size(cache->dtype);
   const int64_t T = io->n_tok, RB = rows64(T);
   char* wk = (char*)workspace;
   char* wv = wk + (int64_t)io->n_head * RB * QI_HEAD_DIM * es;
-  if ((st = prep_kv(io->k, io->v, io->dtype, T, io->n_head, io->tok_stride, prep, wk, wv, RB * QI_HEAD_DIM, s)) !=
-      QI_OK)
+  if ((st = prep_kv(io->k, io->v, io->dtype, T, io->n_head, io->tok_stride, prep, wk, wv, RB * QI_HEAD_DIM,
+                    io->range_flags, s)) != QI_OK)
     return st;
   AttnArgs a = attn_args(io, prep, scale);
   a.masked = 0;
@@ -372,7 +387,22 @@ int qi_attn_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvca
   return run_attn(a, io->dtype, s);
 }
 
-int qi_euler_step(float* x, const void* v, qi_dtype v_dtype, int64_t n, float sigma_k, float sigma_k1,
+}  // namespace
+
+extern "C" {
+
+int qi_attn_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvcache* cache, int32_t layer,
+                          int64_t P, float scale, void* workspace, int64_t workspace_bytes, void* stream) {
+  clear_hip_error();
+  int st = check_target_cached(io, prep, cache, layer, P);
+  if (st != QI_OK) return st;
+  if (!workspace) return QI_ERR_ARG;
+  if (!aligned16(workspace)) return QI_ERR_ALIGN;
+  if (workspace_bytes < qi_attn_cached_workspace_bytes(io->dtype, io->n_tok, io->n_head)) return QI_ERR_CAPACITY;
+  return run_target_cached(io, prep, cache, layer, P, scale, workspace, (hipStream_t)stream);
+}
+
+int qi_euler_step(float* x, const void* v, int32_t v_dtype, int64_t n, float sigma_k, float sigma_k1,
                   void* stream) {
   clear_hip_error();
   if (!x || !v) return QI_ERR_ARG;

@@ -184,10 +184,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
   h8 qf[8];
+  bool qbad = false;   // a scaled query entry that fp16 cannot hold (magnitude >= 65520 or not finite)
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) qf[kk][i] = (_Float16)(x[8 * kk + i] * a.scale_log2);
+    for (int i = 0; i < 8; ++i) {
+      const float y = x[8 * kk + i] * a.scale_log2;
+      qbad |= !(fabsf(y) < 65520.0f);
+      qf[kk][i] = (_Float16)y;
+    }
+  if (a.flags && qbad && qok) atomicOr(a.flags, QI_RANGE_Q);
 
   // ---- key tiles of this tile row ----------------------------------------------------------
   // Sources A and B are tiled separately: tiles 0 .. ntA-1 hold keys 64t .. of A, tiles ntA ..
@@ -219,10 +225,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int bd = 0; bd < 4; ++bd)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) *(u32x2*)(po + 32 * bd + 8 * r4) = u32x2{0u, 0u};
-      if (g == 0) {
-        a.part_ml[2 * row] = -INFINITY;
-        a.part_ml[2 * row + 1] = 0.f;
-      }
+      if (g == 0) *(f32x4*)(a.part_ml + 4 * row) = f32x4{-INFINITY, 0.f, 1.f, 0.f};
     }
     return;
   }
@@ -237,10 +240,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const char* vA = (const char*)a.vA + (int64_t)h * a.a_head_stride * 2;
   const char* kB = (const char*)a.kB + (int64_t)h * a.b_head_stride * 2;
   const char* vB = (const char*)a.vB + (int64_t)h * a.b_head_stride * 2;
-  const __amdgpu_buffer_rsrc_t rkA = __builtin_amdgcn_make_buffer_rsrc((void*)kA, (short)0, ntA * TILE_B, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rvA = __builtin_amdgcn_make_buffer_rsrc((void*)vA, (short)0, ntA * TILE_B, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rkB = __builtin_amdgcn_make_buffer_rsrc((void*)kB, (short)0, ntB * TILE_B, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rvB = __builtin_amdgcn_make_buffer_rsrc((void*)vB, (short)0, ntB * TILE_B, 0x00020000);
+  // sizes in bytes as the descriptor's unsigned 32-bit record count (at most 2^31 for the largest
+  // source the entry points accept, so the product is formed unsigned)
+  const int bytesA = (int)((uint32_t)ntA * (uint32_t)TILE_B), bytesB = (int)((uint32_t)ntB * (uint32_t)TILE_B);
+  const __amdgpu_buffer_rsrc_t rkA = __builtin_amdgcn_make_buffer_rsrc((void*)kA, (short)0, bytesA, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rvA = __builtin_amdgcn_make_buffer_rsrc((void*)vA, (short)0, bytesA, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rkB = __builtin_amdgcn_make_buffer_rsrc((void*)kB, (short)0, bytesB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rvB = __builtin_amdgcn_make_buffer_rsrc((void*)vB, (short)0, bytesB, 0x00020000);
   const int voff = lane * 16;
   // copy j (0 or 1) of the K (is_k) or V tile t into K or V slot `slot`
   auto copy = [&](int t, int slot, int j, auto is_k_tag) {
@@ -540,30 +546,39 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           *(u32x2*)(op + 32 * bd + 8 * r4) = w;
         }
     } else {
-      // the chunk's output divided by its own sum: a convex combination of fp16 V rows, so it
-      // fits fp16, which halves the partial traffic; the merge weights it back by (m, l)
+      // the chunk's output divided by its own sum (a convex combination of fp16 V rows), times
+      // 2^e chosen per row so that the row's largest magnitude lies in [2^14, 2^15): every entry
+      // within 2^29 of it keeps fp16's 11-bit precision, however small V is, and none overflows.
+      // The merge weights it back by (m, l) and undoes the scale with s = 2^-e (exact).
       const int64_t row = prow0 + wave * 32 + l32;
       uint16_t* po = a.part_o + row * HD + 4 * g;
-      const float inv = 1.0f / lt;
+      const float inv = 1.0f / lt;    // lt >= 1: the reference key itself contributes 1
+      float amax = 0.f;
+#pragma unroll
+      for (int bd = 0; bd < 4; ++bd)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(o[bd][r]));
+      const float rmax = pair_max(amax) * inv;   // the same value in both lanes of the row
+      int e = rmax > 0.f ? 15 - __builtin_amdgcn_frexp_expf(rmax) : 0;
+      e = e < 100 ? e : 100;
+      const float f = __builtin_ldexpf(inv, e);
 #pragma unroll
       for (int bd = 0; bd < 4; ++bd)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const h2 lo = {(_Float16)(o[bd][4 * r4] * inv), (_Float16)(o[bd][4 * r4 + 1] * inv)};
-          const h2 hi = {(_Float16)(o[bd][4 * r4 + 2] * inv), (_Float16)(o[bd][4 * r4 + 3] * inv)};
+          const h2 lo = {(_Float16)(o[bd][4 * r4] * f), (_Float16)(o[bd][4 * r4 + 1] * f)};
+          const h2 hi = {(_Float16)(o[bd][4 * r4 + 2] * f), (_Float16)(o[bd][4 * r4 + 3] * f)};
           *(u32x2*)(po + 32 * bd + 8 * r4) = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
         }
-      if (g == 0) {
-        a.part_ml[2 * row] = m_run;
-        a.part_ml[2 * row + 1] = lt;
-      }
+      if (g == 0) *(f32x4*)(a.part_ml + 4 * row) = f32x4{m_run, lt, __builtin_ldexpf(1.0f, -e), 0.f};
     }
   }
 }
 
 // Merge of the key chunks: for each row of a chunked unit, with chunk s's normalised output
-// A_s = O_s / l_s (fp16), O = sum_s w_s A_s / sum_s w_s with w_s = 2^(m_s - M) l_s and M = max_s
-// m_s, rounded to bf16.  16 threads per row, 8 dims each.
+// A_s = O_s / l_s stored as fp16 A_s / s_s (s_s a power of two per row and chunk), O = sum_s w_s
+// s_s (A_s / s_s) / sum_s w_s with w_s = 2^(m_s - M) l_s and M = max_s m_s, rounded to bf16.  16
+// threads per row, 8 dims each.
 // Chunked unit tu is the tl-th remaining unit of run x, in run order (see k_attn_f16); its
 // partial rows are [tu][chunk][256].
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml,
@@ -592,18 +607,19 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ pa
   if (row >= n_q) return;
   const int64_t p0 = (int64_t)tu * n_split * BM + rr;   // chunk s of this row: p0 + s * BM
   float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, part_ml[2 * (p0 + s * BM)]);
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, part_ml[4 * (p0 + s * BM)]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   for (int s = 0; s < n_split; ++s) {
     const int64_t pr = p0 + s * BM;
-    const float m = part_ml[2 * pr];
-    if (m == -INFINITY) continue;
-    const float w = __builtin_amdgcn_exp2f(m - M) * part_ml[2 * pr + 1];
+    const f32x4 r = *(const f32x4*)(part_ml + 4 * pr);   // (m, l, 2^-e, 0)
+    if (r[0] == -INFINITY) continue;
+    const float w = __builtin_amdgcn_exp2f(r[0] - M) * r[1];
     den += w;
+    const float ws = w * r[2];
     const h8 x = __builtin_bit_cast(h8, *(const u32x4*)(part_o + pr * HD + d0));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] += w * (float)x[j];
+    for (int j = 0; j < 8; ++j) acc[j] += ws * (float)x[j];
   }
   const float inv = 1.0f / den;
   if (lse && d0 == 0) lse[(int64_t)h * lse_stride + row] = (M + __log2f(den)) * 0.6931471805599453f;
@@ -647,7 +663,7 @@ AttnSched attn_f16_schedule(int64_t n_q, int32_t n_head) {
 
 int64_t attn_f16_partial_bytes(int64_t n_q, int32_t n_head) {
   const AttnSched sc = attn_f16_schedule(n_q, n_head);
-  return (int64_t)sc.tail_units * sc.n_split * BM * (HD * (int64_t)sizeof(uint16_t) + 2 * (int64_t)sizeof(float));
+  return (int64_t)sc.tail_units * sc.n_split * BM * (HD * (int64_t)sizeof(uint16_t) + 4 * (int64_t)sizeof(float));
 }
 
 hipError_t launch_attn_f16(const AttnArgs& a_in, hipStream_t s) {

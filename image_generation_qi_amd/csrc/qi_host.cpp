@@ -100,7 +100,7 @@ const char* qi_status_str(int status) {
   }
 }
 
-int qi_version(void) { return 2; }
+int qi_version(void) { return 3; }
 
 int qi_layout_tokens(const qi_layout* layout, int64_t* S, int64_t* P, int64_t* T) {
   LayoutInfo li;
@@ -188,7 +188,7 @@ int qi_blockmap(const qi_layout* layout, int32_t tile_q, int32_t tile_k, uint8_t
   return QI_OK;
 }
 
-int qi_attn_tile_shape(qi_dtype dtype, int32_t* tile_q, int32_t* tile_k) {
+int qi_attn_tile_shape(int32_t dtype, int32_t* tile_q, int32_t* tile_k) {
   if (!tile_q || !tile_k) return QI_ERR_ARG;
   if (dtype == QI_BF16) {
     *tile_q = kAttnF16TileQ;
@@ -214,7 +214,7 @@ int qi_attn_schedule(int64_t n_q, int32_t n_head, int32_t* key_chunks, int32_t* 
 
 // K and V rows, [n_head][rows][128]: fp16 for bf16 attention, fp32 for fp32 attention (callers
 // pass rows already padded to whole 64-key tiles)
-static int64_t rows_bytes(qi_dtype dtype, int64_t rows, int32_t n_head) {
+static int64_t rows_bytes(int32_t dtype, int64_t rows, int32_t n_head) {
   if (rows < 0 || n_head < 1) return QI_ERR_ARG;
   if (dtype == QI_BF16) return 2 * (int64_t)n_head * rows * QI_HEAD_DIM * 2;
   if (dtype == QI_F32) return 2 * (int64_t)n_head * rows * QI_HEAD_DIM * 4;
@@ -222,12 +222,12 @@ static int64_t rows_bytes(qi_dtype dtype, int64_t rows, int32_t n_head) {
 }
 
 // Partial outputs of the key chunks (bf16 path only).
-static int64_t partial_bytes(qi_dtype dtype, int64_t n_q, int32_t n_head) {
+static int64_t partial_bytes(int32_t dtype, int64_t n_q, int32_t n_head) {
   return dtype == QI_BF16 ? attn_f16_partial_bytes(n_q, n_head) : 0;
 }
 
 
-int64_t qi_attn_full_workspace_bytes(const qi_layout* layout, qi_dtype dtype, int32_t n_head) {
+int64_t qi_attn_full_workspace_bytes(const qi_layout* layout, int32_t dtype, int32_t n_head) {
   LayoutInfo li;
   int st = analyse_layout(layout, &li);
   if (st != QI_OK) return st;
@@ -240,13 +240,13 @@ int64_t qi_attn_full_workspace_bytes(const qi_layout* layout, qi_dtype dtype, in
   return r + (pt > pp ? pt : pp);
 }
 
-int64_t qi_attn_cached_workspace_bytes(qi_dtype dtype, int64_t T, int32_t n_head) {
+int64_t qi_attn_cached_workspace_bytes(int32_t dtype, int64_t T, int32_t n_head) {
   const int64_t r = rows_bytes(dtype, rows64(T), n_head);
   if (r < 0) return r;
   return r + partial_bytes(dtype, T, n_head);
 }
 
-int64_t qi_kvcache_bytes(qi_dtype cache_dtype, int32_t n_layers, int32_t n_head, int64_t p_cap) {
+int64_t qi_kvcache_bytes(int32_t cache_dtype, int32_t n_layers, int32_t n_head, int64_t p_cap) {
   if (n_layers < 1 || n_head < 1 || p_cap < 0) return QI_ERR_ARG;
   int64_t es = cache_dtype == QI_F16 ? 2 : (cache_dtype == QI_F32 ? 4 : 0);
   if (!es) return QI_ERR_DTYPE;

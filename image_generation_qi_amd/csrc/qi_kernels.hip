@@ -24,6 +24,9 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
   return u >> 16;
 }
 
+// A value that fp16 cannot hold: magnitude 65520 or more (rounds to infinity) or not finite.
+__device__ __forceinline__ bool unfit_f16(float x) { return !(fabsf(x) < 65520.0f); }
+
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   _Float16 ha = (_Float16)a, hb = (_Float16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
@@ -161,6 +164,7 @@ __global__ __launch_bounds__(256) void k_prep_kv64(PrepArgs a) {
       vw[i] = j < a.n_tok ? *(const u32x4*)((const uint16_t*)a.v + j * a.x_tok_stride + (int64_t)h * 128 + d0 + 8 * i)
                           : u32x4{0u, 0u, 0u, 0u};
   }
+  bool kbad = false;
   float x[4][8];
 #pragma unroll
   for (int quarter = 0; quarter < 4; ++quarter) {
@@ -204,8 +208,19 @@ __global__ __launch_bounds__(256) void k_prep_kv64(PrepArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) xq[e] = 0.f;
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kbad |= unfit_f16(xq[e]);
     *(u32x4*)(kt + c * KROW + perm16(r) * 16) =
         u32x4{pack_f16(xq[0], xq[1]), pack_f16(xq[2], xq[3]), pack_f16(xq[4], xq[5]), pack_f16(xq[6], xq[7])};
+  }
+  if (a.flags && kbad) atomicOr(a.flags, QI_RANGE_K);
+  if (WITH_V && a.flags) {
+    bool vbad = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vbad |= unfit_f16(bf16_lo(vw[i][e])) || unfit_f16(bf16_hi(vw[i][e]));
+    if (vbad) atomicOr(a.flags, QI_RANGE_V);
   }
   __syncthreads();
   // K tile out: piece p (16 bytes) = chunk p / 64, slot p % 64

@@ -33,6 +33,7 @@ struct PrepArgs {
   const float* sin_t;
   const float* rms_w;  // nullable (no norm); [128]
   float eps;
+  uint32_t* flags;     // nullable: fp16 outputs OR QI_RANGE_K / QI_RANGE_V here for values that do not fit
 };
 
 hipError_t launch_prep_bf16_to_f16(const PrepArgs& a, hipStream_t s);  // bf16 in, fp16 out
@@ -76,8 +77,10 @@ struct AttnArgs {
   float* lse;           // nullable: [n_head][lse_stride], row q of the launch at lse[h * lse_stride + q]
   int64_t lse_stride;
   int32_t n_split, split_tiles, xcd_whole;
-  uint16_t* part_o;    // [chunked unit][chunk][256 rows][128] fp16, divided by the chunk's own sum
-  float* part_ml;      // [chunked unit][chunk][256 rows][2]
+  uint16_t* part_o;    // [chunked unit][chunk][256 rows][128] fp16: the chunk's output divided by
+                       // its own sum, times a power of two per row
+  float* part_ml;      // [chunked unit][chunk][256 rows][4]: max, sum, the inverse power of two, 0
+  uint32_t* flags;     // nullable: QI_RANGE_Q when a scaled, rotated query does not fit fp16
   SegTable segs;
 };
 

@@ -15,7 +15,9 @@ from ctypes import POINTER, c_char_p, c_double, c_float, c_int, c_int32, c_int64
 from typing import Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqi.so")
+# QI_LIBRARY names another build of the same library (the host-sanitized libqi_san.so of the CPU
+# sanitizer tests); it must export the same ABI version.
+LIB_PATH = os.environ.get("QI_LIBRARY") or os.path.join(_HERE, "libqi.so")
 
 QI_OK, QI_ERR_ARG, QI_ERR_DTYPE, QI_ERR_SHAPE, QI_ERR_ALIGN, QI_ERR_LAYOUT, QI_ERR_HIP, QI_ERR_CAPACITY = \
     0, -1, -2, -3, -4, -5, -6, -7
@@ -24,8 +26,9 @@ QI_SEG_TEXT, QI_SEG_IMAGE, QI_SEG_TEXT_BIDIR = 0, 1, 2
 QI_EPI_STORE, QI_EPI_STORE_F32, QI_EPI_GATED_RESIDUAL, QI_EPI_SWIGLU, QI_EPI_GELU = 0, 1, 2, 3, 4
 QI_EPI_GATED_RESIDUAL_LINEAR = 5
 QI_MAX_SOURCE_KEYS = 8388607   # keys per source of the bf16 attention (include/qi.h)
-QI_ABI_VERSION = 2             # the qi_version() these bindings are written against
+QI_ABI_VERSION = 3             # the qi_version() these bindings are written against
 QI_ATTN_BLOCK_CAUSAL, QI_ATTN_FULL = 0, 1
+QI_RANGE_Q, QI_RANGE_K, QI_RANGE_V = 1, 2, 4   # range flags of the fp16 operands (include/qi.h)
 QI_HEAD_DIM = 128
 
 
@@ -60,7 +63,8 @@ class qi_kvcache(ctypes.Structure):
 
 class qi_qkv(ctypes.Structure):
     _fields_ = [("q", c_void_p), ("k", c_void_p), ("v", c_void_p), ("o", c_void_p), ("dtype", c_int),
-                ("n_tok", c_int64), ("n_head", c_int32), ("tok_stride", c_int64), ("lse", c_void_p)]
+                ("n_tok", c_int64), ("n_head", c_int32), ("tok_stride", c_int64), ("lse", c_void_p),
+                ("range_flags", c_void_p)]
 
 
 class qi_qkprep(ctypes.Structure):
@@ -87,7 +91,7 @@ _SIGS = {
     "qi_attn_blockcausal_full": (c_int, [POINTER(qi_qkv), POINTER(qi_qkprep), POINTER(qi_layout), c_float,
                                          POINTER(qi_kvcache), c_int32, c_void_p, c_int64, c_void_p]),
     "qi_attn_prefix_store": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_int32, c_int64, POINTER(qi_qkprep),
-                                     POINTER(qi_kvcache), c_int32, c_void_p]),
+                                     POINTER(qi_kvcache), c_int32, c_void_p, c_void_p]),
     "qi_attn_target_cached": (c_int, [POINTER(qi_qkv), POINTER(qi_qkprep), POINTER(qi_kvcache), c_int32,
                                       c_int64, c_float, c_void_p, c_int64, c_void_p]),
     "qi_euler_step": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_float, c_float, c_void_p]),
@@ -183,8 +187,9 @@ def make_layout(segments, head_dim: int = 128, bands=(16, 56, 56), theta: float 
     return L
 
 
-def make_qkv(q, k, v, o, dtype: int, n_tok: int, n_head: int, tok_stride: int, lse=None) -> qi_qkv:
-    return qi_qkv(_p(q), _p(k), _p(v), _p(o), dtype, n_tok, n_head, tok_stride, _p(lse))
+def make_qkv(q, k, v, o, dtype: int, n_tok: int, n_head: int, tok_stride: int, lse=None,
+             range_flags=None) -> qi_qkv:
+    return qi_qkv(_p(q), _p(k), _p(v), _p(o), dtype, n_tok, n_head, tok_stride, _p(lse), _p(range_flags))
 
 
 def make_prep(cos_t=None, sin_t=None, q_rms_w=None, k_rms_w=None, eps: float = 1e-6) -> qi_qkprep:
@@ -265,9 +270,9 @@ def qi_attn_blockcausal_full(io: qi_qkv, prep: Optional[qi_qkprep], layout: qi_l
 
 
 def qi_attn_prefix_store(k, v, dtype: int, P: int, n_head: int, tok_stride: int, prep: Optional[qi_qkprep],
-                         cache: qi_kvcache, layer: int, stream=None) -> int:
+                         cache: qi_kvcache, layer: int, range_flags=None, stream=None) -> int:
     return lib().qi_attn_prefix_store(_p(k), _p(v), dtype, P, n_head, tok_stride, _ref(prep), _ref(cache), layer,
-                                      _p(stream))
+                                      _p(range_flags), _p(stream))
 
 
 def qi_attn_target_cached(io: qi_qkv, prep: Optional[qi_qkprep], cache: qi_kvcache, layer: int, P: int,

@@ -89,8 +89,13 @@ def _ws(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
+class RangeError(RuntimeError):
+    """A q, k or v value did not fit the fp16 operands of the bf16 attention path."""
+
+
 class Attention:
-    """Owns the workspaces for one (layout, heads, dtype) and issues the ABI calls."""
+    """Owns the workspaces and the range-flag word for one (layout, heads, dtype) and issues the
+    ABI calls.  Every call ORs its QI_RANGE_* bits into the flag word; range_flags() reads it."""
 
     def __init__(self, layout: Layout, n_head: int, io_dtype: int = Q.QI_BF16, device="cuda"):
         self.L, self.H, self.dtype, self.device = layout, n_head, io_dtype, device
@@ -98,6 +103,21 @@ class Attention:
         self.ws_cached_bytes = Q.qi_attn_cached_workspace_bytes(io_dtype, layout.T, n_head)
         self.ws_full = None
         self.ws_cached = None
+        self.flags = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def range_flags(self, clear: bool = True) -> int:
+        """QI_RANGE_* bits raised since the last clear (waits for the device)."""
+        v = int(self.flags.item())
+        if clear:
+            self.flags.zero_()
+        return v
+
+    def check_range(self):
+        """Raise RangeError if a call since the last check met a value that does not fit fp16."""
+        v = self.range_flags()
+        if v:
+            names = [n for b, n in ((Q.QI_RANGE_Q, "q"), (Q.QI_RANGE_K, "k"), (Q.QI_RANGE_V, "v")) if v & b]
+            raise RangeError(f"values of {', '.join(names)} outside the fp16 range of the attention operands")
 
     def _stride(self, t: torch.Tensor) -> int:
         assert t.dim() == 3 and t.shape[1] == self.H and t.shape[2] == 128 and t.stride(2) == 1 and t.stride(1) == 128
@@ -108,27 +128,30 @@ class Attention:
         return Q.make_prep(cos, sin, q_w, k_w, eps), (cos, sin)
 
     def full(self, q, k, v, q_w=None, k_w=None, eps=1e-6, cache: Optional[KVCache] = None, layer: int = 0,
-             scale: float = 0.0, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None) -> torch.Tensor:
-        """Step 1 over the layout; lse (optional fp32 [H][S]) receives each row's log-sum-exp."""
+             scale: float = 0.0, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+             rotate: bool = True) -> torch.Tensor:
+        """Step 1 over the layout; lse (optional fp32 [H][S]) receives each row's log-sum-exp;
+        rotate=False passes no rotation tables (q and k already rotated)."""
         if self.ws_full is None:
             self.ws_full = _ws(self.ws_full_bytes, self.device)
         o = out if out is not None else torch.empty((self.L.S, self.H, 128), dtype=q.dtype, device=self.device)
         if lse is not None:
             assert lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == (self.H, self.L.S)
-        io = Q.make_qkv(q, k, v, o, self.dtype, self.L.S, self.H, self._stride(q), lse)
-        prep, keep = self.prep(slice(0, self.L.S), q_w, k_w, eps)
+        io = Q.make_qkv(q, k, v, o, self.dtype, self.L.S, self.H, self._stride(q), lse, self.flags)
+        prep, keep = self.prep(slice(0, self.L.S), q_w, k_w, eps, rotate)
         Q.check(Q.qi_attn_blockcausal_full(io, prep, self.L.c, scale, cache.c if cache else None, layer,
                                            self.ws_full, self.ws_full_bytes, stream_handle(self.device)),
                 "qi_attn_blockcausal_full")
         return o
 
-    def store(self, k, v, cache: KVCache, layer: int = 0, k_w=None, eps=1e-6):
-        prep, keep = self.prep(slice(0, self.L.P), None, k_w, eps)
+    def store(self, k, v, cache: KVCache, layer: int = 0, k_w=None, eps=1e-6, rotate: bool = True):
+        prep, keep = self.prep(slice(0, self.L.P), None, k_w, eps, rotate)
         Q.check(Q.qi_attn_prefix_store(k, v, self.dtype, self.L.P, self.H, self._stride(k), prep, cache.c, layer,
-                                       stream_handle(self.device)), "qi_attn_prefix_store")
+                                       self.flags, stream_handle(self.device)), "qi_attn_prefix_store")
 
     def cached(self, q_t, k_t, v_t, cache: KVCache, layer: int = 0, q_w=None, k_w=None, eps=1e-6,
-               scale: float = 0.0, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+               scale: float = 0.0, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+               rotate: bool = True) -> torch.Tensor:
         """A cached target step; lse (optional fp32 [H][T]) receives each row's log-sum-exp."""
         if self.ws_cached is None:
             self.ws_cached = _ws(self.ws_cached_bytes, self.device)
@@ -136,8 +159,8 @@ class Attention:
         o = out if out is not None else torch.empty((T, self.H, 128), dtype=q_t.dtype, device=self.device)
         if lse is not None:
             assert lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == (self.H, T)
-        io = Q.make_qkv(q_t, k_t, v_t, o, self.dtype, T, self.H, self._stride(q_t), lse)
-        prep, keep = self.prep(slice(self.L.P, self.L.P + T), q_w, k_w, eps)
+        io = Q.make_qkv(q_t, k_t, v_t, o, self.dtype, T, self.H, self._stride(q_t), lse, self.flags)
+        prep, keep = self.prep(slice(self.L.P, self.L.P + T), q_w, k_w, eps, rotate)
         Q.check(Q.qi_attn_target_cached(io, prep, cache.c, layer, self.L.P, scale, self.ws_cached,
                                         self.ws_cached_bytes, stream_handle(self.device)), "qi_attn_target_cached")
         return o

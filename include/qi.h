@@ -29,7 +29,11 @@
  *   - Floating point: bf16 inputs are upcast exactly; normalisation and rotation run in fp32;
  *     the attention contractions use fp16 MFMA operands (rotated Q and K, softmax
  *     probabilities, V) with fp32 accumulation and an fp32 online softmax; outputs are
- *     rounded to bf16 (nearest even).  fp32 I/O runs fp32 arithmetic throughout.
+ *     rounded to bf16 (nearest even).  Query tiles whose keys are split into chunks (see
+ *     qi_attn_schedule) pass each chunk's normalised output through fp16 with a power-of-two
+ *     scale per row (relative error at most 2^-11 for entries within 2^29 of the row's largest)
+ *     before the merge rounds the result to bf16.  Values that do not fit fp16 are reported
+ *     through range flags (QI_RANGE_*).  fp32 I/O runs fp32 arithmetic throughout.
  *   - bf16 attention takes at most QI_MAX_SOURCE_KEYS prefix keys and as many target keys
  *     (QI_ERR_SHAPE beyond).
  */
@@ -55,6 +59,9 @@ typedef enum {
   QI_ERR_CAPACITY = -7   /* cache capacity, layer index or workspace size exceeded */
 } qi_status;
 
+/* Element types.  Every dtype field and parameter of this ABI is an int32_t holding one of these
+ * values (a plain integer, so that any value a caller stores is well defined to read and an
+ * unknown one is refused with QI_ERR_DTYPE). */
 typedef enum { QI_F32 = 0, QI_BF16 = 1, QI_F16 = 2 } qi_dtype;
 
 /* Segment kinds of the joint sequence ([OV] card 3C: text is causal, the tokens of one image
@@ -101,32 +108,48 @@ typedef struct {
  * keys past the stored count in the last tile are zero), laid out in the order the attention
  * kernel's matrix-core operands read them: K as [16 dim chunks][64 key slots][8 dims], where
  * slot p holds key p with rows 4-7 and 8-11 of every 16 exchanged; V as [8 key chunks][128
- * dims][8 keys].  dtype must be QI_F16 for bf16 attention and QI_F32 for fp32 attention.  fp16 holds every bf16 V with
- * 2^-17 <= |v| < 65504 exactly (smaller values round to the fp16 subnormal grid, absolute
- * error <= 2^-25; larger ones overflow to infinity), and keeps rotated K with 3 more mantissa
+ * dims][8 keys].  dtype must be QI_F16 for bf16 attention and QI_F32 for fp32 attention.  fp16
+ * holds every bf16 V with 2^-17 <= |v| <= 65280 exactly (smaller values round to the fp16
+ * subnormal grid, absolute error <= 2^-25; the next bf16 value, 65536, would overflow, which the
+ * calls report through their range flags, QI_RANGE_*), and keeps rotated K with 3 more mantissa
  * bits than bf16 would. */
 typedef struct {
   void* k;
   void* v;
-  qi_dtype dtype;
+  int32_t dtype;               /* a qi_dtype value */
   int32_t n_layers, n_head;
   int64_t p_cap;
 } qi_kvcache;
 
+/* Range flags of the bf16 path's fp16 operands.  The bf16 attention converts the rotated,
+ * scaled Q (scale * log2(e) * q), the rotated K and V to fp16 for the matrix cores and the fp16
+ * cache.  A value whose magnitude is 65520 or more (it would round to infinity) or that is not
+ * finite sets the bit of its tensor in the caller's flag word; the call's outputs (and, for K and
+ * V, the cache rows it wrote) are then not meaningful.  Every value below that bound converts
+ * with at most half an fp16 unit in the last place of error.  fp32 I/O converts nothing and never
+ * sets a flag. */
+#define QI_RANGE_Q 1u
+#define QI_RANGE_K 2u
+#define QI_RANGE_V 4u
+
 /* Attention operands.  q, k, v: device, token-major with `tok_stride`; o: device, dense
  * [n_tok][n_head*128].  dtype: QI_BF16 or QI_F32 for all four.  lse: NULL, or device fp32
  * [n_head][n_tok] that receives each query row's log-sum-exp, ln(sum_k exp(scale * q.k)) over its
- * visible keys (the softmax denominator; what a merge of attention over split key ranges needs). */
+ * visible keys (the softmax denominator; what a merge of attention over split key ranges needs).
+ * range_flags: NULL, or a device uint32 (4-byte aligned) into which the call ORs QI_RANGE_* bits
+ * when a q, k or v value does not fit fp16; the library never clears it (the caller zeroes it and
+ * reads it back when it chooses). */
 typedef struct {
   const void* q;
   const void* k;
   const void* v;
   void* o;
-  qi_dtype dtype;
+  int32_t dtype;               /* a qi_dtype value */
   int64_t n_tok;
   int32_t n_head;
   int64_t tok_stride;
   float* lse;
+  uint32_t* range_flags;
 } qi_qkv;
 
 /* Per-token preparation of Q and K before the contraction ([EDIT] section 6: QK-RMSNorm per
@@ -149,7 +172,8 @@ typedef struct {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* qi_status_str(int status);
 
-/* Library ABI version (increments on any signature or struct change; 2 added qi_qkv.lse). */
+/* Library ABI version (increments on any signature or struct change; 2 added qi_qkv.lse, 3 the
+ * range flags and int32_t dtype fields). */
 int qi_version(void);
 
 /* Token counts of a layout: S = all, P = prefix (all but the last segment), T = target.
@@ -174,7 +198,7 @@ int qi_rope3d_tables(const qi_layout* layout, float* cos_t, float* sin_t);
 int qi_blockmap(const qi_layout* layout, int32_t tile_q, int32_t tile_k, uint8_t* map);
 
 /* Query-tile and key-tile sizes of the attention kernel for an I/O dtype. */
-int qi_attn_tile_shape(qi_dtype dtype, int32_t* tile_q, int32_t* tile_k);
+int qi_attn_tile_shape(int32_t dtype, int32_t* tile_q, int32_t* tile_k);
 
 /* Work schedule of a bf16 attention launch over n_q query rows and n_head heads whose query tiles
  * all see the same keys (every cached step, the target rows of step 1, unmasked layouts): the
@@ -192,12 +216,12 @@ int qi_attn_schedule(int64_t n_q, int32_t n_head, int32_t* key_chunks, int32_t* 
  * split into (target rows always; prefix rows of step 1 when every prefix tile sees the same
  * key tiles, as in an unmasked layout; otherwise the prefix rows run unchunked).
  * Negative = error status. */
-int64_t qi_attn_full_workspace_bytes(const qi_layout* layout, qi_dtype dtype, int32_t n_head);
-int64_t qi_attn_cached_workspace_bytes(qi_dtype dtype, int64_t T, int32_t n_head);
+int64_t qi_attn_full_workspace_bytes(const qi_layout* layout, int32_t dtype, int32_t n_head);
+int64_t qi_attn_cached_workspace_bytes(int32_t dtype, int64_t T, int32_t n_head);
 
 /* Bytes of one cache tensor (k or v) for the given shape (fp16 rows padded to a multiple of
  * 64).  Negative = error status. */
-int64_t qi_kvcache_bytes(qi_dtype cache_dtype, int32_t n_layers, int32_t n_head, int64_t p_cap);
+int64_t qi_kvcache_bytes(int32_t cache_dtype, int32_t n_layers, int32_t n_head, int64_t p_cap);
 
 /* ------------------------------------------------------------------------------------------
  * Device calls
@@ -208,7 +232,7 @@ int64_t qi_kvcache_bytes(qi_dtype cache_dtype, int32_t n_layers, int32_t n_head,
  * token-major [n_tok][tok_stride] tensor of `dtype` (QI_BF16 or QI_F32) holding n_head heads
  * of 128.  Tables as in qi_qkprep.  bf16 results are rounded to nearest even.
  * ([3A] section 1; [EDIT] section 6.) */
-int qi_rope3d_apply(void* x, qi_dtype dtype, int64_t n_tok, int32_t n_head, int64_t tok_stride,
+int qi_rope3d_apply(void* x, int32_t dtype, int64_t n_tok, int32_t n_head, int64_t tok_stride,
                     const float* cos_t, const float* sin_t, const float* rms_w, float eps,
                     void* stream);
 
@@ -225,10 +249,11 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
 
 /* Prefix store alone: prepare K (QK-RMSNorm if prep->k_rms_w, then rotation) and copy V of
  * the P prefix tokens into cache layer `layer`, rows 0..P-1 ([OV] card 6A "Store").  k, v:
- * device token-major of `dtype`; prep tables have P rows. */
-int qi_attn_prefix_store(const void* k, const void* v, qi_dtype dtype, int64_t P, int32_t n_head,
+ * device token-major of `dtype`; prep tables have P rows.  range_flags: NULL or a device uint32
+ * that receives QI_RANGE_K / QI_RANGE_V as described for qi_qkv. */
+int qi_attn_prefix_store(const void* k, const void* v, int32_t dtype, int64_t P, int32_t n_head,
                          int64_t tok_stride, const qi_qkprep* prep, const qi_kvcache* cache,
-                         int32_t layer, void* stream);
+                         int32_t layer, uint32_t* range_flags, void* stream);
 
 /* Steps 2..N: target-only attention ([OV] card 6A "Load"): the T = io->n_tok target queries
  * attend, without a mask (the target sees every token, [OV] card 3C), to the P cached prefix
@@ -242,7 +267,7 @@ int qi_attn_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvca
 
 /* Euler update of the latent ([OV] learning goals, card 6B): x[i] += (sigma_k1 - sigma_k) * v[i]
  * for i < n.  x: device fp32; v: device, QI_F32 or QI_BF16.  The step is computed in fp32. */
-int qi_euler_step(float* x, const void* v, qi_dtype v_dtype, int64_t n, float sigma_k,
+int qi_euler_step(float* x, const void* v, int32_t v_dtype, int64_t n, float sigma_k,
                   float sigma_k1, void* stream);
 
 /* ------------------------------------------------------------------------------------------

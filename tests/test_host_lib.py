@@ -155,7 +155,7 @@ def test_tile_shape_and_sizes():
     assert Q.qi_attn_schedule(101 * 256, 5) == (1, 32, 0)   # 505 tiles: the remaining 32 / 31 run whole
     assert Q.qi_attn_schedule(0, 24) == (1, 0, 0)
     L3 = Q.make_layout(qin.WORKLOADS["txt1024_4ref64_tgt64"].segments)
-    PART = 256 * (128 * 2 + 2 * 4)   # partials of one chunk of one query tile: 256 rows x (128 fp16 + fp32 max, sum)
+    PART = 256 * (128 * 2 + 4 * 4)   # partials of one chunk of one query tile: 256 rows x (128 fp16 + fp32 max, sum, scale, pad)
     # 4096-token target: 16 x 24 = 384 query tiles (48 per XCD): per XCD 32 whole, 16 in 2 key
     # chunks: K/V fp16 rows plus the partials of the 128 chunked tiles
     # (the block-causal prefix rows of step 1 run whole)
@@ -402,7 +402,7 @@ def test_schedule_invariants_over_shapes():
     an XCD's share, a launch cuts tiles into 1..8 key chunks only when some remain after the whole
     rounds, exactly those remaining tiles are chunked, and the cached workspace holds the prepared
     K/V rows plus exactly their partials."""
-    PART = 256 * (128 * 2 + 2 * 4)
+    PART = 256 * (128 * 2 + 4 * 4)
     rng = np.random.default_rng(7)
     shapes = [(int(n), int(h)) for n, h in zip(rng.integers(1, 70000, 200), rng.integers(1, 48, 200))]
     shapes += [(256 * t, h) for t in (1, 2, 31, 32, 33) for h in (1, 8, 24, 40)]
