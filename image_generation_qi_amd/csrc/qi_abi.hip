@@ -1,7 +1,8 @@
 // qi_abi.hip - device entry points of the C ABI: argument checks, then kernel launches.
 //
 // Every check runs before the first launch, so a negative status means nothing was enqueued.
-// The library holds no device memory: caches and workspaces are caller buffers.
+// Caches and workspaces are caller buffers; the only device memory the library holds is the
+// scratch array of the allocation-free cached step (qi_attn_target_cached_noalloc).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -387,6 +388,35 @@ int run_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvcache*
   return run_attn(a, io->dtype, s);
 }
 
+// ---- the scratch buffer of the allocation-free cached step -----------------------------------
+// Device memory of a file-scope array: every GPU the library runs on holds its own copy from the
+// time the code object is loaded there until the process ends.  Host code never uses the array's
+// name as an address (on the host it is a stand-in symbol); the device address of each GPU's copy
+// is looked up once, with that GPU current, and kept.
+__device__ __align__(256) char scratch[QI_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// Device address of the current GPU's scratch array (nullptr and the HIP error on failure).
+void* scratch_address(hipError_t* err) {
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= 64) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -400,6 +430,20 @@ int qi_attn_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvca
   if (!aligned16(workspace)) return QI_ERR_ALIGN;
   if (workspace_bytes < qi_attn_cached_workspace_bytes(io->dtype, io->n_tok, io->n_head)) return QI_ERR_CAPACITY;
   return run_target_cached(io, prep, cache, layer, P, scale, workspace, (hipStream_t)stream);
+}
+
+int qi_attn_target_cached_noalloc(const qi_qkv* io, const qi_qkprep* prep, const qi_kvcache* cache, int32_t layer,
+                                  int64_t P, float scale, void* stream) {
+  clear_hip_error();
+  int st = check_target_cached(io, prep, cache, layer, P);
+  if (st != QI_OK) return st;
+  const int64_t need = qi_attn_cached_workspace_bytes(io->dtype, io->n_tok, io->n_head);
+  if (need < 0) return (int)need;
+  if (need > (int64_t)QI_NOALLOC_SCRATCH_BYTES) return QI_ERR_CAPACITY;
+  hipError_t e;
+  void* ws = scratch_address(&e);
+  if (!ws) return launch_status(e);
+  return run_target_cached(io, prep, cache, layer, P, scale, ws, (hipStream_t)stream);
 }
 
 int qi_euler_step(float* x, const void* v, int32_t v_dtype, int64_t n, float sigma_k, float sigma_k1,

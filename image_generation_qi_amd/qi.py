@@ -26,7 +26,8 @@ QI_SEG_TEXT, QI_SEG_IMAGE, QI_SEG_TEXT_BIDIR = 0, 1, 2
 QI_EPI_STORE, QI_EPI_STORE_F32, QI_EPI_GATED_RESIDUAL, QI_EPI_SWIGLU, QI_EPI_GELU = 0, 1, 2, 3, 4
 QI_EPI_GATED_RESIDUAL_LINEAR = 5
 QI_MAX_SOURCE_KEYS = 8388607   # keys per source of the bf16 attention (include/qi.h)
-QI_ABI_VERSION = 3             # the qi_version() these bindings are written against
+QI_ABI_VERSION = 4             # the qi_version() these bindings are written against
+QI_NOALLOC_SCRATCH_BYTES = 96 << 20   # scratch array of qi_attn_target_cached_noalloc (include/qi.h)
 QI_ATTN_BLOCK_CAUSAL, QI_ATTN_FULL = 0, 1
 QI_RANGE_Q, QI_RANGE_K, QI_RANGE_V = 1, 2, 4   # range flags of the fp16 operands (include/qi.h)
 QI_HEAD_DIM = 128
@@ -94,6 +95,8 @@ _SIGS = {
                                      POINTER(qi_kvcache), c_int32, c_void_p, c_void_p]),
     "qi_attn_target_cached": (c_int, [POINTER(qi_qkv), POINTER(qi_qkprep), POINTER(qi_kvcache), c_int32,
                                       c_int64, c_float, c_void_p, c_int64, c_void_p]),
+    "qi_attn_target_cached_noalloc": (c_int, [POINTER(qi_qkv), POINTER(qi_qkprep), POINTER(qi_kvcache), c_int32,
+                                              c_int64, c_float, c_void_p]),
     "qi_euler_step": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_float, c_float, c_void_p]),
     "qi_gemm_bf16": (c_int, [c_void_p, c_int64, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int64, c_int,
                              c_void_p, c_int64, c_int64, c_void_p]),
@@ -279,6 +282,12 @@ def qi_attn_target_cached(io: qi_qkv, prep: Optional[qi_qkprep], cache: qi_kvcac
                           scale: float, workspace, workspace_bytes: int, stream=None) -> int:
     return lib().qi_attn_target_cached(ctypes.byref(io), _ref(prep), _ref(cache), layer, P, scale, _p(workspace),
                                        workspace_bytes, _p(stream))
+
+
+def qi_attn_target_cached_noalloc(io: qi_qkv, prep: Optional[qi_qkprep], cache: qi_kvcache, layer: int, P: int,
+                                  scale: float, stream=None) -> int:
+    return lib().qi_attn_target_cached_noalloc(ctypes.byref(io), _ref(prep), _ref(cache), layer, P, scale,
+                                               _p(stream))
 
 
 def qi_euler_step(x, v, v_dtype: int, n: int, sigma_k: float, sigma_k1: float, stream=None) -> int:

@@ -173,7 +173,7 @@ typedef struct {
 const char* qi_status_str(int status);
 
 /* Library ABI version (increments on any signature or struct change; 2 added qi_qkv.lse, 3 the
- * range flags and int32_t dtype fields). */
+ * range flags and int32_t dtype fields, 4 the allocation-free cached step). */
 int qi_version(void);
 
 /* Token counts of a layout: S = all, P = prefix (all but the last segment), T = target.
@@ -264,6 +264,20 @@ int qi_attn_prefix_store(const void* k, const void* v, int32_t dtype, int64_t P,
 int qi_attn_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvcache* cache,
                           int32_t layer, int64_t P, float scale, void* workspace,
                           int64_t workspace_bytes, void* stream);
+
+/* qi_attn_target_cached for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same launches and the same
+ * output bits, with the workspace taken from a scratch array of QI_NOALLOC_SCRATCH_BYTES that the
+ * library holds in device memory on every GPU it runs on (from the first use on that GPU until
+ * the process ends).  The call allocates nothing.  QI_ERR_CAPACITY (nothing launched) when
+ * qi_attn_cached_workspace_bytes(io->dtype, io->n_tok, io->n_head) exceeds the array, e.g. above
+ * the 4,096-token target at 24 heads (65 MiB) by more than half.  All calls on one GPU share its
+ * array: calls that overlap in time on that GPU (other streams, other threads) race and must be
+ * serialised by the caller.  No part of the array needs clearing: each call writes every byte it
+ * reads before reading it.  Other arguments and errors as qi_attn_target_cached. */
+#define QI_NOALLOC_SCRATCH_BYTES (96ll << 20)
+int qi_attn_target_cached_noalloc(const qi_qkv* io, const qi_qkprep* prep, const qi_kvcache* cache,
+                                  int32_t layer, int64_t P, float scale, void* stream);
 
 /* Euler update of the latent ([OV] learning goals, card 6B): x[i] += (sigma_k1 - sigma_k) * v[i]
  * for i < n.  x: device fp32; v: device, QI_F32 or QI_BF16.  The step is computed in fp32. */
