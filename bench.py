@@ -10,6 +10,7 @@ resident in HBM before timing starts.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload txt1024_4ref64_tgt64|txt512_4ref64_tgt64|txt512_tgt64] [--no-cpu]
     python bench.py --dit [--layers L] [--steps K]     # full single-stream layer steps (see below)
     python bench.py --v1edit [--steps K]                # v1 / Edit-Plus full joint attention
+    python bench.py --configs [--steps K]               # the other attention workloads, one line each
 
 Prints one JSON line.  value = attention TFLOP/s over the timed steps (visible-pair flops,
 4*d per pair); roofline = one attention call's average device time (the attention kernel plus,
@@ -105,9 +106,21 @@ def visible_pairs_per_head(segments) -> int:
     return total
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, budget_s: float = 12.0):
     """The fp64 oracle's cached target step, one head at a time on the host (each head of each
-    layer with its own seeded inputs), until the budget is used (at least one head)."""
+    layer with its own seeded inputs), until the budget is used (at least one head).  The inputs
+    are fp64 N(0,1) draws used as they are (not rounded to bf16 first): the oracle's time does not
+    depend on the values."""
     import numpy as np
 
     import qi_inputs as qin
@@ -115,8 +128,10 @@ def cpu_baseline(wl, budget_s: float = 12.0):
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        blas = sorted({f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info() if i.get("user_api") == "blas"})
     except Exception:
         threads = os.cpu_count() or 1
+        blas = []
     S, P, T = wl.S, wl.P, wl.T
     cos, sin = O.rope_tables(O.positions(wl.segments))
     done, elapsed = 0, 0.0
@@ -133,7 +148,10 @@ def cpu_baseline(wl, budget_s: float = 12.0):
     flops = 4.0 * 128 * T * S * done
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} single-head cached target steps ({done / wl.n_head:.2f} layers of {wl.n_head} "
-                      f"heads; {T} queries x {S} keys, fp64 NumPy), {elapsed:.1f} s"}
+                      f"heads; {T} queries x {S} keys, fp64 NumPy on unrounded fp64 draws), {elapsed:.1f} s",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(), "blas": blas,
+            "thread_env": {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                                          "MKL_NUM_THREADS")}}
 
 
 def dit_bench(args):
@@ -160,7 +178,8 @@ def dit_bench(args):
                               lin(F, D), lin(D, F)) for _ in range(NL)]
     shared = rt.SharedWeights(lin(D, 256), lin(D, D), lin(6 * D, D), lin(D, D), lin(64, D), lin(D, 64))
     layout = rt.Layout(wl.segments, dev)
-    model = rt.DiT(layout, shared, layers, dev)
+    model = rt.DiT(layout, shared, layers, dev)   # keeps fp16 copies of the projection weights
+    del layers
     n_text = wl.segments[0].n_tokens
     # the context path: synthetic vision-language rows through the TextProjection give the text rows
     tp = rt.TextProjection(vec(D), lin(D, D), lin(D, D))
@@ -196,7 +215,7 @@ def dit_bench(args):
     res = {
         "metric": "single-stream DiT denoiser step time (conditioning + layers + head + Euler)",
         "value": round(msc, 3), "unit": "ms per cached step", "higher_is_better": False,
-        "n_gpus": 1, "steps": args.steps, "dtype": "bf16", "data": "synthetic, random-init weights",
+        "n_gpus": 1, "steps": args.steps, "dtype": "f16", "data": "synthetic, random-init weights",
         "config": {"workload": f"text {n_text} (context through the TextProjection) + 10 refs 32x32 + target 64x64 (S={S}, P={P}, T={T}); "
                                f"hidden {D}, {H}x128 heads, SwiGLU {F}; {NL} layers",
                    "step1_ms": round(ms1, 3), "step1_tflops": round(f_step1 / (ms1 * 1e-3) / 1e12, 1),
@@ -289,6 +308,133 @@ def v1edit_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def configs_bench(args):
+    """Per-call timings of the other attention workloads (one JSON line each):
+    txt256_ref32_tgt32: the 8-step loop of one layer (step 1 with the prefix store, then 7 cached
+      steps, each followed by the Euler update of the 1024 x 64 latent), QK-RMSNorm on;
+    txt512_tgt64: step 1 (4,608 tokens) and the cached target step (4,096 over 4,608 keys);
+    txt512_4ref64_tgt64: the cached target step (4,096 queries over 20,992 keys).
+    call_ms brackets the whole library call (K/V prep included) with events on the launch
+    stream; kernel_ms is the attention kernel plus merge from the library's own HIP events."""
+    import torch
+
+    import qi_inputs as qin
+    from image_generation_qi_amd import qi as Q
+    from image_generation_qi_amd import runtime as rt
+
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(99)
+    n_sets = 4
+
+    def ev_time(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        Q.qi_kernel_timing(True)
+        e0.record()
+        for i in range(reps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        kern = sorted(Q.qi_kernel_timing_read_each())
+        Q.qi_kernel_timing(False)
+        return e0.elapsed_time(e1) / reps, kern
+
+    def line(name, what, flops, call_ms, kern):
+        k50 = pct(kern, 50)
+        return {"metric": f"attention TFLOP/s, {what}", "value": round(flops / (call_ms * 1e-3) / 1e12, 1),
+                "unit": "TFLOP/s", "higher_is_better": True, "n_gpus": 1, "dtype": "f16", "data": "synthetic",
+                "config": {"workload": name, "flops_per_call": flops, "call_ms": round(call_ms, 4),
+                           "kernel_ms_p50": round(k50, 4), "kernel_tflops_p50": round(flops / (k50 * 1e-3) / 1e12, 1),
+                           "pct_of_peak_kernel": round(100.0 * flops / (k50 * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2)}}
+
+    reps = max(args.steps, 8)
+    # txt256_ref32_tgt32: one layer's 8-step loop
+    wl = qin.WORKLOADS["txt256_ref32_tgt32"]
+    S, P, T, H = wl.S, wl.P, wl.T, wl.n_head
+    L = rt.Layout(wl.segments, dev)
+    att = rt.Attention(L, H, Q.QI_BF16, dev)
+    cache = rt.KVCache(1, H, P, Q.QI_BF16, dev)
+    qw = (1.0 + 0.02 * torch.randn(128, generator=g, device=dev)).contiguous()
+    kw = (1.0 + 0.02 * torch.randn(128, generator=g, device=dev)).contiguous()
+    full = [torch.randn((S, 3, H, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(n_sets)]
+    tgt = [torch.randn((T, 3, H, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(n_sets)]
+    x = torch.randn((T, 64), generator=g, device=dev)
+    vel = torch.randn((T, 64), generator=g, device=dev).to(torch.bfloat16)
+    o_full = torch.empty((S, H, 128), dtype=torch.bfloat16, device=dev)
+    o_t = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    sig = qin.sigmas(8)
+
+    def loop(i):
+        f = full[i % n_sets]
+        att.full(f[:, 0], f[:, 1], f[:, 2], qw, kw, cache=cache, out=o_full)
+        rt.euler_step(x, vel, float(sig[0]), float(sig[1]))
+        for k in range(1, 8):
+            t = tgt[(i + k) % n_sets]
+            att.cached(t[:, 0], t[:, 1], t[:, 2], cache, 0, qw, kw, out=o_t)
+            rt.euler_step(x, vel, float(sig[k]), float(sig[k + 1]))
+
+    for i in range(2):
+        loop(i)
+    loop_ms, kern = ev_time(loop, reps)
+    f1 = 4.0 * 128 * H * visible_pairs_per_head(wl.segments)
+    fc = 4.0 * 128 * H * T * S
+    res = line(wl.name, "one layer's 8-step loop (step 1 + 7 cached steps + Euler)", f1 + 7 * fc, loop_ms, kern)
+    res["config"].update({"step1_flops": f1, "cached_flops": fc, "qk_rmsnorm": True, "heads": H})
+    print(json.dumps(res), flush=True)
+    del full, tgt, cache, att
+
+    # txt512_tgt64: step 1 and the cached target step
+    wl = qin.WORKLOADS["txt512_tgt64"]
+    S, P, T, H = wl.S, wl.P, wl.T, wl.n_head
+    L = rt.Layout(wl.segments, dev)
+    att = rt.Attention(L, H, Q.QI_BF16, dev)
+    cache = rt.KVCache(1, H, P, Q.QI_BF16, dev)
+    full = [torch.randn((S, 3, H, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(n_sets)]
+    o_full = torch.empty((S, H, 128), dtype=torch.bfloat16, device=dev)
+    o_t = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+
+    def step1(i):
+        f = full[i % n_sets]
+        att.full(f[:, 0], f[:, 1], f[:, 2], cache=cache, out=o_full)
+
+    def cached(i):
+        f = full[i % n_sets]
+        att.cached(f[P:, 0], f[P:, 1], f[P:, 2], cache, 0, out=o_t)
+
+    step1(0)
+    cached(0)
+    ms1, k1 = ev_time(step1, reps)
+    msc, kc = ev_time(cached, reps)
+    f1 = 4.0 * 128 * H * visible_pairs_per_head(wl.segments)
+    fc = 4.0 * 128 * H * T * S
+    print(json.dumps(line(wl.name, "step 1 (block-causal, 4,608 tokens)", f1, ms1, k1)), flush=True)
+    print(json.dumps(line(wl.name, "cached target step (4,096 queries over 4,608 keys)", fc, msc, kc)), flush=True)
+    del full, cache, att
+
+    # txt512_4ref64_tgt64: the cached target step over 20,992 keys (32 layer caches, round robin)
+    wl = qin.WORKLOADS["txt512_4ref64_tgt64"]
+    S, P, T, H = wl.S, wl.P, wl.T, wl.n_head
+    NL = N_LAYERS
+    L = rt.Layout(wl.segments, dev)
+    att = rt.Attention(L, H, Q.QI_BF16, dev)
+    cache = rt.KVCache(NL, H, P, Q.QI_BF16, dev)
+    for layer in range(NL):
+        kv = torch.randn((P, 2, H, 128), generator=g, device=dev).to(torch.bfloat16)
+        att.store(kv[:, 0], kv[:, 1], cache, layer)
+        del kv
+    tq = [torch.randn((T, 3, H, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(n_sets)]
+    o_t = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+
+    def cached3(i):
+        t = tq[i % n_sets]
+        att.cached(t[:, 0], t[:, 1], t[:, 2], cache, i % NL, out=o_t)
+
+    for i in range(4):
+        cached3(i)
+    msc, kc = ev_time(cached3, NL * 4)
+    fc = 4.0 * 128 * H * T * S
+    print(json.dumps(line(wl.name, "cached target step (4,096 queries over 20,992 keys)", fc, msc, kc)), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -303,6 +449,8 @@ def main():
     ap.add_argument("--dit", action="store_true", help="time full single-stream layer steps instead")
     ap.add_argument("--v1edit", action="store_true",
                     help="time the v1 / Edit-Plus joint full attention (text 512 + target + 2 references) instead")
+    ap.add_argument("--configs", action="store_true",
+                    help="time the other attention workloads instead (one JSON line each)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -316,6 +464,11 @@ def main():
         from image_generation_qi_amd import qi as Q
         Q.lib()
         v1edit_bench(args)
+        return
+    if args.configs:
+        from image_generation_qi_amd import qi as Q
+        Q.lib()
+        configs_bench(args)
         return
 
     import torch
@@ -438,11 +591,16 @@ def main():
     }
     sclk = sclk_from_profile()
     if sclk:
-        # the same fraction against the MFMA rate at the clock the chip actually ran the kernel at
-        # (256 CUs x 4 SIMDs x 1,024 flop per clock; from the committed counter summary)
+        # context from the committed counter summary (another run, possibly another box), not
+        # measured in this run: the shader clock that run held during the kernel, and this run's
+        # rate as a fraction of the MFMA rate at that clock (256 CUs x 4,096 flop per clock)
         peak_at_sclk = 256 * 4096 * sclk * 1e9 / 1e12
-        res["roofline"]["sclk_ghz_measured"] = sclk
-        res["roofline"]["frac_at_measured_sclk"] = round(achieved / peak_at_sclk, 4)
+        res["roofline"]["profile_sclk_ghz"] = sclk
+        res["roofline"]["frac_at_profile_sclk"] = round(achieved / peak_at_sclk, 4)
+        res["roofline"]["profile"] = os.path.relpath(PROFILE, ROOT)
+    if res["roofline"]["traffic"] is not None:
+        # the traffic figure also comes from that committed summary (same kernel source)
+        res["roofline"]["traffic_source"] = os.path.relpath(PROFILE, ROOT)
     res["config"].update(extra)
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")

@@ -21,7 +21,7 @@ int elem_size(int32_t t) { return t == QI_F32 ? 4 : (t == QI_BF16 || t == QI_F16
 
 int check_tensor(const void* p, int32_t dtype, int64_t n_tok, int32_t n_head, int64_t tok_stride) {
   if (!p) return QI_ERR_ARG;
-  if (dtype != QI_BF16 && dtype != QI_F32) return QI_ERR_DTYPE;
+  if (dtype != QI_BF16 && dtype != QI_F16 && dtype != QI_F32) return QI_ERR_DTYPE;
   if (n_tok < 1 || n_head < 1 || n_tok > INT32_MAX) return QI_ERR_SHAPE;
   if (tok_stride < (int64_t)n_head * QI_HEAD_DIM) return QI_ERR_SHAPE;
   if (!aligned16(p) || (tok_stride % 8) != 0) return QI_ERR_ALIGN;
@@ -40,7 +40,7 @@ int check_prep(const qi_qkprep* prep) {
 
 int check_cache(const qi_kvcache* c, int32_t io_dtype, int32_t n_head, int32_t layer, int64_t P) {
   if (!c || !c->k || !c->v) return QI_ERR_ARG;
-  const int32_t want = io_dtype == QI_BF16 ? QI_F16 : QI_F32;
+  const int32_t want = io_dtype == QI_F32 ? QI_F32 : QI_F16;
   if (c->dtype != want) return QI_ERR_DTYPE;
   if (c->n_head != n_head || c->n_layers < 1 || c->p_cap < 0) return QI_ERR_SHAPE;
   if (layer < 0 || layer >= c->n_layers || P < 0 || P > c->p_cap) return QI_ERR_CAPACITY;
@@ -123,7 +123,7 @@ int prep_kv(const void* k, const void* v, int32_t dtype, int64_t n, int32_t n_he
   pa.rms_w = prep ? prep->k_rms_w : nullptr;
   pa.eps = prep ? prep->eps : 0.f;
   pa.flags = flags;
-  return launch_status(dtype == QI_BF16 ? launch_prep_bf16_to_f16(pa, s) : launch_prep_f32(pa, s));
+  return launch_status(dtype != QI_F32 ? launch_prep_to_f16_tiles(pa, dtype == QI_F16, s) : launch_prep_f32(pa, s));
 }
 
 AttnArgs attn_args(const qi_qkv* io, const qi_qkprep* prep, float scale) {
@@ -142,7 +142,8 @@ AttnArgs attn_args(const qi_qkv* io, const qi_qkprep* prep, float scale) {
   a.n_q = (int32_t)io->n_tok;
   a.n_head = io->n_head;
   const double sc = softmax_scale(scale);
-  a.scale_log2 = io->dtype == QI_BF16 ? (float)(sc * 1.4426950408889634) : (float)sc;
+  a.scale_log2 = io->dtype != QI_F32 ? (float)(sc * 1.4426950408889634) : (float)sc;
+  a.io_f16 = io->dtype == QI_F16;
   return a;
 }
 
@@ -154,7 +155,7 @@ void set_partials(AttnArgs& a, char* base, int32_t dtype) {
   a.n_split = 1;
   a.part_o = nullptr;
   a.part_ml = nullptr;
-  if (dtype != QI_BF16) return;
+  if (dtype == QI_F32) return;
   const AttnSched sc = attn_f16_schedule(a.n_q, a.n_head);
   a.xcd_sched = 1;
   a.part_o = (uint16_t*)base;
@@ -163,9 +164,9 @@ void set_partials(AttnArgs& a, char* base, int32_t dtype) {
 
 int run_attn(const AttnArgs& a, int32_t dtype, hipStream_t s) {
   // the bf16 path addresses each key source through a buffer resource with 32-bit byte offsets
-  if (dtype == QI_BF16 && (a.nA > QI_MAX_SOURCE_KEYS || a.nB > QI_MAX_SOURCE_KEYS)) return QI_ERR_SHAPE;
+  if (dtype != QI_F32 && (a.nA > QI_MAX_SOURCE_KEYS || a.nB > QI_MAX_SOURCE_KEYS)) return QI_ERR_SHAPE;
   TimedLaunch t(s);
-  return launch_status(dtype == QI_BF16 ? launch_attn_f16(a, s) : launch_attn_f32(a, s));
+  return launch_status(dtype != QI_F32 ? launch_attn_f16(a, s) : launch_attn_f32(a, s));
 }
 
 // Step 1 on the bf16 path: the prefix query rows [0, P) run as one launch, the target rows
@@ -230,7 +231,8 @@ int qi_rope3d_apply(void* x, int32_t dtype, int64_t n_tok, int32_t n_head, int64
   pa.rms_w = rms_w;
   pa.eps = eps;
   hipStream_t s = (hipStream_t)stream;
-  return launch_status(dtype == QI_BF16 ? launch_prep_bf16_to_bf16(pa, s) : launch_prep_f32(pa, s));
+  return launch_status(dtype == QI_BF16 ? launch_prep_bf16_to_bf16(pa, s)
+                       : dtype == QI_F16 ? launch_prep_f16_to_f16(pa, s) : launch_prep_f32(pa, s));
 }
 
 int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_layout* layout, float scale,
@@ -248,7 +250,7 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
   if (!aligned16(io->o)) return QI_ERR_ALIGN;
   if (io->n_tok != li.S) return QI_ERR_SHAPE;
   // the bf16 path addresses each key source through a buffer resource with 32-bit byte offsets
-  if (io->dtype == QI_BF16 && (li.P > QI_MAX_SOURCE_KEYS || li.T > QI_MAX_SOURCE_KEYS)) return QI_ERR_SHAPE;
+  if (io->dtype != QI_F32 && (li.P > QI_MAX_SOURCE_KEYS || li.T > QI_MAX_SOURCE_KEYS)) return QI_ERR_SHAPE;
   if ((reinterpret_cast<uintptr_t>(io->lse) & 3) || (reinterpret_cast<uintptr_t>(io->range_flags) & 3))
     return QI_ERR_ALIGN;
   if ((st = check_prep(prep)) != QI_OK) return st;
@@ -258,7 +260,7 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
   if (workspace_bytes < qi_attn_full_workspace_bytes(layout, io->dtype, io->n_head)) return QI_ERR_CAPACITY;
 
   hipStream_t s = (hipStream_t)stream;
-  const int es = elem_size(io->dtype == QI_BF16 ? QI_F16 : QI_F32);
+  const int es = elem_size(io->dtype == QI_F32 ? QI_F32 : QI_F16);
   // workspace: K then V, each [head][RA + RB][128] with the prefix rows at row 0 and the target
   // rows at row RA (both padded to whole 64-key tiles), then the partial outputs of the key
   // chunks; the same layout with or without a cache (which then holds the prefix instead)
@@ -271,7 +273,7 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
   a.q_row0 = 0;
   // (the bf16 launches set their own schedule in run_attn_step1_f16)
   // target rows: K/V prepared into the workspace at row RA (with the target's table rows)
-  const int64_t off = li.P * io->tok_stride * (io->dtype == QI_BF16 ? 2 : 4);
+  const int64_t off = li.P * io->tok_stride * (io->dtype == QI_F32 ? 4 : 2);
   qi_qkprep tprep{};
   if (prep) {
     tprep = *prep;
@@ -311,7 +313,7 @@ int qi_attn_blockcausal_full(const qi_qkv* io, const qi_qkprep* prep, const qi_l
     a.a_head_stride = R * QI_HEAD_DIM;
   }
   a.nA = li.P;
-  if (io->dtype == QI_BF16)
+  if (io->dtype != QI_F32)
     return run_attn_step1_f16(a, li.tab, li.P, li.T, (char*)workspace + 2 * (int64_t)io->n_head * R * QI_HEAD_DIM * es, s);
   return run_attn(a, io->dtype, s);
 }
@@ -323,7 +325,7 @@ int qi_attn_prefix_store(const void* k, const void* v, int32_t dtype, int64_t P,
   int st;
   if (P < 0) return QI_ERR_SHAPE;
   if (P == 0) {
-    if (dtype != QI_BF16 && dtype != QI_F32) return QI_ERR_DTYPE;
+    if (dtype != QI_BF16 && dtype != QI_F16 && dtype != QI_F32) return QI_ERR_DTYPE;
     return check_cache(cache, dtype, n_head, layer, 0);
   }
   if ((st = check_tensor(k, dtype, P, n_head, tok_stride)) != QI_OK) return st;
@@ -353,7 +355,7 @@ int check_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvcach
   if ((st = check_prep(prep)) != QI_OK) return st;
   if ((st = check_cache(cache, io->dtype, io->n_head, layer, P)) != QI_OK) return st;
   if (P + io->n_tok > INT32_MAX) return QI_ERR_SHAPE;
-  if (io->dtype == QI_BF16 && (P > QI_MAX_SOURCE_KEYS || io->n_tok > QI_MAX_SOURCE_KEYS)) return QI_ERR_SHAPE;
+  if (io->dtype != QI_F32 && (P > QI_MAX_SOURCE_KEYS || io->n_tok > QI_MAX_SOURCE_KEYS)) return QI_ERR_SHAPE;
   if ((reinterpret_cast<uintptr_t>(io->lse) & 3) || (reinterpret_cast<uintptr_t>(io->range_flags) & 3))
     return QI_ERR_ALIGN;
   return QI_OK;
@@ -459,11 +461,12 @@ int qi_euler_step(float* x, const void* v, int32_t v_dtype, int64_t n, float sig
   return launch_status(launch_euler(x, v, v_dtype == QI_BF16, n, sigma_k1 - sigma_k, (hipStream_t)stream));
 }
 
-static int gemm_bf16(const void* x, int64_t ldx, const void* w, const float* bias, void* out, int64_t ldo,
-                     int64_t M, int64_t N, int64_t K, int epilogue, const float* gate, int64_t row0, int64_t P,
-                     int32_t tile_n, void* stream) {
+static int gemm_impl(const void* x, int64_t ldx, const void* w, const float* bias, void* out, int64_t ldo,
+                     int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t epilogue, const float* gate, int64_t row0,
+                     int64_t P, int32_t tile_n, uint32_t* flags, void* stream) {
   clear_hip_error();
   if (!x || !w || !out) return QI_ERR_ARG;
+  if (dtype != QI_BF16 && dtype != QI_F16) return QI_ERR_DTYPE;
   if (epilogue < QI_EPI_STORE || epilogue > QI_EPI_GATED_RESIDUAL_LINEAR) return QI_ERR_ARG;
   if ((epilogue == QI_EPI_GATED_RESIDUAL || epilogue == QI_EPI_GATED_RESIDUAL_LINEAR) && !gate) return QI_ERR_ARG;
   if (tile_n != 0 && tile_n != 256 && tile_n != 192 && tile_n != 128) return QI_ERR_ARG;
@@ -473,21 +476,27 @@ static int gemm_bf16(const void* x, int64_t ldx, const void* w, const float* bia
   // x and w are addressed through buffer resources with 32-bit byte offsets
   if (M > INT32_MAX / 2 / ldx || N > INT32_MAX / 2 / K) return QI_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(w) || !aligned16(out) || !aligned16(gate) || !aligned16(bias) || (ldx % 8) ||
-      (ldo % 8))
+      (ldo % 8) || (reinterpret_cast<uintptr_t>(flags) & 3))
     return QI_ERR_ALIGN;
   if (M == 0) return QI_OK;
-  GemmArgs a{x, ldx, w, out, ldo, M, N, K, gate, row0, P, bias};
-  return launch_status(launch_gemm(a, epilogue, tile_n, (hipStream_t)stream));
+  GemmArgs a{x, ldx, w, out, ldo, M, N, K, gate, row0, P, bias, flags};
+  return launch_status(launch_gemm(a, epilogue, tile_n, dtype == QI_F16, (hipStream_t)stream));
+}
+
+int qi_gemm(const void* x, int64_t ldx, const void* w, const float* bias, void* out, int64_t ldo, int64_t M, int64_t N,
+            int64_t K, int32_t dtype, int32_t epilogue, const float* gate, int64_t row0, int64_t P, int32_t tile_n,
+            uint32_t* range_flags, void* stream) {
+  return gemm_impl(x, ldx, w, bias, out, ldo, M, N, K, dtype, epilogue, gate, row0, P, tile_n, range_flags, stream);
 }
 
 int qi_gemm_bf16_ex(const void* x, int64_t ldx, const void* w, void* out, int64_t ldo, int64_t M, int64_t N,
                     int64_t K, int epilogue, const float* gate, int64_t row0, int64_t P, int32_t tile_n, void* stream) {
-  return gemm_bf16(x, ldx, w, nullptr, out, ldo, M, N, K, epilogue, gate, row0, P, tile_n, stream);
+  return gemm_impl(x, ldx, w, nullptr, out, ldo, M, N, K, QI_BF16, epilogue, gate, row0, P, tile_n, nullptr, stream);
 }
 
 int qi_gemm_bf16_bias(const void* x, int64_t ldx, const void* w, const float* bias, void* out, int64_t ldo, int64_t M,
                       int64_t N, int64_t K, int epilogue, const float* gate, int64_t row0, int64_t P, void* stream) {
-  return gemm_bf16(x, ldx, w, bias, out, ldo, M, N, K, epilogue, gate, row0, P, 0, stream);
+  return gemm_impl(x, ldx, w, bias, out, ldo, M, N, K, QI_BF16, epilogue, gate, row0, P, 0, nullptr, stream);
 }
 
 int qi_gemm_bf16(const void* x, int64_t ldx, const void* w, void* out, int64_t ldo, int64_t M, int64_t N, int64_t K,
@@ -495,32 +504,32 @@ int qi_gemm_bf16(const void* x, int64_t ldx, const void* w, void* out, int64_t l
   return qi_gemm_bf16_ex(x, ldx, w, out, ldo, M, N, K, epilogue, gate, row0, P, 0, stream);
 }
 
-int qi_zc_rmsnorm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64_t M, int32_t D, const float* w,
-                      const float* scale, const float* shift, int64_t row0, int64_t P, float eps, void* stream) {
+int qi_norm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64_t M, int32_t D, const float* w,
+                const float* scale, const float* shift, int64_t row0, int64_t P, float eps, int32_t center,
+                int32_t out_dtype, uint32_t* range_flags, void* stream) {
   clear_hip_error();
   if (!x || !out) return QI_ERR_ARG;
+  if (out_dtype != QI_BF16 && out_dtype != QI_F16) return QI_ERR_DTYPE;
+  if (center != 0 && center != 1) return QI_ERR_ARG;
+  if (center && w) return QI_ERR_ARG;   // LayerNorm without affine parameters
   if (M < 0 || D < 4 || (D % 4) || ldx < D || ldo < D || M > INT32_MAX) return QI_ERR_SHAPE;
   if (!(eps >= 0.f) || !std::isfinite(eps)) return QI_ERR_ARG;
   if (!aligned16(x) || !aligned16(w) || !aligned16(scale) || !aligned16(shift) || (ldx % 4) || (ldo % 4) ||
-      (reinterpret_cast<uintptr_t>(out) & 7))
+      (reinterpret_cast<uintptr_t>(out) & 7) || (reinterpret_cast<uintptr_t>(range_flags) & 3))
     return QI_ERR_ALIGN;
   if (M == 0) return QI_OK;
-  NormArgs a{x, ldx, out, ldo, M, D, w, scale, shift, row0, P, eps, 0};
-  return launch_status(launch_zc_norm_mod(a, (hipStream_t)stream));
+  NormArgs a{x, ldx, out, ldo, M, D, w, scale, shift, row0, P, eps, center, range_flags};
+  return launch_status(launch_zc_norm_mod(a, out_dtype == QI_F16, (hipStream_t)stream));
+}
+
+int qi_zc_rmsnorm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64_t M, int32_t D, const float* w,
+                      const float* scale, const float* shift, int64_t row0, int64_t P, float eps, void* stream) {
+  return qi_norm_mod(x, ldx, out, ldo, M, D, w, scale, shift, row0, P, eps, 0, QI_BF16, nullptr, stream);
 }
 
 int qi_layernorm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64_t M, int32_t D, const float* scale,
                      const float* shift, int64_t row0, int64_t P, float eps, void* stream) {
-  clear_hip_error();
-  if (!x || !out) return QI_ERR_ARG;
-  if (M < 0 || D < 4 || (D % 4) || ldx < D || ldo < D || M > INT32_MAX) return QI_ERR_SHAPE;
-  if (!(eps >= 0.f) || !std::isfinite(eps)) return QI_ERR_ARG;
-  if (!aligned16(x) || !aligned16(scale) || !aligned16(shift) || (ldx % 4) || (ldo % 4) ||
-      (reinterpret_cast<uintptr_t>(out) & 7))
-    return QI_ERR_ALIGN;
-  if (M == 0) return QI_OK;
-  NormArgs a{x, ldx, out, ldo, M, D, nullptr, scale, shift, row0, P, eps, 1};
-  return launch_status(launch_zc_norm_mod(a, (hipStream_t)stream));
+  return qi_norm_mod(x, ldx, out, ldo, M, D, nullptr, scale, shift, row0, P, eps, 1, QI_BF16, nullptr, stream);
 }
 
 int qi_timestep_embed(const float* t, int32_t n, int32_t dim, float* out, void* stream) {
@@ -547,13 +556,18 @@ int qi_linear_small(const float* x, int32_t n_vec, int32_t I, const void* w, int
   return qi_linear_small_bias(x, n_vec, I, w, nullptr, O, silu_in, y, stream);
 }
 
-int qi_cast_bf16(const float* x, void* y, int64_t n, void* stream) {
+int qi_cast(const float* x, void* y, int64_t n, int32_t dtype, uint32_t* range_flags, void* stream) {
   clear_hip_error();
   if (!x || !y) return QI_ERR_ARG;
+  if (dtype != QI_BF16 && dtype != QI_F16) return QI_ERR_DTYPE;
   if (n < 0) return QI_ERR_SHAPE;
-  if ((reinterpret_cast<uintptr_t>(x) & 3) || (reinterpret_cast<uintptr_t>(y) & 1)) return QI_ERR_ALIGN;
-  return launch_status(launch_cast_bf16(x, y, n, (hipStream_t)stream));
+  if ((reinterpret_cast<uintptr_t>(x) & 3) || (reinterpret_cast<uintptr_t>(y) & 1) ||
+      (reinterpret_cast<uintptr_t>(range_flags) & 3))
+    return QI_ERR_ALIGN;
+  return launch_status(launch_cast(x, y, n, dtype == QI_F16, range_flags, (hipStream_t)stream));
 }
+
+int qi_cast_bf16(const float* x, void* y, int64_t n, void* stream) { return qi_cast(x, y, n, QI_BF16, nullptr, stream); }
 
 int qi_last_hip_error(void) { return g_last_hip_error; }
 

@@ -1,4 +1,4 @@
-// qi_attn_f16.hip - flash-style attention for bf16 I/O on gfx950 (MI355X).
+// qi_attn_f16.hip - flash-style attention for bf16 or fp16 I/O on gfx950 (MI355X), fp16 matrix-core operands.
 //
 // Computes, per head, O = softmax(Q K^T * scale) V over the visible keys of every query
 // ("QwenImageTransformer2DModel source reading (Qwen-Image-Edit)", section 6: one joint
@@ -95,7 +95,19 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-template <bool MASKED>
+// Two fp32 values as one word of the output type: bf16, or fp16 with IO16 (nearest even).
+template <bool IO16>
+__device__ __forceinline__ uint32_t out2(float a, float b) {
+  if constexpr (IO16) {
+    const h2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    return to_bf16(a) | (to_bf16(b) << 16);
+  }
+}
+
+// IO16: q and o are fp16 (else bf16); the K/V sources are fp16 tiles either way.
+template <bool MASKED, bool IO16>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_f16(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * SLOTS * TILE_B];   // K slots, then V slots
 
@@ -146,8 +158,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       u32x4 w = qok ? *(const u32x4*)(qp + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        x[8 * kk + 2 * j] = __uint_as_float(w[j] << 16);
-        x[8 * kk + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+        if constexpr (IO16) {
+          // (through a scalar: this compiler's bit_cast of a vector element reads element 0)
+          const uint32_t wj = w[j];
+          const h2 v = __builtin_bit_cast(h2, wj);
+          x[8 * kk + 2 * j] = (float)v[0];
+          x[8 * kk + 2 * j + 1] = (float)v[1];
+        } else {
+          x[8 * kk + 2 * j] = __uint_as_float(w[j] << 16);
+          x[8 * kk + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+        }
       }
     }
   }
@@ -541,8 +561,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int bd = 0; bd < 4; ++bd)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const u32x2 w = {to_bf16(o[bd][4 * r4] * inv) | (to_bf16(o[bd][4 * r4 + 1] * inv) << 16),
-                           to_bf16(o[bd][4 * r4 + 2] * inv) | (to_bf16(o[bd][4 * r4 + 3] * inv) << 16)};
+          const u32x2 w = {out2<IO16>(o[bd][4 * r4] * inv, o[bd][4 * r4 + 1] * inv),
+                           out2<IO16>(o[bd][4 * r4 + 2] * inv, o[bd][4 * r4 + 3] * inv)};
           *(u32x2*)(op + 32 * bd + 8 * r4) = w;
         }
     } else {
@@ -581,6 +601,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // threads per row, 8 dims each.
 // Chunked unit tu is the tl-th remaining unit of run x, in run order (see k_attn_f16); its
 // partial rows are [tu][chunk][256].
+template <bool IO16>
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml,
                                                  uint16_t* __restrict__ o, int64_t o_stride, float* __restrict__ lse,
                                                  int64_t lse_stride, int n_q, int n_head, int n_split, int xcd_whole,
@@ -625,7 +646,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ pa
   if (lse && d0 == 0) lse[(int64_t)h * lse_stride + row] = (M + __log2f(den)) * 0.6931471805599453f;
   u32x4 w;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) w[j] = to_bf16(acc[2 * j] * inv) | (to_bf16(acc[2 * j + 1] * inv) << 16);
+  for (int j = 0; j < 4; ++j) w[j] = out2<IO16>(acc[2 * j] * inv, acc[2 * j + 1] * inv);
   *(u32x4*)(o + (int64_t)row * o_stride + h * HD + d0) = w;
 }
 
@@ -686,16 +707,28 @@ hipError_t launch_attn_f16(const AttnArgs& a_in, hipStream_t s) {
   a.split_tiles = (int)((kt_total + a.n_split - 1) / a.n_split);
   if (a.split_tiles < 1) a.split_tiles = 1;
   if (blocks <= 0) return hipSuccess;
-  if (a.masked)
-    hipLaunchKernelGGL(k_attn_f16<true>, dim3((unsigned)blocks), dim3(2 * BM), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_attn_f16<false>, dim3((unsigned)blocks), dim3(2 * BM), 0, s, a);
+  const dim3 grid((unsigned)blocks);
+  if (a.io_f16) {
+    if (a.masked)
+      hipLaunchKernelGGL((k_attn_f16<true, true>), grid, dim3(2 * BM), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_attn_f16<false, true>), grid, dim3(2 * BM), 0, s, a);
+  } else {
+    if (a.masked)
+      hipLaunchKernelGGL((k_attn_f16<true, false>), grid, dim3(2 * BM), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_attn_f16<false, false>), grid, dim3(2 * BM), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   const int64_t threads = (int64_t)n_tail * BM * 16;
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a.part_o, a.part_ml,
-                     (uint16_t*)a.o, a.o_stride, a.lse, a.lse_stride, a.n_q, a.n_head, a.n_split, a.xcd_whole,
-                     n_tail);
+  const dim3 cgrid((unsigned)((threads + 255) / 256));
+  if (a.io_f16)
+    hipLaunchKernelGGL(k_combine<true>, cgrid, dim3(256), 0, s, a.part_o, a.part_ml, (uint16_t*)a.o, a.o_stride,
+                       a.lse, a.lse_stride, a.n_q, a.n_head, a.n_split, a.xcd_whole, n_tail);
+  else
+    hipLaunchKernelGGL(k_combine<false>, cgrid, dim3(256), 0, s, a.part_o, a.part_ml, (uint16_t*)a.o, a.o_stride,
+                       a.lse, a.lse_stride, a.n_q, a.n_head, a.n_split, a.xcd_whole, n_tail);
   return hipGetLastError();
 }
 

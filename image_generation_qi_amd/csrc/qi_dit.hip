@@ -1,5 +1,6 @@
 // qi_dit.hip - the non-attention kernels of one single-stream DiT layer step on gfx950:
-//   - k_gemm_big<EPI, BN>: y = x W^T on bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulation) with
+//   - k_gemm_big<EPI, BN, F16>: y = x W^T on bf16 or fp16 MFMA (v_mfma_f32_32x32x16_bf16 / _f16, fp32
+//     accumulation; the fp16 form carries the layer chain's activations with 3 more mantissa bits) with
 //     fused epilogues: bf16 store (QKV projection), fp32 store (img_in, velocity head),
 //     tanh-gated residual add into the fp32 residual stream (attention out-projection and FFN
 //     down-projection), SwiGLU (FFN gate|up projection) ("Qwen-Image-2.1" course overview,
@@ -14,8 +15,10 @@
 //   - k_timestep_embed: sinusoidal embedding, cos half first (source reading, section 5.1).
 //   - k_linear_small: conditioning linears on 1..4 vectors (t-embedding MLP, shared
 //     modulation, head scale), memory-bound on the weight.
-//   - k_cast_bf16: fp32 -> bf16 (latents into img_in).
+//   - k_cast_bf16 / k_cast_f16: fp32 -> bf16 or fp16 (latents into img_in).
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "qi_launch.h"
 
@@ -23,6 +26,8 @@ namespace qi {
 namespace {
 
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -41,6 +46,19 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
 }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two fp32 values as one word of the 16-bit activation type (both rounded to nearest even): bf16
+// or, with F16, fp16.  fp16 results of magnitude 65520 or more (infinite) or not finite set `bad`.
+template <bool F16>
+__device__ __forceinline__ uint32_t pack2(float a, float b, bool& bad) {
+  if constexpr (F16) {
+    bad |= !(fabsf(a) < 65520.0f) || !(fabsf(b) < 65520.0f);
+    const h2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    return to_bf16(a) | (to_bf16(b) << 16);
+  }
+}
 
 // blockIdx -> logical tile: the hardware hands consecutive workgroups to the 8 XCDs in turn;
 // this gives each XCD a contiguous run of logical tiles (which then share panels in its L2).
@@ -67,15 +85,18 @@ __device__ __forceinline__ int gswz(int r) { return (r ^ (r >> 3)) & 7; }
 // and are not read (their results are never stored).
 constexpr int BBM = 256;
 
-template <int EPI, int BN>
+template <int EPI, int BN, bool F16>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_big(GemmArgs a) {
+  // operands and 16-bit outputs: bf16 (v_mfma_f32_32x32x16_bf16) or fp16 (..._f16)
+  using E = std::conditional_t<F16, _Float16, __bf16>;
+  using e8 = std::conditional_t<F16, h8, bf8>;
   constexpr int WTM = 64, WTN = BN / 2;    // wave tile
   constexpr int MB = WTM / 32, NB = WTN / 32;
   constexpr int XT = BBM * GBK, WT = BN * GBK, ST = XT + WT;
   constexpr int NXC = 4;                   // X copies of 1 KB (8 rows) per wave and stage
   constexpr int NWT = BN / 8;              // W copies per stage, spread over the 8 waves
   constexpr int NWC = (NWT + 7) / 8;       // most W copies of one wave
-  __shared__ __attribute__((aligned(16))) __bf16 smem[GSTAGES * ST];
+  __shared__ __attribute__((aligned(16))) E smem[GSTAGES * ST];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int wm = wave & 3, wn = wave >> 2;
@@ -114,38 +135,42 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto copy_slice = [&](int kt, int st) {
 #pragma unroll
     for (int j = 0; j < NXC; ++j) {
-      __bf16* dst = smem + st * ST + (32 * wave + 8 * j) * GBK;
+      E* dst = smem + st * ST + (32 * wave + 8 * j) * GBK;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)dst, 16, xo[j], kt * GBK * 2, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < NWC; ++j) {
       if (j < nwc) {
-        __bf16* dst = smem + st * ST + XT + 8 * (wave + 8 * j) * GBK;
+        E* dst = smem + st * ST + XT + 8 * (wave + 8 * j) * GBK;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)dst, 16, wo[j], kt * GBK * 2, 0, 0);
       }
     }
   };
   // operands of reduction step kk (of 4) from stage st
-  auto read_ops = [&](int st, int kk, bf8 (&xf)[2], bf8 (&wf)[4]) {
-    const __bf16* X = smem + st * ST;
-    const __bf16* W = X + XT;
+  auto read_ops = [&](int st, int kk, e8 (&xf)[2], e8 (&wf)[4]) {
+    const E* X = smem + st * ST;
+    const E* W = X + XT;
 #pragma unroll
     for (int b = 0; b < MB; ++b) {
       const int r = WTM * wm + 32 * b + l32;
-      xf[b] = *(const bf8*)(X + r * GBK + 8 * ((2 * kk + g) ^ gswz(r)));
+      xf[b] = *(const e8*)(X + r * GBK + 8 * ((2 * kk + g) ^ gswz(r)));
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int r = WTN * wn + 32 * b + l32;
-      wf[b] = *(const bf8*)(W + r * GBK + 8 * ((2 * kk + g) ^ gswz(r)));
+      wf[b] = *(const e8*)(W + r * GBK + 8 * ((2 * kk + g) ^ gswz(r)));
     }
   };
-  auto mfmas = [&](f32x16 (&acc)[MB][NB], const bf8 (&xf)[2], const bf8 (&wf)[4]) {
+  auto mfmas = [&](f32x16 (&acc)[MB][NB], const e8 (&xf)[2], const e8 (&wf)[4]) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], xf[mb], acc[mb][nb], 0, 0, 0);
+      for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (F16)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[nb], xf[mb], acc[mb][nb], 0, 0, 0);
+        else
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], xf[mb], acc[mb][nb], 0, 0, 0);
+      }
   };
   f32x16 acc[MB][NB];
 #pragma unroll
@@ -160,7 +185,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   copy_slice(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  bf8 xf[2][2], wf[2][4];
+  e8 xf[2][2], wf[2][4];
   read_ops(0, 0, xf[0], wf[0]);
   for (int kt = 0; kt < nkt; ++kt) {
     const int st = kt & 1;
@@ -179,6 +204,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // epilogue: acc[mb][nb][r] = y[m][n], m = m0 + 64wm + 32mb + l32,
   // n = n0 + WTN*wn + 32nb + 8(r/4) + 4g + r%4
+  bool bad = false;   // an fp16 output that does not fit
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int64_t m = m0 + WTM * wm + 32 * mb + l32;
@@ -203,7 +229,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int blk = 0; blk < NB / 2; ++blk) {
         if (n0 + WTN * wn + 64 * blk >= a.N) continue;
         const int64_t f0 = (n0 + WTN * wn + 64 * blk) / 2;
-        __bf16* op = (__bf16*)a.out + m * a.ldo + f0 + 4 * g;
+        E* op = (E*)a.out + m * a.ldo + f0 + 4 * g;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           uint32_t w2[2];
@@ -215,7 +241,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               const float gt = acc[mb][2 * blk][4 * r4 + 2 * h + e], up = acc[mb][2 * blk + 1][4 * r4 + 2 * h + e];
               v[e] = gt / (1.0f + __expf(-gt)) * up;
             }
-            w2[h] = to_bf16(v[0]) | (to_bf16(v[1]) << 16);
+            w2[h] = pack2<F16>(v[0], v[1], bad);
           }
           *(u32x2*)(op + 8 * r4) = u32x2{w2[0], w2[1]};
         }
@@ -230,8 +256,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           if (n >= a.N) continue;
           const f32x4 y = {acc[mb][nb][4 * r4], acc[mb][nb][4 * r4 + 1], acc[mb][nb][4 * r4 + 2], acc[mb][nb][4 * r4 + 3]};
           if constexpr (EPI == QI_EPI_STORE) {
-            *(u32x2*)((__bf16*)a.out + m * a.ldo + n) =
-                u32x2{to_bf16(y[0]) | (to_bf16(y[1]) << 16), to_bf16(y[2]) | (to_bf16(y[3]) << 16)};
+            *(u32x2*)((E*)a.out + m * a.ldo + n) = u32x2{pack2<F16>(y[0], y[1], bad), pack2<F16>(y[2], y[3], bad)};
           } else if constexpr (EPI == QI_EPI_STORE_F32) {
             *(f32x4*)((float*)a.out + m * a.ldo + n) = y;
           } else if constexpr (EPI == QI_EPI_GELU) {
@@ -242,8 +267,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               const float u = 0.7978845608028654f * __builtin_fmaf(0.044715f * y[e] * y[e], y[e], y[e]);
               gl[e] = 0.5f * y[e] * (1.0f + tanhf(u));
             }
-            *(u32x2*)((__bf16*)a.out + m * a.ldo + n) =
-                u32x2{to_bf16(gl[0]) | (to_bf16(gl[1]) << 16), to_bf16(gl[2]) | (to_bf16(gl[3]) << 16)};
+            *(u32x2*)((E*)a.out + m * a.ldo + n) = u32x2{pack2<F16>(gl[0], gl[1], bad), pack2<F16>(gl[2], gl[3], bad)};
           } else {  // QI_EPI_GATED_RESIDUAL (tanh gate) or QI_EPI_GATED_RESIDUAL_LINEAR (gate as is)
             const f32x4 gt = *(const f32x4*)(a.gate + ((m + a.row0 < a.P) ? 0 : a.N) + n);
             f32x4* xp = (f32x4*)((float*)a.out + m * a.ldo + n);
@@ -257,13 +281,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   }
+  if (F16 && a.flags && bad) atomicOr(a.flags, QI_RANGE_OUT);
 }
 
 // ZeroCenterRMSNorm + modulation, one workgroup per row; D % 4 == 0.
 // The same for rows of up to 256 * NCH features: one wave per row (four rows per workgroup), the
 // row held in registers (NCH float4 per lane, all loads in flight at once), so the mean, the sum of
 // squares and the output need one read of the row.
-template <int NCH>
+template <int NCH, bool F16>
 __global__ __launch_bounds__(256) void k_norm_rows(NormArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -302,7 +327,8 @@ __global__ __launch_bounds__(256) void k_norm_rows(NormArgs a) {
   const int seg = (m + a.row0 < a.P) ? 0 : 1;
   const float* sc = a.scale ? a.scale + seg * a.D : nullptr;
   const float* sh = a.shift ? a.shift + seg * a.D : nullptr;
-  __bf16* out = (__bf16*)a.out + m * a.ldo;
+  uint16_t* out = (uint16_t*)a.out + m * a.ldo;
+  bool bad = false;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int q = lane + 64 * c;
@@ -326,10 +352,12 @@ __global__ __launch_bounds__(256) void k_norm_rows(NormArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[e] += t[e];
     }
-    *(u32x2*)(out + i) = u32x2{to_bf16(y[0]) | (to_bf16(y[1]) << 16), to_bf16(y[2]) | (to_bf16(y[3]) << 16)};
+    *(u32x2*)(out + i) = u32x2{pack2<F16>(y[0], y[1], bad), pack2<F16>(y[2], y[3], bad)};
   }
+  if (F16 && a.flags && bad) atomicOr(a.flags, QI_RANGE_OUT);
 }
 
+template <bool F16>
 __global__ __launch_bounds__(256) void k_zc_norm_mod(NormArgs a) {
   __shared__ float red[8];
   const int64_t m = blockIdx.x;
@@ -363,7 +391,8 @@ __global__ __launch_bounds__(256) void k_zc_norm_mod(NormArgs a) {
   const int seg = (m + a.row0 < a.P) ? 0 : 1;
   const float* sc = a.scale ? a.scale + seg * a.D : nullptr;
   const float* sh = a.shift ? a.shift + seg * a.D : nullptr;
-  __bf16* out = (__bf16*)a.out + m * a.ldo;
+  uint16_t* out = (uint16_t*)a.out + m * a.ldo;
+  bool bad = false;
   for (int i = 4 * threadIdx.x; i < a.D; i += 1024) {
     const f32x4 v = *(const f32x4*)(x + i);
     float y[4];
@@ -375,8 +404,9 @@ __global__ __launch_bounds__(256) void k_zc_norm_mod(NormArgs a) {
       if (sh) t += sh[i + e];
       y[e] = t;
     }
-    *(u32x2*)(out + i) = u32x2{to_bf16(y[0]) | (to_bf16(y[1]) << 16), to_bf16(y[2]) | (to_bf16(y[3]) << 16)};
+    *(u32x2*)(out + i) = u32x2{pack2<F16>(y[0], y[1], bad), pack2<F16>(y[2], y[3], bad)};
   }
+  if (F16 && a.flags && bad) atomicOr(a.flags, QI_RANGE_OUT);
 }
 
 // out[j][i] = cos(t_j f_i) for i < half, sin(t_j f_{i-half}) after; f_i = 10000^(-i/half).
@@ -433,6 +463,14 @@ __global__ void k_cast_bf16(const float* __restrict__ x, __bf16* __restrict__ y,
   if (i < n) ((uint16_t*)y)[i] = (uint16_t)to_bf16(x[i]);
 }
 
+// fp32 -> fp16 (nearest even; beyond the fp16 range infinity, reported through the flags)
+__global__ void k_cast_f16(const float* __restrict__ x, _Float16* __restrict__ y, int64_t n, uint32_t* flags) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  y[i] = (_Float16)x[i];
+  if (flags && !(fabsf(x[i]) < 65520.0f)) atomicOr(flags, QI_RANGE_OUT);
+}
+
 }  // namespace
 
 namespace {
@@ -440,9 +478,10 @@ namespace {
 // Kernel template instances are launched from plain functions: instantiated only inside another
 // function template, their host stubs are not emitted by this compiler.
 #define QI_LAUNCH_BIG(EPI_, BN_) \
-  hipLaunchKernelGGL((k_gemm_big<EPI_, BN_>), dim3(blocks), dim3(512), 0, s, a)
+  hipLaunchKernelGGL((k_gemm_big<EPI_, BN_, QI_GEMM_F16>), dim3(blocks), dim3(512), 0, s, a)
 
-hipError_t launch_big(const GemmArgs& a, int epi, int bn, hipStream_t s) {
+#define QI_GEMM_F16 false
+hipError_t launch_big_bf16(const GemmArgs& a, int epi, int bn, hipStream_t s) {
   const unsigned blocks = (unsigned)(((a.M + BBM - 1) / BBM) * ((a.N + bn - 1) / bn));
   if (bn == 256) {
     switch (epi) {
@@ -478,6 +517,45 @@ hipError_t launch_big(const GemmArgs& a, int epi, int bn, hipStream_t s) {
   }
   return hipGetLastError();
 }
+#undef QI_GEMM_F16
+#define QI_GEMM_F16 true
+hipError_t launch_big_f16(const GemmArgs& a, int epi, int bn, hipStream_t s) {
+  const unsigned blocks = (unsigned)(((a.M + BBM - 1) / BBM) * ((a.N + bn - 1) / bn));
+  if (bn == 256) {
+    switch (epi) {
+      case QI_EPI_STORE: QI_LAUNCH_BIG(QI_EPI_STORE, 256); break;
+      case QI_EPI_STORE_F32: QI_LAUNCH_BIG(QI_EPI_STORE_F32, 256); break;
+      case QI_EPI_GATED_RESIDUAL: QI_LAUNCH_BIG(QI_EPI_GATED_RESIDUAL, 256); break;
+      case QI_EPI_GELU: QI_LAUNCH_BIG(QI_EPI_GELU, 256); break;
+      case QI_EPI_GATED_RESIDUAL_LINEAR: QI_LAUNCH_BIG(QI_EPI_GATED_RESIDUAL_LINEAR, 256); break;
+      case QI_EPI_SWIGLU: QI_LAUNCH_BIG(QI_EPI_SWIGLU, 256); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (bn == 192) {
+    switch (epi) {
+      case QI_EPI_STORE: QI_LAUNCH_BIG(QI_EPI_STORE, 192); break;
+      case QI_EPI_STORE_F32: QI_LAUNCH_BIG(QI_EPI_STORE_F32, 192); break;
+      case QI_EPI_GATED_RESIDUAL: QI_LAUNCH_BIG(QI_EPI_GATED_RESIDUAL, 192); break;
+      case QI_EPI_GELU: QI_LAUNCH_BIG(QI_EPI_GELU, 192); break;
+      case QI_EPI_GATED_RESIDUAL_LINEAR: QI_LAUNCH_BIG(QI_EPI_GATED_RESIDUAL_LINEAR, 192); break;
+      default: return hipErrorInvalidValue;   // SwiGLU needs whole 64-row gate|up blocks per wave
+    }
+  } else if (bn == 128) {
+    switch (epi) {
+      case QI_EPI_STORE: QI_LAUNCH_BIG(QI_EPI_STORE, 128); break;
+      case QI_EPI_STORE_F32: QI_LAUNCH_BIG(QI_EPI_STORE_F32, 128); break;
+      case QI_EPI_GATED_RESIDUAL: QI_LAUNCH_BIG(QI_EPI_GATED_RESIDUAL, 128); break;
+      case QI_EPI_GELU: QI_LAUNCH_BIG(QI_EPI_GELU, 128); break;
+      case QI_EPI_GATED_RESIDUAL_LINEAR: QI_LAUNCH_BIG(QI_EPI_GATED_RESIDUAL_LINEAR, 128); break;
+      case QI_EPI_SWIGLU: QI_LAUNCH_BIG(QI_EPI_SWIGLU, 128); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+#undef QI_GEMM_F16
 #undef QI_LAUNCH_BIG
 
 }  // namespace
@@ -506,20 +584,31 @@ int gemm_config(int64_t M, int64_t N, int epi) {
   return best;
 }
 
-hipError_t launch_gemm(const GemmArgs& a, int epi, int tile_n, hipStream_t s) {
+hipError_t launch_gemm(const GemmArgs& a, int epi, int tile_n, bool f16, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  return launch_big(a, epi, tile_n ? tile_n : gemm_config(a.M, a.N, epi), s);
+  const int bn = tile_n ? tile_n : gemm_config(a.M, a.N, epi);
+  return f16 ? launch_big_f16(a, epi, bn, s) : launch_big_bf16(a, epi, bn, s);
 }
 
-hipError_t launch_zc_norm_mod(const NormArgs& a, hipStream_t s) {
+hipError_t launch_zc_norm_mod(const NormArgs& a, bool f16, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
   const unsigned rows4 = (unsigned)((a.M + 3) / 4);
-  if (a.D <= 1024)
-    hipLaunchKernelGGL(k_norm_rows<4>, dim3(rows4), dim3(256), 0, s, a);
-  else if (a.D <= 4096)
-    hipLaunchKernelGGL(k_norm_rows<16>, dim3(rows4), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_zc_norm_mod, dim3((unsigned)a.M), dim3(256), 0, s, a);
+  if (a.D <= 1024) {
+    if (f16)
+      hipLaunchKernelGGL((k_norm_rows<4, true>), dim3(rows4), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_norm_rows<4, false>), dim3(rows4), dim3(256), 0, s, a);
+  } else if (a.D <= 4096) {
+    if (f16)
+      hipLaunchKernelGGL((k_norm_rows<16, true>), dim3(rows4), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_norm_rows<16, false>), dim3(rows4), dim3(256), 0, s, a);
+  } else {
+    if (f16)
+      hipLaunchKernelGGL(k_zc_norm_mod<true>, dim3((unsigned)a.M), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(k_zc_norm_mod<false>, dim3((unsigned)a.M), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -538,9 +627,12 @@ hipError_t launch_linear_small(const float* x, int nv, int I, const void* w, con
   return hipGetLastError();
 }
 
-hipError_t launch_cast_bf16(const float* x, void* y, int64_t n, hipStream_t s) {
+hipError_t launch_cast(const float* x, void* y, int64_t n, bool f16, uint32_t* flags, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_cast_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, (__bf16*)y, n);
+  if (f16)
+    hipLaunchKernelGGL(k_cast_f16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, (_Float16*)y, n, flags);
+  else
+    hipLaunchKernelGGL(k_cast_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, (__bf16*)y, n);
   return hipGetLastError();
 }
 

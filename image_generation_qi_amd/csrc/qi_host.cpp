@@ -100,7 +100,7 @@ const char* qi_status_str(int status) {
   }
 }
 
-int qi_version(void) { return 4; }
+int qi_version(void) { return 5; }
 
 int qi_layout_tokens(const qi_layout* layout, int64_t* S, int64_t* P, int64_t* T) {
   LayoutInfo li;
@@ -190,7 +190,7 @@ int qi_blockmap(const qi_layout* layout, int32_t tile_q, int32_t tile_k, uint8_t
 
 int qi_attn_tile_shape(int32_t dtype, int32_t* tile_q, int32_t* tile_k) {
   if (!tile_q || !tile_k) return QI_ERR_ARG;
-  if (dtype == QI_BF16) {
+  if (dtype == QI_BF16 || dtype == QI_F16) {
     *tile_q = kAttnF16TileQ;
     *tile_k = 64;
   } else if (dtype == QI_F32) {
@@ -212,18 +212,18 @@ int qi_attn_schedule(int64_t n_q, int32_t n_head, int32_t* key_chunks, int32_t* 
   return QI_OK;
 }
 
-// K and V rows, [n_head][rows][128]: fp16 for bf16 attention, fp32 for fp32 attention (callers
+// K and V rows, [n_head][rows][128]: fp16 for bf16 and fp16 attention, fp32 for fp32 attention (callers
 // pass rows already padded to whole 64-key tiles)
 static int64_t rows_bytes(int32_t dtype, int64_t rows, int32_t n_head) {
   if (rows < 0 || n_head < 1) return QI_ERR_ARG;
-  if (dtype == QI_BF16) return 2 * (int64_t)n_head * rows * QI_HEAD_DIM * 2;
+  if (dtype == QI_BF16 || dtype == QI_F16) return 2 * (int64_t)n_head * rows * QI_HEAD_DIM * 2;
   if (dtype == QI_F32) return 2 * (int64_t)n_head * rows * QI_HEAD_DIM * 4;
   return QI_ERR_DTYPE;
 }
 
-// Partial outputs of the key chunks (bf16 path only).
+// Partial outputs of the key chunks (16-bit paths only).
 static int64_t partial_bytes(int32_t dtype, int64_t n_q, int32_t n_head) {
-  return dtype == QI_BF16 ? attn_f16_partial_bytes(n_q, n_head) : 0;
+  return (dtype == QI_BF16 || dtype == QI_F16) ? attn_f16_partial_bytes(n_q, n_head) : 0;
 }
 
 

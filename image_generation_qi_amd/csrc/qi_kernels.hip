@@ -12,6 +12,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -36,7 +37,7 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 // QK preparation: 16 threads per (token, head) row, 8 consecutive elements per thread, so one
 // row is one coalesced 256-byte (bf16) or 512-byte (fp32) segment.
 // ---------------------------------------------------------------------------------------------
-enum { IN_BF16 = 0, IN_F32 = 1 };
+enum { IN_BF16 = 0, IN_F32 = 1, IN_F16 = 2 };
 enum { OUT_BF16 = 0, OUT_F16 = 1, OUT_F32 = 2 };
 
 template <int IN, int OUT>
@@ -47,6 +48,17 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, float x[8])
     for (int j = 0; j < 4; ++j) {
       x[2 * j] = bf16_lo(w[j]);
       x[2 * j + 1] = bf16_hi(w[j]);
+    }
+  } else if (IN == IN_F16) {
+    const u32x4 w = *(const u32x4*)((const uint16_t*)base + off);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // (the element goes through a scalar first: this compiler's bit_cast of an element of a
+      // vector value reads element 0 whatever the index)
+      const uint32_t wj = w[j];
+      const h2 v = __builtin_bit_cast(h2, wj);
+      x[2 * j] = (float)v[0];
+      x[2 * j + 1] = (float)v[1];
     }
   } else {
     const f32x4* p = (const f32x4*)((const float*)base + off);
@@ -143,7 +155,7 @@ __device__ __forceinline__ int perm16(int p) {
 // (chunk rows padded by 16 bytes, so the 16 chunks of one key land in distinct banks); V: the bf16
 // rows go through LDS as fp16 [key][dim].  Both tiles then leave as whole 1 KB runs: every global
 // read is a run of 256 bytes of one token's row and every write 16 contiguous bytes per lane.
-template <bool WITH_V>
+template <bool WITH_V, int IN>
 __global__ __launch_bounds__(256) void k_prep_kv64(PrepArgs a) {
   constexpr int KROW = 64 * 16 + 16;           // bytes per dim chunk of the staged K tile (padded)
   // one staging buffer, the K tile first and then the V tile (16.6 KB, so that 8 workgroups fit a
@@ -170,7 +182,7 @@ __global__ __launch_bounds__(256) void k_prep_kv64(PrepArgs a) {
   for (int quarter = 0; quarter < 4; ++quarter) {
     const int64_t j = (int64_t)t * 64 + rr + 16 * quarter;
     if (j < a.n_tok) {
-      load8<IN_BF16, OUT_F16>(a.x, j * a.x_tok_stride + (int64_t)h * 128 + 8 * c, x[quarter]);
+      load8<IN, OUT_F16>(a.x, j * a.x_tok_stride + (int64_t)h * 128 + 8 * c, x[quarter]);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[quarter][e] = 0.f;
@@ -214,7 +226,7 @@ __global__ __launch_bounds__(256) void k_prep_kv64(PrepArgs a) {
         u32x4{pack_f16(xq[0], xq[1]), pack_f16(xq[2], xq[3]), pack_f16(xq[4], xq[5]), pack_f16(xq[6], xq[7])};
   }
   if (a.flags && kbad) atomicOr(a.flags, QI_RANGE_K);
-  if (WITH_V && a.flags) {
+  if (WITH_V && IN == IN_BF16 && a.flags) {   // (fp16 V is in range by construction)
     bool vbad = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -237,7 +249,8 @@ __global__ __launch_bounds__(256) void k_prep_kv64(PrepArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vt[key][(d0 + 8 * i) / 2 + e] = pack_f16(bf16_lo(vw[i][e]), bf16_hi(vw[i][e]));
+        for (int e = 0; e < 4; ++e)
+          vt[key][(d0 + 8 * i) / 2 + e] = IN == IN_F16 ? vw[i][e] : pack_f16(bf16_lo(vw[i][e]), bf16_hi(vw[i][e]));
     }
     __syncthreads();
     // V tile out: piece p = key chunk p / 128, dim p % 128 (8 keys of that dim)
@@ -386,16 +399,24 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
 
 }  // namespace
 
-hipError_t launch_prep_bf16_to_f16(const PrepArgs& a, hipStream_t s) {
+hipError_t launch_prep_to_f16_tiles(const PrepArgs& a, bool in_f16, hipStream_t s) {
   if (a.n_tok <= 0) return hipSuccess;
   const dim3 grid((unsigned)((a.n_tok + 63) / 64), (unsigned)a.n_head);
-  if (a.v)
-    hipLaunchKernelGGL(k_prep_kv64<true>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_prep_kv64<false>, grid, dim3(256), 0, s, a);
+  if (in_f16) {
+    if (a.v)
+      hipLaunchKernelGGL((k_prep_kv64<true, IN_F16>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_prep_kv64<false, IN_F16>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.v)
+      hipLaunchKernelGGL((k_prep_kv64<true, IN_BF16>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_prep_kv64<false, IN_BF16>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 hipError_t launch_prep_bf16_to_bf16(const PrepArgs& a, hipStream_t s) { return launch_prep<IN_BF16, OUT_BF16>(a, s); }
+hipError_t launch_prep_f16_to_f16(const PrepArgs& a, hipStream_t s) { return launch_prep<IN_F16, OUT_F16>(a, s); }
 hipError_t launch_prep_f32(const PrepArgs& a, hipStream_t s) { return launch_prep<IN_F32, OUT_F32>(a, s); }
 
 hipError_t launch_euler(float* x, const void* v, bool v_bf16, int64_t n, float dt, hipStream_t s) {

@@ -36,8 +36,9 @@ struct PrepArgs {
   uint32_t* flags;     // nullable: fp16 outputs OR QI_RANGE_K / QI_RANGE_V here for values that do not fit
 };
 
-hipError_t launch_prep_bf16_to_f16(const PrepArgs& a, hipStream_t s);  // bf16 in, fp16 out
+hipError_t launch_prep_to_f16_tiles(const PrepArgs& a, bool in_f16, hipStream_t s);  // bf16 / fp16 in, fp16 tiles out
 hipError_t launch_prep_bf16_to_bf16(const PrepArgs& a, hipStream_t s); // bf16 in, bf16 out
+hipError_t launch_prep_f16_to_f16(const PrepArgs& a, hipStream_t s);   // fp16 in, fp16 out
 hipError_t launch_prep_f32(const PrepArgs& a, hipStream_t s);          // fp32 in, fp32 out
 
 hipError_t launch_euler(float* x, const void* v, bool v_bf16, int64_t n, float dt, hipStream_t s);
@@ -81,6 +82,7 @@ struct AttnArgs {
                        // its own sum, times a power of two per row
   float* part_ml;      // [chunked unit][chunk][256 rows][4]: max, sum, the inverse power of two, 0
   uint32_t* flags;     // nullable: QI_RANGE_Q when a scaled, rotated query does not fit fp16
+  int32_t io_f16;      // fp16 path: q, o (and the merge's output) are fp16 instead of bf16
   SegTable segs;
 };
 
@@ -115,6 +117,7 @@ struct GemmArgs {
   const float* gate;   // gated residual epilogues: fp32 [2][N]; row m uses gate[(m + row0 < P) ? 0 : 1]
   int64_t row0, P;
   const float* bias;   // nullable fp32 [N], added to y before the epilogue
+  uint32_t* flags;     // nullable: fp16 outputs that do not fit set QI_RANGE_OUT
 };
 // ZeroCenterRMSNorm + modulation of fp32 rows into bf16 rows.
 struct NormArgs {
@@ -130,17 +133,19 @@ struct NormArgs {
   int64_t row0, P;
   float eps;
   int32_t center;       // 1: subtract the row mean first (LayerNorm without affine)
+  uint32_t* flags;      // nullable: fp16 outputs that do not fit set QI_RANGE_OUT
 };
 
 // tile_n: feature width of the 256 x tile_n workgroup tiles (256, 192 or 128; 192 not with
 // SwiGLU), 0 = chosen by gemm_config.
-hipError_t launch_gemm(const GemmArgs& a, int epilogue, int tile_n, hipStream_t s);
+// f16: x, w and the 16-bit outputs are fp16 (else bf16).
+hipError_t launch_gemm(const GemmArgs& a, int epilogue, int tile_n, bool f16, hipStream_t s);
 int gemm_config(int64_t M, int64_t N, int epilogue);
-hipError_t launch_zc_norm_mod(const NormArgs& a, hipStream_t s);
+hipError_t launch_zc_norm_mod(const NormArgs& a, bool f16, hipStream_t s);   // f16: fp16 output (else bf16)
 hipError_t launch_timestep_embed(const float* t, int n, int dim, float* out, hipStream_t s);
 hipError_t launch_linear_small(const float* x, int nv, int I, const void* w, const float* bias, int O, int silu_in, float* y,
                                hipStream_t s);
-hipError_t launch_cast_bf16(const float* x, void* y, int64_t n, hipStream_t s);
+hipError_t launch_cast(const float* x, void* y, int64_t n, bool f16, uint32_t* flags, hipStream_t s);
 
 hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);   // bf16 q/o, fp16 K/V sources
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);   // fp32 throughout

@@ -26,10 +26,10 @@ QI_SEG_TEXT, QI_SEG_IMAGE, QI_SEG_TEXT_BIDIR = 0, 1, 2
 QI_EPI_STORE, QI_EPI_STORE_F32, QI_EPI_GATED_RESIDUAL, QI_EPI_SWIGLU, QI_EPI_GELU = 0, 1, 2, 3, 4
 QI_EPI_GATED_RESIDUAL_LINEAR = 5
 QI_MAX_SOURCE_KEYS = 8388607   # keys per source of the bf16 attention (include/qi.h)
-QI_ABI_VERSION = 4             # the qi_version() these bindings are written against
+QI_ABI_VERSION = 5             # the qi_version() these bindings are written against
 QI_NOALLOC_SCRATCH_BYTES = 96 << 20   # scratch array of qi_attn_target_cached_noalloc (include/qi.h)
 QI_ATTN_BLOCK_CAUSAL, QI_ATTN_FULL = 0, 1
-QI_RANGE_Q, QI_RANGE_K, QI_RANGE_V = 1, 2, 4   # range flags of the fp16 operands (include/qi.h)
+QI_RANGE_Q, QI_RANGE_K, QI_RANGE_V, QI_RANGE_OUT = 1, 2, 4, 8   # range flags of fp16 values (include/qi.h)
 QI_HEAD_DIM = 128
 
 
@@ -113,6 +113,11 @@ _SIGS = {
     "qi_linear_small_bias": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
                                      c_void_p]),
     "qi_cast_bf16": (c_int, [c_void_p, c_void_p, c_int64, c_void_p]),
+    "qi_gemm": (c_int, [c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int64, c_int32,
+                        c_int32, c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p]),
+    "qi_norm_mod": (c_int, [c_void_p, c_int64, c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p,
+                            c_int64, c_int64, c_float, c_int32, c_int32, c_void_p, c_void_p]),
+    "qi_cast": (c_int, [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p]),
     "qi_kernel_timing": (c_int, [c_int]),
     "qi_kernel_timing_read": (c_int, [POINTER(c_double), POINTER(c_int64)]),
     "qi_kernel_timing_read_each": (c_int, [POINTER(c_float), c_int64, POINTER(c_int64)]),
@@ -336,6 +341,23 @@ def qi_linear_small(x, n_vec: int, I: int, w, O: int, silu_in: bool, y, stream=N
 
 def qi_cast_bf16(x, y, n: int, stream=None) -> int:
     return lib().qi_cast_bf16(_p(x), _p(y), n, _p(stream))
+
+
+def qi_gemm(x, ldx: int, w, bias, out, ldo: int, M: int, N: int, K: int, dtype: int, epilogue: int, gate=None,
+            row0: int = 0, P: int = 0, tile_n: int = 0, range_flags=None, stream=None) -> int:
+    return lib().qi_gemm(_p(x), ldx, _p(w), _p(bias), _p(out), ldo, M, N, K, dtype, epilogue, _p(gate), row0, P,
+                         tile_n, _p(range_flags), _p(stream))
+
+
+def qi_norm_mod(x, ldx: int, out, ldo: int, M: int, D: int, w=None, scale=None, shift=None, row0: int = 0,
+                P: int = 0, eps: float = 1e-6, center: int = 0, out_dtype: int = QI_BF16, range_flags=None,
+                stream=None) -> int:
+    return lib().qi_norm_mod(_p(x), ldx, _p(out), ldo, M, D, _p(w), _p(scale), _p(shift), row0, P, eps, center,
+                             out_dtype, _p(range_flags), _p(stream))
+
+
+def qi_cast(x, y, n: int, dtype: int, range_flags=None, stream=None) -> int:
+    return lib().qi_cast(_p(x), _p(y), n, dtype, _p(range_flags), _p(stream))
 
 
 def qi_kernel_timing(enable: bool) -> int:

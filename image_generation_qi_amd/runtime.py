@@ -14,6 +14,12 @@ from . import qi as Q
 
 TORCH_DTYPE = {Q.QI_BF16: torch.bfloat16, Q.QI_F32: torch.float32, Q.QI_F16: torch.float16}
 
+# 16-bit activation type of the composed layer paths (DiT, TextProjection, V1Block): fp16 rounds
+# each activation to 11 bits instead of bf16's 8 at the same matrix-core rate, which keeps a whole
+# layer's residual increment within the bf16 bar; the model's bf16 weights convert to it exactly
+# (magnitudes 2^-17 .. 65504).  Values it cannot hold raise the range flags.
+ACT = torch.float16
+
 
 def stream_handle(device=None) -> int:
     return torch.cuda.current_stream(device).cuda_stream
@@ -58,7 +64,7 @@ class KVCache:
                 for p in range(64)]
 
     def __init__(self, n_layers: int, n_head: int, p_cap: int, io_dtype: int = Q.QI_BF16, device="cuda"):
-        self.dtype = Q.QI_F16 if io_dtype == Q.QI_BF16 else Q.QI_F32
+        self.dtype = Q.QI_F32 if io_dtype == Q.QI_F32 else Q.QI_F16
         td = TORCH_DTYPE[self.dtype]
         rows = (p_cap + 63) // 64 * 64 if self.dtype == Q.QI_F16 else p_cap
         self.rows = max(rows, 64 if self.dtype == Q.QI_F16 else 1)
@@ -90,7 +96,8 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 
 
 class RangeError(RuntimeError):
-    """A q, k or v value did not fit the fp16 operands of the bf16 attention path."""
+    """A value did not fit fp16: a q, k or v operand of the attention's matrix cores, or an fp16
+    activation of the layer chain."""
 
 
 class Attention:
@@ -116,8 +123,9 @@ class Attention:
         """Raise RangeError if a call since the last check met a value that does not fit fp16."""
         v = self.range_flags()
         if v:
-            names = [n for b, n in ((Q.QI_RANGE_Q, "q"), (Q.QI_RANGE_K, "k"), (Q.QI_RANGE_V, "v")) if v & b]
-            raise RangeError(f"values of {', '.join(names)} outside the fp16 range of the attention operands")
+            names = [n for b, n in ((Q.QI_RANGE_Q, "q"), (Q.QI_RANGE_K, "k"), (Q.QI_RANGE_V, "v"),
+                                    (Q.QI_RANGE_OUT, "layer outputs")) if v & b]
+            raise RangeError(f"values of {', '.join(names)} outside the fp16 range")
 
     def _stride(self, t: torch.Tensor) -> int:
         assert t.dim() == 3 and t.shape[1] == self.H and t.shape[2] == 128 and t.stride(2) == 1 and t.stride(1) == 128
@@ -173,18 +181,25 @@ def euler_step(x: torch.Tensor, v: torch.Tensor, sigma_k: float, sigma_k1: float
     return x
 
 
+def code_of(t: torch.Tensor) -> int:
+    """qi_dtype of a tensor's element type."""
+    return {torch.bfloat16: Q.QI_BF16, torch.float16: Q.QI_F16, torch.float32: Q.QI_F32}[t.dtype]
+
+
 def rope3d_apply(x: torch.Tensor, cos, sin, rms_w=None, eps: float = 1e-6):
     assert x.dim() == 3 and x.shape[2] == 128 and x.stride(2) == 1 and x.stride(1) == 128
-    dt = Q.QI_BF16 if x.dtype == torch.bfloat16 else Q.QI_F32
+    dt = code_of(x)
     Q.check(Q.qi_rope3d_apply(x, dt, x.shape[0], x.shape[1], x.stride(0), cos, sin, rms_w, eps,
                               stream_handle(x.device)), "qi_rope3d_apply")
     return x
 
 
 def from_bits(bits: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
-    """Device tensor holding exactly the given stored values (bf16 bit patterns or fp32)."""
+    """Device tensor holding exactly the given stored values (bf16 or fp16 bit patterns, or fp32)."""
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+    if dtype == "f16":
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.float16).to(device)
     return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.float32)).to(device)
 
 
@@ -211,6 +226,15 @@ class LayerWeights:
         self.D = self.w_out.shape[0]
         self.F = w_gate.shape[0]
 
+    def as_dtype(self, dtype) -> "LayerWeights":
+        """The same layer with its Linear weights converted to `dtype` (fp16 for the fp16 layer
+        chain: exact for the bf16 weights of magnitude 2^-17 .. 65504)."""
+        W = LayerWeights.__new__(LayerWeights)
+        W.norm1, W.norm2, W.q_norm, W.k_norm = self.norm1, self.norm2, self.q_norm, self.k_norm
+        W.w_qkv, W.w_out, W.w_down, W.w_gu = (t.to(dtype) for t in (self.w_qkv, self.w_out, self.w_down, self.w_gu))
+        W.D, W.F = self.D, self.F
+        return W
+
 
 class SharedWeights:
     """Device weights shared by all layers: timestep MLP, shared modulation, head, img_in."""
@@ -224,59 +248,73 @@ class SharedWeights:
 
 
 def gemm(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor, epilogue: int, gate=None, row0: int = 0, P: int = 0,
-         tile_n: int = 0, bias=None):
+         tile_n: int = 0, bias=None, flags=None):
+    """y = x W^T with an epilogue; x and w both bf16 (bf16 matrix cores, bf16 16-bit outputs) or
+    both fp16 (fp16 matrix cores and outputs)."""
     M, K = x.shape
     N = w.shape[0]
-    assert x.dtype == torch.bfloat16 and w.dtype == torch.bfloat16 and w.shape[1] == K and x.stride(1) == 1
+    assert x.dtype in (torch.bfloat16, torch.float16) and w.dtype == x.dtype and w.shape[1] == K and x.stride(1) == 1
     assert out.stride(1) == 1 and out.shape[0] == M
     if bias is not None:
-        assert tile_n == 0 and bias.dtype == torch.float32 and bias.is_contiguous() and bias.numel() == N
-        Q.check(Q.qi_gemm_bf16_bias(x, x.stride(0), w, bias, out, out.stride(0), M, N, K, epilogue, gate, row0, P,
-                                    stream_handle(x.device)), "qi_gemm_bf16_bias")
-        return out
-    Q.check(Q.qi_gemm_bf16_ex(x, x.stride(0), w, out, out.stride(0), M, N, K, epilogue, gate, row0, P, tile_n,
-                              stream_handle(x.device)), "qi_gemm_bf16_ex")
+        assert bias.dtype == torch.float32 and bias.is_contiguous() and bias.numel() == N
+    Q.check(Q.qi_gemm(x, x.stride(0), w, bias, out, out.stride(0), M, N, K, code_of(x), epilogue, gate, row0, P,
+                      tile_n, flags, stream_handle(x.device)), "qi_gemm")
     return out
 
 
 def norm_mod(x: torch.Tensor, out: torch.Tensor, w=None, scale=None, shift=None, row0: int = 0, P: int = 0,
-             eps: float = 1e-6):
+             eps: float = 1e-6, flags=None):
+    """ZeroCenterRMSNorm + modulation of fp32 rows into bf16 or fp16 rows (out's type)."""
     M, D = x.shape
-    assert x.dtype == torch.float32 and out.dtype == torch.bfloat16 and x.stride(1) == 1 and out.stride(1) == 1
-    Q.check(Q.qi_zc_rmsnorm_mod(x, x.stride(0), out, out.stride(0), M, D, w, scale, shift, row0, P, eps,
-                                stream_handle(x.device)), "qi_zc_rmsnorm_mod")
+    assert x.dtype == torch.float32 and out.dtype in (torch.bfloat16, torch.float16)
+    assert x.stride(1) == 1 and out.stride(1) == 1
+    Q.check(Q.qi_norm_mod(x, x.stride(0), out, out.stride(0), M, D, w, scale, shift, row0, P, eps, 0, code_of(out),
+                          flags, stream_handle(x.device)), "qi_norm_mod")
     return out
 
 
 def layernorm_mod(x: torch.Tensor, out: torch.Tensor, scale=None, shift=None, row0: int = 0, P: int = 0,
-                  eps: float = 1e-6):
+                  eps: float = 1e-6, flags=None):
+    """LayerNorm (no affine) + modulation of fp32 rows into bf16 or fp16 rows (out's type)."""
     M, D = x.shape
-    assert x.dtype == torch.float32 and out.dtype == torch.bfloat16 and x.stride(1) == 1 and out.stride(1) == 1
-    Q.check(Q.qi_layernorm_mod(x, x.stride(0), out, out.stride(0), M, D, scale, shift, row0, P, eps,
-                               stream_handle(x.device)), "qi_layernorm_mod")
+    assert x.dtype == torch.float32 and out.dtype in (torch.bfloat16, torch.float16)
+    assert x.stride(1) == 1 and out.stride(1) == 1
+    Q.check(Q.qi_norm_mod(x, x.stride(0), out, out.stride(0), M, D, None, scale, shift, row0, P, eps, 1,
+                          code_of(out), flags, stream_handle(x.device)), "qi_norm_mod")
     return out
+
+
+def cast(x: torch.Tensor, y: torch.Tensor, flags=None):
+    """fp32 -> bf16 or fp16 (y's type), nearest even."""
+    assert x.dtype == torch.float32 and x.is_contiguous() and y.is_contiguous() and y.numel() >= x.numel()
+    Q.check(Q.qi_cast(x, y, x.numel(), code_of(y), flags, stream_handle(x.device)), "qi_cast")
+    return y
 
 
 class TextProjection:
     """The context path of [1B] sections 1-3: ZeroCenterRMSNorm (weights stored as scale - 1),
     Linear, GELU(tanh), Linear; vision-language context rows (fp32 [n][D]) in, the DiT's text
     rows (fp32 [n][D]) out.  Three library calls: the norm, a GEMM with the GELU epilogue, a GEMM
-    with the fp32 store."""
+    with the fp32 store.  The normed rows, the GELU output and the weights are fp16 (the weights
+    converted once)."""
 
     def __init__(self, norm_w: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, eps: float = 1e-6):
-        self.norm_w, self.w1, self.w2, self.eps = norm_w.contiguous(), w1.contiguous(), w2.contiguous(), eps
+        self.act = act_dtype = ACT
+        self.norm_w, self.eps = norm_w.contiguous(), eps
+        self.w1, self.w2 = w1.to(act_dtype).contiguous(), w2.to(act_dtype).contiguous()
         self.D = self.w1.shape[1]
         assert self.w1.shape == (self.D, self.D) and self.w2.shape == (self.D, self.D)
+        self.flags = torch.zeros(1, dtype=torch.int32, device=w1.device)
 
     def __call__(self, x_ctx: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
         n, D = x_ctx.shape
         assert D == self.D and x_ctx.dtype == torch.float32
         dev = x_ctx.device
-        h = torch.empty((n, D), dtype=torch.bfloat16, device=dev)
-        a = torch.empty((n, D), dtype=torch.bfloat16, device=dev)
+        h = torch.empty((n, D), dtype=self.act, device=dev)
+        a = torch.empty((n, D), dtype=self.act, device=dev)
         out = torch.empty((n, D), dtype=torch.float32, device=dev) if out is None else out
-        norm_mod(x_ctx, h, self.norm_w, None, None, 0, 0, self.eps)
-        gemm(h, self.w1, a, Q.QI_EPI_GELU)
+        norm_mod(x_ctx, h, self.norm_w, None, None, 0, 0, self.eps, flags=self.flags)
+        gemm(h, self.w1, a, Q.QI_EPI_GELU, flags=self.flags)
         gemm(a, self.w2, out, Q.QI_EPI_STORE_F32)
         return out
 
@@ -301,14 +339,21 @@ class DiT:
     buffers and issues the calls in order on the current stream."""
 
     def __init__(self, layout: Layout, shared: SharedWeights, layers, device="cuda", eps: float = 1e-6):
-        self.L, self.sw, self.layers, self.device, self.eps = layout, shared, list(layers), device, eps
+        """The layer chain's 16-bit activations (normed rows, QKV, attention output, SwiGLU output,
+        the latents into img_in) and the projection weights are fp16 (the weights converted once
+        from the model's bf16)."""
+        self.L, self.sw, self.device, self.eps, self.act = layout, shared, device, eps, ACT
+        act_dtype = ACT
+        self.layers = [W.as_dtype(act_dtype) for W in layers]
+        self.w_in, self.w_head = shared.w_in.to(act_dtype), shared.w_head.to(act_dtype)
         self.D = shared.D
         self.H = self.D // 128
         self.F = self.layers[0].F if self.layers else 0
-        self.attn = Attention(layout, self.H, Q.QI_BF16, device)
-        self.cache = KVCache(len(self.layers), self.H, layout.P, Q.QI_BF16, device)
+        self.attn = Attention(layout, self.H, code_of(torch.empty(0, dtype=act_dtype)), device)
+        self.cache = KVCache(len(self.layers), self.H, layout.P, self.attn.dtype, device)
         S, D = layout.S, self.D
-        bf, f32 = torch.bfloat16, torch.float32
+        bf, f32 = act_dtype, torch.float32
+        self.flags = self.attn.flags                                    # QI_RANGE_* of every call
         self.x = torch.empty((S, D), dtype=f32, device=device)          # residual stream
         self.h = torch.empty((S, D), dtype=bf, device=device)           # normed + modulated
         self.qkv = torch.empty((S, 3 * D), dtype=bf, device=device)
@@ -342,9 +387,9 @@ class DiT:
         W, D, F, eps = self.layers[li], self.D, self.F, self.eps
         r0, n, P = rows.start, rows.stop - rows.start, self.L.P
         x, h, qkv, o, a = self.x[rows], self.h[:n], self.qkv[:n], self.o[:n], self.a[:n]
-        m = self.mods
-        norm_mod(x, h, W.norm1, m[1], m[0], r0, P, eps)
-        gemm(h, W.w_qkv, qkv, Q.QI_EPI_STORE)
+        m, fl = self.mods, self.flags
+        norm_mod(x, h, W.norm1, m[1], m[0], r0, P, eps, flags=fl)
+        gemm(h, W.w_qkv, qkv, Q.QI_EPI_STORE, flags=fl)
         q = qkv[:, :D].view(n, self.H, 128)
         k = qkv[:, D:2 * D].view(n, self.H, 128)
         v = qkv[:, 2 * D:].view(n, self.H, 128)
@@ -353,16 +398,16 @@ class DiT:
         else:
             self.attn.full(q, k, v, W.q_norm, W.k_norm, eps, cache=self.cache, layer=li, out=o)
         gemm(o.view(n, D), W.w_out, x, Q.QI_EPI_GATED_RESIDUAL, m[2], r0, P)
-        norm_mod(x, h, W.norm2, m[4], m[3], r0, P, eps)
-        gemm(h, W.w_gu, a, Q.QI_EPI_SWIGLU)
+        norm_mod(x, h, W.norm2, m[4], m[3], r0, P, eps, flags=fl)
+        gemm(h, W.w_gu, a, Q.QI_EPI_SWIGLU, flags=fl)
         gemm(a, W.w_down, x, Q.QI_EPI_GATED_RESIDUAL, m[5], r0, P)
 
     # -- inputs, head, Euler -----------------------------------------------------------------
     def embed(self, lat: torch.Tensor, out: torch.Tensor):
-        """img_in: fp32 latents [n][64] -> bf16 -> fp32 tokens [n][D]."""
+        """img_in: fp32 latents [n][64] -> the activation type -> fp32 tokens [n][D]."""
         n = lat.shape[0]
-        Q.check(Q.qi_cast_bf16(lat, self.lat_bf, lat.numel(), stream_handle(self.device)), "qi_cast_bf16")
-        gemm(self.lat_bf[:n], self.sw.w_in, out, Q.QI_EPI_STORE_F32)
+        cast(lat, self.lat_bf, self.flags)
+        gemm(self.lat_bf[:n], self.w_in, out, Q.QI_EPI_STORE_F32)
 
     def set_prefix(self, x_text: torch.Tensor, lat_ref: Optional[torch.Tensor]):
         """Fill the prefix rows of the residual stream in segment order: text rows copied from
@@ -382,9 +427,13 @@ class DiT:
         """Scale-only final norm, the velocity projection, and the Euler update of lat (in place)."""
         P, T = self.L.P, self.L.T
         h = self.h[:T]
-        norm_mod(self.x[P:], h, None, self.hscale, None, P, P, self.eps)
-        gemm(h, self.sw.w_head, self.vel, Q.QI_EPI_STORE_F32)
+        norm_mod(self.x[P:], h, None, self.hscale, None, P, P, self.eps, flags=self.flags)
+        gemm(h, self.w_head, self.vel, Q.QI_EPI_STORE_F32)
         euler_step(lat, self.vel, sigma_k, sigma_k1)
+
+    def check_range(self):
+        """Raise RangeError if any call since the last check met a value that fp16 cannot hold."""
+        self.attn.check_range()
 
     def step(self, k: int, lat: torch.Tensor, sig, x_text=None, lat_ref=None):
         """Euler step k (0-based) of the loop: step 0 runs the whole sequence and fills the caches."""
@@ -439,10 +488,13 @@ class V1Block:
     gate2 * y)."""
 
     def __init__(self, W: V1BlockWeights, layout: Layout, n_head: int, device="cuda", eps: float = 1e-6):
+        """The activations and the GEMM weights (converted once) are fp16."""
         assert layout.attention == Q.QI_ATTN_FULL
         assert W.D == n_head * 128
-        self.W, self.L, self.H, self.eps, self.device = W, layout, n_head, eps, device
-        self.att = Attention(layout, n_head, Q.QI_BF16, device)
+        act_dtype = ACT
+        self.W, self.L, self.H, self.eps, self.device, self.act = W, layout, n_head, eps, device, act_dtype
+        self.att = Attention(layout, n_head, code_of(torch.empty(0, dtype=act_dtype)), device)
+        self.w = {name: W[name + "_w"].to(act_dtype) for name in V1_LINEARS if not name.endswith("_mod")}
 
     def __call__(self, x_txt: torch.Tensor, x_img: torch.Tensor, cond: torch.Tensor, n_noise: Optional[int] = None):
         """x_txt fp32 [Lt][D] and x_img fp32 [Li][D] (updated in place and returned); cond fp32
@@ -464,22 +516,57 @@ class V1Block:
                 linear_small(cond, W[name + "_mod_w"][i * D:(i + 1) * D], m[i], True,
                              W[name + "_mod_b"][i * D:(i + 1) * D])
             mods[name] = m
-        h = torch.empty((S, D), dtype=torch.bfloat16, device=dev)
-        qkv = torch.empty((S, 3, H, 128), dtype=torch.bfloat16, device=dev)
+        h = torch.empty((S, D), dtype=self.act, device=dev)
+        qkv = torch.empty((S, 3, H, 128), dtype=self.act, device=dev)
+        fl, w = self.att.flags, self.w
         for name, x, r0, n, P, nq, nk in streams:
             m = mods[name]
-            layernorm_mod(x, h[r0:r0 + n], m[1], m[0], 0, P, eps)
-            gemm(h[r0:r0 + n], W[name + "_qkv_w"], qkv[r0:r0 + n].view(n, 3 * D), Q.QI_EPI_STORE,
-                 bias=W[name + "_qkv_b"])
+            layernorm_mod(x, h[r0:r0 + n], m[1], m[0], 0, P, eps, flags=fl)
+            gemm(h[r0:r0 + n], w[name + "_qkv"], qkv[r0:r0 + n].view(n, 3 * D), Q.QI_EPI_STORE,
+                 bias=W[name + "_qkv_b"], flags=fl)
             rope3d_apply(qkv[r0:r0 + n, 0], None, None, W[nq], eps)
             rope3d_apply(qkv[r0:r0 + n, 1], None, None, W[nk], eps)
         o = self.att.full(qkv[:, 0], qkv[:, 1], qkv[:, 2])
-        a = torch.empty((max(Lt, Li), W.F), dtype=torch.bfloat16, device=dev)
+        a = torch.empty((max(Lt, Li), W.F), dtype=self.act, device=dev)
         for name, x, r0, n, P, nq, nk in streams:
             m = mods[name]
-            gemm(o[r0:r0 + n].view(n, D), W[name + "_out_w"], x, Q.QI_EPI_GATED_RESIDUAL_LINEAR, m[2], 0, P,
+            gemm(o[r0:r0 + n].view(n, D), w[name + "_out"], x, Q.QI_EPI_GATED_RESIDUAL_LINEAR, m[2], 0, P,
                  bias=W[name + "_out_b"])
-            layernorm_mod(x, h[r0:r0 + n], m[4], m[3], 0, P, eps)
-            gemm(h[r0:r0 + n], W[name + "_fc1_w"], a[:n], Q.QI_EPI_GELU, bias=W[name + "_fc1_b"])
-            gemm(a[:n], W[name + "_fc2_w"], x, Q.QI_EPI_GATED_RESIDUAL_LINEAR, m[5], 0, P, bias=W[name + "_fc2_b"])
+            layernorm_mod(x, h[r0:r0 + n], m[4], m[3], 0, P, eps, flags=fl)
+            gemm(h[r0:r0 + n], w[name + "_fc1"], a[:n], Q.QI_EPI_GELU, bias=W[name + "_fc1_b"], flags=fl)
+            gemm(a[:n], w[name + "_fc2"], x, Q.QI_EPI_GATED_RESIDUAL_LINEAR, m[5], 0, P, bias=W[name + "_fc2_b"])
         return x_txt, x_img
+
+
+class V1Head:
+    """The v1 / Edit model's exit ("QwenImageTransformer2DModel source reading (Qwen-Image-Edit)",
+    section 5.3) on the image stream: norm_out (SiLU(temb) through one Linear with bias giving
+    scale then shift; LayerNorm without affine, times (1 + scale), plus shift) and proj_out
+    (Linear D -> 64 with bias).  Two conditioning linears, the norm into fp16 rows and one fp16
+    GEMM with the bias and the fp32 store."""
+
+    def __init__(self, norm_out_w: torch.Tensor, norm_out_b: torch.Tensor, proj_out_w: torch.Tensor,
+                 proj_out_b: torch.Tensor, eps: float = 1e-6):
+        D = proj_out_w.shape[1]
+        assert norm_out_w.shape == (2 * D, D) and norm_out_w.dtype == torch.bfloat16
+        self.D, self.eps = D, eps
+        self.w_scale, self.w_shift = norm_out_w[:D].contiguous(), norm_out_w[D:].contiguous()
+        self.b_scale, self.b_shift = norm_out_b[:D].contiguous(), norm_out_b[D:].contiguous()
+        self.w_proj = proj_out_w.to(ACT).contiguous()
+        self.b_proj = proj_out_b.contiguous()
+        self.flags = torch.zeros(1, dtype=torch.int32, device=proj_out_w.device)
+
+    def __call__(self, x_img: torch.Tensor, temb: torch.Tensor) -> torch.Tensor:
+        """x_img fp32 [Li][D], temb fp32 [D] -> fp32 [Li][64]."""
+        Li, D = x_img.shape
+        dev = x_img.device
+        cond = temb.reshape(1, D).expand(2, D).contiguous()      # the same vector for both row sets
+        scale = torch.empty((2, D), dtype=torch.float32, device=dev)
+        shift = torch.empty((2, D), dtype=torch.float32, device=dev)
+        linear_small(cond, self.w_scale, scale, True, self.b_scale)
+        linear_small(cond, self.w_shift, shift, True, self.b_shift)
+        h = torch.empty((Li, D), dtype=ACT, device=dev)
+        layernorm_mod(x_img, h, scale, shift, 0, 0, self.eps, flags=self.flags)
+        out = torch.empty((Li, self.w_proj.shape[0]), dtype=torch.float32, device=dev)
+        gemm(h, self.w_proj, out, Q.QI_EPI_STORE_F32, bias=self.b_proj)
+        return out

@@ -26,7 +26,7 @@
  *     so a fused [tokens, 3, heads, 128] QKV buffer can be passed with three base pointers.
  *     Device pointers must be 16-byte aligned and tok_stride a multiple of 8 elements.
  *   - Attention outputs are dense [n_tok][n_head*128] in the I/O dtype.
- *   - Floating point: bf16 inputs are upcast exactly; normalisation and rotation run in fp32;
+ *   - Floating point: bf16 (and fp16) inputs are upcast exactly; normalisation and rotation run in fp32;
  *     the attention contractions use fp16 MFMA operands (rotated Q and K, softmax
  *     probabilities, V) with fp32 accumulation and an fp32 online softmax; outputs are
  *     rounded to bf16 (nearest even).  Query tiles whose keys are split into chunks (see
@@ -131,9 +131,12 @@ typedef struct {
 #define QI_RANGE_Q 1u
 #define QI_RANGE_K 2u
 #define QI_RANGE_V 4u
+#define QI_RANGE_OUT 8u   /* an fp16 output of qi_gemm, qi_norm_mod or qi_cast did not fit */
 
 /* Attention operands.  q, k, v: device, token-major with `tok_stride`; o: device, dense
- * [n_tok][n_head*128].  dtype: QI_BF16 or QI_F32 for all four.  lse: NULL, or device fp32
+ * [n_tok][n_head*128].  dtype: QI_BF16, QI_F16 or QI_F32 for all four (QI_F16 runs the bf16
+ * path's kernels with fp16 loads and stores: the operands are already fp16, so only the rotated
+ * K can leave the fp16 range; it uses the same fp16 cache).  lse: NULL, or device fp32
  * [n_head][n_tok] that receives each query row's log-sum-exp, ln(sum_k exp(scale * q.k)) over its
  * visible keys (the softmax denominator; what a merge of attention over split key ranges needs).
  * range_flags: NULL, or a device uint32 (4-byte aligned) into which the call ORs QI_RANGE_* bits
@@ -173,7 +176,8 @@ typedef struct {
 const char* qi_status_str(int status);
 
 /* Library ABI version (increments on any signature or struct change; 2 added qi_qkv.lse, 3 the
- * range flags and int32_t dtype fields, 4 the allocation-free cached step). */
+ * range flags and int32_t dtype fields, 4 the allocation-free cached step, 5 fp16 activations
+ * (QI_F16 attention I/O, qi_gemm, qi_norm_mod, qi_cast)). */
 int qi_version(void);
 
 /* Token counts of a layout: S = all, P = prefix (all but the last segment), T = target.
@@ -229,8 +233,8 @@ int64_t qi_kvcache_bytes(int32_t cache_dtype, int32_t n_layers, int32_t n_head, 
 
 /* In-place QK preparation of one tensor: optional per-head RMSNorm (rms_w != NULL), then the
  * 3D rotation (cos_t/sin_t != NULL; at least one of the two must be given) of x, a device
- * token-major [n_tok][tok_stride] tensor of `dtype` (QI_BF16 or QI_F32) holding n_head heads
- * of 128.  Tables as in qi_qkprep.  bf16 results are rounded to nearest even.
+ * token-major [n_tok][tok_stride] tensor of `dtype` (QI_BF16, QI_F16 or QI_F32) holding n_head
+ * heads of 128.  Tables as in qi_qkprep.  16-bit results are rounded to nearest even.
  * ([3A] section 1; [EDIT] section 6.) */
 int qi_rope3d_apply(void* x, int32_t dtype, int64_t n_tok, int32_t n_head, int64_t tok_stride,
                     const float* cos_t, const float* sin_t, const float* rms_w, float eps,
@@ -380,6 +384,31 @@ int qi_linear_small_bias(const float* x, int32_t n_vec, int32_t I, const void* w
  * [n], y device bf16 [n].  Errors: QI_ERR_ARG (NULL pointer), QI_ERR_SHAPE (n < 0), QI_ERR_ALIGN
  * (x not 4-byte or y not 2-byte aligned), QI_ERR_HIP (launch). */
 int qi_cast_bf16(const float* x, void* y, int64_t n, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * The same layer pieces for either 16-bit activation type.  dtype QI_BF16 is the bf16 form of
+ * the calls above; QI_F16 keeps the layer chain's 16-bit activations (normed rows, projections,
+ * attention output, SwiGLU / GELU output) and the weights as fp16, which rounds each of them to
+ * 11 bits instead of 8 (the model's bf16 weights convert exactly when 2^-17 <= |w| < 65520) at the
+ * same matrix-core rate; fp16 outputs of magnitude 65520 or more (or not finite) set QI_RANGE_OUT
+ * in *range_flags (device uint32, nullable; never cleared by the library).
+ * ------------------------------------------------------------------------------------------ */
+
+/* qi_gemm_bf16_ex / qi_gemm_bf16_bias with x, w and the 16-bit outputs (QI_EPI_STORE,
+ * QI_EPI_SWIGLU, QI_EPI_GELU) of `dtype` (QI_BF16 or QI_F16, QI_ERR_DTYPE otherwise); bias
+ * nullable; tile_n as qi_gemm_bf16_ex.  Other arguments and errors as qi_gemm_bf16. */
+int qi_gemm(const void* x, int64_t ldx, const void* w, const float* bias, void* out, int64_t ldo, int64_t M,
+            int64_t N, int64_t K, int32_t dtype, int32_t epilogue, const float* gate, int64_t row0, int64_t P,
+            int32_t tile_n, uint32_t* range_flags, void* stream);
+
+/* qi_zc_rmsnorm_mod (center = 0; w nullable) or qi_layernorm_mod (center = 1; w must be NULL)
+ * with an output of out_dtype (QI_BF16 or QI_F16).  Other arguments and errors as those. */
+int qi_norm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64_t M, int32_t D, const float* w,
+                const float* scale, const float* shift, int64_t row0, int64_t P, float eps, int32_t center,
+                int32_t out_dtype, uint32_t* range_flags, void* stream);
+
+/* fp32 -> dtype (QI_BF16 or QI_F16, nearest even) of n elements.  Errors as qi_cast_bf16. */
+int qi_cast(const float* x, void* y, int64_t n, int32_t dtype, uint32_t* range_flags, void* stream);
 
 /* HIP error code of the last launch of this library that failed in the calling thread (the
  * cause behind a QI_ERR_HIP status; 0 if none), and its name (a static string). */

@@ -470,7 +470,7 @@ def linear_bias(x, w, b):
 
 
 def v1_block(x_txt, x_img, temb, B, cos_t, sin_t, temb0=None, n_noise: Optional[int] = None,
-             eps: float = 1e-6):
+             eps: float = 1e-6, rows_txt=None, rows_img=None):
     """One dual-stream block of the v1 / Edit model ([EDIT] section 5.2 for the block's forward,
     section 6 for the attention processor), both streams in fp64.
 
@@ -490,7 +490,9 @@ def v1_block(x_txt, x_img, temb, B, cos_t, sin_t, temb0=None, n_noise: Optional[
         h2 = LayerNorm(x) (1 + scale2) + shift2
         x += gate2 * (GELU_tanh(h2 W1^T + b1) W2^T + b2)        (img_mlp / txt_mlp, D -> 4 D -> D)
     cos_t / sin_t: rotation tables of the joint sequence [Lt + Li, 64] (text positions first).
-    B: dict of the block's weights (keys as read below).  Returns (x_txt, x_img)."""
+    B: dict of the block's weights (keys as read below).  Returns (x_txt, x_img).  With rows_txt
+    and rows_img (index arrays), only those output rows are formed (the keys and values still
+    come from every row): returns (x_txt[rows_txt], x_img[rows_img]) of the block's output."""
     xt = np.asarray(x_txt, np.float64)
     xi = np.asarray(x_img, np.float64)
     Lt, D = xt.shape
@@ -520,7 +522,16 @@ def v1_block(x_txt, x_img, temb, B, cos_t, sin_t, temb0=None, n_noise: Optional[
     q = rotate(np.concatenate([qt, qi]), cos_t, sin_t)
     k = rotate(np.concatenate([kt, ki]), cos_t, sin_t)
     v = np.concatenate([vt, vi])
-    o = attention(q, k, v).reshape(Lt + Li, D)
+    if rows_txt is not None:
+        rt_ = np.asarray(rows_txt, np.int64)
+        ri_ = np.asarray(rows_img, np.int64)
+        q = q[np.concatenate([rt_, Lt + ri_])]
+        xt, xi = xt[rt_], xi[ri_]
+        pick = lambda a, r: a[r] if np.ndim(a) == 2 else a
+        sc2t, sh2t, g1t, g2t = (pick(a, rt_) for a in (sc2t, sh2t, g1t, g2t))
+        sc2i, sh2i, g1i, g2i = (pick(a, ri_) for a in (sc2i, sh2i, g1i, g2i))
+        Lt = len(rt_)
+    o = attention(q, k, v).reshape(q.shape[0], D)
     xt = xt + g1t * linear_bias(o[:Lt], B["txt_out_w"], B["txt_out_b"])
     xi = xi + g1i * linear_bias(o[Lt:], B["img_out_w"], B["img_out_b"])
 
@@ -530,6 +541,28 @@ def v1_block(x_txt, x_img, temb, B, cos_t, sin_t, temb0=None, n_noise: Optional[
         return x + g * linear_bias(a, B[pre + "_fc2_w"], B[pre + "_fc2_b"])
 
     return mlp(xt, sc2t, sh2t, g2t, "txt"), mlp(xi, sc2i, sh2i, g2i, "img")
+
+
+def v1_output_head(x_img, temb, Hd, eps: float = 1e-6):
+    """The v1 / Edit model's exit ([EDIT] section 5.3): norm_out, an AdaLN with a single Linear
+    on SiLU(temb) giving 2 D values cut into (scale, shift) in that order, applied as
+    LayerNorm(x) (1 + scale) + shift (no affine, eps 1e-6); then proj_out, a Linear(D -> 64)
+    with bias, on the image stream.  Hd: norm_out_w [2D][D], norm_out_b [2D], proj_out_w [64][D],
+    proj_out_b [64]."""
+    xi = np.asarray(x_img, np.float64)
+    D = xi.shape[1]
+    emb = linear_bias(silu(np.atleast_2d(temb)), Hd["norm_out_w"], Hd["norm_out_b"])[0]
+    scale, shift = emb[:D], emb[D:]
+    return linear_bias(layer_norm(xi, eps) * (1.0 + scale) + shift, Hd["proj_out_w"], Hd["proj_out_b"])
+
+
+def v1_forward(x_txt, x_img, temb, blocks, Hd, cos_t, sin_t, eps: float = 1e-6):
+    """Dual-stream blocks in sequence, then the exit on the image stream ([EDIT] section 5.3: only
+    the image part leaves through norm_out and proj_out).  Returns [Li, 64]."""
+    xt, xi = x_txt, x_img
+    for B in blocks:
+        xt, xi = v1_block(xt, xi, temb, B, cos_t, sin_t, eps=eps)
+    return v1_output_head(xi, temb, Hd, eps)
 
 
 def velocity_head(x_t, temb, w_scale, w_head, eps: float = 1e-6):

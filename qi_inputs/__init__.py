@@ -161,6 +161,9 @@ def stored(x64: np.ndarray, dtype: str) -> Stored:
     if dtype == "f32":
         f = x64.astype(np.float32)
         return Stored(f, f.astype(np.float64), dtype)
+    if dtype == "f16":   # by way of fp32, nearest even (values beyond fp16's range become infinite)
+        h = x64.astype(np.float32).astype(np.float16)
+        return Stored(h.view(np.uint16), h.astype(np.float64), dtype)
     raise ValueError(dtype)
 
 
@@ -267,6 +270,18 @@ def v1_block_weights(cfg_id: int, D: int, F: int, layer: int = 0) -> dict:
                      ("norm_added_k", W_V1_AKN)):
         out[key] = f32_vector(cfg_id, idx, (128,), layer, 1.0, 0.02)
     return out
+
+
+W_V1_NOUT, W_V1_NOUTB, W_V1_POUT, W_V1_POUTB = range(61, 65)
+
+
+def v1_head_weights(cfg_id: int, D: int, out_ch: int = 64) -> dict:
+    """Random-init exit of the v1 model: norm_out's Linear [2D][D] and proj_out [out_ch][D], both
+    N(0, 1/D) in bf16 with fp32 biases N(0, 0.1^2)."""
+    return {"norm_out_w": linear_weight(cfg_id, W_V1_NOUT, 2 * D, D),
+            "norm_out_b": f32_vector(cfg_id, W_V1_NOUTB, (2 * D,), 0, 0.0, 0.1),
+            "proj_out_w": linear_weight(cfg_id, W_V1_POUT, out_ch, D),
+            "proj_out_b": f32_vector(cfg_id, W_V1_POUTB, (out_ch,), 0, 0.0, 0.1)}
 
 
 def v1_block_inputs(cfg_id: int, n_txt: int, n_img: int, D: int):

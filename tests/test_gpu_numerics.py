@@ -303,6 +303,43 @@ def test_perturbed_target_rows_match_oracle():
 
 
 # ---------------------------------------------------------------------------------------------
+# fp16 I/O (the layer chain's activation type): the same kernels with fp16 loads and stores
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("segs,heads,qk", [((qin.text(77), qin.image(13, 9, 1), qin.image(15, 17, 0)), 3, True),
+                                           ((qin.text(200), qin.image(12, 16, 1), qin.image(16, 20, 2),
+                                             qin.image(17, 19, 0)), 2, False)])
+def test_f16_io_step1_and_cached(segs, heads, qk):
+    wl = qin.small_workload("f16_io", segs, n_head=heads, dtype="f16", qk_rmsnorm=qk)
+    S, P, T = wl.S, wl.P, wl.T
+    say(f"fp16 I/O step 1 + cached step: S={S} heads={heads} qk_norm={qk}")
+    q, k, v = qin.qkv(wl, S)
+    q2, k2, v2 = qin.qkv(wl, S, step=1)
+    qw, kw = qin.qk_norm_weights(wl) if qk else (None, None)
+    qwd = None if qw is None else torch.tensor(qw, dtype=torch.float32, device=DEV)
+    kwd = None if kw is None else torch.tensor(kw, dtype=torch.float32, device=DEV)
+    L = rt.Layout(segs, DEV)
+    att = rt.Attention(L, heads, Q.QI_F16, DEV)
+    cache = rt.KVCache(1, heads, P, Q.QI_F16, DEV)
+    qd, kd, vd = (rt.from_bits(t.bits, "f16", DEV) for t in (q, k, v))
+    o = att.full(qd, kd, vd, qwd, kwd, cache=cache)
+    q2d, k2d, v2d = (rt.from_bits(t.bits, "f16", DEV) for t in (q2, k2, v2))
+    ot = att.cached(q2d[P:], k2d[P:], v2d[P:], cache, 0, qwd, kwd)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float16 and att.range_flags() == 0
+    c, s = O.rope_tables(O.positions(segs))
+    ref, oc = O.step1(q.f64, k.f64, v.f64, segs, c, s, qw, kw)
+    check(to_np(o), ref, "fp16 I/O step 1")
+    ref_t = O.cached_step(q2.f64[P:], k2.f64[P:], v2.f64[P:], oc, c[P:], s[P:], qw, kw)
+    check(to_np(ot), ref_t, "fp16 I/O cached step")
+    # the cached step equals the full recompute on [prefix | new target], bit for bit
+    qn, kn, vn = (torch.cat([a[:P], b[P:]]) for a, b in ((qd, q2d), (kd, k2d), (vd, v2d)))
+    of = att.full(qn, kn, vn, qwd, kwd)
+    torch.cuda.synchronize()
+    assert torch.equal(ot.view(torch.int16), of[P:].view(torch.int16))
+
+
+# ---------------------------------------------------------------------------------------------
 # range flags of the fp16 operands
 # ---------------------------------------------------------------------------------------------
 

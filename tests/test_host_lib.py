@@ -146,6 +146,9 @@ def test_blockmap_bit_exact_full_size(name, tiles):
 
 def test_tile_shape_and_sizes():
     assert Q.qi_attn_tile_shape(Q.QI_BF16) == (256, 64)
+    assert Q.qi_attn_tile_shape(Q.QI_F16) == (256, 64)     # fp16 I/O runs the same kernels
+    for T in (64, 1024, 4096, 5000):
+        assert Q.qi_attn_cached_workspace_bytes(Q.QI_F16, T, 24) == Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, T, 24)
     assert Q.qi_attn_tile_shape(Q.QI_F32) == (1, 64)
     # schedules: (key chunks, whole tiles per XCD run, chunked tiles)
     assert Q.qi_attn_schedule(4096, 24) == (2, 32, 128)     # 384 tiles: 48 per XCD
@@ -207,7 +210,7 @@ def _cached(io, prep, cache, layer=0, P=50, ws=FAKE + 0x8000, wsb=1 << 40):
 
 @pytest.mark.parametrize("case,want", [
     ("null_q", Q.QI_ERR_ARG), ("null_o", Q.QI_ERR_ARG), ("bad_dtype", Q.QI_ERR_DTYPE),
-    ("f16_io", Q.QI_ERR_DTYPE), ("stride_small", Q.QI_ERR_SHAPE), ("zero_tokens", Q.QI_ERR_SHAPE),
+    ("f16_io_f32_cache", Q.QI_ERR_DTYPE), ("stride_small", Q.QI_ERR_SHAPE), ("zero_tokens", Q.QI_ERR_SHAPE),
     ("misaligned", Q.QI_ERR_ALIGN), ("stride_not8", Q.QI_ERR_ALIGN), ("layer_oob", Q.QI_ERR_CAPACITY),
     ("layer_neg", Q.QI_ERR_CAPACITY), ("P_over_cap", Q.QI_ERR_CAPACITY), ("cache_dtype", Q.QI_ERR_DTYPE),
     ("cache_heads", Q.QI_ERR_SHAPE), ("ws_small", Q.QI_ERR_CAPACITY), ("ws_null", Q.QI_ERR_ARG),
@@ -220,7 +223,9 @@ def test_target_cached_rejects(case, want):
     if case == "null_q": io.q = None
     elif case == "null_o": io.o = None
     elif case == "bad_dtype": io.dtype = 7
-    elif case == "f16_io": io.dtype = Q.QI_F16
+    elif case == "f16_io_f32_cache":   # fp16 I/O takes the fp16 cache
+        io.dtype = Q.QI_F16
+        cache.dtype = Q.QI_F32
     elif case == "stride_small": io.tok_stride = 128
     elif case == "zero_tokens": io.n_tok = 0
     elif case == "misaligned": io.k = FAKE + 0x1008
@@ -301,7 +306,7 @@ def test_other_entry_points_reject():
     assert Q.qi_rope3d_apply(FAKE, Q.QI_BF16, 8, 2, 256, None, None, None, 1e-6, None) == Q.QI_ERR_ARG
     assert Q.qi_rope3d_apply(FAKE, Q.QI_BF16, 8, 2, 256, FAKE, None, None, 1e-6, None) == Q.QI_ERR_ARG
     assert Q.qi_rope3d_apply(FAKE + 2, Q.QI_BF16, 8, 2, 256, FAKE, FAKE, None, 1e-6, None) == Q.QI_ERR_ALIGN
-    assert Q.qi_rope3d_apply(FAKE, Q.QI_F16, 8, 2, 256, FAKE, FAKE, None, 1e-6, None) == Q.QI_ERR_DTYPE
+    assert Q.qi_rope3d_apply(FAKE, 5, 8, 2, 256, FAKE, FAKE, None, 1e-6, None) == Q.QI_ERR_DTYPE
     # euler
     assert Q.qi_euler_step(None, FAKE, Q.QI_F32, 8, 1.0, 0.875, None) == Q.QI_ERR_ARG
     assert Q.qi_euler_step(FAKE, FAKE, Q.QI_F16, 8, 1.0, 0.875, None) == Q.QI_ERR_DTYPE
@@ -312,7 +317,7 @@ def test_other_entry_points_reject():
     L = Q.make_layout([qin.image(2, 2, 0)])
     assert Q.qi_rope3d_positions(L, None) == Q.QI_ERR_ARG
     assert Q.qi_blockmap(L, 0, 64, np.zeros(4, np.uint8)) == Q.QI_ERR_ARG
-    assert Q.lib().qi_attn_tile_shape(Q.QI_F16, ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32())) == Q.QI_ERR_DTYPE
+    assert Q.lib().qi_attn_tile_shape(9, ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32())) == Q.QI_ERR_DTYPE
     assert Q.lib().qi_attn_schedule(-1, 24, ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32())) == Q.QI_ERR_ARG
     assert Q.lib().qi_attn_schedule(4096, 0, ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32())) == Q.QI_ERR_ARG
     assert Q.lib().qi_attn_schedule(4096, 24, None, ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32())) == Q.QI_ERR_ARG

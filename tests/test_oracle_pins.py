@@ -888,6 +888,88 @@ def _v1_scale_gate_swapped(xt, xi, temb, B, cos, sin, temb0=None, n_noise=None, 
     return _ORIG_V1(xt, xi, temb, B2, cos, sin, temb0, n_noise, eps)
 
 
+def test_v1_block_rows_equal_full_rows():
+    # the row-restricted evaluation (keys and values from every row, outputs for the given rows
+    # only) equals the corresponding rows of the whole block, with and without the per-token
+    # modulation
+    B, xt, xi, temb, cos, sin = _v1_small(D=256, Lt=5, Li=8, seed=13)
+    temb0 = np.random.default_rng(14).standard_normal(256)
+    for t0, nn_ in ((None, None), (temb0, 3)):
+        yt, yi = O.v1_block(xt, xi, temb, B, cos, sin, t0, nn_)
+        for rt_, ri_ in (([0, 4], [1, 2, 7]), ([3], [5]), (list(range(5)), list(range(8)))):
+            st, si = O.v1_block(xt, xi, temb, B, cos, sin, t0, nn_, rows_txt=rt_, rows_img=ri_)
+            assert np.max(np.abs(st - yt[rt_])) < 1e-12 and np.max(np.abs(si - yi[ri_])) < 1e-12
+
+
+def _v1_head_weights(D=256, seed=17):
+    rng = np.random.default_rng(seed)
+    return {"norm_out_w": rng.standard_normal((2 * D, D)) / math.sqrt(D), "norm_out_b": 0.3 * rng.standard_normal(2 * D),
+            "proj_out_w": rng.standard_normal((64, D)) / math.sqrt(D), "proj_out_b": 0.1 * rng.standard_normal(64)}
+
+
+def test_v1_output_head_by_hand():
+    # [EDIT] section 5.3: emb = Linear(SiLU(temb)); scale is the first half, shift the second;
+    # LayerNorm without affine, x (1 + scale) + shift, then proj_out with its bias
+    D = 256
+    Hd = _v1_head_weights(D)
+    rng = np.random.default_rng(18)
+    xi = rng.standard_normal((7, D)) * 2 + 0.5
+    temb = rng.standard_normal(D)
+    got = O.v1_output_head(xi, temb, Hd)
+    s = temb / (1.0 + np.exp(-temb))
+    emb = Hd["norm_out_w"] @ s + Hd["norm_out_b"]
+    scale, shift = emb[:D], emb[D:]
+    ref = np.empty((7, 64))
+    for r in range(7):
+        mu = xi[r].sum() / D
+        var = ((xi[r] - mu) ** 2).sum() / D
+        n = (xi[r] - mu) / math.sqrt(var + 1e-6)
+        ref[r] = Hd["proj_out_w"] @ (n * (1.0 + scale) + shift) + Hd["proj_out_b"]
+    assert np.max(np.abs(got - ref)) < 1e-12
+    assert not np.allclose(scale, shift)
+
+
+def test_v1_forward_is_blocks_then_head_on_the_image_stream():
+    B1, xt, xi, temb, cos, sin = _v1_small(D=256, Lt=3, Li=4, seed=19)
+    B2 = _v1_small(D=256, Lt=3, Li=4, seed=20)[0]
+    Hd = _v1_head_weights(256, 21)
+    got = O.v1_forward(xt, xi, temb, [B1, B2], Hd, cos, sin)
+    t1, i1 = O.v1_block(xt, xi, temb, B1, cos, sin)
+    t2, i2 = O.v1_block(t1, i1, temb, B2, cos, sin)
+    assert got.shape == (4, 64)
+    assert np.max(np.abs(got - O.v1_output_head(i2, temb, Hd))) < 1e-12
+    # the text stream does not leave: changing the last block's text output path changes nothing
+    B2t = dict(B2)
+    B2t["txt_fc2_b"] = B2["txt_fc2_b"] + 5.0
+    assert np.max(np.abs(O.v1_forward(xt, xi, temb, [B1, B2t], Hd, cos, sin) - got)) < 1e-12
+
+
+def _v1_head_shift_first(x_img, temb, Hd, eps=1e-6):
+    D = np.asarray(x_img).shape[1]
+    H2 = dict(Hd)
+    H2["norm_out_w"] = np.concatenate([Hd["norm_out_w"][D:], Hd["norm_out_w"][:D]])
+    H2["norm_out_b"] = np.concatenate([Hd["norm_out_b"][D:], Hd["norm_out_b"][:D]])
+    return _ORIG_V1_HEAD(x_img, temb, H2, eps)
+
+
+def _v1_forward_text_stream(x_txt, x_img, temb, blocks, Hd, cos_t, sin_t, eps=1e-6):
+    xt, xi = x_txt, x_img
+    for B in blocks:
+        xt, xi = O.v1_block(xt, xi, temb, B, cos_t, sin_t, eps=eps)
+    return O.v1_output_head(np.concatenate([xt, xi])[:xi.shape[0]], temb, Hd, eps)
+
+
+def _v1_block_rows_unpicked(x_txt, x_img, temb, B, cos_t, sin_t, temb0=None, n_noise=None, eps=1e-6,
+                            rows_txt=None, rows_img=None):
+    # the restricted rows keep the modulation of the first rows instead of their own
+    if rows_txt is None:
+        return _ORIG_V1(x_txt, x_img, temb, B, cos_t, sin_t, temb0, n_noise, eps)
+    yt, yi = _ORIG_V1(x_txt, x_img, temb, B, cos_t, sin_t, temb0, n_noise, eps)
+    return yt[rows_txt], yi[np.arange(len(rows_img))]
+
+
+_ORIG_V1_HEAD = O.v1_output_head
+
 def _v1_selection_reversed(xt, xi, temb, B, cos, sin, temb0=None, n_noise=None, eps=1e-6):
     if temb0 is None:
         return _ORIG_V1(xt, xi, temb, B, cos, sin, None, n_noise, eps)
@@ -903,6 +985,9 @@ PLANTED_V1 = [
     ("v1_block", _v1_out_swapped, [test_v1_block_attention_half_by_hand]),
     ("v1_block", _v1_scale_gate_swapped, [test_v1_block_attention_half_by_hand, test_v1_block_mlp_half_by_hand]),
     ("v1_block", _v1_selection_reversed, [test_v1_block_per_token_modulation_selects_noise_rows]),
+    ("v1_block", _v1_block_rows_unpicked, [test_v1_block_rows_equal_full_rows]),
+    ("v1_output_head", _v1_head_shift_first, [test_v1_output_head_by_hand]),
+    ("v1_forward", _v1_forward_text_stream, [test_v1_forward_is_blocks_then_head_on_the_image_stream]),
 ]
 
 
