@@ -338,12 +338,15 @@ def configs_bench(args):
         Q.qi_kernel_timing(False)
         return e0.elapsed_time(e1) / reps, kern
 
-    def line(name, what, flops, call_ms, kern):
-        k50 = pct(kern, 50)
+    def line(name, what, flops, call_ms, kern, kern_per_unit=None):
+        # kern_per_unit: attention-kernel time of one unit of `flops` when a unit is several calls
+        # (the 8-step loop); else the median single call
+        k50 = pct(kern, 50) if kern_per_unit is None else kern_per_unit
+        key = "kernel_ms_p50" if kern_per_unit is None else "kernel_ms_per_loop"
         return {"metric": f"attention TFLOP/s, {what}", "value": round(flops / (call_ms * 1e-3) / 1e12, 1),
                 "unit": "TFLOP/s", "higher_is_better": True, "n_gpus": 1, "dtype": "f16", "data": "synthetic",
                 "config": {"workload": name, "flops_per_call": flops, "call_ms": round(call_ms, 4),
-                           "kernel_ms_p50": round(k50, 4), "kernel_tflops_p50": round(flops / (k50 * 1e-3) / 1e12, 1),
+                           key: round(k50, 4), "kernel_tflops": round(flops / (k50 * 1e-3) / 1e12, 1),
                            "pct_of_peak_kernel": round(100.0 * flops / (k50 * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2)}}
 
     reps = max(args.steps, 8)
@@ -377,7 +380,8 @@ def configs_bench(args):
     loop_ms, kern = ev_time(loop, reps)
     f1 = 4.0 * 128 * H * visible_pairs_per_head(wl.segments)
     fc = 4.0 * 128 * H * T * S
-    res = line(wl.name, "one layer's 8-step loop (step 1 + 7 cached steps + Euler)", f1 + 7 * fc, loop_ms, kern)
+    res = line(wl.name, "one layer's 8-step loop (step 1 + 7 cached steps + Euler)", f1 + 7 * fc, loop_ms, kern,
+               kern_per_unit=sum(kern) / reps)
     res["config"].update({"step1_flops": f1, "cached_flops": fc, "qk_rmsnorm": True, "heads": H})
     print(json.dumps(res), flush=True)
     del full, tgt, cache, att
@@ -435,6 +439,70 @@ def configs_bench(args):
     print(json.dumps(line(wl.name, "cached target step (4,096 queries over 20,992 keys)", fc, msc, kc)), flush=True)
 
 
+def data_sensitivity_bench(args):
+    """The headline cached step (4,096 queries over 21,504 keys, 24 heads) with the same shapes,
+    launches and instruction stream on inputs of different statistics: N(0,1) (the workload's),
+    N(0,1) rounded to half-integers (few mantissa bits), all ones and all zeros.  On a
+    power-limited chip the clock, and so the kernel time, follows the switching activity of the
+    data; one JSON line per input kind."""
+    import torch
+
+    import qi_inputs as qin
+    from image_generation_qi_amd import qi as Q
+    from image_generation_qi_amd import runtime as rt
+
+    dev = "cuda:0"
+    wl = qin.WORKLOADS["txt1024_4ref64_tgt64"]
+    P, T, H = wl.P, wl.T, wl.n_head
+    L = rt.Layout(wl.segments, dev)
+    att = rt.Attention(L, H, Q.QI_BF16, dev)
+    g = torch.Generator(device=dev).manual_seed(5)
+    NL = 4
+    flops = 4.0 * 128 * H * T * (P + T)
+
+    def draw(kind, shape):
+        if kind == "zeros":
+            return torch.zeros(shape, device=dev, dtype=torch.bfloat16)
+        if kind == "ones":
+            return torch.ones(shape, device=dev, dtype=torch.bfloat16)
+        x = torch.randn(shape, generator=g, device=dev)
+        if kind == "randn_half_integers":
+            x = torch.round(x * 2) / 2
+        return x.to(torch.bfloat16)
+
+    for kind in ("randn", "randn_half_integers", "ones", "zeros"):
+        cache = rt.KVCache(NL, H, P, Q.QI_BF16, dev)
+        for layer in range(NL):
+            kv = draw(kind, (P, 2, H, 128))
+            att.store(kv[:, 0], kv[:, 1], cache, layer)
+            del kv
+        qkv = [draw(kind, (T, 3, H, 128)) for _ in range(NL)]
+        out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+
+        def run(n):
+            for _ in range(n):
+                for layer in range(NL):
+                    t = qkv[layer]
+                    att.cached(t[:, 0], t[:, 1], t[:, 2], cache, layer, out=out)
+
+        run(max(args.warmup, 1) * 30)   # long enough for the clock to settle
+        torch.cuda.synchronize()
+        Q.qi_kernel_timing(True)
+        run(max(args.steps, 1) * 4)
+        torch.cuda.synchronize()
+        kern = sorted(Q.qi_kernel_timing_read_each())
+        Q.qi_kernel_timing(False)
+        k50 = pct(kern, 50)
+        print(json.dumps({"metric": "attention kernel TFLOP/s vs input statistics, cached target step",
+                          "value": round(flops / (k50 * 1e-3) / 1e12, 1), "unit": "TFLOP/s", "higher_is_better": True,
+                          "n_gpus": 1, "dtype": "f16", "data": kind,
+                          "config": {"workload": wl.name, "kernel_ms_p50": round(k50, 4), "launches": len(kern),
+                                     "pct_of_peak": round(100.0 * flops / (k50 * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2)}}),
+              flush=True)
+        del cache, qkv, out
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -451,6 +519,8 @@ def main():
                     help="time the v1 / Edit-Plus joint full attention (text 512 + target + 2 references) instead")
     ap.add_argument("--configs", action="store_true",
                     help="time the other attention workloads instead (one JSON line each)")
+    ap.add_argument("--data-sensitivity", action="store_true",
+                    help="time the headline cached step on N(0,1), low-mantissa, ones and zeros inputs instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -469,6 +539,11 @@ def main():
         from image_generation_qi_amd import qi as Q
         Q.lib()
         configs_bench(args)
+        return
+    if args.data_sensitivity:
+        from image_generation_qi_amd import qi as Q
+        Q.lib()
+        data_sensitivity_bench(args)
         return
 
     import torch

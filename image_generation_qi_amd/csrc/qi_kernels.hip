@@ -166,24 +166,34 @@ __global__ __launch_bounds__(256) void k_prep_kv64(PrepArgs a) {
   uint32_t(*vt)[65] = reinterpret_cast<uint32_t(*)[65]>(lds);   // [key][dim pair]: fp16 pairs
   const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int rr = tid >> 4, c = tid & 15;
-  // V rows first (their loads overlap the K arithmetic)
+  // Every thread issues all of its loads at once: rows past n_tok read the last row and are
+  // zeroed afterwards (loads behind a per-lane condition compile to branches with a wait after
+  // each load, which leaves one load in flight per thread).  V rows first (their loads overlap
+  // the K arithmetic).
   u32x4 vw[4];
   if (WITH_V) {
     const int key = tid >> 2, d0 = (tid & 3) * 32;
     const int64_t j = (int64_t)t * 64 + key;
+    const int64_t js = j < a.n_tok ? j : a.n_tok - 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      vw[i] = j < a.n_tok ? *(const u32x4*)((const uint16_t*)a.v + j * a.x_tok_stride + (int64_t)h * 128 + d0 + 8 * i)
-                          : u32x4{0u, 0u, 0u, 0u};
+      vw[i] = *(const u32x4*)((const uint16_t*)a.v + js * a.x_tok_stride + (int64_t)h * 128 + d0 + 8 * i);
+    if (j >= a.n_tok) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vw[i] = u32x4{0u, 0u, 0u, 0u};
+    }
   }
   bool kbad = false;
   float x[4][8];
 #pragma unroll
   for (int quarter = 0; quarter < 4; ++quarter) {
     const int64_t j = (int64_t)t * 64 + rr + 16 * quarter;
-    if (j < a.n_tok) {
-      load8<IN, OUT_F16>(a.x, j * a.x_tok_stride + (int64_t)h * 128 + 8 * c, x[quarter]);
-    } else {
+    const int64_t js = j < a.n_tok ? j : a.n_tok - 1;
+    load8<IN, OUT_F16>(a.x, js * a.x_tok_stride + (int64_t)h * 128 + 8 * c, x[quarter]);
+  }
+#pragma unroll
+  for (int quarter = 0; quarter < 4; ++quarter) {
+    if ((int64_t)t * 64 + rr + 16 * quarter >= a.n_tok) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[quarter][e] = 0.f;
     }
