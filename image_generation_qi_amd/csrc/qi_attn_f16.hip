@@ -6,34 +6,39 @@
 // card 3C: Block-Causal visibility; card 6A: target-only steps read a cached prefix).
 //
 // Work decomposition
-//   - one workgroup = 8 wavefronts = 256 query rows of one head; wave w owns rows 32w..32w+31.
-//     Two waves share each SIMD and one workgroup fills a CU, so every K/V tile brought into
-//     LDS serves 256 queries.
+//   - one workgroup = 8 wavefronts = 256 query rows of one head; wave w owns rows 32w..32w+31 as
+//     two row blocks of 16.  Two waves share each SIMD and one workgroup fills a CU, so every K/V
+//     tile brought into LDS serves 256 queries.
 //   - keys stream in tiles of 64 through LDS (four slots for K tiles and four for V tiles, 128 KB;
 //     K runs three tiles ahead, V one, and one wait and barrier end each pair of tiles), copied
 //     whole with MUBUF buffer -> LDS loads (which keep the compute phases' LDS waits exact).  The tiles are
 //     stored by the prep kernels in the order the MFMA operands are read (K as [16 dim chunks][64
-//     key slots][8 dims], V as [8 key chunks][128 dims][8 keys]): every operand read of 16 lanes
-//     is 256 contiguous bytes (no bank conflicts, no swizzle) at a constant offset from one
+//     keys][8 dims], V as [2 key halves][4 key groups][128 dims][8 keys]): every operand read of 16
+//     lanes is 256 contiguous bytes (no bank conflicts, no swizzle) at a constant offset from one
 //     per-lane base, the stage of each read is known at compile time, and every 1 KB copy is
 //     contiguous at both ends.  Source A (cache or workspace prefix) and source B (fresh keys)
 //     are tiled separately, so every copy reads one source.
-//   - S^T = K Q^T - m with v_mfma_f32_32x32x16_f16: A = 32 keys x 16 dims from LDS, B = the
-//     wave's 32 queries (rotated, scaled by scale*log2(e), fp16) held in registers; the
+//   - the matrix cores run v_mfma_f32_16x16x32_f16.  On the chip's power limit this shape does
+//     the same work for less energy than 32x32x16: its 4-register accumulators are read and
+//     written once per 16K flops instead of 16 registers per 32K, and with N(0,1) data the
+//     attention runs about 7 % faster with it, while MFMA, LDS and VALU counts per flop match.
+//   - S^T = K Q^T - m: A = 16 keys x 32 dims from LDS, B = 16 queries (rotated, scaled by
+//     scale*log2(e), fp16) held in registers; each K operand read feeds both row blocks.  The
 //     accumulators start at minus the row's reference m (kept broadcast in registers), so the
-//     scores come out shifted.  Each lane then holds one query and 16 keys per 32-key block.
-//   - O^T += V^T P^T with the same instruction: B = the lane's own probabilities (fp16), A = V^T
-//     (32 dims x 16 keys).  K's key slots are permuted inside every 16 (rows 4-7 and 8-11
-//     exchanged), so that the keys a lane holds in S^T are 8 consecutive keys per 16-key chunk:
-//     P never moves between lanes.
+//     scores come out shifted; lane l (group g = l / 16) holds keys 4g .. 4g + 3 of a 16-key
+//     block for query l % 16.
+//   - O^T += V^T P^T with the same instruction: B = the lane's own probabilities (fp16) for a
+//     32-key half, A = V^T (16 dims x those 32 keys).  V's tile order lists each lane group's
+//     keys in the order the S^T accumulators hold them, so P never moves between lanes.
 //   - online softmax in base 2 with a lazy reference: probabilities 2^(s) are formed against the
-//     current reference and only rows whose 32 probabilities in a lane sum above 2^8 (or that
+//     current reference and only rows whose 16 probabilities in a lane sum above 2^8 (or that
 //     have no reference yet) move it (a rare, wave-uniform branch); other rows keep a factor of
-//     exactly 1.  Every probability therefore stays at or below 2^8.
+//     exactly 1.  Every probability therefore stays at or below 2^8.  Row statistics combine the
+//     four lanes of a row with two lane exchanges.
 //   - software pipeline: the PV MFMAs of tile kt-1, the QK^T MFMAs of tile kt+1, the
 //     probabilities of tile kt (with their row sums), the LDS operand reads one step ahead and
-//     the copies of later tiles are one fenced sequence of 16 two-MFMA steps, so the softmax
-//     VALU work is spread over all 32 MFMAs of a tile and MFMA, VALU, LDS and memory work
+//     the copies of later tiles are one fenced sequence of 16 four-MFMA steps, so the softmax
+//     VALU work is spread over all 64 MFMAs of a tile and MFMA, VALU, LDS and memory work
 //     interleave.
 //   - the Block-Causal mask is applied per tile from the row limits (see qi_common.h): tiles
 //     with no visible pair are never loaded, tiles with all pairs visible run unmasked.
@@ -55,12 +60,11 @@ namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = kAttnF16TileQ;   // query rows per workgroup (8 waves of 32)
+constexpr int BM = kAttnF16TileQ;   // query rows per workgroup (8 waves of 2 x 16)
 constexpr int BN = 64;              // keys per tile
 constexpr int HD = 128;             // head dim
 constexpr int TILE_B = BN * HD * 2; // bytes of one K or V tile (16 KB)
@@ -84,15 +88,27 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <int N>
 using ic = std::integral_constant<int, N>;
 
-// Both halves of a wave exchanged: for lane l, returns (x[l], x[l ^ 32]) in an order that is
-// the same for the two lanes of the pair, so any symmetric combination is bit-identical.
-__device__ __forceinline__ float pair_max(float x) {
-  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+// Reductions over the four lanes of a row (lanes l16, l16 + 16, l16 + 32, l16 + 48): lanes 16
+// apart exchanged, then lanes 32 apart.  Each exchange hands both lanes of the pair the two values
+// in the same order, so every lane of the row ends with the same bits.
+__device__ __forceinline__ float row_sum4(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+__device__ __forceinline__ float row_max4(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ bool row_or4(bool b) {
+  const uint32_t x = b ? 1u : 0u;
+  const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const uint32_t y = p[0] | p[1];
+  const auto q = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return (q[0] | q[1]) != 0u;
 }
 
 // Two fp32 values as one word of the output type: bf16, or fp16 with IO16 (nearest even).
@@ -144,18 +160,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 5, l32 = lane & 31;
+  const int G = lane >> 4, l16 = lane & 15;   // lane group (of 16) and lane within it
   const int nA = (int)a.nA, nB = (int)a.nB, nkeys = nA + nB;
 
-  // ---- this lane's query: load, optional RMSNorm, rotate, scale, to fp16 --------------------
-  const int qrow = qt * BM + wave * 32 + l32;
-  const bool qok = qrow < a.n_q;
-  float x[64];
-  {
-    const uint16_t* qp = (const uint16_t*)a.q + (int64_t)(qok ? qrow : 0) * a.q_stride + h * HD + 8 * g;
+  // ---- this lane's two queries (rows 16rb + l16 of the wave's 32), dims 32kk + 8G .. + 7 of
+  // each: load, optional RMSNorm, rotate, scale, to fp16 ----------------------------------------
+  int qrow[2];
+  bool qok[2];
+  h8 qf[2][4];
+  bool qbad = false;   // a scaled query entry that fp16 cannot hold (magnitude >= 65520 or not finite)
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      u32x4 w = qok ? *(const u32x4*)(qp + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
+  for (int rb = 0; rb < 2; ++rb) {
+    qrow[rb] = qt * BM + wave * 32 + 16 * rb + l16;
+    qok[rb] = qrow[rb] < a.n_q;
+    float x[32];
+    const uint16_t* qp = (const uint16_t*)a.q + (int64_t)(qok[rb] ? qrow[rb] : 0) * a.q_stride + h * HD + 8 * G;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4 w = qok[rb] ? *(const u32x4*)(qp + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if constexpr (IO16) {
@@ -170,50 +192,49 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     }
-  }
-  if (a.q_rms_w) {
-    float ss = 0.f;
+    if (a.q_rms_w) {
+      float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < 64; ++i) ss += x[i] * x[i];
-    ss += __shfl_xor(ss, 32);
-    const float r = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
+      for (int i = 0; i < 32; ++i) ss += x[i] * x[i];
+      ss = row_sum4(ss);
+      const float r = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const f32x4 w0 = *(const f32x4*)(a.q_rms_w + 16 * kk + 8 * g);
-      const f32x4 w1 = *(const f32x4*)(a.q_rms_w + 16 * kk + 8 * g + 4);
+      for (int kk = 0; kk < 4; ++kk) {
+        const f32x4 w0 = *(const f32x4*)(a.q_rms_w + 32 * kk + 8 * G);
+        const f32x4 w1 = *(const f32x4*)(a.q_rms_w + 32 * kk + 8 * G + 4);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[8 * kk + j] *= r * w0[j];
-        x[8 * kk + 4 + j] *= r * w1[j];
+        for (int j = 0; j < 4; ++j) {
+          x[8 * kk + j] *= r * w0[j];
+          x[8 * kk + 4 + j] *= r * w1[j];
+        }
       }
     }
-  }
-  if (a.cos_q && qok) {
-    const float* cp = a.cos_q + (int64_t)qrow * 64 + 4 * g;
-    const float* sp = a.sin_q + (int64_t)qrow * 64 + 4 * g;
+    if (a.cos_q && qok[rb]) {
+      // pair (32kk + 8G + 2j, + 1) is rotation pair 16kk + 4G + j of the row
+      const float* cp = a.cos_q + (int64_t)qrow[rb] * 64 + 4 * G;
+      const float* sp = a.sin_q + (int64_t)qrow[rb] * 64 + 4 * G;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const f32x4 c = *(const f32x4*)(cp + 8 * kk);
-      const f32x4 s = *(const f32x4*)(sp + 8 * kk);
+      for (int kk = 0; kk < 4; ++kk) {
+        const f32x4 c = *(const f32x4*)(cp + 16 * kk);
+        const f32x4 s = *(const f32x4*)(sp + 16 * kk);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x0 = x[8 * kk + 2 * j], x1 = x[8 * kk + 2 * j + 1];
-        x[8 * kk + 2 * j] = x0 * c[j] - x1 * s[j];
-        x[8 * kk + 2 * j + 1] = x0 * s[j] + x1 * c[j];
+        for (int j = 0; j < 4; ++j) {
+          const float x0 = x[8 * kk + 2 * j], x1 = x[8 * kk + 2 * j + 1];
+          x[8 * kk + 2 * j] = x0 * c[j] - x1 * s[j];
+          x[8 * kk + 2 * j + 1] = x0 * s[j] + x1 * c[j];
+        }
       }
     }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float y = x[8 * kk + i] * a.scale_log2;
+        qbad |= qok[rb] && !(fabsf(y) < 65520.0f);
+        qf[rb][kk][i] = (_Float16)y;
+      }
   }
-  h8 qf[8];
-  bool qbad = false;   // a scaled query entry that fp16 cannot hold (magnitude >= 65520 or not finite)
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float y = x[8 * kk + i] * a.scale_log2;
-      qbad |= !(fabsf(y) < 65520.0f);
-      qf[kk][i] = (_Float16)y;
-    }
-  if (a.flags && qbad && qok) atomicOr(a.flags, QI_RANGE_Q);
+  if (a.flags && qbad) atomicOr(a.flags, QI_RANGE_Q);
 
   // ---- key tiles of this tile row ----------------------------------------------------------
   // Sources A and B are tiled separately: tiles 0 .. ntA-1 hold keys 64t .. of A, tiles ntA ..
@@ -221,12 +242,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int ntA = (nA + BN - 1) / BN;
   const int q_first = qt * BM;
   const int q_last = (q_first + BM < a.n_q ? q_first + BM : a.n_q) - 1;
-  int lim = nkeys - 1, lim_first = nkeys - 1, lim_last = nkeys - 1;
+  int lim[2] = {nkeys - 1, nkeys - 1};
+  int lim_first = nkeys - 1, lim_last = nkeys - 1;
   if (MASKED) {
-    lim = (int)row_limit(a.segs, a.q_row0 + (qok ? qrow : q_last));
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      lim[rb] = (int)row_limit(a.segs, a.q_row0 + (qok[rb] ? qrow[rb] : q_last));
+      lim[rb] = lim[rb] < nkeys - 1 ? lim[rb] : nkeys - 1;
+    }
     lim_first = (int)row_limit(a.segs, a.q_row0 + q_first);
     lim_last = (int)row_limit(a.segs, a.q_row0 + q_last);
-    lim = lim < nkeys - 1 ? lim : nkeys - 1;
     lim_first = lim_first < nkeys - 1 ? lim_first : nkeys - 1;
     lim_last = lim_last < nkeys - 1 ? lim_last : nkeys - 1;
   }
@@ -238,14 +263,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int t_begin = nsp == 1 ? 0 : split * a.split_tiles;
   const int t_stop = (nsp == 1 || t_begin + a.split_tiles > kt_end) ? kt_end : t_begin + a.split_tiles;
   if (t_begin >= t_stop) {  // the chunk holds no visible key for any row of the tile
-    if (qok) {
-      const int64_t row = prow0 + wave * 32 + l32;
-      uint16_t* po = a.part_o + row * HD + 4 * g;
 #pragma unroll
-      for (int bd = 0; bd < 4; ++bd)
+    for (int rb = 0; rb < 2; ++rb) {
+      if (qok[rb]) {
+        const int64_t row = prow0 + wave * 32 + 16 * rb + l16;
+        uint16_t* po = a.part_o + row * HD + 4 * G;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) *(u32x2*)(po + 32 * bd + 8 * r4) = u32x2{0u, 0u};
-      if (g == 0) *(f32x4*)(a.part_ml + 4 * row) = f32x4{-INFINITY, 0.f, 1.f, 0.f};
+        for (int db = 0; db < 8; ++db) *(u32x2*)(po + 16 * db) = u32x2{0u, 0u};
+        if (G == 0) *(f32x4*)(a.part_ml + 4 * row) = f32x4{-INFINITY, 0.f, 1.f, 0.f};
+      }
     }
     return;
   }
@@ -279,65 +305,70 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, soff, 0, 0);
   };
 
-  f32x16 o[4];
+  // O^T accumulators: o[rb][db][r] = dim 16db + 4G + r of row 16rb + l16
+  f32x4 o[2][8];
 #pragma unroll
-  for (int bd = 0; bd < 4; ++bd)
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[bd][r] = 0.f;
+    for (int db = 0; db < 8; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   // m_run: the reference (log2 units) the scores of the current tile were taken against; -inf
   // until a row has seen a visible key (its scores are then taken against 0).  ninit holds the
-  // accumulator start value (minus the reference, 0 while it is -inf) broadcast over 16 entries.
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x16 ninit;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) ninit[r] = 0.f;
+  // accumulator start value (minus the reference, 0 while it is -inf) broadcast over 4 entries.
+  // All four lanes of a row hold the same m_run, ninit and (after the row sum) l_run.
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  f32x4 ninit[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 
   // ---- LDS operand reads (byte offsets from one per-lane base, the rest constant) -----------
-  // K (reduction step kk, key block kb): slot 32kb + l32, dims 16kk + 8g .. + 7 = piece
-  // (2kk + g) * 1024 + slot * 16.  V^T (16-key chunk c, dims 32bd + l32): keys 16c + 8g .. + 7 =
-  // piece (2c + g) * 2048 + dim * 16.
+  // K (key block kb of 16, dims 32kk .. + 31): key 16kb + l16, dims 32kk + 8G .. + 7 = dim chunk
+  // 4kk + G: (4kk + G) * 1024 + (16kb + l16) * 16.  V^T (32-key half c, dims 16db .. + 15): dim
+  // 16db + l16, keys of group G of half c: (4c + G) * 2048 + (16db + l16) * 16.
   // The slot of every read is a compile-time constant; the V base holds the V region's offset,
   // so all constant parts stay within the 16-bit offset field of ds_read_b128.
-  const int base_k = g * 1024 + l32 * 16;
-  const int base_v = SLOTS * TILE_B + g * 2048 + l32 * 16;
+  const int base_k = G * 1024 + l16 * 16;
+  const int base_v = SLOTS * TILE_B + G * 2048 + l16 * 16;
   auto read_k = [&](auto stag, int kk, int kb) -> h8 {
-    return *(const h8*)(smem + base_k + (decltype(stag)::value * TILE_B + kk * 2048 + kb * 512));
+    return *(const h8*)(smem + base_k + (decltype(stag)::value * TILE_B + kk * 4096 + kb * 256));
   };
-  auto read_v = [&](auto stag, int c, int bd) -> h8 {
-    return *(const h8*)(smem + base_v + (decltype(stag)::value * TILE_B + c * 4096 + bd * 512));
+  auto read_v = [&](auto stag, int c, int db) -> h8 {
+    return *(const h8*)(smem + base_v + (decltype(stag)::value * TILE_B + c * 8192 + db * 256));
   };
 
-  // S^T - m = K Q^T - m for the 64 keys of K slot 0.  Prologue only.
-  auto qk0 = [&](f32x16& s0, f32x16& s1) {
+  // S^T - m = K Q^T - m for the 64 keys of K slot 0 (s[rb][kb][r] = key 16kb + 4G + r of row
+  // 16rb + l16).  Prologue only.
+  auto qk0 = [&](f32x4 (&s)[2][4]) {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const h8 k0 = read_k(ic<0>{}, kk, 0), k1 = read_k(ic<0>{}, kk, 1);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qf[kk], kk ? s0 : ninit, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qf[kk], kk ? s1 : ninit, 0, 0, 0);
-    }
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const h8 k = read_k(ic<0>{}, kk, kb);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k, qf[rb][kk], kk ? s[rb][kb] : ninit[rb], 0, 0, 0);
+      }
   };
 
-  // One iteration's compute as a single fenced sequence of 16 steps of two MFMAs each: steps 0-7
-  // are the PV of the previous tile (probabilities pp, chunk i/2, dims 64(i%2) .. + 63), steps
-  // 8-15 the QK^T of the next tile (reduction step i - 8, both 32-key blocks, accumulators
-  // starting at minus the reference).  Every step also issues the LDS operand reads of the next
-  // step and forms two probabilities 2^s of the current tile (scores 2i, 2i+1 of the first
-  // 32-key block in steps 0-7, of the second in steps 8-15), rounded to fp16 and added into the
-  // row sum; steps 0-3 issue the wave's four copies of later tiles (K of tile tk into K slot kcs,
-  // V of tile tv into V slot vcs).  So the softmax VALU work is spread over all 32 MFMAs of the
-  // tile.  ktag / vtag: the slots the K and V operands are read from.
-  auto seq = [&](auto ktag, auto vtag, int kcs, int vcs, int tk, int tv, f32x16& sn0, f32x16& sn1,
-                 const f32x16& s0, const f32x16& s1, const h8 (&pp)[4], h8 (&pf)[4]) -> float {
-    const h2 one2 = {(_Float16)1.f, (_Float16)1.f};
-    // operands of step n: V^T (chunk n/2, dims 64(n%2) + 32e ..) for n < 8, K (step n - 8,
-    // key blocks e = 0, 1) after
+  // One iteration's compute as a single fenced sequence of 16 steps of four MFMAs each (two LDS
+  // operands, each multiplied into both row blocks): steps 0-7 are the PV of the previous tile
+  // (probabilities pp, key half i/4, dim blocks 2(i%4), 2(i%4) + 1), steps 8-15 the QK^T of the
+  // next tile (dims 32((i-8)/2) .., key blocks 2((i-8)%2), + 1; accumulators starting at minus
+  // the reference).  Every step also issues the LDS operand reads of the next step and forms two
+  // probabilities 2^s of the current tile (the first key half's scores in steps 0-7, the second's
+  // in steps 8-15; row block (i%8)/4), rounded to fp16 and added (unrounded, fp32) into the row
+  // block's sum; steps 0-3 issue the wave's four copies of later tiles (K of tile tk into K slot
+  // kcs, V of tile tv into V slot vcs).  The empty asm statements keep each step's probability
+  // and sum inside that step (compiler passes would otherwise sink them past the iteration's last
+  // MFMA, where they would stall the matrix core).  ktag / vtag: the slots the operands come from.
+  auto seq = [&](auto ktag, auto vtag, int kcs, int vcs, int tk, int tv, f32x4 (&sn)[2][4], const f32x4 (&s)[2][4],
+                 const h8 (&pp)[2][2], h8 (&pf)[2][2], float (&ps)[2]) {
     auto read_ops = [&](int n, h8 (&d)[2]) {
 #pragma unroll
-      for (int e = 0; e < 2; ++e) d[e] = n < 8 ? read_v(vtag, n >> 1, 2 * (n & 1) + e) : read_k(ktag, n - 8, e);
+      for (int e = 0; e < 2; ++e)
+        d[e] = n < 8 ? read_v(vtag, n >> 2, 2 * (n & 3) + e) : read_k(ktag, (n - 8) >> 1, 2 * ((n - 8) & 1) + e);
     };
     h8 op[2][2];
     read_ops(0, op[0]);
-    float ps0 = 0.f, ps1 = 0.f;
+    ps[0] = 0.f;
+    ps[1] = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i + 1 < 16) read_ops(i + 1, op[(i + 1) & 1]);
@@ -347,37 +378,47 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         copy(tv, vcs, i - 2, std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
       if (i < 8) {
-        const int c = i >> 1, bd = 2 * (i & 1);
-        o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[i & 1][0], pp[c], o[bd], 0, 0, 0);
-        o[bd + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[i & 1][1], pp[c], o[bd + 1], 0, 0, 0);
+        const int c = i >> 2, db = 2 * (i & 3);
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            o[rb][db + e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(op[i & 1][e], pp[rb][c], o[rb][db + e], 0, 0, 0);
       } else {
-        const int kk = i - 8;
-        sn0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[i & 1][0], qf[kk], kk ? sn0 : ninit, 0, 0, 0);
-        sn1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[i & 1][1], qf[kk], kk ? sn1 : ninit, 0, 0, 0);
+        const int kk = (i - 8) >> 1, kb = 2 * ((i - 8) & 1);
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            sn[rb][kb + e] =
+                __builtin_amdgcn_mfma_f32_16x16x32_f16(op[i & 1][e], qf[rb][kk], kk ? sn[rb][kb + e] : ninit[rb], 0, 0, 0);
       }
-      const int j = i & 7;
-      const float p0 = __builtin_amdgcn_exp2f(i < 8 ? s0[2 * j] : s1[2 * j]);
-      const float p1 = __builtin_amdgcn_exp2f(i < 8 ? s0[2 * j + 1] : s1[2 * j + 1]);
-      const h2 q = {(_Float16)p0, (_Float16)p1};
-      pf[(i < 8 ? 0 : 2) + (j >> 2)][2 * (j & 3)] = q[0];
-      pf[(i < 8 ? 0 : 2) + (j >> 2)][2 * (j & 3) + 1] = q[1];
-      if (i < 8)
-        ps0 = __builtin_amdgcn_fdot2(q, one2, ps0, false);
-      else
-        ps1 = __builtin_amdgcn_fdot2(q, one2, ps1, false);
+      {
+        const int n = i & 7, c = i >> 3, rb = n >> 2, kh = (n >> 1) & 1, r = 2 * (n & 1);
+        const float p0 = __builtin_amdgcn_exp2f(s[rb][2 * c + kh][r]);
+        const float p1 = __builtin_amdgcn_exp2f(s[rb][2 * c + kh][r + 1]);
+        h2 q = {(_Float16)p0, (_Float16)p1};
+        asm volatile("" : "+v"(q));
+        pf[rb][c][4 * kh + r] = q[0];
+        pf[rb][c][4 * kh + r + 1] = q[1];
+        ps[rb] += p0 + p1;
+        asm volatile("" : "+v"(ps[rb]));
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    return ps0 + ps1;
   };
 
   // PV of the last tile (V in slot `slot`, known only at run time), after the loop.
-  auto pv_last = [&](int slot, const h8 (&pp)[4]) {
+  auto pv_last = [&](int slot, const h8 (&pp)[2][2]) {
     const char* vs = smem + slot * TILE_B + base_v;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int bd = 0; bd < 4; ++bd)
-        o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const h8*)(vs + c * 4096 + bd * 512), pp[c], o[bd], 0, 0, 0);
+      for (int db = 0; db < 8; ++db) {
+        const h8 v = *(const h8*)(vs + c * 8192 + db * 256);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, pp[rb][c], o[rb][db], 0, 0, 0);
+      }
   };
 
   // ---- software-pipelined main loop ------------------------------------------------------
@@ -409,188 +450,191 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  f32x16 sa0, sa1, sb0, sb1;
-  qk0(sa0, sa1);
+  f32x4 sa[2][4], sb[2][4];
+  qk0(sa);
   // every wave has read K slot 0 before the pair that copies into it
   __syncthreads();
   int kt = t_begin;
   const int kt_mid = kt_full < t_begin ? t_begin : (kt_full < t_stop ? kt_full : t_stop);
   const int kt_mid4 = t_begin + ((kt_mid - t_begin) & ~3);   // unmasked groups of four end here
   // probabilities of the previous and the current tile (two register sets, swapped per iteration)
-  h8 pa[4], pb[4];
+  h8 pa[2][2], pb[2][2];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pa[c][e] = (_Float16)0.f;
-  auto iteration = [&](auto rtag, auto masked_tag, f32x16& s0, f32x16& s1, f32x16& sn0, f32x16& sn1,
-                       const h8 (&pp)[4], h8 (&pf)[4]) {
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pa[rb][c][e] = (_Float16)0.f;
+  auto iteration = [&](auto rtag, auto masked_tag, f32x4 (&s)[2][4], f32x4 (&sn)[2][4], const h8 (&pp)[2][2],
+                       h8 (&pf)[2][2]) {
     constexpr int R = decltype(rtag)::value;
     constexpr bool MT = decltype(masked_tag)::value;
     if constexpr (MT) {
       const int key0 = kt < ntA ? kt * BN : nA + (kt - ntA) * BN;
       const int cnt = kt < ntA ? nA - kt * BN : nkeys - key0;   // keys of the tile (capped below)
-      int rel = lim - key0;
-      if (rel > cnt - 1) rel = cnt - 1;
-      rel -= 8 * g;                 // offset (in tile, minus 8g) of the last visible key
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kr = 16 * (r >> 3) + (r & 7);   // key of accumulator entry r (slots permuted)
-        if (kr > rel) s0[r] = -INFINITY;
-        if (kr + 32 > rel) s1[r] = -INFINITY;
+      for (int rb = 0; rb < 2; ++rb) {
+        int rel = lim[rb] - key0;
+        if (rel > cnt - 1) rel = cnt - 1;
+        rel -= 4 * G;                 // offset (in tile, minus 4G) of the last visible key
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * kb + r > rel) s[rb][kb][r] = -INFINITY;
       }
     }
     // next tile's scores (on the last iteration from a stale, in-bounds slot, discarded); copies
     // past the last tile repeat the last tile into slots nothing reads again
-    float ps = seq(ic<(R + 1) % SLOTS>{}, ic<(R + 3) % SLOTS>{}, (R + 3) % SLOTS, (R + 1) % SLOTS, last(kt + 3),
-                   last(kt + 1), sn0, sn1, s0, s1, pp, pf);
-    // Rare path: a row's first visible tile (reference still -inf) or a lane's 32 probabilities
-    // summing above 2^8 (which includes +inf and NaN).  The row's new reference is its true max;
-    // the probabilities and their sum are recomputed, the running output and sum are rescaled by
-    // alpha, the next tile's scores (taken against the old reference) are shifted and the
-    // accumulator start value follows the new reference.  Rows that do not take it keep alpha =
-    // 1 exactly, so each row's arithmetic never depends on the other rows of the wave.
-    const bool need1 = !(ps <= 256.f) || m_run == -INFINITY;
-    if (__builtin_expect(__any(need1), 0)) {
-      const auto sw = __builtin_amdgcn_permlane32_swap(need1 ? 1u : 0u, need1 ? 1u : 0u, false, false);
-      const bool need = (sw[0] | sw[1]) != 0u;     // either half of the row
-      float mt = fmaxf(s0[0], s1[0]);
+    float ps[2];
+    seq(ic<(R + 1) % SLOTS>{}, ic<(R + 3) % SLOTS>{}, (R + 3) % SLOTS, (R + 1) % SLOTS, last(kt + 3), last(kt + 1),
+        sn, s, pp, pf, ps);
+    // Rare path: a row's first visible tile (reference still -inf) or a lane's 16 probabilities
+    // of a row summing above 2^8 (which includes +inf and NaN).  The row's new reference is its
+    // true max; the probabilities and their sum are recomputed, the running output and sum are
+    // rescaled by alpha, the next tile's scores (taken against the old reference) are shifted
+    // and the accumulator start value follows the new reference.  Rows that do not take it keep
+    // alpha = 1 exactly, so each row's arithmetic never depends on the other rows of the wave.
+    bool need1[2];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, fmaxf(s0[r], s1[r]));
-      mt = pair_max(mt);                           // row max of the shifted scores
-      float shift = 0.f, alpha = 1.f;
-      if (need) {
-        if (m_run == -INFINITY) {
-          alpha = 0.f;
-          shift = (mt == -INFINITY) ? 0.f : mt;
-          m_run = mt;
-        } else {
-          alpha = __builtin_amdgcn_exp2f(-mt);
-          shift = mt;
-          m_run = m_run + mt;
+    for (int rb = 0; rb < 2; ++rb) need1[rb] = !(ps[rb] <= 256.f) || m_run[rb] == -INFINITY;
+    if (__builtin_expect(__any(need1[0] || need1[1]), 0)) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const bool need = row_or4(need1[rb]);      // any of the row's four lanes
+        float mt = s[rb][0][0];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[rb][kb][r]);
+        mt = row_max4(mt);                         // row max of the shifted scores
+        float shift = 0.f, alpha = 1.f;
+        if (need) {
+          if (m_run[rb] == -INFINITY) {
+            alpha = 0.f;
+            shift = (mt == -INFINITY) ? 0.f : mt;
+            m_run[rb] = mt;
+          } else {
+            alpha = __builtin_amdgcn_exp2f(-mt);
+            shift = mt;
+            m_run[rb] = m_run[rb] + mt;
+          }
         }
+        float sum = 0.f;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float p = __builtin_amdgcn_exp2f(s[rb][2 * c + kh][r] - shift);
+              pf[rb][c][4 * kh + r] = (_Float16)p;
+              sum += p;
+            }
+        ps[rb] = sum;
+        const float nm = (m_run[rb] == -INFINITY) ? 0.f : -m_run[rb];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) sn[rb][kb] = sn[rb][kb] - shift;
+        ninit[rb] = f32x4{nm, nm, nm, nm};
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[rb][db] = o[rb][db] * alpha;
+        l_run[rb] *= alpha;
       }
-      const h2 one2 = {(_Float16)1.f, (_Float16)1.f};
-      float sum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const h2 q0 = {(_Float16)__builtin_amdgcn_exp2f(s0[r] - shift), (_Float16)__builtin_amdgcn_exp2f(s0[r + 1] - shift)};
-        const h2 q1 = {(_Float16)__builtin_amdgcn_exp2f(s1[r] - shift), (_Float16)__builtin_amdgcn_exp2f(s1[r + 1] - shift)};
-        pf[r >> 3][r & 7] = q0[0];
-        pf[r >> 3][(r & 7) + 1] = q0[1];
-        pf[2 + (r >> 3)][r & 7] = q1[0];
-        pf[2 + (r >> 3)][(r & 7) + 1] = q1[1];
-        sum = __builtin_amdgcn_fdot2(q0, one2, sum, false);
-        sum = __builtin_amdgcn_fdot2(q1, one2, sum, false);
-      }
-      ps = sum;
-      const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sn0[r] -= shift;
-        sn1[r] -= shift;
-        ninit[r] = nm;
-      }
-#pragma unroll
-      for (int bd = 0; bd < 4; ++bd)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[bd][r] *= alpha;
-      l_run *= alpha;
     }
-    l_run += ps;
+    l_run[0] += ps[0];
+    l_run[1] += ps[1];
   };
   auto pair_end = [&]() {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
   while (kt + 3 < kt_mid4) {
-    iteration(ic<0>{}, std::false_type{}, sa0, sa1, sb0, sb1, pa, pb);
+    iteration(ic<0>{}, std::false_type{}, sa, sb, pa, pb);
     ++kt;
-    iteration(ic<1>{}, std::false_type{}, sb0, sb1, sa0, sa1, pb, pa);
+    iteration(ic<1>{}, std::false_type{}, sb, sa, pb, pa);
     ++kt;
     pair_end();
-    iteration(ic<2>{}, std::false_type{}, sa0, sa1, sb0, sb1, pa, pb);
+    iteration(ic<2>{}, std::false_type{}, sa, sb, pa, pb);
     ++kt;
-    iteration(ic<3>{}, std::false_type{}, sb0, sb1, sa0, sa1, pb, pa);
+    iteration(ic<3>{}, std::false_type{}, sb, sa, pb, pa);
     ++kt;
     pair_end();
   }
   while (kt + 3 < t_stop) {
-    iteration(ic<0>{}, std::true_type{}, sa0, sa1, sb0, sb1, pa, pb);
+    iteration(ic<0>{}, std::true_type{}, sa, sb, pa, pb);
     ++kt;
-    iteration(ic<1>{}, std::true_type{}, sb0, sb1, sa0, sa1, pb, pa);
+    iteration(ic<1>{}, std::true_type{}, sb, sa, pb, pa);
     ++kt;
     pair_end();
-    iteration(ic<2>{}, std::true_type{}, sa0, sa1, sb0, sb1, pa, pb);
+    iteration(ic<2>{}, std::true_type{}, sa, sb, pa, pb);
     ++kt;
-    iteration(ic<3>{}, std::true_type{}, sb0, sb1, sa0, sa1, pb, pa);
+    iteration(ic<3>{}, std::true_type{}, sb, sa, pb, pa);
     ++kt;
     pair_end();
   }
   // up to three more tiles (slots 0, 1, 2)
   const int rest = t_stop - kt;
   if (rest >= 1) {
-    iteration(ic<0>{}, std::true_type{}, sa0, sa1, sb0, sb1, pa, pb);
+    iteration(ic<0>{}, std::true_type{}, sa, sb, pa, pb);
     ++kt;
     if (rest >= 2) {
-      iteration(ic<1>{}, std::true_type{}, sb0, sb1, sa0, sa1, pb, pa);
+      iteration(ic<1>{}, std::true_type{}, sb, sa, pb, pa);
       ++kt;
       if (rest >= 3) {
         pair_end();
-        iteration(ic<2>{}, std::true_type{}, sa0, sa1, sb0, sb1, pa, pb);
+        iteration(ic<2>{}, std::true_type{}, sa, sb, pa, pb);
         ++kt;
       }
     }
     if (rest != 2) {   // the latest probabilities are in pb
 #pragma unroll
-      for (int c = 0; c < 4; ++c) pa[c] = pb[c];
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) pa[rb][c] = pb[rb][c];
     }
   }
   // every wave's copies of the last V tile have landed before its PV
   pair_end();
   pv_last((kt - 1 - t_begin) % SLOTS, pa);
 
-  // ---- epilogue: normalise and store bf16, or store the chunk's partial ---------------------
-  const float lt = pair_sum(l_run);
-  if (qok) {
+  // ---- epilogue: normalise and store, or store the chunk's partial --------------------------
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const float lt = row_sum4(l_run[rb]);
+    if (!qok[rb]) continue;
     if (nsp == 1) {
       // log-sum-exp in natural units: the scores are in units of log2(e) against the reference
-      if (a.lse && g == 0) a.lse[(int64_t)h * a.lse_stride + qrow] = (m_run + __log2f(lt)) * 0.6931471805599453f;
+      if (a.lse && G == 0) a.lse[(int64_t)h * a.lse_stride + qrow[rb]] = (m_run[rb] + __log2f(lt)) * 0.6931471805599453f;
       const float inv = 1.0f / lt;
-      uint16_t* op = (uint16_t*)a.o + (int64_t)qrow * a.o_stride + h * HD + 4 * g;
+      uint16_t* op = (uint16_t*)a.o + (int64_t)qrow[rb] * a.o_stride + h * HD + 4 * G;
 #pragma unroll
-      for (int bd = 0; bd < 4; ++bd)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const u32x2 w = {out2<IO16>(o[bd][4 * r4] * inv, o[bd][4 * r4 + 1] * inv),
-                           out2<IO16>(o[bd][4 * r4 + 2] * inv, o[bd][4 * r4 + 3] * inv)};
-          *(u32x2*)(op + 32 * bd + 8 * r4) = w;
-        }
+      for (int db = 0; db < 8; ++db)
+        *(u32x2*)(op + 16 * db) = u32x2{out2<IO16>(o[rb][db][0] * inv, o[rb][db][1] * inv),
+                                        out2<IO16>(o[rb][db][2] * inv, o[rb][db][3] * inv)};
     } else {
       // the chunk's output divided by its own sum (a convex combination of fp16 V rows), times
       // 2^e chosen per row so that the row's largest magnitude lies in [2^14, 2^15): every entry
       // within 2^29 of it keeps fp16's 11-bit precision, however small V is, and none overflows.
       // The merge weights it back by (m, l) and undoes the scale with s = 2^-e (exact).
-      const int64_t row = prow0 + wave * 32 + l32;
-      uint16_t* po = a.part_o + row * HD + 4 * g;
+      const int64_t row = prow0 + wave * 32 + 16 * rb + l16;
+      uint16_t* po = a.part_o + row * HD + 4 * G;
       const float inv = 1.0f / lt;    // lt >= 1: the reference key itself contributes 1
       float amax = 0.f;
 #pragma unroll
-      for (int bd = 0; bd < 4; ++bd)
+      for (int db = 0; db < 8; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(o[bd][r]));
-      const float rmax = pair_max(amax) * inv;   // the same value in both lanes of the row
+        for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(o[rb][db][r]));
+      const float rmax = row_max4(amax) * inv;   // the same value in the row's four lanes
       int e = rmax > 0.f ? 15 - __builtin_amdgcn_frexp_expf(rmax) : 0;
       e = e < 100 ? e : 100;
       const float f = __builtin_ldexpf(inv, e);
 #pragma unroll
-      for (int bd = 0; bd < 4; ++bd)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const h2 lo = {(_Float16)(o[bd][4 * r4] * f), (_Float16)(o[bd][4 * r4 + 1] * f)};
-          const h2 hi = {(_Float16)(o[bd][4 * r4 + 2] * f), (_Float16)(o[bd][4 * r4 + 3] * f)};
-          *(u32x2*)(po + 32 * bd + 8 * r4) = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-        }
-      if (g == 0) *(f32x4*)(a.part_ml + 4 * row) = f32x4{m_run, lt, __builtin_ldexpf(1.0f, -e), 0.f};
+      for (int db = 0; db < 8; ++db) {
+        const h2 lo = {(_Float16)(o[rb][db][0] * f), (_Float16)(o[rb][db][1] * f)};
+        const h2 hi = {(_Float16)(o[rb][db][2] * f), (_Float16)(o[rb][db][3] * f)};
+        *(u32x2*)(po + 16 * db) = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+      }
+      if (G == 0) *(f32x4*)(a.part_ml + 4 * row) = f32x4{m_run[rb], lt, __builtin_ldexpf(1.0f, -e), 0.f};
     }
   }
 }

@@ -137,18 +137,17 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
 }
 
 // K and V of the fp16 attention path, in the tiles its kernel copies whole into LDS: per head,
-// tiles of 64 keys, 16 KB each, keys at or past n written as zero.
-//   K tile: [16 dim chunks][64 key slots][8 dims] fp16.  Slot p holds key perm16(p) of the tile,
-//     perm16 exchanging rows 4-7 and 8-11 of every 16: then the keys a lane holds in the S^T
-//     accumulator of v_mfma_f32_32x32x16_f16 are 8 consecutive keys per 16-key chunk.
-//   V tile: [8 key chunks][128 dims][8 keys] fp16 (V transposed per 8-key chunk), so the P V
-//     MFMA's V^T operand (one dim, 8 keys) is one 16-byte piece.
+// tiles of 64 keys, 16 KB each, keys at or past n written as zero.  The attention multiplies them
+// with v_mfma_f32_16x16x32_f16, whose A operand gives lane l (group g = l / 16) 8 consecutive
+// reduction elements 8g .. 8g + 7 of row l % 16.
+//   K tile: [16 dim chunks][64 keys][8 dims] fp16: the QK^T operand of key block kb and dims
+//     32kk .. is chunk 4kk + g, keys 16kb + l % 16.
+//   V tile: [2 key halves][4 key groups][128 dims][8 keys] fp16: element e of group g of half c is
+//     key 32c + 16(e / 4) + 4g + e % 4.  These are the keys whose probabilities lane group g holds
+//     for half c in the S^T accumulators (rows 4g .. 4g + 3 of key blocks 2c and 2c + 1), so the
+//     P V MFMA's V^T operand (one dim, 8 keys) is one 16-byte piece and P never moves between lanes.
 // In both, the 16-byte pieces that one MFMA operand read takes for 16 consecutive lanes are
 // consecutive in memory, and every 1 KB of a tile is one contiguous copy.
-__device__ __forceinline__ int perm16(int p) {
-  const int grp = (p >> 2) & 3;
-  return (p & ~15) | ((grp == 1 ? 2 : (grp == 2 ? 1 : grp)) << 2) | (p & 3);
-}
 
 // One workgroup per (64-key tile, head).  K: 16 threads per key row (8 dims each, four rows per
 // thread) normalise and rotate, and put each row's fp16 chunks at their tile positions in LDS
@@ -232,7 +231,7 @@ __global__ __launch_bounds__(256) void k_prep_kv64(PrepArgs a) {
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) kbad |= unfit_f16(xq[e]);
-    *(u32x4*)(kt + c * KROW + perm16(r) * 16) =
+    *(u32x4*)(kt + c * KROW + r * 16) =
         u32x4{pack_f16(xq[0], xq[1]), pack_f16(xq[2], xq[3]), pack_f16(xq[4], xq[5]), pack_f16(xq[6], xq[7])};
   }
   if (a.flags && kbad) atomicOr(a.flags, QI_RANGE_K);
@@ -263,19 +262,21 @@ __global__ __launch_bounds__(256) void k_prep_kv64(PrepArgs a) {
           vt[key][(d0 + 8 * i) / 2 + e] = IN == IN_F16 ? vw[i][e] : pack_f16(bf16_lo(vw[i][e]), bf16_hi(vw[i][e]));
     }
     __syncthreads();
-    // V tile out: piece p = key chunk p / 128, dim p % 128 (8 keys of that dim)
+    // V tile out: piece p = (half c, group g, dim d) with c = p / 512, g = p / 128 % 4, d = p %
+    // 128; its word k holds keys 32c + 16(k / 2) + 4g + 2(k % 2) and the next one
     uint16_t* vtile = (uint16_t*)a.dst_v + (int64_t)h * a.dst_head_stride + (int64_t)t * 8192;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int piece = tid + 256 * i;
-      const int kc = piece >> 7, d = piece & 127;
+      const int c = piece >> 9, gq = (piece >> 7) & 3, d = piece & 127;
       uint32_t w[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = vt[8 * kc + 2 * e][d >> 1], hi = vt[8 * kc + 2 * e + 1][d >> 1];
-        w[e] = (d & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+      for (int k = 0; k < 4; ++k) {
+        const int key = 32 * c + 16 * (k >> 1) + 4 * gq + 2 * (k & 1);
+        const uint32_t lo = vt[key][d >> 1], hi = vt[key + 1][d >> 1];
+        w[k] = (d & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
       }
-      *(u32x4*)(vtile + kc * 1024 + d * 8) = u32x4{w[0], w[1], w[2], w[3]};
+      *(u32x4*)(vtile + piece * 8) = u32x4{w[0], w[1], w[2], w[3]};
     }
   }
 }

@@ -26,7 +26,7 @@ QI_SEG_TEXT, QI_SEG_IMAGE, QI_SEG_TEXT_BIDIR = 0, 1, 2
 QI_EPI_STORE, QI_EPI_STORE_F32, QI_EPI_GATED_RESIDUAL, QI_EPI_SWIGLU, QI_EPI_GELU = 0, 1, 2, 3, 4
 QI_EPI_GATED_RESIDUAL_LINEAR = 5
 QI_MAX_SOURCE_KEYS = 8388607   # keys per source of the bf16 attention (include/qi.h)
-QI_ABI_VERSION = 5             # the qi_version() these bindings are written against
+QI_ABI_VERSION = 6             # the qi_version() these bindings are written against
 QI_NOALLOC_SCRATCH_BYTES = 96 << 20   # scratch array of qi_attn_target_cached_noalloc (include/qi.h)
 QI_ATTN_BLOCK_CAUSAL, QI_ATTN_FULL = 0, 1
 QI_RANGE_Q, QI_RANGE_K, QI_RANGE_V, QI_RANGE_OUT = 1, 2, 4, 8   # range flags of fp16 values (include/qi.h)

@@ -55,13 +55,9 @@ class KVCache:
 
     k, v: [n_layers][n_head][R][128] storage.  fp32 caches hold row-major K and V rows (R =
     p_cap).  fp16 caches (R = p_cap rounded up to a multiple of 64) hold each head's keys in
-    tiles of 64 keys: K as [16 dim chunks][64 key slots][8 dims] with the slots of every 16
-    keys in the order 0-3, 8-11, 4-7, 12-15, V as [8 key chunks][128 dims][8 keys]; k_rows and
-    v_rows return plain [n_head][R][128] rows."""
-
-    # key held by each of the 64 slots of an fp16 K tile (the permutation is its own inverse)
-    SLOT_KEY = [(p & ~15) | ((2 if (p >> 2) & 3 == 1 else 1 if (p >> 2) & 3 == 2 else (p >> 2) & 3) << 2) | (p & 3)
-                for p in range(64)]
+    tiles of 64 keys: K as [16 dim chunks][64 keys][8 dims], V as [2 key halves][4 key
+    groups][128 dims][8 keys] with element e of group g of half c holding key 32c + 16(e // 4) +
+    4g + e % 4; k_rows and v_rows return plain [n_head][R][128] rows."""
 
     def __init__(self, n_layers: int, n_head: int, p_cap: int, io_dtype: int = Q.QI_BF16, device="cuda"):
         self.dtype = Q.QI_F32 if io_dtype == Q.QI_F32 else Q.QI_F16
@@ -78,9 +74,7 @@ class KVCache:
         if self.dtype != Q.QI_F16:
             return k
         H = k.shape[0]
-        t = k.reshape(H, self.rows // 64, 16, 64, 8).permute(0, 1, 3, 2, 4).reshape(H, self.rows // 64, 64, 128)
-        idx = torch.tensor(self.SLOT_KEY, device=k.device)
-        return t[:, :, idx].reshape(H, self.rows, 128)
+        return k.reshape(H, self.rows // 64, 16, 64, 8).permute(0, 1, 3, 2, 4).reshape(H, self.rows, 128)
 
     def v_rows(self, layer: int) -> torch.Tensor:
         """V of one layer as [n_head][R][128] rows (a copy for fp16 caches)."""
@@ -88,7 +82,9 @@ class KVCache:
         if self.dtype != Q.QI_F16:
             return v
         H = v.shape[0]
-        return v.reshape(H, self.rows // 64, 8, 128, 8).permute(0, 1, 2, 4, 3).reshape(H, self.rows, 128)
+        # [tile][half c][group g][dim][e_hi][e_lo] -> key order (c, e_hi, g, e_lo)
+        t = v.reshape(H, self.rows // 64, 2, 4, 128, 2, 4).permute(0, 1, 2, 5, 3, 6, 4)
+        return t.reshape(H, self.rows, 128)
 
 
 def _ws(nbytes: int, device) -> torch.Tensor:

@@ -106,9 +106,9 @@ typedef struct {
  * the size).  K is stored after the optional QK-RMSNorm and the 3D rotation, V as given.
  * QI_F32: both row-major.  QI_F16: each head's keys form R/64 tiles of 64 keys (16 KB each;
  * keys past the stored count in the last tile are zero), laid out in the order the attention
- * kernel's matrix-core operands read them: K as [16 dim chunks][64 key slots][8 dims], where
- * slot p holds key p with rows 4-7 and 8-11 of every 16 exchanged; V as [8 key chunks][128
- * dims][8 keys].  dtype must be QI_F16 for bf16 attention and QI_F32 for fp32 attention.  fp16
+ * kernel's matrix-core operands read them: K as [16 dim chunks][64 keys][8 dims]; V as [2 key
+ * halves][4 key groups][128 dims][8 keys], element e of group g of half c holding key 32c +
+ * 16(e/4) + 4g + e%4.  dtype must be QI_F16 for bf16 attention and QI_F32 for fp32 attention.  fp16
  * holds every bf16 V with 2^-17 <= |v| <= 65280 exactly (smaller values round to the fp16
  * subnormal grid, absolute error <= 2^-25; the next bf16 value, 65536, would overflow, which the
  * calls report through their range flags, QI_RANGE_*), and keeps rotated K with 3 more mantissa
@@ -177,7 +177,8 @@ const char* qi_status_str(int status);
 
 /* Library ABI version (increments on any signature or struct change; 2 added qi_qkv.lse, 3 the
  * range flags and int32_t dtype fields, 4 the allocation-free cached step, 5 fp16 activations
- * (QI_F16 attention I/O, qi_gemm, qi_norm_mod, qi_cast)). */
+ * (QI_F16 attention I/O, qi_gemm, qi_norm_mod, qi_cast), 6 the fp16 cache's tile layout for the
+ * 16 x 16 x 32 matrix-core operands). */
 int qi_version(void);
 
 /* Token counts of a layout: S = all, P = prefix (all but the last segment), T = target.
