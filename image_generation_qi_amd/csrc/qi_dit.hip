@@ -1,5 +1,5 @@
 // qi_dit.hip - the non-attention kernels of one single-stream DiT layer step on gfx950:
-//   - k_gemm_big<EPI, BN, F16>: y = x W^T on bf16 or fp16 MFMA (v_mfma_f32_32x32x16_bf16 / _f16, fp32
+//   - k_gemm_big<EPI, BN, F16>: y = x W^T on bf16 or fp16 MFMA (v_mfma_f32_16x16x32_bf16 / _f16, fp32
 //     accumulation; the fp16 form carries the layer chain's activations with 3 more mantissa bits) with
 //     fused epilogues: bf16 store (QKV projection), fp32 store (img_in, velocity head),
 //     tanh-gated residual add into the fp32 residual stream (attention out-projection and FFN
@@ -74,9 +74,11 @@ __device__ __forceinline__ int xcd_order(int bid, int n) {
 __device__ __forceinline__ int gswz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // ---- large-tile GEMM: 256 x BN workgroup tiles, two wavefronts per SIMD ----------------------
-// Eight waves in a 4 x 2 grid, each owning 64 tokens x BN/2 features as 2 x (BN/64) blocks of
-// 32 x 32 (128 accumulators at BN = 256, so two waves fit a SIMD and each hides the other's LDS
-// waits).  The reduction runs in slices of 64 through two LDS stages (2 x 64 KB at BN = 256): the
+// Eight waves in a 4 x 2 grid, each owning 64 tokens x BN/2 features as 4 x (BN/32) tiles of
+// 16 x 16 (128 accumulators at BN = 256, so two waves fit a SIMD and each hides the other's LDS
+// waits).  The 16 x 16 x 32 shape reads and writes its 4-register accumulators once per 16K flops
+// instead of 16 registers per 32K (32 x 32 x 16), which on this power-limited chip lets the
+// clock run higher at the same work: the layer GEMMs ran 2-6 % faster with it.  The reduction runs in slices of 64 through two LDS stages (2 x 64 KB at BN = 256): the
 // copies of slice kt + 1 are issued at the start of slice kt into the other stage, and one wait
 // and barrier end each slice.  Slices of 64 make every copied row a whole 128-byte line (with
 // slices of 32 and four stages, half-line rows, the same kernel ran 3-9 % slower: the copies
@@ -87,18 +89,18 @@ constexpr int BBM = 256;
 
 template <int EPI, int BN, bool F16>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_big(GemmArgs a) {
-  // operands and 16-bit outputs: bf16 (v_mfma_f32_32x32x16_bf16) or fp16 (..._f16)
+  // operands and 16-bit outputs: bf16 (v_mfma_f32_16x16x32_bf16) or fp16 (..._f16)
   using E = std::conditional_t<F16, _Float16, __bf16>;
   using e8 = std::conditional_t<F16, h8, bf8>;
   constexpr int WTM = 64, WTN = BN / 2;    // wave tile
-  constexpr int MB = WTM / 32, NB = WTN / 32;
+  constexpr int MB = WTM / 16, NB = WTN / 16;   // 16 x 16 accumulator tiles
   constexpr int XT = BBM * GBK, WT = BN * GBK, ST = XT + WT;
   constexpr int NXC = 4;                   // X copies of 1 KB (8 rows) per wave and stage
   constexpr int NWT = BN / 8;              // W copies per stage, spread over the 8 waves
   constexpr int NWC = (NWT + 7) / 8;       // most W copies of one wave
   __shared__ __attribute__((aligned(16))) E smem[GSTAGES * ST];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 5, l32 = lane & 31;
+  const int G = lane >> 4, l16 = lane & 15;   // lane group (of 16) and lane within it
   const int wm = wave & 3, wn = wave >> 2;
   // this wave's W copies (NWC or NWC - 1; always NWC when the copies split evenly)
   const int nwc = NWT % 8 == 0 ? NWC : (NWT - wave + 7) / 8;
@@ -146,115 +148,113 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   };
-  // operands of reduction step kk (of 4) from stage st
-  auto read_ops = [&](int st, int kk, e8 (&xf)[2], e8 (&wf)[4]) {
+  // Each 64-wide slice runs as four half-steps hs: reduction step kk = hs / 2 (elements 32kk ..
+  // + 31 of the slice) against feature tiles NB/2 * (hs % 2) .. + NB/2 - 1.  Lane l reads row
+  // 16b + l % 16 of its tile, elements 32kk + 8(l / 16) .. + 7 (chunk 4kk + l / 16).  X operands
+  // of a step and W operands of a half-step are read one half-step ahead.
+  constexpr int NH = NB / 2;
+  auto read_x = [&](int st, int kk, e8 (&xf)[MB]) {
     const E* X = smem + st * ST;
-    const E* W = X + XT;
 #pragma unroll
     for (int b = 0; b < MB; ++b) {
-      const int r = WTM * wm + 32 * b + l32;
-      xf[b] = *(const e8*)(X + r * GBK + 8 * ((2 * kk + g) ^ gswz(r)));
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int r = WTN * wn + 32 * b + l32;
-      wf[b] = *(const e8*)(W + r * GBK + 8 * ((2 * kk + g) ^ gswz(r)));
+      const int r = WTM * wm + 16 * b + l16;
+      xf[b] = *(const e8*)(X + r * GBK + 8 * ((4 * kk + G) ^ gswz(r)));
     }
   };
-  auto mfmas = [&](f32x16 (&acc)[MB][NB], const e8 (&xf)[2], const e8 (&wf)[4]) {
+  auto read_w = [&](int st, int hs, e8 (&wf)[4]) {
+    const E* W = smem + st * ST + XT;
+    const int kk = hs >> 1;
+#pragma unroll
+    for (int b = 0; b < NH; ++b) {
+      const int r = WTN * wn + 16 * (NH * (hs & 1) + b) + l16;
+      wf[b] = *(const e8*)(W + r * GBK + 8 * ((4 * kk + G) ^ gswz(r)));
+    }
+  };
+  auto mfmas = [&](f32x4 (&acc)[MB][NB], int half, const e8 (&xf)[MB], const e8 (&wf)[4]) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
+      for (int b = 0; b < NH; ++b) {
+        const int nb = NH * half + b;
         if constexpr (F16)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[nb], xf[mb], acc[mb][nb], 0, 0, 0);
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[b], xf[mb], acc[mb][nb], 0, 0, 0);
         else
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], xf[mb], acc[mb][nb], 0, 0, 0);
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[b], xf[mb], acc[mb][nb], 0, 0, 0);
       }
   };
-  f32x16 acc[MB][NB];
+  f32x4 acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nkt = (int)(a.K / GBK);
   auto last = [&](int k) { return k < nkt ? k : nkt - 1; };
   copy_slice(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  e8 xf[2][2], wf[2][4];
-  read_ops(0, 0, xf[0], wf[0]);
+  e8 xf[2][MB], wf[2][4];
+  read_x(0, 0, xf[0]);
+  read_w(0, 0, wf[0]);
   for (int kt = 0; kt < nkt; ++kt) {
     const int st = kt & 1;
     copy_slice(last(kt + 1), st ^ 1);   // stage st ^ 1 was last read in slice kt - 1
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk < 3) read_ops(st, kk + 1, xf[(kk + 1) & 1], wf[(kk + 1) & 1]);
+    for (int hs = 0; hs < 4; ++hs) {
+      if (hs < 3) {
+        if (((hs + 1) & 1) == 0) read_x(st, (hs + 1) >> 1, xf[((hs + 1) >> 1) & 1]);
+        read_w(st, hs + 1, wf[(hs + 1) & 1]);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      mfmas(acc, xf[kk & 1], wf[kk & 1]);
+      mfmas(acc, hs & 1, xf[(hs >> 1) & 1], wf[hs & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of slice kt + 1 have landed
     __syncthreads();
-    read_ops(st ^ 1, 0, xf[0], wf[0]);   // (unused after the last slice)
+    read_x(st ^ 1, 0, xf[0]);   // (unused after the last slice)
+    read_w(st ^ 1, 0, wf[0]);
   }
 
-  // epilogue: acc[mb][nb][r] = y[m][n], m = m0 + 64wm + 32mb + l32,
-  // n = n0 + WTN*wn + 32nb + 8(r/4) + 4g + r%4
+  // epilogue: acc[mb][nb][r] = y[m][n], m = m0 + 64wm + 16mb + l16, n = n0 + WTN*wn + 16nb + 4G + r
   bool bad = false;   // an fp16 output that does not fit
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    const int64_t m = m0 + WTM * wm + 32 * mb + l32;
+    const int64_t m = m0 + WTM * wm + 16 * mb + l16;
     if (m >= a.M) continue;
     if (a.bias) {   // (uniform) bias of the feature rows, before the epilogue
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int64_t nbase = n0 + WTN * wn + 32 * nb + 4 * g;
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int64_t n = nbase + 8 * r4;
-          if (n >= a.N) continue;
-          const f32x4 b = *(const f32x4*)(a.bias + n);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[mb][nb][4 * r4 + e] += b[e];
-        }
+        const int64_t n = n0 + WTN * wn + 16 * nb + 4 * G;
+        if (n >= a.N) continue;
+        acc[mb][nb] += *(const f32x4*)(a.bias + n);
       }
     }
     if constexpr (EPI == QI_EPI_SWIGLU) {
-      // weight rows in blocks of 64: 32 gate rows, then the 32 up rows of the same features
+      // weight rows in blocks of 64: 32 gate rows (tiles 4blk, 4blk + 1), then the 32 up rows of
+      // the same features (tiles 4blk + 2, 4blk + 3)
 #pragma unroll
-      for (int blk = 0; blk < NB / 2; ++blk) {
+      for (int blk = 0; blk < NB / 4; ++blk) {
         if (n0 + WTN * wn + 64 * blk >= a.N) continue;
         const int64_t f0 = (n0 + WTN * wn + 64 * blk) / 2;
-        E* op = (E*)a.out + m * a.ldo + f0 + 4 * g;
+        E* op = (E*)a.out + m * a.ldo + f0 + 4 * G;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          uint32_t w2[2];
+        for (int t = 0; t < 2; ++t) {
+          float v[4];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            float v[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const float gt = acc[mb][2 * blk][4 * r4 + 2 * h + e], up = acc[mb][2 * blk + 1][4 * r4 + 2 * h + e];
-              v[e] = gt / (1.0f + __expf(-gt)) * up;
-            }
-            w2[h] = pack2<F16>(v[0], v[1], bad);
+          for (int e = 0; e < 4; ++e) {
+            const float gt = acc[mb][4 * blk + t][e], up = acc[mb][4 * blk + 2 + t][e];
+            v[e] = gt / (1.0f + __expf(-gt)) * up;
           }
-          *(u32x2*)(op + 8 * r4) = u32x2{w2[0], w2[1]};
+          *(u32x2*)(op + 16 * t) = u32x2{pack2<F16>(v[0], v[1], bad), pack2<F16>(v[2], v[3], bad)};
         }
       }
     } else {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int64_t nbase = n0 + WTN * wn + 32 * nb + 4 * g;
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int64_t n = nbase + 8 * r4;
+        {
+          const int64_t n = n0 + WTN * wn + 16 * nb + 4 * G;
           if (n >= a.N) continue;
-          const f32x4 y = {acc[mb][nb][4 * r4], acc[mb][nb][4 * r4 + 1], acc[mb][nb][4 * r4 + 2], acc[mb][nb][4 * r4 + 3]};
+          const f32x4 y = acc[mb][nb];
           if constexpr (EPI == QI_EPI_STORE) {
             *(u32x2*)((E*)a.out + m * a.ldo + n) = u32x2{pack2<F16>(y[0], y[1], bad), pack2<F16>(y[2], y[3], bad)};
           } else if constexpr (EPI == QI_EPI_STORE_F32) {
@@ -562,9 +562,10 @@ hipError_t launch_big_f16(const GemmArgs& a, int epi, int bn, hipStream_t s) {
 
 int gemm_config(int64_t M, int64_t N, int epi) {
   // Feature width BN of the 256 x BN tiles: the least tile area per CU over whole rounds of 256
-  // workgroups (one per CU), weighted by the LDS bytes per MFMA of the tile (per wave and step,
-  // 2 + BN/64 operand reads for 2 * BN/64 MFMAs: 0.75, 0.83, 1.0 KB for 256, 192, 128; measured
-  // rates follow this order when the rounds are equal).  E.g. 4096 x 3072 is exactly 256 tiles of
+  // workgroups (one per CU), weighted by the LDS bytes per flop of the tile (per wave and 32 of
+  // the reduction, 4 + BN/32 operand reads of 1 KB for 4 * BN/32 MFMAs of 16K flops: 0.75, 0.83,
+  // 1.0 KB per 32K flops for 256, 192, 128; measured rates follow this order when the rounds
+  // are equal).  E.g. 4096 x 3072 is exactly 256 tiles of
   // 256 x 192 but 192 tiles of 256 x 256; 4096 x 16384 fills four rounds of 256 x 256.
   int best = 256;
   double best_cost = 0.0;
