@@ -649,7 +649,7 @@ def main():
                                f"{wl.segments[0].n_tokens} + {len(wl.segments) - 2} refs + target "
                                f"{wl.segments[-1].grid_h}x{wl.segments[-1].grid_w}; {T} queries over {P + T} keys "
                                f"({P} cached); {NL} layers + Euler per step",
-                   "io_dtype": "bf16", "cache_dtype": "f16", "mfma": "v_mfma_f32_32x32x16_f16",
+                   "io_dtype": "bf16", "cache_dtype": "f16", "mfma": "v_mfma_f32_16x16x32_f16",
                    "layers_per_step": NL, "target_tokens": T, "prefix_tokens": P, "heads": H,
                    "pct_of_peak": round(100.0 * value / PEAK_F16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
