@@ -78,6 +78,7 @@ struct AttnArgs {
   float* lse;           // nullable: [n_head][lse_stride], row q of the launch at lse[h * lse_stride + q]
   int64_t lse_stride;
   int32_t n_split, split_tiles, xcd_whole;
+  int32_t pair_tail;   // the runs of each XCD pair share their chunked units (see k_attn_f16)
   uint16_t* part_o;    // [chunked unit][chunk][256 rows][128] fp16: the chunk's output divided by
                        // its own sum, times a power of two per row
   float* part_ml;      // [chunked unit][chunk][256 rows][4]: max, sum, the inverse power of two, 0
