@@ -329,30 +329,44 @@ __global__ __launch_bounds__(256) void k_norm_rows(NormArgs a) {
   const float* sh = a.shift ? a.shift + seg * a.D : nullptr;
   uint16_t* out = (uint16_t*)a.out + m * a.ldo;
   bool bad = false;
+  // the per-feature parameters of four chunks at a time are loaded together (indices clamped into
+  // the row, so the loads need no per-lane branch) before any of them is used: one wait per group
+  // instead of one per parameter and chunk
+  constexpr int GRP = NCH < 4 ? NCH : 4;
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int q = lane + 64 * c;
-    if (q >= nq) continue;
-    const int i = 4 * q;
-    float y[4];
+  for (int c0 = 0; c0 < NCH; c0 += GRP) {
+    f32x4 wv[GRP], sv[GRP], hv[GRP];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) y[e] = (v[c][e] - mu) * rr;
-    if (a.w) {
-      const f32x4 w = *(const f32x4*)(a.w + i);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] *= w[e] + 1.0f;
+    for (int k = 0; k < GRP; ++k) {
+      const int q = lane + 64 * (c0 + k);
+      const int i = 4 * (q < nq ? q : nq - 1);
+      if (a.w) wv[k] = *(const f32x4*)(a.w + i);
+      if (sc) sv[k] = *(const f32x4*)(sc + i);
+      if (sh) hv[k] = *(const f32x4*)(sh + i);
     }
-    if (sc) {
-      const f32x4 t = *(const f32x4*)(sc + i);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] *= 1.0f + t[e];
-    }
-    if (sh) {
-      const f32x4 t = *(const f32x4*)(sh + i);
+    for (int k = 0; k < GRP; ++k) {
+      const int c = c0 + k;
+      const int q = lane + 64 * c;
+      if (q >= nq) continue;
+      const int i = 4 * q;
+      float y[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] += t[e];
+      for (int e = 0; e < 4; ++e) y[e] = (v[c][e] - mu) * rr;
+      if (a.w) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] *= wv[k][e] + 1.0f;
+      }
+      if (sc) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] *= 1.0f + sv[k][e];
+      }
+      if (sh) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] += hv[k][e];
+      }
+      *(u32x2*)(out + i) = u32x2{pack2<F16>(y[0], y[1], bad), pack2<F16>(y[2], y[3], bad)};
     }
-    *(u32x2*)(out + i) = u32x2{pack2<F16>(y[0], y[1], bad), pack2<F16>(y[2], y[3], bad)};
   }
   if (F16 && a.flags && bad) atomicOr(a.flags, QI_RANGE_OUT);
 }
@@ -599,6 +613,11 @@ hipError_t launch_zc_norm_mod(const NormArgs& a, bool f16, hipStream_t s) {
       hipLaunchKernelGGL((k_norm_rows<4, true>), dim3(rows4), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL((k_norm_rows<4, false>), dim3(rows4), dim3(256), 0, s, a);
+  } else if (a.D <= 3072) {
+    if (f16)
+      hipLaunchKernelGGL((k_norm_rows<12, true>), dim3(rows4), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_norm_rows<12, false>), dim3(rows4), dim3(256), 0, s, a);
   } else if (a.D <= 4096) {
     if (f16)
       hipLaunchKernelGGL((k_norm_rows<16, true>), dim3(rows4), dim3(256), 0, s, a);
