@@ -18,8 +18,8 @@ inline int64_t rows64(int64_t n) { return (n + 63) / 64 * 64; }
 // K/V preparation.  fp32 outputs: x (K) rows go to dst[head][row][128] with dst_tok_stride =
 // 128, v rows to dst_v the same way.  fp16 outputs (bf16 inputs): both go to 64-key tiles of
 // 16 KB per head (dst_head_stride apart, a multiple of 8192 elements), K as [16 dim chunks][64
-// key slots, rows 4-7 and 8-11 of every 16 exchanged][8 dims], V as [8 key chunks][128 dims][8
-// keys]; keys of the last tile past n_tok are zero.
+// keys][8 dims], V as [2 key halves][4 key groups][128 dims][8 keys] (element e of group g of half
+// c holds key 32c + 16(e / 4) + 4g + e % 4); keys of the last tile past n_tok are zero.
 struct PrepArgs {
   const void* x;
   int64_t x_tok_stride;
