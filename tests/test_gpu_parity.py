@@ -405,7 +405,7 @@ def test_full_attention_full_size_sampled(name):
 # ---------------------------------------------------------------------------------------------
 # the work schedule: query-tile unit counts that take each path of the per-XCD schedule
 # (runs of unequal length with idle blocks, whole rounds plus chunked remainders, remainders
-# run whole, many chunks per unit), on sampled rows including the first and last row of every
+# run whole, many chunks per unit, chunks shared by an XCD pair), on sampled rows including the first and last row of every
 # query tile; the step-1 target rows of the same shapes equal the cached step bit for bit
 # ---------------------------------------------------------------------------------------------
 
@@ -416,6 +416,9 @@ SCHED_CASES = [
     ("u270", (60, 64), 18),           # 270 units: 32 whole per run, then runs of 2 and 1 in 8 chunks
     ("u505_whole_tail", (101, 256), 5),   # 505 units: 32 whole, then 32 or 31 more run whole
     ("u567", (115, 180), 7),          # 567 units: 64 whole per run, then 7 each in 4 chunks
+    # 128 units, no whole rounds: the runs of each XCD pair share their 32 units' two key chunks,
+    # the first (31 of 65 key tiles) on the odd run; last query tile 129 rows, last key tile 1 key
+    ("u128_paired", (63, 63), 8),
 ]
 
 
