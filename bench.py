@@ -611,7 +611,7 @@ def main():
     log(f"timed {args.steps} steps in {wall:.3f} s; attention kernel {kern_ms / max(n_launch, 1):.4f} ms/launch")
 
     flops_launch = 4.0 * 128 * H * T * (P + T)
-    n_chunks, whole_per_xcd, chunked_tiles = Q.qi_attn_schedule(T, H)
+    n_chunks, whole_per_xcd, chunked_tiles = Q.qi_attn_schedule(T, H, P, T)
     value = flops_launch * NL * args.steps / wall / 1e12
     avg_ms = kern_ms / max(n_launch, 1)
     achieved = flops_launch / (avg_ms * 1e-3) / 1e12

@@ -148,7 +148,8 @@ AttnArgs attn_args(const qi_qkv* io, const qi_qkprep* prep, float scale) {
 }
 
 // The chunked schedule for a launch over a.n_q rows of units of equal cost, with its
-// partial-output buffers placed at `base` in the workspace (bf16 path only).
+// partial-output buffers placed at `base` in the workspace (bf16 path only).  a.nA and a.nB must
+// be set: the chunk count depends on the key tiles, exactly as in launch_attn_f16.
 void set_partials(AttnArgs& a, char* base, int32_t dtype) {
   a.xcd_sched = 0;
   a.reverse_qt = 0;
@@ -156,7 +157,7 @@ void set_partials(AttnArgs& a, char* base, int32_t dtype) {
   a.part_o = nullptr;
   a.part_ml = nullptr;
   if (dtype == QI_F32) return;
-  const AttnSched sc = attn_f16_schedule(a.n_q, a.n_head);
+  const AttnSched sc = attn_f16_schedule(a.n_q, a.n_head, attn_key_tiles(a.nA, a.nB));
   a.xcd_sched = 1;
   a.part_o = (uint16_t*)base;
   a.part_ml = (float*)(base + (int64_t)sc.tail_units * sc.n_split * kAttnF16TileQ * QI_HEAD_DIM * (int64_t)sizeof(uint16_t));
@@ -377,7 +378,6 @@ int run_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvcache*
     return st;
   AttnArgs a = attn_args(io, prep, scale);
   a.masked = 0;
-  set_partials(a, wk + 2 * (int64_t)io->n_head * RB * QI_HEAD_DIM * es, io->dtype);
   a.kA = cache_layer(cache->k, cache, layer);
   a.vA = cache_layer(cache->v, cache, layer);
   a.a_head_stride = cache_rows(cache) * QI_HEAD_DIM;
@@ -387,6 +387,7 @@ int run_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvcache*
   a.b_head_stride = RB * QI_HEAD_DIM;
   a.nB = T;
   a.q_row0 = P;
+  set_partials(a, wk + 2 * (int64_t)io->n_head * RB * QI_HEAD_DIM * es, io->dtype);   // after nA, nB
   return run_attn(a, io->dtype, s);
 }
 

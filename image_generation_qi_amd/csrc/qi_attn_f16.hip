@@ -709,29 +709,38 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ pa
 
 }  // namespace
 
-AttnSched attn_f16_schedule(int64_t n_q, int32_t n_head) {
+AttnSched attn_f16_schedule(int64_t n_q, int32_t n_head, int64_t key_tiles) {
   // For query-tile units of equal cost.  One workgroup fills a CU; the 256 CUs are 8 XCDs of 32,
   // and block b runs on XCD b % 8.  The U units are spread over the 8 XCDs (the first U % 8 get
   // one more), each XCD runs whole rounds of whole units (one per CU) and cuts only its
-  // remaining units into s key chunks, s = 1 .. 8 chosen for the shortest tail (each chunk
-  // beyond the first charged 1 % of a unit, chunking at all 3 %).  The 4,096-token target at 24
-  // heads (384 units, 48 per XCD) runs 32 whole units and 16 units in 2 chunks per XCD: every
-  // CU does one whole unit and one half.
+  // remaining units into s key chunks, s = 1 .. 8 chosen for the shortest tail: the rounds the
+  // chunks take, each chunk 1/s of a unit, plus per round a chunk's fixed prologue and epilogue
+  // (about 8.5 key tiles, so 8.5 / key_tiles of a unit; not charged when key_tiles is 0), plus 1 %
+  // per chunk and 3 % for chunking at all for the merge.  The chunk count never exceeds the one
+  // chosen without the fixed cost, so workspaces sized for key_tiles = 0 always suffice.  The
+  // 4,096-token target at 24 heads (384 units, 48 per XCD) runs 32 whole units and 16 units in 2
+  // chunks per XCD: every CU does one whole unit and one half.
   constexpr int64_t per_xcd = 32;
   AttnSched r{1, 0, 0, 0};
   const int64_t units = (n_q + BM - 1) / BM * n_head;
   if (units <= 0) return r;
   const int64_t u8 = units / 8, wx = per_xcd * (u8 / per_xcd);
   const int64_t rmax = u8 - wx + (units % 8 != 0);   // remaining units of the longest run
-  int best = 1;
-  double best_t = 1e30;
-  for (int s = 1; s <= 8 && rmax > 0; ++s) {
-    const double t = (double)((rmax * s + per_xcd - 1) / per_xcd) / s + 0.01 * s + (s > 1 ? 0.03 : 0.0);
-    if (t < best_t - 1e-9) {
-      best_t = t;
-      best = s;
+  auto best_split = [&](double fixed, int cap) {
+    int best = 1;
+    double best_t = 1e30;
+    for (int s = 1; s <= cap && rmax > 0; ++s) {
+      const int64_t rounds = (rmax * s + per_xcd - 1) / per_xcd;
+      const double t = (double)rounds / s + fixed * (double)rounds + 0.01 * s + (s > 1 ? 0.03 : 0.0);
+      if (t < best_t - 1e-9) {
+        best_t = t;
+        best = s;
+      }
     }
-  }
+    return best;
+  };
+  int best = best_split(0.0, 8);
+  if (key_tiles > 0) best = best_split(8.5 / (double)key_tiles, best);
   r.n_split = best;
   r.xcd_whole = (int32_t)wx;
   r.tail_units = best > 1 ? (int32_t)(units - 8 * wx) : 0;
@@ -740,7 +749,7 @@ AttnSched attn_f16_schedule(int64_t n_q, int32_t n_head) {
 }
 
 int64_t attn_f16_partial_bytes(int64_t n_q, int32_t n_head) {
-  const AttnSched sc = attn_f16_schedule(n_q, n_head);
+  const AttnSched sc = attn_f16_schedule(n_q, n_head, 0);
   return (int64_t)sc.tail_units * sc.n_split * BM * (HD * (int64_t)sizeof(uint16_t) + 4 * (int64_t)sizeof(float));
 }
 
@@ -751,7 +760,7 @@ hipError_t launch_attn_f16(const AttnArgs& a_in, hipStream_t s) {
   int64_t blocks = n_qt * a.n_head;
   int32_t n_tail = 0;
   if (a.xcd_sched) {
-    const AttnSched sc = attn_f16_schedule(a.n_q, a.n_head);
+    const AttnSched sc = attn_f16_schedule(a.n_q, a.n_head, kt_total);
     a.n_split = sc.n_split;
     a.xcd_whole = sc.xcd_whole;
     a.reverse_qt = 0;

@@ -100,7 +100,7 @@ const char* qi_status_str(int status) {
   }
 }
 
-int qi_version(void) { return 6; }
+int qi_version(void) { return 7; }
 
 int qi_layout_tokens(const qi_layout* layout, int64_t* S, int64_t* P, int64_t* T) {
   LayoutInfo li;
@@ -202,10 +202,11 @@ int qi_attn_tile_shape(int32_t dtype, int32_t* tile_q, int32_t* tile_k) {
   return QI_OK;
 }
 
-int qi_attn_schedule(int64_t n_q, int32_t n_head, int32_t* key_chunks, int32_t* whole_per_xcd,
-                     int32_t* chunked_tiles) {
-  if (n_q < 0 || n_head < 1 || !key_chunks || !whole_per_xcd || !chunked_tiles) return QI_ERR_ARG;
-  const AttnSched sc = attn_f16_schedule(n_q, n_head);
+int qi_attn_schedule(int64_t n_q, int32_t n_head, int64_t n_keys_a, int64_t n_keys_b, int32_t* key_chunks,
+                     int32_t* whole_per_xcd, int32_t* chunked_tiles) {
+  if (n_q < 0 || n_head < 1 || n_keys_a < 0 || n_keys_b < 0 || !key_chunks || !whole_per_xcd || !chunked_tiles)
+    return QI_ERR_ARG;
+  const AttnSched sc = attn_f16_schedule(n_q, n_head, attn_key_tiles(n_keys_a, n_keys_b));
   *key_chunks = sc.n_split;
   *whole_per_xcd = sc.xcd_whole;
   *chunked_tiles = sc.tail_units;

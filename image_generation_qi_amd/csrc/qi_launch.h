@@ -94,7 +94,11 @@ struct AttnSched {
   int32_t tail_units;   // chunked units over all runs (0 when n_split == 1)
   int64_t blocks;       // workgroups (8 runs of equal length; surplus blocks exit at once)
 };
-AttnSched attn_f16_schedule(int64_t n_q, int32_t n_head);
+// key_tiles: the key tiles every query tile of the launch reads (0: not known; the chunk count is
+// then the largest the schedule takes for any key count).
+AttnSched attn_f16_schedule(int64_t n_q, int32_t n_head, int64_t key_tiles);
+// Key tiles of a launch over key sources of nA and nB keys (tiled separately).
+inline int64_t attn_key_tiles(int64_t nA, int64_t nB) { return (nA + 63) / 64 + (nB + 63) / 64; }
 
 // Query rows per workgroup of the fp16 path (the tile height reported by qi_attn_tile_shape).
 constexpr int kAttnF16TileQ = 256;

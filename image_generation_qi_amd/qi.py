@@ -26,7 +26,7 @@ QI_SEG_TEXT, QI_SEG_IMAGE, QI_SEG_TEXT_BIDIR = 0, 1, 2
 QI_EPI_STORE, QI_EPI_STORE_F32, QI_EPI_GATED_RESIDUAL, QI_EPI_SWIGLU, QI_EPI_GELU = 0, 1, 2, 3, 4
 QI_EPI_GATED_RESIDUAL_LINEAR = 5
 QI_MAX_SOURCE_KEYS = 8388607   # keys per source of the bf16 attention (include/qi.h)
-QI_ABI_VERSION = 6             # the qi_version() these bindings are written against
+QI_ABI_VERSION = 7             # the qi_version() these bindings are written against
 QI_NOALLOC_SCRATCH_BYTES = 96 << 20   # scratch array of qi_attn_target_cached_noalloc (include/qi.h)
 QI_ATTN_BLOCK_CAUSAL, QI_ATTN_FULL = 0, 1
 QI_RANGE_Q, QI_RANGE_K, QI_RANGE_V, QI_RANGE_OUT = 1, 2, 4, 8   # range flags of fp16 values (include/qi.h)
@@ -83,7 +83,8 @@ _SIGS = {
     "qi_rope3d_tables": (c_int, [POINTER(qi_layout), c_void_p, c_void_p]),
     "qi_blockmap": (c_int, [POINTER(qi_layout), c_int32, c_int32, c_void_p]),
     "qi_attn_tile_shape": (c_int, [c_int, POINTER(c_int32), POINTER(c_int32)]),
-    "qi_attn_schedule": (c_int, [c_int64, c_int32, POINTER(c_int32), POINTER(c_int32), POINTER(c_int32)]),
+    "qi_attn_schedule": (c_int, [c_int64, c_int32, c_int64, c_int64, POINTER(c_int32), POINTER(c_int32),
+                                 POINTER(c_int32)]),
     "qi_attn_full_workspace_bytes": (c_int64, [POINTER(qi_layout), c_int, c_int32]),
     "qi_attn_cached_workspace_bytes": (c_int64, [c_int, c_int64, c_int32]),
     "qi_kvcache_bytes": (c_int64, [c_int, c_int32, c_int32, c_int64]),
@@ -245,10 +246,13 @@ def qi_attn_tile_shape(dtype: int):
     return tq.value, tk.value
 
 
-def qi_attn_schedule(n_q: int, n_head: int):
-    """(key chunks per cut query tile, whole tiles per XCD run, cut tiles) of a bf16 launch."""
+def qi_attn_schedule(n_q: int, n_head: int, n_keys_a: int = 0, n_keys_b: int = 0):
+    """(key chunks per cut query tile, whole tiles per XCD run, cut tiles) of a bf16 launch over
+    key sources of n_keys_a and n_keys_b keys (0, 0: the key-independent bound the workspace
+    queries size for)."""
     s, w, c = c_int32(), c_int32(), c_int32()
-    check(lib().qi_attn_schedule(n_q, n_head, ctypes.byref(s), ctypes.byref(w), ctypes.byref(c)), "qi_attn_schedule")
+    check(lib().qi_attn_schedule(n_q, n_head, n_keys_a, n_keys_b, ctypes.byref(s), ctypes.byref(w), ctypes.byref(c)),
+          "qi_attn_schedule")
     return s.value, w.value, c.value
 
 

@@ -178,7 +178,7 @@ const char* qi_status_str(int status);
 /* Library ABI version (increments on any signature or struct change; 2 added qi_qkv.lse, 3 the
  * range flags and int32_t dtype fields, 4 the allocation-free cached step, 5 fp16 activations
  * (QI_F16 attention I/O, qi_gemm, qi_norm_mod, qi_cast), 6 the fp16 cache's tile layout for the
- * 16 x 16 x 32 matrix-core operands). */
+ * 16 x 16 x 32 matrix-core operands, 7 the key counts of qi_attn_schedule). */
 int qi_version(void);
 
 /* Token counts of a layout: S = all, P = prefix (all but the last segment), T = target.
@@ -206,14 +206,18 @@ int qi_blockmap(const qi_layout* layout, int32_t tile_q, int32_t tile_k, uint8_t
 int qi_attn_tile_shape(int32_t dtype, int32_t* tile_q, int32_t* tile_k);
 
 /* Work schedule of a bf16 attention launch over n_q query rows and n_head heads whose query tiles
- * all see the same keys (every cached step, the target rows of step 1, unmasked layouts): the
+ * all see the same keys (every cached step, the target rows of step 1, unmasked layouts), with
+ * key sources of n_keys_a and n_keys_b keys (prefix and target; each tiled by 64 keys): the
  * ceil(n_q / 256) * n_head query tiles are spread over the 8 XCDs; each XCD runs whole rounds of
- * one tile per CU and cuts only its remaining tiles into key chunks, merged afterwards.  Host
- * query (no GPU): *key_chunks = chunks per cut tile (1: no tile is cut), *whole_per_xcd = whole
- * tiles at the start of each XCD's run, *chunked_tiles = cut tiles over all XCDs.  QI_OK, or
- * QI_ERR_ARG for n_q < 0, n_head < 1 or a null output pointer. */
-int qi_attn_schedule(int64_t n_q, int32_t n_head, int32_t* key_chunks, int32_t* whole_per_xcd,
-                     int32_t* chunked_tiles);
+ * one tile per CU and cuts only its remaining tiles into key chunks, merged afterwards.  The chunk
+ * count weighs the rounds the chunks take against a fixed cost per chunk round of about 8.5 key
+ * tiles, and never exceeds the count for n_keys_a = n_keys_b = 0 (no fixed cost charged), which
+ * is the one the workspace queries size for.  Host query (no GPU): *key_chunks = chunks per cut
+ * tile (1: no tile is cut), *whole_per_xcd = whole tiles at the start of each XCD's run,
+ * *chunked_tiles = cut tiles over all XCDs.  QI_OK, or QI_ERR_ARG for n_q < 0, n_head < 1, a
+ * negative key count or a null output pointer. */
+int qi_attn_schedule(int64_t n_q, int32_t n_head, int64_t n_keys_a, int64_t n_keys_b, int32_t* key_chunks,
+                     int32_t* whole_per_xcd, int32_t* chunked_tiles);
 
 /* Workspace bytes needed by qi_attn_blockcausal_full for `layout` (with or without a cache) and
  * by qi_attn_target_cached for T target tokens: prepared K/V rows plus, for bf16, the partial

@@ -96,7 +96,7 @@ def headline_heads():
     """(whole head, chunked head) of the 4,096-query, 24-head launch: 384 query tiles, 48 per
     XCD run; a run's first 32 tiles (two heads) run whole and its last 16 (the third head) in
     two key chunks."""
-    assert Q.qi_attn_schedule(4096, 24) == (2, 32, 128)
+    assert Q.qi_attn_schedule(4096, 24, 17408, 4096) == (2, 32, 128)
     return 0, 2
 
 

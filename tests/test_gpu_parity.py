@@ -419,6 +419,9 @@ SCHED_CASES = [
     # 128 units, no whole rounds: the runs of each XCD pair share their 32 units' two key chunks,
     # the first (31 of 65 key tiles) on the odd run; last query tile 129 rows, last key tile 1 key
     ("u128_paired", (63, 63), 8),
+    # 96 units over 18 key tiles: 2 key chunks in one round (5 chunks in two rounds without the
+    # per-chunk cost), the runs of each XCD pair sharing them; last query tile 255 rows
+    ("u96_key_aware", (31, 33), 24),
 ]
 
 
@@ -429,7 +432,10 @@ def test_schedule_unit_counts(name, grid, heads):
     c = Case(wl)
     P, T = c.P, c.T
     n_qt = (T + 255) // 256
-    say(f"schedule {name}: T={T} heads={heads} units={n_qt * heads}")
+    sched = Q.qi_attn_schedule(T, heads, P, T)
+    say(f"schedule {name}: T={T} heads={heads} units={n_qt * heads} schedule={sched}")
+    if name == "u96_key_aware":
+        assert sched == (2, 0, 96) and Q.qi_attn_schedule(T, heads) == (5, 0, 96)
     L, att = make(wl)
     cache = rt.KVCache(1, heads, P, Q.QI_BF16, DEV)
     o1 = att.full(c.qd, c.kd, c.vd, cache=cache)

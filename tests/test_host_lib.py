@@ -157,6 +157,12 @@ def test_tile_shape_and_sizes():
     assert Q.qi_attn_schedule(8704, 24) == (5, 96, 48)      # 816 tiles: 102 per XCD
     assert Q.qi_attn_schedule(101 * 256, 5) == (1, 32, 0)   # 505 tiles: the remaining 32 / 31 run whole
     assert Q.qi_attn_schedule(0, 24) == (1, 0, 0)
+    # with the key counts: a chunk round costs about 8.5 key tiles more, so short key ranges take
+    # fewer chunks (never more than the key-independent count the workspaces are sized for)
+    assert Q.qi_attn_schedule(4096, 24, 17408, 4096) == (2, 32, 128)   # 336 key tiles: unchanged
+    assert Q.qi_attn_schedule(1024, 24, 1280, 1024) == (2, 0, 96)      # 36 key tiles: 1 round of 2 chunks, not 2 of 5
+    assert Q.qi_attn_schedule(512, 24, 0, 512) == (5, 0, 48)           # 8 key tiles: 5 chunks still fit one round
+    assert Q.qi_attn_schedule(1024, 24, 0, 0) == Q.qi_attn_schedule(1024, 24)
     L3 = Q.make_layout(qin.WORKLOADS["txt1024_4ref64_tgt64"].segments)
     PART = 256 * (128 * 2 + 4 * 4)   # partials of one chunk of one query tile: 256 rows x (128 fp16 + fp32 max, sum, scale, pad)
     # 4096-token target: 16 x 24 = 384 query tiles (48 per XCD): per XCD 32 whole, 16 in 2 key
@@ -318,9 +324,12 @@ def test_other_entry_points_reject():
     assert Q.qi_rope3d_positions(L, None) == Q.QI_ERR_ARG
     assert Q.qi_blockmap(L, 0, 64, np.zeros(4, np.uint8)) == Q.QI_ERR_ARG
     assert Q.lib().qi_attn_tile_shape(9, ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32())) == Q.QI_ERR_DTYPE
-    assert Q.lib().qi_attn_schedule(-1, 24, ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32())) == Q.QI_ERR_ARG
-    assert Q.lib().qi_attn_schedule(4096, 0, ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32())) == Q.QI_ERR_ARG
-    assert Q.lib().qi_attn_schedule(4096, 24, None, ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32())) == Q.QI_ERR_ARG
+    i32 = lambda: ctypes.byref(ctypes.c_int32())
+    assert Q.lib().qi_attn_schedule(-1, 24, 0, 0, i32(), i32(), i32()) == Q.QI_ERR_ARG
+    assert Q.lib().qi_attn_schedule(4096, 0, 0, 0, i32(), i32(), i32()) == Q.QI_ERR_ARG
+    assert Q.lib().qi_attn_schedule(4096, 24, -1, 0, i32(), i32(), i32()) == Q.QI_ERR_ARG
+    assert Q.lib().qi_attn_schedule(4096, 24, 0, -64, i32(), i32(), i32()) == Q.QI_ERR_ARG
+    assert Q.lib().qi_attn_schedule(4096, 24, 0, 0, None, i32(), i32()) == Q.QI_ERR_ARG
 
 
 def test_full_attention_layout_maps_and_positions():
@@ -423,3 +432,9 @@ def test_schedule_invariants_over_shapes():
             assert chunks == 1
         rows = -(-n_q // 64) * 64
         assert Q.qi_attn_cached_workspace_bytes(Q.QI_BF16, n_q, heads) == 2 * heads * rows * 128 * 2 + chunked * chunks * PART, (n_q, heads)
+        # with key counts: the same whole rounds, at most as many chunks, partials within the workspace's
+        for n_keys_a in (0, 64, 1280, int(rng.integers(0, 40000))):
+            kc, kw, kch = Q.qi_attn_schedule(n_q, heads, n_keys_a, n_q)
+            assert 1 <= kc <= chunks and kw == whole, (n_q, heads, n_keys_a)
+            assert kch == (rest if kc > 1 else 0), (n_q, heads, n_keys_a)
+            assert kch * kc <= chunked * chunks, (n_q, heads, n_keys_a)
