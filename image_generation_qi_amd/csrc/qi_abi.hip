@@ -464,7 +464,7 @@ int qi_euler_step(float* x, const void* v, int32_t v_dtype, int64_t n, float sig
 
 static int gemm_impl(const void* x, int64_t ldx, const void* w, const float* bias, void* out, int64_t ldo,
                      int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t epilogue, const float* gate, int64_t row0,
-                     int64_t P, int32_t tile_n, uint32_t* flags, void* stream) {
+                     int64_t P, int32_t tile_n, uint32_t* flags, void* stream, const qi_norm_fold* fold = nullptr) {
   clear_hip_error();
   if (!x || !w || !out) return QI_ERR_ARG;
   if (dtype != QI_BF16 && dtype != QI_F16) return QI_ERR_DTYPE;
@@ -479,9 +479,63 @@ static int gemm_impl(const void* x, int64_t ldx, const void* w, const float* bia
   if (!aligned16(x) || !aligned16(w) || !aligned16(out) || !aligned16(gate) || !aligned16(bias) || (ldx % 8) ||
       (ldo % 8) || (reinterpret_cast<uintptr_t>(flags) & 3))
     return QI_ERR_ALIGN;
-  if (M == 0) return QI_OK;
   GemmArgs a{x, ldx, w, out, ldo, M, N, K, gate, row0, P, bias, flags};
+  if (fold) {
+    const bool gated = epilogue == QI_EPI_GATED_RESIDUAL || epilogue == QI_EPI_GATED_RESIDUAL_LINEAR;
+    if (fold->sumsq && (!(fold->eps >= 0.f) || !std::isfinite(fold->eps))) return QI_ERR_ARG;
+    if (fold->xc && (!gated || !fold->sumsq_out)) return QI_ERR_ARG;
+    if (!fold->xc && (fold->sumsq_out || fold->next_w || fold->next_scale)) return QI_ERR_ARG;
+    if (fold->xc && fold->ldxc < N) return QI_ERR_SHAPE;
+    if (fold->xc && tile_n != 0 && tile_n != 192) return QI_ERR_ARG;   // the producing side runs 256 x 192 tiles
+    if (!aligned16(fold->sumsq) || !aligned16(fold->bias_t) || !aligned16(fold->xc) || !aligned16(fold->next_w) ||
+        !aligned16(fold->next_scale) || (reinterpret_cast<uintptr_t>(fold->sumsq_out) & 3) ||
+        (fold->xc && (fold->ldxc % 8)))
+      return QI_ERR_ALIGN;
+    a.bias_t = fold->bias_t;
+    a.sumsq = fold->sumsq;
+    a.eps = fold->eps;
+    a.xc = fold->xc;
+    a.ldxc = fold->ldxc;
+    a.nw = fold->next_w;
+    a.nscale = fold->next_scale;
+    a.sumsq_out = fold->sumsq_out;
+  }
+  if (M == 0) return QI_OK;
   return launch_status(launch_gemm(a, epilogue, tile_n, dtype == QI_F16, (hipStream_t)stream));
+}
+
+int qi_gemm_norm_fold(const void* x, int64_t ldx, const void* w, const float* bias, void* out, int64_t ldo,
+                      int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t epilogue, const float* gate,
+                      int64_t row0, int64_t P, int32_t tile_n, const qi_norm_fold* fold, uint32_t* range_flags,
+                      void* stream) {
+  return gemm_impl(x, ldx, w, bias, out, ldo, M, N, K, dtype, epilogue, gate, row0, P, tile_n, range_flags, stream,
+                   fold);
+}
+
+int qi_norm_fold_rows(const float* x, int64_t ldx, void* xc, int64_t ldxc, float* sumsq_out, int64_t M, int32_t D,
+                      const float* w, const float* scale, int64_t row0, int64_t P, int32_t dtype,
+                      uint32_t* range_flags, void* stream) {
+  clear_hip_error();
+  if (!x || !xc || !sumsq_out) return QI_ERR_ARG;
+  if (dtype != QI_BF16 && dtype != QI_F16) return QI_ERR_DTYPE;
+  if (M < 0 || M > INT32_MAX || D < 32 || (D % 32) || D > 4096 || ldx < D || ldxc < D) return QI_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(scale) || (ldx % 4) || (ldxc % 4) ||
+      (reinterpret_cast<uintptr_t>(xc) & 7) || (reinterpret_cast<uintptr_t>(sumsq_out) & 3) ||
+      (reinterpret_cast<uintptr_t>(range_flags) & 3))
+    return QI_ERR_ALIGN;
+  if (M == 0) return QI_OK;
+  NormArgs a{x, ldx, xc, ldxc, M, D, w, scale, nullptr, row0, P, 0.f, 0, range_flags, sumsq_out};
+  return launch_status(launch_zc_norm_mod(a, dtype == QI_F16, (hipStream_t)stream));
+}
+
+int qi_linear_multi(const float* x, int32_t n_vec, int32_t I, const void* w, int32_t w_dtype, int32_t O, float* y,
+                    void* stream) {
+  clear_hip_error();
+  if (!x || !w || !y) return QI_ERR_ARG;
+  if (w_dtype != QI_BF16 && w_dtype != QI_F16) return QI_ERR_DTYPE;
+  if (n_vec < 1 || n_vec > 16 || I < 8 || (I % 8) || O < 0 || (int64_t)O * I > (1ll << 40)) return QI_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || (reinterpret_cast<uintptr_t>(y) & 3)) return QI_ERR_ALIGN;
+  return launch_status(launch_linear_multi(x, n_vec, I, w, w_dtype == QI_F16, O, y, (hipStream_t)stream));
 }
 
 int qi_gemm(const void* x, int64_t ldx, const void* w, const float* bias, void* out, int64_t ldo, int64_t M, int64_t N,
@@ -519,7 +573,7 @@ int qi_norm_mod(const float* x, int64_t ldx, void* out, int64_t ldo, int64_t M, 
       (reinterpret_cast<uintptr_t>(out) & 7) || (reinterpret_cast<uintptr_t>(range_flags) & 3))
     return QI_ERR_ALIGN;
   if (M == 0) return QI_OK;
-  NormArgs a{x, ldx, out, ldo, M, D, w, scale, shift, row0, P, eps, center, range_flags};
+  NormArgs a{x, ldx, out, ldo, M, D, w, scale, shift, row0, P, eps, center, range_flags, nullptr};
   return launch_status(launch_zc_norm_mod(a, out_dtype == QI_F16, (hipStream_t)stream));
 }
 

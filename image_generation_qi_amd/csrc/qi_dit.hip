@@ -36,6 +36,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
 constexpr int GBK = 64;    // reduction slice per LDS stage: copied rows are whole 128-byte lines
+// Norm fold: a row's sum of squares is carried as partial sums over each FOLD_W features (the
+// feature range of one wave of a producing 256 x 192 tile), ceil(D / FOLD_W) per row
+constexpr int FOLD_W = 96;
 constexpr int GSTAGES = 2; // LDS stages (2 x 64 KB at BN = 256)
 
 __device__ __forceinline__ uint32_t to_bf16(float f) {
@@ -98,7 +101,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int NXC = 4;                   // X copies of 1 KB (8 rows) per wave and stage
   constexpr int NWT = BN / 8;              // W copies per stage, spread over the 8 waves
   constexpr int NWC = (NWT + 7) / 8;       // most W copies of one wave
-  __shared__ __attribute__((aligned(16))) E smem[GSTAGES * ST];
+  // The stages, then fp32 per-row and per-feature epilogue values: rr_s [256] the rows' rsqrt(mean
+  // square + eps) (norm fold), bs_s [2][BN] the bias of each row class, gt_s [2][BN] the gate of
+  // each row class (tanh applied once per feature, not per output), cf_s [2][BN] the next norm's
+  // (1 + w)(1 + scale) (norm fold).  Read from LDS in the epilogue, these cost no memory latency
+  // there.  One
+  // LDS object: with a second one the compiler no longer separates the stage being read from the
+  // one being copied into and waits for the copies before every slice's first MFMA (28 % slower).
+  constexpr bool GATED = EPI == QI_EPI_GATED_RESIDUAL || EPI == QI_EPI_GATED_RESIDUAL_LINEAR;
+  constexpr int EXTRA = BBM + 2 * BN + (GATED ? 4 * BN : 0);   // floats after the stages
+  __shared__ __attribute__((aligned(16))) E smem[GSTAGES * ST + 2 * EXTRA];
+  float* const rr_s = (float*)(smem + GSTAGES * ST);
+  float* const bs_s = rr_s + BBM;      // [2][BN] the bias of each row class
+  float* const gt_s = bs_s + 2 * BN;
+  float* const cf_s = gt_s + 2 * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = lane >> 4, l16 = lane & 15;   // lane group (of 16) and lane within it
   const int wm = wave & 3, wn = wave >> 2;
@@ -191,6 +207,65 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int nkt = (int)(a.K / GBK);
   auto last = [&](int k) { return k < nkt ? k : nkt - 1; };
   copy_slice(0, 0);
+  // Epilogue values into LDS while the first slice's copies are in flight.  Every load is issued
+  // before any result is used, so the prologue waits for memory once.
+  //  - norm fold: a row's mean square from its ceil(K / 96) partial sums, two threads per row, each
+  //    summing its half in order (the pair's sum is the same bits on both);
+  //  - the bias of each row class and, for the gated epilogues, the gate (tanh applied here, once
+  //    per feature) and the next norm's (1 + w)(1 + scale), for the tile's BN features (2 BN <=
+  //    512 values: one per thread).
+  const bool has_bias = a.bias || a.bias_t;
+  const int nps = (int)((a.K + FOLD_W - 1) / FOLD_W), half = (nps + 1) / 2;
+  const int prow = tid >> 1, ph = tid & 1, pnq = ph ? nps - half : half;
+  const bool pvec = (nps & 7) == 0 && pnq <= 64;   // whole f32x4 loads of the partial sums
+  const bool prow_ok = a.sumsq && m0 + prow < a.M;
+  const float* pp = prow_ok ? a.sumsq + (m0 + prow) * nps + ph * half : nullptr;
+  f32x4 pv[16];
+  if (prow_ok && pvec) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pv[i] = 4 * i < pnq ? *(const f32x4*)(pp + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int pj = tid, pcls = pj >= BN ? 1 : 0;
+  const int64_t pn = n0 + pj - pcls * BN;
+  const bool pn_ok = pj < 2 * BN && pn < a.N;
+  float bval = 0.f, gval = 0.f, wval = 0.f, sval = 0.f;
+  if (has_bias && pn_ok) {
+    const float* b = (pcls && a.bias_t) ? a.bias_t : a.bias;
+    if (b) bval = b[pn];
+  }
+  if (GATED && pn_ok) {
+    gval = a.gate[pcls * a.N + pn];
+    if (a.xc && a.nw) wval = a.nw[pn];
+    if (a.xc && a.nscale) sval = a.nscale[pcls * a.N + pn];
+  }
+  if (a.sumsq) {
+    float s = 0.f;
+    if (prow_ok) {
+      if (pvec) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (4 * i < pnq) {
+            s += pv[i][0];
+            s += pv[i][1];
+            s += pv[i][2];
+            s += pv[i][3];
+          }
+        }
+      } else {
+        for (int i = 0; i < pnq; ++i) s += pp[i];   // (the same order)
+      }
+    }
+    const float o = __shfl_xor(s, 1);
+    const float tot = ph ? o + s : s + o;
+    if (!ph) rr_s[prow] = rsqrtf(tot / (float)a.K + a.eps);
+  }
+  if (pj < 2 * BN) {
+    if (has_bias) bs_s[pj] = bval;
+    if constexpr (GATED) {
+      gt_s[pj] = EPI == QI_EPI_GATED_RESIDUAL ? tanhf(gval) : gval;
+      cf_s[pj] = (wval + 1.0f) * (1.0f + sval);
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   e8 xf[2][MB], wf[2][4];
@@ -221,13 +296,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int mb = 0; mb < MB; ++mb) {
     const int64_t m = m0 + WTM * wm + 16 * mb + l16;
     if (m >= a.M) continue;
-    if (a.bias) {   // (uniform) bias of the feature rows, before the epilogue
+    const bool tgt = m + a.row0 >= a.P;
+    if (a.sumsq) {   // norm fold: the row's rrms (then the bias of shift W^T)
+      const float r = rr_s[WTM * wm + 16 * mb + l16];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int64_t n = n0 + WTN * wn + 16 * nb + 4 * G;
-        if (n >= a.N) continue;
-        acc[mb][nb] += *(const f32x4*)(a.bias + n);
-      }
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] *= r;
+    }
+    if (has_bias) {   // the bias of the row's class, before the epilogue
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[mb][nb] += *(const f32x4*)(bs_s + (tgt ? BN : 0) + WTN * wn + 16 * nb + 4 * G);
     }
     if constexpr (EPI == QI_EPI_SWIGLU) {
       // weight rows in blocks of 64: 32 gate rows (tiles 4blk, 4blk + 1), then the 32 up rows of
@@ -249,6 +327,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     } else {
+      float sq = 0.f;   // norm fold: the sum of squares of the updated residual over the wave's features
+      // gated residual: the row's residual values are all loaded before any is used or stored
+      // (interleaved with the stores, each load would wait for the one before)
+      f32x4 xres[NB];
+      if constexpr (GATED) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int64_t n = n0 + WTN * wn + 16 * nb + 4 * G;
+          xres[nb] = n < a.N ? *(const f32x4*)((const float*)a.out + m * a.ldo + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         {
@@ -269,14 +358,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
             *(u32x2*)((E*)a.out + m * a.ldo + n) = u32x2{pack2<F16>(gl[0], gl[1], bad), pack2<F16>(gl[2], gl[3], bad)};
           } else {  // QI_EPI_GATED_RESIDUAL (tanh gate) or QI_EPI_GATED_RESIDUAL_LINEAR (gate as is)
-            const f32x4 gt = *(const f32x4*)(a.gate + ((m + a.row0 < a.P) ? 0 : a.N) + n);
-            f32x4* xp = (f32x4*)((float*)a.out + m * a.ldo + n);
-            f32x4 xv = *xp;
+            const int c0 = (tgt ? BN : 0) + WTN * wn + 16 * nb + 4 * G;   // this lane's features in LDS
+            const f32x4 gt = *(const f32x4*)(gt_s + c0);
+            f32x4 xv = xres[nb];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              xv[e] = __builtin_fmaf(EPI == QI_EPI_GATED_RESIDUAL ? tanhf(gt[e]) : gt[e], y[e], xv[e]);
-            *xp = xv;
+            for (int e = 0; e < 4; ++e) xv[e] = __builtin_fmaf(gt[e], y[e], xv[e]);
+            *(f32x4*)((float*)a.out + m * a.ldo + n) = xv;
+            if (a.xc) {   // norm fold: the next norm's x (1 + w)(1 + scale) and its squares
+              const f32x4 cf = *(const f32x4*)(cf_s + c0);
+              *(u32x2*)((E*)a.xc + m * a.ldxc + n) =
+                  u32x2{pack2<F16>(xv[0] * cf[0], xv[1] * cf[1], bad), pack2<F16>(xv[2] * cf[2], xv[3] * cf[3], bad)};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) sq += xv[e] * xv[e];
+            }
           }
+        }
+      }
+      if constexpr (GATED && WTN == FOLD_W) {   // (the producing side runs 256 x 192 tiles only)
+        if (a.xc) {
+          // the row's features of this wave lie in the four lane groups: combine them (each lane
+          // gets the same bits, the additions commuting); group 0 writes the partial sum
+          float v = sq;
+          v += __shfl_xor(v, 16);
+          v += __shfl_xor(v, 32);
+          const int64_t nc = n0 + WTN * wn;
+          if (G == 0 && nc < a.N) a.sumsq_out[m * ((a.N + FOLD_W - 1) / FOLD_W) + nc / FOLD_W] = v;
         }
       }
     }
@@ -290,6 +396,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // squares and the output need one read of the row.
 template <int NCH, bool F16>
 __global__ __launch_bounds__(256) void k_norm_rows(NormArgs a) {
+  __shared__ float t_s[4 * 64 * NCH];   // norm fold: the four rows' per-chunk sums of squares
   const int lane = threadIdx.x & 63;
   const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= a.M) return;
@@ -323,7 +430,28 @@ __global__ __launch_bounds__(256) void k_norm_rows(NormArgs a) {
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-  const float rr = rsqrtf(ss / (float)a.D + a.eps);
+  float rr = rsqrtf(ss / (float)a.D + a.eps);
+  if (a.sumsq_out) {
+    // norm fold: sums of x^2 over each 96 features (24 four-feature chunks), through this wave's
+    // row of LDS, each summed in order by one lane; the output takes no rrms (the consuming GEMM
+    // applies it)
+    float* t = t_s + (threadIdx.x >> 6) * (64 * NCH);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      float u = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u += v[c][e] * v[c][e];
+      t[lane + 64 * c] = u;
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int nps = (a.D + FOLD_W - 1) / FOLD_W;
+    if (lane < nps) {
+      float u = 0.f;
+      for (int q = 24 * lane; q < 24 * lane + 24 && q < nq; ++q) u += t[q];
+      a.sumsq_out[m * nps + lane] = u;
+    }
+    rr = 1.0f;
+  }
   const int seg = (m + a.row0 < a.P) ? 0 : 1;
   const float* sc = a.scale ? a.scale + seg * a.D : nullptr;
   const float* sh = a.shift ? a.shift + seg * a.D : nullptr;
@@ -472,6 +600,69 @@ __global__ __launch_bounds__(256) void k_linear_small(const float* __restrict__ 
   }
 }
 
+// y[v][o] = sum_i x[v][i] * W[o][i] for v < nv <= 16 (the norm fold's bias tables shift W^T for
+// every step of a schedule, one pass over W); each wave computes four outputs, lanes striding
+// over i by 8, then each sum is combined over the 64 lanes in a fixed order.
+template <bool F16W>
+__global__ __launch_bounds__(256) void k_linear_multi(const float* __restrict__ x, int nv, int I,
+                                                      const uint16_t* __restrict__ w, int O, float* __restrict__ y) {
+  constexpr int NV = 16, R = 4;
+  const int lane = threadIdx.x & 63;
+  const int o0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
+  if (o0 >= O) return;
+  float acc[NV][R];
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[v][r] = 0.f;
+  for (int i = 8 * lane; i < I; i += 512) {
+    float wf[R][8];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int o = o0 + r < O ? o0 + r : O - 1;
+      const u32x4 wv = *(const u32x4*)(w + (int64_t)o * I + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (F16W) {
+          // (the halves through 16-bit integers: a bit cast of the vector element itself kept
+          // only element 0 of wv in this compiler)
+          const uint32_t u = wv[e];
+          wf[r][2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFFu));
+          wf[r][2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+        } else {
+          wf[r][2 * e] = bf_lo(wv[e]);
+          wf[r][2 * e + 1] = bf_hi(wv[e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      if (v < nv) {
+        const f32x4 xa = *(const f32x4*)(x + (int64_t)v * I + i);
+        const f32x4 xb = *(const f32x4*)(x + (int64_t)v * I + i + 4);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[v][r] = __builtin_fmaf(xa[e], wf[r][e], acc[v][r]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[v][r] = __builtin_fmaf(xb[e], wf[r][4 + e], acc[v][r]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    if (v >= nv) continue;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float s = acc[v][r];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+      if (lane == 0 && o0 + r < O) y[(int64_t)v * O + o0 + r] = s;
+    }
+  }
+}
+
 __global__ void k_cast_bf16(const float* __restrict__ x, __bf16* __restrict__ y, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) ((uint16_t*)y)[i] = (uint16_t)to_bf16(x[i]);
@@ -601,7 +792,8 @@ int gemm_config(int64_t M, int64_t N, int epi) {
 
 hipError_t launch_gemm(const GemmArgs& a, int epi, int tile_n, bool f16, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  const int bn = tile_n ? tile_n : gemm_config(a.M, a.N, epi);
+  // the norm fold's producing side writes one partial sum per wave of a 256 x 192 tile
+  const int bn = a.xc ? 192 : tile_n ? tile_n : gemm_config(a.M, a.N, epi);
   return f16 ? launch_big_f16(a, epi, bn, s) : launch_big_bf16(a, epi, bn, s);
 }
 
@@ -644,6 +836,16 @@ hipError_t launch_linear_small(const float* x, int nv, int I, const void* w, con
   if (O <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_linear_small, dim3((O + 3) / 4), dim3(256), 0, s, x, nv, I, (const __bf16*)w, bias, O, silu_in,
                      y);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_multi(const float* x, int nv, int I, const void* w, bool w_f16, int O, float* y, hipStream_t s) {
+  if (O <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((O + 15) / 16);
+  if (w_f16)
+    hipLaunchKernelGGL(k_linear_multi<true>, dim3(blocks), dim3(256), 0, s, x, nv, I, (const uint16_t*)w, O, y);
+  else
+    hipLaunchKernelGGL(k_linear_multi<false>, dim3(blocks), dim3(256), 0, s, x, nv, I, (const uint16_t*)w, O, y);
   return hipGetLastError();
 }
 

@@ -123,6 +123,19 @@ struct GemmArgs {
   int64_t row0, P;
   const float* bias;   // nullable fp32 [N], added to y before the epilogue
   uint32_t* flags;     // nullable: fp16 outputs that do not fit set QI_RANGE_OUT
+  // norm fold, consuming side: with sumsq ([M][K/32] partial sums of squares of the rows that
+  // x was formed from), y = acc * rsqrt(sum / K + eps) + bias of the row's class
+  const float* bias_t; // nullable fp32 [N]: bias of rows with m + row0 >= P (else `bias`)
+  const float* sumsq;
+  float eps;
+  // norm fold, producing side (gated residual epilogues): with xc, also write
+  // xc = x * (1 + nw) * (1 + nscale[class]) of the updated residual and its partial sums of
+  // squares sumsq_out [M][N/32] (32 features each)
+  void* xc;
+  int64_t ldxc;
+  const float* nw;     // nullable fp32 [N]
+  const float* nscale; // nullable fp32 [2][N]
+  float* sumsq_out;
 };
 // ZeroCenterRMSNorm + modulation of fp32 rows into bf16 rows.
 struct NormArgs {
@@ -139,6 +152,9 @@ struct NormArgs {
   float eps;
   int32_t center;       // 1: subtract the row mean first (LayerNorm without affine)
   uint32_t* flags;      // nullable: fp16 outputs that do not fit set QI_RANGE_OUT
+  // norm fold: with sumsq_out ([M][D/32]), out receives x * (w + 1) * (1 + scale) (no rrms, no
+  // shift) and sumsq_out the sums of x^2 over each 32 features
+  float* sumsq_out;
 };
 
 // tile_n: feature width of the 256 x tile_n workgroup tiles (256, 192 or 128; 192 not with
@@ -151,6 +167,8 @@ hipError_t launch_timestep_embed(const float* t, int n, int dim, float* out, hip
 hipError_t launch_linear_small(const float* x, int nv, int I, const void* w, const float* bias, int O, int silu_in, float* y,
                                hipStream_t s);
 hipError_t launch_cast(const float* x, void* y, int64_t n, bool f16, uint32_t* flags, hipStream_t s);
+// y[v][o] = sum_i x[v][i] w[o][i] for nv <= 16 fp32 vectors, w bf16 or (w_f16) fp16 [O][I], I % 8 == 0
+hipError_t launch_linear_multi(const float* x, int nv, int I, const void* w, bool w_f16, int O, float* y, hipStream_t s);
 
 hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);   // bf16 q/o, fp16 K/V sources
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);   // fp32 throughout

@@ -26,7 +26,7 @@ QI_SEG_TEXT, QI_SEG_IMAGE, QI_SEG_TEXT_BIDIR = 0, 1, 2
 QI_EPI_STORE, QI_EPI_STORE_F32, QI_EPI_GATED_RESIDUAL, QI_EPI_SWIGLU, QI_EPI_GELU = 0, 1, 2, 3, 4
 QI_EPI_GATED_RESIDUAL_LINEAR = 5
 QI_MAX_SOURCE_KEYS = 8388607   # keys per source of the bf16 attention (include/qi.h)
-QI_ABI_VERSION = 7             # the qi_version() these bindings are written against
+QI_ABI_VERSION = 8             # the qi_version() these bindings are written against
 QI_NOALLOC_SCRATCH_BYTES = 96 << 20   # scratch array of qi_attn_target_cached_noalloc (include/qi.h)
 QI_ATTN_BLOCK_CAUSAL, QI_ATTN_FULL = 0, 1
 QI_RANGE_Q, QI_RANGE_K, QI_RANGE_V, QI_RANGE_OUT = 1, 2, 4, 8   # range flags of fp16 values (include/qi.h)
@@ -71,6 +71,11 @@ class qi_qkv(ctypes.Structure):
 class qi_qkprep(ctypes.Structure):
     _fields_ = [("cos_t", c_void_p), ("sin_t", c_void_p), ("q_rms_w", c_void_p), ("k_rms_w", c_void_p),
                 ("eps", c_float)]
+
+
+class qi_norm_fold(ctypes.Structure):
+    _fields_ = [("sumsq", c_void_p), ("eps", c_float), ("bias_t", c_void_p), ("xc", c_void_p), ("ldxc", c_int64),
+                ("next_w", c_void_p), ("next_scale", c_void_p), ("sumsq_out", c_void_p)]
 
 
 _SIGS = {
@@ -119,6 +124,12 @@ _SIGS = {
     "qi_norm_mod": (c_int, [c_void_p, c_int64, c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p,
                             c_int64, c_int64, c_float, c_int32, c_int32, c_void_p, c_void_p]),
     "qi_cast": (c_int, [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p]),
+    "qi_gemm_norm_fold": (c_int, [c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int64,
+                                  c_int64, c_int32, c_int32, c_void_p, c_int64, c_int64, c_int32,
+                                  POINTER(qi_norm_fold), c_void_p, c_void_p]),
+    "qi_norm_fold_rows": (c_int, [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p,
+                                  c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p]),
+    "qi_linear_multi": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
     "qi_kernel_timing": (c_int, [c_int]),
     "qi_kernel_timing_read": (c_int, [POINTER(c_double), POINTER(c_int64)]),
     "qi_kernel_timing_read_each": (c_int, [POINTER(c_float), c_int64, POINTER(c_int64)]),
@@ -362,6 +373,29 @@ def qi_norm_mod(x, ldx: int, out, ldo: int, M: int, D: int, w=None, scale=None, 
 
 def qi_cast(x, y, n: int, dtype: int, range_flags=None, stream=None) -> int:
     return lib().qi_cast(_p(x), _p(y), n, dtype, _p(range_flags), _p(stream))
+
+
+def make_norm_fold(sumsq=None, eps: float = 1e-6, bias_t=None, xc=None, ldxc: int = 0, next_w=None,
+                   next_scale=None, sumsq_out=None) -> qi_norm_fold:
+    return qi_norm_fold(_p(sumsq), eps, _p(bias_t), _p(xc), ldxc, _p(next_w), _p(next_scale), _p(sumsq_out))
+
+
+def qi_gemm_norm_fold(x, ldx: int, w, bias, out, ldo: int, M: int, N: int, K: int, dtype: int, epilogue: int,
+                      gate=None, row0: int = 0, P: int = 0, tile_n: int = 0, fold: Optional[qi_norm_fold] = None,
+                      range_flags=None, stream=None) -> int:
+    return lib().qi_gemm_norm_fold(_p(x), ldx, _p(w), _p(bias), _p(out), ldo, M, N, K, dtype, epilogue, _p(gate),
+                                   row0, P, tile_n, ctypes.byref(fold) if fold is not None else None,
+                                   _p(range_flags), _p(stream))
+
+
+def qi_norm_fold_rows(x, ldx: int, xc, ldxc: int, sumsq_out, M: int, D: int, w=None, scale=None, row0: int = 0,
+                      P: int = 0, dtype: int = QI_F16, range_flags=None, stream=None) -> int:
+    return lib().qi_norm_fold_rows(_p(x), ldx, _p(xc), ldxc, _p(sumsq_out), M, D, _p(w), _p(scale), row0, P, dtype,
+                                   _p(range_flags), _p(stream))
+
+
+def qi_linear_multi(x, n_vec: int, I: int, w, w_dtype: int, O: int, y, stream=None) -> int:
+    return lib().qi_linear_multi(_p(x), n_vec, I, _p(w), w_dtype, O, _p(y), _p(stream))
 
 
 def qi_kernel_timing(enable: bool) -> int:

@@ -244,18 +244,81 @@ class SharedWeights:
 
 
 def gemm(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor, epilogue: int, gate=None, row0: int = 0, P: int = 0,
-         tile_n: int = 0, bias=None, flags=None):
+         tile_n: int = 0, bias=None, flags=None, fold: Optional["NormFold"] = None):
     """y = x W^T with an epilogue; x and w both bf16 (bf16 matrix cores, bf16 16-bit outputs) or
-    both fp16 (fp16 matrix cores and outputs)."""
+    both fp16 (fp16 matrix cores and outputs).  fold: the norm fold's consuming and/or producing
+    side (qi_gemm_norm_fold)."""
     M, K = x.shape
     N = w.shape[0]
     assert x.dtype in (torch.bfloat16, torch.float16) and w.dtype == x.dtype and w.shape[1] == K and x.stride(1) == 1
     assert out.stride(1) == 1 and out.shape[0] == M
     if bias is not None:
         assert bias.dtype == torch.float32 and bias.is_contiguous() and bias.numel() == N
-    Q.check(Q.qi_gemm(x, x.stride(0), w, bias, out, out.stride(0), M, N, K, code_of(x), epilogue, gate, row0, P,
-                      tile_n, flags, stream_handle(x.device)), "qi_gemm")
+    if fold is None:
+        Q.check(Q.qi_gemm(x, x.stride(0), w, bias, out, out.stride(0), M, N, K, code_of(x), epilogue, gate, row0, P,
+                          tile_n, flags, stream_handle(x.device)), "qi_gemm")
+        return out
+    fold.check(M, N, K, x.dtype)
+    Q.check(Q.qi_gemm_norm_fold(x, x.stride(0), w, bias, out, out.stride(0), M, N, K, code_of(x), epilogue, gate,
+                                row0, P, tile_n, fold.struct(), flags, stream_handle(x.device)), "qi_gemm_norm_fold")
     return out
+
+
+FOLD_W = 96   # features per partial sum of squares of the norm fold (include/qi.h)
+
+
+def fold_parts(D: int) -> int:
+    """Partial sums of squares per row of D features: ceil(D / 96)."""
+    return -(-D // FOLD_W)
+
+
+class NormFold:
+    """Arguments of the norm fold (include/qi.h, qi_norm_fold): the consuming side (sumsq
+    [M][ceil(K/96)] of the rows x was formed from, eps, the target rows' bias bias_t) and/or the
+    producing side of a gated residual epilogue (xc [M][N] of the activation type, next_w [N],
+    next_scale [2][N], sumsq_out [M][ceil(N/96)])."""
+
+    def __init__(self, sumsq=None, eps: float = 1e-6, bias_t=None, xc=None, next_w=None, next_scale=None,
+                 sumsq_out=None):
+        self.sumsq, self.eps, self.bias_t = sumsq, eps, bias_t
+        self.xc, self.next_w, self.next_scale, self.sumsq_out = xc, next_w, next_scale, sumsq_out
+
+    def check(self, M, N, K, dtype):
+        if self.sumsq is not None:
+            assert self.sumsq.dtype == torch.float32 and self.sumsq.is_contiguous()
+            assert self.sumsq.shape[0] >= M and self.sumsq.shape[1] == fold_parts(K)
+        if self.bias_t is not None:
+            assert self.bias_t.dtype == torch.float32 and self.bias_t.is_contiguous() and self.bias_t.numel() == N
+        if self.xc is not None:
+            assert self.xc.dtype == dtype and self.xc.stride(1) == 1 and self.xc.shape[0] >= M
+            assert self.sumsq_out.dtype == torch.float32 and self.sumsq_out.is_contiguous()
+            assert self.sumsq_out.shape[0] >= M and self.sumsq_out.shape[1] == fold_parts(N)
+
+    def struct(self):
+        return Q.make_norm_fold(self.sumsq, self.eps, self.bias_t, self.xc,
+                                self.xc.stride(0) if self.xc is not None else 0, self.next_w, self.next_scale,
+                                self.sumsq_out)
+
+
+def norm_fold_rows(x: torch.Tensor, xc: torch.Tensor, sumsq: torch.Tensor, w=None, scale=None, row0: int = 0,
+                   P: int = 0, flags=None):
+    """The norm fold's producing side for fp32 rows: xc = x (1 + w)(1 + scale), sumsq [M][ceil(D/96)]."""
+    M, D = x.shape
+    assert x.dtype == torch.float32 and x.stride(1) == 1 and xc.stride(1) == 1 and xc.shape[0] >= M
+    assert sumsq.dtype == torch.float32 and sumsq.is_contiguous() and sumsq.shape[0] >= M and sumsq.shape[1] == fold_parts(D)
+    Q.check(Q.qi_norm_fold_rows(x, x.stride(0), xc, xc.stride(0), sumsq, M, D, w, scale, row0, P, code_of(xc), flags,
+                                stream_handle(x.device)), "qi_norm_fold_rows")
+    return xc
+
+
+def linear_multi(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor):
+    """y[v] = x[v] W^T for up to 16 fp32 vectors (one pass over W)."""
+    nv, I = x.shape
+    O_ = w.shape[0]
+    assert x.dtype == torch.float32 and x.is_contiguous() and w.is_contiguous() and w.shape[1] == I
+    assert y.dtype == torch.float32 and y.is_contiguous() and y.shape == (nv, O_)
+    Q.check(Q.qi_linear_multi(x, nv, I, w, code_of(w), O_, y, stream_handle(x.device)), "qi_linear_multi")
+    return y
 
 
 def norm_mod(x: torch.Tensor, out: torch.Tensor, w=None, scale=None, shift=None, row0: int = 0, P: int = 0,
@@ -334,11 +397,14 @@ class DiT:
     scale-only head and the Euler update.  All arithmetic runs in libqi kernels; this class owns
     buffers and issues the calls in order on the current stream."""
 
-    def __init__(self, layout: Layout, shared: SharedWeights, layers, device="cuda", eps: float = 1e-6):
+    def __init__(self, layout: Layout, shared: SharedWeights, layers, device="cuda", eps: float = 1e-6,
+                 fold: bool = True):
         """The layer chain's 16-bit activations (normed rows, QKV, attention output, SwiGLU output,
         the latents into img_in) and the projection weights are fp16 (the weights converted once
-        from the model's bf16)."""
+        from the model's bf16).  fold: the layer's two norms folded into its GEMMs (qi_norm_fold;
+        seven launches per cached layer) instead of launched on their own (nine)."""
         self.L, self.sw, self.device, self.eps, self.act = layout, shared, device, eps, ACT
+        self.fold = fold
         act_dtype = ACT
         self.layers = [W.as_dtype(act_dtype) for W in layers]
         self.w_in, self.w_head = shared.w_in.to(act_dtype), shared.w_head.to(act_dtype)
@@ -363,6 +429,14 @@ class DiT:
         self.temb = torch.empty((2, D), dtype=f32, device=device)
         self.mods = torch.empty((6, 2, D), dtype=f32, device=device)     # [chunk][prefix | target][D]
         self.hscale = torch.empty((2, D), dtype=f32, device=device)
+        # norm fold: partial sums of squares of the rows in h, and the bias tables shift W^T of the
+        # QKV and gate|up projections ([prefix (t = 0) | target] of the current conditioning)
+        nl = len(self.layers)
+        self.sq = torch.empty((S, fold_parts(D)), dtype=f32, device=device)
+        self.bq = torch.empty((nl, 2, 3 * D), dtype=f32, device=device)
+        self.bgu = torch.empty((nl, 2, 2 * max(self.F, 1)), dtype=f32, device=device)
+        self._sched = None     # conditioning of a whole schedule (prepare)
+        self._k = None         # the schedule's step whose conditioning is current
 
     # -- conditioning ------------------------------------------------------------------------
     def condition(self, sigma: float):
@@ -376,6 +450,62 @@ class DiT:
         for c in range(6):
             linear_small(self.temb, sw.w_mod[c * D:(c + 1) * D], self.mods[c], True)
         linear_small(self.temb, sw.w_scale, self.hscale, True)
+        self._k = None
+        if self.fold:
+            for li, W in enumerate(self.layers):
+                linear_multi(self.mods[0], W.w_qkv, self.bq[li])
+                linear_multi(self.mods[3], W.w_gu, self.bgu[li])
+
+    def prepare(self, sig):
+        """The conditioning of every step of the schedule sig (sigmas of n steps + the end point):
+        the modulation and head-scale vectors per step, and with the fold the bias tables of every
+        layer for all steps in one pass over its weights (entry 0: the prefix rows' t = 0, entry
+        1 + k: the target rows at step k).  step() then copies a step's vectors instead of
+        recomputing them."""
+        n = len(sig) - 1
+        assert 1 <= n <= 15
+        D = self.D
+        mods = torch.empty((n, 6, 2, D), dtype=torch.float32, device=self.device)
+        hsc = torch.empty((n, 2, D), dtype=torch.float32, device=self.device)
+        fold = self.fold
+        self.fold = False          # the vectors only: the tables below take every step at once
+        try:
+            for k in range(n):
+                self.condition(float(sig[k]))
+                mods[k].copy_(self.mods)
+                hsc[k].copy_(self.hscale)
+        finally:
+            self.fold = fold
+        tabs = None
+        if fold:
+            v1 = torch.cat([mods[0, 0, 0:1], mods[:, 0, 1]]).contiguous()   # shift1: t = 0, then each step
+            v2 = torch.cat([mods[0, 3, 0:1], mods[:, 3, 1]]).contiguous()   # shift2
+            nl = len(self.layers)
+            tq = torch.empty((nl, n + 1, 3 * D), dtype=torch.float32, device=self.device)
+            tg = torch.empty((nl, n + 1, self.bgu.shape[2]), dtype=torch.float32, device=self.device)
+            for li, W in enumerate(self.layers):
+                linear_multi(v1, W.w_qkv, tq[li])
+                linear_multi(v2, W.w_gu, tg[li])
+            tabs = (tq, tg)
+        self._sched = (tuple(float(v) for v in sig), mods, hsc, tabs)
+        self._k = None
+
+    def _use_step(self, k: int, sig) -> bool:
+        """Make step k of a prepared schedule current; False if sig is not the prepared one."""
+        if self._sched is None or self._sched[0] != tuple(float(v) for v in sig):
+            return False
+        _, mods, hsc, _ = self._sched
+        self.mods.copy_(mods[k])
+        self.hscale.copy_(hsc[k])
+        self._k = k
+        return True
+
+    def _biases(self, li: int):
+        """(prefix, target) bias rows of layer li's QKV and gate|up projections."""
+        if self._k is not None:
+            tq, tg = self._sched[3]
+            return tq[li, 0], tq[li, 1 + self._k], tg[li, 0], tg[li, 1 + self._k]
+        return self.bq[li, 0], self.bq[li, 1], self.bgu[li, 0], self.bgu[li, 1]
 
     # -- one layer ---------------------------------------------------------------------------
     def layer(self, li: int, rows: slice, cached: bool):
@@ -384,8 +514,17 @@ class DiT:
         r0, n, P = rows.start, rows.stop - rows.start, self.L.P
         x, h, qkv, o, a = self.x[rows], self.h[:n], self.qkv[:n], self.o[:n], self.a[:n]
         m, fl = self.mods, self.flags
-        norm_mod(x, h, W.norm1, m[1], m[0], r0, P, eps, flags=fl)
-        gemm(h, W.w_qkv, qkv, Q.QI_EPI_STORE, flags=fl)
+        if self.fold:
+            # h holds x (1 + w)(1 + scale) of the next norm and sq its rows' partial sums of squares:
+            # written here for the first layer, else by the previous down-projection's epilogue
+            sq = self.sq[:n]
+            bq_p, bq_t, bg_p, bg_t = self._biases(li)
+            if li == 0:
+                norm_fold_rows(x, h, sq, W.norm1, m[1], r0, P, flags=fl)
+            gemm(h, W.w_qkv, qkv, Q.QI_EPI_STORE, None, r0, P, bias=bq_p, flags=fl, fold=NormFold(sq, eps, bq_t))
+        else:
+            norm_mod(x, h, W.norm1, m[1], m[0], r0, P, eps, flags=fl)
+            gemm(h, W.w_qkv, qkv, Q.QI_EPI_STORE, flags=fl)
         q = qkv[:, :D].view(n, self.H, 128)
         k = qkv[:, D:2 * D].view(n, self.H, 128)
         v = qkv[:, 2 * D:].view(n, self.H, 128)
@@ -393,6 +532,14 @@ class DiT:
             self.attn.cached(q, k, v, self.cache, li, W.q_norm, W.k_norm, eps, out=o)
         else:
             self.attn.full(q, k, v, W.q_norm, W.k_norm, eps, cache=self.cache, layer=li, out=o)
+        if self.fold:
+            gemm(o.view(n, D), W.w_out, x, Q.QI_EPI_GATED_RESIDUAL, m[2], r0, P, flags=fl,
+                 fold=NormFold(xc=h, next_w=W.norm2, next_scale=m[4], sumsq_out=sq))
+            gemm(h, W.w_gu, a, Q.QI_EPI_SWIGLU, None, r0, P, bias=bg_p, flags=fl, fold=NormFold(sq, eps, bg_t))
+            nxt = self.layers[li + 1] if li + 1 < len(self.layers) else None
+            gemm(a, W.w_down, x, Q.QI_EPI_GATED_RESIDUAL, m[5], r0, P, flags=fl,
+                 fold=NormFold(xc=h, next_w=nxt.norm1, next_scale=m[1], sumsq_out=sq) if nxt else None)
+            return
         gemm(o.view(n, D), W.w_out, x, Q.QI_EPI_GATED_RESIDUAL, m[2], r0, P)
         norm_mod(x, h, W.norm2, m[4], m[3], r0, P, eps, flags=fl)
         gemm(h, W.w_gu, a, Q.QI_EPI_SWIGLU, flags=fl)
@@ -434,7 +581,8 @@ class DiT:
     def step(self, k: int, lat: torch.Tensor, sig, x_text=None, lat_ref=None):
         """Euler step k (0-based) of the loop: step 0 runs the whole sequence and fills the caches."""
         S, P = self.L.S, self.L.P
-        self.condition(float(sig[k]))
+        if not self._use_step(k, sig):
+            self.condition(float(sig[k]))
         self.embed(lat, self.x[P:])
         if k == 0:
             self.set_prefix(x_text, lat_ref)

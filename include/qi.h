@@ -178,7 +178,8 @@ const char* qi_status_str(int status);
 /* Library ABI version (increments on any signature or struct change; 2 added qi_qkv.lse, 3 the
  * range flags and int32_t dtype fields, 4 the allocation-free cached step, 5 fp16 activations
  * (QI_F16 attention I/O, qi_gemm, qi_norm_mod, qi_cast), 6 the fp16 cache's tile layout for the
- * 16 x 16 x 32 matrix-core operands, 7 the key counts of qi_attn_schedule). */
+ * 16 x 16 x 32 matrix-core operands, 7 the key counts of qi_attn_schedule, 8 the norm fold:
+ * qi_gemm_norm_fold, qi_norm_fold_rows, qi_linear_multi). */
 int qi_version(void);
 
 /* Token counts of a layout: S = all, P = prefix (all but the last segment), T = target.
@@ -405,6 +406,71 @@ int qi_cast_bf16(const float* x, void* y, int64_t n, void* stream);
 int qi_gemm(const void* x, int64_t ldx, const void* w, const float* bias, void* out, int64_t ldo, int64_t M,
             int64_t N, int64_t K, int32_t dtype, int32_t epilogue, const float* gate, int64_t row0, int64_t P,
             int32_t tile_n, uint32_t* range_flags, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * The norm fold of the single-stream layer.  A ZeroCenterRMSNorm with modulation followed by a
+ * Linear ([1B] sections 1-3; [EDIT] section 5.2; [OV] cards 4A and 5A: every projection of the
+ * layer reads a modulated norm of the residual stream),
+ *     y = h W^T,  h = x * rrms(x) * (1 + w) * (1 + scale) + shift,  rrms = 1 / sqrt(mean(x^2) + eps),
+ * equals, since rrms is one number per row and shift one vector per row class,
+ *     y = rrms(x) * ((x * (1 + w) * (1 + scale)) W^T) + shift W^T.
+ * So the norm needs no pass of its own: the epilogue that updates the residual x (the tanh-gated
+ * out- and down-projections) also writes xc = x (1 + w)(1 + scale) in the 16-bit type and the sums
+ * of x^2 over each 96 features (QI_FOLD_W; the features of one wave of its 256 x 192 tiles, which
+ * the producing side always runs); the next GEMM reads xc as its operand, sums the partial sums of
+ * its rows in its prologue and applies rrms and the bias table shift W^T (qi_linear_multi) in its
+ * epilogue.  A row's partial sums do not depend on the consuming GEMM's tiles, so neither do the
+ * results.
+ * ------------------------------------------------------------------------------------------ */
+#define QI_FOLD_W 96   /* features per partial sum of squares of the norm fold */
+
+typedef struct {
+  /* consuming side: y = rsqrt(sum_j sumsq[m][j] / K + eps) * (x W^T) + bias of the row's class */
+  const float* sumsq;        /* NULL = off; device fp32 [M][ceil(K/96)], 16-byte aligned */
+  float eps;
+  const float* bias_t;       /* NULL, or device fp32 [N] (16-byte aligned): the bias of rows with
+                                row0 + m >= P (target rows); `bias` stays the other rows' */
+  /* producing side (QI_EPI_GATED_RESIDUAL, QI_EPI_GATED_RESIDUAL_LINEAR): after x += g * y */
+  void* xc;                  /* NULL = off; device `dtype` [M][ldxc] (16-byte aligned, ldxc >= N,
+                                ldxc % 8 == 0): x * (1 + next_w) * (1 + next_scale[class]) */
+  int64_t ldxc;
+  const float* next_w;       /* NULL (no (1 + w) factor) or device fp32 [N], 16-byte aligned */
+  const float* next_scale;   /* NULL or device fp32 [2][N] (prefix | target rows), 16-byte aligned */
+  float* sumsq_out;          /* device fp32 [M][ceil(N/96)] (4-byte aligned), required with xc: sum
+                                over features 96j .. min(96j + 95, N - 1) of the updated x^2 */
+} qi_norm_fold;
+
+/* qi_gemm with the norm fold (fold NULL: exactly qi_gemm).  A producing side runs 256 x 192 tiles
+ * (tile_n 0 or 192).  Errors as qi_gemm, and QI_ERR_ARG for a producing side on another epilogue
+ * or another tile_n, xc without sumsq_out or producing fields without xc, eps negative or not
+ * finite; QI_ERR_SHAPE for ldxc < N; QI_ERR_ALIGN for the alignments above.
+ * Overlapping xc, sumsq_out and the other buffers are not detected (their contents are then
+ * undefined). */
+int qi_gemm_norm_fold(const void* x, int64_t ldx, const void* w, const float* bias, void* out, int64_t ldo,
+                      int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t epilogue, const float* gate,
+                      int64_t row0, int64_t P, int32_t tile_n, const qi_norm_fold* fold, uint32_t* range_flags,
+                      void* stream);
+
+/* The fold's producing side for rows that no GEMM epilogue produced (the first layer's input):
+ * x device fp32 [M][ldx] -> xc device `dtype` (QI_BF16 or QI_F16) [M][ldxc] = x (1 + w)(1 + scale
+ * of the row's class) and sumsq_out device fp32 [M][ceil(D/96)] the sums of x^2 over each 96
+ * features (the layout the consuming GEMM reads); w
+ * fp32 [D] or NULL, scale fp32 [2][D] or NULL (row m using index 0 if row0 + m < P).  D % 32 == 0
+ * and D <= 4096.  Errors: QI_ERR_ARG (NULL x, xc or sumsq_out), QI_ERR_DTYPE, QI_ERR_SHAPE (M < 0 or
+ * above 2^31 - 1, D, ldx or ldxc < D), QI_ERR_ALIGN (x, w, scale not 16-byte aligned, ldx or ldxc
+ * not a multiple of 4, xc not 8-byte or sumsq_out not 4-byte aligned), QI_ERR_HIP (launch). */
+int qi_norm_fold_rows(const float* x, int64_t ldx, void* xc, int64_t ldxc, float* sumsq_out, int64_t M, int32_t D,
+                      const float* w, const float* scale, int64_t row0, int64_t P, int32_t dtype,
+                      uint32_t* range_flags, void* stream);
+
+/* y[v][o] = sum_i x[v][i] w[o][i] for 1 <= n_vec <= 16 vectors in one pass over w (the fold's bias
+ * tables: the shift vectors of every step of a schedule times a layer's weights).  x device fp32
+ * [n_vec][I] (16-byte aligned), w device w_dtype (QI_BF16 or QI_F16) [O][I] (16-byte aligned, I % 8
+ * == 0), y device fp32 [n_vec][O]; fp32 products and sums.  Errors: QI_ERR_ARG (NULL pointer),
+ * QI_ERR_DTYPE, QI_ERR_SHAPE (n_vec outside 1..16, I < 8 or I % 8, O < 0, O * I above 2^40),
+ * QI_ERR_ALIGN, QI_ERR_HIP (launch). */
+int qi_linear_multi(const float* x, int32_t n_vec, int32_t I, const void* w, int32_t w_dtype, int32_t O, float* y,
+                    void* stream);
 
 /* qi_zc_rmsnorm_mod (center = 0; w nullable) or qi_layernorm_mod (center = 1; w must be NULL)
  * with an output of out_dtype (QI_BF16 or QI_F16).  Other arguments and errors as those. */

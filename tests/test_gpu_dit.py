@@ -375,7 +375,7 @@ def test_text_projection(n, D):
 # one whole layer, the conditioning, and a small sampling loop
 # ------------------------------------------------------------------------------------------------
 
-def make_model(segments, D, F, n_layers, cfg=CFG):
+def make_model(segments, D, F, n_layers, cfg=CFG, fold=True):
     layout = rt.Layout(segments, DEV)
     sw_np = qin.shared_weights(cfg, D)
     lw_np = [qin.layer_weights(cfg, D, F, l) for l in range(n_layers)]
@@ -383,7 +383,7 @@ def make_model(segments, D, F, n_layers, cfg=CFG):
     layers = [rt.LayerWeights(f32(L["norm1"]), f32(L["norm2"]), f32(L["q_norm"]), f32(L["k_norm"]),
                               bf(L["w_qkv"]), bf(L["w_out"]), bf(L["w_gate"]), bf(L["w_up"]), bf(L["w_down"]))
               for L in lw_np]
-    model = rt.DiT(layout, sw, layers, DEV)
+    model = rt.DiT(layout, sw, layers, DEV, fold=fold)
     shared64 = {k: v.f64 for k, v in sw_np.items()}
     layers64 = [{k: (v.f64 if isinstance(v, qin.Stored) else v) for k, v in L.items()} for L in lw_np]
     return model, shared64, layers64
@@ -409,11 +409,12 @@ def gpu_mods(model):
     return tuple(m[c][0] for c in range(6)), tuple(m[c][1] for c in range(6))
 
 
+@pytest.mark.parametrize("fold", [True, False])
 @pytest.mark.parametrize("segments,D,F", [(SMALL, 256, 512), ((qin.text(130), qin.image(8, 16, 1), qin.text(3),
                                                              qin.image(10, 10, 2), qin.image(16, 9, 0)), 384, 320)])
-def test_layer_step1_and_cached(segments, D, F):
-    say(f"[layer] S={sum(g.n_tokens for g in segments)} D={D} F={F}")
-    model, sh, layers64 = make_model(segments, D, F, 1)
+def test_layer_step1_and_cached(segments, D, F, fold):
+    say(f"[layer] S={sum(g.n_tokens for g in segments)} D={D} F={F} fold={fold}")
+    model, sh, layers64 = make_model(segments, D, F, 1, fold=fold)
     L = model.L
     S, P, T = L.S, L.P, L.T
     c, s = O.rope_tables(O.positions(segments))
@@ -439,10 +440,11 @@ def test_layer_step1_and_cached(segments, D, F):
     assert model.attn.range_flags() == 0
 
 
-def test_cached_layer_equals_step1_target_rows_bitwise():
+@pytest.mark.parametrize("fold", [True, False])
+def test_cached_layer_equals_step1_target_rows_bitwise(fold):
     # the same target input through step 1 (whole sequence) and through the cached path gives the
     # same target rows, bit for bit: the prefix K/V in the cache are the ones step 1 used
-    model, _, _ = make_model(SMALL, 256, 512, 1)
+    model, _, _ = make_model(SMALL, 256, 512, 1, fold=fold)
     S, P = model.L.S, model.L.P
     model.condition(0.5)
     x_in = f32(qin.normal(CFG, 272, (S, 256)))
@@ -455,10 +457,12 @@ def test_cached_layer_equals_step1_target_rows_bitwise():
     assert torch.equal(model.x[P:], full_t)
 
 
-def test_sampling_loop_small():
+@pytest.mark.parametrize("fold,prepared", [(True, True), (True, False), (False, True)])
+def test_sampling_loop_small(fold, prepared):
     segments = (qin.text(20), qin.image(6, 5, 1), qin.image(7, 6, 0))
     D, F, n_layers, n_steps = 256, 512, 2, 3
-    model, sh, layers64 = make_model(segments, D, F, n_layers)
+    say(f"[sampling loop] fold={fold} prepared={prepared}")
+    model, sh, layers64 = make_model(segments, D, F, n_layers, fold=fold)
     L = model.L
     n_text = 20
     x_text, lat_ref = qin.prefix_inputs(CFG, n_text, 30, D)
@@ -467,6 +471,8 @@ def test_sampling_loop_small():
     lat = f32(lat0)
     vels = []
     xt, lr = f32(x_text), f32(lat_ref)
+    if prepared:
+        model.prepare(sig)
     for k in range(n_steps):
         model.step(k, lat, sig, xt, lr)
         vels.append(host(model.vel))
@@ -541,3 +547,65 @@ def test_full_size_layer_stages_sampled():
     sync()
     ref_x2 = x1[rows] + np.tanh(sel(5, rows)) * O.linear(a64[rows], W["w_down"])
     check(host(model.x[rows]), ref_x2, "f32", "down-proj residual")
+
+
+@pytest.mark.parametrize("cached", [False, True])
+def test_full_size_layer_norm_fold_sampled(cached):
+    # the layer's norm fold at the 14,848-token shape (step 1: every row; cached: the 4,096 target
+    # rows) through the launches the denoiser makes, each stage against the oracle on sampled rows
+    wl = qin.WORKLOADS["txt512_10ref32_tgt64"]
+    D, F = 3072, 8192
+    say(f"[layer fold full] S={wl.S} P={wl.P} T={wl.T} cached={cached}")
+    model, sh, layers64 = make_model(wl.segments, D, F, 1, cfg=wl.cfg_id)
+    W, Lw = layers64[0], model.layers[0]
+    S, P = wl.S, wl.P
+    r0 = P if cached else 0
+    n = S - r0
+    rows = np.unique(np.concatenate([[0, n - 1, max(P - r0 - 1, 0), P - r0 if P > r0 else 0],
+                                     qin.rng(CFG, 290 + int(cached)).integers(0, n, 24)]))
+    model.condition(0.625)
+    mods = gpu_mods(model)
+    m = model.mods
+    sel = lambda i, r: O.per_row(mods[0][i], mods[1][i], n, r0, P)[r]
+    x_in = qin.normal(CFG, 291, (n, D)).astype(np.float32)
+    x = model.x[r0:]
+    x.copy_(f32(x_in))
+    x64 = x_in.astype(np.float64)
+    h, sq = model.h[:n], model.sq[:n]
+    bq = model.bq[0]
+    # norm1 folded: xc, partial sums, then the QKV projection with rrms and the shift bias
+    rt.norm_fold_rows(x, h, sq, Lw.norm1, m[1], r0, P)
+    qkv = model.qkv[:n]
+    rt.gemm(h, Lw.w_qkv, qkv, Q.QI_EPI_STORE, None, r0, P, bias=bq[0], fold=rt.NormFold(sq, 1e-6, bq[1]))
+    sync()
+    check(host(bq[1]), O.linear(mods[1][0][None, :], host(Lw.w_qkv))[0], "f32", "QKV bias table (target)")
+    h1 = O.norm_mod(x64[rows], W["norm1"], sel(1, rows), sel(0, rows))
+    check(host(qkv[rows]), O.linear(h1, W["w_qkv"]), "bf16", "qkv (norm1 folded)")
+    # out-projection (a synthetic attention output) producing norm2's operand
+    o = torch.from_numpy(qin.normal(CFG, 292, (n, D)).astype(np.float16)).to(DEV)
+    rt.gemm(o, Lw.w_out, x, Q.QI_EPI_GATED_RESIDUAL, m[2], r0, P,
+            fold=rt.NormFold(xc=h, next_w=Lw.norm2, next_scale=m[4], sumsq_out=sq))
+    sync()
+    o64 = host(o)
+    ref_x1 = x64[rows] + np.tanh(sel(2, rows)) * O.linear(o64[rows], W["w_out"])
+    check(host(x[rows]), ref_x1, "f32", "out-proj residual")
+    x1 = host(x)
+    check(host(h[rows]), x1[rows] * (1.0 + W["norm2"]) * (1.0 + sel(4, rows)), "f16", "xc for norm2")
+    check(host(sq[rows]), (x1[rows] ** 2).reshape(len(rows), D // 96, 96).sum(axis=2), "f32", "norm2 partial sums")
+    # gate|up with norm2 folded
+    bg = model.bgu[0]
+    a = model.a[:n]
+    rt.gemm(h, Lw.w_gu, a, Q.QI_EPI_SWIGLU, None, r0, P, bias=bg[0], fold=rt.NormFold(sq, 1e-6, bg[1]))
+    sync()
+    h2 = O.norm_mod(x1[rows], W["norm2"], sel(4, rows), sel(3, rows))
+    check(host(a[rows]), O.swiglu(O.linear(h2, W["w_gate"]), O.linear(h2, W["w_up"])), "bf16", "swiglu (norm2 folded)")
+    # down-projection producing the next layer's norm1 operand
+    a64 = host(a)
+    rt.gemm(a, Lw.w_down, x, Q.QI_EPI_GATED_RESIDUAL, m[5], r0, P,
+            fold=rt.NormFold(xc=h, next_w=Lw.norm1, next_scale=m[1], sumsq_out=sq))   # (as a next layer's)
+    sync()
+    ref_x2 = x1[rows] + np.tanh(sel(5, rows)) * O.linear(a64[rows], W["w_down"])
+    check(host(x[rows]), ref_x2, "f32", "down-proj residual")
+    x2 = host(x[rows])
+    check(host(h[rows]), x2 * (1.0 + W["norm1"]) * (1.0 + sel(1, rows)), "f16", "xc for the next norm1")
+    assert model.attn.range_flags() == 0

@@ -438,3 +438,66 @@ def test_schedule_invariants_over_shapes():
             assert 1 <= kc <= chunks and kw == whole, (n_q, heads, n_keys_a)
             assert kch == (rest if kc > 1 else 0), (n_q, heads, n_keys_a)
             assert kch * kc <= chunked * chunks, (n_q, heads, n_keys_a)
+
+
+def test_norm_fold_entry_points_reject():
+    # qi_gemm_norm_fold, qi_norm_fold_rows and qi_linear_multi: every case fails a check before
+    # any launch (include/qi.h documents each status)
+    G, F16 = Q.QI_EPI_GATED_RESIDUAL, Q.QI_F16
+
+    def gemm(fold, epi=G, M=256, N=256, K=256, gate=FAKE):
+        return Q.qi_gemm_norm_fold(FAKE, K, FAKE + 0x10000, None, FAKE + 0x20000, N, M, N, K, F16, epi, gate, 0, 0,
+                                   0, fold, None, None)
+
+    mk = Q.make_norm_fold
+    prod = dict(xc=FAKE + 0x30000, ldxc=256, sumsq_out=FAKE + 0x40000)
+    assert gemm(mk(**prod), epi=Q.QI_EPI_STORE, gate=None) == Q.QI_ERR_ARG          # producer on a store epilogue
+    assert gemm(mk(xc=FAKE + 0x30000, ldxc=256)) == Q.QI_ERR_ARG                    # xc without sumsq_out
+    assert gemm(mk(sumsq_out=FAKE + 0x40000)) == Q.QI_ERR_ARG                       # producer fields without xc
+    assert gemm(mk(next_w=FAKE + 0x50000)) == Q.QI_ERR_ARG
+    assert gemm(mk(sumsq=FAKE + 0x60000, eps=-1.0)) == Q.QI_ERR_ARG                 # negative eps
+    assert gemm(mk(sumsq=FAKE + 0x60000, eps=float("nan"))) == Q.QI_ERR_ARG
+    assert gemm(mk(xc=FAKE + 0x30000, ldxc=128, sumsq_out=FAKE + 0x40000)) == Q.QI_ERR_SHAPE   # ldxc < N
+    assert gemm(mk(xc=FAKE + 0x30000, ldxc=260, sumsq_out=FAKE + 0x40000)) == Q.QI_ERR_ALIGN   # ldxc % 8
+    assert gemm(mk(xc=FAKE + 0x30008, ldxc=256, sumsq_out=FAKE + 0x40000)) == Q.QI_ERR_ALIGN   # xc alignment
+    assert gemm(mk(sumsq=FAKE + 0x60004)) == Q.QI_ERR_ALIGN
+    assert gemm(mk(sumsq=FAKE + 0x60000, bias_t=FAKE + 0x70004)) == Q.QI_ERR_ALIGN
+    assert gemm(mk(**prod, next_scale=FAKE + 0x50008)) == Q.QI_ERR_ALIGN
+    assert gemm(mk(xc=FAKE + 0x30000, ldxc=256, sumsq_out=FAKE + 0x40002)) == Q.QI_ERR_ALIGN
+    assert gemm(mk(), N=96) == Q.QI_ERR_SHAPE                                       # the plain checks still apply
+    # the producing side for fp32 rows
+    nf = Q.qi_norm_fold_rows
+    assert nf(None, 256, FAKE, 256, FAKE, 8, 256) == Q.QI_ERR_ARG
+    assert nf(FAKE, 256, FAKE, 256, None, 8, 256) == Q.QI_ERR_ARG
+    assert nf(FAKE, 256, FAKE, 256, FAKE, 8, 256, dtype=Q.QI_F32) == Q.QI_ERR_DTYPE
+    assert nf(FAKE, 256, FAKE, 256, FAKE, 8, 240) == Q.QI_ERR_SHAPE                 # D % 32
+    assert nf(FAKE, 8192, FAKE, 8192, FAKE, 8, 8192) == Q.QI_ERR_SHAPE              # D > 4096
+    assert nf(FAKE, 128, FAKE, 256, FAKE, 8, 256) == Q.QI_ERR_SHAPE                 # ldx < D
+    assert nf(FAKE, 256, FAKE, 256, FAKE, -1, 256) == Q.QI_ERR_SHAPE
+    assert nf(FAKE + 4, 256, FAKE, 256, FAKE, 8, 256) == Q.QI_ERR_ALIGN
+    assert nf(FAKE, 256, FAKE + 4, 256, FAKE, 8, 256) == Q.QI_ERR_ALIGN
+    assert nf(FAKE, 256, FAKE, 256, FAKE + 2, 8, 256) == Q.QI_ERR_ALIGN
+    assert nf(FAKE, 256, FAKE, 256, FAKE, 8, 256, w=FAKE + 8) == Q.QI_ERR_ALIGN
+    assert nf(FAKE, 256, FAKE, 256, FAKE, 0, 256) == Q.QI_OK                        # nothing to do, no launch
+    # bias tables
+    lm = Q.qi_linear_multi
+    assert lm(None, 2, 256, FAKE, Q.QI_F16, 8, FAKE) == Q.QI_ERR_ARG
+    assert lm(FAKE, 2, 256, FAKE, Q.QI_F32, 8, FAKE) == Q.QI_ERR_DTYPE
+    assert lm(FAKE, 0, 256, FAKE, Q.QI_F16, 8, FAKE) == Q.QI_ERR_SHAPE
+    assert lm(FAKE, 17, 256, FAKE, Q.QI_F16, 8, FAKE) == Q.QI_ERR_SHAPE
+    assert lm(FAKE, 2, 260, FAKE, Q.QI_F16, 8, FAKE) == Q.QI_ERR_SHAPE
+    assert lm(FAKE, 2, 256, FAKE, Q.QI_F16, -1, FAKE) == Q.QI_ERR_SHAPE
+    assert lm(FAKE + 4, 2, 256, FAKE, Q.QI_F16, 8, FAKE) == Q.QI_ERR_ALIGN
+    assert lm(FAKE, 2, 256, FAKE + 8, Q.QI_BF16, 8, FAKE) == Q.QI_ERR_ALIGN
+    assert lm(FAKE, 2, 256, FAKE, Q.QI_BF16, 0, FAKE) == Q.QI_OK                    # no outputs, no launch
+
+
+def test_norm_fold_producer_tile_and_width():
+    # the producing side runs 256 x 192 tiles only; the header's partial-sum width is the binding's
+    f = Q.make_norm_fold(xc=FAKE + 0x30000, ldxc=256, sumsq_out=FAKE + 0x40000)
+    for tile in (128, 256):
+        assert Q.qi_gemm_norm_fold(FAKE, 256, FAKE + 0x10000, None, FAKE + 0x20000, 256, 256, 256, 256, Q.QI_F16,
+                                   Q.QI_EPI_GATED_RESIDUAL, FAKE, 0, 0, tile, f, None, None) == Q.QI_ERR_ARG
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "qi.h")).read()
+    from image_generation_qi_amd import runtime as rt
+    assert int(re.search(r"#define QI_FOLD_W (\d+)", hdr).group(1)) == rt.FOLD_W
