@@ -380,8 +380,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
     h8 op[2][2];
     read_ops(0, op[0]);
-    ps[0] = 0.f;
-    ps[1] = 0.f;
+    // the row sums from the fp16 probabilities: steps 8-15 add each pair to the pair of the same
+    // row block and keys of the other key half (formed in steps 0-7), four such sums then make a
+    // row block's sum (16 fp16 probabilities, at most 2^8 each, so no partial sum overflows)
+    h2 hs[8];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i + 1 < 16) read_ops(i + 1, op[(i + 1) & 1]);
@@ -414,10 +416,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         asm volatile("" : "+v"(q));
         pf[rb][c][4 * kh + r] = q[0];
         pf[rb][c][4 * kh + r + 1] = q[1];
-        ps[rb] += p0 + p1;
-        asm volatile("" : "+v"(ps[rb]));
+        if (c) {   // (the first key half's pair of these keys is in pf[rb][0])
+          const h2 q0 = {pf[rb][0][4 * kh + r], pf[rb][0][4 * kh + r + 1]};
+          hs[n] = q0 + q;
+          asm volatile("" : "+v"(hs[n]));
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const h2 t = (hs[4 * rb] + hs[4 * rb + 1]) + (hs[4 * rb + 2] + hs[4 * rb + 3]);
+      ps[rb] = (float)t[0] + (float)t[1];
     }
   };
 
