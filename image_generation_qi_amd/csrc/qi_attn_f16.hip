@@ -366,8 +366,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // next tile (dims 32((i-8)/2) .., key blocks 2((i-8)%2), + 1; accumulators starting at minus
   // the reference).  Every step also issues the LDS operand reads of the next step and forms two
   // probabilities 2^s of the current tile (the first key half's scores in steps 0-7, the second's
-  // in steps 8-15; row block (i%8)/4), rounded to fp16 and added (unrounded, fp32) into the row
-  // block's sum; steps 0-3 issue the wave's four copies of later tiles (K of tile tk into K slot
+  // in steps 8-15; row block (i%8)/4), rounded to fp16; steps 8-15 add each fp16 pair to the
+  // first half's pair of the same keys (the row sums); steps 0-3 issue the wave's four copies of
+  // later tiles (K of tile tk into K slot
   // kcs, V of tile tv into V slot vcs).  The empty asm statements keep each step's probability
   // and sum inside that step (compiler passes would otherwise sink them past the iteration's last
   // MFMA, where they would stall the matrix core).  ktag / vtag: the slots the operands come from.
