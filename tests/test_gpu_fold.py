@@ -134,7 +134,7 @@ def test_norm_fold_rows(M, D, row0, P, dt):
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 @pytest.mark.parametrize("tile", [0, 192])   # (the producing side runs 256 x 192 tiles)
-@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("M,N,K", SHAPES + WIDE_K)
 def test_fold_producer(M, N, K, tile, dt):
     say(f"[fold producer] M={M} N={N} K={K} tile={tile} {dt}")
     a = qin.stored(qin.normal(CFG, 320, (M, K)), dt)
