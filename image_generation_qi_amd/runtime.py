@@ -461,9 +461,9 @@ class DiT:
         the modulation and head-scale vectors per step, and with the fold the bias tables of every
         layer for all steps in one pass over its weights (entry 0: the prefix rows' t = 0, entry
         1 + k: the target rows at step k).  step() then copies a step's vectors instead of
-        recomputing them."""
+        recomputing them (and prepares a schedule it has not seen)."""
         n = len(sig) - 1
-        assert 1 <= n <= 15
+        assert n >= 1
         D = self.D
         mods = torch.empty((n, 6, 2, D), dtype=torch.float32, device=self.device)
         hsc = torch.empty((n, 2, D), dtype=torch.float32, device=self.device)
@@ -484,8 +484,9 @@ class DiT:
             tq = torch.empty((nl, n + 1, 3 * D), dtype=torch.float32, device=self.device)
             tg = torch.empty((nl, n + 1, self.bgu.shape[2]), dtype=torch.float32, device=self.device)
             for li, W in enumerate(self.layers):
-                linear_multi(v1, W.w_qkv, tq[li])
-                linear_multi(v2, W.w_gu, tg[li])
+                for j in range(0, n + 1, 16):   # (at most 16 vectors per pass over the weights)
+                    linear_multi(v1[j:j + 16], W.w_qkv, tq[li, j:j + 16])
+                    linear_multi(v2[j:j + 16], W.w_gu, tg[li, j:j + 16])
             tabs = (tq, tg)
         self._sched = (tuple(float(v) for v in sig), mods, hsc, tabs)
         self._k = None
@@ -581,8 +582,9 @@ class DiT:
     def step(self, k: int, lat: torch.Tensor, sig, x_text=None, lat_ref=None):
         """Euler step k (0-based) of the loop: step 0 runs the whole sequence and fills the caches."""
         S, P = self.L.S, self.L.P
-        if not self._use_step(k, sig):
-            self.condition(float(sig[k]))
+        if not self._use_step(k, sig):   # a schedule not prepared yet: prepare it once
+            self.prepare(sig)
+            self._use_step(k, sig)
         self.embed(lat, self.x[P:])
         if k == 0:
             self.set_prefix(x_text, lat_ref)

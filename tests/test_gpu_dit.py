@@ -457,7 +457,7 @@ def test_cached_layer_equals_step1_target_rows_bitwise(fold):
     assert torch.equal(model.x[P:], full_t)
 
 
-@pytest.mark.parametrize("fold,prepared", [(True, True), (True, False), (False, True)])
+@pytest.mark.parametrize("fold,prepared", [(True, True), (True, False), (False, True)])   # (step() prepares itself)
 def test_sampling_loop_small(fold, prepared):
     segments = (qin.text(20), qin.image(6, 5, 1), qin.image(7, 6, 0))
     D, F, n_layers, n_steps = 256, 512, 2, 3
@@ -609,3 +609,18 @@ def test_full_size_layer_norm_fold_sampled(cached):
     x2 = host(x[rows])
     check(host(h[rows]), x2 * (1.0 + W["norm1"]) * (1.0 + sel(1, rows)), "f16", "xc for the next norm1")
     assert model.attn.range_flags() == 0
+
+
+def test_prepared_schedule_equals_per_step_conditioning():
+    # the prepared conditioning of a 17-step schedule (bias tables in two passes of at most 16
+    # vectors) equals the conditioning computed for each step on its own, bit for bit
+    model, _, _ = make_model(SMALL, 256, 512, 2)
+    sig = qin.sigmas(17)
+    model.prepare(sig)
+    for k in (0, 9, 16):
+        assert model._use_step(k, sig)
+        mods = model.mods.clone()
+        tabs = [t.clone() for li in range(2) for t in model._biases(li)]
+        model.condition(float(sig[k]))
+        assert torch.equal(model.mods, mods)
+        assert all(torch.equal(a, b) for a, b in zip(tabs, [t for li in range(2) for t in model._biases(li)]))
