@@ -526,6 +526,8 @@ def main():
     ap.add_argument("--step1", action="store_true", help="also time one full step-1 attention per layer")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 10 device-to-device copies of MIB MiB (reference kernel for HBM counters)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the same step captured in a HIP graph and replayed (launch overheads)")
     ap.add_argument("--dit", action="store_true", help="time full single-stream layer steps instead")
     ap.add_argument("--v1edit", action="store_true",
                     help="time the v1 / Edit-Plus joint full attention (text 512 + target + 2 references) instead")
@@ -688,6 +690,24 @@ def main():
     if res["roofline"]["traffic"] is not None:
         # the traffic figure also comes from that committed summary (same kernel source)
         res["roofline"]["traffic_source"] = os.path.relpath(PROFILE, ROOT)
+    if args.graph:
+        # the same step (32 layers' calls + Euler) captured once and replayed: the launch gaps between
+        # the 97 kernels of a step are what the graph can remove; the value above stays the eager one
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_step(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        gms = e0.elapsed_time(e1) / args.steps
+        extra["graph_ms_per_step"] = round(gms, 4)
+        extra["graph_tflops"] = round(flops_launch * NL / (gms * 1e-3) / 1e12, 2)
+        del graph
     res["config"].update(extra)
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
