@@ -304,6 +304,17 @@ def v1edit_bench(args):
     e1.record()
     torch.cuda.synchronize()
     blk_ms = e0.elapsed_time(e1) / n_blk
+    # the same block with both streams' calls on one stream
+    blk1 = rt.V1Block(rt.V1BlockWeights(Wt), layout, H, dev, two_streams=False)
+    blk1(x_txt, x_img, cond)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n_blk):
+        blk1(x_txt, x_img, cond)
+    e1.record()
+    torch.cuda.synchronize()
+    blk1_ms = e0.elapsed_time(e1) / n_blk
+    del blk1
     blk_flops = 2.0 * S * D * (3 * D + D + 2 * F) + flops
     res = {"metric": "v1 / Edit-Plus joint full attention TFLOP/s per call", "value": round(flops / (ms * 1e-3) / 1e12, 2),
            "unit": "TFLOP/s", "higher_is_better": True, "n_gpus": 1, "steps": args.steps, "dtype": "f16",
@@ -316,7 +327,8 @@ def v1edit_bench(args):
                       # MLPs with the joint attention), random-init weights, D 3072, MLP 12288
                       "block_ms": round(blk_ms, 3), "block_flops": blk_flops,
                       "block_tflops": round(blk_flops / (blk_ms * 1e-3) / 1e12, 1),
-                      "block_attention_share": round(ms / blk_ms, 3)}}
+                      "block_attention_share": round(ms / blk_ms, 3),
+                      "block_ms_one_stream": round(blk1_ms, 3)}}
     print(json.dumps(res), flush=True)
 
 

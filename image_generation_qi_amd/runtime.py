@@ -633,14 +633,19 @@ class V1Block:
     LayerNorm + modulation, the MLP (GEMM with bias and GELU(tanh), GEMM with bias adding
     gate2 * y)."""
 
-    def __init__(self, W: V1BlockWeights, layout: Layout, n_head: int, device="cuda", eps: float = 1e-6):
-        """The activations and the GEMM weights (converted once) are fp16."""
+    def __init__(self, W: V1BlockWeights, layout: Layout, n_head: int, device="cuda", eps: float = 1e-6,
+                 two_streams: bool = True):
+        """The activations and the GEMM weights (converted once) are fp16.  two_streams: the text
+        stream's calls on a second stream beside the image stream's (else all on the calling one)."""
         assert layout.attention == Q.QI_ATTN_FULL
         assert W.D == n_head * 128
         act_dtype = ACT
         self.W, self.L, self.H, self.eps, self.device, self.act = W, layout, n_head, eps, device, act_dtype
         self.att = Attention(layout, n_head, code_of(torch.empty(0, dtype=act_dtype)), device)
         self.w = {name: W[name + "_w"].to(act_dtype) for name in V1_LINEARS if not name.endswith("_mod")}
+        # the text stream's calls run on a second stream (default priority) beside the image
+        # stream's: its 512-row GEMMs fill a fraction of the chip, and the image GEMMs fill the rest
+        self.side = torch.cuda.Stream(device=device) if two_streams else None
 
     def __call__(self, x_txt: torch.Tensor, x_img: torch.Tensor, cond: torch.Tensor, n_noise: Optional[int] = None):
         """x_txt fp32 [Lt][D] and x_img fp32 [Li][D] (updated in place and returned); cond fp32
@@ -654,33 +659,52 @@ class V1Block:
         assert cond.shape == (2, D) and cond.dtype == torch.float32 and cond.is_contiguous()
         streams = (("txt", x_txt, 0, Lt, Lt, "norm_added_q", "norm_added_k"),
                    ("img", x_img, Lt, Li, Li if n_noise is None else n_noise, "norm_q", "norm_k"))
-        # modulation: chunk i of a stream for both conditioning rows, [2][D] each
-        mods = {}
-        for name, *_ in streams:
-            m = torch.empty((6, 2, D), dtype=torch.float32, device=dev)
+        # every buffer is allocated on the calling stream before the two streams fork
+        mods = {name: torch.empty((6, 2, D), dtype=torch.float32, device=dev) for name, *_ in streams}
+        h = torch.empty((S, D), dtype=self.act, device=dev)
+        qkv = torch.empty((S, 3, H, 128), dtype=self.act, device=dev)
+        o = torch.empty((S, H, 128), dtype=self.act, device=dev)
+        acts = {name: torch.empty((n, W.F), dtype=self.act, device=dev) for name, _, _, n, *_ in streams}
+        fl, w = self.att.flags, self.w
+        main = torch.cuda.current_stream(dev)
+        side = self.side if self.side is not None else main
+
+        def pre(name, x, r0, n, P, nq, nk):
+            # modulation (chunk i of the stream for both conditioning rows, [2][D] each), LayerNorm
+            # + modulation, the QKV projection into the joint buffer, the stream's QK-RMSNorm
+            m = mods[name]
             for i in range(6):
                 linear_small(cond, W[name + "_mod_w"][i * D:(i + 1) * D], m[i], True,
                              W[name + "_mod_b"][i * D:(i + 1) * D])
-            mods[name] = m
-        h = torch.empty((S, D), dtype=self.act, device=dev)
-        qkv = torch.empty((S, 3, H, 128), dtype=self.act, device=dev)
-        fl, w = self.att.flags, self.w
-        for name, x, r0, n, P, nq, nk in streams:
-            m = mods[name]
             layernorm_mod(x, h[r0:r0 + n], m[1], m[0], 0, P, eps, flags=fl)
             gemm(h[r0:r0 + n], w[name + "_qkv"], qkv[r0:r0 + n].view(n, 3 * D), Q.QI_EPI_STORE,
                  bias=W[name + "_qkv_b"], flags=fl)
             rope3d_apply(qkv[r0:r0 + n, 0], None, None, W[nq], eps)
             rope3d_apply(qkv[r0:r0 + n, 1], None, None, W[nk], eps)
-        o = self.att.full(qkv[:, 0], qkv[:, 1], qkv[:, 2])
-        a = torch.empty((max(Lt, Li), W.F), dtype=self.act, device=dev)
-        for name, x, r0, n, P, nq, nk in streams:
+
+        def post(name, x, r0, n, P, nq, nk):
+            # out-projection into the residual, LayerNorm + modulation, the GELU MLP into the residual
             m = mods[name]
             gemm(o[r0:r0 + n].view(n, D), w[name + "_out"], x, Q.QI_EPI_GATED_RESIDUAL_LINEAR, m[2], 0, P,
                  bias=W[name + "_out_b"])
             layernorm_mod(x, h[r0:r0 + n], m[4], m[3], 0, P, eps, flags=fl)
-            gemm(h[r0:r0 + n], w[name + "_fc1"], a[:n], Q.QI_EPI_GELU, bias=W[name + "_fc1_b"], flags=fl)
-            gemm(a[:n], w[name + "_fc2"], x, Q.QI_EPI_GATED_RESIDUAL_LINEAR, m[5], 0, P, bias=W[name + "_fc2_b"])
+            a = acts[name]
+            gemm(h[r0:r0 + n], w[name + "_fc1"], a, Q.QI_EPI_GELU, bias=W[name + "_fc1_b"], flags=fl)
+            gemm(a, w[name + "_fc2"], x, Q.QI_EPI_GATED_RESIDUAL_LINEAR, m[5], 0, P, bias=W[name + "_fc2_b"])
+
+        # the text stream on the side stream, the image stream on the calling one; they join for the
+        # joint attention and at the end (the streams touch disjoint rows of h, qkv and o)
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            pre(*streams[0])
+        pre(*streams[1])
+        main.wait_stream(side)
+        self.att.full(qkv[:, 0], qkv[:, 1], qkv[:, 2], out=o)
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            post(*streams[0])
+        post(*streams[1])
+        main.wait_stream(side)
         return x_txt, x_img
 
 
