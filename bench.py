@@ -527,6 +527,75 @@ def data_sensitivity_bench(args):
         torch.cuda.empty_cache()
 
 
+def gemm_sweep_bench(args):
+    """The layer GEMM at 4,096 rows over a sweep of reduction lengths K, with each epilogue the
+    denoiser uses at that shape (fp16 store, fp32 store, tanh-gated residual, gated residual with
+    the norm fold's producing side), beside hipBLASLt (torch.matmul, fp16, plain store) on the same
+    operands.  A line fit over K separates the time that grows with K (per 64-deep slice) from the
+    time each launch pays once (launch, first slices' loads, the epilogue's traffic).  One JSON line
+    per (N, K) and one per epilogue with the fit."""
+    import torch
+
+    from image_generation_qi_amd import qi as Q
+    from image_generation_qi_amd import runtime as rt
+
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(11)
+    M = 4096
+
+    def ev_median(f, n=20):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        for i in range(n):
+            ev[i].record()
+            f()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(n))[n // 2] * 1000.0
+
+    fits = {}
+    for N in (3072, 9216):
+        for K in (64, 768, 3072, 8192):
+            x = (torch.randn((M, K), generator=g, device=dev) * 0.5).half()
+            w = (torch.randn((N, K), generator=g, device=dev) / K ** 0.5).half()
+            wt = w.t()
+            o16 = torch.empty((M, N), device=dev, dtype=torch.float16)
+            o32 = torch.empty((M, N), device=dev)
+            cases = {"store_f16": lambda: rt.gemm(x, w, o16, Q.QI_EPI_STORE, tile_n=192),
+                     "store_f32": lambda: rt.gemm(x, w, o32, Q.QI_EPI_STORE_F32, tile_n=192),
+                     "hipblaslt_f16": lambda: torch.matmul(x, wt, out=o16)}
+            if N == 3072:
+                gate = torch.randn((2, N), generator=g, device=dev) * 0.1
+                nw = torch.randn(N, generator=g, device=dev) * 0.1
+                ns = torch.randn((2, N), generator=g, device=dev) * 0.1
+                h = torch.empty((M, N), device=dev, dtype=torch.float16)
+                sq = torch.empty((M, rt.fold_parts(N)), device=dev)
+                fold = rt.NormFold(xc=h, next_w=nw, next_scale=ns, sumsq_out=sq)
+                cases["gated"] = lambda: rt.gemm(x, w, o32, Q.QI_EPI_GATED_RESIDUAL, gate, 0, 0, tile_n=192)
+                cases["gated_norm_fold"] = lambda: rt.gemm(x, w, o32, Q.QI_EPI_GATED_RESIDUAL, gate, 0, 0, fold=fold)
+            us = {name: round(ev_median(f), 1) for name, f in cases.items()}
+            for name, t in us.items():
+                fits.setdefault((N, name), {})[K] = t
+            fl = 2.0 * M * N * K
+            print(json.dumps({"metric": "layer GEMM time per launch (HIP events, median of 20)", "unit": "us",
+                              "value": us["store_f16"], "higher_is_better": False, "n_gpus": 1, "dtype": "f16",
+                              "data": "synthetic",
+                              "config": {"workload": f"{M} x {N} x {K}", "us": us,
+                                         "tflops": {k: round(fl / (t * 1e-6) / 1e12, 1) for k, t in us.items()}}}),
+                  flush=True)
+            del x, w, wt, o16, o32
+    for (N, name), t in fits.items():
+        per_slice = (t[8192] - t[3072]) / ((8192 - 3072) / 64)
+        print(json.dumps({"metric": "layer GEMM line fit over K (3,072 and 8,192)", "unit": "us",
+                          "value": round(t[3072] - 48 * per_slice, 1), "higher_is_better": False, "n_gpus": 1,
+                          "dtype": "f16", "data": "synthetic",
+                          "config": {"workload": f"{M} x {N}", "epilogue": name,
+                                     "us_per_64_deep_slice": round(per_slice, 3),
+                                     "fixed_us_per_launch": round(t[3072] - 48 * per_slice, 1)}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -545,6 +614,8 @@ def main():
                     help="time the v1 / Edit-Plus joint full attention (text 512 + target + 2 references) instead")
     ap.add_argument("--configs", action="store_true",
                     help="time the other attention workloads instead (one JSON line each)")
+    ap.add_argument("--gemm-sweep", action="store_true",
+                    help="time the layer GEMM at 4,096 rows over a sweep of K with each epilogue, beside hipBLASLt")
     ap.add_argument("--data-sensitivity", action="store_true",
                     help="time the headline cached step on N(0,1), low-mantissa, ones and zeros inputs instead")
     args = ap.parse_args()
@@ -570,6 +641,11 @@ def main():
         from image_generation_qi_amd import qi as Q
         Q.lib()
         data_sensitivity_bench(args)
+        return
+    if args.gemm_sweep:
+        from image_generation_qi_amd import qi as Q
+        Q.lib()
+        gemm_sweep_bench(args)
         return
 
     import torch
