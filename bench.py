@@ -11,6 +11,9 @@ resident in HBM before timing starts.
     python bench.py --dit [--layers L] [--steps K]     # full single-stream layer steps (see below)
     python bench.py --v1edit [--steps K]                # v1 / Edit-Plus full joint attention
     python bench.py --configs [--steps K]               # the other attention workloads, one line each
+    python bench.py --graph                             # also the step replayed from a HIP graph
+    python bench.py --data-sensitivity                  # the headline step on inputs of other statistics
+    python bench.py --gemm-sweep                        # the layer GEMM over K, each epilogue, hipBLASLt
 
 Prints one JSON line.  value = attention TFLOP/s over the timed steps (visible-pair flops,
 4*d per pair); roofline = one attention call's average device time (the attention kernel plus,
