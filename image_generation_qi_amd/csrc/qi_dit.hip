@@ -565,33 +565,62 @@ __global__ void k_timestep_embed(const float* t, int n, int dim, float* out) {
   out[(int64_t)j * dim + half + i] = (float)sin(arg);
 }
 
-// y[v][o] = sum_i act(x[v][i]) * W[o][i] for v < nv <= 4; one wavefront per output o.
+// y[v][o] = sum_i act(x[v][i]) * W[o][i] for v < nv <= 4; one wavefront per output o.  Memory-bound
+// on W: each lane issues the loads of all its W chunks of a batch of the row before it uses any
+// (batches of 3,072 elements: a whole row at hidden 3072, and three workgroups with their 48 KB of
+// LDS fit a CU, so the 768 workgroups of O = 3072 run in one round), and act(x) of the batch is
+// formed once per workgroup in LDS.  Lane l sums elements 8l + 512k + e in order of k then e; the
+// 64 lane sums are combined in a fixed order.
+constexpr int LS_CH = 6;                  // W chunks of 8 elements per lane and batch
+constexpr int LS_B = 512 * LS_CH;         // elements per batch
 __global__ __launch_bounds__(256) void k_linear_small(const float* __restrict__ x, int nv, int I,
                                                      const __bf16* __restrict__ w, const float* __restrict__ bias,
                                                      int O, int silu_in, float* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) float xs[4 * LS_B];   // act(x) of the batch, [v][element]
   const int o = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (o >= O) return;
+  const bool live = o < O;   // (every wave takes part in the batches' barriers)
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  const __bf16* wr = w + (int64_t)o * I;
-  for (int i = 8 * lane; i < I; i += 512) {
-    const u32x4 wv = *(const u32x4*)(wr + i);
-    float wf[8];
+  const __bf16* wr = w + (int64_t)(live ? o : 0) * I;
+  for (int i0 = 0; i0 < I; i0 += LS_B) {
+    // this lane's W chunks: chunks past the row read its last chunk and are not used
+    u32x4 wv[LS_CH];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      wf[2 * e] = bf_lo(wv[e]);
-      wf[2 * e + 1] = bf_hi(wv[e]);
+    for (int k = 0; k < LS_CH; ++k) {
+      const int i = i0 + 512 * k + 8 * lane;
+      wv[k] = *(const u32x4*)(wr + (i < I ? i : I - 8));
     }
-    for (int v = 0; v < nv; ++v) {
-      const float* xr = x + (int64_t)v * I + i;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float xe = xr[e];
+    const int nb = I - i0 < LS_B ? I - i0 : LS_B;   // elements in this batch
+    for (int j = threadIdx.x; j < nv * LS_B; j += 256) {
+      const int v = j / LS_B, e = j % LS_B;
+      if (e < nb) {
+        float xe = x[(int64_t)v * I + i0 + e];
         if (silu_in) xe = xe / (1.0f + __expf(-xe));
-        acc[v] = __builtin_fmaf(xe, wf[e], acc[v]);
+        xs[j] = xe;
       }
     }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < LS_CH; ++k) {
+      const int e0 = 512 * k + 8 * lane;
+      if (e0 < nb) {
+        float wf[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          wf[2 * q] = bf_lo(wv[k][q]);
+          wf[2 * q + 1] = bf_hi(wv[k][q]);
+        }
+        for (int v = 0; v < nv; ++v) {
+          const f32x4 a0 = *(const f32x4*)(xs + v * LS_B + e0), a1 = *(const f32x4*)(xs + v * LS_B + e0 + 4);
+          const float xe[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[v] = __builtin_fmaf(xe[e], wf[e], acc[v]);
+        }
+      }
+    }
+    __syncthreads();   // the batch's act(x) has been read before the next batch overwrites it
   }
+  if (!live) return;
   for (int v = 0; v < nv; ++v) {
     float s = acc[v];
 #pragma unroll

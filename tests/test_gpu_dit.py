@@ -299,7 +299,9 @@ def test_timestep_embed():
 
 
 @pytest.mark.parametrize("nv,I,O_,silu", [(2, 256, 3072, False), (2, 3072, 3072, True), (1, 8, 5, True),
-                                           (4, 520, 70, False), (3, 3072, 18432, True)])
+                                           (4, 520, 70, False), (3, 3072, 18432, True),
+                                           # rows of several 3,072-element batches, the last ragged
+                                           (2, 8200, 70, True), (1, 3080, 33, False), (4, 6144, 130, True)])
 def test_linear_small(nv, I, O_, silu):
     say(f"[linear small] nv={nv} I={I} O={O_} silu={silu}")
     x = qin.normal(CFG, 250, (nv, I), std=2.0).astype(np.float32).astype(np.float64)
@@ -309,6 +311,19 @@ def test_linear_small(nv, I, O_, silu):
     sync()
     ref = O.linear(O.silu(x) if silu else x, w.f64)
     check(host(y), ref, "f32", "linear_small")
+
+
+def test_linear_small_rows_independent_of_vector_count():
+    # each vector's sums take the same order whatever the number of vectors in the call
+    x = qin.normal(CFG, 251, (4, 3072), std=2.0).astype(np.float32)
+    w = bf(qin.linear_weight(CFG, 61, 200, 3072))
+    y4 = torch.empty((4, 200), dtype=torch.float32, device=DEV)
+    rt.linear_small(f32(x), w, y4, True)
+    for v in range(4):
+        y1 = torch.empty((1, 200), dtype=torch.float32, device=DEV)
+        rt.linear_small(f32(x[v:v + 1]), w, y1, True)
+        sync()
+        assert torch.equal(y1[0], y4[v])
 
 
 def test_cast_bf16_bit_exact():
