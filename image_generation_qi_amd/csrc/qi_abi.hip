@@ -48,6 +48,14 @@ int check_cache(const qi_kvcache* c, int32_t io_dtype, int32_t n_head, int32_t l
   return QI_OK;
 }
 
+// fp16 K/V tiles of n keys for n_head heads.
+int check_tiles(const qi_kvtiles* t, int32_t n_head, int64_t n) {
+  if (!t || !t->k || !t->v) return QI_ERR_ARG;
+  if (t->n_head != n_head || t->rows < rows64(n) || (t->rows % 64)) return QI_ERR_SHAPE;
+  if (!aligned16(t->k) || !aligned16(t->v)) return QI_ERR_ALIGN;
+  return QI_OK;
+}
+
 float softmax_scale(float scale) { return scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)QI_HEAD_DIM)); }
 
 // rows per head of a cache: fp16 caches are padded to whole 64-key tiles
@@ -662,6 +670,142 @@ int qi_kernel_timing_read_each(float* ms, int64_t cap, int64_t* n) {
   }
   *n = (int64_t)g_used;
   return QI_OK;
+}
+
+
+int qi_gemm_qkv_tiles(const void* x, int64_t ldx, const void* w, const float* bias, void* q_out, int64_t ldq,
+                      int64_t M, int32_t n_head, int64_t K, int32_t dtype, int64_t row0, int64_t P, int64_t T,
+                      const qi_norm_fold* fold, const qi_qkprep* prep, const qi_kvcache* cache, int32_t layer,
+                      const qi_kvtiles* target, uint32_t* range_flags, void* stream) {
+  clear_hip_error();
+  if (!x || !w || !q_out) return QI_ERR_ARG;
+  if (dtype != QI_BF16 && dtype != QI_F16) return QI_ERR_DTYPE;
+  if (n_head < 1 || n_head > 4096 || M < 0 || K < 64 || (K % 64) || row0 < 0 || P < 0 || T < 1) return QI_ERR_SHAPE;
+  if (P + T > INT32_MAX || row0 + M > P + T) return QI_ERR_SHAPE;
+  const int64_t N = 3 * (int64_t)n_head * QI_HEAD_DIM;
+  if (ldx < K || ldq < (int64_t)n_head * QI_HEAD_DIM) return QI_ERR_SHAPE;
+  // x and w are addressed through buffer resources with 32-bit byte offsets
+  if (M > INT32_MAX / 2 / ldx || N > INT32_MAX / 2 / K) return QI_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(q_out) || !aligned16(bias) || (ldx % 8) || (ldq % 8) ||
+      (reinterpret_cast<uintptr_t>(range_flags) & 3))
+    return QI_ERR_ALIGN;
+  int st;
+  if ((st = check_prep(prep)) != QI_OK) return st;
+  const bool any_pre = M > 0 && row0 < P, any_tgt = M > 0 && row0 + M > P;
+  if (any_pre && (st = check_cache(cache, dtype, n_head, layer, P)) != QI_OK) return st;
+  if (any_tgt && (st = check_tiles(target, n_head, T)) != QI_OK) return st;
+  GemmArgs a{x, ldx, w, q_out, ldq, M, N, K, nullptr, row0, P, bias, range_flags};
+  if (fold) {
+    if (fold->xc || fold->sumsq_out || fold->next_w || fold->next_scale) return QI_ERR_ARG;   // consuming side only
+    if (fold->sumsq && (!(fold->eps >= 0.f) || !std::isfinite(fold->eps))) return QI_ERR_ARG;
+    if (!aligned16(fold->sumsq) || !aligned16(fold->bias_t)) return QI_ERR_ALIGN;
+    a.bias_t = fold->bias_t;
+    a.sumsq = fold->sumsq;
+    a.eps = fold->eps;
+  }
+  a.n_head = n_head;
+  if (any_pre) {
+    a.kA = (void*)cache_layer(cache->k, cache, layer);
+    a.vA = (void*)cache_layer(cache->v, cache, layer);
+    a.hsA = cache_rows(cache) * QI_HEAD_DIM;
+  }
+  if (any_tgt) {
+    a.kB = target->k;
+    a.vB = target->v;
+    a.hsB = target->rows * QI_HEAD_DIM;
+  }
+  if (prep) {
+    a.cos_t = prep->cos_t;
+    a.sin_t = prep->sin_t;
+    a.k_rms_w = prep->k_rms_w;
+    a.qk_eps = prep->eps;
+  }
+  a.vfast = (row0 % 64 == 0) && (P % 64 == 0) && ((row0 + M) % 64 == 0 || row0 + M == P + T);
+  if (M == 0) return QI_OK;
+  hipStream_t s = (hipStream_t)stream;
+  // the keys past each source's last in its last tile, when this call writes that source's last key
+  hipError_t e = hipSuccess;
+  if (any_pre && row0 + M >= P && (P % 64))
+    e = launch_kv_tile_zero(a.kA, a.vA, a.hsA, n_head, (P - 1) / 64, (int32_t)(P % 64), s);
+  if (e == hipSuccess && any_tgt && row0 + M == P + T && (T % 64))
+    e = launch_kv_tile_zero(a.kB, a.vB, a.hsB, n_head, (T - 1) / 64, (int32_t)(T % 64), s);
+  if (e != hipSuccess) return launch_status(e);
+  return launch_status(launch_gemm_kv_tiles(a, dtype == QI_F16, s));
+}
+
+int qi_attn_target_cached_tiled(const qi_qkv* io, const qi_qkprep* prep, const qi_kvcache* cache, int32_t layer,
+                                int64_t P, float scale, const qi_kvtiles* target, void* workspace,
+                                int64_t workspace_bytes, void* stream) {
+  clear_hip_error();
+  if (!io) return QI_ERR_ARG;
+  int st;
+  if ((st = check_tensor(io->q, io->dtype, io->n_tok, io->n_head, io->tok_stride)) != QI_OK) return st;
+  if (io->dtype == QI_F32) return QI_ERR_DTYPE;
+  if (!io->o) return QI_ERR_ARG;
+  if (!aligned16(io->o)) return QI_ERR_ALIGN;
+  if ((st = check_prep(prep)) != QI_OK) return st;
+  if ((st = check_cache(cache, io->dtype, io->n_head, layer, P)) != QI_OK) return st;
+  if ((st = check_tiles(target, io->n_head, io->n_tok)) != QI_OK) return st;
+  if (P + io->n_tok > INT32_MAX) return QI_ERR_SHAPE;
+  if (P > QI_MAX_SOURCE_KEYS || io->n_tok > QI_MAX_SOURCE_KEYS) return QI_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(io->lse) & 3) || (reinterpret_cast<uintptr_t>(io->range_flags) & 3))
+    return QI_ERR_ALIGN;
+  const int64_t need = attn_f16_partial_bytes(io->n_tok, io->n_head);
+  if (need > 0 && !workspace) return QI_ERR_ARG;
+  if (!aligned16(workspace)) return QI_ERR_ALIGN;
+  if (workspace_bytes < need) return QI_ERR_CAPACITY;
+  AttnArgs a = attn_args(io, prep, scale);
+  a.masked = 0;
+  a.kA = cache_layer(cache->k, cache, layer);
+  a.vA = cache_layer(cache->v, cache, layer);
+  a.a_head_stride = cache_rows(cache) * QI_HEAD_DIM;
+  a.nA = P;
+  a.kB = target->k;
+  a.vB = target->v;
+  a.b_head_stride = target->rows * QI_HEAD_DIM;
+  a.nB = io->n_tok;
+  a.q_row0 = P;
+  set_partials(a, (char*)workspace, io->dtype);   // after nA, nB
+  return run_attn(a, io->dtype, (hipStream_t)stream);
+}
+
+int qi_attn_blockcausal_full_tiled(const qi_qkv* io, const qi_qkprep* prep, const qi_layout* layout, float scale,
+                                   const qi_kvcache* cache, int32_t layer, const qi_kvtiles* target, void* workspace,
+                                   int64_t workspace_bytes, void* stream) {
+  clear_hip_error();
+  if (!io) return QI_ERR_ARG;
+  LayoutInfo li;
+  int st = analyse_layout(layout, &li);
+  if (st != QI_OK) return st;
+  if ((st = check_tensor(io->q, io->dtype, io->n_tok, io->n_head, io->tok_stride)) != QI_OK) return st;
+  if (io->dtype == QI_F32) return QI_ERR_DTYPE;
+  if (!io->o) return QI_ERR_ARG;
+  if (!aligned16(io->o)) return QI_ERR_ALIGN;
+  if (io->n_tok != li.S) return QI_ERR_SHAPE;
+  if (li.P > QI_MAX_SOURCE_KEYS || li.T > QI_MAX_SOURCE_KEYS) return QI_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(io->lse) & 3) || (reinterpret_cast<uintptr_t>(io->range_flags) & 3))
+    return QI_ERR_ALIGN;
+  if ((st = check_prep(prep)) != QI_OK) return st;
+  if ((st = check_cache(cache, io->dtype, io->n_head, layer, li.P)) != QI_OK) return st;
+  if ((st = check_tiles(target, io->n_head, li.T)) != QI_OK) return st;
+  const int64_t need = qi_attn_tiled_workspace_bytes(layout, io->n_head);
+  if (need < 0) return (int)need;
+  if (need > 0 && !workspace) return QI_ERR_ARG;
+  if (!aligned16(workspace)) return QI_ERR_ALIGN;
+  if (workspace_bytes < need) return QI_ERR_CAPACITY;
+  AttnArgs a = attn_args(io, prep, scale);
+  a.masked = 1;
+  a.segs = li.tab;
+  a.q_row0 = 0;
+  a.kA = cache_layer(cache->k, cache, layer);
+  a.vA = cache_layer(cache->v, cache, layer);
+  a.a_head_stride = cache_rows(cache) * QI_HEAD_DIM;
+  a.nA = li.P;
+  a.kB = target->k;
+  a.vB = target->v;
+  a.b_head_stride = target->rows * QI_HEAD_DIM;
+  a.nB = li.T;
+  return run_attn_step1_f16(a, li.tab, li.P, li.T, (char*)workspace, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -30,6 +30,7 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -60,6 +61,28 @@ __device__ __forceinline__ uint32_t pack2(float a, float b, bool& bad) {
     return __builtin_bit_cast(uint32_t, v);
   } else {
     return to_bf16(a) | (to_bf16(b) << 16);
+  }
+}
+
+// The value of the lane whose index differs in bit 0 (quad_xor1) or bit 1 (quad_xor2): DPP
+// quad permutes [1, 0, 3, 2] and [2, 3, 0, 1].
+__device__ __forceinline__ float quad_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
+// Four consecutive dims d .. d + 3 of key slot j of a 64-key V tile of the attention (fp16, [2 key
+// halves][4 key groups][128 dims][8 keys], element e of group g of half c holding key 32c +
+// 16(e / 4) + 4g + e % 4): one 2-byte store each (a dim's keys are 16 bytes apart from the next
+// dim's).  Values that fp16 cannot hold set `bad`.
+__device__ __forceinline__ void store_v_tile(_Float16* vt, int j, int d, const f32x4& y, bool& bad) {
+  _Float16* p = vt + (((j >> 5) * 4 + ((j & 15) >> 2)) * 128 + d) * 8 + ((j >> 4) & 1) * 4 + (j & 3);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    bad |= !(fabsf(y[e]) < 65520.0f);
+    p[8 * e] = (_Float16)y[e];
   }
 }
 
@@ -288,6 +311,207 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
     read_x(st ^ 1, 0, xf[0]);   // (unused after the last slice)
     read_w(st ^ 1, 0, wf[0]);
+  }
+
+  if constexpr (EPI == EPI_KV_TILES || EPI == EPI_KV_TILES_EACH) {
+    // The QKV projection writing the attention's operands ("Qwen-Image-2.1" course overview, cards
+    // 4A and 6A: per-head QK-RMSNorm and the 3D rotation of K, the prefix K/V stored once; source
+    // reading, section 6: the per-head norm, then RoPE).  Weight rows in the tile order: tile tn < H
+    // holds K of head tn (tile columns 0..127) and its V dims 0..63 (128..191); the later tiles hold
+    // V dims 64..127 of every head (64 columns per head from column 192 H), then Q (from 256 H).
+    // The norm and the rotation are selects, not branches (no norm: r = w = 1; no tables: cos = 1,
+    // sin = 0), so the unrolled epilogue exists once: its code, not its arithmetic, is what costs.
+    static_assert(BN == 192, "the K/V tile epilogue runs 256 x 192 tiles");
+    constexpr bool VPIECES = EPI == EPI_KV_TILES;   // V as 16-byte pieces (whole key tiles per wave)
+    const int H = a.n_head;
+    const bool kvt = tn < H;                    // workgroup-uniform
+    const bool knorm = kvt && a.k_rms_w;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int64_t m = m0 + WTM * wm + 16 * mb + l16;
+      const bool tgt = m + a.row0 >= a.P;
+      if (a.sumsq) {   // norm fold: the row's rrms, then the bias of shift W^T
+        const float r = rr_s[WTM * wm + 16 * mb + l16];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] *= r;
+      }
+      if (has_bias) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[mb][nb] += *(const f32x4*)(bs_s + (tgt ? BN : 0) + WTN * wn + 16 * nb + 4 * G);
+      }
+    }
+    // K's sum of squares per row as 8 block sums of 16 features (the stages are free now), each
+    // block summed in one fixed order and the blocks added in a fixed order, so the K bits do not
+    // depend on which rows a launch covers: wave column 0 holds blocks 0..5, wave column 1 blocks
+    // 6 and 7
+    float* ks_s = (float*)smem;   // [256 rows][8]
+    if (knorm) {
+      const int nbk = wn == 0 ? 6 : 2;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          if (nb < nbk) {
+            const f32x4 y = acc[mb][nb];
+            float v = (y[0] * y[0] + y[1] * y[1]) + (y[2] * y[2] + y[3] * y[3]);
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            if (G == 0) ks_s[(WTM * wm + 16 * mb + l16) * 8 + 6 * wn + nb] = v;
+          }
+        }
+      __syncthreads();
+    }
+    bool badk = false, badv = false, bado = false;
+    f32x4 kwv[NB];   // the K columns' norm weights (1 without a norm)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int cb = WTN * wn + 16 * nb;
+      kwv[nb] = (knorm && cb < 128) ? *(const f32x4*)(a.k_rms_w + cb + 4 * G) : f32x4{1.f, 1.f, 1.f, 1.f};
+    }
+    // The rotation factors of the tile's rows go through LDS (after the K sums, in the free
+    // stages): in two passes, row blocks 0, 1 then 2, 3 of every wave (128 rows, cos then sin, a
+    // row every TS floats), loaded as whole 16-byte pieces of the tables' rows.
+    constexpr int TS = 136;                     // floats per staged row (64 cos, 64 sin, padding)
+    float* const tab_s = (float*)smem + 256 * 8;
+    const bool rot = a.cos_t != nullptr;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if (kvt && (mb & 1) == 0) {
+        if (mb) __syncthreads();                // every wave has read the previous pass's rows
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int idx = tid + 512 * i, sl = idx >> 5, ch = idx & 31;   // staged row, piece
+          const int64_t mr = m0 + 64 * (sl >> 5) + 16 * mb + (sl & 31);
+          f32x4 v = ch < 16 ? f32x4{1.f, 1.f, 1.f, 1.f} : f32x4{0.f, 0.f, 0.f, 0.f};
+          if (rot && mr < a.M) v = *(const f32x4*)((ch < 16 ? a.cos_t : a.sin_t) + mr * 64 + 4 * (ch & 15));
+          *(f32x4*)(tab_s + sl * TS + 4 * ch) = v;
+        }
+        __syncthreads();
+      }
+      const int rl = WTM * wm + 16 * mb + l16;
+      const int64_t m = m0 + rl;
+      if (m >= a.M) continue;
+      const int64_t g = m + a.row0;
+      const bool pre = g < a.P;
+      const int64_t j = pre ? g : g - a.P;
+      const int slot = (int)(j & 63);
+      const int64_t hs = pre ? a.hsA : a.hsB;
+      if (kvt) {
+        _Float16* const kt = (_Float16*)(pre ? a.kA : a.kB) + (j >> 6) * 8192 + tn * hs;
+        const float* const trow = tab_s + (32 * wm + 16 * (mb & 1) + l16) * TS;
+        const f32x4 b0 = *(const f32x4*)(ks_s + rl * 8), b1 = *(const f32x4*)(ks_s + rl * 8 + 4);
+        const float ss = ((b0[0] + b0[1]) + (b0[2] + b0[3])) + ((b1[0] + b1[1]) + (b1[2] + b1[3]));
+        const float r = knorm ? rsqrtf(ss * (1.0f / 128.0f) + a.qk_eps) : 1.0f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          // tile column c: K dim c, or V dim c - 128 (the test on the block's first column is
+          // wave-uniform: wn is)
+          const int cb = WTN * wn + 16 * nb, c = cb + 4 * G;
+          f32x4 y = acc[mb][nb];
+          if (cb < 128) {
+            const f32x4 w = kwv[nb];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = y[e] * r * w[e];
+            const f32x2 cs = *(const f32x2*)(trow + c / 2);      // the pairs (c, c + 1), (c + 2, c + 3)
+            const f32x2 sn = *(const f32x2*)(trow + 64 + c / 2);
+            const float x0 = y[0], x1 = y[1], x2 = y[2], x3 = y[3];
+            y[0] = x0 * cs[0] - x1 * sn[0];
+            y[1] = x0 * sn[0] + x1 * cs[0];
+            y[2] = x2 * cs[1] - x3 * sn[1];
+            y[3] = x2 * sn[1] + x3 * cs[1];
+            *(u32x2*)(kt + ((c >> 3) * 64 + slot) * 8 + (c & 7)) =
+                u32x2{pack2<true>(y[0], y[1], badk), pack2<true>(y[2], y[3], badk)};
+          } else if constexpr (!VPIECES) {
+            _Float16* const vt = (_Float16*)(pre ? a.vA : a.vB) + (j >> 6) * 8192 + tn * hs;
+            store_v_tile(vt, slot, c - 128, y, badv);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int64_t nbase = n0 + WTN * wn + 16 * nb, n = nbase + 4 * G;   // (N % 16 == 0)
+          if (nbase >= a.N) continue;
+          const f32x4 y = acc[mb][nb];
+          if (nbase < 256 * (int64_t)H) {   // V dims 64 + (n - 192 H) % 64 .. of head (n - 192 H) / 64
+            if constexpr (!VPIECES) {
+              const int64_t i = n - 192 * (int64_t)H;
+              _Float16* const vt = (_Float16*)(pre ? a.vA : a.vB) + (j >> 6) * 8192 + (i >> 6) * hs;
+              store_v_tile(vt, slot, 64 + (int)(i & 63), y, badv);
+            }
+          } else {                      // Q
+            *(u32x2*)((E*)a.out + m * a.ldo + (n - 256 * (int64_t)H)) =
+                u32x2{pack2<F16>(y[0], y[1], bado), pack2<F16>(y[2], y[3], bado)};
+          }
+        }
+      }
+    }
+    if constexpr (VPIECES) {
+      if (m0 + WTM * wm < a.M) {
+        // V as whole 16-byte pieces: the wave's 64 rows are key slots 0..63 of one tile, row 16 mb
+        // + l16 slot 16 mb + l16, so the piece of (dim d, key group g, half c) -- keys 32c + 4g + e
+        // and 32c + 16 + 4g + e, e = 0..3 -- lies in row blocks 2c and 2c + 1 of the four lanes l16
+        // = 4g .. 4g + 3 that hold d.  A transpose among those four lanes (lane 4g + r then holds
+        // dim 4G + r of the lane group's 16 columns for the four keys) gives each lane one piece
+        // per half.  Rows at or past M (keys past the last, within the last tile) are written as
+        // zero.
+        const int64_t g0 = m0 + WTM * wm + a.row0;
+        const bool pre = g0 < a.P;
+        const int64_t j0 = pre ? g0 : g0 - a.P;
+        _Float16* const vt = (_Float16*)(pre ? a.vA : a.vB) + (j0 >> 6) * 8192;
+        const int64_t hs = pre ? a.hsA : a.hsB;
+        const int r = l16 & 3, gk = l16 >> 2;
+        const bool odd = r & 1, hi = r & 2;
+        // t[i] = (the value of lane 4gk + i at index r), a 4 x 4 transpose within each quad of
+        // lanes in two butterfly stages (partners r ^ 1, then r ^ 2, by DPP quad permutes): after
+        // the first, lane r holds its pair's values of columns r & ~1 .. of its 2 x 2 blocks
+        auto tr4 = [&](const f32x4& v, float (&t)[4]) {
+          const float r1 = quad_xor1(odd ? v[0] : v[1]);
+          const float r2 = quad_xor1(odd ? v[2] : v[3]);
+          const float b0 = odd ? r1 : v[0], b1 = odd ? v[1] : r1, b2 = odd ? r2 : v[2], b3 = odd ? v[3] : r2;
+          const float s0 = quad_xor2(hi ? b0 : b2), s1 = quad_xor2(hi ? b1 : b3);
+          t[0] = hi ? s0 : b0;
+          t[1] = hi ? s1 : b1;
+          t[2] = hi ? b2 : s0;
+          t[3] = hi ? b3 : s1;
+        };
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          // this 16-column block's head and first V dim (uniform over the lane groups)
+          int64_t head;
+          int d0;
+          if (kvt) {
+            const int c = WTN * wn + 16 * nb;
+            if (c < 128) continue;
+            head = tn;
+            d0 = c - 128;
+          } else {
+            const int64_t n = n0 + WTN * wn + 16 * nb;
+            if (n >= 256 * (int64_t)H || n >= a.N) continue;
+            head = (n - 192 * (int64_t)H) >> 6;
+            d0 = 64 + (int)((n - 192 * (int64_t)H) & 63);
+          }
+          const int d = d0 + 4 * G + r;
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            f32x4 lo = acc[2 * c][nb], hi = acc[2 * c + 1][nb];
+            if (m0 + WTM * wm + 32 * c + l16 >= a.M) lo = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (m0 + WTM * wm + 32 * c + 16 + l16 >= a.M) hi = f32x4{0.f, 0.f, 0.f, 0.f};
+            float b0[4] = {0.f, 0.f, 0.f, 0.f}, b1[4] = {0.f, 0.f, 0.f, 0.f};
+            tr4(lo, b0);
+            tr4(hi, b1);
+            *(u32x4*)(vt + head * hs + ((c * 4 + gk) * 128 + d) * 8) =
+                u32x4{pack2<true>(b0[0], b0[1], badv), pack2<true>(b0[2], b0[3], badv),
+                      pack2<true>(b1[0], b1[1], badv), pack2<true>(b1[2], b1[3], badv)};
+          }
+        }
+      }
+    }
+    if (a.flags) {
+      const uint32_t f = (badk ? QI_RANGE_K : 0u) | (badv ? QI_RANGE_V : 0u) | ((F16 && bado) ? QI_RANGE_OUT : 0u);
+      if (f) atomicOr(a.flags, f);
+    }
+    return;
   }
 
   // epilogue: acc[mb][nb][r] = y[m][n], m = m0 + 64wm + 16mb + l16, n = n0 + WTN*wn + 16nb + 4G + r
@@ -692,6 +916,18 @@ __global__ __launch_bounds__(256) void k_linear_multi(const float* __restrict__ 
   }
 }
 
+// Zero key slots [slot0, 64) of key tile `tile` of every head (blockIdx.x) of fp16 K/V tiles: the
+// keys past a source's last in its last tile, which the attention multiplies by zero probability.
+__global__ __launch_bounds__(64) void k_kv_tile_zero(uint16_t* k, uint16_t* v, int64_t hs, int64_t tile, int slot0) {
+  const int j = threadIdx.x;
+  if (j < slot0) return;
+  uint16_t* kt = k + blockIdx.x * hs + tile * 8192;
+  uint16_t* vt = v + blockIdx.x * hs + tile * 8192 + ((j >> 5) * 4 + ((j & 15) >> 2)) * 1024 + ((j >> 4) & 1) * 4 + (j & 3);
+#pragma unroll
+  for (int c = 0; c < 16; ++c) *(u32x4*)(kt + (c * 64 + j) * 8) = u32x4{0u, 0u, 0u, 0u};
+  for (int d = 0; d < 128; ++d) vt[d * 8] = 0;
+}
+
 __global__ void k_cast_bf16(const float* __restrict__ x, __bf16* __restrict__ y, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) ((uint16_t*)y)[i] = (uint16_t)to_bf16(x[i]);
@@ -824,6 +1060,28 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, int tile_n, bool f16, hipStre
   // the norm fold's producing side writes one partial sum per wave of a 256 x 192 tile
   const int bn = a.xc ? 192 : tile_n ? tile_n : gemm_config(a.M, a.N, epi);
   return f16 ? launch_big_f16(a, epi, bn, s) : launch_big_bf16(a, epi, bn, s);
+}
+
+hipError_t launch_gemm_kv_tiles(const GemmArgs& a, bool f16, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)(((a.M + BBM - 1) / BBM) * ((a.N + 191) / 192));
+  if (f16 && a.vfast)
+    hipLaunchKernelGGL((k_gemm_big<EPI_KV_TILES, 192, true>), dim3(blocks), dim3(512), 0, s, a);
+  else if (f16)
+    hipLaunchKernelGGL((k_gemm_big<EPI_KV_TILES_EACH, 192, true>), dim3(blocks), dim3(512), 0, s, a);
+  else if (a.vfast)
+    hipLaunchKernelGGL((k_gemm_big<EPI_KV_TILES, 192, false>), dim3(blocks), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_gemm_big<EPI_KV_TILES_EACH, 192, false>), dim3(blocks), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_tile_zero(void* k, void* v, int64_t head_stride, int32_t n_head, int64_t tile, int32_t slot0,
+                               hipStream_t s) {
+  if (n_head <= 0 || slot0 >= 64) return hipSuccess;
+  hipLaunchKernelGGL(k_kv_tile_zero, dim3((unsigned)n_head), dim3(64), 0, s, (uint16_t*)k, (uint16_t*)v, head_stride,
+                     tile, slot0);
+  return hipGetLastError();
 }
 
 hipError_t launch_zc_norm_mod(const NormArgs& a, bool f16, hipStream_t s) {

@@ -100,7 +100,7 @@ const char* qi_status_str(int status) {
   }
 }
 
-int qi_version(void) { return 8; }
+int qi_version(void) { return 9; }
 
 int qi_layout_tokens(const qi_layout* layout, int64_t* S, int64_t* P, int64_t* T) {
   LayoutInfo li;
@@ -245,6 +245,17 @@ int64_t qi_attn_cached_workspace_bytes(int32_t dtype, int64_t T, int32_t n_head)
   const int64_t r = rows_bytes(dtype, rows64(T), n_head);
   if (r < 0) return r;
   return r + partial_bytes(dtype, T, n_head);
+}
+
+int64_t qi_attn_tiled_workspace_bytes(const qi_layout* layout, int32_t n_head) {
+  LayoutInfo li;
+  int st = analyse_layout(layout, &li);
+  if (st != QI_OK) return st;
+  if (n_head < 1) return QI_ERR_SHAPE;
+  // the partial outputs only: the cached step's target launch, or step 1's two launches (shared)
+  const int64_t pt = attn_f16_partial_bytes(li.T, n_head);
+  const int64_t pp = attn_prefix_tiles_equal(li.tab, li.P, li.T) ? attn_f16_partial_bytes(li.P, n_head) : 0;
+  return pt > pp ? pt : pp;
 }
 
 int64_t qi_kvcache_bytes(int32_t cache_dtype, int32_t n_layers, int32_t n_head, int64_t p_cap) {

@@ -136,7 +136,30 @@ struct GemmArgs {
   const float* nw;     // nullable fp32 [N]
   const float* nscale; // nullable fp32 [2][N]
   float* sumsq_out;
+  // K/V tile epilogue (EPI_KV_TILES*, 256 x 192 tiles): the QKV projection with its weight rows in
+  // the tile order (for each head h: K_h, then V_h dims 0..63; then V_h dims 64..127 of every head;
+  // then Q), writing Q rows to out and K (RMSNorm with k_rms_w, rotation) and V as fp16 attention
+  // tiles: row m is token row0 + m, tokens < P into the A tiles (slot = token), the others into
+  // the B tiles (slot = token - P); head strides in elements; cos_t/sin_t [M][64] by row.
+  int32_t n_head;
+  void* kA;
+  void* vA;
+  int64_t hsA;
+  void* kB;
+  void* vB;
+  int64_t hsB;
+  const float* cos_t;   // nullable: no rotation
+  const float* sin_t;
+  const float* k_rms_w; // nullable: no norm
+  float qk_eps;
+  // every wave's 64 rows are one whole key tile of one source (row0 and P multiples of 64, and the
+  // call ends on a tile boundary or at the last token): V leaves as 16-byte pieces
+  int32_t vfast;
 };
+// Internal epilogue codes of the K/V tile epilogue (not qi_epilogue values): V written as whole
+// 16-byte pieces (vfast launches) or element by element.
+constexpr int EPI_KV_TILES = 16;
+constexpr int EPI_KV_TILES_EACH = 17;
 // ZeroCenterRMSNorm + modulation of fp32 rows into bf16 rows.
 struct NormArgs {
   const float* x;
@@ -162,6 +185,12 @@ struct NormArgs {
 // f16: x, w and the 16-bit outputs are fp16 (else bf16).
 hipError_t launch_gemm(const GemmArgs& a, int epilogue, int tile_n, bool f16, hipStream_t s);
 int gemm_config(int64_t M, int64_t N, int epilogue);
+// The K/V tile epilogue's GEMM (a.n_head and the tile fields set; N = 384 n_head, fp16 or bf16 x
+// and w), and the zero fill of key slots [slot0, 64) of key tile `tile` of every head of one
+// source's fp16 tiles (the padding of a ragged last tile).
+hipError_t launch_gemm_kv_tiles(const GemmArgs& a, bool f16, hipStream_t s);
+hipError_t launch_kv_tile_zero(void* k, void* v, int64_t head_stride, int32_t n_head, int64_t tile, int32_t slot0,
+                               hipStream_t s);
 hipError_t launch_zc_norm_mod(const NormArgs& a, bool f16, hipStream_t s);   // f16: fp16 output (else bf16)
 hipError_t launch_timestep_embed(const float* t, int n, int dim, float* out, hipStream_t s);
 hipError_t launch_linear_small(const float* x, int nv, int I, const void* w, const float* bias, int O, int silu_in, float* y,

@@ -26,7 +26,7 @@ QI_SEG_TEXT, QI_SEG_IMAGE, QI_SEG_TEXT_BIDIR = 0, 1, 2
 QI_EPI_STORE, QI_EPI_STORE_F32, QI_EPI_GATED_RESIDUAL, QI_EPI_SWIGLU, QI_EPI_GELU = 0, 1, 2, 3, 4
 QI_EPI_GATED_RESIDUAL_LINEAR = 5
 QI_MAX_SOURCE_KEYS = 8388607   # keys per source of the bf16 attention (include/qi.h)
-QI_ABI_VERSION = 8             # the qi_version() these bindings are written against
+QI_ABI_VERSION = 9             # the qi_version() these bindings are written against
 QI_NOALLOC_SCRATCH_BYTES = 96 << 20   # scratch array of qi_attn_target_cached_noalloc (include/qi.h)
 QI_ATTN_BLOCK_CAUSAL, QI_ATTN_FULL = 0, 1
 QI_RANGE_Q, QI_RANGE_K, QI_RANGE_V, QI_RANGE_OUT = 1, 2, 4, 8   # range flags of fp16 values (include/qi.h)
@@ -71,6 +71,10 @@ class qi_qkv(ctypes.Structure):
 class qi_qkprep(ctypes.Structure):
     _fields_ = [("cos_t", c_void_p), ("sin_t", c_void_p), ("q_rms_w", c_void_p), ("k_rms_w", c_void_p),
                 ("eps", c_float)]
+
+
+class qi_kvtiles(ctypes.Structure):
+    _fields_ = [("k", c_void_p), ("v", c_void_p), ("n_head", c_int32), ("rows", c_int64)]
 
 
 class qi_norm_fold(ctypes.Structure):
@@ -130,6 +134,15 @@ _SIGS = {
     "qi_norm_fold_rows": (c_int, [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p,
                                   c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p]),
     "qi_linear_multi": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+    "qi_attn_tiled_workspace_bytes": (c_int64, [POINTER(qi_layout), c_int32]),
+    "qi_gemm_qkv_tiles": (c_int, [c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int32, c_int64,
+                                  c_int32, c_int64, c_int64, c_int64, POINTER(qi_norm_fold), POINTER(qi_qkprep),
+                                  POINTER(qi_kvcache), c_int32, POINTER(qi_kvtiles), c_void_p, c_void_p]),
+    "qi_attn_target_cached_tiled": (c_int, [POINTER(qi_qkv), POINTER(qi_qkprep), POINTER(qi_kvcache), c_int32,
+                                            c_int64, c_float, POINTER(qi_kvtiles), c_void_p, c_int64, c_void_p]),
+    "qi_attn_blockcausal_full_tiled": (c_int, [POINTER(qi_qkv), POINTER(qi_qkprep), POINTER(qi_layout), c_float,
+                                               POINTER(qi_kvcache), c_int32, POINTER(qi_kvtiles), c_void_p, c_int64,
+                                               c_void_p]),
     "qi_kernel_timing": (c_int, [c_int]),
     "qi_kernel_timing_read": (c_int, [POINTER(c_double), POINTER(c_int64)]),
     "qi_kernel_timing_read_each": (c_int, [POINTER(c_float), c_int64, POINTER(c_int64)]),
@@ -220,6 +233,10 @@ def make_cache(k, v, dtype: int, n_layers: int, n_head: int, p_cap: int) -> qi_k
     return qi_kvcache(_p(k), _p(v), dtype, n_layers, n_head, p_cap)
 
 
+def make_tiles(k, v, n_head: int, rows: int) -> qi_kvtiles:
+    return qi_kvtiles(_p(k), _p(v), n_head, rows)
+
+
 # ------------------------------------------------------------------------------------------------
 # the C ABI, same names
 # ------------------------------------------------------------------------------------------------
@@ -308,6 +325,33 @@ def qi_attn_target_cached_noalloc(io: qi_qkv, prep: Optional[qi_qkprep], cache: 
                                   scale: float, stream=None) -> int:
     return lib().qi_attn_target_cached_noalloc(ctypes.byref(io), _ref(prep), _ref(cache), layer, P, scale,
                                                _p(stream))
+
+
+def qi_attn_tiled_workspace_bytes(layout: qi_layout, n_head: int) -> int:
+    return lib().qi_attn_tiled_workspace_bytes(ctypes.byref(layout), n_head)
+
+
+def qi_gemm_qkv_tiles(x, ldx: int, w, bias, q_out, ldq: int, M: int, n_head: int, K: int, dtype: int, row0: int,
+                      P: int, T: int, fold: Optional[qi_norm_fold], prep: Optional[qi_qkprep],
+                      cache: Optional[qi_kvcache], layer: int, target: Optional[qi_kvtiles], range_flags=None,
+                      stream=None) -> int:
+    return lib().qi_gemm_qkv_tiles(_p(x), ldx, _p(w), _p(bias), _p(q_out), ldq, M, n_head, K, dtype, row0, P, T,
+                                   _ref(fold), _ref(prep), _ref(cache), layer, _ref(target), _p(range_flags),
+                                   _p(stream))
+
+
+def qi_attn_target_cached_tiled(io: qi_qkv, prep: Optional[qi_qkprep], cache: qi_kvcache, layer: int, P: int,
+                                scale: float, target: qi_kvtiles, workspace, workspace_bytes: int, stream=None) -> int:
+    return lib().qi_attn_target_cached_tiled(ctypes.byref(io), _ref(prep), _ref(cache), layer, P, scale,
+                                             _ref(target), _p(workspace), workspace_bytes, _p(stream))
+
+
+def qi_attn_blockcausal_full_tiled(io: qi_qkv, prep: Optional[qi_qkprep], layout: qi_layout, scale: float,
+                                   cache: qi_kvcache, layer: int, target: qi_kvtiles, workspace,
+                                   workspace_bytes: int, stream=None) -> int:
+    return lib().qi_attn_blockcausal_full_tiled(ctypes.byref(io), _ref(prep), ctypes.byref(layout), scale,
+                                                _ref(cache), layer, _ref(target), _p(workspace), workspace_bytes,
+                                                _p(stream))
 
 
 def qi_euler_step(x, v, v_dtype: int, n: int, sigma_k: float, sigma_k1: float, stream=None) -> int:

@@ -87,6 +87,30 @@ class KVCache:
         return t.reshape(H, self.rows, 128)
 
 
+class KVTiles:
+    """fp16 K/V tiles of one key source outside a cache (qi_kvtiles): the target tokens of the fused
+    QKV path, written by gemm_qkv_tiles and read by Attention.cached_tiled / full_tiled.  k, v:
+    [n_head][R][128] storage in the fp16 cache's tile layout (R = n_keys rounded up to 64)."""
+
+    def __init__(self, n_keys: int, n_head: int, device="cuda"):
+        self.rows = max((n_keys + 63) // 64 * 64, 64)
+        self.n_head = n_head
+        self.k = torch.zeros((n_head, self.rows, 128), dtype=torch.float16, device=device)
+        self.v = torch.zeros_like(self.k)
+        self.c = Q.make_tiles(self.k, self.v, n_head, self.rows)
+
+    def k_rows(self) -> torch.Tensor:
+        """K as [n_head][R][128] rows (a copy)."""
+        H = self.n_head
+        return self.k.reshape(H, self.rows // 64, 16, 64, 8).permute(0, 1, 3, 2, 4).reshape(H, self.rows, 128)
+
+    def v_rows(self) -> torch.Tensor:
+        """V as [n_head][R][128] rows (a copy)."""
+        H = self.n_head
+        t = self.v.reshape(H, self.rows // 64, 2, 4, 128, 2, 4).permute(0, 1, 2, 5, 3, 6, 4)
+        return t.reshape(H, self.rows, 128)
+
+
 def _ws(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
@@ -104,8 +128,10 @@ class Attention:
         self.L, self.H, self.dtype, self.device = layout, n_head, io_dtype, device
         self.ws_full_bytes = Q.qi_attn_full_workspace_bytes(layout.c, io_dtype, n_head)
         self.ws_cached_bytes = Q.qi_attn_cached_workspace_bytes(io_dtype, layout.T, n_head)
+        self.ws_tiled_bytes = Q.qi_attn_tiled_workspace_bytes(layout.c, n_head) if io_dtype != Q.QI_F32 else 0
         self.ws_full = None
         self.ws_cached = None
+        self.ws_tiled = None
         self.flags = torch.zeros(1, dtype=torch.int32, device=device)
 
     def range_flags(self, clear: bool = True) -> int:
@@ -170,6 +196,38 @@ class Attention:
         return o
 
 
+    def _tiled_ws(self):
+        if self.ws_tiled is None:
+            self.ws_tiled = _ws(self.ws_tiled_bytes, self.device)
+        return self.ws_tiled
+
+    def cached_tiled(self, q_t, cache: KVCache, layer: int, target: KVTiles, q_w=None, eps=1e-6, scale: float = 0.0,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     rotate: bool = True) -> torch.Tensor:
+        """A cached target step whose target K/V are already tiles (written by gemm_qkv_tiles)."""
+        T = q_t.shape[0]
+        o = out if out is not None else torch.empty((T, self.H, 128), dtype=q_t.dtype, device=self.device)
+        io = Q.make_qkv(q_t, None, None, o, self.dtype, T, self.H, self._stride(q_t), lse, self.flags)
+        prep, keep = self.prep(slice(self.L.P, self.L.P + T), q_w, None, eps, rotate)
+        Q.check(Q.qi_attn_target_cached_tiled(io, prep, cache.c, layer, self.L.P, scale, target.c, self._tiled_ws(),
+                                              self.ws_tiled_bytes, stream_handle(self.device)),
+                "qi_attn_target_cached_tiled")
+        return o
+
+    def full_tiled(self, q, cache: KVCache, layer: int, target: KVTiles, q_w=None, eps=1e-6, scale: float = 0.0,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   rotate: bool = True) -> torch.Tensor:
+        """Step 1 with the prefix K/V in cache layer `layer` and the target's in `target`, both
+        already tiles (written by gemm_qkv_tiles)."""
+        o = out if out is not None else torch.empty((self.L.S, self.H, 128), dtype=q.dtype, device=self.device)
+        io = Q.make_qkv(q, None, None, o, self.dtype, self.L.S, self.H, self._stride(q), lse, self.flags)
+        prep, keep = self.prep(slice(0, self.L.S), q_w, None, eps, rotate)
+        Q.check(Q.qi_attn_blockcausal_full_tiled(io, prep, self.L.c, scale, cache.c, layer, target.c, self._tiled_ws(),
+                                                 self.ws_tiled_bytes, stream_handle(self.device)),
+                "qi_attn_blockcausal_full_tiled")
+        return o
+
+
 def euler_step(x: torch.Tensor, v: torch.Tensor, sigma_k: float, sigma_k1: float):
     assert x.dtype == torch.float32 and x.is_contiguous() and v.is_contiguous() and v.numel() == x.numel()
     vd = Q.QI_BF16 if v.dtype == torch.bfloat16 else Q.QI_F32
@@ -209,6 +267,50 @@ def pack_swiglu(w_gate: torch.Tensor, w_up: torch.Tensor) -> torch.Tensor:
     F, D = w_gate.shape
     assert w_up.shape == (F, D) and F % 32 == 0
     return torch.stack([w_gate.reshape(F // 32, 32, D), w_up.reshape(F // 32, 32, D)], dim=1).reshape(2 * F, D).contiguous()
+
+
+def pack_qkv_tiles(w_qkv: torch.Tensor, n_head: int) -> torch.Tensor:
+    """Rows of W_qkv [3D][D_in] (the Q, K and V rows, D = 128 n_head each) in the tile order that
+    gemm_qkv_tiles reads: for each head h, the rows of K_h then of V_h dims 0..63; then the rows of
+    V_h dims 64..127 of every head; then the Q rows."""
+    D = 128 * n_head
+    assert w_qkv.shape[0] == 3 * D
+    k = w_qkv[D:2 * D].reshape(n_head, 128, -1)
+    v = w_qkv[2 * D:].reshape(n_head, 128, -1)
+    first = torch.cat([k, v[:, :64]], dim=1).reshape(n_head * 192, -1)
+    return torch.cat([first, v[:, 64:].reshape(n_head * 64, -1), w_qkv[:D]], dim=0).contiguous()
+
+
+def gemm_qkv_tiles(x: torch.Tensor, w: torch.Tensor, q_out: torch.Tensor, n_head: int, row0: int, P: int, T: int,
+                   cache: Optional[KVCache], layer: int, target: Optional[KVTiles], tables=None, k_w=None,
+                   eps: float = 1e-6, bias=None, flags=None, fold: Optional["NormFold"] = None):
+    """The QKV projection writing Q rows to q_out and K/V as attention tiles (qi_gemm_qkv_tiles):
+    x [M][K] rows are tokens row0.. of a sequence of P prefix and T target tokens; w in the tile
+    order (pack_qkv_tiles); tables = (cos, sin) rows of those tokens (None: no rotation); k_w the
+    K RMSNorm weight (None: no norm)."""
+    M, K = x.shape
+    assert x.dtype in (torch.bfloat16, torch.float16) and w.dtype == x.dtype and x.stride(1) == 1
+    assert w.shape == (384 * n_head, K) and q_out.dtype == x.dtype and q_out.stride(1) == 1 and q_out.shape[0] >= M
+    cos, sin = tables if tables is not None else (None, None)
+    prep = Q.make_prep(cos, sin, None, k_w, eps)
+    fs = None
+    if fold is not None:
+        fold.check(M, 384 * n_head, K, x.dtype)
+        fs = fold.struct()
+    Q.check(Q.qi_gemm_qkv_tiles(x, x.stride(0), w, bias, q_out, q_out.stride(0), M, n_head, K, code_of(x), row0, P, T,
+                                fs, prep, cache.c if cache is not None else None, layer,
+                                target.c if target is not None else None, flags, stream_handle(x.device)),
+            "qi_gemm_qkv_tiles")
+    return q_out
+
+
+def unpack_qkv_tiles(w_tiles: torch.Tensor, n_head: int) -> torch.Tensor:
+    """The inverse of pack_qkv_tiles: rows back in the Q | K | V order."""
+    perm = pack_qkv_tiles(torch.arange(w_tiles.shape[0], device=w_tiles.device, dtype=torch.float32)[:, None],
+                          n_head)[:, 0].long()
+    w = torch.empty_like(w_tiles)
+    w[perm] = w_tiles
+    return w
 
 
 class LayerWeights:
@@ -398,21 +500,31 @@ class DiT:
     buffers and issues the calls in order on the current stream."""
 
     def __init__(self, layout: Layout, shared: SharedWeights, layers, device="cuda", eps: float = 1e-6,
-                 fold: bool = True):
+                 fold: bool = True, kv_tiles: bool = False):
         """The layer chain's 16-bit activations (normed rows, QKV, attention output, SwiGLU output,
         the latents into img_in) and the projection weights are fp16 (the weights converted once
-        from the model's bf16).  fold: the layer's two norms folded into its GEMMs (qi_norm_fold;
-        seven launches per cached layer) instead of launched on their own (nine)."""
+        from the model's bf16).  fold: the layer's two norms folded into its GEMMs (qi_norm_fold)
+        instead of launched on their own (two launches more per layer).  kv_tiles: the QKV
+        projection writes K (normed, rotated) and V as the attention's fp16 tiles
+        (qi_gemm_qkv_tiles, its weights packed once in the tile order), so no K/V preparation
+        launch runs and a cached layer is six launches; off by default, because its epilogue
+        (after the MFMA loop, in every round of tiles) costs more than the preparation launch it
+        replaces at the model's shapes."""
         self.L, self.sw, self.device, self.eps, self.act = layout, shared, device, eps, ACT
         self.fold = fold
+        self.kv_tiles = kv_tiles
         act_dtype = ACT
         self.layers = [W.as_dtype(act_dtype) for W in layers]
+        if kv_tiles:
+            for W in self.layers:
+                W.w_qkv = pack_qkv_tiles(W.w_qkv, W.D // 128)
         self.w_in, self.w_head = shared.w_in.to(act_dtype), shared.w_head.to(act_dtype)
         self.D = shared.D
         self.H = self.D // 128
         self.F = self.layers[0].F if self.layers else 0
         self.attn = Attention(layout, self.H, code_of(torch.empty(0, dtype=act_dtype)), device)
         self.cache = KVCache(len(self.layers), self.H, layout.P, self.attn.dtype, device)
+        self.kvt = KVTiles(layout.T, self.H, device) if kv_tiles else None
         S, D = layout.S, self.D
         bf, f32 = act_dtype, torch.float32
         self.flags = self.attn.flags                                    # QI_RANGE_* of every call
@@ -437,6 +549,19 @@ class DiT:
         self.bgu = torch.empty((nl, 2, 2 * max(self.F, 1)), dtype=f32, device=device)
         self._sched = None     # conditioning of a whole schedule (prepare)
         self._k = None         # the schedule's step whose conditioning is current
+
+    def use_kv_tiles(self, on: bool):
+        """Switch the fused QKV path on or off (repacks the QKV weights; the next step prepares
+        its schedule's bias tables again, since their columns follow the weight rows)."""
+        if on == self.kv_tiles:
+            return
+        for W in self.layers:
+            W.w_qkv = pack_qkv_tiles(W.w_qkv, self.H) if on else unpack_qkv_tiles(W.w_qkv, self.H)
+        if on and self.kvt is None:
+            self.kvt = KVTiles(self.L.T, self.H, self.device)
+        self.kv_tiles = on
+        self._sched = None
+        self._k = None
 
     # -- conditioning ------------------------------------------------------------------------
     def condition(self, sigma: float):
@@ -522,10 +647,27 @@ class DiT:
             bq_p, bq_t, bg_p, bg_t = self._biases(li)
             if li == 0:
                 norm_fold_rows(x, h, sq, W.norm1, m[1], r0, P, flags=fl)
-            gemm(h, W.w_qkv, qkv, Q.QI_EPI_STORE, None, r0, P, bias=bq_p, flags=fl, fold=NormFold(sq, eps, bq_t))
+            qfold, qbias = NormFold(sq, eps, bq_t), bq_p
         else:
             norm_mod(x, h, W.norm1, m[1], m[0], r0, P, eps, flags=fl)
-            gemm(h, W.w_qkv, qkv, Q.QI_EPI_STORE, flags=fl)
+            qfold, qbias = None, None
+        if self.kv_tiles:
+            # Q rows into qkv[:, :D]; K and V as tiles: prefix tokens into the cache, target tokens
+            # into kvt; then the attention on those tiles
+            gemm_qkv_tiles(h, W.w_qkv, qkv[:, :D], self.H, r0, P, self.L.T, self.cache, li, self.kvt,
+                           self.L.rows(r0, r0 + n), W.k_norm, eps, bias=qbias, flags=fl, fold=qfold)
+            qv = qkv[:, :D].view(n, self.H, 128)
+            if cached:
+                self.attn.cached_tiled(qv, self.cache, li, self.kvt, W.q_norm, eps, out=o)
+            else:
+                self.attn.full_tiled(qv, self.cache, li, self.kvt, W.q_norm, eps, out=o)
+        else:
+            gemm(h, W.w_qkv, qkv, Q.QI_EPI_STORE, None, r0, P, bias=qbias, flags=fl, fold=qfold)
+            self._attention(li, qkv, o, n, cached)
+        self._rest(li, W, x, h, o, a, n, r0, P)
+
+    def _attention(self, li: int, qkv, o, n: int, cached: bool):
+        W, D, eps = self.layers[li], self.D, self.eps
         q = qkv[:, :D].view(n, self.H, 128)
         k = qkv[:, D:2 * D].view(n, self.H, 128)
         v = qkv[:, 2 * D:].view(n, self.H, 128)
@@ -533,7 +675,13 @@ class DiT:
             self.attn.cached(q, k, v, self.cache, li, W.q_norm, W.k_norm, eps, out=o)
         else:
             self.attn.full(q, k, v, W.q_norm, W.k_norm, eps, cache=self.cache, layer=li, out=o)
+
+    def _rest(self, li: int, W, x, h, o, a, n: int, r0: int, P: int):
+        """The out-projection, the FFN and their residual updates."""
+        D, eps, m, fl = self.D, self.eps, self.mods, self.flags
         if self.fold:
+            sq = self.sq[:n]
+            _, _, bg_p, bg_t = self._biases(li)
             gemm(o.view(n, D), W.w_out, x, Q.QI_EPI_GATED_RESIDUAL, m[2], r0, P, flags=fl,
                  fold=NormFold(xc=h, next_w=W.norm2, next_scale=m[4], sumsq_out=sq))
             gemm(h, W.w_gu, a, Q.QI_EPI_SWIGLU, None, r0, P, bias=bg_p, flags=fl, fold=NormFold(sq, eps, bg_t))

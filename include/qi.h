@@ -168,6 +168,17 @@ typedef struct {
   float eps;
 } qi_qkprep;
 
+/* fp16 K/V tiles of one key source outside a cache (the target tokens of the fused QKV path):
+ * k and v each [n_head][rows][128] fp16 in the fp16 cache's tile layout (qi_kvcache, QI_F16),
+ * rows a multiple of 64 and at least the source's key count rounded up to one; device memory
+ * owned by the caller, 16-byte aligned. */
+typedef struct {
+  void* k;
+  void* v;
+  int32_t n_head;
+  int64_t rows;
+} qi_kvtiles;
+
 /* ------------------------------------------------------------------------------------------
  * Host-only helpers (no device work; usable without a GPU)
  * ------------------------------------------------------------------------------------------ */
@@ -179,7 +190,9 @@ const char* qi_status_str(int status);
  * range flags and int32_t dtype fields, 4 the allocation-free cached step, 5 fp16 activations
  * (QI_F16 attention I/O, qi_gemm, qi_norm_mod, qi_cast), 6 the fp16 cache's tile layout for the
  * 16 x 16 x 32 matrix-core operands, 7 the key counts of qi_attn_schedule, 8 the norm fold:
- * qi_gemm_norm_fold, qi_norm_fold_rows, qi_linear_multi). */
+ * qi_gemm_norm_fold, qi_norm_fold_rows, qi_linear_multi, 9 the fused QKV path: qi_kvtiles,
+ * qi_gemm_qkv_tiles, qi_attn_target_cached_tiled, qi_attn_blockcausal_full_tiled,
+ * qi_attn_tiled_workspace_bytes). */
 int qi_version(void);
 
 /* Token counts of a layout: S = all, P = prefix (all but the last segment), T = target.
@@ -228,6 +241,10 @@ int qi_attn_schedule(int64_t n_q, int32_t n_head, int64_t n_keys_a, int64_t n_ke
  * Negative = error status. */
 int64_t qi_attn_full_workspace_bytes(const qi_layout* layout, int32_t dtype, int32_t n_head);
 int64_t qi_attn_cached_workspace_bytes(int32_t dtype, int64_t T, int32_t n_head);
+/* Workspace bytes of qi_attn_target_cached_tiled (the layout's T target rows) and
+ * qi_attn_blockcausal_full_tiled over `layout`: the partial outputs of the key chunks only (the
+ * K/V tiles are the caller's).  May be 0.  Negative = error status. */
+int64_t qi_attn_tiled_workspace_bytes(const qi_layout* layout, int32_t n_head);
 
 /* Bytes of one cache tensor (k or v) for the given shape (fp16 rows padded to a multiple of
  * 64).  Negative = error status. */
@@ -288,6 +305,27 @@ int qi_attn_target_cached(const qi_qkv* io, const qi_qkprep* prep, const qi_kvca
 #define QI_NOALLOC_SCRATCH_BYTES (96ll << 20)
 int qi_attn_target_cached_noalloc(const qi_qkv* io, const qi_qkprep* prep, const qi_kvcache* cache,
                                   int32_t layer, int64_t P, float scale, void* stream);
+
+/* The fused QKV path's attention (the fused layer of [OV] cards 4A and 6A): the K/V operands
+ * were written as fp16 tiles by qi_gemm_qkv_tiles (the prefix into cache layer `layer` at step 1,
+ * the target into `target`), so these calls launch only the attention and the merge of its key
+ * chunks.  io->q, io->o, dtype (QI_BF16 or QI_F16; QI_ERR_DTYPE otherwise), n_tok, n_head,
+ * tok_stride, lse and range_flags as in qi_attn_target_cached / qi_attn_blockcausal_full; io->k
+ * and io->v are not read.  prep: the Q side only (cos_t/sin_t rows of the queries, q_rms_w, eps).
+ * workspace: at least qi_attn_tiled_workspace_bytes(layout, n_head) bytes (NULL when that is 0).
+ * Errors as those calls, and QI_ERR_ARG / QI_ERR_SHAPE / QI_ERR_ALIGN for a NULL, too small
+ * (rows < the key count rounded up to 64, or not a multiple of 64), other-head-count or misaligned
+ * `target`.  Given the same tiles, the outputs equal those of the unfused calls bit for bit.
+ *   - cached step: the T = io->n_tok target queries against the P cached keys and the T target
+ *     keys of `target`; prep tables hold the target rows.
+ *   - step 1: all S queries of `layout` (io->n_tok = S) under its mask against the P prefix keys
+ *     of the cache and the T target keys of `target` (cache required). */
+int qi_attn_target_cached_tiled(const qi_qkv* io, const qi_qkprep* prep, const qi_kvcache* cache, int32_t layer,
+                                int64_t P, float scale, const qi_kvtiles* target, void* workspace,
+                                int64_t workspace_bytes, void* stream);
+int qi_attn_blockcausal_full_tiled(const qi_qkv* io, const qi_qkprep* prep, const qi_layout* layout, float scale,
+                                   const qi_kvcache* cache, int32_t layer, const qi_kvtiles* target, void* workspace,
+                                   int64_t workspace_bytes, void* stream);
 
 /* Euler update of the latent ([OV] learning goals, card 6B): x[i] += (sigma_k1 - sigma_k) * v[i]
  * for i < n.  x: device fp32; v: device, QI_F32 or QI_BF16.  The step is computed in fp32. */
@@ -450,6 +488,38 @@ int qi_gemm_norm_fold(const void* x, int64_t ldx, const void* w, const float* bi
                       int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t epilogue, const float* gate,
                       int64_t row0, int64_t P, int32_t tile_n, const qi_norm_fold* fold, uint32_t* range_flags,
                       void* stream);
+
+/* The QKV projection writing the attention's operands (the fused layer of [OV] cards 4A and 6A:
+ * RoPE and the prefix K/V store in the projection's epilogue; [EDIT] section 6: per-head
+ * QK-RMSNorm, then the rotation): y = x W^T with x `dtype` (QI_BF16 or QI_F16) [M][ldx] and W
+ * `dtype` [3 * 128 * n_head][K] holding the rows of W_q, W_k, W_v in the TILE ORDER: for each head
+ * h, the 128 rows of K_h then the rows of V_h dims 0..63; then the rows of V_h dims 64..127 for
+ * each head h; then the rows of Q in their order.  Row m of x is token row0 + m of a sequence of
+ * P prefix and T target tokens (row0 + M <= P + T).  Each output row gets the bias of its class
+ * (`bias`, or fold->bias_t for target rows) and, with fold->sumsq, the norm fold's rrms (the
+ * consuming side of qi_norm_fold; its producing fields must be NULL).  Then:
+ *   - Q (128 n_head values): `dtype` into q_out [M][ldq] (ldq >= 128 n_head), unrotated (the
+ *     attention rotates Q as it loads it);
+ *   - K of each head: RMSNorm over its 128 values with prep->k_rms_w and prep->eps (none if
+ *     k_rms_w is NULL; the sum of squares in a fixed order, so the bits do not depend on M or
+ *     row0), then the rotation with prep->cos_t/sin_t ([M][64], row i for row i of x; none if
+ *     NULL), rounded once to fp16;
+ *   - V of each head: rounded once to fp16;
+ *   K and V of prefix tokens into cache layer `layer` (QI_F16 cache, key slot = token), of target
+ *   tokens into `target` (slot = token - P), in the tile layout of qi_kvcache.  When the call
+ *   writes a source's last key, the rest of that source's last tile is zeroed.  prep->q_rms_w is
+ *   not used.  256 x 192 workgroup tiles; K % 64 == 0.  Values that fp16 cannot hold raise
+ *   QI_RANGE_K / QI_RANGE_V (and QI_RANGE_OUT for an fp16 Q) in *range_flags (may be NULL).
+ * Errors: QI_ERR_ARG (NULL x, w or q_out, producing fold fields, bad eps, NULL cache or target
+ * when rows of that source are written), QI_ERR_DTYPE (dtype; a cache that is not QI_F16),
+ * QI_ERR_SHAPE (n_head outside 1..4096, M < 0, K, ldx < K, ldq, row0 < 0, P < 0, T < 1, row0 + M >
+ * P + T, 32-bit operand offsets; cache or target of another head count, target rows too few),
+ * QI_ERR_CAPACITY (layer or P outside the cache), QI_ERR_ALIGN (x, w, q_out, bias, the fold's and
+ * prep's arrays, cache and target not 16-byte aligned, ldx or ldq % 8), QI_ERR_HIP (launch). */
+int qi_gemm_qkv_tiles(const void* x, int64_t ldx, const void* w, const float* bias, void* q_out, int64_t ldq,
+                      int64_t M, int32_t n_head, int64_t K, int32_t dtype, int64_t row0, int64_t P, int64_t T,
+                      const qi_norm_fold* fold, const qi_qkprep* prep, const qi_kvcache* cache, int32_t layer,
+                      const qi_kvtiles* target, uint32_t* range_flags, void* stream);
 
 /* The fold's producing side for rows that no GEMM epilogue produced (the first layer's input):
  * x device fp32 [M][ldx] -> xc device `dtype` (QI_BF16 or QI_F16) [M][ldxc] = x (1 + w)(1 + scale

@@ -390,7 +390,7 @@ def test_text_projection(n, D):
 # one whole layer, the conditioning, and a small sampling loop
 # ------------------------------------------------------------------------------------------------
 
-def make_model(segments, D, F, n_layers, cfg=CFG, fold=True):
+def make_model(segments, D, F, n_layers, cfg=CFG, fold=True, kv_tiles=True):
     layout = rt.Layout(segments, DEV)
     sw_np = qin.shared_weights(cfg, D)
     lw_np = [qin.layer_weights(cfg, D, F, l) for l in range(n_layers)]
@@ -398,7 +398,7 @@ def make_model(segments, D, F, n_layers, cfg=CFG, fold=True):
     layers = [rt.LayerWeights(f32(L["norm1"]), f32(L["norm2"]), f32(L["q_norm"]), f32(L["k_norm"]),
                               bf(L["w_qkv"]), bf(L["w_out"]), bf(L["w_gate"]), bf(L["w_up"]), bf(L["w_down"]))
               for L in lw_np]
-    model = rt.DiT(layout, sw, layers, DEV, fold=fold)
+    model = rt.DiT(layout, sw, layers, DEV, fold=fold, kv_tiles=kv_tiles)
     shared64 = {k: v.f64 for k, v in sw_np.items()}
     layers64 = [{k: (v.f64 if isinstance(v, qin.Stored) else v) for k, v in L.items()} for L in lw_np]
     return model, shared64, layers64
@@ -424,12 +424,16 @@ def gpu_mods(model):
     return tuple(m[c][0] for c in range(6)), tuple(m[c][1] for c in range(6))
 
 
-@pytest.mark.parametrize("fold", [True, False])
+# (norm fold, fused QKV path writing the K/V tiles)
+MODES = [(True, True), (True, False), (False, False), (False, True)]
+
+
+@pytest.mark.parametrize("fold,kv", MODES)
 @pytest.mark.parametrize("segments,D,F", [(SMALL, 256, 512), ((qin.text(130), qin.image(8, 16, 1), qin.text(3),
                                                              qin.image(10, 10, 2), qin.image(16, 9, 0)), 384, 320)])
-def test_layer_step1_and_cached(segments, D, F, fold):
-    say(f"[layer] S={sum(g.n_tokens for g in segments)} D={D} F={F} fold={fold}")
-    model, sh, layers64 = make_model(segments, D, F, 1, fold=fold)
+def test_layer_step1_and_cached(segments, D, F, fold, kv):
+    say(f"[layer] S={sum(g.n_tokens for g in segments)} D={D} F={F} fold={fold} kv_tiles={kv}")
+    model, sh, layers64 = make_model(segments, D, F, 1, fold=fold, kv_tiles=kv)
     L = model.L
     S, P, T = L.S, L.P, L.T
     c, s = O.rope_tables(O.positions(segments))
@@ -455,11 +459,11 @@ def test_layer_step1_and_cached(segments, D, F, fold):
     assert model.attn.range_flags() == 0
 
 
-@pytest.mark.parametrize("fold", [True, False])
-def test_cached_layer_equals_step1_target_rows_bitwise(fold):
+@pytest.mark.parametrize("fold,kv", MODES)
+def test_cached_layer_equals_step1_target_rows_bitwise(fold, kv):
     # the same target input through step 1 (whole sequence) and through the cached path gives the
     # same target rows, bit for bit: the prefix K/V in the cache are the ones step 1 used
-    model, _, _ = make_model(SMALL, 256, 512, 1, fold=fold)
+    model, _, _ = make_model(SMALL, 256, 512, 1, fold=fold, kv_tiles=kv)
     S, P = model.L.S, model.L.P
     model.condition(0.5)
     x_in = f32(qin.normal(CFG, 272, (S, 256)))
@@ -472,12 +476,13 @@ def test_cached_layer_equals_step1_target_rows_bitwise(fold):
     assert torch.equal(model.x[P:], full_t)
 
 
-@pytest.mark.parametrize("fold,prepared", [(True, True), (True, False), (False, True)])   # (step() prepares itself)
-def test_sampling_loop_small(fold, prepared):
+@pytest.mark.parametrize("fold,prepared,kv", [(True, True, True), (True, False, True), (False, True, False),
+                                               (True, True, False)])   # (step() prepares itself)
+def test_sampling_loop_small(fold, prepared, kv):
     segments = (qin.text(20), qin.image(6, 5, 1), qin.image(7, 6, 0))
     D, F, n_layers, n_steps = 256, 512, 2, 3
-    say(f"[sampling loop] fold={fold} prepared={prepared}")
-    model, sh, layers64 = make_model(segments, D, F, n_layers, fold=fold)
+    say(f"[sampling loop] fold={fold} prepared={prepared} kv_tiles={kv}")
+    model, sh, layers64 = make_model(segments, D, F, n_layers, fold=fold, kv_tiles=kv)
     L = model.L
     n_text = 20
     x_text, lat_ref = qin.prefix_inputs(CFG, n_text, 30, D)
@@ -507,7 +512,7 @@ def test_full_size_layer_stages_sampled():
     wl = qin.WORKLOADS["txt512_10ref32_tgt64"]
     D, F, H = 3072, 8192, 24
     say(f"[layer full] S={wl.S} P={wl.P} T={wl.T}")
-    model, sh, layers64 = make_model(wl.segments, D, F, 1, cfg=wl.cfg_id)
+    model, sh, layers64 = make_model(wl.segments, D, F, 1, cfg=wl.cfg_id, kv_tiles=False)
     W = layers64[0]
     Lw = model.layers[0]
     S, P, T = wl.S, wl.P, wl.T
@@ -571,7 +576,7 @@ def test_full_size_layer_norm_fold_sampled(cached):
     wl = qin.WORKLOADS["txt512_10ref32_tgt64"]
     D, F = 3072, 8192
     say(f"[layer fold full] S={wl.S} P={wl.P} T={wl.T} cached={cached}")
-    model, sh, layers64 = make_model(wl.segments, D, F, 1, cfg=wl.cfg_id)
+    model, sh, layers64 = make_model(wl.segments, D, F, 1, cfg=wl.cfg_id, kv_tiles=False)
     W, Lw = layers64[0], model.layers[0]
     S, P = wl.S, wl.P
     r0 = P if cached else 0

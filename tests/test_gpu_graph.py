@@ -81,8 +81,9 @@ def test_cached_attention_and_euler_replay_equal_eager():
 
 
 def test_cached_dit_layer_replay_equals_eager():
-    # one cached layer of the single-stream denoiser (norm fold on): QKV, K/V prep, attention,
-    # merge, out-projection, gate-up and down-projection, captured and replayed
+    # one cached layer of the single-stream denoiser (norm fold and the fused QKV path on): QKV with
+    # the K/V tiles, attention, merge, out-projection, gate-up and down-projection, captured and
+    # replayed
     segs = (qin.text(40), qin.image(8, 10, 1), qin.image(12, 10, 0))
     D, F, H = 256, 512, 2
     say("[graph] cached DiT layer")

@@ -501,3 +501,42 @@ def test_norm_fold_producer_tile_and_width():
     hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "qi.h")).read()
     from image_generation_qi_amd import runtime as rt
     assert int(re.search(r"#define QI_FOLD_W (\d+)", hdr).group(1)) == rt.FOLD_W
+
+
+def test_fused_qkv_entry_points_reject():
+    # the fused QKV path's checks, all before any launch
+    io, prep, cache = _good()
+    L = Q.make_layout((qin.text(16), qin.image(4, 4, 0)))
+    tiles = Q.qi_kvtiles(FAKE + 0x10000, FAKE + 0x20000, 2, 64)
+    base = dict(x=FAKE, ldx=64, w=FAKE, bias=None, q_out=FAKE, ldq=256, M=32, n_head=2, K=64, dtype=Q.QI_F16,
+                row0=0, P=16, T=16, fold=None, prep=None, cache=cache, layer=0, target=tiles)
+    g = lambda **kw: Q.qi_gemm_qkv_tiles(**dict(base, **kw))
+    assert g(x=None) == Q.QI_ERR_ARG
+    assert g(dtype=Q.QI_F32) == Q.QI_ERR_DTYPE
+    assert g(K=96, ldx=96) == Q.QI_ERR_SHAPE                 # K % 64
+    assert g(M=33) == Q.QI_ERR_SHAPE                         # rows past P + T
+    assert g(T=0) == Q.QI_ERR_SHAPE
+    assert g(ldq=248) == Q.QI_ERR_SHAPE                      # below 128 n_head
+    assert g(ldx=68, K=64) == Q.QI_ERR_ALIGN                 # ldx % 8
+    assert g(q_out=FAKE + 8) == Q.QI_ERR_ALIGN
+    assert g(cache=None) == Q.QI_ERR_ARG                     # prefix rows need the cache
+    assert g(target=None) == Q.QI_ERR_ARG                    # target rows need the tile buffer
+    assert g(target=Q.qi_kvtiles(FAKE, FAKE, 3, 64)) == Q.QI_ERR_SHAPE   # head count
+    assert g(target=Q.qi_kvtiles(FAKE, FAKE, 2, 0)) == Q.QI_ERR_SHAPE    # rows below the key count
+    assert g(layer=5) == Q.QI_ERR_CAPACITY
+    assert g(fold=Q.make_norm_fold(None, 1e-6, None, FAKE, 64)) == Q.QI_ERR_ARG   # a producing side
+    assert g(M=0) == Q.QI_OK                                 # nothing to do: no launch
+    # the tiled attention entry points
+    q1 = Q.qi_qkv(FAKE, None, None, FAKE + 0x3000, Q.QI_BF16, 16, 2, 256)
+    ws = Q.qi_attn_tiled_workspace_bytes(L, 2)
+    assert ws >= 0
+    assert Q.qi_attn_target_cached_tiled(q1, None, cache, 0, 16, 0.0, None, FAKE, ws, None) == Q.QI_ERR_ARG
+    assert Q.qi_attn_target_cached_tiled(q1, None, cache, 0, 16, 0.0, Q.qi_kvtiles(FAKE, FAKE, 2, 0), FAKE, ws,
+                                         None) == Q.QI_ERR_SHAPE
+    q32 = Q.qi_qkv(FAKE, None, None, FAKE + 0x3000, Q.QI_F32, 16, 2, 256)
+    assert Q.qi_attn_target_cached_tiled(q32, None, cache, 0, 16, 0.0, tiles, FAKE, ws, None) == Q.QI_ERR_DTYPE
+    qs = Q.qi_qkv(FAKE, None, None, FAKE + 0x3000, Q.QI_BF16, 31, 2, 256)   # n_tok != S
+    assert Q.qi_attn_blockcausal_full_tiled(qs, None, L, 0.0, cache, 0, tiles, FAKE, ws, None) == Q.QI_ERR_SHAPE
+    qf = Q.qi_qkv(FAKE, None, None, FAKE + 0x3000, Q.QI_BF16, 32, 2, 256)
+    assert Q.qi_attn_blockcausal_full_tiled(qf, None, L, 0.0, None, 0, tiles, FAKE, ws, None) == Q.QI_ERR_ARG
+    assert Q.qi_attn_tiled_workspace_bytes(L, 0) == Q.QI_ERR_SHAPE
