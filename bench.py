@@ -224,13 +224,13 @@ def dit_bench(args):
     unf = [timed(lambda k=1 + i % n_cached: model.step(k, lat, sig)) for i in range(max(2, args.steps // 2))]
     model.fold = True
     ms_unf = sum(unf) / len(unf)
-    # and with the QKV projection writing K (normed, rotated) and V as the attention's tiles (the
-    # fused K/V path, six launches per cached layer), step 1 too
-    model.use_kv_tiles(True)
+    # and with the QKV projection storing plain K/V rows that a launch of their own prepares for the
+    # attention (without the fused K/V tiles: seven launches per cached layer), step 1 too
+    model.use_kv_tiles(False)
     model.step(1, lat, sig)
     kvs = [timed(lambda k=1 + i % n_cached: model.step(k, lat, sig)) for i in range(max(2, args.steps // 2))]
     ms1_kv = timed(lambda: model.step(0, lat, sig, tp(x_ctx, out=x_text), lat_ref))
-    model.use_kv_tiles(False)
+    model.use_kv_tiles(True)
     model.step(1, lat, sig)
     ms_kv = sum(kvs) / len(kvs)
     res = {
@@ -243,9 +243,10 @@ def dit_bench(args):
                    "cached_step_tflops": round(f_cached / (msc * 1e-3) / 1e12, 1),
                    "eight_step_loop_ms": round(ms_prep + ms1 + 7 * msc, 2),
                    "schedule_prepare_ms": round(ms_prep, 3),
-                   "norm_fold": True, "kv_tiles": False, "cached_step_ms_without_fold": round(ms_unf, 3),
-                   "cached_step_ms_with_kv_tiles": round(ms_kv, 3), "step1_ms_with_kv_tiles": round(ms1_kv, 3),
-                   "launches_per_cached_layer": 7,
+                   "norm_fold": True, "kv_tiles": True, "cached_step_ms_without_fold": round(ms_unf, 3),
+                   "cached_step_ms_without_kv_tiles": round(ms_kv, 3),
+                   "step1_ms_without_kv_tiles": round(ms1_kv, 3),
+                   "launches_per_cached_layer": 6,
                    "text_projection_ms": round(ms_tp, 4),
                    "text_projection_tflops": round(2 * 2 * n_text * D * D / (ms_tp * 1e-3) / 1e12, 1)},
     }

@@ -80,13 +80,14 @@ def test_cached_attention_and_euler_replay_equal_eager():
     assert att.range_flags() == 0
 
 
-def test_cached_dit_layer_replay_equals_eager():
-    # one cached layer of the single-stream denoiser (norm fold and the fused QKV path on): QKV with
-    # the K/V tiles, attention, merge, out-projection, gate-up and down-projection, captured and
-    # replayed
+@pytest.mark.parametrize("kv", [True, False])
+def test_cached_dit_layer_replay_equals_eager(kv):
+    # two cached layers of the single-stream denoiser (norm fold on; with the fused QKV path, QKV with
+    # the K/V tiles, else QKV and the K/V preparation; then attention, merge, out-projection,
+    # gate-up and down-projection), captured and replayed
     segs = (qin.text(40), qin.image(8, 10, 1), qin.image(12, 10, 0))
     D, F, H = 256, 512, 2
-    say("[graph] cached DiT layer")
+    say(f"[graph] cached DiT layers, kv_tiles={kv}")
     g = torch.Generator(device=DEV).manual_seed(8)
 
     def lin(n_out, n_in):
@@ -99,7 +100,7 @@ def test_cached_dit_layer_replay_equals_eager():
                               lin(F, D), lin(D, F)) for _ in range(2)]
     shared = rt.SharedWeights(lin(D, 256), lin(D, D), lin(6 * D, D), lin(D, D), lin(64, D), lin(D, 64))
     L = rt.Layout(segs, DEV)
-    model = rt.DiT(L, shared, layers, DEV)
+    model = rt.DiT(L, shared, layers, DEV, kv_tiles=kv)
     S, P = L.S, L.P
     model.condition(1.0)
     model.x.copy_(torch.randn((S, D), generator=g, device=DEV))
