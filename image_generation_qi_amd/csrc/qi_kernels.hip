@@ -190,6 +190,23 @@ __global__ __launch_bounds__(256) void k_prep_kv64(PrepArgs a) {
     const int64_t js = j < a.n_tok ? j : a.n_tok - 1;
     load8<IN, OUT_F16>(a.x, js * a.x_tok_stride + (int64_t)h * 128 + 8 * c, x[quarter]);
   }
+  // the norm weights of this thread's 8 dims and the rotation factors of its rows, loaded with the
+  // rows (rows past n_tok read the last row's factors, which are not used)
+  f32x4 rw0 = f32x4{1.f, 1.f, 1.f, 1.f}, rw1 = rw0;
+  if (a.rms_w) {
+    rw0 = *(const f32x4*)(a.rms_w + 8 * c);
+    rw1 = *(const f32x4*)(a.rms_w + 8 * c + 4);
+  }
+  f32x4 cs[4], sn[4];
+  if (a.cos_t) {
+#pragma unroll
+    for (int quarter = 0; quarter < 4; ++quarter) {
+      const int64_t j = (int64_t)t * 64 + rr + 16 * quarter;
+      const int64_t js = j < a.n_tok ? j : a.n_tok - 1;
+      cs[quarter] = *(const f32x4*)(a.cos_t + js * 64 + 4 * c);
+      sn[quarter] = *(const f32x4*)(a.sin_t + js * 64 + 4 * c);
+    }
+  }
 #pragma unroll
   for (int quarter = 0; quarter < 4; ++quarter) {
     if ((int64_t)t * 64 + rr + 16 * quarter >= a.n_tok) {
@@ -213,16 +230,17 @@ __global__ __launch_bounds__(256) void k_prep_kv64(PrepArgs a) {
       ss += __shfl_xor(ss, 8);
       const float rs = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xq[e] = xq[e] * rs * a.rms_w[8 * c + e];
+      for (int e = 0; e < 4; ++e) {
+        xq[e] = xq[e] * rs * rw0[e];
+        xq[4 + e] = xq[4 + e] * rs * rw1[e];
+      }
     }
     if (a.cos_t && ok) {
-      const f32x4 cs = *(const f32x4*)(a.cos_t + j * 64 + 4 * c);
-      const f32x4 sn = *(const f32x4*)(a.sin_t + j * 64 + 4 * c);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float x0 = xq[2 * e], x1 = xq[2 * e + 1];
-        xq[2 * e] = x0 * cs[e] - x1 * sn[e];
-        xq[2 * e + 1] = x0 * sn[e] + x1 * cs[e];
+        xq[2 * e] = x0 * cs[quarter][e] - x1 * sn[quarter][e];
+        xq[2 * e + 1] = x0 * sn[quarter][e] + x1 * cs[quarter][e];
       }
     }
     if (!ok) {
