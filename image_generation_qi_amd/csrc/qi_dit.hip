@@ -341,6 +341,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           acc[mb][nb] += *(const f32x4*)(bs_s + (tgt ? BN : 0) + WTN * wn + 16 * nb + 4 * G);
       }
     }
+    // The rotation factors of the tile's rows go through LDS (after the K sums, in the free
+    // stages): in two passes, row blocks 0, 1 then 2, 3 of every wave (128 rows, cos then sin, a
+    // row every TS floats), loaded as whole 16-byte pieces of the tables' rows.  Each pass's loads
+    // are issued ahead of the work before its LDS writes (the first before the K sums, the second
+    // before the first pass's rows are processed), so their latency overlaps it.
+    constexpr int TS = 136;                     // floats per staged row (64 cos, 64 sin, padding)
+    float* const tab_s = (float*)smem + 256 * 8;
+    const bool rot = a.cos_t != nullptr;
+    f32x4 tv[8];
+    auto table_loads = [&](int mb) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int idx = tid + 512 * i, sl = idx >> 5, ch = idx & 31;   // staged row, piece
+        const int64_t mr = m0 + 64 * (sl >> 5) + 16 * mb + (sl & 31);
+        tv[i] = ch < 16 ? f32x4{1.f, 1.f, 1.f, 1.f} : f32x4{0.f, 0.f, 0.f, 0.f};
+        if (rot && mr < a.M) tv[i] = *(const f32x4*)((ch < 16 ? a.cos_t : a.sin_t) + mr * 64 + 4 * (ch & 15));
+      }
+    };
+    auto table_store = [&]() {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int idx = tid + 512 * i, sl = idx >> 5, ch = idx & 31;
+        *(f32x4*)(tab_s + sl * TS + 4 * ch) = tv[i];
+      }
+    };
+    if (kvt) table_loads(0);
     // K's sum of squares per row as 8 block sums of 16 features (the stages are free now), each
     // block summed in one fixed order and the blocks added in a fixed order, so the K bits do not
     // depend on which rows a launch covers: wave column 0 holds blocks 0..5, wave column 1 blocks
@@ -369,24 +395,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int cb = WTN * wn + 16 * nb;
       kwv[nb] = (knorm && cb < 128) ? *(const f32x4*)(a.k_rms_w + cb + 4 * G) : f32x4{1.f, 1.f, 1.f, 1.f};
     }
-    // The rotation factors of the tile's rows go through LDS (after the K sums, in the free
-    // stages): in two passes, row blocks 0, 1 then 2, 3 of every wave (128 rows, cos then sin, a
-    // row every TS floats), loaded as whole 16-byte pieces of the tables' rows.
-    constexpr int TS = 136;                     // floats per staged row (64 cos, 64 sin, padding)
-    float* const tab_s = (float*)smem + 256 * 8;
-    const bool rot = a.cos_t != nullptr;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       if (kvt && (mb & 1) == 0) {
         if (mb) __syncthreads();                // every wave has read the previous pass's rows
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int idx = tid + 512 * i, sl = idx >> 5, ch = idx & 31;   // staged row, piece
-          const int64_t mr = m0 + 64 * (sl >> 5) + 16 * mb + (sl & 31);
-          f32x4 v = ch < 16 ? f32x4{1.f, 1.f, 1.f, 1.f} : f32x4{0.f, 0.f, 0.f, 0.f};
-          if (rot && mr < a.M) v = *(const f32x4*)((ch < 16 ? a.cos_t : a.sin_t) + mr * 64 + 4 * (ch & 15));
-          *(f32x4*)(tab_s + sl * TS + 4 * ch) = v;
-        }
+        table_store();
+        if (mb == 0) table_loads(2);            // the second pass's loads, in flight meanwhile
         __syncthreads();
       }
       const int rl = WTM * wm + 16 * mb + l16;
