@@ -224,15 +224,23 @@ def dit_bench(args):
     unf = [timed(lambda k=1 + i % n_cached: model.step(k, lat, sig)) for i in range(max(2, args.steps // 2))]
     model.fold = True
     ms_unf = sum(unf) / len(unf)
-    # and with the QKV projection storing plain K/V rows that a launch of their own prepares for the
-    # attention (without the fused K/V tiles: seven launches per cached layer), step 1 too
-    model.use_kv_tiles(False)
-    model.step(1, lat, sig)
-    kvs = [timed(lambda k=1 + i % n_cached: model.step(k, lat, sig)) for i in range(max(2, args.steps // 2))]
-    ms1_kv = timed(lambda: model.step(0, lat, sig, tp(x_ctx, out=x_text), lat_ref))
-    model.use_kv_tiles(True)
-    model.step(1, lat, sig)
-    ms_kv = sum(kvs) / len(kvs)
+    # the two forms of the QKV projection side by side, alternating step by step (phases of one run
+    # differ by a few tenths of a ms): the K/V tiles written by its epilogue (the default, six
+    # launches per cached layer) and plain K/V rows that a launch of their own prepares for the
+    # attention (seven); after each switch the schedule is prepared and one step warms up, untimed
+    pair = {True: [], False: []}
+    pair1 = {True: [], False: []}
+    for i in range(max(2, args.steps // 2)):
+        for form in (False, True):
+            model.use_kv_tiles(form)
+            model.prepare(sig)
+            model.step(1, lat, sig)
+            pair[form].append(timed(lambda k=1 + i % n_cached: model.step(k, lat, sig)))
+            if i == 0:
+                pair1[form].append(timed(lambda: model.step(0, lat, sig, tp(x_ctx, out=x_text), lat_ref)))
+    ms_kv = sum(pair[False]) / len(pair[False])
+    ms_kv_on = sum(pair[True]) / len(pair[True])
+    ms1_kv, ms1_kv_on = pair1[False][0], pair1[True][0]
     res = {
         "metric": "single-stream DiT denoiser step time (conditioning + layers + head + Euler)",
         "value": round(msc, 3), "unit": "ms per cached step", "higher_is_better": False,
@@ -244,8 +252,8 @@ def dit_bench(args):
                    "eight_step_loop_ms": round(ms_prep + ms1 + 7 * msc, 2),
                    "schedule_prepare_ms": round(ms_prep, 3),
                    "norm_fold": True, "kv_tiles": True, "cached_step_ms_without_fold": round(ms_unf, 3),
-                   "cached_step_ms_without_kv_tiles": round(ms_kv, 3),
-                   "step1_ms_without_kv_tiles": round(ms1_kv, 3),
+                   "alternating_cached_step_ms": {"kv_tiles": round(ms_kv_on, 3), "without_kv_tiles": round(ms_kv, 3)},
+                   "alternating_step1_ms": {"kv_tiles": round(ms1_kv_on, 3), "without_kv_tiles": round(ms1_kv, 3)},
                    "launches_per_cached_layer": 6,
                    "text_projection_ms": round(ms_tp, 4),
                    "text_projection_tflops": round(2 * 2 * n_text * D * D / (ms_tp * 1e-3) / 1e12, 1)},
