@@ -89,28 +89,35 @@ LAYOUTS = [
 
 
 @pytest.mark.parametrize("case", range(len(LAYOUTS)))
-@pytest.mark.parametrize("norm,rot", [(True, True), (False, True), (True, False)])
-def test_gemm_qkv_tiles_vs_oracle(case, norm, rot):
+@pytest.mark.parametrize("norm,rot,dt", [(True, True, "f16"), (False, True, "f16"), (True, False, "f16"),
+                                         (True, True, "bf16")])
+def test_gemm_qkv_tiles_vs_oracle(case, norm, rot, dt):
     segments, H, Kd = LAYOUTS[case]
     L = rt.Layout(segments, DEV)
     S, P, T = L.S, L.P, L.T
-    say(f"[qkv tiles] S={S} P={P} T={T} H={H} K={Kd} norm={norm} rot={rot}")
+    say(f"[qkv tiles] S={S} P={P} T={T} H={H} K={Kd} norm={norm} rot={rot} {dt}")
     x, w, kw = inputs(S, H, Kd, case)
-    xd = dev16(x.f64)
-    wt = rt.pack_qkv_tiles(rt.from_bits(w.bits, "bf16", DEV).to(torch.float16), H)
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    if dt == "bf16":   # bf16 activations and weights: the operands as stored (bf16 MFMA), Q rows bf16
+        x = qin.stored(x.f64, "bf16")
+        xd = rt.from_bits(x.bits, "bf16", DEV)
+    else:
+        xd = dev16(x.f64)
+    wt = rt.pack_qkv_tiles(rt.from_bits(w.bits, "bf16", DEV).to(tdt), H)
     cache = rt.KVCache(2, H, P, Q.QI_BF16, DEV)
     cache.k.fill_(float("nan"))
     cache.v.fill_(float("nan"))
     kvt = rt.KVTiles(T, H, DEV)
     kvt.k.fill_(float("nan"))
     kvt.v.fill_(float("nan"))
-    q = torch.full((S, 128 * H), float("nan"), dtype=torch.float16, device=DEV)
+    q = torch.full((S, 128 * H), float("nan"), dtype=tdt, device=DEV)
     flags = torch.zeros(1, dtype=torch.int32, device=DEV)
     kwd = torch.from_numpy(kw).to(DEV) if norm else None
     rt.gemm_qkv_tiles(xd, wt, q, H, 0, P, T, cache, 1, kvt, L.rows(0, S) if rot else None, kwd, 1e-6, flags=flags)
     sync()
     c, s = O.rope_tables(O.positions(segments))
-    wf16 = w.f64.astype(np.float16).astype(np.float64)   # the weights the GPU multiplies (fp16 copies)
+    # the weights the GPU multiplies (fp16 copies of the bf16 weights, or the bf16 weights as stored)
+    wf16 = w.f64.astype(np.float16).astype(np.float64) if dt == "f16" else w.f64
     rq, rk, rv = oracle_qkv(x.f64, wf16, H, c if rot else None, s if rot else None,
                             kw.astype(np.float64) if norm else None)
     check(host(q).reshape(S, H, 128), rq, "Q")
@@ -127,7 +134,7 @@ def test_gemm_qkv_tiles_vs_oracle(case, norm, rot):
     k1, v1 = kvt.k.clone(), kvt.v.clone()
     kvt.k.fill_(float("nan"))
     kvt.v.fill_(float("nan"))
-    q2 = torch.empty((T, 128 * H), dtype=torch.float16, device=DEV)
+    q2 = torch.empty((T, 128 * H), dtype=tdt, device=DEV)
     rt.gemm_qkv_tiles(xd[P:], wt, q2, H, P, P, T, None, 0, kvt, L.rows(P, S) if rot else None, kwd, 1e-6)
     sync()
     assert torch.equal(kvt.k, k1) and torch.equal(kvt.v, v1)
