@@ -348,3 +348,29 @@ def test_v_store_paths_agree_bitwise():
     for u, v in zip(out[0], out[1]):
         assert torch.equal(u, v)
     assert not torch.isnan(out[0][3]).any() and torch.all(kvt.v_rows()[:, T:] == 0)
+
+
+def test_attention_tiled_equals_unfused_bitwise_headline_shape():
+    # the 21,504-token layout (text 1024 + four 64 x 64 references + the 64 x 64 target), 24 heads:
+    # the tiled entry points against the unfused ones on the same tiles, every output bit
+    wl = qin.WORKLOADS["txt1024_4ref64_tgt64"]
+    H = wl.n_head
+    L = rt.Layout(wl.segments, DEV)
+    S, P, T = L.S, L.P, L.T
+    say(f"[attn tiled, headline shape] S={S} P={P} T={T} H={H}")
+    g = torch.Generator(device=DEV).manual_seed(11)
+    q, k, v = (torch.randn((S, H, 128), generator=g, device=DEV).to(torch.bfloat16) for _ in range(3))
+    kw = 1.0 + 0.02 * torch.randn(128, generator=g, device=DEV)
+    qw = 1.0 + 0.02 * torch.randn(128, generator=g, device=DEV)
+    att = rt.Attention(L, H, Q.QI_BF16, DEV)
+    cache = rt.KVCache(1, H, P, Q.QI_BF16, DEV)
+    o_ref = att.full(q, k, v, qw, kw, cache=cache, layer=0)
+    kvt = _tiles_of(k[P:], v[P:], H, T, L.rows(P, S), kw)
+    o_t = att.full_tiled(q, cache, 0, kvt, qw)
+    o_c = att.cached(q[P:], k[P:], v[P:], cache, 0, qw, kw)
+    o_ct = att.cached_tiled(q[P:], cache, 0, kvt, qw)
+    sync()
+    assert torch.equal(o_t, o_ref)
+    assert torch.equal(o_ct, o_c)
+    assert torch.equal(o_ct, o_ref[P:])
+    assert att.range_flags() == 0
