@@ -73,6 +73,17 @@ __device__ __forceinline__ float quad_xor2(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
 }
 
+// Sum over the four lane groups of a row (lanes l16, l16 + 16, l16 + 32, l16 + 48): lanes 16 apart
+// exchanged, then lanes 32 apart, by permlane swaps (no trip through the LDS unit, as ds_bpermute
+// takes); each exchange hands both lanes the two values in the same order, so all four lanes end
+// with the same bits.
+__device__ __forceinline__ float group_sum4(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // Four consecutive dims d .. d + 3 of key slot j of a 64-key V tile of the attention (fp16, [2 key
 // halves][4 key groups][128 dims][8 keys], element e of group g of half c holding key 32c +
 // 16(e / 4) + 4g + e % 4): one 2-byte store each (a dim's keys are 16 bytes apart from the next
@@ -380,9 +391,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int nb = 0; nb < NB; ++nb) {
           if (nb < nbk) {
             const f32x4 y = acc[mb][nb];
-            float v = (y[0] * y[0] + y[1] * y[1]) + (y[2] * y[2] + y[3] * y[3]);
-            v += __shfl_xor(v, 16);
-            v += __shfl_xor(v, 32);
+            const float v = group_sum4((y[0] * y[0] + y[1] * y[1]) + (y[2] * y[2] + y[3] * y[3]));
             if (G == 0) ks_s[(WTM * wm + 16 * mb + l16) * 8 + 6 * wn + nb] = v;
           }
         }
