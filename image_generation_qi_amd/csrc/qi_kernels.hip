@@ -28,6 +28,23 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
 // A value that fp16 cannot hold: magnitude 65520 or more (rounds to infinity) or not finite.
 __device__ __forceinline__ bool unfit_f16(float x) { return !(fabsf(x) < 65520.0f); }
 
+// Sum over the 16 lanes of a DPP row (one token's 128 dims, 8 per lane) in four butterfly steps of
+// DPP moves (partners: lane ^ 1, lane ^ 2, the mirrored lane within 8, the mirrored lane within
+// 16), each lane adding its partner's value to its own: every step pairs the same groups as lane
+// xor 1, 2, 4, 8 would and the additions commute, so all 16 lanes end with the same bits, without
+// a trip through the LDS unit.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+  v += dpp_mov<0x141>(v);   // row_half_mirror
+  v += dpp_mov<0x140>(v);   // row_mirror
+  return v;
+}
+
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   _Float16 ha = (_Float16)a, hb = (_Float16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
@@ -109,10 +126,7 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
-    ss += __shfl_xor(ss, 1);
-    ss += __shfl_xor(ss, 2);
-    ss += __shfl_xor(ss, 4);
-    ss += __shfl_xor(ss, 8);
+    ss = row16_sum(ss);
     const float r = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
 #pragma unroll
     for (int j = 0; j < 8; ++j) x[j] = x[j] * r * a.rms_w[8 * c + j];
@@ -224,10 +238,7 @@ __global__ __launch_bounds__(256) void k_prep_kv64(PrepArgs a) {
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss += xq[e] * xq[e];
-      ss += __shfl_xor(ss, 1);
-      ss += __shfl_xor(ss, 2);
-      ss += __shfl_xor(ss, 4);
-      ss += __shfl_xor(ss, 8);
+      ss = row16_sum(ss);
       const float rs = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
